@@ -1,0 +1,385 @@
+/*
+ * slay_oracle.c -- plain fp64 CPU oracle for causal SLAY attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the independent checker of the HIP
+ * library.  Only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark may load it.  It shares no code, header, table or constant
+ * with the GPU library: the Gauss-Laguerre rule, the feature map and every
+ * attention form below are written out here on their own.
+ *
+ * Everything is fp64 and written as plain loops in the order the method
+ * states its steps: no blocking, fusion or reordering beyond what each
+ * definition itself says.  Random draws (anchor vectors a, PRF vectors g)
+ * are inputs, never generated here.
+ *
+ * Sources (web pages; section names as printed on each page):
+ *   [SLAY-abs]  "SLAY: Geometry-Aware Spherical Linearized Attention with
+ *               Yat-Kernel", arXiv 2602.04915, English abstract (paperdance).
+ *   [SLAY-rev]  nubint.ai review of the same paper, sections "Motivation and
+ *               goals" (연구 동기 및 목표) and "Proposed method" (제안 방법,
+ *               six bullets, cited as bullet 1..6).
+ *
+ * Readings taken where the pages are silent (each marked READING below):
+ *   - K(u) = u^2 / (2 - 2u + eps): the E-product (q.k)^2/(|q-k|^2+eps) on
+ *     unit vectors, where |q-k|^2 = 2 - 2u.
+ *   - Laplace variable t = x/(2+eps), plain Gauss-Laguerre (weight e^{-x}).
+ *   - anchor feature (a.xh)^2 with a ~ N(0, I); PRF exp(sqrt(beta) g.xh -
+ *     beta/2) with g ~ N(0, I); tensor sketch = elementwise product of the
+ *     t-th anchor and t-th PRF feature of one node, scaled by sqrt(alpha/m).
+ *   - causal mask includes the diagonal (j <= i); no denominator guard.
+ *   - zero rows are normalised as x / max(|x|, 1e-12).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_BAD 1
+
+/* ------------------------------------------------------------------------ */
+/* Laguerre polynomials L_n(x) with L_n(0) = 1, by the three-term recurrence
+ * (n+1) L_{n+1} = (2n+1-x) L_n - n L_{n-1}.                                  */
+static double laguerre(int n, double x) {
+  double lm1 = 1.0, l = 1.0 - x;
+  if (n == 0) return 1.0;
+  for (int k = 1; k < n; ++k) {
+    double lp1 = ((2.0 * k + 1.0 - x) * l - k * lm1) / (k + 1.0);
+    lm1 = l;
+    l = lp1;
+  }
+  return l;
+}
+
+static double bisect_root(int n, double lo, double hi) {
+  double flo = laguerre(n, lo);
+  for (int it = 0; it < 200; ++it) {
+    double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    double fm = laguerre(n, mid);
+    if (fm == 0.0) return mid;
+    if ((fm > 0) == (flo > 0)) { lo = mid; flo = fm; } else { hi = mid; }
+  }
+  return 0.5 * (lo + hi);
+}
+
+/* R-point Gauss-Laguerre rule for int_0^inf e^{-x} f(x) dx
+ * ([SLAY-rev] Proposed method, bullet 4: the Laplace integral is discretised
+ * with Gauss-Laguerre quadrature).
+ * Nodes: the zeros of L_R.  The zeros of L_{n-1} interlace those of L_n, so
+ * the rule is built up from n = 1: each zero of L_n is bracketed between
+ * consecutive zeros of L_{n-1} (and 0 / an upper bound 4n+6) and found by
+ * bisection.  Weights: w_i = x_i / ((R+1)^2 L_{R+1}(x_i)^2).                 */
+int orc_gauss_laguerre(int R, double* x, double* w) {
+  if (R < 1 || R > 128 || !x || !w) return ORC_BAD;
+  double* prev = (double*)malloc(sizeof(double) * (size_t)R);
+  double* cur = (double*)malloc(sizeof(double) * (size_t)R);
+  if (!prev || !cur) { free(prev); free(cur); return ORC_BAD; }
+  cur[0] = 1.0; /* the zero of L_1 */
+  for (int n = 2; n <= R; ++n) {
+    memcpy(prev, cur, sizeof(double) * (size_t)(n - 1));
+    for (int i = 0; i < n; ++i) {
+      double lo = (i == 0) ? 0.0 : prev[i - 1];
+      double hi = (i == n - 1) ? 4.0 * n + 6.0 : prev[i];
+      cur[i] = bisect_root(n, lo, hi);
+    }
+  }
+  for (int i = 0; i < R; ++i) {
+    double lr1 = laguerre(R + 1, cur[i]);
+    x[i] = cur[i];
+    w[i] = cur[i] / ((R + 1.0) * (R + 1.0) * lr1 * lr1);
+  }
+  free(prev);
+  free(cur);
+  return ORC_OK;
+}
+
+/* Mixture parameters of node r ([SLAY-rev] Proposed method, bullets 2 and 4):
+ * 1/(2+eps-2u) = int_0^inf e^{-s(2+eps)} e^{2su} ds; with s = x/(2+eps) the
+ * integral becomes (1/(2+eps)) int e^{-x} e^{(2x/(2+eps)) u} dx, so
+ * alpha_r = w_r/(2+eps) and beta_r = 2 x_r/(2+eps).                           */
+int orc_node_params(int R, double eps, double* alpha, double* beta) {
+  if (!(eps > 0.0)) return ORC_BAD;
+  double* x = (double*)malloc(sizeof(double) * (size_t)R);
+  double* w = (double*)malloc(sizeof(double) * (size_t)R);
+  if (!x || !w) { free(x); free(w); return ORC_BAD; }
+  int st = orc_gauss_laguerre(R, x, w);
+  if (st == ORC_OK)
+    for (int r = 0; r < R; ++r) {
+      alpha[r] = w[r] / (2.0 + eps);
+      beta[r] = 2.0 * x[r] / (2.0 + eps);
+    }
+  free(x);
+  free(w);
+  return st;
+}
+
+/* Spherical Yat kernel K(u) = u^2/(2-2u+eps) ([SLAY-abs]; [SLAY-rev]
+ * Proposed method, bullet 1).  READING: the formula is not printed on the
+ * pages; this is the E-product restricted to the unit sphere.                */
+void orc_yat_kernel(int64_t n, const double* u, double eps, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = u[i] * u[i] / (2.0 - 2.0 * u[i] + eps);
+}
+
+/* Gauss-Laguerre mixture K_R(u) = sum_r alpha_r u^2 e^{beta_r u}
+ * ([SLAY-rev] Proposed method, bullets 2 and 4).                              */
+int orc_yat_mixture(int64_t n, const double* u, double eps, int R, double* out) {
+  double* alpha = (double*)malloc(sizeof(double) * (size_t)R);
+  double* beta = (double*)malloc(sizeof(double) * (size_t)R);
+  if (!alpha || !beta) { free(alpha); free(beta); return ORC_BAD; }
+  int st = orc_node_params(R, eps, alpha, beta);
+  if (st == ORC_OK)
+    for (int64_t i = 0; i < n; ++i) {
+      double s = 0.0;
+      for (int r = 0; r < R; ++r) s += alpha[r] * u[i] * u[i] * exp(beta[r] * u[i]);
+      out[i] = s;
+    }
+  free(alpha);
+  free(beta);
+  return st;
+}
+
+/* ------------------------------------------------------------------------ */
+/* SLAY feature map of n rows x[n][d] ([SLAY-abs]; [SLAY-rev] Proposed method,
+ * bullets 1, 3 and 5).
+ *   xh = x / max(|x|, 1e-12)                                  (unit sphere)
+ *   psi_{r,t}  = (a_{r,t} . xh)^2                           (anchor feature)
+ *   prf_{r,t}  = exp(sqrt(beta_r) g_{r,t} . xh - beta_r/2)     (positive RF)
+ *   phi[r*m+t] = sqrt(alpha_r/m) psi_{r,t} prf_{r,t}          (tensor sketch)
+ * a, g: [R*m][d] (row r*m+t).  phi: [n][R*m].                               */
+int orc_featmap(int64_t n, int d, int R, int m, double eps, const double* x,
+                const double* a, const double* g, double* phi) {
+  if (n < 0 || d < 1 || R < 1 || m < 1) return ORC_BAD;
+  double* alpha = (double*)malloc(sizeof(double) * (size_t)R);
+  double* beta = (double*)malloc(sizeof(double) * (size_t)R);
+  if (!alpha || !beta) { free(alpha); free(beta); return ORC_BAD; }
+  int st = orc_node_params(R, eps, alpha, beta);
+  if (st != ORC_OK) { free(alpha); free(beta); return st; }
+  const int F = R * m;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const double* xi = x + i * d;
+    double nrm = 0.0;
+    for (int c = 0; c < d; ++c) nrm += xi[c] * xi[c];
+    nrm = sqrt(nrm);
+    if (nrm < 1e-12) nrm = 1e-12;
+    for (int r = 0; r < R; ++r) {
+      for (int t = 0; t < m; ++t) {
+        const double* ar = a + (size_t)(r * m + t) * d;
+        const double* gr = g + (size_t)(r * m + t) * d;
+        double pa = 0.0, pg = 0.0;
+        for (int c = 0; c < d; ++c) {
+          pa += ar[c] * (xi[c] / nrm);
+          pg += gr[c] * (xi[c] / nrm);
+        }
+        double psi = pa * pa;
+        double prf = exp(sqrt(beta[r]) * pg - 0.5 * beta[r]);
+        phi[i * F + r * m + t] = sqrt(alpha[r] / m) * psi * prf;
+      }
+    }
+  }
+  free(alpha);
+  free(beta);
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Causal normalised attention on features, one head
+ * ([SLAY-rev] Proposed method, bullet 6; [SLAY-abs]):
+ *   s_ij = phq_i . phk_j,   o_i = sum_{j<=i} s_ij v_j / sum_{j<=i} s_ij.
+ * Three forms, written independently, that must agree to rounding.           */
+
+/* (1) brute force: forms the masked L x L score matrix row by row.
+ * An initial state (S0 [F][dv], z0 [F]) adds phq_i.S0 and phq_i.z0. */
+void orc_attn_brute(int64_t L, int F, int dv, const double* phq, const double* phk,
+                    const double* v, const double* S0, const double* z0, double* o) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+  for (int64_t i = 0; i < L; ++i) {
+    for (int64_t j = 0; j <= i; ++j) {
+      double acc = 0.0;
+      for (int f = 0; f < F; ++f) acc += phq[i * F + f] * phk[j * F + f];
+      s[j] = acc;
+    }
+    double den = 0.0;
+    for (int64_t j = 0; j <= i; ++j) den += s[j];
+    if (z0)
+      for (int f = 0; f < F; ++f) den += phq[i * F + f] * z0[f];
+    for (int e = 0; e < dv; ++e) {
+      double num = 0.0;
+      for (int64_t j = 0; j <= i; ++j) num += s[j] * v[j * dv + e];
+      if (S0)
+        for (int f = 0; f < F; ++f) num += phq[i * F + f] * S0[(size_t)f * dv + e];
+      o[i * dv + e] = num / den;
+    }
+  }
+  free(s);
+}
+
+/* (2) recurrent: S_i = S_{i-1} + phk_i v_i^T, z_i = z_{i-1} + phk_i, then
+ * o_i = phq_i^T S_i / phq_i^T z_i (update first, so S_i includes j = i).
+ * S [F][dv], z [F] are in/out (the running state).                          */
+void orc_attn_recurrent(int64_t L, int F, int dv, const double* phq, const double* phk,
+                        const double* v, double* S, double* z, double* o) {
+  for (int64_t i = 0; i < L; ++i) {
+    for (int f = 0; f < F; ++f) {
+      double kf = phk[i * F + f];
+      for (int e = 0; e < dv; ++e) S[(size_t)f * dv + e] += kf * v[i * dv + e];
+      z[f] += kf;
+    }
+    double den = 0.0;
+    for (int f = 0; f < F; ++f) den += phq[i * F + f] * z[f];
+    for (int e = 0; e < dv; ++e) {
+      double num = 0.0;
+      for (int f = 0; f < F; ++f) num += phq[i * F + f] * S[(size_t)f * dv + e];
+      o[i * dv + e] = num / den;
+    }
+  }
+}
+
+/* (3) chunked: for chunks [c0, c0+C), the masked intra-chunk block
+ * A = tril(phq_c phk_c^T) gives A v_c and A 1; the state before the chunk
+ * gives phq_c S and phq_c z; then S += phk_c^T v_c, z += phk_c^T 1.
+ * S, z in/out as in (2).                                                     */
+void orc_attn_chunked(int64_t L, int F, int dv, int C, const double* phq, const double* phk,
+                      const double* v, double* S, double* z, double* o) {
+  double* A = (double*)malloc(sizeof(double) * (size_t)C * (size_t)C);
+  for (int64_t c0 = 0; c0 < L; c0 += C) {
+    int64_t n = (L - c0 < C) ? (L - c0) : C;
+    for (int64_t i = 0; i < n; ++i)
+      for (int64_t j = 0; j < n; ++j) {
+        double acc = 0.0;
+        if (j <= i)
+          for (int f = 0; f < F; ++f) acc += phq[(c0 + i) * F + f] * phk[(c0 + j) * F + f];
+        A[i * C + j] = acc;
+      }
+    for (int64_t i = 0; i < n; ++i) {
+      double den = 0.0;
+      for (int64_t j = 0; j < n; ++j) den += A[i * C + j];
+      for (int f = 0; f < F; ++f) den += phq[(c0 + i) * F + f] * z[f];
+      for (int e = 0; e < dv; ++e) {
+        double num = 0.0;
+        for (int64_t j = 0; j < n; ++j) num += A[i * C + j] * v[(c0 + j) * dv + e];
+        for (int f = 0; f < F; ++f) num += phq[(c0 + i) * F + f] * S[(size_t)f * dv + e];
+        o[(c0 + i) * dv + e] = num / den;
+      }
+    }
+    for (int64_t j = 0; j < n; ++j)
+      for (int f = 0; f < F; ++f) {
+        double kf = phk[(c0 + j) * F + f];
+        for (int e = 0; e < dv; ++e) S[(size_t)f * dv + e] += kf * v[(c0 + j) * dv + e];
+        z[f] += kf;
+      }
+  }
+  free(A);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole causal SLAY forward over nh = B*H heads (parallel over heads):
+ * q, k [nh][L][d], v [nh][L][dv] -> o [nh][L][dv]; draws [R*m][d] shared by
+ * every head (or, if draw_head_stride > 0, head h uses a + h*stride).
+ * form: 0 brute, 1 recurrent, 2 chunked (chunk C).  S0/z0 nullable initial
+ * state [nh][F][dv] / [nh][F]; S_out/z_out nullable final state.            */
+int orc_slay_causal(int64_t nh, int64_t L, int d, int dv, int R, int m, double eps,
+                    const double* q, const double* k, const double* v, const double* a,
+                    const double* g, int64_t draw_head_stride, int form, int C,
+                    const double* S0, const double* z0, double* o, double* S_out, double* z_out) {
+  if (nh < 0 || L < 0 || d < 1 || dv < 1 || R < 1 || m < 1) return ORC_BAD;
+  if (form == 2 && C < 1) return ORC_BAD;
+  const int F = R * m;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t h = 0; h < nh; ++h) {
+    const double* ah = a + (draw_head_stride > 0 ? h * draw_head_stride : 0);
+    const double* gh = g + (draw_head_stride > 0 ? h * draw_head_stride : 0);
+    double* phq = (double*)malloc(sizeof(double) * (size_t)(L * F + 1));
+    double* phk = (double*)malloc(sizeof(double) * (size_t)(L * F + 1));
+    double* S = (double*)calloc((size_t)F * dv, sizeof(double));
+    double* z = (double*)calloc((size_t)F, sizeof(double));
+    if (!phq || !phk || !S || !z) { bad |= 1; free(phq); free(phk); free(S); free(z); continue; }
+    bad |= orc_featmap(L, d, R, m, eps, q + h * L * d, ah, gh, phq);
+    bad |= orc_featmap(L, d, R, m, eps, k + h * L * d, ah, gh, phk);
+    if (S0) memcpy(S, S0 + h * (int64_t)F * dv, sizeof(double) * (size_t)F * dv);
+    if (z0) memcpy(z, z0 + h * (int64_t)F, sizeof(double) * (size_t)F);
+    const double* vh = v + h * L * dv;
+    double* oh = o + h * L * dv;
+    if (form == 0) {
+      orc_attn_brute(L, F, dv, phq, phk, vh, S0 ? S : NULL, z0 ? z : NULL, oh);
+      /* final state for the brute-force form: the plain sums */
+      for (int64_t j = 0; j < L; ++j)
+        for (int f = 0; f < F; ++f) {
+          for (int e = 0; e < dv; ++e) S[(size_t)f * dv + e] += phk[j * F + f] * vh[j * dv + e];
+          z[f] += phk[j * F + f];
+        }
+    } else if (form == 1) {
+      orc_attn_recurrent(L, F, dv, phq, phk, vh, S, z, oh);
+    } else {
+      orc_attn_chunked(L, F, dv, C, phq, phk, vh, S, z, oh);
+    }
+    if (S_out) memcpy(S_out + h * (int64_t)F * dv, S, sizeof(double) * (size_t)F * dv);
+    if (z_out) memcpy(z_out + h * (int64_t)F, z, sizeof(double) * (size_t)F);
+    free(phq);
+    free(phk);
+    free(S);
+    free(z);
+  }
+  return bad ? ORC_BAD : ORC_OK;
+}
+
+/* Exact spherical-Yat causal attention (no features), one pass over nh heads:
+ * o_i = sum_{j<=i} K(qh_i.kh_j) v_j / sum_{j<=i} K(qh_i.kh_j)
+ * ([SLAY-rev] Main results, bullet 1: the comparison point "full spherical
+ * YAT attention").  Reported, not used as a parity target.                  */
+int orc_yat_exact_causal(int64_t nh, int64_t L, int d, int dv, double eps, const double* q,
+                         const double* k, const double* v, double* o) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t h = 0; h < nh; ++h) {
+    const double* qh = q + h * L * d;
+    const double* kh = k + h * L * d;
+    const double* vh = v + h * L * dv;
+    double* oh = o + h * L * dv;
+    for (int64_t i = 0; i < L; ++i) {
+      double nq = 0.0;
+      for (int c = 0; c < d; ++c) nq += qh[i * d + c] * qh[i * d + c];
+      nq = fmax(sqrt(nq), 1e-12);
+      double den = 0.0;
+      for (int e = 0; e < dv; ++e) oh[i * dv + e] = 0.0;
+      for (int64_t j = 0; j <= i; ++j) {
+        double nk = 0.0, u = 0.0;
+        for (int c = 0; c < d; ++c) {
+          nk += kh[j * d + c] * kh[j * d + c];
+          u += qh[i * d + c] * kh[j * d + c];
+        }
+        nk = fmax(sqrt(nk), 1e-12);
+        u = u / (nq * nk);
+        double s = u * u / (2.0 - 2.0 * u + eps);
+        den += s;
+        for (int e = 0; e < dv; ++e) oh[i * dv + e] += s * vh[j * dv + e];
+      }
+      for (int e = 0; e < dv; ++e) oh[i * dv + e] /= den;
+    }
+  }
+  return ORC_OK;
+}
+
+/* Selected rows i of the causal attention of one head, each computed on its
+ * own as sum_{j<=i} s_ij v_j / sum_{j<=i} s_ij (spot checks at sizes where
+ * the whole forward is too slow).  phq_rows [n_rows][F] holds the features
+ * of the selected queries; phk [L][F], v [L][dv] cover every key j <= i.     */
+void orc_attn_rows(int64_t n_rows, const int64_t* rows, int F, int dv, const double* phq_rows,
+                   const double* phk, const double* v, double* o_rows) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int64_t i = rows[r];
+    const double* qf = phq_rows + r * F;
+    double den = 0.0;
+    double* orow = o_rows + r * dv;
+    for (int e = 0; e < dv; ++e) orow[e] = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+      double s = 0.0;
+      for (int f = 0; f < F; ++f) s += qf[f] * phk[j * F + f];
+      den += s;
+      for (int e = 0; e < dv; ++e) orow[e] += s * v[j * dv + e];
+    }
+    for (int e = 0; e < dv; ++e) orow[e] /= den;
+  }
+}

@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for causal SLAY workloads.
+
+Shared by the tests, the smoke check and the benchmark; imported by both the
+HIP path's tests and the oracle's tests.  It holds none of the method's
+arithmetic: only Gaussian draws, the workload recipe's fp32 unit
+normalisation of q and k, and fp32 -> bf16 round-to-nearest-even.
+
+Recipe (the pages train on corpora and image/label sets that are not
+available; these synthetic inputs stand in for them):
+  q, k, v ~ i.i.d. N(0, 1) in fp32; q and k are then scaled to unit L2 norm
+  in fp32 and, for bf16 workloads, rounded to bf16 (RNE).  The anchor and PRF
+  draws are i.i.d. N(0, 1) of shape [R*m, d] (row r*m + t), rounded to bf16
+  for bf16 workloads.  Seeds: inputs use ``default_rng([workload_id, 0])``,
+  draws ``[workload_id, 1]``, decode step t ``[workload_id, 2, t]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    wid: int
+    B: int
+    H: int
+    L: int
+    d: int
+    dv: int
+    R: int
+    m: int
+    chunk: int
+    dtype: str  # "f32" or "bf16"
+    eps: float = 1e-3
+    steps: int = 0  # decode workloads: number of single-token steps
+
+    @property
+    def F(self) -> int:
+        return self.R * self.m
+
+    @property
+    def n_heads(self) -> int:
+        return self.B * self.H
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    # tiny fp32 forward (parity only)
+    "tiny_f32": Workload("tiny_f32", 1, B=1, H=1, L=256, d=64, dv=64, R=2, m=16, chunk=32, dtype="f32"),
+    # B4 H8 L2048 bf16 forward
+    "b4h8_l2k_bf16": Workload("b4h8_l2k_bf16", 2, B=4, H=8, L=2048, d=64, dv=64, R=3, m=32, chunk=64,
+                              dtype="bf16"),
+    # B1 H16 L16384 bf16 forward (the headline workload)
+    "h16_l16k_bf16": Workload("h16_l16k_bf16", 3, B=1, H=16, L=16384, d=64, dv=64, R=4, m=64, chunk=64,
+                              dtype="bf16"),
+    # B1 H8 L131072 d=dv=128 bf16 forward
+    "h8_l128k_d128_bf16": Workload("h8_l128k_d128_bf16", 4, B=1, H=8, L=131072, d=128, dv=128, R=4, m=128,
+                                   chunk=128, dtype="bf16"),
+    # recurrent decode: 256 sequences x 16 heads, 4096 single-token steps, fp32
+    "decode_256x16_f32": Workload("decode_256x16_f32", 5, B=256, H=16, L=1, d=64, dv=64, R=4, m=64, chunk=1,
+                                  dtype="f32", steps=4096),
+}
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32 holding bf16 values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bias = ((u >> 16) & 1) + 0x7FFF
+    r = ((u + bias) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32).reshape(x.shape)
+
+
+def _unit_rows(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True, dtype=np.float32))
+    return (x / n).astype(np.float32)
+
+
+def _finish(x: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_round(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def make_draws(w: Workload, seed=None):
+    """Anchor and PRF draws, each [R*m, d] fp32 (bf16-exact for bf16 workloads)."""
+    rng = np.random.default_rng([w.wid, 1] if seed is None else seed)
+    a = rng.standard_normal((w.F, w.d), dtype=np.float32)
+    g = rng.standard_normal((w.F, w.d), dtype=np.float32)
+    return _finish(a, w.dtype), _finish(g, w.dtype)
+
+
+def make_qkv(w: Workload, seed=None, near_pairs: float = 0.0):
+    """q, k [B, H, L, d] and v [B, H, L, dv] fp32 (bf16-exact for bf16 workloads).
+
+    near_pairs > 0 builds a stress set with large q.k: k = unit(q + near_pairs * noise).
+    """
+    rng = np.random.default_rng([w.wid, 0] if seed is None else seed)
+    shp = (w.B, w.H, w.L)
+    q = rng.standard_normal(shp + (w.d,), dtype=np.float32)
+    k = rng.standard_normal(shp + (w.d,), dtype=np.float32)
+    v = rng.standard_normal(shp + (w.dv,), dtype=np.float32)
+    q = _unit_rows(q)
+    if near_pairs > 0:
+        k = q + np.float32(near_pairs) * k
+    k = _unit_rows(k)
+    return _finish(q, w.dtype), _finish(k, w.dtype), _finish(v, w.dtype)
+
+
+def make_decode_step(w: Workload, t: int, n_heads: int | None = None):
+    """Single-token q, k [n_heads, d] and v [n_heads, dv] for decode step t (fp32)."""
+    nh = w.n_heads if n_heads is None else n_heads
+    rng = np.random.default_rng([w.wid, 2, int(t)])
+    q = rng.standard_normal((nh, w.d), dtype=np.float32)
+    k = rng.standard_normal((nh, w.d), dtype=np.float32)
+    v = rng.standard_normal((nh, w.dv), dtype=np.float32)
+    return _finish(_unit_rows(q), w.dtype), _finish(_unit_rows(k), w.dtype), _finish(v, w.dtype)

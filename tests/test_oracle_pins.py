@@ -1,0 +1,365 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's own formula: each checks the oracle
+against a textbook closed form, a library routine, an invariant, brute force
+on a tiny case, or a Monte Carlo mean with a known closed form, chosen so that
+a dropped term, a wrong sign, a wrong index or a transposed operand fails.
+
+Pages: "SLAY: Geometry-Aware Spherical Linearized Attention with Yat-Kernel"
+(arXiv 2602.04915, English abstract) and the nubint.ai review of it
+("Proposed method" bullets 1-6; "Main results").
+"""
+import math
+
+import numpy as np
+import pytest
+from numpy.polynomial import laguerre as npl
+from scipy import integrate
+
+EPS = 1e-3
+
+
+# ----------------------------------------------------------------------------
+# Gauss-Laguerre rule (review, "Proposed method" bullet 4)
+
+def test_gl_two_point_closed_form(orc):
+    # textbook: zeros of L_2 = (x^2 - 4x + 2)/2 are 2 -+ sqrt 2, weights (2 +- sqrt 2)/4
+    x, w = orc.gauss_laguerre(2)
+    s2 = math.sqrt(2.0)
+    np.testing.assert_allclose(x, [2 - s2, 2 + s2], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(w, [(2 + s2) / 4, (2 - s2) / 4], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 8, 12, 16])
+def test_gl_exact_on_polynomials(orc, R):
+    # an R-point Gauss rule integrates x^k e^{-x} exactly for k <= 2R-1: int = k!
+    x, w = orc.gauss_laguerre(R)
+    for k in range(2 * R):
+        got = float(np.sum(w * x ** k))
+        assert abs(got - math.factorial(k)) <= 1e-11 * math.factorial(k), (R, k, got)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 6, 8, 16, 24, 32])
+def test_gl_matches_numpy_laggauss(orc, R):
+    x, w = orc.gauss_laguerre(R)
+    xr, wr = npl.laggauss(R)
+    np.testing.assert_allclose(x, xr, rtol=1e-11, atol=0)
+    np.testing.assert_allclose(w, wr, rtol=1e-9, atol=1e-300)
+    # nodes are zeros of L_R (library evaluation of the Laguerre series)
+    c = np.zeros(R + 1)
+    c[R] = 1.0
+    step = npl.lagval(x, c) / npl.lagval(x, npl.lagder(c))  # Newton step to the nearest zero
+    assert np.max(np.abs(step) / x) < 1e-11
+
+
+def test_node_params_scaling(orc):
+    # alpha_r = w_r/(2+eps), beta_r = 2 x_r/(2+eps); pinned through the library rule
+    for R in (2, 3, 4):
+        a, b = orc.node_params(R, EPS)
+        xr, wr = npl.laggauss(R)
+        np.testing.assert_allclose(a * (2 + EPS), wr, rtol=1e-9)
+        np.testing.assert_allclose(b * (2 + EPS) / 2, xr, rtol=1e-11)
+
+
+# ----------------------------------------------------------------------------
+# The spherical Yat kernel (abstract; review "Proposed method" bullet 1)
+
+def test_yat_kernel_is_eproduct_on_sphere(orc):
+    # E-product (q.k)^2 / (|q-k|^2 + eps) evaluated on explicit unit vectors
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((500, 16))
+    k = rng.standard_normal((500, 16))
+    k[:50] = q[:50] + 0.01 * k[:50]  # include nearly aligned pairs
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    u = np.sum(q * k, axis=1)
+    eprod = u ** 2 / (np.sum((q - k) ** 2, axis=1) + EPS)
+    np.testing.assert_allclose(orc.yat_kernel(u, EPS), eprod, rtol=1e-9)
+
+
+def test_yat_kernel_special_values_and_bounds(orc):
+    assert orc.yat_kernel([-1.0], EPS)[0] == pytest.approx(1.0 / (4.0 + EPS), rel=1e-15)
+    assert orc.yat_kernel([0.0], EPS)[0] == 0.0
+    assert orc.yat_kernel([1.0], EPS)[0] == pytest.approx(1.0 / EPS, rel=1e-15)
+    u = np.linspace(-1, 1, 20001)
+    K = orc.yat_kernel(u, EPS)
+    assert np.all(K >= 0) and np.all(K <= 1.0 / EPS * (1 + 1e-15))  # boundedness (abstract)
+
+
+def test_laplace_representation(orc):
+    # review bullet 2: 1/(2+eps-2u) = int_0^inf e^{-s(2+eps)} e^{2su} ds (scipy quadrature)
+    for u in (-1.0, -0.5, 0.0, 0.3, 0.75, 0.95):
+        val, _ = integrate.quad(lambda s: u * u * math.exp(-s * (2 + EPS) + 2 * s * u), 0, np.inf,
+                                epsabs=0, epsrel=1e-12, limit=400)
+        assert val == pytest.approx(float(orc.yat_kernel([u], EPS)[0]), rel=1e-9, abs=1e-300)
+
+
+def test_mixture_converges_to_kernel(orc):
+    # review bullet 4: the Gauss-Laguerre sum converges to K as R grows
+    u = np.linspace(-1.0, 0.75, 701)
+    K = orc.yat_kernel(u, EPS)
+    K32 = orc.yat_mixture(u, EPS, 32)
+    nz = np.abs(u) > 1e-3
+    assert np.max(np.abs(K32[nz] - K[nz]) / K[nz]) < 1e-12
+    # coarse rules stay within the spectral accuracy expected of them on [-1, 0.5]
+    u = np.linspace(-1.0, 0.5, 601)
+    K = orc.yat_kernel(u, EPS)
+    nz = np.abs(u) > 1e-3
+    errs = {R: np.max(np.abs(orc.yat_mixture(u, EPS, R)[nz] - K[nz]) / K[nz]) for R in (2, 3, 4, 8)}
+    assert errs[2] < 5e-2 and errs[3] < 1e-2 and errs[4] < 1e-3 and errs[8] < 1e-6
+    assert errs[2] > errs[3] > errs[4] > errs[8]
+
+
+def test_kernels_positive_definite_on_sphere(orc):
+    # abstract: positive definiteness on the sphere -- Gram matrices are PSD
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((120, 8))
+    X /= np.linalg.norm(X, axis=1, keepdims=True)
+    U = np.clip(X @ X.T, -1, 1)
+    for G in (orc.yat_kernel(U, EPS).reshape(U.shape), orc.yat_mixture(U, EPS, 4).reshape(U.shape),
+              orc.mean_kernel_closed_form(U, EPS, 4).reshape(U.shape)):
+        ev = np.linalg.eigvalsh(0.5 * (G + G.T))
+        assert ev.min() >= -1e-12 * ev.max()
+
+
+# ----------------------------------------------------------------------------
+# Feature map (review bullets 3 and 5)
+
+def _params(orc, R):
+    return orc.node_params(R, EPS)
+
+
+def test_featmap_basis_anchors_zero_prf(orc):
+    # anchors a_f = e_{f mod d}, PRF draws g = 0: phi_f = sqrt(alpha_r/m) xh_{f mod d}^2 e^{-beta_r/2}
+    R, m, d = 3, 8, 5
+    F = R * m
+    A = np.zeros((F, d))
+    A[np.arange(F), np.arange(F) % d] = 1.0
+    G = np.zeros((F, d))
+    x = np.array([[3.0, -4.0, 1.0, 0.5, -2.0], [0.1, 0.2, -0.3, 0.4, 0.9]])
+    phi = orc.featmap(x, A, G, EPS, R, m)
+    alpha, beta = _params(orc, R)
+    xh = x / np.linalg.norm(x, axis=1, keepdims=True)
+    for f in range(F):
+        r = f // m
+        want = np.sqrt(alpha[r] / m) * xh[:, f % d] ** 2 * np.exp(-beta[r] / 2)
+        np.testing.assert_allclose(phi[:, f], want, rtol=1e-13)
+
+
+def test_featmap_aligned_anchors_basis_prf(orc):
+    # anchors along xh (psi = 1), PRF g_f = e_{f mod d}: phi_f = sqrt(alpha_r/m) exp(sqrt(beta_r) xh_j - beta_r/2)
+    R, m, d = 2, 6, 4
+    F = R * m
+    x = np.array([[1.0, 2.0, -2.0, 4.0]])
+    xh = x[0] / np.linalg.norm(x[0])
+    A = np.tile(xh, (F, 1))
+    G = np.zeros((F, d))
+    G[np.arange(F), np.arange(F) % d] = 1.0
+    phi = orc.featmap(x, A, G, EPS, R, m)[0]
+    alpha, beta = _params(orc, R)
+    for f in range(F):
+        r = f // m
+        want = np.sqrt(alpha[r] / m) * np.exp(np.sqrt(beta[r]) * xh[f % d] - beta[r] / 2)
+        assert phi[f] == pytest.approx(want, rel=1e-13)
+
+
+def test_featmap_scale_invariant_and_positive(orc):
+    # unit-sphere projection (abstract): phi(c x) = phi(x) for c > 0; strictly positive
+    rng = np.random.default_rng(3)
+    R, m, d = 4, 16, 64
+    A = rng.standard_normal((R * m, d))
+    G = rng.standard_normal((R * m, d))
+    x = rng.standard_normal((50, d))
+    p1 = orc.featmap(x, A, G, EPS, R, m)
+    p2 = orc.featmap(7.5 * x, A, G, EPS, R, m)
+    np.testing.assert_allclose(p1, p2, rtol=1e-12)
+    assert np.all(p1 > 0)
+
+
+@pytest.mark.parametrize("R,c,u", [(2, 1.0, -0.5), (2, 1.0, 0.0), (2, 1.0, 0.125), (2, 1.0, 0.5),
+                                   (3, 0.35, -0.5), (3, 0.35, 0.25), (3, 0.35, 0.9), (4, 0.3, 0.6)])
+def test_featmap_monte_carlo_mean(orc, R, c, u):
+    """Node means of phi(q).phi(k) over the draws against their closed form.
+
+    Features of one node are i.i.d. over t, so one call with large m gives m
+    independent samples per node; each node's mean is tested on its own.  With
+    PRF draws scaled to c*g the node mean is
+        alpha_r (1 + 2u^2) exp(beta_r c^2 (1 + u) - beta_r)
+    (Isserlis' theorem for the anchor factor, the Gaussian moment generating
+    function for the PRF factor); c = 1 gives the unbiased PRF mean
+    alpha_r (1 + 2u^2) e^{beta_r u}.  c < 1 keeps the log-normal PRF product
+    light-tailed enough for a 4.5-sigma test at large beta_r and u.
+    """
+    m, d = 40000, 8
+    rng = np.random.default_rng([17, R, int(100 * c), int(1000 * (u + 1))])
+    q = np.zeros(d)
+    q[0] = 1.0
+    k = np.zeros(d)
+    k[0], k[1] = u, math.sqrt(1 - u * u)
+    A = rng.standard_normal((R * m, d))
+    G = c * rng.standard_normal((R * m, d))
+    phi = orc.featmap(np.stack([q, k]), A, G, EPS, R, m)
+    alpha, beta = _params(orc, R)
+    prod = (phi[0] * phi[1]).reshape(R, m)
+    for r in range(R):
+        samples = prod[r] * m / alpha[r]
+        want = (1 + 2 * u * u) * math.exp(beta[r] * c * c * (1 + u) - beta[r])
+        z = (samples.mean() - want) / (samples.std(ddof=1) / math.sqrt(m))
+        assert abs(z) < 4.5, (r, samples.mean(), want, z)
+    if c == 1.0:
+        # the whole estimator's mean is the closed-form mixture mean (1+2u^2) sum_r alpha_r e^{beta_r u}
+        total = (phi[0] * phi[1]).reshape(R, m).sum(1)
+        assert total.sum() == pytest.approx(float(orc.mean_kernel_closed_form([u], EPS, R)[0]), rel=0.1)
+
+
+def test_featmap_anchor_factor_mean_isserlis(orc):
+    # with zero PRF draws the PRF factor is the constant e^{-beta/2}: the node mean is
+    # E[(a.q)^2 (a.k)^2] e^{-beta_r} = (1 + 2u^2) e^{-beta_r} (Isserlis)
+    R, m, d, u = 2, 60000, 6, 0.3
+    rng = np.random.default_rng(23)
+    q = np.array([1.0, 0, 0, 0, 0, 0])
+    k = np.array([u, math.sqrt(1 - u * u), 0, 0, 0, 0])
+    A = rng.standard_normal((R * m, d))
+    phi = orc.featmap(np.stack([q, k]), A, np.zeros((R * m, d)), EPS, R, m)
+    alpha, beta = _params(orc, R)
+    prod = (phi[0] * phi[1]).reshape(R, m)
+    for r in range(R):
+        s = prod[r] * m / alpha[r]
+        want = (1 + 2 * u * u) * math.exp(-beta[r])
+        z = (s.mean() - want) / (s.std(ddof=1) / math.sqrt(m))
+        assert abs(z) < 4.5
+
+
+# ----------------------------------------------------------------------------
+# Attention forms (review bullet 6)
+
+def _rand_feats(rng, L, F, dv):
+    phq = rng.uniform(0.01, 1.0, (L, F))
+    phk = rng.uniform(0.01, 1.0, (L, F))
+    v = rng.standard_normal((L, dv))
+    return phq, phk, v
+
+
+def test_onehot_keys_give_weighted_prefix_average(orc):
+    # phk_j = e_j makes s_ij = phq_i[j]: o_i is the weighted average of v_0..v_i
+    rng = np.random.default_rng(2)
+    L, dv = 9, 3
+    phk = np.eye(L)
+    phq = rng.uniform(0.1, 2.0, (L, L))
+    v = rng.standard_normal((L, dv))
+    want = np.stack([np.average(v[: i + 1], axis=0, weights=phq[i, : i + 1]) for i in range(L)])
+    np.testing.assert_allclose(orc.attn_brute(phq, phk, v), want, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(orc.attn_recurrent(phq, phk, v)[0], want, rtol=1e-13, atol=1e-14)
+    for C in (1, 2, 4, 9):
+        np.testing.assert_allclose(orc.attn_chunked(phq, phk, v, C)[0], want, rtol=1e-13, atol=1e-14)
+
+
+def test_onehot_queries_and_keys_give_identity(orc):
+    # phq_i = e_i, phk_j = e_j + tiny: s_ij ~ delta_ij, so o_i ~ v_i
+    L, dv = 6, 2
+    phk = np.eye(L) + 1e-300
+    phq = np.eye(L)
+    v = np.arange(L * dv, dtype=float).reshape(L, dv)
+    np.testing.assert_allclose(orc.attn_brute(phq, phk, v), v, rtol=1e-12)
+    np.testing.assert_allclose(orc.attn_chunked(phq, phk, v, 4)[0], v, rtol=1e-12)
+
+
+def test_equal_scores_give_prefix_mean(orc):
+    L, F, dv = 40, 5, 4
+    rng = np.random.default_rng(9)
+    phq = np.tile(rng.uniform(0.1, 1, F), (L, 1))
+    phk = np.tile(rng.uniform(0.1, 1, F), (L, 1))
+    v = rng.standard_normal((L, dv))
+    want = np.cumsum(v, axis=0) / np.arange(1, L + 1)[:, None]
+    np.testing.assert_allclose(orc.attn_recurrent(phq, phk, v)[0], want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("C", [1, 7, 32, 100, 128])
+def test_forms_agree(orc, C):
+    rng = np.random.default_rng(C)
+    L, F, dv = 100, 24, 8
+    phq, phk, v = _rand_feats(rng, L, F, dv)
+    ob = orc.attn_brute(phq, phk, v)
+    orr, Sr, zr = orc.attn_recurrent(phq, phk, v)
+    oc, Sc, zc = orc.attn_chunked(phq, phk, v, C)
+    np.testing.assert_allclose(orr, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(oc, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Sc, Sr, rtol=1e-12)
+    np.testing.assert_allclose(zc, zr, rtol=1e-12)
+    np.testing.assert_allclose(zr, phk.sum(0), rtol=1e-12)
+    np.testing.assert_allclose(Sr, phk.T @ v, rtol=1e-10, atol=1e-12)
+
+
+def test_invariants(orc):
+    rng = np.random.default_rng(4)
+    L, F, dv = 60, 16, 6
+    phq, phk, v = _rand_feats(rng, L, F, dv)
+    o = orc.attn_brute(phq, phk, v)
+    np.testing.assert_allclose(o[0], v[0], rtol=1e-14)  # o_1 = v_1
+    lo = np.minimum.accumulate(v, axis=0)
+    hi = np.maximum.accumulate(v, axis=0)
+    assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12)  # convex combination
+    np.testing.assert_allclose(orc.attn_brute(phq, phk, 3.0 * v - 2.0), 3.0 * o - 2.0, rtol=1e-12, atol=1e-12)
+
+
+def test_state_handoff(orc):
+    # running [0, L) in two parts with the state carried equals one pass
+    rng = np.random.default_rng(6)
+    L, F, dv, cut = 90, 12, 5, 37
+    phq, phk, v = _rand_feats(rng, L, F, dv)
+    o_all, S_all, z_all = orc.attn_recurrent(phq, phk, v)
+    o1, S1, z1 = orc.attn_chunked(phq[:cut], phk[:cut], v[:cut], 16)
+    o2, S2, z2 = orc.attn_chunked(phq[cut:], phk[cut:], v[cut:], 16, S1, z1)
+    np.testing.assert_allclose(np.concatenate([o1, o2]), o_all, rtol=1e-12)
+    np.testing.assert_allclose(S2, S_all, rtol=1e-12)
+    ob2 = orc.attn_brute(phq[cut:], phk[cut:], v[cut:], S1, z1)
+    np.testing.assert_allclose(ob2, o_all[cut:], rtol=1e-12)
+
+
+def test_rows_match_brute(orc):
+    rng = np.random.default_rng(8)
+    L, F, dv = 70, 10, 4
+    phq, phk, v = _rand_feats(rng, L, F, dv)
+    rows = np.array([0, 5, 33, 69])
+    np.testing.assert_allclose(orc.attn_rows(rows, phq[rows], phk, v), orc.attn_brute(phq, phk, v)[rows],
+                               rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# Whole forward over heads
+
+def test_slay_causal_forms_and_positivity(orc):
+    import slay_synth as ss
+
+    w = ss.WORKLOADS["tiny_f32"].with_(L=96, H=2)
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    outs = {f: orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m, form=f, chunk=w.chunk)
+            for f in ("brute", "recurrent", "chunked")}
+    for f in ("recurrent", "chunked"):
+        np.testing.assert_allclose(outs[f][0], outs["brute"][0], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(outs[f][1], outs["brute"][1], rtol=1e-11, atol=1e-12)
+    # features and scores strictly positive (abstract: well-defined nonnegative scores)
+    phq = orc.featmap(q.reshape(-1, w.d), A, G, w.eps, w.R, w.m)
+    phk = orc.featmap(k.reshape(-1, w.d), A, G, w.eps, w.R, w.m)
+    assert phq.min() > 0 and phk.min() > 0
+    assert (phq[:96] @ phk[:96].T).min() > 0
+    # per-head draws: head h uses its own draw slice
+    A2 = np.stack([A, A[::-1]])
+    G2 = np.stack([G, G[::-1]])
+    o2 = orc.slay_causal(q, k, v, A2, G2, w.eps, w.R, w.m, per_head_draws=True)[0]
+    np.testing.assert_allclose(o2[0, 0], outs["recurrent"][0][0, 0], rtol=1e-12)
+    o_h1 = orc.slay_causal(q[:, 1:], k[:, 1:], v[:, 1:], A[::-1], G[::-1], w.eps, w.R, w.m)[0]
+    np.testing.assert_allclose(o2[0, 1], o_h1[0, 0], rtol=1e-12)
+
+
+def test_yat_exact_sanity(orc):
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((1, 30, 8))
+    k = rng.standard_normal((1, 30, 8))
+    v = rng.standard_normal((1, 30, 3))
+    o = orc.yat_exact_causal(q, k, v, EPS)
+    np.testing.assert_allclose(o[0, 0], v[0, 0], rtol=1e-12)
+    lo = np.minimum.accumulate(v[0], axis=0)
+    hi = np.maximum.accumulate(v[0], axis=0)
+    assert np.all(o[0] >= lo - 1e-12) and np.all(o[0] <= hi + 1e-12)
