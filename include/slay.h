@@ -1,0 +1,148 @@
+/*
+ * slay.h -- C ABI of libslay: causal SLAY attention (Spherical Linearized
+ * Attention with Yat kernels) on AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (web pages; cited by title and section):
+ *   - "SLAY: Geometry-Aware Spherical Linearized Attention with Yat-Kernel",
+ *     arXiv 2602.04915, English abstract: queries and keys on the unit
+ *     sphere; the spherical Yat kernel written (Bernstein's theorem) as a
+ *     nonnegative mixture of polynomial x exponential kernels; a strictly
+ *     positive random-feature approximation giving O(L) attention.
+ *   - nubint.ai review of that paper, "Proposed method" (six bullets):
+ *     (1) Yat kernel as a spherical similarity on unit-norm q, k; (2) the
+ *     denominator linearised through its Laplace representation; (3) anchor
+ *     features for the polynomial part, PRF for the exponential part;
+ *     (4) Gauss-Laguerre discretisation of the integral; (5) the two feature
+ *     sets fused by a random tensor sketch; (6) standard causal linear
+ *     attention contraction without the L x L matrix.
+ *
+ * The computation, with u = q.k on unit vectors and eps > 0:
+ *   K(u)    = u^2 / (2 - 2u + eps)                      (spherical Yat kernel)
+ *   K_R(u)  = sum_r alpha_r u^2 exp(beta_r u),  alpha_r = w_r/(2+eps),
+ *             beta_r = 2 x_r/(2+eps), (x_r, w_r) the R-point Gauss-Laguerre rule
+ *   phi(x)[r*m+t] = sqrt(alpha_r/m) (a_rt . xh)^2 exp(sqrt(beta_r) g_rt . xh - beta_r/2),
+ *             xh = x / max(|x|, 1e-12),  F = R*m features
+ *   o_i     = phi(q_i)^T S_i / phi(q_i)^T z_i,
+ *             S_i = S0 + sum_{j<=i} phi(k_j) v_j^T,  z_i = z0 + sum_{j<=i} phi(k_j)
+ * The anchor vectors a_rt and PRF vectors g_rt are drawn by the caller
+ * (i.i.d. N(0, I) for the estimator the pages describe) and passed in.
+ *
+ * Conventions for every call:
+ *   - Device pointers are HIP device memory owned by the caller; the library
+ *     never allocates or frees device memory and keeps no device state.
+ *   - All arrays are dense and row-major with the shapes given; 16-byte
+ *     aligned base pointers are required for q, k, v, x, o, phi and draws.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and is asynchronous; nothing synchronises.  Calls are thread-safe.
+ *   - Argument checking happens on the host before anything is enqueued:
+ *     SLAY_E_INVALID (bad argument; nothing enqueued), SLAY_E_UNSUPPORTED
+ *     (valid but not implemented; nothing enqueued), SLAY_E_DEVICE (a HIP
+ *     launch error; the stream may hold part of the work).  The last error
+ *     message of the calling thread is returned by slay_last_error().
+ */
+#ifndef SLAY_H
+#define SLAY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLAY_OK = 0,
+  SLAY_E_INVALID = 1,
+  SLAY_E_UNSUPPORTED = 2,
+  SLAY_E_DEVICE = 3
+} slay_status_t;
+
+typedef enum { SLAY_F32 = 0, SLAY_BF16 = 1 } slay_dtype_t;
+
+/* Feature-map parameters (review, "Proposed method" bullets 3-5).
+ * anchors, prf: device arrays [n_draw_sets][R*m][d] of draw_dtype; row r*m+t
+ * is the vector of feature t of Gauss-Laguerre node r.  Head h (0-based
+ * index over B*H heads, or over the n_heads of a decode step) uses draw set
+ * h % n_draw_sets; n_draw_sets = 1 shares one draw across all heads.
+ * Limits: d in {32, 64, 128}; 1 <= R <= 16; m a multiple of 16; eps > 0. */
+typedef struct {
+  int32_t d;
+  int32_t R;
+  int32_t m;
+  double eps;
+  const void* anchors;
+  const void* prf;
+  slay_dtype_t draw_dtype;
+  int32_t n_draw_sets;
+  int64_t draw_set_stride; /* elements between consecutive draw sets (>= R*m*d) */
+} slay_params_t;
+
+/* Feature map phi of n_rows rows of x (abstract; review "Proposed method"
+ * bullets 1, 3, 5).
+ *   x   : device [n_rows][d], dtype x_dtype (must equal params->draw_dtype)
+ *   phi : device [n_rows][R*m], dtype phi_dtype (f32 or bf16, RNE rounding)
+ *   rows_per_head: rows belonging to one head, for draw-set selection
+ *                  (row i uses set (i / rows_per_head) % n_draw_sets); must
+ *                  divide n_rows; ignored (may be 0) when n_draw_sets == 1.
+ * Projection on MFMA (fp32 accumulate), features in fp32, then rounded. */
+slay_status_t slay_featmap(const slay_params_t* params, const void* x, slay_dtype_t x_dtype, int64_t n_rows,
+                           int64_t rows_per_head, void* phi, slay_dtype_t phi_dtype, void* stream);
+
+/* Workspace bytes slay_attn_chunked_fwd needs for this shape (0 is possible). */
+size_t slay_attn_chunked_fwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t L,
+                                            int32_t dv, int32_t chunk, slay_dtype_t io_dtype);
+
+/* Causal SLAY forward (review, "Proposed method" bullet 6), chunked:
+ * within a chunk of `chunk` tokens the masked block tril(phi(Q) phi(K)^T)
+ * (diagonal included) is applied to v, the state of all earlier chunks adds
+ * phi(q) S and phi(q) z; no L x L matrix is formed.
+ *   q, k : device [B][H][L][d];  v, o : device [B][H][L][dv];  dtype io_dtype
+ *          (draws must have the same dtype).  bf16: fp32 accumulation,
+ *          outputs rounded to bf16 (RNE).
+ *   S0, z0     : nullable device fp32 initial state [B*H][R*m][dv], [B*H][R*m]
+ *                (NULL = zero state);
+ *   S_out, z_out: nullable device fp32 final state, same shapes; S_out may
+ *                alias S0 and z_out may alias z0 (the state carried in place).
+ *   workspace  : device scratch of at least
+ *                slay_attn_chunked_fwd_workspace_size(...) bytes (NULL if 0).
+ * L need not be a multiple of chunk (the tail chunk is masked); L = 0 only
+ * copies S0/z0 to S_out/z_out.  chunk in [1, 128].
+ * bf16 with d = dv = 64, chunk = 64 and R*m in {64, 96, 128, 256} runs the
+ * fused MFMA kernels; every other accepted shape runs the general kernels. */
+slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                    slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L, int32_t dv,
+                                    int32_t chunk, const float* S0, const float* z0, void* o, float* S_out,
+                                    float* z_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* One O(1)-per-token decode step for n_heads independent heads (the
+ * recurrent form of the same attention): phi(q), phi(k) of the new token,
+ * S += phi(k) v^T, z += phi(k), then o = phi(q)^T S / phi(q)^T z.
+ *   q, k : device [n_heads][d];  v, o : device [n_heads][dv];  dtype io_dtype
+ *   S, z : device fp32 state [n_heads][R*m][dv], [n_heads][R*m], updated in place
+ *   draws: fp32 or bf16 (params->draw_dtype), any io_dtype.
+ * d in {32, 64}, dv in {32, 64}, R*m in {64, 128, 192, 256} run the fused
+ * streaming kernel; other accepted shapes need a workspace and are rejected
+ * here with SLAY_E_UNSUPPORTED. */
+slay_status_t slay_attn_recurrent_step(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                       slay_dtype_t io_dtype, int64_t n_heads, int32_t dv, float* S, float* z,
+                                       void* o, void* stream);
+
+/* Host-only: the R-point Gauss-Laguerre mixture parameters used by the
+ * library, alpha[r] = w_r/(2+eps), beta[r] = 2 x_r/(2+eps) (fp64, R <= 16).
+ * Returns SLAY_OK or SLAY_E_INVALID. */
+slay_status_t slay_gl_table(int32_t R, double eps, double* alpha, double* beta);
+
+/* Static description of a status code. */
+const char* slay_status_string(slay_status_t status);
+
+/* Message of the last failed call on the calling thread ("" if none). */
+const char* slay_last_error(void);
+
+/* ABI version (major * 10000 + minor * 100 + patch). */
+int32_t slay_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLAY_H */

@@ -1,0 +1,265 @@
+// slay_chunked_generic.hip -- the general causal SLAY forward (any dtype and
+// shape the ABI accepts) and the inter-chunk prefix scan of (S, z).
+//
+// Method ("SLAY: Geometry-Aware Spherical Linearized Attention with
+// Yat-Kernel", abstract; nubint.ai review, "Proposed method" bullet 6):
+// o_i = phi(q_i)^T S_i / phi(q_i)^T z_i with S_i = sum_{j<=i} phi(k_j) v_j^T,
+// z_i = sum_{j<=i} phi(k_j), evaluated chunk by chunk without the L x L
+// matrix: a masked C x C block inside each chunk plus the state carried in
+// from the chunks before it.
+//
+// This path is unfused and uses plain fp32 FMA for the contractions:
+//   1. the feature-map kernel writes fp32 phi(q), phi(k) to the workspace;
+//   2. chunk_state: per (head, chunk) dS_c = phi(k_c)^T [v_c | 1];
+//   3. scan: exclusive prefix of dS over chunks (plus S0), total -> S_out;
+//   4. chunk_out: per (head, chunk) masked intra block + phi(q) S_c, divide.
+// It serves fp32 callers (1e-4 parity) and shapes without a fused MFMA
+// variant; the bf16 headline shapes take slay_chunked_fused.hip.
+#include "slay_device.hpp"
+#include "slay_internal.hpp"
+
+namespace slay {
+
+namespace {
+
+constexpr int kGThreads = 256;
+
+__device__ __forceinline__ void scan_map(int64_t idx, int F, int dv, int layout, int& f, int& e) {
+  if (layout == 0) {
+    f = (int)(idx / (dv + 1));
+    e = (int)(idx - (int64_t)f * (dv + 1));
+  } else {
+    const int NE = (dv + 16) / 16;
+    const int i = (int)(idx & 3);
+    const int lane = (int)((idx >> 2) & 63);
+    const int64_t tile = idx >> 8;
+    const int et = (int)(tile % NE);
+    const int fb = (int)(tile / NE);
+    f = fb * 16 + 4 * (lane >> 4) + i;
+    e = et * 16 + (lane & 15);
+  }
+}
+
+// In-place exclusive prefix over items: item i <- init + sum_{i' < i} delta_i'.
+__global__ __launch_bounds__(kGThreads) void scan_kernel(ScanArgs a, int64_t E) {
+  const int64_t h = blockIdx.y;
+  const int64_t idx = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
+  if (idx >= E) return;
+  int f, e;
+  scan_map(idx, a.F, a.dv, a.layout, f, e);
+  float run = 0.f;
+  if (e < a.dv) {
+    if (a.S0) run = a.S0[(h * a.F + f) * a.dv + e];
+  } else if (e == a.dv) {
+    if (a.z0) run = a.z0[h * a.F + f];
+  }
+  float* st = a.states + h * a.n_items * E + idx;
+  for (int64_t it = 0; it < a.n_items; ++it) {
+    const float d = (it < a.n_terms) ? st[it * E] : 0.f;
+    st[it * E] = run;
+    run += d;
+  }
+  if (a.n_terms > a.n_items) run += st[a.n_items * E];  // never: n_terms <= n_items
+  if (e < a.dv) {
+    if (a.S_out) a.S_out[(h * a.F + f) * a.dv + e] = run;
+  } else if (e == a.dv) {
+    if (a.z_out) a.z_out[h * a.F + f] = run;
+  }
+}
+
+// dS_c[f][e] = sum_{j in chunk} phik[j][f] * vx[j][e], with vx = [v | 1].
+// Each thread owns a 4 (f) x 4 (e) block of the (F, dv+1) state.
+template <typename TV>
+__global__ __launch_bounds__(kGThreads) void chunk_state_kernel(const float* __restrict__ phik,
+                                                                const TV* __restrict__ v, int64_t L,
+                                                                int F, int dv, int C, int64_t n_chunks,
+                                                                float* __restrict__ states) {
+  const int64_t h = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int64_t j0 = c * C;
+  const int nj = (int)min<int64_t>(C, L - j0);
+  const int E1 = dv + 1;
+  const int nfb = (F + 3) / 4, neb = (E1 + 3) / 4;
+  const float* pk = phik + (h * L + j0) * F;
+  const TV* vv = v + (h * L + j0) * dv;
+  float* out = states + (h * n_chunks + c) * (int64_t)F * E1;
+  for (int blk = threadIdx.x; blk < nfb * neb; blk += kGThreads) {
+    const int f0 = (blk / neb) * 4, e0 = (blk % neb) * 4;
+    float acc[4][4] = {};
+    for (int j = 0; j < nj; ++j) {
+      float kf[4], ve[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) kf[a] = (f0 + a < F) ? pk[(int64_t)j * F + f0 + a] : 0.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int e = e0 + b;
+        ve[b] = (e < dv) ? Mma<TV>::to_f32(vv[(int64_t)j * dv + e]) : (e == dv ? 1.f : 0.f);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(kf[a], ve[b], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (f0 + a < F && e0 + b < E1) out[(int64_t)(f0 + a) * E1 + e0 + b] = acc[a][b];
+  }
+}
+
+template <typename TV>
+__device__ __forceinline__ void store_out(TV* p, float x);
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, float x) { *p = x; }
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+
+// o_i = (sum_{j<=i in chunk} A_ij v_j + phiq_i S_c) / (sum_j A_ij + phiq_i z_c),
+// A_ij = phiq_i . phik_j.  The masked block A lives in LDS (C <= 128).
+template <typename TV>
+__global__ __launch_bounds__(kGThreads) void chunk_out_kernel(const float* __restrict__ phiq,
+                                                              const float* __restrict__ phik,
+                                                              const TV* __restrict__ v, int64_t L, int F,
+                                                              int dv, int C, int64_t n_chunks,
+                                                              const float* __restrict__ states,
+                                                              TV* __restrict__ o) {
+  extern __shared__ float sA[];  // [C][C]
+  const int64_t h = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int64_t i0 = c * C;
+  const int n = (int)min<int64_t>(C, L - i0);
+  const int E1 = dv + 1;
+  const float* pq = phiq + (h * L + i0) * F;
+  const float* pk = phik + (h * L + i0) * F;
+  const TV* vv = v + (h * L + i0) * dv;
+  const float* S = states + (h * n_chunks + c) * (int64_t)F * E1;
+  for (int p = threadIdx.x; p < n * n; p += kGThreads) {
+    const int i = p / n, j = p - (p / n) * n;
+    float acc = 0.f;
+    if (j <= i)
+      for (int f = 0; f < F; ++f) acc = fmaf(pq[(int64_t)i * F + f], pk[(int64_t)j * F + f], acc);
+    sA[i * C + j] = acc;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < n * dv; p += kGThreads) {
+    const int i = p / dv, e = p - (p / dv) * dv;
+    float num = 0.f, den = 0.f;
+    for (int j = 0; j <= i; ++j) {
+      const float a = sA[i * C + j];
+      num = fmaf(a, Mma<TV>::to_f32(vv[(int64_t)j * dv + e]), num);
+      den += a;
+    }
+    for (int f = 0; f < F; ++f) {
+      const float qf = pq[(int64_t)i * F + f];
+      num = fmaf(qf, S[(int64_t)f * E1 + e], num);
+      den = fmaf(qf, S[(int64_t)f * E1 + dv], den);
+    }
+    store_out<TV>(o + (h * L + i0 + i) * dv + e, num / den);
+  }
+}
+
+template <typename TV>
+hipError_t launch_generic_t(const ChunkedArgs& a, hipStream_t s) {
+  const int64_t nrow = a.n_heads * a.L;
+  const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+  float* phiq = static_cast<float*>(a.ws);
+  float* phik = phiq + nrow * a.F;
+  float* states = phik + nrow * a.F;
+
+  FeatmapArgs fa{};
+  fa.rows_per_head = a.L;
+  fa.n_heads = a.n_heads;
+  fa.d = a.d;
+  fa.F = a.F;
+  fa.m = a.m;
+  fa.x_bf16 = a.io_bf16;
+  fa.anchors = a.anchors;
+  fa.prf = a.prf;
+  fa.draw_set_stride = a.draw_set_stride;
+  fa.n_draw_sets = a.n_draw_sets;
+  fa.nc = a.nc;
+  fa.phi_bf16 = false;
+  fa.x = a.q;
+  fa.phi = phiq;
+  hipError_t e = launch_featmap(fa, s);
+  if (e != hipSuccess) return e;
+  fa.x = a.k;
+  fa.phi = phik;
+  e = launch_featmap(fa, s);
+  if (e != hipSuccess) return e;
+
+  dim3 grid((unsigned)n_chunks, (unsigned)a.n_heads);
+  hipLaunchKernelGGL(chunk_state_kernel<TV>, grid, dim3(kGThreads), 0, s, phik,
+                     static_cast<const TV*>(a.v), a.L, a.F, a.dv, a.chunk, n_chunks, states);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  ScanArgs sa{};
+  sa.states = states;
+  sa.n_heads = a.n_heads;
+  sa.n_items = n_chunks;
+  sa.n_terms = n_chunks;
+  sa.F = a.F;
+  sa.dv = a.dv;
+  sa.layout = 0;
+  sa.S0 = a.S0;
+  sa.z0 = a.z0;
+  sa.S_out = a.S_out;
+  sa.z_out = a.z_out;
+  e = launch_scan(sa, s);
+  if (e != hipSuccess) return e;
+
+  const size_t lds = sizeof(float) * (size_t)a.chunk * a.chunk;
+  hipLaunchKernelGGL(chunk_out_kernel<TV>, grid, dim3(kGThreads), lds, s, phiq, phik,
+                     static_cast<const TV*>(a.v), a.L, a.F, a.dv, a.chunk, n_chunks, states,
+                     static_cast<TV*>(a.o));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t scan_state_elems(int F, int dv, int layout) {
+  return layout == 0 ? (int64_t)F * (dv + 1) : (int64_t)F * (dv + 16);
+}
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
+  const int64_t E = scan_state_elems(a.F, a.dv, a.layout);
+  if (a.n_heads == 0 || E == 0) return hipSuccess;
+  dim3 grid((unsigned)((E + kGThreads - 1) / kGThreads), (unsigned)a.n_heads);
+  hipLaunchKernelGGL(scan_kernel, grid, dim3(kGThreads), 0, s, a, E);
+  return hipGetLastError();
+}
+
+bool generic_supported(const ChunkedArgs& a) {
+  return featmap_supported(a.d) && a.F % 16 == 0 && a.m % 16 == 0 && a.chunk >= 1 && a.chunk <= 128 &&
+         a.dv >= 1 && a.dv <= 1024;
+}
+
+size_t generic_workspace_bytes(const ChunkedArgs& a) {
+  const int64_t nrow = a.n_heads * a.L;
+  const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+  return sizeof(float) * (size_t)(2 * nrow * a.F + a.n_heads * n_chunks * (int64_t)a.F * (a.dv + 1));
+}
+
+hipError_t launch_generic(const ChunkedArgs& a, hipStream_t s) {
+  if (a.n_heads == 0 || a.L == 0) {
+    // no tokens: the final state is the initial one
+    ScanArgs sa{};
+    sa.states = nullptr;
+    sa.n_heads = a.n_heads;
+    sa.n_items = 0;
+    sa.n_terms = 0;
+    sa.F = a.F;
+    sa.dv = a.dv;
+    sa.layout = 0;
+    sa.S0 = a.S0;
+    sa.z0 = a.z0;
+    sa.S_out = a.S_out;
+    sa.z_out = a.z_out;
+    return (a.S_out || a.z_out) ? launch_scan(sa, s) : hipSuccess;
+  }
+  return a.io_bf16 ? launch_generic_t<uint16_t>(a, s) : launch_generic_t<float>(a, s);
+}
+
+}  // namespace slay

@@ -1,0 +1,100 @@
+// slay_device.hpp -- device-side building blocks shared by the SLAY kernels
+// (gfx950 / CDNA4, wave64).
+//
+// MFMA operand layouts used throughout (checked on gfx950 with a one-wave
+// in-bounds probe), lane l, g = l / 16:
+//   v_mfma_f32_16x16x32_bf16  A[l%16][8g+i], B[8g+i][l%16] (i < 8);  C[4g+i][l%16] (i < 4)
+//   v_mfma_f32_16x16x4_f32    A[l%16][g],    B[g][l%16];             C[4g+i][l%16]
+// So a 16x16 C tile gives each lane four consecutive rows of one column.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace slay {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxNodes = 16;
+
+// Per-node constants of the feature map, in fp32, computed on the host from
+// the fp64 Gauss-Laguerre rule:
+//   phi = (y_a * inv)^2 * exp2(y_g * inv * c1[r] + c0[r])
+//   c1 = sqrt(beta_r) * log2(e),  c0 = (-beta_r / 2) * log2(e) + log2(sqrt(alpha_r / m))
+// with y_a = a.x, y_g = g.x and inv = 1 / max(|x|, 1e-12).
+struct NodeConsts {
+  float c1[kMaxNodes];
+  float c0[kMaxNodes];
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite here).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Element type traits for the 16x16 MFMA step: K contraction elements per
+// instruction, KL consecutive k-elements per lane.
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<uint16_t> {  // bf16 stored as raw 16-bit
+  static constexpr int K = 32;
+  static constexpr int KL = 8;
+  typedef bf16x8 frag;
+  __device__ __forceinline__ static frag load(const uint16_t* p) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+  }
+  __device__ __forceinline__ static f32x4 mma(const frag& a, const frag& b, const f32x4& c) {
+    return mfma_bf16(a, b, c);
+  }
+  __device__ __forceinline__ static float to_f32(uint16_t v) { return bf16_to_f32(v); }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int K = 4;
+  static constexpr int KL = 1;
+  typedef float frag;
+  __device__ __forceinline__ static frag load(const float* p) { return *p; }
+  __device__ __forceinline__ static f32x4 mma(const frag& a, const frag& b, const f32x4& c) {
+    return mfma_f32(a, b, c);
+  }
+  __device__ __forceinline__ static float to_f32(float v) { return v; }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace slay

@@ -1,0 +1,206 @@
+// slay_featmap.hip -- the SLAY feature map phi(x) on MFMA (gfx950).
+//
+// Method ("SLAY: Geometry-Aware Spherical Linearized Attention with
+// Yat-Kernel", abstract; nubint.ai review, "Proposed method" bullets 1, 3, 5):
+// rows are projected onto the unit sphere, node r of the Gauss-Laguerre
+// mixture contributes m features, each the product of an anchor feature
+// (a.xh)^2 and a positive random feature exp(sqrt(beta_r) g.xh - beta_r/2),
+// scaled by sqrt(alpha_r/m):  phi[r*m+t] = sqrt(alpha_r/m) (a_rt.xh)^2 prf_rt(xh).
+//
+// Kernel shape: a 256-thread workgroup owns a slice of 64*FBW features for
+// the whole launch and keeps that slice of the projection matrix
+// P = [anchors | prf] in registers as MFMA A-operands (64 VGPRs).  It walks
+// 64-row tiles of x: stages the tile in LDS (padded rows, so the per-lane
+// 16-byte reads are bank-conflict free), computes 1/|x| per row, then per
+// 16-token block runs Y^T = P_slice x^T on 16x16 MFMA tiles and applies the
+// square / exp2 / scale epilogue straight from the accumulators.  The 1/|x|
+// scale is applied to the fp32 accumulator, (x/|x|).P = (x.P)/|x|, so bf16
+// inputs are never rounded twice.
+#include "slay_device.hpp"
+#include "slay_internal.hpp"
+
+namespace slay {
+
+namespace {
+
+constexpr int kTileRows = 64;
+constexpr int kThreads = 256;
+
+template <typename TI>
+struct XStage {
+  static constexpr int kPad = 16 / sizeof(TI);  // one 16-byte slot per row
+};
+
+template <typename TO>
+__device__ __forceinline__ void store4(TO* p, float a, float b, float c, float d);
+
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = pack_bf16x2(a, b);
+  v.y = pack_bf16x2(c, d);
+  *reinterpret_cast<uint2*>(p) = v;
+}
+
+template <typename TI, typename TO, int D, int FBW>
+__global__ __launch_bounds__(kThreads) void featmap_kernel(
+    const TI* __restrict__ x, int64_t rows_per_head, int64_t n_heads, const TI* __restrict__ anchors,
+    const TI* __restrict__ prf, int64_t draw_set_stride, int n_draw_sets, int F, int m, NodeConsts nc,
+    TO* __restrict__ phi) {
+  using M = Mma<TI>;
+  constexpr int KS = D / M::K;               // MFMA k-steps over d
+  constexpr int LDX = D + XStage<TI>::kPad;  // padded LDS row stride (elements)
+  constexpr int VEC = 16 / sizeof(TI);       // elements per 16-byte vector
+  constexpr int VPR = D / VEC;               // 16-byte vectors per row
+  static_assert(D % M::K == 0, "d must be a multiple of the MFMA k-step");
+  static_assert((kTileRows * VPR) % kThreads == 0, "tile staging must divide evenly");
+
+  __shared__ __align__(16) TI sx[kTileRows * LDX];
+  __shared__ float sinv[kTileRows];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int n_fblk = F / 16;
+  const int fblk0 = blockIdx.y * (4 * FBW) + wave * FBW;
+
+  const int64_t tiles_per_head = (rows_per_head + kTileRows - 1) / kTileRows;
+  const int64_t n_tiles = tiles_per_head * n_heads;
+
+  typename M::frag pa[FBW][KS], pg[FBW][KS];
+  int cur_set = -1;
+
+  for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int64_t h = t / tiles_per_head;
+    const int64_t row0 = (t - h * tiles_per_head) * kTileRows;  // row within head
+    const int64_t nrow = min<int64_t>(kTileRows, rows_per_head - row0);
+    const TI* xt = x + (h * rows_per_head + row0) * D;
+    TO* pt = phi + (h * rows_per_head + row0) * (int64_t)F;
+
+    // (re)load this wave's slice of P when the draw set changes
+    const int set = (int)(h % n_draw_sets);
+    if (set != cur_set) {
+      cur_set = set;
+      const TI* a = anchors + (int64_t)set * draw_set_stride;
+      const TI* gg = prf + (int64_t)set * draw_set_stride;
+#pragma unroll
+      for (int j = 0; j < FBW; ++j) {
+        const int fb = min(fblk0 + j, n_fblk - 1);
+        const int64_t rowoff = (int64_t)(fb * 16 + col) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          pa[j][ks] = M::load(a + rowoff + ks * M::K + M::KL * g);
+          pg[j][ks] = M::load(gg + rowoff + ks * M::K + M::KL * g);
+        }
+      }
+    }
+
+    // stage the x tile in LDS and compute 1/max(|x|, 1e-12) per row
+    constexpr int PER_T = kTileRows * VPR / kThreads;
+    constexpr int TPR = kThreads / kTileRows;  // threads per row (4)
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int v = threadIdx.x * PER_T + i;  // vector index in tile (row-major)
+      const int r = v / VPR;
+      const int c = (v - r * VPR) * VEC;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (r < nrow) val = *reinterpret_cast<const uint4*>(xt + (int64_t)r * D + c);
+      *reinterpret_cast<uint4*>(&sx[r * LDX + c]) = val;
+      const TI* e = reinterpret_cast<const TI*>(&val);
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) {
+        const float f = M::to_f32(e[q]);
+        ss += f * f;
+      }
+    }
+    // the PER_T vectors of a thread lie in one row; TPR consecutive threads share a row
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    if ((threadIdx.x % TPR) == 0) sinv[threadIdx.x / TPR] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    __syncthreads();
+
+#pragma unroll
+    for (int tb = 0; tb < kTileRows / 16; ++tb) {
+      f32x4 ya[FBW], yg[FBW];
+#pragma unroll
+      for (int j = 0; j < FBW; ++j) {
+        ya[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        yg[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const typename M::frag b = M::load(&sx[(tb * 16 + col) * LDX + ks * M::K + M::KL * g]);
+#pragma unroll
+        for (int j = 0; j < FBW; ++j) {
+          ya[j] = M::mma(pa[j][ks], b, ya[j]);
+          yg[j] = M::mma(pg[j][ks], b, yg[j]);
+        }
+      }
+      const int r = tb * 16 + col;  // token of this lane's C column
+      const float inv = sinv[r];
+#pragma unroll
+      for (int j = 0; j < FBW; ++j) {
+        const int fb = fblk0 + j;
+        if (fb >= n_fblk) continue;
+        const int node = (fb * 16) / m;
+        const float s1 = inv * nc.c1[node];
+        const float c0 = nc.c0[node];
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = ya[j][i] * inv;
+          o[i] = a * a * fast_exp2(fmaf(yg[j][i], s1, c0));
+        }
+        if (r < nrow) store4<TO>(pt + (int64_t)r * F + fb * 16 + 4 * g, o[0], o[1], o[2], o[3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename TI, typename TO, int D, int FBW>
+hipError_t launch_t(const FeatmapArgs& a, hipStream_t s) {
+  const int FW = 4 * FBW * 16;
+  const int gy = (a.F + FW - 1) / FW;
+  const int64_t tiles = ((a.rows_per_head + kTileRows - 1) / kTileRows) * a.n_heads;
+  int64_t gx = 2048 / gy;
+  if (gx < 1) gx = 1;
+  if (gx > tiles) gx = tiles;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((featmap_kernel<TI, TO, D, FBW>), dim3((unsigned)gx, gy), dim3(kThreads), 0, s,
+                     static_cast<const TI*>(a.x), a.rows_per_head, a.n_heads,
+                     static_cast<const TI*>(a.anchors), static_cast<const TI*>(a.prf), a.draw_set_stride,
+                     a.n_draw_sets, a.F, a.m, a.nc, static_cast<TO*>(a.phi));
+  return hipGetLastError();
+}
+
+template <typename TI, typename TO>
+hipError_t launch_d(const FeatmapArgs& a, hipStream_t s) {
+  constexpr bool bf = sizeof(TI) == 2;
+  switch (a.d) {
+    case 32: return launch_t<TI, TO, 32, 4>(a, s);
+    case 64: return launch_t<TI, TO, 64, bf ? 4 : 2>(a, s);
+    case 128: return launch_t<TI, TO, 128, bf ? 2 : 1>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool featmap_supported(int d) { return d == 32 || d == 64 || d == 128; }
+
+hipError_t launch_featmap(const FeatmapArgs& a, hipStream_t s) {
+  if (a.x_bf16) {
+    return a.phi_bf16 ? launch_d<uint16_t, uint16_t>(a, s) : launch_d<uint16_t, float>(a, s);
+  }
+  return a.phi_bf16 ? launch_d<float, uint16_t>(a, s) : launch_d<float, float>(a, s);
+}
+
+}  // namespace slay

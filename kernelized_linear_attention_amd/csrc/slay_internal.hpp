@@ -1,0 +1,100 @@
+// slay_internal.hpp -- host-side launch interface between the C ABI layer
+// (slay_api.cpp) and the HIP kernels.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "slay_device.hpp"
+
+namespace slay {
+
+struct FeatmapArgs {
+  const void* x;          // [n_heads * rows_per_head][d]
+  int64_t rows_per_head;  // rows sharing one draw set
+  int64_t n_heads;
+  int d, F, m;
+  bool x_bf16;            // x and draws: bf16 if true, else fp32
+  const void* anchors;    // [n_draw_sets][F][d]
+  const void* prf;
+  int64_t draw_set_stride;  // elements between draw sets
+  int n_draw_sets;          // head h uses set h % n_draw_sets
+  NodeConsts nc;
+  void* phi;              // [rows][F]
+  bool phi_bf16;
+};
+
+bool featmap_supported(int d);
+hipError_t launch_featmap(const FeatmapArgs& a, hipStream_t s);
+
+// Causal chunked forward over n_heads = B*H heads.
+struct ChunkedArgs {
+  const void* q;  // [n_heads][L][d]
+  const void* k;
+  const void* v;  // [n_heads][L][dv]
+  bool io_bf16;
+  int64_t n_heads, L;
+  int d, dv, F, m, R, chunk;
+  const void* anchors;
+  const void* prf;
+  int64_t draw_set_stride;
+  int n_draw_sets;
+  NodeConsts nc;
+  const float* S0;  // nullable [n_heads][F][dv]
+  const float* z0;  // nullable [n_heads][F]
+  void* o;          // [n_heads][L][dv]
+  float* S_out;     // nullable
+  float* z_out;     // nullable
+  void* ws;
+  size_t ws_bytes;
+};
+
+// Fused MFMA path (bf16): returns true if the shape has a compiled variant.
+bool fused_supported(const ChunkedArgs& a);
+size_t fused_workspace_bytes(const ChunkedArgs& a);
+hipError_t launch_fused(const ChunkedArgs& a, hipStream_t s);
+
+// Generic path (any supported dtype/shape; unfused, plain FMA).
+bool generic_supported(const ChunkedArgs& a);
+size_t generic_workspace_bytes(const ChunkedArgs& a);
+hipError_t launch_generic(const ChunkedArgs& a, hipStream_t s);
+
+// Prefix scan of per-item states (shared by both paths).
+// layout 0: plain [F][dv+1] (z in column dv); layout 1: MFMA fragment order
+// with dv+16 columns (z in column dv), see slay_chunked_fused.hip.
+struct ScanArgs {
+  float* states;      // [n_heads][n_items][E], in place: item i <- init + sum_{i'<i} item i'
+  int64_t n_heads;
+  int64_t n_items;    // number of prefix entries written
+  int64_t n_terms;    // number of delta items read (n_items or n_items - 1)
+  int F, dv, layout;
+  const float* S0;    // nullable init
+  const float* z0;
+  float* S_out;       // nullable: init + sum of all n_terms items
+  float* z_out;
+};
+int64_t scan_state_elems(int F, int dv, int layout);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+
+// Recurrent decode step.
+struct DecodeArgs {
+  const void* q;  // [n_heads][d]
+  const void* k;
+  const void* v;  // [n_heads][dv]
+  bool io_bf16;
+  int64_t n_heads;
+  int d, dv, F, m;
+  const void* anchors;  // fp32 draws
+  const void* prf;
+  bool draws_bf16;
+  int64_t draw_set_stride;
+  int n_draw_sets;
+  NodeConsts nc;
+  float* S;  // [n_heads][F][dv]
+  float* z;  // [n_heads][F]
+  void* o;   // [n_heads][dv]
+};
+bool decode_supported(const DecodeArgs& a);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace slay

@@ -1,0 +1,168 @@
+"""PyTorch-facing wrappers of the libslay C ABI.
+
+Argument marshalling only: tensors supply device pointers and the current
+HIP stream; every step of the computation runs in the HIP kernels behind
+include/slay.h.  There is no CPU or PyTorch fallback -- if libslay.so is
+missing or the tensors are not on a GPU the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return _lib.SLAY_F32
+    if t == torch.bfloat16:
+        return _lib.SLAY_BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    if not t.is_cuda:
+        raise RuntimeError("libslay works on GPU tensors only")
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None) -> None:
+    if not t.is_cuda:
+        raise RuntimeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+@dataclass
+class FeatureMap:
+    """Anchor and PRF draws plus the Gauss-Laguerre mixture settings.
+
+    anchors, prf: [R*m, d] (one draw for every head) or [n_sets, R*m, d]
+    (head h uses set h % n_sets), float32 or bfloat16, on the GPU.
+    """
+
+    anchors: torch.Tensor
+    prf: torch.Tensor
+    R: int
+    m: int
+    eps: float = 1e-3
+
+    def __post_init__(self):
+        _need(self.anchors, "anchors")
+        _need(self.prf, "prf", tuple(self.anchors.shape), self.anchors.dtype)
+        if self.anchors.shape[-2] != self.R * self.m:
+            raise ValueError("draws must have R*m rows")
+        self.n_sets = 1 if self.anchors.dim() == 2 else int(self.anchors.shape[0])
+        self.d = int(self.anchors.shape[-1])
+        self._c = _lib.SlayParams(self.d, self.R, self.m, float(self.eps), self.anchors.data_ptr(),
+                                  self.prf.data_ptr(), _dtype_code(self.anchors.dtype), self.n_sets,
+                                  self.R * self.m * self.d)
+
+    @property
+    def F(self) -> int:
+        return self.R * self.m
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.anchors.dtype
+
+    def c_params(self):
+        return ctypes.byref(self._c)
+
+
+def gl_table(R: int, eps: float):
+    """The library's mixture parameters (alpha_r, beta_r), fp64 (host only)."""
+    lib = _lib.load()
+    a = (ctypes.c_double * R)()
+    b = (ctypes.c_double * R)()
+    _lib.check(lib.slay_gl_table(R, eps, a, b), "slay_gl_table")
+    return np.array(a[:]), np.array(b[:])
+
+
+def featmap(fm: FeatureMap, x: torch.Tensor, out_dtype: torch.dtype | None = None,
+            rows_per_head: int = 0) -> torch.Tensor:
+    """phi(x) for rows x [..., d]; returns [..., R*m] in out_dtype (default x.dtype)."""
+    lib = _lib.load()
+    _need(x, "x")
+    out_dtype = out_dtype or x.dtype
+    n = x.numel() // fm.d
+    phi = torch.empty(x.shape[:-1] + (fm.F,), dtype=out_dtype, device=x.device)
+    st = lib.slay_featmap(fm.c_params(), x.data_ptr(), _dtype_code(x.dtype), n, rows_per_head, phi.data_ptr(),
+                          _dtype_code(out_dtype), _stream(x))
+    _lib.check(st, "slay_featmap")
+    return phi
+
+
+def chunked_fwd_workspace_size(fm: FeatureMap, B: int, H: int, L: int, dv: int, chunk: int,
+                               dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.slay_attn_chunked_fwd_workspace_size(fm.c_params(), B, H, L, dv, chunk, _dtype_code(dtype)))
+
+
+def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk: int,
+                S0: torch.Tensor | None = None, z0: torch.Tensor | None = None, return_state: bool = False,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, S_out=None, z_out=None):
+    """Causal SLAY forward.  q, k [B, H, L, d]; v [B, H, L, dv] -> o [B, H, L, dv].
+
+    S0, z0: optional fp32 initial state [B*H, F, dv], [B*H, F].  With
+    return_state the final state (S, z) is returned as well.
+    """
+    lib = _lib.load()
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.shape, q.dtype)
+    _need(v, "v", (B, H, L, dv), q.dtype)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    _need(out, "out", (B, H, L, dv), q.dtype)
+    for t, name, shp in ((S0, "S0", (B * H, fm.F, dv)), (z0, "z0", (B * H, fm.F))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
+    if return_state:
+        if S_out is None:
+            S_out = torch.empty((B * H, fm.F, dv), dtype=torch.float32, device=q.device)
+        if z_out is None:
+            z_out = torch.empty((B * H, fm.F), dtype=torch.float32, device=q.device)
+    nbytes = chunked_fwd_workspace_size(fm, B, H, L, dv, chunk, q.dtype)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.slay_attn_chunked_fwd(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype), B,
+                                   H, L, dv, chunk, _ptr(S0), _ptr(z0), out.data_ptr(), _ptr(S_out), _ptr(z_out),
+                                   _ptr(workspace), wsz, _stream(q))
+    _lib.check(st, "slay_attn_chunked_fwd")
+    if return_state:
+        return out, S_out, z_out
+    return out
+
+
+def recurrent_step(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor,
+                   z: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step for n heads: q, k [n, d], v [n, dv]; S [n, F, dv], z [n, F] fp32 in place."""
+    lib = _lib.load()
+    n, d = q.shape
+    dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.shape, q.dtype)
+    _need(v, "v", (n, dv), q.dtype)
+    _need(S, "S", (n, fm.F, dv), torch.float32)
+    _need(z, "z", (n, fm.F), torch.float32)
+    if out is None:
+        out = torch.empty((n, dv), dtype=q.dtype, device=q.device)
+    st = lib.slay_attn_recurrent_step(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype),
+                                      n, dv, S.data_ptr(), z.data_ptr(), out.data_ptr(), _stream(q))
+    _lib.check(st, "slay_attn_recurrent_step")
+    return out

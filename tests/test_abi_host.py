@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function include/slay.h declares, build
+the same Gauss-Laguerre mixture the oracle does, and reject bad arguments on
+the host with a status code and a message before any work is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from numpy.polynomial import laguerre as npl
+
+from kernelized_linear_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_function(lib):
+    hdr = open(os.path.join(ROOT, "include", "slay.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(slay_\w+)\s*\(", hdr, flags=re.M))
+    assert declared == set(_lib.EXPORTS), declared ^ set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.slay_version() == 100
+    assert lib.slay_status_string(0) == b"ok"
+    assert lib.slay_status_string(3) == b"device error"
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 8, 16])
+def test_gl_table_matches_library_rule_and_oracle(lib, orc, R):
+    eps = 1e-3
+    a = (ctypes.c_double * R)()
+    b = (ctypes.c_double * R)()
+    assert lib.slay_gl_table(R, eps, a, b) == 0
+    x, w = npl.laggauss(R)
+    np.testing.assert_allclose(np.array(a[:]) * (2 + eps), w, rtol=1e-12)
+    np.testing.assert_allclose(np.array(b[:]) * (2 + eps) / 2, x, rtol=1e-13)
+    oa, ob = orc.node_params(R, eps)
+    np.testing.assert_allclose(a[:], oa, rtol=1e-12)
+    np.testing.assert_allclose(b[:], ob, rtol=1e-13)
+
+
+def test_gl_table_rejects(lib):
+    a = (ctypes.c_double * 20)()
+    assert lib.slay_gl_table(0, 1e-3, a, a) == _lib.SLAY_E_INVALID
+    assert lib.slay_gl_table(17, 1e-3, a, a) == _lib.SLAY_E_INVALID
+    assert lib.slay_gl_table(2, 0.0, a, a) == _lib.SLAY_E_INVALID
+    assert lib.slay_gl_table(2, 1e-3, None, a) == _lib.SLAY_E_INVALID
+    assert b"R in [1, 16]" in lib.slay_last_error()
+
+
+FAKE = 0x10000  # 16-byte aligned stand-in pointer: every case below fails before any launch
+
+
+def _params(d=64, R=4, m=64, eps=1e-3, dt=_lib.SLAY_BF16, sets=1, stride=0, anchors=FAKE, prf=FAKE):
+    return _lib.SlayParams(d, R, m, eps, anchors, prf, dt, sets, stride)
+
+
+def _fwd(lib, p, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, dt=_lib.SLAY_BF16, B=1, H=16, L=16384, dv=64, chunk=64, S0=None, z0=None,
+                o=FAKE, S_out=None, z_out=None, ws=None, ws_bytes=0)
+    args.update(kw)
+    return lib.slay_attn_chunked_fwd(ctypes.byref(p) if p is not None else None, args["q"], args["k"], args["v"],
+                                     args["dt"], args["B"], args["H"], args["L"], args["dv"], args["chunk"],
+                                     args["S0"], args["z0"], args["o"], args["S_out"], args["z_out"], args["ws"],
+                                     args["ws_bytes"], None)
+
+
+def test_chunked_fwd_validation(lib):
+    E_INV, E_UNS = _lib.SLAY_E_INVALID, _lib.SLAY_E_UNSUPPORTED
+    assert _fwd(lib, None) == E_INV
+    assert _fwd(lib, _params(d=48)) == E_UNS
+    assert _fwd(lib, _params(R=0)) == E_INV
+    assert _fwd(lib, _params(m=24)) == E_UNS
+    assert _fwd(lib, _params(eps=0.0)) == E_INV
+    assert _fwd(lib, _params(eps=float("nan"))) == E_INV
+    assert _fwd(lib, _params(anchors=None)) == E_INV
+    assert _fwd(lib, _params(prf=FAKE + 2)) == E_INV  # misaligned draws
+    assert _fwd(lib, _params(sets=2, stride=10)) == E_INV
+    assert _fwd(lib, _params(), chunk=0) == E_INV
+    assert _fwd(lib, _params(), chunk=129) == E_INV
+    assert _fwd(lib, _params(), L=-1) == E_INV
+    assert _fwd(lib, _params(), dv=0) == E_INV
+    assert _fwd(lib, _params(), dt=_lib.SLAY_F32) == E_UNS  # io dtype must equal the draw dtype
+    assert _fwd(lib, _params(), q=None) == E_INV
+    assert _fwd(lib, _params(), o=FAKE + 4) == E_INV  # misaligned output
+    assert _fwd(lib, _params(), dv=12) == E_UNS  # rows not whole 16-byte vectors
+    assert b"workspace too small" in (lib.slay_last_error() if _fwd(lib, _params()) == E_INV else b"")
+    need = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(_params()), 1, 16, 16384, 64, 64, _lib.SLAY_BF16)
+    assert need > 0
+    assert _fwd(lib, _params(), ws=None, ws_bytes=need) == E_INV  # NULL workspace
+    assert _fwd(lib, _params(), ws=FAKE + 8, ws_bytes=need) == E_INV  # misaligned workspace
+    assert _fwd(lib, _params(), B=2 ** 31 - 1, H=2 ** 31 - 1, L=2 ** 40) == E_INV  # overflow
+
+
+def test_workspace_sizes(lib):
+    p = _params()
+    # fused path: per-segment states, n_seg = 16 segments of 1024 tokens for 16 heads
+    n = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p), 1, 16, 16384, 64, 64, _lib.SLAY_BF16)
+    assert n == 4 * 16 * 16 * 256 * (64 + 16)
+    # many heads: one segment, no workspace
+    assert lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p), 64, 16, 2048, 64, 64, _lib.SLAY_BF16) == 0
+    # general path (fp32): phi(q), phi(k) and per-chunk states
+    p32 = _params(R=2, m=16, dt=_lib.SLAY_F32)
+    n = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p32), 1, 1, 256, 64, 32, _lib.SLAY_F32)
+    assert n == 4 * (2 * 256 * 32 + 8 * 32 * 65)
+    assert lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p), 1, 16, 0, 64, 64, _lib.SLAY_BF16) == 0
+
+
+def test_featmap_and_decode_validation(lib):
+    p = _params()
+    assert lib.slay_featmap(None, FAKE, _lib.SLAY_BF16, 10, 0, FAKE, _lib.SLAY_BF16, None) == _lib.SLAY_E_INVALID
+    assert lib.slay_featmap(ctypes.byref(p), FAKE, _lib.SLAY_F32, 10, 0, FAKE, _lib.SLAY_BF16, None) == \
+        _lib.SLAY_E_UNSUPPORTED
+    assert lib.slay_featmap(ctypes.byref(p), None, _lib.SLAY_BF16, 10, 0, FAKE, _lib.SLAY_BF16, None) == \
+        _lib.SLAY_E_INVALID
+    assert lib.slay_featmap(ctypes.byref(p), FAKE, _lib.SLAY_BF16, -1, 0, FAKE, _lib.SLAY_BF16, None) == \
+        _lib.SLAY_E_INVALID
+    assert lib.slay_featmap(ctypes.byref(p), FAKE, _lib.SLAY_BF16, 0, 0, FAKE, _lib.SLAY_BF16, None) == _lib.SLAY_OK
+    ps = _params(sets=2, stride=4 * 64 * 64)
+    assert lib.slay_featmap(ctypes.byref(ps), FAKE, _lib.SLAY_BF16, 10, 3, FAKE, _lib.SLAY_BF16, None) == \
+        _lib.SLAY_E_INVALID  # rows_per_head must divide n_rows
+    # decode
+    pd = _params(dt=_lib.SLAY_F32)
+    st = lib.slay_attn_recurrent_step(ctypes.byref(pd), FAKE, FAKE, FAKE, _lib.SLAY_F32, 10, 64, None, FAKE, FAKE,
+                                      None)
+    assert st == _lib.SLAY_E_INVALID
+    st = lib.slay_attn_recurrent_step(ctypes.byref(_params(d=128, dt=_lib.SLAY_F32)), FAKE, FAKE, FAKE,
+                                      _lib.SLAY_F32, 10, 64, FAKE, FAKE, FAKE, None)
+    assert st == _lib.SLAY_E_UNSUPPORTED and b"decode shape" in lib.slay_last_error()
+    st = lib.slay_attn_recurrent_step(ctypes.byref(pd), FAKE, FAKE, FAKE, _lib.SLAY_F32, 0, 64, FAKE, FAKE, FAKE,
+                                      None)
+    assert st == _lib.SLAY_OK and lib.slay_last_error() == b""
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Both sides read the same seeded inputs and the same anchor / PRF draws
+(bf16 workloads: the bf16-rounded values, upcast exactly for the oracle).
+Bar: row-normwise max relative error 1e-4 for fp32 inputs, 2e-2 for bf16.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import slay_synth as ss
+from helpers import TOL, elem_rel, rownorm_rel, to_dev, to_np, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from kernelized_linear_attention_amd import ops
+
+    return ops
+
+
+def _fm(ops, w, A, G):
+    return ops.FeatureMap(to_dev(A, w.dtype), to_dev(G, w.dtype), w.R, w.m, w.eps)
+
+
+# ----------------------------------------------------------------------------
+# feature map
+
+@pytest.mark.parametrize("name,out", [("tiny_f32", "f32"), ("b4h8_l2k_bf16", "bf16"), ("b4h8_l2k_bf16", "f32"),
+                                      ("h16_l16k_bf16", "bf16"), ("h8_l128k_d128_bf16", "bf16")])
+def test_featmap_parity(lib, orc, name, out):
+    import torch
+
+    w = ss.WORKLOADS[name].with_(B=1, H=1, L=1000)  # ragged row count (not a multiple of 64)
+    _say(f"featmap parity {name} out={out} rows={w.L}")
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    fm = _fm(lib, w, A, G)
+    x = q.reshape(-1, w.d)
+    phi = lib.featmap(fm, to_dev(x, w.dtype), torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    ref = orc.featmap(x, A, G, w.eps, w.R, w.m)
+    got = to_np(phi)
+    err = rownorm_rel(got, ref)
+    _say(f"  rownorm rel err {err:.3e}, elementwise {elem_rel(got, ref):.3e}")
+    tol = TOL["bf16"] if out == "bf16" else (TOL["f32"] if w.dtype == "f32" else 1e-4)
+    assert err < tol
+    assert np.all(got > 0)  # strictly positive features
+
+
+def test_featmap_per_head_draws(lib, orc):
+    import torch
+
+    w = ss.WORKLOADS["h16_l16k_bf16"].with_(B=1, H=3, L=128)
+    q, _, _ = ss.make_qkv(w)
+    sets = [ss.make_draws(w, seed=[99, s]) for s in range(2)]
+    A = np.stack([s[0] for s in sets])
+    G = np.stack([s[1] for s in sets])
+    fm = _fm(lib, w, A, G)
+    phi = to_np(lib.featmap(fm, to_dev(q.reshape(-1, w.d), w.dtype), torch.float32, rows_per_head=w.L))
+    torch.cuda.synchronize()
+    for h in range(3):
+        ref = orc.featmap(q[0, h], A[h % 2], G[h % 2], w.eps, w.R, w.m)
+        assert rownorm_rel(phi[h * w.L:(h + 1) * w.L], ref) < 1e-4
+
+
+# ----------------------------------------------------------------------------
+# chunked causal forward
+
+def _run_fwd(lib, w, q, k, v, A, G, chunk=None, S0=None, z0=None, state=False):
+    import torch
+
+    fm = _fm(lib, w, A, G)
+    res = lib.chunked_fwd(fm, to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), chunk or w.chunk,
+                          S0=None if S0 is None else torch.from_numpy(np.float32(S0)).cuda(),
+                          z0=None if z0 is None else torch.from_numpy(np.float32(z0)).cuda(), return_state=state)
+    torch.cuda.synchronize()
+    if state:
+        return tuple(to_np(t) for t in res)
+    return to_np(res)
+
+
+@pytest.mark.parametrize("name,L,chunk", [
+    ("tiny_f32", 256, 32),       # the tiny fp32 workload as specified
+    ("tiny_f32", 200, 32),       # ragged tail
+    ("tiny_f32", 256, 1),        # chunk of one token
+    ("tiny_f32", 97, 128),       # one partial chunk
+    ("b4h8_l2k_bf16", 2048, 64),  # fused MFMA path, F = 96
+    ("h16_l16k_bf16", 1000, 64),  # fused MFMA path, F = 256, ragged tail, 1 segment per head
+    ("h16_l16k_bf16", 1000, 32),  # general path in bf16
+])
+def test_chunked_parity(lib, orc, name, L, chunk):
+    w = ss.WORKLOADS[name].with_(L=L, chunk=chunk)
+    if name == "b4h8_l2k_bf16":
+        w = w.with_(B=2, H=4)
+    if name == "h16_l16k_bf16":
+        w = w.with_(H=3)
+    _say(f"chunked parity {name} B={w.B} H={w.H} L={L} chunk={chunk} dtype={w.dtype}")
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    o, S, z = _run_fwd(lib, w, q, k, v, A, G, state=True)
+    ro, rS, rz = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m, form="recurrent")
+    err = rownorm_rel(o, ro)
+    _say(f"  o rownorm rel err {err:.3e} elementwise {elem_rel(o, ro):.3e}; "
+         f"S {rownorm_rel(S, rS):.3e} z {rownorm_rel(z[..., None], rz[..., None]):.3e}")
+    assert err < TOL[w.dtype]
+    assert rownorm_rel(S.reshape(-1, w.dv), rS.reshape(-1, w.dv)) < TOL[w.dtype]
+    assert np.max(np.abs(z - rz) / rz) < TOL[w.dtype]
+    np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], rtol=TOL[w.dtype], atol=TOL[w.dtype])  # o_1 = v_1
+
+
+def test_chunked_initial_state_and_handoff(lib, orc):
+    """Running [0, L1) then [L1, L) with the state carried equals one pass; S_out may alias S0."""
+    import torch
+
+    for name in ("tiny_f32", "h16_l16k_bf16"):
+        w = ss.WORKLOADS[name].with_(H=2, L=640)
+        _say(f"state handoff {name}")
+        q, k, v = ss.make_qkv(w)
+        A, G = ss.make_draws(w)
+        cut = 320 if name != "tiny_f32" else 96
+        o1, S1, z1 = _run_fwd(lib, w, q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], A, G, state=True)
+        o2, S2, z2 = _run_fwd(lib, w, q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], A, G, S0=S1, z0=z1, state=True)
+        ro, rS, rz = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m, form="recurrent")
+        got = np.concatenate([o1, o2], axis=2)
+        assert rownorm_rel(got, ro) < TOL[w.dtype]
+        assert rownorm_rel(S2.reshape(-1, w.dv), rS.reshape(-1, w.dv)) < TOL[w.dtype]
+        # in place: S_out aliases S0
+        fm = _fm(lib, w, A, G)
+        S = torch.from_numpy(np.float32(S1)).cuda()
+        z = torch.from_numpy(np.float32(z1)).cuda()
+        o3 = lib.chunked_fwd(fm, to_dev(q[:, :, cut:], w.dtype), to_dev(k[:, :, cut:], w.dtype),
+                             to_dev(v[:, :, cut:], w.dtype), w.chunk, S0=S, z0=z, S_out=S, z_out=z,
+                             return_state=True)[0]
+        torch.cuda.synchronize()
+        assert rownorm_rel(to_np(o3), ro[:, :, cut:]) < TOL[w.dtype]
+        assert rownorm_rel(to_np(S).reshape(-1, w.dv), rS.reshape(-1, w.dv)) < TOL[w.dtype]
+
+
+def test_chunked_chunk_size_invariance(lib):
+    """Chunk size only changes summation order (fp32 general path)."""
+    w = ss.WORKLOADS["tiny_f32"].with_(L=300)
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    outs = [_run_fwd(lib, w, q, k, v, A, G, chunk=c) for c in (1, 16, 32, 100, 128)]
+    for o in outs[1:]:
+        assert rownorm_rel(o, outs[0]) < 1e-5
+
+
+def test_chunked_edge_cases(lib):
+    import torch
+
+    w = ss.WORKLOADS["h16_l16k_bf16"].with_(H=2, L=64)
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    fm = _fm(lib, w, A, G)
+    # L = 0: only the state passes through
+    S0 = torch.randn(2, w.F, w.dv, device="cuda").abs()
+    z0 = torch.rand(2, w.F, device="cuda") + 0.5
+    e = torch.empty(1, 2, 0, w.d, dtype=torch.bfloat16, device="cuda")
+    ev = torch.empty(1, 2, 0, w.dv, dtype=torch.bfloat16, device="cuda")
+    o, S, z = lib.chunked_fwd(fm, e, e, ev, 64, S0=S0, z0=z0, return_state=True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(S, S0) and torch.equal(z, z0)
+    # B*H = 0
+    e0 = torch.empty(0, 2, 64, w.d, dtype=torch.bfloat16, device="cuda")
+    lib.chunked_fwd(fm, e0, e0, e0, 64)
+    # zero q rows give finite outputs only where the features vanish: the row is 0/0 -> NaN by
+    # the method's definition; a zero key simply contributes nothing
+    k0 = k.copy()
+    k0[:, :, 5] = 0
+    o = _run_fwd(lib, w, q, k0, v, A, G)
+    assert np.all(np.isfinite(o))
+
+
+def test_fused_full_size_h16_l16k(lib, orc):
+    """The headline workload at full size (B1 H16 L16384, F=256, chunk 64) in the bench's launch
+    configuration; two whole heads are checked against the oracle's recurrent form."""
+    w = ss.WORKLOADS["h16_l16k_bf16"]
+    _say("full size h16_l16k_bf16: GPU forward")
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    o, S, z = _run_fwd(lib, w, q, k, v, A, G, state=True)
+    assert np.all(np.isfinite(o))
+    for h in (0, 11):
+        _say(f"  oracle head {h}")
+        ro, rS, rz = orc.slay_causal(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], A, G, w.eps, w.R, w.m)
+        err = rownorm_rel(o[:, h:h + 1], ro)
+        _say(f"  head {h}: o rownorm rel err {err:.3e}; S {rownorm_rel(S[h], rS[0]):.3e}")
+        assert err < TOL["bf16"]
+        assert rownorm_rel(S[h], rS[0]) < TOL["bf16"]
+    # convex hull invariant on all heads
+    lo = np.minimum.accumulate(v, axis=2)
+    hi = np.maximum.accumulate(v, axis=2)
+    slack = 0.02 * (hi - lo) + 1e-2
+    assert np.all(o >= lo - slack) and np.all(o <= hi + slack)
+
+
+def test_full_size_b4h8_l2k(lib, orc):
+    w = ss.WORKLOADS["b4h8_l2k_bf16"]
+    _say("full size b4h8_l2k_bf16")
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    o = _run_fwd(lib, w, q, k, v, A, G)
+    ro = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m)[0]
+    err = rownorm_rel(o, ro)
+    _say(f"  o rownorm rel err {err:.3e}")
+    assert err < TOL["bf16"]
+
+
+def test_full_size_h8_l128k_d128_sampled(lib, orc):
+    """B1 H8 L131072 d=dv=128, F=512, chunk 128 at full size; sampled rows of two heads are
+    checked one by one against the oracle."""
+    w = ss.WORKLOADS["h8_l128k_d128_bf16"]
+    _say("full size h8_l128k_d128_bf16: GPU forward")
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    o = _run_fwd(lib, w, q, k, v, A, G)
+    assert np.all(np.isfinite(o))
+    rows = np.array([0, 1, 127, 128, 129, 4095, 65537, w.L - 1])
+    for h in (0, 7):
+        _say(f"  oracle rows of head {h}")
+        phk = orc.featmap(k[0, h], A, G, w.eps, w.R, w.m)
+        phq = orc.featmap(q[0, h, rows], A, G, w.eps, w.R, w.m)
+        ref = orc.attn_rows(rows, phq, phk, v[0, h])
+        err = rownorm_rel(o[0, h, rows], ref)
+        _say(f"  head {h}: rownorm rel err {err:.3e}")
+        assert err < TOL["bf16"]
+
+
+# ----------------------------------------------------------------------------
+# recurrent decode
+
+def _decode_inputs(w, n_heads, steps):
+    qs, ks, vs = [], [], []
+    for t in range(steps):
+        q, k, v = ss.make_decode_step(w, t, n_heads)
+        qs.append(q)
+        ks.append(k)
+        vs.append(v)
+    return np.stack(qs, 1), np.stack(ks, 1), np.stack(vs, 1)  # [n_heads, steps, d]
+
+
+@pytest.mark.parametrize("n_heads,steps", [(128, 4096), (4096, 3)])
+def test_decode_parity(lib, orc, n_heads, steps):
+    import torch
+
+    w = ss.WORKLOADS["decode_256x16_f32"]
+    _say(f"decode parity heads={n_heads} steps={steps}")
+    A, G = ss.make_draws(w)
+    q, k, v = _decode_inputs(w, n_heads, steps)
+    fm = _fm(lib, w, A, G)
+    S = torch.zeros(n_heads, w.F, w.dv, device="cuda")
+    z = torch.zeros(n_heads, w.F, device="cuda")
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    outs = torch.empty(n_heads, steps, w.dv, device="cuda")
+    for t in range(steps):
+        outs[:, t] = lib.recurrent_step(fm, qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(), S, z)
+    torch.cuda.synchronize()
+    ro, rS, rz = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m, form="recurrent")
+    got = to_np(outs)
+    err = rownorm_rel(got, ro)
+    _say(f"  o rownorm rel err {err:.3e}; S {rownorm_rel(to_np(S).reshape(-1, w.dv), rS.reshape(-1, w.dv)):.3e}")
+    assert err < TOL["f32"]
+    assert rownorm_rel(to_np(S).reshape(-1, w.dv), rS.reshape(-1, w.dv)) < TOL["f32"]
+    assert np.max(np.abs(to_np(z) - rz) / rz) < TOL["f32"]
+    np.testing.assert_allclose(got[:, 0], v[:, 0], rtol=1e-5, atol=1e-5)  # first step from zero state returns v
+
+
+def test_decode_continues_prefill(lib, orc):
+    """Chunked forward exports (S, z); decode steps continuing from it equal the all-recurrent run."""
+    import torch
+
+    w = ss.WORKLOADS["decode_256x16_f32"]
+    wf = ss.WORKLOADS["tiny_f32"].with_(R=4, m=64, H=4, L=100)
+    A, G = ss.make_draws(w)
+    q, k, v = ss.make_qkv(wf)
+    fm = _fm(lib, w, A, G)
+    _, S, z = lib.chunked_fwd(fm, to_dev(q[:, :, :90], "f32"), to_dev(k[:, :, :90], "f32"),
+                              to_dev(v[:, :, :90], "f32"), 32, return_state=True)
+    outs = []
+    for t in range(90, 100):
+        outs.append(to_np(lib.recurrent_step(fm, to_dev(q[0, :, t], "f32"), to_dev(k[0, :, t], "f32"),
+                                             to_dev(v[0, :, t], "f32"), S, z)))
+    torch.cuda.synchronize()
+    ro = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m)[0]
+    got = np.stack(outs, 1)
+    assert rownorm_rel(got, ro[0, :, 90:]) < TOL["f32"]
