@@ -1,0 +1,233 @@
+"""Benchmark of the causal SLAY forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one causal forward (slay_attn_chunked_fwd: feature map fused into
+the chunked contraction, segment states, prefix scan) over B1 H16 L16384,
+d = dv = 64, R = 4 Gauss-Laguerre nodes x m = 64 features (F = 256), chunk
+64, bf16 in / fp32 accumulate / bf16 out, on seeded synthetic inputs already
+resident in HBM.  Prints one JSON line.  Beside the forward it times the
+standalone feature map on the same q and k (HBM-bound) and one recurrent
+decode step for 256 sequences x 16 heads (HBM-bound on the fp32 state), and
+the fp64 CPU oracle on a bounded prefix of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+WORKLOAD = "h16_l16k_bf16"
+DECODE = "decode_256x16_f32"
+KERNEL_SOURCES = ("slay_chunked_fused.hip", "slay_chunked_generic.hip", "slay_featmap.hip", "slay_decode.hip",
+                  "slay_device.hpp")
+
+
+def fwd_flops_per_token_head(w) -> int:
+    """Algorithmic flops of the causal forward per (token, head).
+
+    feature map of q and k: 2 sides x 2 projections (anchor, PRF) x F columns x d x 2 = 8 d F;
+    inter-chunk: phi(q).S and the state update 2 x 2 F dv, phi(q).z and z update 3 F;
+    intra-chunk (causal half of each C x C block): (C+1)(F + dv) + (C+1)/2.
+    """
+    F, d, dv, C = w.F, w.d, w.dv, w.chunk
+    return 8 * d * F + 4 * F * dv + 3 * F + (C + 1) * (F + dv) + (C + 1) // 2
+
+
+def featmap_bytes_per_row(w) -> int:
+    return 2 * w.d + 2 * w.F  # bf16 row in, bf16 features out
+
+
+def decode_bytes_per_head(w) -> int:
+    # fp32 state S (F x dv) and z (F) read and written, q, k, v read and o written (fp32)
+    return 4 * 2 * (w.F * w.dv + w.F) + 4 * (2 * w.d + 2 * w.dv)
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "kernelized_linear_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kind: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"^sources_sha256_16:\s*(\w+)", txt, re.M)
+    m_val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m_src or not m_val or m_src.group(1) != sources_digest():
+        return None
+    return float(m_val.group(1))
+
+
+def event_time_ms(fn, steps: int, stream) -> float:
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, q, k, v, A, G, L_sample: int):
+    import oracle
+
+    oracle.build(force=False)
+    qs, ks, vs = (x[:, :, :L_sample] for x in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.slay_causal(qs, ks, vs, A, G, w.eps, w.R, w.m, form="recurrent")
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": w.B * L_sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 recurrent form, all {w.H} heads x first {L_sample} of {w.L} tokens "
+                      f"({dt:.2f} s wall); per-token cost is independent of L"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per head of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--only", choices=["all", "fwd", "featmap", "decode"], default="all")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import slay_synth as ss
+    from kernelized_linear_attention_amd import ops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    w = ss.WORKLOADS[WORKLOAD]
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+
+    def dev_bf16(a):
+        return torch.from_numpy(a).to(dev).to(torch.bfloat16)
+
+    fm = ops.FeatureMap(dev_bf16(A), dev_bf16(G), w.R, w.m, w.eps)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out = torch.empty_like(vd)
+    ws_bytes = ops.chunked_fwd_workspace_size(fm, w.B, w.H, w.L, w.dv, w.chunk, torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def fwd():
+        ops.chunked_fwd(fm, qd, kd, vd, w.chunk, out=out, workspace=ws)
+
+    result = {}
+    if args.only in ("all", "fwd"):
+        for _ in range(args.warmup):
+            fwd()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ms = event_time_ms(fwd, args.steps, stream)
+        wall = (time.perf_counter() - t0) / args.steps * 1e3
+        flops = fwd_flops_per_token_head(w) * w.B * w.H * w.L
+        achieved = flops / (ms * 1e-3) / 1e12
+        result = {
+            "metric": "SLAY causal fwd tokens/s at L=16k,H=16 on 1 GPU; % bf16 MFMA peak",
+            "value": w.B * w.L / (ms * 1e-3),
+            "unit": "tokens/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": WORKLOAD, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "dv": w.dv, "R": w.R,
+                       "m": w.m, "F": w.F, "chunk": w.chunk, "eps": w.eps, "parallelism": "single GPU"},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_BF16_TFLOPS, "traffic": read_traffic("fused_fwd_h16_l16k_bf16"),
+                         "kernel": "fused causal forward: segment-state pass + prefix scan + main pass, one stream",
+                         "algorithmic_flops_per_launch": flops},
+            "wall_ms_per_step": wall,
+        }
+    also = []
+    if args.only in ("all", "featmap"):
+        phi = torch.empty(w.B, w.H, w.L, w.F, dtype=torch.bfloat16, device=dev)
+
+        def fmap():  # phi(q) then phi(k): two launches on the same stream
+            for x in (qd, kd):
+                ops.featmap(fm, x, torch.bfloat16, out=phi)
+
+        for _ in range(args.warmup):
+            fmap()
+        ms = event_time_ms(fmap, args.steps, stream) / 2  # per launch
+        rows = w.B * w.H * w.L
+        nbytes = rows * featmap_bytes_per_row(w)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        also.append({"name": "featmap_h16_l16k_bf16", "ms_per_launch": ms, "rows_per_launch": rows,
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("featmap_h16_l16k_bf16"),
+                                  "algorithmic_bytes_per_launch": nbytes}})
+    if args.only in ("all", "decode"):
+        wd = ss.WORKLOADS[DECODE]
+        nh = wd.n_heads
+        Ad, Gd = ss.make_draws(wd)
+        fmd = ops.FeatureMap(torch.from_numpy(Ad).to(dev), torch.from_numpy(Gd).to(dev), wd.R, wd.m, wd.eps)
+        n_in = 32
+        steps_in = [ss.make_decode_step(wd, t) for t in range(n_in)]
+        qs = torch.from_numpy(np.stack([s[0] for s in steps_in])).to(dev)
+        ks_ = torch.from_numpy(np.stack([s[1] for s in steps_in])).to(dev)
+        vs = torch.from_numpy(np.stack([s[2] for s in steps_in])).to(dev)
+        S = torch.zeros(nh, wd.F, wd.dv, device=dev)
+        z = torch.zeros(nh, wd.F, device=dev)
+        o = torch.empty(nh, wd.dv, device=dev)
+        it = [0]
+
+        def dstep():
+            t = it[0] % n_in
+            it[0] += 1
+            ops.recurrent_step(fmd, qs[t], ks_[t], vs[t], S, z, out=o)
+
+        for _ in range(args.warmup):
+            dstep()
+        ms = event_time_ms(dstep, args.decode_steps, stream)
+        nbytes = nh * decode_bytes_per_head(wd)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        also.append({"name": "decode_256x16_f32", "ms_per_step": ms, "tokens_per_s": wd.B / (ms * 1e-3),
+                     "heads": nh, "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                               "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                               "traffic": read_traffic("decode_256x16_f32"),
+                                               "algorithmic_bytes_per_launch": nbytes}})
+    if also:
+        result["also"] = also
+    if args.only in ("all", "fwd") and not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, A, G, min(args.cpu_tokens, w.L))
+    result["sources_sha256_16"] = sources_digest()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -92,13 +92,16 @@ def gl_table(R: int, eps: float):
 
 
 def featmap(fm: FeatureMap, x: torch.Tensor, out_dtype: torch.dtype | None = None,
-            rows_per_head: int = 0) -> torch.Tensor:
+            rows_per_head: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
     """phi(x) for rows x [..., d]; returns [..., R*m] in out_dtype (default x.dtype)."""
     lib = _lib.load()
     _need(x, "x")
     out_dtype = out_dtype or x.dtype
     n = x.numel() // fm.d
-    phi = torch.empty(x.shape[:-1] + (fm.F,), dtype=out_dtype, device=x.device)
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (fm.F,), dtype=out_dtype, device=x.device)
+    _need(out, "out", x.shape[:-1] + (fm.F,), out_dtype)
+    phi = out
     st = lib.slay_featmap(fm.c_params(), x.data_ptr(), _dtype_code(x.dtype), n, rows_per_head, phi.data_ptr(),
                           _dtype_code(out_dtype), _stream(x))
     _lib.check(st, "slay_featmap")
