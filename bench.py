@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per head of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--only", choices=["all", "fwd", "featmap", "decode"], default="all")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run 3 plain device copies of this many MiB (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -126,6 +128,13 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = ss.WORKLOADS[WORKLOAD]
     q, k, v = ss.make_qkv(w)
     A, G = ss.make_draws(w)

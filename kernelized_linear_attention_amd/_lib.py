@@ -34,13 +34,22 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load libslay.so; raises if it has not been built (there is no fallback)."""
+    """Load libslay.so; raises if it has not been built (there is no fallback).
+
+    PyTorch-ROCm ships its own HIP runtime.  One process must hold a single
+    HIP runtime, so torch (when installed) is imported first and libslay's
+    libamdhip64 dependency resolves to the runtime torch already loaded.
+    """
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m kernelized_linear_attention_amd.build`")
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER(SlayParams)
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t

@@ -14,7 +14,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/slay.h"
+#include "slay.h"
 #include "slay_internal.hpp"
 
 namespace {

@@ -60,24 +60,32 @@ struct Cfg {
   static constexpr int NE = DVP / 16;      // 16-column tiles of the state
   static constexpr int NFK = F / 32;       // k-steps over features
   static constexpr int NTS = C / 32;       // k-steps over tokens
+  // Rows of v'^T and of the bf16 copy of S'^T kept in LDS: the DV value
+  // rows, row DV (ones / z) and one zero row that stands for rows DV+1..DV+15.
+  static constexpr int VROWS = DV + 2;
   static constexpr int LDX = D + 8;        // padded row strides (elements)
-  static constexpr int LDV = C + 8;
+  static constexpr int LDV = C + 4;        // 34 dwords: 16 lanes x 8 bytes hit 32 distinct banks
   static constexpr int LDF = F + 8;
   static constexpr int NINTER = (NW - NTB) < NTB ? (NW - NTB) : NTB;  // inter tasks on their own wave
   static_assert(C % 32 == 0 && D % 32 == 0 && DV % 16 == 0, "tile sizes");
   static_assert(NW >= NTB, "one intra task per wave at most");
-  // LDS (bytes)
+  // pass 2 LDS (bytes); v'^T is double-buffered
   static constexpr int kQ = 0;
   static constexpr int kK = kQ + C * LDX * 2;
   static constexpr int kV = kK + C * LDX * 2;
-  static constexpr int kPq = kV + DVP * LDV * 2;
+  static constexpr int kVbuf = VROWS * LDV * 2;
+  static constexpr int kPq = kV + 2 * kVbuf;
   static constexpr int kPk = kPq + C * LDF * 2;
   static constexpr int kSt = kPk + C * LDF * 2;
-  static constexpr int kX = kSt + DVP * LDF * 2;
+  static constexpr int kX = kSt + VROWS * LDF * 2;
   static constexpr int kInv = kX + (NINTER > 0 ? NINTER : 1) * NE * 64 * 16;
-  static constexpr int kLds = kInv + 2 * C * 4;
-  static constexpr int kLds1 = kV + DVP * LDV * 2 + 2 * C * 4;  // pass 1 footprint (K and v' only)
+  static constexpr int kLds = kInv + 4 * C * 4;  // inv and log2 scale of q and k rows
   static_assert(kLds <= 160 * 1024, "LDS budget");
+  // pass 1 LDS: k tile, v'^T and row scales, all double-buffered
+  static constexpr int kStage1 = C * LDX * 2 + kVbuf + 2 * C * 4;
+  static constexpr int kLds1 = 2 * kStage1;
+  // pass 1 splits the features over FS1 workgroups of NW / FS1 waves
+  static constexpr int FS1 = 1;
 };
 
 struct Params {
@@ -88,13 +96,15 @@ struct Params {
   int64_t L;
   int64_t seg_len;  // tokens per segment (multiple of C)
   int n_seg;
+  int sub;          // pass-1 sub-segments per segment (seg_len / sub is a multiple of C)
   int m;
   const uint16_t* anchors;
   const uint16_t* prf;
   int64_t draw_set_stride;
   int n_draw_sets;
   NodeConsts nc;
-  float* ws;         // [n_heads][n_seg][F/16][NE][64][4] fragment-ordered states
+  float* ws;         // [n_heads][n_items][F/16][NE][64][4] fragment-ordered states,
+                     // n_items = (n_seg - 1) * sub + 1; item s * sub is the prefix of segment s
   const float* S0;   // used when there is a single segment
   const float* z0;
   float* S_out;
@@ -108,16 +118,50 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   return r;
 }
 
-// Load this wave's slice of P as MFMA operands and its node constants.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 4, 8 or 16), in DPP.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<0xB1>(v);                     // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);                     // quad_perm [2,3,0,1]
+  if (N >= 8) v += dpp<0x141>(v);        // row_half_mirror
+  if (N >= 16) v += dpp<0x140>(v);       // row_mirror
+  return v;
+}
+
+// LDS row that holds state column e = et*16 + col: the value rows, row DV for
+// column DV (z / ones), and the shared zero row for the padding columns.
 template <class K>
-__device__ __forceinline__ void load_p(const Params& p, int set, int wave, int lane, bf16x8 (&pa)[K::FBW][K::NKS],
+__device__ __forceinline__ int vrow(int et, int col) {
+  return et < K::NE - 1 ? et * 16 + col : (col == 0 ? K::DV : K::DV + 1);
+}
+
+// Per-lane LDS element offsets of the rows that hold state-column tile et,
+// for a buffer with row stride LD.
+template <class K, int LD>
+struct RowOff {
+  int off[K::NE];
+  __device__ __forceinline__ explicit RowOff(int col) {
+#pragma unroll
+    for (int et = 0; et < K::NE; ++et) off[et] = vrow<K>(et, col) * LD;
+  }
+};
+
+// Load this wave's slice of P as MFMA operands and its node constants.
+// fb0: first 16-feature block of this wave.
+template <class K>
+__device__ __forceinline__ void load_p(const Params& p, int set, int fb0, int lane, bf16x8 (&pa)[K::FBW][K::NKS],
                                        bf16x8 (&pg)[K::FBW][K::NKS], float (&c1)[K::FBW], float (&c0)[K::FBW]) {
   const int g = lane >> 4, col = lane & 15;
   const uint16_t* a = p.anchors + (int64_t)set * p.draw_set_stride;
   const uint16_t* gg = p.prf + (int64_t)set * p.draw_set_stride;
 #pragma unroll
   for (int j = 0; j < K::FBW; ++j) {
-    const int fb = wave * K::FBW + j;
+    const int fb = fb0 + j;
     const int64_t off = (int64_t)(fb * 16 + col) * K::D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < K::NKS; ++ks) {
@@ -130,18 +174,68 @@ __device__ __forceinline__ void load_p(const Params& p, int set, int wave, int l
   }
 }
 
-// Stage a tile of C rows of x (bf16 [.][D]) into LDS; rows >= n are zero.
-// Writes 1/max(|x|, 1e-12) per row to sinv.
-template <class K>
-__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int n, uint16_t* sx, float* sinv) {
-  constexpr int VPR = K::D / 8;  // 16-byte vectors per row
-  static_assert((K::NT % VPR) == 0, "rows must not straddle threads groups");
-  for (int v = threadIdx.x; v < K::C * VPR; v += K::NT) {
-    const int r = v / VPR, c = (v % VPR) * 8;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < n) val = *reinterpret_cast<const uint4*>(x + (int64_t)r * K::D + c);
-    *reinterpret_cast<uint4*>(sx + r * K::LDX + c) = val;
-    const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+// Chunk inputs in flight: q, k rows as 16-byte vectors, v as 8-byte pieces
+// of two consecutive tokens.  Loaded one chunk ahead into registers and
+// written to LDS one step later.
+template <class K, int NT = K::NT>
+struct Prefetch {
+  static constexpr int XV = (K::C * (K::D / 8) + NT - 1) / NT;          // q/k vectors per thread
+  static constexpr int VV = ((K::C / 2) * (K::DV / 4) + NT - 1) / NT;   // v pieces per thread
+  uint4 q[XV], k[XV];
+  uint2 v0[VV], v1[VV];
+};
+
+template <class K, int NT = K::NT>
+__device__ __forceinline__ void load_x(const uint16_t* __restrict__ x, int n, uint4 (&r)[Prefetch<K, NT>::XV]) {
+  constexpr int VPR = K::D / 8;
+#pragma unroll
+  for (int i = 0; i < Prefetch<K, NT>::XV; ++i) {
+    const int vec = threadIdx.x + i * NT;
+    const int row = vec / VPR, c = (vec % VPR) * 8;
+    r[i] = make_uint4(0, 0, 0, 0);
+    if (vec < K::C * VPR && row < n) r[i] = *reinterpret_cast<const uint4*>(x + (int64_t)row * K::D + c);
+  }
+}
+
+template <class K, int NT = K::NT>
+__device__ __forceinline__ void load_v(const uint16_t* __restrict__ v, int n, uint2 (&r0)[Prefetch<K, NT>::VV],
+                                       uint2 (&r1)[Prefetch<K, NT>::VV]) {
+  constexpr int HP = K::C / 2;  // token pairs
+#pragma unroll
+  for (int i = 0; i < Prefetch<K, NT>::VV; ++i) {
+    const int item = threadIdx.x + i * NT;
+    const int rp = item % HP, e4 = item / HP;
+    r0[i] = make_uint2(0, 0);
+    r1[i] = make_uint2(0, 0);
+    if (item < HP * (K::DV / 4)) {
+      if (2 * rp < n) r0[i] = *reinterpret_cast<const uint2*>(v + (int64_t)(2 * rp) * K::DV + 4 * e4);
+      if (2 * rp + 1 < n) r1[i] = *reinterpret_cast<const uint2*>(v + (int64_t)(2 * rp + 1) * K::DV + 4 * e4);
+    }
+  }
+}
+
+template <class K, int NT = K::NT>
+__device__ __forceinline__ void issue_loads(const Params& p, int64_t head, int64_t c0t, int n, bool want_q,
+                                            Prefetch<K, NT>& pf) {
+  if (want_q) load_x<K, NT>(p.q + (head * p.L + c0t) * K::D, n, pf.q);
+  load_x<K, NT>(p.k + (head * p.L + c0t) * K::D, n, pf.k);
+  load_v<K, NT>(p.v + (head * p.L + c0t) * K::DV, n, pf.v0, pf.v1);
+}
+
+// Write staged q or k vectors to LDS (padded rows) with, per row,
+// inv = 1/max(|x|, 1e-12) and lg = log2(inv^2).
+template <class K, int NT = K::NT>
+__device__ __forceinline__ void store_x(const uint4 (&r)[Prefetch<K, NT>::XV], uint16_t* sx, float* sinv,
+                                        float* slg) {
+  constexpr int VPR = K::D / 8;  // 16-byte vectors per row, consecutive threads
+  static_assert((NT % VPR) == 0 && (VPR == 4 || VPR == 8 || VPR == 16), "rows must not straddle lane groups");
+#pragma unroll
+  for (int i = 0; i < Prefetch<K, NT>::XV; ++i) {
+    const int vec = threadIdx.x + i * NT;
+    if (vec >= K::C * VPR) break;  // uniform over whole waves
+    const int row = vec / VPR, c = (vec % VPR) * 8;
+    *reinterpret_cast<uint4*>(sx + row * K::LDX + c) = r[i];
+    const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -149,57 +243,63 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int n, u
       ss = fmaf(lo, lo, ss);
       ss = fmaf(hi, hi, ss);
     }
-#pragma unroll
-    for (int o = 1; o < VPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
-    if ((v % VPR) == 0) sinv[r] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
-  }
-}
-
-// Stage v (bf16 [.][DV]) transposed into v'^T rows 0..DV-1; tokens >= n are zero.
-template <class K>
-__device__ __forceinline__ void stage_v(const uint16_t* __restrict__ v, int n, uint16_t* sv) {
-  constexpr int VPR = K::DV / 8;
-  for (int t = threadIdx.x; t < K::C * VPR; t += K::NT) {
-    const int r = t / VPR, c = (t % VPR) * 8;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < n) val = *reinterpret_cast<const uint4*>(v + (int64_t)r * K::DV + c);
-    const uint32_t w[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      sv[(c + 2 * q) * K::LDV + r] = (uint16_t)(w[q] & 0xFFFF);
-      sv[(c + 2 * q + 1) * K::LDV + r] = (uint16_t)(w[q] >> 16);
+    ss = group_sum<VPR>(ss);
+    if ((vec % VPR) == 0) {
+      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+      sinv[row] = inv;
+      slg[row] = 2.0f * __builtin_amdgcn_logf(inv);  // v_log_f32 is log2
     }
   }
 }
 
-// Constant rows of v'^T: row DV is all ones (the z column), rows DV+1.. zero.
-template <class K>
-__device__ __forceinline__ void init_vones(uint16_t* sv) {
-  for (int t = threadIdx.x; t < 16 * K::LDV; t += K::NT) {
-    const int r = t / K::LDV;
-    sv[(K::DV + r) * K::LDV + (t % K::LDV)] = (r == 0) ? kBf16One : (uint16_t)0;
+// Write staged v transposed into v'^T rows 0..DV-1: each thread packs the
+// same 4 columns of two consecutive tokens into four 32-bit words.
+template <class K, int NT = K::NT>
+__device__ __forceinline__ void store_v(const uint2 (&r0)[Prefetch<K, NT>::VV],
+                                        const uint2 (&r1)[Prefetch<K, NT>::VV], uint16_t* sv) {
+  constexpr int HP = K::C / 2;
+#pragma unroll
+  for (int i = 0; i < Prefetch<K, NT>::VV; ++i) {
+    const int item = threadIdx.x + i * NT;
+    if (item >= HP * (K::DV / 4)) break;
+    const int rp = item % HP, e4 = item / HP;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(sv + (4 * e4) * K::LDV + 2 * rp);
+    dst[0] = lo16_pair(r0[i].x, r1[i].x);
+    dst[K::LDV / 2] = hi16_pair(r0[i].x, r1[i].x);
+    dst[K::LDV] = lo16_pair(r0[i].y, r1[i].y);
+    dst[3 * K::LDV / 2] = hi16_pair(r0[i].y, r1[i].y);
   }
+}
+
+// Constant rows of a v'^T buffer: row DV all ones (the z column), row DV+1 zero.
+template <class K, int NT = K::NT>
+__device__ __forceinline__ void init_vconst(uint16_t* sv) {
+  for (int t = threadIdx.x; t < 2 * K::LDV; t += NT)
+    sv[K::DV * K::LDV + t] = (t < K::LDV) ? kBf16One : (uint16_t)0;
 }
 
 // v' operand for a token k-step s and state column tile et: lane (e = et*16+col,
 // group g) gets tokens 32s+4g..+3 and 32s+16+4g..+3 (the shared permutation).
 template <class K>
-__device__ __forceinline__ bf16x8 vfrag(const uint16_t* sv, int et, int s, int lane) {
-  const int g = lane >> 4, col = lane & 15;
-  const uint16_t* row = sv + (et * 16 + col) * K::LDV + 32 * s + 4 * g;
+__device__ __forceinline__ bf16x8 vfrag(const uint16_t* sv, const RowOff<K, K::LDV>& vo, int et, int s, int lane) {
+  const int g = lane >> 4;
+  const uint16_t* row = sv + vo.off[et] + 32 * s + 4 * g;
   const uint2 lo = *reinterpret_cast<const uint2*>(row);
   const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// phi(k) of the staged chunk for this wave's features (tokens as M).  Returns
-// the bf16 A-operands of the state update in kf[j][s]; if PHI_LDS, also
-// stores phi(k)[j][f] into LDS.
+// phi = (y_a inv)^2 exp2(y_g inv c1 + c0) = y_a^2 exp2(y_g (inv c1) + (c0 + log2 inv^2)).
+// With tokens as M each lane holds 4 tokens of one feature; s1 = inv c1 and
+// c0' = c0 + log2 inv^2 are formed per token and node.
+// The wave's FBW feature blocks belong to one Gauss-Laguerre node (the
+// dispatcher requires m % (16 FBW) == 0), so s1 and c0' are formed once per
+// token and block of 16 tokens.
 template <class K, bool PHI_LDS>
-__device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, uint16_t* spk, int wave, int lane,
-                                        const bf16x8 (&pa)[K::FBW][K::NKS], const bf16x8 (&pg)[K::FBW][K::NKS],
-                                        const float (&c1)[K::FBW], const float (&c0)[K::FBW],
-                                        bf16x8 (&kf)[K::FBW][K::NTS]) {
+__device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, const float* slg, uint16_t* spk,
+                                        int fb0, int lane, const bf16x8 (&pa)[K::FBW][K::NKS],
+                                        const bf16x8 (&pg)[K::FBW][K::NKS], const float (&c1)[K::FBW],
+                                        const float (&c0)[K::FBW], bf16x8 (&kf)[K::FBW][K::NTS]) {
   const int g = lane >> 4, col = lane & 15;
 #pragma unroll
   for (int tb = 0; tb < K::NTB; ++tb) {
@@ -208,7 +308,9 @@ __device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, u
     for (int ks = 0; ks < K::NKS; ++ks)
       xa[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sx + (tb * 16 + col) * K::LDX + ks * 32 + 8 * g));
     const float4 inv4 = *reinterpret_cast<const float4*>(sinv + tb * 16 + 4 * g);
-    const float inv[4] = {inv4.x, inv4.y, inv4.z, inv4.w};
+    const float4 lg4 = *reinterpret_cast<const float4*>(slg + tb * 16 + 4 * g);
+    const float s1[4] = {inv4.x * c1[0], inv4.y * c1[0], inv4.z * c1[0], inv4.w * c1[0]};
+    const float c0p[4] = {c0[0] + lg4.x, c0[0] + lg4.y, c0[0] + lg4.z, c0[0] + lg4.w};
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j) {
       f32x4 ya = {0.f, 0.f, 0.f, 0.f}, yg = {0.f, 0.f, 0.f, 0.f};
@@ -219,10 +321,7 @@ __device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, u
       }
       float ph[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = ya[i] * inv[i];
-        ph[i] = a * a * fast_exp2(fmaf(yg[i], inv[i] * c1[j], c0[j]));
-      }
+      for (int i = 0; i < 4; ++i) ph[i] = ya[i] * ya[i] * fast_exp2(fmaf(yg[i], s1[i], c0p[i]));
       const uint2 pk = pack4(ph[0], ph[1], ph[2], ph[3]);
       // kf[j][s] = (tokens 32s+4g..+3 | 32s+16+4g..+3)
       uint4 cur = __builtin_bit_cast(uint4, kf[j][tb >> 1]);
@@ -235,12 +334,19 @@ __device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, u
       }
       kf[j][tb >> 1] = as_bf16x8(cur);
       if (PHI_LDS) {
-        const int f = (wave * K::FBW + j) * 16 + col;
-        uint16_t* dst = spk + (tb * 16 + 4 * g) * K::LDF + f;
-        dst[0] = (uint16_t)(pk.x & 0xFFFF);
-        dst[K::LDF] = (uint16_t)(pk.x >> 16);
-        dst[2 * K::LDF] = (uint16_t)(pk.y & 0xFFFF);
-        dst[3 * K::LDF] = (uint16_t)(pk.y >> 16);
+        // lanes col, col^1 hold features f, f+1 of tokens t..t+3: the even lane
+        // writes the (f, f+1) words of tokens t, t+1, the odd lane those of
+        // t+2, t+3.  Bytes 0-3 of the v_perm source are this lane's word,
+        // 4-7 the neighbour's; the selector puts feature f in the low half.
+        const bool odd = col & 1;
+        const uint32_t mine = odd ? pk.y : pk.x;
+        const uint32_t recv = swap_lane_pair(odd ? pk.x : pk.y);
+        const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;
+        const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;
+        const int f = (fb0 + j) * 16 + (col & ~1);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(spk + (tb * 16 + 4 * g + (odd ? 2 : 0)) * K::LDF + f);
+        dst[0] = __builtin_amdgcn_perm(recv, mine, sel0);
+        dst[K::LDF / 2] = __builtin_amdgcn_perm(recv, mine, sel1);
       }
     }
   }
@@ -248,9 +354,10 @@ __device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, u
 
 // phi(q) of the staged chunk for this wave's features (features as M), to LDS phi(q)[i][f].
 template <class K>
-__device__ __forceinline__ void phase_q(const uint16_t* sx, const float* sinv, uint16_t* spq, int wave, int lane,
-                                        const bf16x8 (&pa)[K::FBW][K::NKS], const bf16x8 (&pg)[K::FBW][K::NKS],
-                                        const float (&c1)[K::FBW], const float (&c0)[K::FBW]) {
+__device__ __forceinline__ void phase_q(const uint16_t* sx, const float* sinv, const float* slg, uint16_t* spq,
+                                        int wave, int lane, const bf16x8 (&pa)[K::FBW][K::NKS],
+                                        const bf16x8 (&pg)[K::FBW][K::NKS], const float (&c1)[K::FBW],
+                                        const float (&c0)[K::FBW]) {
   const int g = lane >> 4, col = lane & 15;
 #pragma unroll
   for (int tb = 0; tb < K::NTB; ++tb) {
@@ -258,7 +365,7 @@ __device__ __forceinline__ void phase_q(const uint16_t* sx, const float* sinv, u
 #pragma unroll
     for (int ks = 0; ks < K::NKS; ++ks)
       xb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sx + (tb * 16 + col) * K::LDX + ks * 32 + 8 * g));
-    const float inv = sinv[tb * 16 + col];
+    const float inv = sinv[tb * 16 + col], lg = slg[tb * 16 + col];
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j) {
       f32x4 ya = {0.f, 0.f, 0.f, 0.f}, yg = {0.f, 0.f, 0.f, 0.f};
@@ -267,13 +374,10 @@ __device__ __forceinline__ void phase_q(const uint16_t* sx, const float* sinv, u
         ya = mfma_bf16(pa[j][ks], xb[ks], ya);
         yg = mfma_bf16(pg[j][ks], xb[ks], yg);
       }
-      const float s1 = inv * c1[j];
+      const float s1 = inv * c1[j], c0p = c0[j] + lg;
       float ph[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = ya[i] * inv;
-        ph[i] = a * a * fast_exp2(fmaf(yg[i], s1, c0[j]));
-      }
+      for (int i = 0; i < 4; ++i) ph[i] = ya[i] * ya[i] * fast_exp2(fmaf(yg[i], s1, c0p));
       const int f0 = (wave * K::FBW + j) * 16 + 4 * g;
       *reinterpret_cast<uint2*>(spq + (tb * 16 + col) * K::LDF + f0) = pack4(ph[0], ph[1], ph[2], ph[3]);
     }
@@ -282,28 +386,30 @@ __device__ __forceinline__ void phase_q(const uint16_t* sx, const float* sinv, u
 
 // State update S'[own features] += phi(k)^T v' (tokens contracted).
 template <class K>
-__device__ __forceinline__ void state_update(const uint16_t* sv, int lane, const bf16x8 (&kf)[K::FBW][K::NTS],
-                                             f32x4 (&st)[K::FBW][K::NE]) {
+__device__ __forceinline__ void state_update(const uint16_t* sv, const RowOff<K, K::LDV>& vo, int lane,
+                                             const bf16x8 (&kf)[K::FBW][K::NTS], f32x4 (&st)[K::FBW][K::NE]) {
 #pragma unroll
   for (int s = 0; s < K::NTS; ++s)
 #pragma unroll
     for (int et = 0; et < K::NE; ++et) {
-      const bf16x8 vb = vfrag<K>(sv, et, s, lane);
+      const bf16x8 vb = vfrag<K>(sv, vo, et, s, lane);
 #pragma unroll
       for (int j = 0; j < K::FBW; ++j) st[j][et] = mfma_bf16(kf[j][s], vb, st[j][et]);
     }
 }
 
-// Write this wave's S' slice as bf16 rows of S'^T in LDS.
+// Write this wave's S' slice as bf16 rows of S'^T in LDS (value rows and the z row).
 template <class K>
-__device__ __forceinline__ void write_st(uint16_t* sst, int wave, int lane, const f32x4 (&st)[K::FBW][K::NE]) {
+__device__ __forceinline__ void write_st(uint16_t* sst, const RowOff<K, K::LDF>& so, int wave, int lane,
+                                         const f32x4 (&st)[K::FBW][K::NE]) {
   const int g = lane >> 4, col = lane & 15;
 #pragma unroll
   for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
     for (int et = 0; et < K::NE; ++et) {
+      if (et == K::NE - 1 && col != 0) continue;  // padding columns are not stored
       const int f0 = (wave * K::FBW + j) * 16 + 4 * g;
-      *reinterpret_cast<uint2*>(sst + (et * 16 + col) * K::LDF + f0) =
+      *reinterpret_cast<uint2*>(sst + so.off[et] + f0) =
           pack4(st[j][et][0], st[j][et][1], st[j][et][2], st[j][et][3]);
     }
 }
@@ -314,62 +420,156 @@ __device__ __forceinline__ int64_t frag_off(int fb, int et, int lane) {
   return ((int64_t)(fb * K::NE + et) * 64 + lane) * 4;
 }
 
-// ---------------------------------------------------------------------------
+// intra(IB): A^T = phi(k) phi(q)^T on the causal 16x16 blocks (jb, IB),
+// jb <= IB, masked on the diagonal, rounded to bf16 and used in registers as
+// the B-operand of num'^T += v'^T A^T.
+template <class K, int IB>
+__device__ __forceinline__ void intra_task(const uint16_t* sPq, const uint16_t* sPk, const uint16_t* sVc,
+                                           const RowOff<K, K::LDV>& vo, int lane, f32x4 (&acc)[K::NE]) {
+  if constexpr (IB < K::NTB) {
+    const int g = lane >> 4, col = lane & 15;
+    f32x4 at[IB + 1];
+#pragma unroll
+    for (int jb = 0; jb <= IB; ++jb) at[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
+      const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(sPq + (IB * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
+#pragma unroll
+      for (int jb = 0; jb <= IB; ++jb) {
+        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(sPk + (jb * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
+        at[jb] = mfma_bf16(ak, bq, at[jb]);
+      }
+    }
+    // causal mask on the diagonal block: keep j <= i (row 4g+i, column col)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g + i > col) at[IB][i] = 0.f;
+#pragma unroll
+    for (int s = 0; 2 * s <= IB; ++s) {
+      const uint2 lo = pack4(at[2 * s][0], at[2 * s][1], at[2 * s][2], at[2 * s][3]);
+      uint2 hi = make_uint2(0, 0);
+      if constexpr (true) {
+        if (2 * s + 1 <= IB)
+          hi = pack4(at[(2 * s + 1) % (IB + 1)][0], at[(2 * s + 1) % (IB + 1)][1], at[(2 * s + 1) % (IB + 1)][2],
+                     at[(2 * s + 1) % (IB + 1)][3]);
+      }
+      const bf16x8 ab = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int et = 0; et < K::NE; ++et) acc[et] = mfma_bf16(vfrag<K>(sVc, vo, et, s, lane), ab, acc[et]);
+    }
+  }
+}
+
+// inter(ib): num'^T += S'^T phi(q)^T from the bf16 copy of S'^T in LDS.
 template <class K>
-__global__ __launch_bounds__(K::NT) void pass1_kernel(Params p) {
+__device__ __forceinline__ void inter_task(const uint16_t* sPq, const uint16_t* sSt, const RowOff<K, K::LDF>& so,
+                                           int ib, int lane, f32x4 (&acc)[K::NE]) {
+  const int g = lane >> 4, col = lane & 15;
+  const uint16_t* q0 = sPq + (ib * 16 + col) * K::LDF + 8 * g;
+#pragma unroll
+  for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
+    const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(q0 + kf_ * 32));
+#pragma unroll
+    for (int et = 0; et < K::NE; ++et) {
+      const bf16x8 as = as_bf16x8(*reinterpret_cast<const uint4*>(sSt + so.off[et] + kf_ * 32 + 8 * g));
+      acc[et] = mfma_bf16(as, bq, acc[et]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pass 1: per-segment state deltas.  The state of a feature depends only on
+// that feature, so the F features are split over FS workgroups of NW/FS
+// waves each (more, smaller workgroups hide latency better); every one of
+// them stages the whole chunk.  One barrier per chunk: the k tile and v'^T
+// are double-buffered, so staging chunk c+1 runs beside phi(k) and the state
+// update of chunk c.
+template <class K, int FS>
+__global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
+  constexpr int NT1 = K::NT / FS;
   extern __shared__ __align__(16) unsigned char lds[];
-  uint16_t* sK = reinterpret_cast<uint16_t*>(lds + K::kK - K::kK);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(lds + K::C * K::LDX * 2);
-  float* sinv = reinterpret_cast<float*>(lds + K::C * K::LDX * 2 + K::DVP * K::LDV * 2);
+  auto sK = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * K::kStage1); };
+  auto sV = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * K::kStage1 + K::C * K::LDX * 2); };
+  auto sInv = [&](int b) {
+    return reinterpret_cast<float*>(lds + b * K::kStage1 + K::C * K::LDX * 2 + K::kVbuf);
+  };
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nseg1 = p.n_seg - 1;
-  const int64_t head = blockIdx.x / nseg1;
-  const int seg = (int)(blockIdx.x - head * nseg1);
+  const int nsub = (p.n_seg - 1) * p.sub;  // sub-segments covered by pass 1
+  const int n_items = nsub + 1;
+  const int fs = (int)(blockIdx.x % FS);
+  const int64_t hs = blockIdx.x / FS;
+  const int64_t head = hs / nsub;
+  const int seg = (int)(hs - head * nsub);  // sub-segment index
   const int set = (int)(head % p.n_draw_sets);
+  const int fb0 = (fs * (K::NW / FS) + wave) * K::FBW;
 
   bf16x8 pa[K::FBW][K::NKS], pg[K::FBW][K::NKS];
   float c1[K::FBW], c0[K::FBW];
-  load_p<K>(p, set, wave, lane, pa, pg, c1, c0);
+  load_p<K>(p, set, fb0, lane, pa, pg, c1, c0);
   f32x4 st[K::FBW][K::NE];
 #pragma unroll
   for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
     for (int et = 0; et < K::NE; ++et) st[j][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 kf[K::FBW][K::NTS];
-  init_vones<K>(sV);
+  bf16x8 kf[K::FBW][K::NTS] = {};
+  const RowOff<K, K::LDV> vo(lane & 15);
+  init_vconst<K, NT1>(sV(0));
+  init_vconst<K, NT1>(sV(1));
 
-  const int64_t t0 = (int64_t)seg * p.seg_len;
-  const int64_t t1 = min<int64_t>(p.L, t0 + p.seg_len);
-  for (int64_t c0t = t0; c0t < t1; c0t += K::C) {
-    const int n = (int)min<int64_t>(K::C, t1 - c0t);
+  const int64_t sub_len = p.seg_len / p.sub;
+  const int64_t t0 = (int64_t)seg * sub_len;
+  const int64_t t1 = min<int64_t>(p.L, t0 + sub_len);
+  const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
+  Prefetch<K, NT1> pf;
+  issue_loads<K, NT1>(p, head, t0, (int)min<int64_t>(K::C, t1 - t0), false, pf);
+  store_x<K, NT1>(pf.k, sK(0), sInv(0), sInv(0) + K::C);
+  store_v<K, NT1>(pf.v0, pf.v1, sV(0));
+  if (nch > 1) issue_loads<K, NT1>(p, head, t0 + K::C, (int)min<int64_t>(K::C, t1 - t0 - K::C), false, pf);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nch) {
+      store_x<K, NT1>(pf.k, sK(b ^ 1), sInv(b ^ 1), sInv(b ^ 1) + K::C);
+      store_v<K, NT1>(pf.v0, pf.v1, sV(b ^ 1));
+      const int64_t c2 = t0 + (int64_t)(c + 2) * K::C;
+      if (c + 2 < nch) issue_loads<K, NT1>(p, head, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
+    }
+    phase_k<K, false>(sK(b), sInv(b), sInv(b) + K::C, nullptr, fb0, lane, pa, pg, c1, c0, kf);
+    state_update<K>(sV(b), vo, lane, kf, st);
     __syncthreads();
-    stage_x<K>(p.k + (head * p.L + c0t) * K::D, n, sK, sinv);
-    stage_v<K>(p.v + (head * p.L + c0t) * K::DV, n, sV);
-    __syncthreads();
-    phase_k<K, false>(sK, sinv, nullptr, wave, lane, pa, pg, c1, c0, kf);
-    state_update<K>(sV, lane, kf, st);
   }
-  float* out = p.ws + (head * p.n_seg + seg) * (int64_t)K::F * K::DVP;
+  float* out = p.ws + (head * n_items + seg) * (int64_t)K::F * K::DVP;
 #pragma unroll
   for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
     for (int et = 0; et < K::NE; ++et)
-      *reinterpret_cast<f32x4*>(out + frag_off<K>(wave * K::FBW + j, et, lane)) = st[j][et];
+      *reinterpret_cast<f32x4*>(out + frag_off<K>(fb0 + j, et, lane)) = st[j][et];
 }
 
+// ---------------------------------------------------------------------------
+// pass 2: the segment's chunks in order, state on chip.  Two barriers per
+// chunk c:
+//   [X] before: B1(c) -- intra / inter contractions -- beside the staging of
+//       chunk c+1 (q, k tiles, v'^T into the other buffer, loads of c+2);
+//   [Y] before: B2(c) -- output of c, state update with phi(k) of c, refresh
+//       of the S'^T copy -- beside phase A(c+1): phi(k), phi(q) of chunk c+1.
+// B2 is MFMA work and phase A mostly VALU work, placed in one block so the
+// compiler can interleave them.
 template <class K>
 __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char lds[];
   uint16_t* sQ = reinterpret_cast<uint16_t*>(lds + K::kQ);
   uint16_t* sK = reinterpret_cast<uint16_t*>(lds + K::kK);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(lds + K::kV);
+  auto sV = [&](int b) { return reinterpret_cast<uint16_t*>(lds + K::kV + b * K::kVbuf); };
   uint16_t* sPq = reinterpret_cast<uint16_t*>(lds + K::kPq);
   uint16_t* sPk = reinterpret_cast<uint16_t*>(lds + K::kPk);
   uint16_t* sSt = reinterpret_cast<uint16_t*>(lds + K::kSt);
   f32x4* sX = reinterpret_cast<f32x4*>(lds + K::kX);
   float* sinvq = reinterpret_cast<float*>(lds + K::kInv);
-  float* sinvk = sinvq + K::C;
+  float* slgq = sinvq + K::C;
+  float* sinvk = slgq + K::C;
+  float* slgk = sinvk + K::C;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -379,12 +579,13 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
 
   bf16x8 pa[K::FBW][K::NKS], pg[K::FBW][K::NKS];
   float c1[K::FBW], c0[K::FBW];
-  load_p<K>(p, set, wave, lane, pa, pg, c1, c0);
+  load_p<K>(p, set, wave * K::FBW, lane, pa, pg, c1, c0);
 
   // initial state of the segment
   f32x4 st[K::FBW][K::NE];
   if (p.n_seg > 1) {
-    const float* in = p.ws + (head * p.n_seg + seg) * (int64_t)K::F * K::DVP;
+    const int64_t n_items = (int64_t)(p.n_seg - 1) * p.sub + 1;
+    const float* in = p.ws + (head * n_items + (int64_t)seg * p.sub) * (int64_t)K::F * K::DVP;
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
@@ -409,10 +610,16 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
         }
       }
   }
-  init_vones<K>(sV);
-  write_st<K>(sSt, wave, lane, st);
-  bf16x8 kf[K::FBW][K::NTS];
+  init_vconst<K>(sV(0));
+  init_vconst<K>(sV(1));
+  // the zero row of the S'^T copy (padding columns DV+1..DV+15)
+  for (int t = threadIdx.x; t < K::LDF; t += K::NT) sSt[(K::DV + 1) * K::LDF + t] = 0;
+  const RowOff<K, K::LDV> vo(col);
+  const RowOff<K, K::LDF> so(col);
+  write_st<K>(sSt, so, wave, lane, st);
+  bf16x8 kf[K::FBW][K::NTS] = {};
 
+  const int role = __builtin_amdgcn_readfirstlane(wave < K::NTB ? wave : -1);
   const bool intra_wave = wave < K::NTB;
   const int ib_intra = wave;
   const bool inter_wave = (wave >= K::NTB) && (wave - K::NTB < K::NINTER);
@@ -421,86 +628,64 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
 
   const int64_t t0 = (int64_t)seg * p.seg_len;
   const int64_t t1 = min<int64_t>(p.L, t0 + p.seg_len);
-  for (int64_t c0t = t0; c0t < t1; c0t += K::C) {
-    const int n = (int)min<int64_t>(K::C, t1 - c0t);
-    __syncthreads();  // B0: previous chunk done with every LDS tile
-    stage_x<K>(p.q + (head * p.L + c0t) * K::D, n, sQ, sinvq);
-    stage_x<K>(p.k + (head * p.L + c0t) * K::D, n, sK, sinvk);
-    stage_v<K>(p.v + (head * p.L + c0t) * K::DV, n, sV);
-    __syncthreads();  // B1
-    phase_k<K, true>(sK, sinvk, sPk, wave, lane, pa, pg, c1, c0, kf);
-    phase_q<K>(sQ, sinvq, sPq, wave, lane, pa, pg, c1, c0);
-    __syncthreads();  // B2: phi(q), phi(k) complete
+  const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
 
+  // prologue: stage chunk 0, phase A of chunk 0
+  Prefetch<K> pf;
+  issue_loads<K>(p, head, t0, (int)min<int64_t>(K::C, t1 - t0), true, pf);
+  store_x<K>(pf.q, sQ, sinvq, slgq);
+  store_x<K>(pf.k, sK, sinvk, slgk);
+  store_v<K>(pf.v0, pf.v1, sV(0));
+  if (nch > 1) issue_loads<K>(p, head, t0 + K::C, (int)min<int64_t>(K::C, t1 - t0 - K::C), true, pf);
+  __syncthreads();
+  phase_k<K, true>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf);
+  phase_q<K>(sQ, sinvq, slgq, sPq, wave, lane, pa, pg, c1, c0);
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    const int64_t c0t = t0 + (int64_t)c * K::C;
+    const int n = (int)min<int64_t>(K::C, t1 - c0t);
+    const uint16_t* sVc = sV(b);
+
+    // ---- B1(c): contractions; staging of chunk c+1 ----
     f32x4 acc[K::NE];
 #pragma unroll
     for (int et = 0; et < K::NE; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (intra_wave) {
-      const int ib = ib_intra;
-      // A^T blocks (jb, ib), jb <= ib, contracted over all F features
-      f32x4 at[K::NTB];
-#pragma unroll
-      for (int jb = 0; jb < K::NTB; ++jb) at[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
-        const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(sPq + (ib * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
-#pragma unroll
-        for (int jb = 0; jb < K::NTB; ++jb) {
-          if (jb <= ib) {
-            const bf16x8 ak =
-                as_bf16x8(*reinterpret_cast<const uint4*>(sPk + (jb * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
-            at[jb] = mfma_bf16(ak, bq, at[jb]);
-          }
-        }
-      }
-      // causal mask on the diagonal block: keep j <= i (row 4g+i, column col)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * g + i > col) at[ib][i] = 0.f;
-      // num'^T += v'^T A^T over token k-steps s (blocks 2s, 2s+1)
-#pragma unroll
-      for (int s = 0; s < K::NTS; ++s) {
-        if (2 * s <= ib) {
-          const uint2 lo = pack4(at[2 * s][0], at[2 * s][1], at[2 * s][2], at[2 * s][3]);
-          uint2 hi = make_uint2(0, 0);
-          if (2 * s + 1 <= ib) hi = pack4(at[2 * s + 1][0], at[2 * s + 1][1], at[2 * s + 1][2], at[2 * s + 1][3]);
-          const bf16x8 ab = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-          for (int et = 0; et < K::NE; ++et) acc[et] = mfma_bf16(vfrag<K>(sV, et, s, lane), ab, acc[et]);
-        }
-      }
+    switch (role) {  // wave-uniform (scalar) dispatch
+      case 0: intra_task<K, 0>(sPq, sPk, sVc, vo, lane, acc); break;
+      case 1: intra_task<K, 1>(sPq, sPk, sVc, vo, lane, acc); break;
+      case 2: intra_task<K, 2>(sPq, sPk, sVc, vo, lane, acc); break;
+      case 3: intra_task<K, 3>(sPq, sPk, sVc, vo, lane, acc); break;
+      default: break;
     }
     if (inter_wave || self_inter) {
       const int ib = inter_wave ? ib_inter : ib_intra;
-#pragma unroll 2
-      for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
-        const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(sPq + (ib * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
-#pragma unroll
-        for (int et = 0; et < K::NE; ++et) {
-          const bf16x8 as =
-              as_bf16x8(*reinterpret_cast<const uint4*>(sSt + (et * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
-          acc[et] = mfma_bf16(as, bq, acc[et]);
-        }
-      }
+      inter_task<K>(sPq, sSt, so, ib, lane, acc);
       if (inter_wave) {
 #pragma unroll
         for (int et = 0; et < K::NE; ++et) sX[(ib_inter * K::NE + et) * 64 + lane] = acc[et];
       }
     }
-    __syncthreads();  // B3: inter partials published; S'^T copy no longer read
+    if (c + 1 < nch) {
+      store_x<K>(pf.q, sQ, sinvq, slgq);
+      store_x<K>(pf.k, sK, sinvk, slgk);
+      store_v<K>(pf.v0, pf.v1, sV(b ^ 1));
+      const int64_t c2 = c0t + 2 * K::C;
+      if (c + 2 < nch) issue_loads<K>(p, head, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
+    }
+    __syncthreads();  // X
 
+    // ---- B2(c): output and state update; phase A(c+1) ----
     if (intra_wave) {
       const int ib = ib_intra;
       if (!self_inter) {
 #pragma unroll
-        for (int et = 0; et < K::NE; ++et) {
-          const f32x4 x = sX[(ib * K::NE + et) * 64 + lane];
-          acc[et] += x;
-        }
+        for (int et = 0; et < K::NE; ++et) acc[et] += sX[(ib * K::NE + et) * 64 + lane];
       }
       // den of token col = element (row dv, column col): lane col (g = 0), i = 0 of tile NE-1
       const float den = __shfl(acc[K::NE - 1][0], col, 64);
-      const float rden = 1.0f / den;
+      const float rden = __builtin_amdgcn_rcpf(den);
       const int tok = ib * 16 + col;
       if (tok < n) {
         uint16_t* orow = p.o + (head * p.L + c0t + tok) * K::DV;
@@ -510,8 +695,13 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
               pack4(acc[et][0] * rden, acc[et][1] * rden, acc[et][2] * rden, acc[et][3] * rden);
       }
     }
-    state_update<K>(sV, lane, kf, st);
-    write_st<K>(sSt, wave, lane, st);
+    state_update<K>(sVc, vo, lane, kf, st);
+    write_st<K>(sSt, so, wave, lane, st);
+    if (c + 1 < nch) {
+      phase_k<K, true>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf);
+      phase_q<K>(sQ, sinvq, slgq, sPq, wave, lane, pa, pg, c1, c0);
+    }
+    __syncthreads();  // Y
   }
 
   if (seg == p.n_seg - 1 && (p.S_out || p.z_out)) {
@@ -546,18 +736,27 @@ int pick_segments(const ChunkedArgs& a) {
 template <class K>
 int64_t seg_len_of(const ChunkedArgs& a, int n_seg) {
   const int64_t n_chunks = (a.L + K::C - 1) / K::C;
-  return ((n_chunks + n_seg - 1) / n_seg) * K::C;
+  const int64_t cps = (n_chunks + n_seg - 1) / n_seg;
+  return ((cps + 1) / 2) * 2 * K::C;  // an even number of chunks: pass 1 halves each segment
 }
 
 template <class K>
+int segments_of(const ChunkedArgs& a) {
+  const int64_t seg_len = seg_len_of<K>(a, pick_segments<K>(a));
+  return (int)((a.L + seg_len - 1) / seg_len);
+}
+
+constexpr int kSub = 1;  // pass-1 sub-segments per segment
+
+template <class K>
 size_t ws_bytes_t(const ChunkedArgs& a) {
-  const int n_seg = pick_segments<K>(a);
-  return n_seg > 1 ? sizeof(float) * (size_t)a.n_heads * n_seg * K::F * K::DVP : 0;
+  const int n_seg = segments_of<K>(a);
+  return n_seg > 1 ? sizeof(float) * (size_t)a.n_heads * ((n_seg - 1) * kSub + 1) * K::F * K::DVP : 0;
 }
 
 template <class K>
 hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
-  const int n_seg = pick_segments<K>(a);
+  const int n_seg = segments_of<K>(a);
   Params p{};
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -565,7 +764,8 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
   p.o = static_cast<uint16_t*>(a.o);
   p.L = a.L;
   p.n_seg = n_seg;
-  p.seg_len = seg_len_of<K>(a, n_seg);
+  p.seg_len = seg_len_of<K>(a, pick_segments<K>(a));
+  p.sub = kSub;
   p.m = a.m;
   p.anchors = static_cast<const uint16_t*>(a.anchors);
   p.prf = static_cast<const uint16_t*>(a.prf);
@@ -579,17 +779,19 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
   p.z_out = a.z_out;
   hipError_t e;
   if (n_seg > 1) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K>),
+    constexpr int FS = K::FS1;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K, FS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pass1_kernel<K>, dim3((unsigned)(a.n_heads * (n_seg - 1))), dim3(K::NT), K::kLds1, s, p);
+    hipLaunchKernelGGL((pass1_kernel<K, FS>), dim3((unsigned)(a.n_heads * (n_seg - 1) * kSub * FS)),
+                       dim3(K::NT / FS), K::kLds1, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     ScanArgs sa{};
     sa.states = p.ws;
     sa.n_heads = a.n_heads;
-    sa.n_items = n_seg;
-    sa.n_terms = n_seg - 1;
+    sa.n_items = (n_seg - 1) * kSub + 1;
+    sa.n_terms = (n_seg - 1) * kSub;
     sa.F = K::F;
     sa.dv = K::DV;
     sa.layout = 1;
@@ -616,7 +818,10 @@ template <typename Fn>
 bool dispatch(const ChunkedArgs& a, Fn&& fn) {
   if (!a.io_bf16 || a.d != 64 || a.dv != 64 || a.chunk != 64 || a.m % 16 != 0) return false;
   switch (a.F) {
-    case 256: fn(CfgF256()); return true;
+    case 256:
+      if (a.m % 32 != 0) return false;  // a wave's two feature blocks must share a node
+      fn(CfgF256());
+      return true;
     case 128: fn(CfgF128()); return true;
     case 96: fn(CfgF96()); return true;
     case 64: fn(CfgF64()); return true;

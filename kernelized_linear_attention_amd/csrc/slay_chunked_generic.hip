@@ -54,12 +54,18 @@ __global__ __launch_bounds__(kGThreads) void scan_kernel(ScanArgs a, int64_t E) 
     if (a.z0) run = a.z0[h * a.F + f];
   }
   float* st = a.states + h * a.n_items * E + idx;
-  for (int64_t it = 0; it < a.n_items; ++it) {
-    const float d = (it < a.n_terms) ? st[it * E] : 0.f;
-    st[it * E] = run;
-    run += d;
+  // loads of a batch of items are issued together, then the running sums stored
+  constexpr int kBatch = 16;
+  for (int64_t i0 = 0; i0 < a.n_items; i0 += kBatch) {
+    float d[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) d[b] = (i0 + b < a.n_terms) ? st[(i0 + b) * E] : 0.f;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (i0 + b < a.n_items) st[(i0 + b) * E] = run;
+      run += d[b];
+    }
   }
-  if (a.n_terms > a.n_items) run += st[a.n_items * E];  // never: n_terms <= n_items
   if (e < a.dv) {
     if (a.S_out) a.S_out[(h * a.F + f) * a.dv + e] = run;
   } else if (e == a.dv) {

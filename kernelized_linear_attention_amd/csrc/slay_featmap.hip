@@ -76,11 +76,31 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
   typename M::frag pa[FBW][KS], pg[FBW][KS];
   int cur_set = -1;
 
+  // x tile vectors of the next tile are loaded into registers while the
+  // current tile is computed (one tile of prefetch)
+  constexpr int PER_T = kTileRows * VPR / kThreads;
+  constexpr int TPR = kThreads / kTileRows;  // threads per row (4); a thread's vectors lie in one row
+  uint4 xr[PER_T];
+  auto load_tile = [&](int64_t tt) {
+    const int64_t hh = tt / tiles_per_head;
+    const int64_t r0 = (tt - hh * tiles_per_head) * kTileRows;
+    const int64_t nr = min<int64_t>(kTileRows, rows_per_head - r0);
+    const TI* src = x + (hh * rows_per_head + r0) * D;
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int v = threadIdx.x * PER_T + i;
+      const int r = v / VPR;
+      const int c = (v - r * VPR) * VEC;
+      xr[i] = make_uint4(0, 0, 0, 0);
+      if (r < nr) xr[i] = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + c);
+    }
+  };
+  if (blockIdx.x < n_tiles) load_tile(blockIdx.x);
+
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int64_t h = t / tiles_per_head;
     const int64_t row0 = (t - h * tiles_per_head) * kTileRows;  // row within head
     const int64_t nrow = min<int64_t>(kTileRows, rows_per_head - row0);
-    const TI* xt = x + (h * rows_per_head + row0) * D;
     TO* pt = phi + (h * rows_per_head + row0) * (int64_t)F;
 
     // (re)load this wave's slice of P when the draw set changes
@@ -102,29 +122,25 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
     }
 
     // stage the x tile in LDS and compute 1/max(|x|, 1e-12) per row
-    constexpr int PER_T = kTileRows * VPR / kThreads;
-    constexpr int TPR = kThreads / kTileRows;  // threads per row (4)
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
-      const int v = threadIdx.x * PER_T + i;  // vector index in tile (row-major)
+      const int v = threadIdx.x * PER_T + i;
       const int r = v / VPR;
       const int c = (v - r * VPR) * VEC;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (r < nrow) val = *reinterpret_cast<const uint4*>(xt + (int64_t)r * D + c);
-      *reinterpret_cast<uint4*>(&sx[r * LDX + c]) = val;
-      const TI* e = reinterpret_cast<const TI*>(&val);
+      *reinterpret_cast<uint4*>(&sx[r * LDX + c]) = xr[i];
+      const TI* e = reinterpret_cast<const TI*>(&xr[i]);
 #pragma unroll
       for (int q = 0; q < VEC; ++q) {
         const float f = M::to_f32(e[q]);
         ss += f * f;
       }
     }
-    // the PER_T vectors of a thread lie in one row; TPR consecutive threads share a row
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
     if ((threadIdx.x % TPR) == 0) sinv[threadIdx.x / TPR] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
     __syncthreads();
+    if (t + gridDim.x < n_tiles) load_tile(t + gridDim.x);
 
 #pragma unroll
     for (int tb = 0; tb < kTileRows / 16; ++tb) {
