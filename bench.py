@@ -213,16 +213,24 @@ def main():
         S = torch.zeros(nh, wd.F, wd.dv, device=dev)
         z = torch.zeros(nh, wd.F, device=dev)
         o = torch.empty(nh, wd.dv, device=dev)
-        it = [0]
+        wsd = torch.empty(ops.recurrent_step_workspace_size(fmd, nh, wd.dv, torch.float32), dtype=torch.uint8,
+                          device=dev)
+        # n_in consecutive steps (two launches each: feature map of all heads,
+        # streaming state update) captured once as a HIP graph and replayed, so
+        # host-side launch cost does not starve the GPU between short steps
+        def steps():
+            for t in range(n_in):
+                ops.recurrent_step(fmd, qs[t], ks_[t], vs[t], S, z, out=o, workspace=wsd)
 
-        def dstep():
-            t = it[0] % n_in
-            it[0] += 1
-            ops.recurrent_step(fmd, qs[t], ks_[t], vs[t], S, z, out=o)
-
-        for _ in range(args.warmup):
-            dstep()
-        ms = event_time_ms(dstep, args.decode_steps, stream)
+        steps()  # warm-up, eager
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            steps()
+        reps = max(1, args.decode_steps // n_in)
+        for _ in range(max(1, args.warmup // n_in)):
+            graph.replay()
+        ms = event_time_ms(graph.replay, reps, stream) / n_in
         nbytes = nh * decode_bytes_per_head(wd)
         gbs = nbytes / (ms * 1e-3) / 1e9
         also.append({"name": "decode_256x16_f32", "ms_per_step": ms, "tokens_per_s": wd.B / (ms * 1e-3),

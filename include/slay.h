@@ -114,18 +114,25 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
                                     int32_t chunk, const float* S0, const float* z0, void* o, float* S_out,
                                     float* z_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes slay_attn_recurrent_step needs (2 * n_heads * R*m * 4). */
+size_t slay_attn_recurrent_step_workspace_size(const slay_params_t* params, int64_t n_heads, int32_t dv,
+                                               slay_dtype_t io_dtype);
+
 /* One O(1)-per-token decode step for n_heads independent heads (the
- * recurrent form of the same attention): phi(q), phi(k) of the new token,
- * S += phi(k) v^T, z += phi(k), then o = phi(q)^T S / phi(q)^T z.
+ * recurrent form of the same attention; review, "Proposed method" bullet 6):
+ * phi(q), phi(k) of the new token, S += phi(k) v^T, z += phi(k), then
+ * o = phi(q)^T S / phi(q)^T z.
  *   q, k : device [n_heads][d];  v, o : device [n_heads][dv];  dtype io_dtype
+ *          (must equal params->draw_dtype); outputs in io_dtype
  *   S, z : device fp32 state [n_heads][R*m][dv], [n_heads][R*m], updated in place
- *   draws: fp32 or bf16 (params->draw_dtype), any io_dtype.
- * d in {32, 64}, dv in {32, 64}, R*m in {64, 128, 192, 256} run the fused
- * streaming kernel; other accepted shapes need a workspace and are rejected
- * here with SLAY_E_UNSUPPORTED. */
+ *   workspace: device scratch of slay_attn_recurrent_step_workspace_size()
+ *          bytes (phi(q), phi(k) in fp32).
+ * dv in {16, 32, 64, 128}; R*m a multiple of 16, at most 1024, and a multiple
+ * of 1024/dv.  Two launches: the feature map of all heads, then one streaming
+ * pass over the state. */
 slay_status_t slay_attn_recurrent_step(const slay_params_t* params, const void* q, const void* k, const void* v,
                                        slay_dtype_t io_dtype, int64_t n_heads, int32_t dv, float* S, float* z,
-                                       void* o, void* stream);
+                                       void* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only: the R-point Gauss-Laguerre mixture parameters used by the
  * library, alpha[r] = w_r/(2+eps), beta[r] = 2 x_r/(2+eps) (fp64, R <= 16).

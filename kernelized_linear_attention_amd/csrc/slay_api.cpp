@@ -291,14 +291,9 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
   return device_status(fused ? slay::launch_fused(a, s) : slay::launch_generic(a, s), "slay_attn_chunked_fwd launch");
 }
 
-slay_status_t slay_attn_recurrent_step(const slay_params_t* params, const void* q, const void* k, const void* v,
-                                       slay_dtype_t io_dtype, int64_t n_heads, int32_t dv, float* S, float* z,
-                                       void* o, void* stream) {
-  slay_status_t st = check_params(params);
-  if (st != SLAY_OK) return st;
-  if (n_heads < 0) return fail(SLAY_E_INVALID, "n_heads < 0");
-  if (dv < 1) return fail(SLAY_E_INVALID, "dv must be >= 1");
-  if (io_dtype != SLAY_F32 && io_dtype != SLAY_BF16) return fail(SLAY_E_INVALID, "bad io dtype");
+namespace {
+slay::DecodeArgs decode_args(const slay_params_t* params, const void* q, const void* k, const void* v,
+                             slay_dtype_t io_dtype, int64_t n_heads, int32_t dv, float* S, float* z, void* o) {
   slay::DecodeArgs a{};
   a.q = q;
   a.k = k;
@@ -317,12 +312,38 @@ slay_status_t slay_attn_recurrent_step(const slay_params_t* params, const void* 
   a.S = S;
   a.z = z;
   a.o = o;
+  return a;
+}
+}  // namespace
+
+size_t slay_attn_recurrent_step_workspace_size(const slay_params_t* params, int64_t n_heads, int32_t dv,
+                                               slay_dtype_t io_dtype) {
+  if (check_params(params) != SLAY_OK || n_heads < 0 || dv < 1) return 0;
+  slay::DecodeArgs a = decode_args(params, nullptr, nullptr, nullptr, io_dtype, n_heads, dv, nullptr, nullptr,
+                                   nullptr);
+  return slay::decode_workspace_bytes(a);
+}
+
+slay_status_t slay_attn_recurrent_step(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                       slay_dtype_t io_dtype, int64_t n_heads, int32_t dv, float* S, float* z,
+                                       void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  slay_status_t st = check_params(params);
+  if (st != SLAY_OK) return st;
+  if (n_heads < 0) return fail(SLAY_E_INVALID, "n_heads < 0");
+  if (dv < 1) return fail(SLAY_E_INVALID, "dv must be >= 1");
+  if (io_dtype != SLAY_F32 && io_dtype != SLAY_BF16) return fail(SLAY_E_INVALID, "bad io dtype");
+  slay::DecodeArgs a = decode_args(params, q, k, v, io_dtype, n_heads, dv, S, z, o);
   if (!slay::decode_supported(a))
-    return fail(SLAY_E_UNSUPPORTED, "decode shape not supported (d=%d dv=%d F=%d)", a.d, dv, a.F);
+    return fail(SLAY_E_UNSUPPORTED, "decode shape not supported (d=%d dv=%d F=%d, io and draw dtypes equal)", a.d,
+                dv, a.F);
   if (n_heads == 0) return ok();
   if (!q || !k || !v || !o || !S || !z) return fail(SLAY_E_INVALID, "q/k/v/o/S/z pointer is NULL");
-  if (!aligned16(S)) return fail(SLAY_E_INVALID, "S must be 16-byte aligned");
+  if (!aligned16(S) || !aligned16(q) || !aligned16(k)) return fail(SLAY_E_INVALID, "q, k, S must be 16-byte aligned");
   if (!mul_ok(n_heads, (int64_t)a.F * dv)) return fail(SLAY_E_INVALID, "problem size overflows");
+  const size_t need = slay::decode_workspace_bytes(a);
+  if (workspace_bytes < need) return fail(SLAY_E_INVALID, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (!workspace || !aligned16(workspace)) return fail(SLAY_E_INVALID, "workspace must be non-NULL and 16-byte aligned");
+  a.ws = workspace;
   a.nc = node_consts(params->R, params->m, params->eps);
   return device_status(slay::launch_decode(a, static_cast<hipStream_t>(stream)), "slay_attn_recurrent_step launch");
 }

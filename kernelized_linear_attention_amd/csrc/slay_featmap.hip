@@ -49,9 +49,12 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, 
 
 template <typename TI, typename TO, int D, int FBW>
 __global__ __launch_bounds__(kThreads) void featmap_kernel(
-    const TI* __restrict__ x, int64_t rows_per_head, int64_t n_heads, const TI* __restrict__ anchors,
-    const TI* __restrict__ prf, int64_t draw_set_stride, int n_draw_sets, int F, int m, NodeConsts nc,
-    TO* __restrict__ phi) {
+    const TI* __restrict__ x_a, const TI* __restrict__ x_b, int64_t rows_per_head, int64_t n_heads,
+    const TI* __restrict__ anchors, const TI* __restrict__ prf, int64_t draw_set_stride, int n_draw_sets, int F,
+    int m, NodeConsts nc, TO* __restrict__ phi_a, TO* __restrict__ phi_b) {
+  // blockIdx.z selects the input: z = 1 maps the second input in the same launch
+  const TI* __restrict__ x = blockIdx.z ? x_b : x_a;
+  TO* __restrict__ phi = blockIdx.z ? phi_b : phi_a;
   using M = Mma<TI>;
   constexpr int KS = D / M::K;               // MFMA k-steps over d
   constexpr int LDX = D + XStage<TI>::kPad;  // padded LDS row stride (elements)
@@ -60,8 +63,11 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
   static_assert(D % M::K == 0, "d must be a multiple of the MFMA k-step");
   static_assert((kTileRows * VPR) % kThreads == 0, "tile staging must divide evenly");
 
+  constexpr int FWS = 4 * FBW * 16;              // features per workgroup slice
+  constexpr int LDO = FWS + 16 / sizeof(TO);      // padded output staging stride
   __shared__ __align__(16) TI sx[kTileRows * LDX];
-  __shared__ float sinv[kTileRows];
+  __shared__ __align__(16) TO so[kTileRows * LDO];
+  __shared__ float sinv[kTileRows], slg[kTileRows];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -70,8 +76,8 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
   const int n_fblk = F / 16;
   const int fblk0 = blockIdx.y * (4 * FBW) + wave * FBW;
 
-  const int64_t tiles_per_head = (rows_per_head + kTileRows - 1) / kTileRows;
-  const int64_t n_tiles = tiles_per_head * n_heads;
+  const int tiles_per_head = (int)((rows_per_head + kTileRows - 1) / kTileRows);
+  const int n_tiles = tiles_per_head * (int)n_heads;
 
   typename M::frag pa[FBW][KS], pg[FBW][KS];
   int cur_set = -1;
@@ -81,11 +87,11 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
   constexpr int PER_T = kTileRows * VPR / kThreads;
   constexpr int TPR = kThreads / kTileRows;  // threads per row (4); a thread's vectors lie in one row
   uint4 xr[PER_T];
-  auto load_tile = [&](int64_t tt) {
-    const int64_t hh = tt / tiles_per_head;
-    const int64_t r0 = (tt - hh * tiles_per_head) * kTileRows;
+  auto load_tile = [&](int tt) {
+    const int hh = tt / tiles_per_head;
+    const int64_t r0 = (int64_t)(tt - hh * tiles_per_head) * kTileRows;
     const int64_t nr = min<int64_t>(kTileRows, rows_per_head - r0);
-    const TI* src = x + (hh * rows_per_head + r0) * D;
+    const TI* src = x + ((int64_t)hh * rows_per_head + r0) * D;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int v = threadIdx.x * PER_T + i;
@@ -95,13 +101,13 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
       if (r < nr) xr[i] = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + c);
     }
   };
-  if (blockIdx.x < n_tiles) load_tile(blockIdx.x);
+  if ((int)blockIdx.x < n_tiles) load_tile(blockIdx.x);
 
-  for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const int64_t h = t / tiles_per_head;
-    const int64_t row0 = (t - h * tiles_per_head) * kTileRows;  // row within head
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int h = t / tiles_per_head;
+    const int64_t row0 = (int64_t)(t - h * tiles_per_head) * kTileRows;  // row within head
     const int64_t nrow = min<int64_t>(kTileRows, rows_per_head - row0);
-    TO* pt = phi + (h * rows_per_head + row0) * (int64_t)F;
+    TO* pt = phi + ((int64_t)h * rows_per_head + row0) * (int64_t)F;
 
     // (re)load this wave's slice of P when the draw set changes
     const int set = (int)(h % n_draw_sets);
@@ -138,9 +144,13 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
     }
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
-    if ((threadIdx.x % TPR) == 0) sinv[threadIdx.x / TPR] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    if ((threadIdx.x % TPR) == 0) {
+      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+      sinv[threadIdx.x / TPR] = inv;
+      slg[threadIdx.x / TPR] = 2.0f * __builtin_amdgcn_logf(inv);  // log2(inv^2)
+    }
     __syncthreads();
-    if (t + gridDim.x < n_tiles) load_tile(t + gridDim.x);
+    if (t + (int)gridDim.x < n_tiles) load_tile(t + gridDim.x);
 
 #pragma unroll
     for (int tb = 0; tb < kTileRows / 16; ++tb) {
@@ -160,21 +170,31 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
         }
       }
       const int r = tb * 16 + col;  // token of this lane's C column
-      const float inv = sinv[r];
+      const float inv = sinv[r], lg = slg[r];
 #pragma unroll
       for (int j = 0; j < FBW; ++j) {
-        const int fb = fblk0 + j;
-        if (fb >= n_fblk) continue;
-        const int node = (fb * 16) / m;
+        const int fbl = wave * FBW + j;  // feature block within the workgroup slice
+        const int node = (min(fblk0 + j, n_fblk - 1) * 16) / m;
+        // (y_a inv)^2 exp2(y_g inv c1 + c0) = y_a^2 exp2(y_g (inv c1) + (c0 + log2 inv^2))
         const float s1 = inv * nc.c1[node];
-        const float c0 = nc.c0[node];
+        const float c0 = nc.c0[node] + lg;
         float o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = ya[j][i] * inv;
-          o[i] = a * a * fast_exp2(fmaf(yg[j][i], s1, c0));
-        }
-        if (r < nrow) store4<TO>(pt + (int64_t)r * F + fb * 16 + 4 * g, o[0], o[1], o[2], o[3]);
+        for (int i = 0; i < 4; ++i) o[i] = ya[j][i] * ya[j][i] * fast_exp2(fmaf(yg[j][i], s1, c0));
+        store4<TO>(so + r * LDO + fbl * 16 + 4 * g, o[0], o[1], o[2], o[3]);
+      }
+    }
+    __syncthreads();
+    // coalesced write-out of the tile's feature slice: 16-byte pieces of each row
+    {
+      constexpr int PPR = FWS * (int)sizeof(TO) / 16;  // 16-byte pieces per row of the slice
+      const int fcols = min(FWS, F - (int)blockIdx.y * FWS);
+      const int ppr = fcols * (int)sizeof(TO) / 16;
+      for (int pc = threadIdx.x; pc < kTileRows * PPR; pc += kThreads) {
+        const int rr = pc / PPR, q = pc - (pc / PPR) * PPR;
+        if (rr < nrow && q < ppr)
+          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(pt + (int64_t)rr * F + blockIdx.y * FWS) + q * 16) =
+              *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(so + rr * LDO) + q * 16);
       }
     }
     __syncthreads();
@@ -190,20 +210,25 @@ hipError_t launch_t(const FeatmapArgs& a, hipStream_t s) {
   if (gx < 1) gx = 1;
   if (gx > tiles) gx = tiles;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((featmap_kernel<TI, TO, D, FBW>), dim3((unsigned)gx, gy), dim3(kThreads), 0, s,
-                     static_cast<const TI*>(a.x), a.rows_per_head, a.n_heads,
+  const int gz = a.x2 ? 2 : 1;
+  hipLaunchKernelGGL((featmap_kernel<TI, TO, D, FBW>), dim3((unsigned)gx, gy, gz), dim3(kThreads), 0, s,
+                     static_cast<const TI*>(a.x), static_cast<const TI*>(a.x2), a.rows_per_head, a.n_heads,
                      static_cast<const TI*>(a.anchors), static_cast<const TI*>(a.prf), a.draw_set_stride,
-                     a.n_draw_sets, a.F, a.m, a.nc, static_cast<TO*>(a.phi));
+                     a.n_draw_sets, a.F, a.m, a.nc, static_cast<TO*>(a.phi), static_cast<TO*>(a.phi2));
   return hipGetLastError();
 }
 
 template <typename TI, typename TO>
 hipError_t launch_d(const FeatmapArgs& a, hipStream_t s) {
   constexpr bool bf = sizeof(TI) == 2;
+  // Few row tiles (e.g. one decode token per head): narrower feature slices
+  // per workgroup give more workgroups to hide load latency.
+  const int64_t tiles = ((a.rows_per_head + kTileRows - 1) / kTileRows) * a.n_heads * (a.x2 ? 2 : 1);
+  const bool small = tiles * ((a.F + 127) / 128) < 1024;
   switch (a.d) {
-    case 32: return launch_t<TI, TO, 32, 4>(a, s);
-    case 64: return launch_t<TI, TO, 64, bf ? 4 : 2>(a, s);
-    case 128: return launch_t<TI, TO, 128, bf ? 2 : 1>(a, s);
+    case 32: return small ? launch_t<TI, TO, 32, 1>(a, s) : launch_t<TI, TO, 32, 4>(a, s);
+    case 64: return small ? launch_t<TI, TO, 64, 1>(a, s) : launch_t<TI, TO, 64, 2>(a, s);
+    case 128: return small ? launch_t<TI, TO, 128, 1>(a, s) : launch_t<TI, TO, 128, bf ? 2 : 1>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -11,6 +11,7 @@ namespace slay {
 
 struct FeatmapArgs {
   const void* x;          // [n_heads * rows_per_head][d]
+  const void* x2;         // nullable: a second input of the same shape (phi2 <- phi(x2)), same launch
   int64_t rows_per_head;  // rows sharing one draw set
   int64_t n_heads;
   int d, F, m;
@@ -21,6 +22,7 @@ struct FeatmapArgs {
   int n_draw_sets;          // head h uses set h % n_draw_sets
   NodeConsts nc;
   void* phi;              // [rows][F]
+  void* phi2;             // used when x2 is set
   bool phi_bf16;
 };
 
@@ -93,8 +95,10 @@ struct DecodeArgs {
   float* S;  // [n_heads][F][dv]
   float* z;  // [n_heads][F]
   void* o;   // [n_heads][dv]
+  void* ws;  // phi(q), phi(k): 2 * n_heads * F fp32
 };
 bool decode_supported(const DecodeArgs& a);
+size_t decode_workspace_bytes(const DecodeArgs& a);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 }  // namespace slay

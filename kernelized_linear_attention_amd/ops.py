@@ -152,8 +152,14 @@ def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     return out
 
 
+def recurrent_step_workspace_size(fm: FeatureMap, n_heads: int, dv: int, dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.slay_attn_recurrent_step_workspace_size(fm.c_params(), n_heads, dv, _dtype_code(dtype)))
+
+
 def recurrent_step(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: torch.Tensor,
-                   z: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+                   z: torch.Tensor, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
     """One decode step for n heads: q, k [n, d], v [n, dv]; S [n, F, dv], z [n, F] fp32 in place."""
     lib = _lib.load()
     n, d = q.shape
@@ -165,7 +171,12 @@ def recurrent_step(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Te
     _need(z, "z", (n, fm.F), torch.float32)
     if out is None:
         out = torch.empty((n, dv), dtype=q.dtype, device=q.device)
+    nbytes = recurrent_step_workspace_size(fm, n, dv, q.dtype)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.slay_attn_recurrent_step(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype),
-                                      n, dv, S.data_ptr(), z.data_ptr(), out.data_ptr(), _stream(q))
+                                      n, dv, S.data_ptr(), z.data_ptr(), out.data_ptr(), _ptr(workspace), wsz,
+                                      _stream(q))
     _lib.check(st, "slay_attn_recurrent_step")
     return out

@@ -129,14 +129,22 @@ def test_featmap_and_decode_validation(lib):
         _lib.SLAY_E_INVALID  # rows_per_head must divide n_rows
     # decode
     pd = _params(dt=_lib.SLAY_F32)
+    need = lib.slay_attn_recurrent_step_workspace_size(ctypes.byref(pd), 10, 64, _lib.SLAY_F32)
+    assert need == 2 * 10 * 256 * 4
     st = lib.slay_attn_recurrent_step(ctypes.byref(pd), FAKE, FAKE, FAKE, _lib.SLAY_F32, 10, 64, None, FAKE, FAKE,
-                                      None)
-    assert st == _lib.SLAY_E_INVALID
-    st = lib.slay_attn_recurrent_step(ctypes.byref(_params(d=128, dt=_lib.SLAY_F32)), FAKE, FAKE, FAKE,
-                                      _lib.SLAY_F32, 10, 64, FAKE, FAKE, FAKE, None)
+                                      FAKE, need, None)
+    assert st == _lib.SLAY_E_INVALID  # S is NULL
+    st = lib.slay_attn_recurrent_step(ctypes.byref(pd), FAKE, FAKE, FAKE, _lib.SLAY_F32, 10, 64, FAKE, FAKE, FAKE,
+                                      FAKE, need - 1, None)
+    assert st == _lib.SLAY_E_INVALID and b"workspace too small" in lib.slay_last_error()
+    st = lib.slay_attn_recurrent_step(ctypes.byref(pd), FAKE, FAKE, FAKE, _lib.SLAY_F32, 10, 48, FAKE, FAKE, FAKE,
+                                      FAKE, need, None)
     assert st == _lib.SLAY_E_UNSUPPORTED and b"decode shape" in lib.slay_last_error()
+    st = lib.slay_attn_recurrent_step(ctypes.byref(pd), FAKE, FAKE, FAKE, _lib.SLAY_BF16, 10, 64, FAKE, FAKE, FAKE,
+                                      FAKE, need, None)
+    assert st == _lib.SLAY_E_UNSUPPORTED  # io dtype must equal the draw dtype
     st = lib.slay_attn_recurrent_step(ctypes.byref(pd), FAKE, FAKE, FAKE, _lib.SLAY_F32, 0, 64, FAKE, FAKE, FAKE,
-                                      None)
+                                      None, 0, None)
     assert st == _lib.SLAY_OK and lib.slay_last_error() == b""
 
 

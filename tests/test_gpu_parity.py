@@ -297,3 +297,44 @@ def test_decode_continues_prefill(lib, orc):
     ro = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m)[0]
     got = np.stack(outs, 1)
     assert rownorm_rel(got, ro[0, :, 90:]) < TOL["f32"]
+
+
+def test_decode_graph_replay_matches_eager(lib):
+    """Decode steps captured in a HIP graph and replayed several times (with eager work and
+    synchronisation between replays) give the same state and outputs as eager calls."""
+    import torch
+
+    w = ss.WORKLOADS["decode_256x16_f32"]
+    A, G = ss.make_draws(w)
+    fm = _fm(lib, w, A, G)
+    nh, n_in = 64, 4
+    ins = [tuple(to_dev(a, "f32") for a in ss.make_decode_step(w, t, nh)) for t in range(n_in)]
+    ws = torch.empty(lib.recurrent_step_workspace_size(fm, nh, w.dv, torch.float32), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(S, z, outs):
+        for t, (q, k, v) in enumerate(ins):
+            lib.recurrent_step(fm, q, k, v, S, z, out=outs[t], workspace=ws)
+
+    S_e = torch.zeros(nh, w.F, w.dv, device="cuda")
+    z_e = torch.zeros(nh, w.F, device="cuda")
+    outs_e = [torch.empty(nh, w.dv, device="cuda") for _ in range(n_in)]
+    S_g, z_g = S_e.clone(), z_e.clone()
+    outs_g = [torch.empty(nh, w.dv, device="cuda") for _ in range(n_in)]
+    run(S_g, z_g, outs_g)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    S_g.zero_()
+    z_g.zero_()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(S_g, z_g, outs_g)
+    torch.cuda.synchronize()
+    S_g.zero_()
+    z_g.zero_()
+    for rep in range(3):
+        graph.replay()
+        run(S_e, z_e, outs_e)  # eager work between replays
+        torch.cuda.synchronize()
+        for t in range(n_in):
+            assert torch.equal(outs_g[t], outs_e[t]), (rep, t)
+        assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e)
