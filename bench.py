@@ -76,6 +76,68 @@ def read_traffic(kind: str):
     return float(m_val.group(1))
 
 
+TRAFFIC_UNITS = {
+    # summary name: (kernel-name fragments counted once per launch of the unit, description)
+    "fused_fwd_h16_l16k_bf16": (("pass1_kernel", "scan_kernel", "pass2_kernel<"),
+                                "one causal forward, B1 H16 L16384 bf16 (segment states + scan + main pass)"),
+    "featmap_h16_l16k_bf16": (("featmap_kernel<unsigned short, unsigned short",),
+                              "one feature-map launch over 262144 bf16 rows, F = 256"),
+    "decode_256x16_f32": (("featmap_kernel<float, float", "stream_kernel"),
+                          "one decode step for 4096 heads (q/k feature map + state stream)"),
+}
+CALIB_KERNEL = "copyBuffer"  # the device-to-device copy of --calib-copy-mib MiB
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, calib_mib: int, command: str) -> None:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_*.txt."""
+    import collections
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        per_disp = collections.defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            per_disp[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        by_name = collections.defaultdict(list)
+        for did, v in per_disp.items():
+            by_name[names[did]].append(v)
+        return {n: sum(v) / len(v) for n, v in by_name.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    calib_kib = calib_mib * 1024.0
+
+    def pick(table, frag):
+        vals = [v for n, v in table.items() if frag in n]
+        return max(vals) if vals else None
+
+    f_scale = calib_kib / pick(fetch, CALIB_KERNEL)
+    w_scale = calib_kib / pick(write, CALIB_KERNEL)
+    for name, (frags, desc) in TRAFFIC_UNITS.items():
+        f_kib = sum(pick(fetch, fr) or 0.0 for fr in frags)
+        w_kib = sum(pick(write, fr) or 0.0 for fr in frags)
+        total = (f_kib * f_scale + w_kib * w_scale) * 1024.0
+        lines = [f"# HBM traffic per launch: {name}", "", f"unit: {desc}", "",
+                 "commands (from the repository root on the GPU box):", "",
+                 f"    {command.replace('COUNTER', 'FETCH_SIZE')}",
+                 f"    {command.replace('COUNTER', 'WRITE_SIZE')}",
+                 f"    python bench.py --traffic-summary <FETCH_SIZE dir> <WRITE_SIZE dir> --calib-copy-mib {calib_mib}", "",
+                 f"calibration: a {calib_mib} MiB device copy reads FETCH_SIZE x{1 / f_scale:.3f} and WRITE_SIZE "
+                 f"x{1 / w_scale:.3f} of its bytes; factors {f_scale:.3f} and {w_scale:.3f}", "",
+                 "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch |", "|---|---|---|"]
+        for fr in frags:
+            lines.append(f"| {fr} | {pick(fetch, fr) or 0.0:.0f} | {pick(write, fr) or 0.0:.0f} |")
+        lines += ["", f"hbm_bytes_per_launch: {total:.6e}", f"sources_sha256_16: {sources_digest()}"]
+        with open(os.path.join(ROOT, "profiles", f"traffic_{name}.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(name, f"{total / 1e6:.1f} MB per launch")
+
+
 def event_time_ms(fn, steps: int, stream) -> float:
     import torch
 
@@ -115,7 +177,15 @@ def main():
     ap.add_argument("--only", choices=["all", "fwd", "featmap", "decode"], default="all")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (scale for HBM byte counters)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_*.txt from two rocprofv3 --pmc runs and exit (no GPU)")
+    ap.add_argument("--traffic-command", default="rocprofv3 --pmc COUNTER --output-format csv -d <dir> -o run -- "
+                    "python3 bench.py --steps 5 --warmup 1 --decode-steps 32 --no-cpu --calib-copy-mib 512")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.calib_copy_mib or 512,
+                        args.traffic_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
