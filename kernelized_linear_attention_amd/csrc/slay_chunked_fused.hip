@@ -81,9 +81,9 @@ struct Cfg {
   static constexpr int kInv = kX + (NINTER > 0 ? NINTER : 1) * NE * 64 * 16;
   static constexpr int kLds = kInv + 4 * C * 4;  // inv and log2 scale of q and k rows
   static_assert(kLds <= 160 * 1024, "LDS budget");
-  // pass 1 LDS: k tile, v'^T and row scales, all double-buffered
-  static constexpr int kStage1 = C * LDX * 2 + kVbuf + 2 * C * 4;
-  static constexpr int kLds1 = 2 * kStage1;
+  // pass 1 LDS: k tile with its row scales (two buffers), v'^T (three buffers)
+  static constexpr int kKbuf1 = C * LDX * 2 + 2 * C * 4;
+  static constexpr int kLds1 = 2 * kKbuf1 + 3 * kVbuf;
   // pass 1 splits the features over FS1 workgroups of NW / FS1 waves
   static constexpr int FS1 = 1;
 };
@@ -223,7 +223,9 @@ __device__ __forceinline__ void issue_loads(const Params& p, int64_t head, int64
 }
 
 // Write staged q or k vectors to LDS (padded rows) with, per row,
-// inv = 1/max(|x|, 1e-12) and lg = log2(inv^2).
+// inv = 1/max(|x|, 1e-12) and lg = log2(inv^2).  The squares are summed with
+// the bf16 dot instruction (products of bf16 values are exact in fp32) and
+// inv comes from the hardware reciprocal square root (about 1 ulp).
 template <class K, int NT = K::NT>
 __device__ __forceinline__ void store_x(const uint4 (&r)[Prefetch<K, NT>::XV], uint16_t* sx, float* sinv,
                                         float* slg) {
@@ -239,13 +241,12 @@ __device__ __forceinline__ void store_x(const uint4 (&r)[Prefetch<K, NT>::XV], u
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float lo = __uint_as_float(w[q] << 16), hi = __uint_as_float(w[q] & 0xFFFF0000u);
-      ss = fmaf(lo, lo, ss);
-      ss = fmaf(hi, hi, ss);
+      const bf16x2 h = __builtin_bit_cast(bf16x2, w[q]);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(h, h, ss, false);
     }
     ss = group_sum<VPR>(ss);
     if ((vec % VPR) == 0) {
-      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+      const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
       sinv[row] = inv;
       slg[row] = 2.0f * __builtin_amdgcn_logf(inv);  // v_log_f32 is log2
     }
@@ -289,39 +290,96 @@ __device__ __forceinline__ bf16x8 vfrag(const uint16_t* sv, const RowOff<K, K::L
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// phi = (y_a inv)^2 exp2(y_g inv c1 + c0) = y_a^2 exp2(y_g (inv c1) + (c0 + log2 inv^2)).
-// With tokens as M each lane holds 4 tokens of one feature; s1 = inv c1 and
-// c0' = c0 + log2 inv^2 are formed per token and node.
-// The wave's FBW feature blocks belong to one Gauss-Laguerre node (the
-// dispatcher requires m % (16 FBW) == 0), so s1 and c0' are formed once per
-// token and block of 16 tokens.
-template <class K, bool PHI_LDS>
-__device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, const float* slg, uint16_t* spk,
-                                        int fb0, int lane, const bf16x8 (&pa)[K::FBW][K::NKS],
-                                        const bf16x8 (&pg)[K::FBW][K::NKS], const float (&c1)[K::FBW],
-                                        const float (&c0)[K::FBW], bf16x8 (&kf)[K::FBW][K::NTS]) {
+// Projection accumulators of one 16-token block: y_a (anchor) and y_g (PRF)
+// for each of the wave's FBW feature blocks.
+template <class K>
+struct Proj {
+  f32x4 a[K::FBW], g[K::FBW];
+};
+
+// Projection of token block tb with tokens as M: each lane's accumulator
+// holds tokens 4g..4g+3 of feature col of each block.
+template <class K>
+__device__ __forceinline__ void proj_tok(const uint16_t* sx, int tb, int lane, const bf16x8 (&pa)[K::FBW][K::NKS],
+                                         const bf16x8 (&pg)[K::FBW][K::NKS], Proj<K>& y) {
   const int g = lane >> 4, col = lane & 15;
+  bf16x8 xa[K::NKS];
 #pragma unroll
-  for (int tb = 0; tb < K::NTB; ++tb) {
-    bf16x8 xa[K::NKS];
+  for (int ks = 0; ks < K::NKS; ++ks)
+    xa[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sx + (tb * 16 + col) * K::LDX + ks * 32 + 8 * g));
 #pragma unroll
-    for (int ks = 0; ks < K::NKS; ++ks)
-      xa[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sx + (tb * 16 + col) * K::LDX + ks * 32 + 8 * g));
-    const float4 inv4 = *reinterpret_cast<const float4*>(sinv + tb * 16 + 4 * g);
-    const float4 lg4 = *reinterpret_cast<const float4*>(slg + tb * 16 + 4 * g);
-    const float s1[4] = {inv4.x * c1[0], inv4.y * c1[0], inv4.z * c1[0], inv4.w * c1[0]};
-    const float c0p[4] = {c0[0] + lg4.x, c0[0] + lg4.y, c0[0] + lg4.z, c0[0] + lg4.w};
+  for (int j = 0; j < K::FBW; ++j) {
+    f32x4 ya = mfma_bf16(xa[0], pa[j][0], f32x4{0.f, 0.f, 0.f, 0.f});
+    f32x4 yg = mfma_bf16(xa[0], pg[j][0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-    for (int j = 0; j < K::FBW; ++j) {
-      f32x4 ya = {0.f, 0.f, 0.f, 0.f}, yg = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 1; ks < K::NKS; ++ks) {
+      ya = mfma_bf16(xa[ks], pa[j][ks], ya);
+      yg = mfma_bf16(xa[ks], pg[j][ks], yg);
+    }
+    y.a[j] = ya;
+    y.g[j] = yg;
+  }
+}
+
+// Projection of token block tb with features as M: each lane's accumulator
+// holds features 4g..4g+3 of each block for token col.
+template <class K>
+__device__ __forceinline__ void proj_feat(const uint16_t* sx, int tb, int lane, const bf16x8 (&pa)[K::FBW][K::NKS],
+                                          const bf16x8 (&pg)[K::FBW][K::NKS], Proj<K>& y) {
+  const int g = lane >> 4, col = lane & 15;
+  bf16x8 xb[K::NKS];
 #pragma unroll
-      for (int ks = 0; ks < K::NKS; ++ks) {
-        ya = mfma_bf16(xa[ks], pa[j][ks], ya);
-        yg = mfma_bf16(xa[ks], pg[j][ks], yg);
-      }
+  for (int ks = 0; ks < K::NKS; ++ks)
+    xb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sx + (tb * 16 + col) * K::LDX + ks * 32 + 8 * g));
+#pragma unroll
+  for (int j = 0; j < K::FBW; ++j) {
+    f32x4 ya = mfma_bf16(pa[j][0], xb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+    f32x4 yg = mfma_bf16(pg[j][0], xb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int ks = 1; ks < K::NKS; ++ks) {
+      ya = mfma_bf16(pa[j][ks], xb[ks], ya);
+      yg = mfma_bf16(pg[j][ks], xb[ks], yg);
+    }
+    y.a[j] = ya;
+    y.g[j] = yg;
+  }
+}
+
+// State update slice for token k-step s: S'[own features] += phi(k)^T v'
+// over tokens 32s..32s+31.
+template <class K>
+__device__ __forceinline__ void state_update_step(const uint16_t* sv, const RowOff<K, K::LDV>& vo, int lane, int s,
+                                                  const bf16x8 (&kf)[K::FBW][K::NTS], f32x4 (&st)[K::FBW][K::NE]) {
+#pragma unroll
+  for (int et = 0; et < K::NE; ++et) {
+    const bf16x8 vb = vfrag<K>(sv, vo, et, s, lane);
+#pragma unroll
+    for (int j = 0; j < K::FBW; ++j) st[j][et] = mfma_bf16(kf[j][s], vb, st[j][et]);
+  }
+}
+
+// phi epilogue of a token block projected with tokens as M:
+// phi = (y_a inv)^2 exp2(y_g inv c1 + c0) = y_a^2 exp2(y_g (inv c1) + (c0 + log2 inv^2)).
+// Each lane holds 4 tokens of one feature; s1 = inv c1 and c0' = c0 + log2
+// inv^2 are formed per token.  The wave's FBW feature blocks belong to one
+// Gauss-Laguerre node (the dispatcher requires m % (16 FBW) == 0), so they
+// are formed once per token for all blocks.  Results go to kf (the A operand
+// of the state update) and, with PHI_LDS, to LDS as phi(k)[j][f].
+template <class K, bool PHI_LDS>
+__device__ __forceinline__ void epi_tok(const float* sinv, const float* slg, uint16_t* spk, int fb0, int tb, int lane,
+                                        const float (&c1)[K::FBW], const float (&c0)[K::FBW], const Proj<K>& y,
+                                        bf16x8 (&kf)[K::FBW][K::NTS]) {
+  const int g = lane >> 4, col = lane & 15;
+  const float4 inv4 = *reinterpret_cast<const float4*>(sinv + tb * 16 + 4 * g);
+  const float4 lg4 = *reinterpret_cast<const float4*>(slg + tb * 16 + 4 * g);
+  const float s1[4] = {inv4.x * c1[0], inv4.y * c1[0], inv4.z * c1[0], inv4.w * c1[0]};
+  const float c0p[4] = {c0[0] + lg4.x, c0[0] + lg4.y, c0[0] + lg4.z, c0[0] + lg4.w};
+#pragma unroll
+  for (int j = 0; j < K::FBW; ++j) {
+    {
       float ph[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ph[i] = ya[i] * ya[i] * fast_exp2(fmaf(yg[i], s1[i], c0p[i]));
+      for (int i = 0; i < 4; ++i) ph[i] = y.a[j][i] * y.a[j][i] * fast_exp2(fmaf(y.g[j][i], s1[i], c0p[i]));
       const uint2 pk = pack4(ph[0], ph[1], ph[2], ph[3]);
       // kf[j][s] = (tokens 32s+4g..+3 | 32s+16+4g..+3)
       uint4 cur = __builtin_bit_cast(uint4, kf[j][tb >> 1]);
@@ -352,50 +410,62 @@ __device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, c
   }
 }
 
-// phi(q) of the staged chunk for this wave's features (features as M), to LDS phi(q)[i][f].
+// phi epilogue of a token block projected with features as M, to LDS
+// phi(q)[i][f] with one 8-byte store per lane and block.
+template <class K>
+__device__ __forceinline__ void epi_feat(const float* sinv, const float* slg, uint16_t* spq, int wave, int tb,
+                                         int lane, const float (&c1)[K::FBW], const float (&c0)[K::FBW],
+                                         const Proj<K>& y) {
+  const int g = lane >> 4, col = lane & 15;
+  const float inv = sinv[tb * 16 + col], lg = slg[tb * 16 + col];
+  const float s1 = inv * c1[0], c0p = c0[0] + lg;  // one node per wave, as in epi_tok
+#pragma unroll
+  for (int j = 0; j < K::FBW; ++j) {
+    float ph[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ph[i] = y.a[j][i] * y.a[j][i] * fast_exp2(fmaf(y.g[j][i], s1, c0p));
+    const int f0 = (wave * K::FBW + j) * 16 + 4 * g;
+    *reinterpret_cast<uint2*>(spq + (tb * 16 + col) * K::LDF + f0) = pack4(ph[0], ph[1], ph[2], ph[3]);
+  }
+}
+
+// phi(k) of a staged chunk for this wave's features (tokens as M), software
+// pipelined: the projection MFMAs of block tb+1 are issued before the VALU
+// epilogue of block tb, so the two overlap.  With SU the state update of the
+// previous chunk (from kf_prev and v'^T in sv_prev) is spread over the first
+// NTS steps; it reads kf_prev[.][s] before step s rewrites kf (kf_prev may be
+// the same array as kf).
+template <class K, bool PHI_LDS, bool SU>
+__device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, const float* slg, uint16_t* spk,
+                                        int fb0, int lane, const bf16x8 (&pa)[K::FBW][K::NKS],
+                                        const bf16x8 (&pg)[K::FBW][K::NKS], const float (&c1)[K::FBW],
+                                        const float (&c0)[K::FBW], bf16x8 (&kf)[K::FBW][K::NTS],
+                                        const uint16_t* sv_prev, const RowOff<K, K::LDV>& vo,
+                                        const bf16x8 (&kf_prev)[K::FBW][K::NTS], f32x4 (&st)[K::FBW][K::NE]) {
+  Proj<K> y[2];
+  proj_tok<K>(sx, 0, lane, pa, pg, y[0]);
+#pragma unroll
+  for (int tb = 0; tb < K::NTB; ++tb) {
+    if (tb + 1 < K::NTB) proj_tok<K>(sx, tb + 1, lane, pa, pg, y[(tb + 1) & 1]);
+    if (SU && tb < K::NTS) state_update_step<K>(sv_prev, vo, lane, tb, kf_prev, st);
+    epi_tok<K, PHI_LDS>(sinv, slg, spk, fb0, tb, lane, c1, c0, y[tb & 1], kf);
+  }
+}
+
+// phi(q) of the staged chunk for this wave's features (features as M), to
+// LDS phi(q)[i][f]; pipelined like phase_k.
 template <class K>
 __device__ __forceinline__ void phase_q(const uint16_t* sx, const float* sinv, const float* slg, uint16_t* spq,
                                         int wave, int lane, const bf16x8 (&pa)[K::FBW][K::NKS],
                                         const bf16x8 (&pg)[K::FBW][K::NKS], const float (&c1)[K::FBW],
                                         const float (&c0)[K::FBW]) {
-  const int g = lane >> 4, col = lane & 15;
+  Proj<K> y[2];
+  proj_feat<K>(sx, 0, lane, pa, pg, y[0]);
 #pragma unroll
   for (int tb = 0; tb < K::NTB; ++tb) {
-    bf16x8 xb[K::NKS];
-#pragma unroll
-    for (int ks = 0; ks < K::NKS; ++ks)
-      xb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sx + (tb * 16 + col) * K::LDX + ks * 32 + 8 * g));
-    const float inv = sinv[tb * 16 + col], lg = slg[tb * 16 + col];
-#pragma unroll
-    for (int j = 0; j < K::FBW; ++j) {
-      f32x4 ya = {0.f, 0.f, 0.f, 0.f}, yg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < K::NKS; ++ks) {
-        ya = mfma_bf16(pa[j][ks], xb[ks], ya);
-        yg = mfma_bf16(pg[j][ks], xb[ks], yg);
-      }
-      const float s1 = inv * c1[j], c0p = c0[j] + lg;
-      float ph[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ph[i] = ya[i] * ya[i] * fast_exp2(fmaf(yg[i], s1, c0p));
-      const int f0 = (wave * K::FBW + j) * 16 + 4 * g;
-      *reinterpret_cast<uint2*>(spq + (tb * 16 + col) * K::LDF + f0) = pack4(ph[0], ph[1], ph[2], ph[3]);
-    }
+    if (tb + 1 < K::NTB) proj_feat<K>(sx, tb + 1, lane, pa, pg, y[(tb + 1) & 1]);
+    epi_feat<K>(sinv, slg, spq, wave, tb, lane, c1, c0, y[tb & 1]);
   }
-}
-
-// State update S'[own features] += phi(k)^T v' (tokens contracted).
-template <class K>
-__device__ __forceinline__ void state_update(const uint16_t* sv, const RowOff<K, K::LDV>& vo, int lane,
-                                             const bf16x8 (&kf)[K::FBW][K::NTS], f32x4 (&st)[K::FBW][K::NE]) {
-#pragma unroll
-  for (int s = 0; s < K::NTS; ++s)
-#pragma unroll
-    for (int et = 0; et < K::NE; ++et) {
-      const bf16x8 vb = vfrag<K>(sv, vo, et, s, lane);
-#pragma unroll
-      for (int j = 0; j < K::FBW; ++j) st[j][et] = mfma_bf16(kf[j][s], vb, st[j][et]);
-    }
 }
 
 // Write this wave's S' slice as bf16 rows of S'^T in LDS (value rows and the z row).
@@ -422,7 +492,7 @@ __device__ __forceinline__ int64_t frag_off(int fb, int et, int lane) {
 
 // intra(IB): A^T = phi(k) phi(q)^T on the causal 16x16 blocks (jb, IB),
 // jb <= IB, masked on the diagonal, rounded to bf16 and used in registers as
-// the B-operand of num'^T += v'^T A^T.
+// the B-operand of num'^T += v'^T A^T.  acc starts from zero.
 template <class K, int IB>
 __device__ __forceinline__ void intra_task(const uint16_t* sPq, const uint16_t* sPk, const uint16_t* sVc,
                                            const RowOff<K, K::LDV>& vo, int lane, f32x4 (&acc)[K::NE]) {
@@ -455,13 +525,15 @@ __device__ __forceinline__ void intra_task(const uint16_t* sPq, const uint16_t* 
       }
       const bf16x8 ab = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-      for (int et = 0; et < K::NE; ++et) acc[et] = mfma_bf16(vfrag<K>(sVc, vo, et, s, lane), ab, acc[et]);
+      for (int et = 0; et < K::NE; ++et)
+        acc[et] = mfma_bf16(vfrag<K>(sVc, vo, et, s, lane), ab, s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[et]);
     }
   }
 }
 
-// inter(ib): num'^T += S'^T phi(q)^T from the bf16 copy of S'^T in LDS.
-template <class K>
+// inter(ib): num'^T += S'^T phi(q)^T from the bf16 copy of S'^T in LDS
+// (num'^T = S'^T phi(q)^T when ZERO).
+template <class K, bool ZERO>
 __device__ __forceinline__ void inter_task(const uint16_t* sPq, const uint16_t* sSt, const RowOff<K, K::LDF>& so,
                                            int ib, int lane, f32x4 (&acc)[K::NE]) {
   const int g = lane >> 4, col = lane & 15;
@@ -472,27 +544,26 @@ __device__ __forceinline__ void inter_task(const uint16_t* sPq, const uint16_t* 
 #pragma unroll
     for (int et = 0; et < K::NE; ++et) {
       const bf16x8 as = as_bf16x8(*reinterpret_cast<const uint4*>(sSt + so.off[et] + kf_ * 32 + 8 * g));
-      acc[et] = mfma_bf16(as, bq, acc[et]);
+      acc[et] = mfma_bf16(as, bq, (ZERO && kf_ == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[et]);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// pass 1: per-segment state deltas.  The state of a feature depends only on
-// that feature, so the F features are split over FS workgroups of NW/FS
-// waves each (more, smaller workgroups hide latency better); every one of
-// them stages the whole chunk.  One barrier per chunk: the k tile and v'^T
-// are double-buffered, so staging chunk c+1 runs beside phi(k) and the state
-// update of chunk c.
+// pass 1: per-segment state deltas.  Every workgroup stages the whole chunk;
+// the F features are split over FS workgroups of NW/FS waves.  One barrier
+// per chunk, software pipelined over chunks: step c stages chunk c+1 (loaded
+// one step earlier) and computes phi(k) of chunk c while the state update of
+// chunk c-1 runs beside it, so MFMA and VALU work of two chunks overlap.
+// k tiles are double-buffered, v'^T triple-buffered (chunk c-1 is still read
+// while chunk c+1 is staged), and phi(k) alternates between two register sets.
 template <class K, int FS>
 __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
   constexpr int NT1 = K::NT / FS;
   extern __shared__ __align__(16) unsigned char lds[];
-  auto sK = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * K::kStage1); };
-  auto sV = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * K::kStage1 + K::C * K::LDX * 2); };
-  auto sInv = [&](int b) {
-    return reinterpret_cast<float*>(lds + b * K::kStage1 + K::C * K::LDX * 2 + K::kVbuf);
-  };
+  auto sK = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * K::kKbuf1); };
+  auto sInv = [&](int b) { return reinterpret_cast<float*>(lds + b * K::kKbuf1 + K::C * K::LDX * 2); };
+  auto sV = [&](int b) { return reinterpret_cast<uint16_t*>(lds + 2 * K::kKbuf1 + b * K::kVbuf); };
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nsub = (p.n_seg - 1) * p.sub;  // sub-segments covered by pass 1
@@ -512,32 +583,52 @@ __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
   for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
     for (int et = 0; et < K::NE; ++et) st[j][et] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 kf[K::FBW][K::NTS] = {};
+  // phi(k) of the current and the previous chunk; the "previous" of chunk 0
+  // is zero and meets the zeroed value rows of v'^T buffer 2
+  bf16x8 kfa[K::FBW][K::NTS] = {}, kfb[K::FBW][K::NTS] = {};
   const RowOff<K, K::LDV> vo(lane & 15);
+  for (int t = threadIdx.x; t < K::DV * K::LDV / 2; t += NT1) reinterpret_cast<uint32_t*>(sV(2))[t] = 0u;
   init_vconst<K, NT1>(sV(0));
   init_vconst<K, NT1>(sV(1));
+  init_vconst<K, NT1>(sV(2));
 
   const int64_t sub_len = p.seg_len / p.sub;
   const int64_t t0 = (int64_t)seg * sub_len;
   const int64_t t1 = min<int64_t>(p.L, t0 + sub_len);
   const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
   Prefetch<K, NT1> pf;
-  issue_loads<K, NT1>(p, head, t0, (int)min<int64_t>(K::C, t1 - t0), false, pf);
+  auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
+    const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
+    issue_loads<K, NT1>(p, head, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
+  };
+  load_chunk(0);
   store_x<K, NT1>(pf.k, sK(0), sInv(0), sInv(0) + K::C);
   store_v<K, NT1>(pf.v0, pf.v1, sV(0));
-  if (nch > 1) issue_loads<K, NT1>(p, head, t0 + K::C, (int)min<int64_t>(K::C, t1 - t0 - K::C), false, pf);
+  load_chunk(1);
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
+  // step c: chunk c's phi(k) into kf_cur, chunk c-1's state update from kf_prev
+  auto step = [&](int c, bf16x8(&kf_cur)[K::FBW][K::NTS], const bf16x8(&kf_prev)[K::FBW][K::NTS]) {
+    const int bn = (c + 1) & 1, vn = (c + 1) % 3;
+    store_x<K, NT1>(pf.k, sK(bn), sInv(bn), sInv(bn) + K::C);
+    store_v<K, NT1>(pf.v0, pf.v1, sV(vn));
+    load_chunk(c + 2);
     const int b = c & 1;
-    if (c + 1 < nch) {
-      store_x<K, NT1>(pf.k, sK(b ^ 1), sInv(b ^ 1), sInv(b ^ 1) + K::C);
-      store_v<K, NT1>(pf.v0, pf.v1, sV(b ^ 1));
-      const int64_t c2 = t0 + (int64_t)(c + 2) * K::C;
-      if (c + 2 < nch) issue_loads<K, NT1>(p, head, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
-    }
-    phase_k<K, false>(sK(b), sInv(b), sInv(b) + K::C, nullptr, fb0, lane, pa, pg, c1, c0, kf);
-    state_update<K>(sV(b), vo, lane, kf, st);
+    phase_k<K, false, true>(sK(b), sInv(b), sInv(b) + K::C, nullptr, fb0, lane, pa, pg, c1, c0, kf_cur,
+                            sV((c + 2) % 3), vo, kf_prev, st);
     __syncthreads();
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, kfa, kfb);
+    if (c + 1 < nch) step(c + 1, kfb, kfa);
+  }
+  // state update of the last chunk
+  const uint16_t* sv_last = sV((nch - 1) % 3);
+  if (nch & 1) {
+#pragma unroll
+    for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sv_last, vo, lane, s_, kfa, st);
+  } else {
+#pragma unroll
+    for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sv_last, vo, lane, s_, kfb, st);
   }
   float* out = p.ws + (head * n_items + seg) * (int64_t)K::F * K::DVP;
 #pragma unroll
@@ -552,10 +643,11 @@ __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
 // chunk c:
 //   [X] before: B1(c) -- intra / inter contractions -- beside the staging of
 //       chunk c+1 (q, k tiles, v'^T into the other buffer, loads of c+2);
-//   [Y] before: B2(c) -- output of c, state update with phi(k) of c, refresh
-//       of the S'^T copy -- beside phase A(c+1): phi(k), phi(q) of chunk c+1.
-// B2 is MFMA work and phase A mostly VALU work, placed in one block so the
-// compiler can interleave them.
+//   [Y] before: B2(c) -- output of c, then phase A(c+1): phi(k), phi(q) of
+//       chunk c+1 with the state update by phi(k) of c spread through the
+//       phi(k) pipeline, and the refresh of the S'^T copy.
+// In the last step the staging works on a repeat of the last chunk (its
+// result is never read) and phase A is skipped.
 template <class K>
 __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -632,13 +724,17 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
 
   // prologue: stage chunk 0, phase A of chunk 0
   Prefetch<K> pf;
-  issue_loads<K>(p, head, t0, (int)min<int64_t>(K::C, t1 - t0), true, pf);
+  auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
+    const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
+    issue_loads<K>(p, head, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
+  };
+  load_chunk(0);
   store_x<K>(pf.q, sQ, sinvq, slgq);
   store_x<K>(pf.k, sK, sinvk, slgk);
   store_v<K>(pf.v0, pf.v1, sV(0));
-  if (nch > 1) issue_loads<K>(p, head, t0 + K::C, (int)min<int64_t>(K::C, t1 - t0 - K::C), true, pf);
+  load_chunk(1);
   __syncthreads();
-  phase_k<K, true>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf);
+  phase_k<K, true, false>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf, nullptr, vo, kf, st);
   phase_q<K>(sQ, sinvq, slgq, sPq, wave, lane, pa, pg, c1, c0);
   __syncthreads();
 
@@ -649,9 +745,7 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
     const uint16_t* sVc = sV(b);
 
     // ---- B1(c): contractions; staging of chunk c+1 ----
-    f32x4 acc[K::NE];
-#pragma unroll
-    for (int et = 0; et < K::NE; ++et) acc[et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[K::NE];  // set by the intra task or, on inter waves, the inter task
     switch (role) {  // wave-uniform (scalar) dispatch
       case 0: intra_task<K, 0>(sPq, sPk, sVc, vo, lane, acc); break;
       case 1: intra_task<K, 1>(sPq, sPk, sVc, vo, lane, acc); break;
@@ -659,21 +753,17 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
       case 3: intra_task<K, 3>(sPq, sPk, sVc, vo, lane, acc); break;
       default: break;
     }
-    if (inter_wave || self_inter) {
-      const int ib = inter_wave ? ib_inter : ib_intra;
-      inter_task<K>(sPq, sSt, so, ib, lane, acc);
-      if (inter_wave) {
+    if (inter_wave) {
+      inter_task<K, true>(sPq, sSt, so, ib_inter, lane, acc);
 #pragma unroll
-        for (int et = 0; et < K::NE; ++et) sX[(ib_inter * K::NE + et) * 64 + lane] = acc[et];
-      }
+      for (int et = 0; et < K::NE; ++et) sX[(ib_inter * K::NE + et) * 64 + lane] = acc[et];
+    } else if (self_inter) {
+      inter_task<K, false>(sPq, sSt, so, ib_intra, lane, acc);
     }
-    if (c + 1 < nch) {
-      store_x<K>(pf.q, sQ, sinvq, slgq);
-      store_x<K>(pf.k, sK, sinvk, slgk);
-      store_v<K>(pf.v0, pf.v1, sV(b ^ 1));
-      const int64_t c2 = c0t + 2 * K::C;
-      if (c + 2 < nch) issue_loads<K>(p, head, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
-    }
+    store_x<K>(pf.q, sQ, sinvq, slgq);
+    store_x<K>(pf.k, sK, sinvk, slgk);
+    store_v<K>(pf.v0, pf.v1, sV(b ^ 1));
+    load_chunk(c + 2);
     __syncthreads();  // X
 
     // ---- B2(c): output and state update; phase A(c+1) ----
@@ -695,11 +785,13 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
               pack4(acc[et][0] * rden, acc[et][1] * rden, acc[et][2] * rden, acc[et][3] * rden);
       }
     }
-    state_update<K>(sVc, vo, lane, kf, st);
-    write_st<K>(sSt, so, wave, lane, st);
     if (c + 1 < nch) {
-      phase_k<K, true>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf);
+      phase_k<K, true, true>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf, sVc, vo, kf, st);
+      write_st<K>(sSt, so, wave, lane, st);
       phase_q<K>(sQ, sinvq, slgq, sPq, wave, lane, pa, pg, c1, c0);
+    } else {  // last chunk: its state update only
+#pragma unroll
+      for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sVc, vo, lane, s_, kf, st);
     }
     __syncthreads();  // Y
   }

@@ -9,13 +9,15 @@
 //
 // Kernel shape: a 256-thread workgroup owns a slice of 64*FBW features for
 // the whole launch and keeps that slice of the projection matrix
-// P = [anchors | prf] in registers as MFMA A-operands (64 VGPRs).  It walks
-// 64-row tiles of x: stages the tile in LDS (padded rows, so the per-lane
+// P = [anchors | prf] in registers as MFMA A-operands.  It walks row tiles
+// of x (64 rows; 16 or 32 for small launches such as a decode step's one
+// row per head): stages the tile in LDS (padded rows, so the per-lane
 // 16-byte reads are bank-conflict free), computes 1/|x| per row, then per
 // 16-token block runs Y^T = P_slice x^T on 16x16 MFMA tiles and applies the
 // square / exp2 / scale epilogue straight from the accumulators.  The 1/|x|
 // scale is applied to the fp32 accumulator, (x/|x|).P = (x.P)/|x|, so bf16
-// inputs are never rounded twice.
+// inputs are never rounded twice.  The tile's features are written back from
+// an LDS staging copy with coalesced 16-byte stores.
 #include "slay_device.hpp"
 #include "slay_internal.hpp"
 
@@ -23,7 +25,7 @@ namespace slay {
 
 namespace {
 
-constexpr int kTileRows = 64;
+constexpr int kTileRows = 64;  // rows per tile of large launches
 constexpr int kThreads = 256;
 
 template <typename TI>
@@ -47,7 +49,7 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, 
   *reinterpret_cast<uint2*>(p) = v;
 }
 
-template <typename TI, typename TO, int D, int FBW>
+template <typename TI, typename TO, int D, int FBW, int TR>
 __global__ __launch_bounds__(kThreads) void featmap_kernel(
     const TI* __restrict__ x_a, const TI* __restrict__ x_b, int64_t rows_per_head, int64_t n_heads,
     const TI* __restrict__ anchors, const TI* __restrict__ prf, int64_t draw_set_stride, int n_draw_sets, int F,
@@ -61,13 +63,13 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
   constexpr int VEC = 16 / sizeof(TI);       // elements per 16-byte vector
   constexpr int VPR = D / VEC;               // 16-byte vectors per row
   static_assert(D % M::K == 0, "d must be a multiple of the MFMA k-step");
-  static_assert((kTileRows * VPR) % kThreads == 0, "tile staging must divide evenly");
+  static_assert((TR * VPR) % kThreads == 0 && TR % 16 == 0, "tile staging must divide evenly");
 
   constexpr int FWS = 4 * FBW * 16;              // features per workgroup slice
   constexpr int LDO = FWS + 16 / sizeof(TO);      // padded output staging stride
-  __shared__ __align__(16) TI sx[kTileRows * LDX];
-  __shared__ __align__(16) TO so[kTileRows * LDO];
-  __shared__ float sinv[kTileRows], slg[kTileRows];
+  __shared__ __align__(16) TI sx[TR * LDX];
+  __shared__ __align__(16) TO so[TR * LDO];
+  __shared__ float sinv[TR], slg[TR];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
   const int n_fblk = F / 16;
   const int fblk0 = blockIdx.y * (4 * FBW) + wave * FBW;
 
-  const int tiles_per_head = (int)((rows_per_head + kTileRows - 1) / kTileRows);
+  const int tiles_per_head = (int)((rows_per_head + TR - 1) / TR);
   const int n_tiles = tiles_per_head * (int)n_heads;
 
   typename M::frag pa[FBW][KS], pg[FBW][KS];
@@ -84,13 +86,13 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
 
   // x tile vectors of the next tile are loaded into registers while the
   // current tile is computed (one tile of prefetch)
-  constexpr int PER_T = kTileRows * VPR / kThreads;
-  constexpr int TPR = kThreads / kTileRows;  // threads per row (4); a thread's vectors lie in one row
+  constexpr int PER_T = TR * VPR / kThreads;
+  constexpr int TPR = kThreads / TR;  // threads per row; a thread's vectors lie in one row
   uint4 xr[PER_T];
   auto load_tile = [&](int tt) {
     const int hh = tt / tiles_per_head;
-    const int64_t r0 = (int64_t)(tt - hh * tiles_per_head) * kTileRows;
-    const int64_t nr = min<int64_t>(kTileRows, rows_per_head - r0);
+    const int64_t r0 = (int64_t)(tt - hh * tiles_per_head) * TR;
+    const int64_t nr = min<int64_t>(TR, rows_per_head - r0);
     const TI* src = x + ((int64_t)hh * rows_per_head + r0) * D;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
 
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int h = t / tiles_per_head;
-    const int64_t row0 = (int64_t)(t - h * tiles_per_head) * kTileRows;  // row within head
-    const int64_t nrow = min<int64_t>(kTileRows, rows_per_head - row0);
+    const int64_t row0 = (int64_t)(t - h * tiles_per_head) * TR;  // row within head
+    const int64_t nrow = min<int64_t>(TR, rows_per_head - row0);
     TO* pt = phi + ((int64_t)h * rows_per_head + row0) * (int64_t)F;
 
     // (re)load this wave's slice of P when the draw set changes
@@ -119,10 +121,23 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
       for (int j = 0; j < FBW; ++j) {
         const int fb = min(fblk0 + j, n_fblk - 1);
         const int64_t rowoff = (int64_t)(fb * 16 + col) * D;
+        if constexpr (sizeof(TI) == 4) {
+          // fp32: lane group g owns d in [g D/4, (g+1) D/4), k-step ks its
+          // ks-th element (the x operand below uses the same order, so the
+          // sum over d is unchanged); one lane's operands are contiguous
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          pa[j][ks] = M::load(a + rowoff + ks * M::K + M::KL * g);
-          pg[j][ks] = M::load(gg + rowoff + ks * M::K + M::KL * g);
+          for (int q = 0; q < KS / 4; ++q) {
+            const float4 va = *reinterpret_cast<const float4*>(a + rowoff + g * KS + 4 * q);
+            const float4 vg = *reinterpret_cast<const float4*>(gg + rowoff + g * KS + 4 * q);
+            pa[j][4 * q] = va.x, pa[j][4 * q + 1] = va.y, pa[j][4 * q + 2] = va.z, pa[j][4 * q + 3] = va.w;
+            pg[j][4 * q] = vg.x, pg[j][4 * q + 1] = vg.y, pg[j][4 * q + 2] = vg.z, pg[j][4 * q + 3] = vg.w;
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            pa[j][ks] = M::load(a + rowoff + ks * M::K + M::KL * g);
+            pg[j][ks] = M::load(gg + rowoff + ks * M::K + M::KL * g);
+          }
         }
       }
     }
@@ -153,20 +168,30 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
     if (t + (int)gridDim.x < n_tiles) load_tile(t + gridDim.x);
 
 #pragma unroll
-    for (int tb = 0; tb < kTileRows / 16; ++tb) {
+    for (int tb = 0; tb < TR / 16; ++tb) {
       f32x4 ya[FBW], yg[FBW];
 #pragma unroll
       for (int j = 0; j < FBW; ++j) {
         ya[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         yg[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      typename M::frag b[KS];
+      if constexpr (sizeof(TI) == 4) {  // the permuted fp32 order of the P operands
+#pragma unroll
+        for (int q = 0; q < KS / 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(&sx[(tb * 16 + col) * LDX + g * KS + 4 * q]);
+          b[4 * q] = v.x, b[4 * q + 1] = v.y, b[4 * q + 2] = v.z, b[4 * q + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) b[ks] = M::load(&sx[(tb * 16 + col) * LDX + ks * M::K + M::KL * g]);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const typename M::frag b = M::load(&sx[(tb * 16 + col) * LDX + ks * M::K + M::KL * g]);
 #pragma unroll
         for (int j = 0; j < FBW; ++j) {
-          ya[j] = M::mma(pa[j][ks], b, ya[j]);
-          yg[j] = M::mma(pg[j][ks], b, yg[j]);
+          ya[j] = M::mma(pa[j][ks], b[ks], ya[j]);
+          yg[j] = M::mma(pg[j][ks], b[ks], yg[j]);
         }
       }
       const int r = tb * 16 + col;  // token of this lane's C column
@@ -190,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
       constexpr int PPR = FWS * (int)sizeof(TO) / 16;  // 16-byte pieces per row of the slice
       const int fcols = min(FWS, F - (int)blockIdx.y * FWS);
       const int ppr = fcols * (int)sizeof(TO) / 16;
-      for (int pc = threadIdx.x; pc < kTileRows * PPR; pc += kThreads) {
+      for (int pc = threadIdx.x; pc < TR * PPR; pc += kThreads) {
         const int rr = pc / PPR, q = pc - (pc / PPR) * PPR;
         if (rr < nrow && q < ppr)
           *reinterpret_cast<uint4*>(reinterpret_cast<char*>(pt + (int64_t)rr * F + blockIdx.y * FWS) + q * 16) =
@@ -201,34 +226,50 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
   }
 }
 
-template <typename TI, typename TO, int D, int FBW>
+template <typename TI, typename TO, int D, int FBW, int TR>
 hipError_t launch_t(const FeatmapArgs& a, hipStream_t s) {
   const int FW = 4 * FBW * 16;
   const int gy = (a.F + FW - 1) / FW;
-  const int64_t tiles = ((a.rows_per_head + kTileRows - 1) / kTileRows) * a.n_heads;
+  const int64_t tiles = ((a.rows_per_head + TR - 1) / TR) * a.n_heads;
   int64_t gx = 2048 / gy;
   if (gx < 1) gx = 1;
   if (gx > tiles) gx = tiles;
   if (tiles == 0) return hipSuccess;
   const int gz = a.x2 ? 2 : 1;
-  hipLaunchKernelGGL((featmap_kernel<TI, TO, D, FBW>), dim3((unsigned)gx, gy, gz), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((featmap_kernel<TI, TO, D, FBW, TR>), dim3((unsigned)gx, gy, gz), dim3(kThreads), 0, s,
                      static_cast<const TI*>(a.x), static_cast<const TI*>(a.x2), a.rows_per_head, a.n_heads,
                      static_cast<const TI*>(a.anchors), static_cast<const TI*>(a.prf), a.draw_set_stride,
                      a.n_draw_sets, a.F, a.m, a.nc, static_cast<TO*>(a.phi), static_cast<TO*>(a.phi2));
   return hipGetLastError();
 }
 
+// Row tile of small launches: the smallest of (kSmallRows, 32, 64) whose
+// staging divides evenly over the workgroup.
+constexpr int kSmallRows = 64;
+template <typename TI, int D>
+constexpr int small_tile_rows() {
+  constexpr int vpr = D / (16 / (int)sizeof(TI));
+  return (kSmallRows <= 16 && (16 * vpr) % kThreads == 0)   ? 16
+         : (kSmallRows <= 32 && (32 * vpr) % kThreads == 0) ? 32
+                                                            : 64;
+}
+
 template <typename TI, typename TO>
 hipError_t launch_d(const FeatmapArgs& a, hipStream_t s) {
   constexpr bool bf = sizeof(TI) == 2;
-  // Few row tiles (e.g. one decode token per head): narrower feature slices
-  // per workgroup give more workgroups to hide load latency.
-  const int64_t tiles = ((a.rows_per_head + kTileRows - 1) / kTileRows) * a.n_heads * (a.x2 ? 2 : 1);
-  const bool small = tiles * ((a.F + 127) / 128) < 1024;
+  // Few rows (e.g. one decode token per head): one feature block per wave and
+  // short row tiles give many small workgroups, so the dependent MFMA chains
+  // of different tiles run side by side.
+  const int64_t rows = a.rows_per_head * a.n_heads * (a.x2 ? 2 : 1);
+  const bool small = ((rows + kTileRows - 1) / kTileRows) * ((a.F + 127) / 128) < 1024;
   switch (a.d) {
-    case 32: return small ? launch_t<TI, TO, 32, 1>(a, s) : launch_t<TI, TO, 32, 4>(a, s);
-    case 64: return small ? launch_t<TI, TO, 64, 1>(a, s) : launch_t<TI, TO, 64, 2>(a, s);
-    case 128: return small ? launch_t<TI, TO, 128, 1>(a, s) : launch_t<TI, TO, 128, bf ? 2 : 1>(a, s);
+    case 32:
+      return small ? launch_t<TI, TO, 32, 1, small_tile_rows<TI, 32>()>(a, s) : launch_t<TI, TO, 32, 4, kTileRows>(a, s);
+    case 64:
+      return small ? launch_t<TI, TO, 64, 1, small_tile_rows<TI, 64>()>(a, s) : launch_t<TI, TO, 64, 2, kTileRows>(a, s);
+    case 128:
+      return small ? launch_t<TI, TO, 128, 1, small_tile_rows<TI, 128>()>(a, s)
+                   : launch_t<TI, TO, 128, bf ? 2 : 1, kTileRows>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -19,6 +19,22 @@ def rownorm_rel(got, ref) -> float:
     return float(np.max(num / np.maximum(den, 1e-300)))
 
 
+def headnorm_rel(got, ref) -> float:
+    """Max over heads (leading axis) of the relative Frobenius error of one head's array.
+
+    Used for recurrent states after few tokens: a state row of feature f is
+    then a handful of phi_f values, whose fp32 relative error is unbounded
+    where (a.xh)^2 cancels (a nearly orthogonal to xh), so a per-row ratio is
+    ill-posed the same way an elementwise one is; the head's whole state is
+    the well-conditioned unit.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    g = got.reshape(got.shape[0], -1)
+    r = ref.reshape(ref.shape[0], -1)
+    return float(np.max(np.linalg.norm(g - r, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-300)))
+
+
 def elem_rel(got, ref, floor_frac=1e-3) -> float:
     """Elementwise relative error with a floor of floor_frac * rms(ref) (reported, not gated)."""
     got = np.asarray(got, dtype=np.float64)
