@@ -40,6 +40,8 @@
 // an MFMA k-step (lane group g holds tokens 4g..4g+3 and 16+4g..16+4g+3) on
 // both operands, which leaves the sum unchanged and lets accumulators feed
 // the next MFMA without a transpose.
+#include <type_traits>
+
 #include "slay_device.hpp"
 #include "slay_internal.hpp"
 
@@ -86,6 +88,8 @@ struct Cfg {
   static constexpr int kLds1 = 2 * kKbuf1 + 3 * kVbuf;
   // pass 1 splits the features over FS1 workgroups of NW / FS1 waves
   static constexpr int FS1 = 1;
+  // phi projections of block tb+1 issued before the epilogue of block tb
+  static constexpr bool PIPE = true;
 };
 
 struct Params {
@@ -186,11 +190,12 @@ struct Prefetch {
 };
 
 template <class K, int NT = K::NT>
-__device__ __forceinline__ void load_x(const uint16_t* __restrict__ x, int n, uint4 (&r)[Prefetch<K, NT>::XV]) {
+__device__ __forceinline__ void load_x(int tid, const uint16_t* __restrict__ x, int n,
+                                       uint4 (&r)[Prefetch<K, NT>::XV]) {
   constexpr int VPR = K::D / 8;
 #pragma unroll
   for (int i = 0; i < Prefetch<K, NT>::XV; ++i) {
-    const int vec = threadIdx.x + i * NT;
+    const int vec = tid + i * NT;
     const int row = vec / VPR, c = (vec % VPR) * 8;
     r[i] = make_uint4(0, 0, 0, 0);
     if (vec < K::C * VPR && row < n) r[i] = *reinterpret_cast<const uint4*>(x + (int64_t)row * K::D + c);
@@ -198,12 +203,12 @@ __device__ __forceinline__ void load_x(const uint16_t* __restrict__ x, int n, ui
 }
 
 template <class K, int NT = K::NT>
-__device__ __forceinline__ void load_v(const uint16_t* __restrict__ v, int n, uint2 (&r0)[Prefetch<K, NT>::VV],
+__device__ __forceinline__ void load_v(int tid, const uint16_t* __restrict__ v, int n, uint2 (&r0)[Prefetch<K, NT>::VV],
                                        uint2 (&r1)[Prefetch<K, NT>::VV]) {
   constexpr int HP = K::C / 2;  // token pairs
 #pragma unroll
   for (int i = 0; i < Prefetch<K, NT>::VV; ++i) {
-    const int item = threadIdx.x + i * NT;
+    const int item = tid + i * NT;
     const int rp = item % HP, e4 = item / HP;
     r0[i] = make_uint2(0, 0);
     r1[i] = make_uint2(0, 0);
@@ -215,11 +220,11 @@ __device__ __forceinline__ void load_v(const uint16_t* __restrict__ v, int n, ui
 }
 
 template <class K, int NT = K::NT>
-__device__ __forceinline__ void issue_loads(const Params& p, int64_t head, int64_t c0t, int n, bool want_q,
+__device__ __forceinline__ void issue_loads(int tid, const Params& p, int64_t head, int64_t c0t, int n, bool want_q,
                                             Prefetch<K, NT>& pf) {
-  if (want_q) load_x<K, NT>(p.q + (head * p.L + c0t) * K::D, n, pf.q);
-  load_x<K, NT>(p.k + (head * p.L + c0t) * K::D, n, pf.k);
-  load_v<K, NT>(p.v + (head * p.L + c0t) * K::DV, n, pf.v0, pf.v1);
+  if (want_q) load_x<K, NT>(tid, p.q + (head * p.L + c0t) * K::D, n, pf.q);
+  load_x<K, NT>(tid, p.k + (head * p.L + c0t) * K::D, n, pf.k);
+  load_v<K, NT>(tid, p.v + (head * p.L + c0t) * K::DV, n, pf.v0, pf.v1);
 }
 
 // Write staged q or k vectors to LDS (padded rows) with, per row,
@@ -227,13 +232,13 @@ __device__ __forceinline__ void issue_loads(const Params& p, int64_t head, int64
 // the bf16 dot instruction (products of bf16 values are exact in fp32) and
 // inv comes from the hardware reciprocal square root (about 1 ulp).
 template <class K, int NT = K::NT>
-__device__ __forceinline__ void store_x(const uint4 (&r)[Prefetch<K, NT>::XV], uint16_t* sx, float* sinv,
+__device__ __forceinline__ void store_x(int tid, const uint4 (&r)[Prefetch<K, NT>::XV], uint16_t* sx, float* sinv,
                                         float* slg) {
   constexpr int VPR = K::D / 8;  // 16-byte vectors per row, consecutive threads
   static_assert((NT % VPR) == 0 && (VPR == 4 || VPR == 8 || VPR == 16), "rows must not straddle lane groups");
 #pragma unroll
   for (int i = 0; i < Prefetch<K, NT>::XV; ++i) {
-    const int vec = threadIdx.x + i * NT;
+    const int vec = tid + i * NT;
     if (vec >= K::C * VPR) break;  // uniform over whole waves
     const int row = vec / VPR, c = (vec % VPR) * 8;
     *reinterpret_cast<uint4*>(sx + row * K::LDX + c) = r[i];
@@ -256,12 +261,12 @@ __device__ __forceinline__ void store_x(const uint4 (&r)[Prefetch<K, NT>::XV], u
 // Write staged v transposed into v'^T rows 0..DV-1: each thread packs the
 // same 4 columns of two consecutive tokens into four 32-bit words.
 template <class K, int NT = K::NT>
-__device__ __forceinline__ void store_v(const uint2 (&r0)[Prefetch<K, NT>::VV],
+__device__ __forceinline__ void store_v(int tid, const uint2 (&r0)[Prefetch<K, NT>::VV],
                                         const uint2 (&r1)[Prefetch<K, NT>::VV], uint16_t* sv) {
   constexpr int HP = K::C / 2;
 #pragma unroll
   for (int i = 0; i < Prefetch<K, NT>::VV; ++i) {
-    const int item = threadIdx.x + i * NT;
+    const int item = tid + i * NT;
     if (item >= HP * (K::DV / 4)) break;
     const int rp = item % HP, e4 = item / HP;
     uint32_t* dst = reinterpret_cast<uint32_t*>(sv + (4 * e4) * K::LDV + 2 * rp);
@@ -274,8 +279,8 @@ __device__ __forceinline__ void store_v(const uint2 (&r0)[Prefetch<K, NT>::VV],
 
 // Constant rows of a v'^T buffer: row DV all ones (the z column), row DV+1 zero.
 template <class K, int NT = K::NT>
-__device__ __forceinline__ void init_vconst(uint16_t* sv) {
-  for (int t = threadIdx.x; t < 2 * K::LDV; t += NT)
+__device__ __forceinline__ void init_vconst(int tid, uint16_t* sv) {
+  for (int t = tid; t < 2 * K::LDV; t += NT)
     sv[K::DV * K::LDV + t] = (t < K::LDV) ? kBf16One : (uint16_t)0;
 }
 
@@ -442,13 +447,23 @@ __device__ __forceinline__ void phase_k(const uint16_t* sx, const float* sinv, c
                                         const float (&c0)[K::FBW], bf16x8 (&kf)[K::FBW][K::NTS],
                                         const uint16_t* sv_prev, const RowOff<K, K::LDV>& vo,
                                         const bf16x8 (&kf_prev)[K::FBW][K::NTS], f32x4 (&st)[K::FBW][K::NE]) {
-  Proj<K> y[2];
-  proj_tok<K>(sx, 0, lane, pa, pg, y[0]);
+  if constexpr (K::PIPE) {
+    Proj<K> y[2];
+    proj_tok<K>(sx, 0, lane, pa, pg, y[0]);
 #pragma unroll
-  for (int tb = 0; tb < K::NTB; ++tb) {
-    if (tb + 1 < K::NTB) proj_tok<K>(sx, tb + 1, lane, pa, pg, y[(tb + 1) & 1]);
-    if (SU && tb < K::NTS) state_update_step<K>(sv_prev, vo, lane, tb, kf_prev, st);
-    epi_tok<K, PHI_LDS>(sinv, slg, spk, fb0, tb, lane, c1, c0, y[tb & 1], kf);
+    for (int tb = 0; tb < K::NTB; ++tb) {
+      if (tb + 1 < K::NTB) proj_tok<K>(sx, tb + 1, lane, pa, pg, y[(tb + 1) & 1]);
+      if (SU && tb < K::NTS) state_update_step<K>(sv_prev, vo, lane, tb, kf_prev, st);
+      epi_tok<K, PHI_LDS>(sinv, slg, spk, fb0, tb, lane, c1, c0, y[tb & 1], kf);
+    }
+  } else {  // one block at a time (fewer live registers)
+#pragma unroll
+    for (int tb = 0; tb < K::NTB; ++tb) {
+      Proj<K> y;
+      proj_tok<K>(sx, tb, lane, pa, pg, y);
+      if (SU && tb < K::NTS) state_update_step<K>(sv_prev, vo, lane, tb, kf_prev, st);
+      epi_tok<K, PHI_LDS>(sinv, slg, spk, fb0, tb, lane, c1, c0, y, kf);
+    }
   }
 }
 
@@ -459,12 +474,21 @@ __device__ __forceinline__ void phase_q(const uint16_t* sx, const float* sinv, c
                                         int wave, int lane, const bf16x8 (&pa)[K::FBW][K::NKS],
                                         const bf16x8 (&pg)[K::FBW][K::NKS], const float (&c1)[K::FBW],
                                         const float (&c0)[K::FBW]) {
-  Proj<K> y[2];
-  proj_feat<K>(sx, 0, lane, pa, pg, y[0]);
+  if constexpr (K::PIPE) {
+    Proj<K> y[2];
+    proj_feat<K>(sx, 0, lane, pa, pg, y[0]);
 #pragma unroll
-  for (int tb = 0; tb < K::NTB; ++tb) {
-    if (tb + 1 < K::NTB) proj_feat<K>(sx, tb + 1, lane, pa, pg, y[(tb + 1) & 1]);
-    epi_feat<K>(sinv, slg, spq, wave, tb, lane, c1, c0, y[tb & 1]);
+    for (int tb = 0; tb < K::NTB; ++tb) {
+      if (tb + 1 < K::NTB) proj_feat<K>(sx, tb + 1, lane, pa, pg, y[(tb + 1) & 1]);
+      epi_feat<K>(sinv, slg, spq, wave, tb, lane, c1, c0, y[tb & 1]);
+    }
+  } else {
+#pragma unroll
+    for (int tb = 0; tb < K::NTB; ++tb) {
+      Proj<K> y;
+      proj_feat<K>(sx, tb, lane, pa, pg, y);
+      epi_feat<K>(sinv, slg, spq, wave, tb, lane, c1, c0, y);
+    }
   }
 }
 
@@ -488,6 +512,63 @@ __device__ __forceinline__ void write_st(uint16_t* sst, const RowOff<K, K::LDF>&
 template <class K>
 __device__ __forceinline__ int64_t frag_off(int fb, int et, int lane) {
   return ((int64_t)(fb * K::NE + et) * 64 + lane) * 4;
+}
+
+// Initial state of segment seg for the wave's feature blocks fb0..fb0+FBW-1:
+// the scanned prefix from the workspace, or S0/z0 (zero when absent) when the
+// head is one segment.
+template <class K>
+__device__ __forceinline__ void load_state(const Params& p, int64_t head, int seg, int fb0, int lane,
+                                           f32x4 (&st)[K::FBW][K::NE]) {
+  const int g = lane >> 4, col = lane & 15;
+  if (p.n_seg > 1) {
+    const int64_t n_items = (int64_t)(p.n_seg - 1) * p.sub + 1;
+    const float* in = p.ws + (head * n_items + (int64_t)seg * p.sub) * (int64_t)K::F * K::DVP;
+#pragma unroll
+    for (int j = 0; j < K::FBW; ++j)
+#pragma unroll
+      for (int et = 0; et < K::NE; ++et) st[j][et] = *reinterpret_cast<const f32x4*>(in + frag_off<K>(fb0 + j, et, lane));
+  } else {
+#pragma unroll
+    for (int j = 0; j < K::FBW; ++j)
+#pragma unroll
+      for (int et = 0; et < K::NE; ++et) {
+        const int e = et * 16 + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = (fb0 + j) * 16 + 4 * g + i;
+          float val = 0.f;
+          if (e < K::DV) {
+            if (p.S0) val = p.S0[(head * K::F + f) * K::DV + e];
+          } else if (e == K::DV) {
+            if (p.z0) val = p.z0[head * K::F + f];
+          }
+          st[j][et][i] = val;
+        }
+      }
+  }
+}
+
+// Final state of the head (last segment only) for the wave's feature blocks.
+template <class K>
+__device__ __forceinline__ void store_state_out(const Params& p, int64_t head, int fb0, int lane,
+                                                const f32x4 (&st)[K::FBW][K::NE]) {
+  const int g = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int j = 0; j < K::FBW; ++j)
+#pragma unroll
+    for (int et = 0; et < K::NE; ++et) {
+      const int e = et * 16 + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = (fb0 + j) * 16 + 4 * g + i;
+        if (e < K::DV) {
+          if (p.S_out) p.S_out[(head * K::F + f) * K::DV + e] = st[j][et][i];
+        } else if (e == K::DV) {
+          if (p.z_out) p.z_out[head * K::F + f] = st[j][et][i];
+        }
+      }
+    }
 }
 
 // intra(IB): A^T = phi(k) phi(q)^T on the causal 16x16 blocks (jb, IB),
@@ -588,9 +669,9 @@ __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
   bf16x8 kfa[K::FBW][K::NTS] = {}, kfb[K::FBW][K::NTS] = {};
   const RowOff<K, K::LDV> vo(lane & 15);
   for (int t = threadIdx.x; t < K::DV * K::LDV / 2; t += NT1) reinterpret_cast<uint32_t*>(sV(2))[t] = 0u;
-  init_vconst<K, NT1>(sV(0));
-  init_vconst<K, NT1>(sV(1));
-  init_vconst<K, NT1>(sV(2));
+  init_vconst<K, NT1>(threadIdx.x, sV(0));
+  init_vconst<K, NT1>(threadIdx.x, sV(1));
+  init_vconst<K, NT1>(threadIdx.x, sV(2));
 
   const int64_t sub_len = p.seg_len / p.sub;
   const int64_t t0 = (int64_t)seg * sub_len;
@@ -599,18 +680,18 @@ __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
   Prefetch<K, NT1> pf;
   auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
     const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-    issue_loads<K, NT1>(p, head, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
+    issue_loads<K, NT1>(threadIdx.x, p, head, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
   };
   load_chunk(0);
-  store_x<K, NT1>(pf.k, sK(0), sInv(0), sInv(0) + K::C);
-  store_v<K, NT1>(pf.v0, pf.v1, sV(0));
+  store_x<K, NT1>(threadIdx.x, pf.k, sK(0), sInv(0), sInv(0) + K::C);
+  store_v<K, NT1>(threadIdx.x, pf.v0, pf.v1, sV(0));
   load_chunk(1);
   __syncthreads();
   // step c: chunk c's phi(k) into kf_cur, chunk c-1's state update from kf_prev
   auto step = [&](int c, bf16x8(&kf_cur)[K::FBW][K::NTS], const bf16x8(&kf_prev)[K::FBW][K::NTS]) {
     const int bn = (c + 1) & 1, vn = (c + 1) % 3;
-    store_x<K, NT1>(pf.k, sK(bn), sInv(bn), sInv(bn) + K::C);
-    store_v<K, NT1>(pf.v0, pf.v1, sV(vn));
+    store_x<K, NT1>(threadIdx.x, pf.k, sK(bn), sInv(bn), sInv(bn) + K::C);
+    store_v<K, NT1>(threadIdx.x, pf.v0, pf.v1, sV(vn));
     load_chunk(c + 2);
     const int b = c & 1;
     phase_k<K, false, true>(sK(b), sInv(b), sInv(b) + K::C, nullptr, fb0, lane, pa, pg, c1, c0, kf_cur,
@@ -673,37 +754,10 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
   float c1[K::FBW], c0[K::FBW];
   load_p<K>(p, set, wave * K::FBW, lane, pa, pg, c1, c0);
 
-  // initial state of the segment
   f32x4 st[K::FBW][K::NE];
-  if (p.n_seg > 1) {
-    const int64_t n_items = (int64_t)(p.n_seg - 1) * p.sub + 1;
-    const float* in = p.ws + (head * n_items + (int64_t)seg * p.sub) * (int64_t)K::F * K::DVP;
-#pragma unroll
-    for (int j = 0; j < K::FBW; ++j)
-#pragma unroll
-      for (int et = 0; et < K::NE; ++et)
-        st[j][et] = *reinterpret_cast<const f32x4*>(in + frag_off<K>(wave * K::FBW + j, et, lane));
-  } else {
-#pragma unroll
-    for (int j = 0; j < K::FBW; ++j)
-#pragma unroll
-      for (int et = 0; et < K::NE; ++et) {
-        const int e = et * 16 + col;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int f = (wave * K::FBW + j) * 16 + 4 * g + i;
-          float val = 0.f;
-          if (e < K::DV) {
-            if (p.S0) val = p.S0[(head * K::F + f) * K::DV + e];
-          } else if (e == K::DV) {
-            if (p.z0) val = p.z0[head * K::F + f];
-          }
-          st[j][et][i] = val;
-        }
-      }
-  }
-  init_vconst<K>(sV(0));
-  init_vconst<K>(sV(1));
+  load_state<K>(p, head, seg, wave * K::FBW, lane, st);
+  init_vconst<K>(threadIdx.x, sV(0));
+  init_vconst<K>(threadIdx.x, sV(1));
   // the zero row of the S'^T copy (padding columns DV+1..DV+15)
   for (int t = threadIdx.x; t < K::LDF; t += K::NT) sSt[(K::DV + 1) * K::LDF + t] = 0;
   const RowOff<K, K::LDV> vo(col);
@@ -726,12 +780,12 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
   Prefetch<K> pf;
   auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
     const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-    issue_loads<K>(p, head, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
+    issue_loads<K>(threadIdx.x, p, head, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
   };
   load_chunk(0);
-  store_x<K>(pf.q, sQ, sinvq, slgq);
-  store_x<K>(pf.k, sK, sinvk, slgk);
-  store_v<K>(pf.v0, pf.v1, sV(0));
+  store_x<K>(threadIdx.x, pf.q, sQ, sinvq, slgq);
+  store_x<K>(threadIdx.x, pf.k, sK, sinvk, slgk);
+  store_v<K>(threadIdx.x, pf.v0, pf.v1, sV(0));
   load_chunk(1);
   __syncthreads();
   phase_k<K, true, false>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf, nullptr, vo, kf, st);
@@ -760,9 +814,9 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
     } else if (self_inter) {
       inter_task<K, false>(sPq, sSt, so, ib_intra, lane, acc);
     }
-    store_x<K>(pf.q, sQ, sinvq, slgq);
-    store_x<K>(pf.k, sK, sinvk, slgk);
-    store_v<K>(pf.v0, pf.v1, sV(b ^ 1));
+    store_x<K>(threadIdx.x, pf.q, sQ, sinvq, slgq);
+    store_x<K>(threadIdx.x, pf.k, sK, sinvk, slgk);
+    store_v<K>(threadIdx.x, pf.v0, pf.v1, sV(b ^ 1));
     load_chunk(c + 2);
     __syncthreads();  // X
 
@@ -796,24 +850,249 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
     __syncthreads();  // Y
   }
 
-  if (seg == p.n_seg - 1 && (p.S_out || p.z_out)) {
+  if (seg == p.n_seg - 1 && (p.S_out || p.z_out)) store_state_out<K>(p, head, wave * K::FBW, lane, st);
+}
+
+// ---------------------------------------------------------------------------
+// Warp-specialized main pass.  NP producer waves own the features (their
+// slice of P and of the state S' in registers) and NC = 4 consumer waves own
+// the contractions, so the feature map (VALU) of chunk c+1 runs beside the
+// contractions (MFMA and LDS) of chunk c.  phi(q), phi(k) are double-buffered
+// in LDS, the staged q, k tiles double- and v'^T triple-buffered.  Per chunk:
+//   [A] consumers: intra + inter of chunk c for their (token block, column
+//       half), staging of chunk c+2, loads of chunk c+3; producers: phi(k),
+//       phi(q) of chunk c+1 with the state update by chunk c spread through
+//       the phi(k) pipeline;
+//   [B] producers refresh the bf16 S'^T copy; consumers of the first column
+//       half write their outputs (the denominator comes from the other half).
+template <int D_, int DV_, int NP_, int FBW_>
+struct CfgS : Cfg<D_, DV_, 32, NP_, FBW_> {
+  using B = Cfg<D_, DV_, 32, NP_, FBW_>;
+  static constexpr int NP = NP_, NC = 4;
+  static constexpr bool PIPE = false;  // consumers run beside the producers; keep registers low
+  static constexpr int NTW = (NP + NC) * 64;           // threads
+  static constexpr int ESPLIT = (B::NE + 1) / 2;       // column tiles [0, ESPLIT) | [ESPLIT, NE)
+  static constexpr int kXt = B::C * B::LDX * 2;        // one staged x tile (bytes)
+  static constexpr int kPt = B::C * B::LDF * 2;        // one phi tile
+  static constexpr int kSQ = 0;                        // sQ[2]
+  static constexpr int kSK = kSQ + 2 * kXt;            // sK[2]
+  static constexpr int kSV = kSK + 2 * kXt;            // v'^T [3]
+  static constexpr int kSPq = kSV + 3 * B::kVbuf;      // phi(q) [2]
+  static constexpr int kSPk = kSPq + 2 * kPt;          // phi(k) [2]
+  static constexpr int kSSt = kSPk + 2 * kPt;          // bf16 S'^T
+  static constexpr int kSInv = kSSt + B::VROWS * B::LDF * 2;  // [2][inv q, lg q, inv k, lg k][C]
+  static constexpr int kSDen = kSInv + 2 * 4 * B::C * 4;      // [NTB][16] denominators
+  static constexpr int kLdsS = kSDen + B::NTB * 16 * 4;
+  static_assert(B::NTB == 2 && B::NTS == 1, "one consumer per (token block, column half)");
+  static_assert(kLdsS <= 160 * 1024, "LDS budget");
+};
+
+// Consumer task: columns [E0, E1) of num'^T for token block IB of the staged
+// chunk = intra (A^T of the causal blocks, then v'^T A^T) + inter (S'^T phi(q)^T).
+template <class K, int IB, int E0, int E1>
+__device__ __forceinline__ void consumer_task(const uint16_t* sPq, const uint16_t* sPk, const uint16_t* sVc,
+                                              const uint16_t* sSt, const RowOff<K, K::LDV>& vo,
+                                              const RowOff<K, K::LDF>& so, int lane, f32x4 (&acc)[E1 - E0]) {
+  const int g = lane >> 4, col = lane & 15;
+  f32x4 at[IB + 1];
 #pragma unroll
-    for (int j = 0; j < K::FBW; ++j)
+  for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
+    const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(sPq + (IB * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
 #pragma unroll
-      for (int et = 0; et < K::NE; ++et) {
-        const int e = et * 16 + col;
+    for (int jb = 0; jb <= IB; ++jb) {
+      const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(sPk + (jb * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
+      at[jb] = mfma_bf16(ak, bq, kf_ == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : at[jb]);
+    }
+  }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int f = (wave * K::FBW + j) * 16 + 4 * g + i;
-          if (e < K::DV) {
-            if (p.S_out) p.S_out[(head * K::F + f) * K::DV + e] = st[j][et][i];
-          } else if (e == K::DV) {
-            if (p.z_out) p.z_out[head * K::F + f] = st[j][et][i];
-          }
-        }
-      }
+  for (int i = 0; i < 4; ++i)
+    if (4 * g + i > col) at[IB][i] = 0.f;  // causal mask, diagonal block: keep j <= i
+  const uint2 lo = pack4(at[0][0], at[0][1], at[0][2], at[0][3]);
+  uint2 hi = make_uint2(0, 0);
+  if constexpr (IB == 1) hi = pack4(at[IB][0], at[IB][1], at[IB][2], at[IB][3]);
+  const bf16x8 ab = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+  for (int et = E0; et < E1; ++et) acc[et - E0] = mfma_bf16(vfrag<K>(sVc, vo, et, 0, lane), ab, f32x4{0.f, 0.f, 0.f, 0.f});
+  const uint16_t* q0 = sPq + (IB * 16 + col) * K::LDF + 8 * g;
+#pragma unroll
+  for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
+    const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(q0 + kf_ * 32));
+#pragma unroll
+    for (int et = E0; et < E1; ++et) {
+      const bf16x8 as = as_bf16x8(*reinterpret_cast<const uint4*>(sSt + so.off[et] + kf_ * 32 + 8 * g));
+      acc[et - E0] = mfma_bf16(as, bq, acc[et - E0]);
+    }
   }
 }
+
+// o = num / den for columns [E0, E1) of token block IB (den of token col in rden).
+template <class K, int IB, int E0, int E1>
+__device__ __forceinline__ void consumer_out(const Params& p, int64_t row0, int n, int lane, float rden,
+                                             const f32x4 (&acc)[E1 - E0]) {
+  const int g = lane >> 4, col = lane & 15;
+  const int tok = IB * 16 + col;
+  if (tok < n) {
+    uint16_t* orow = p.o + (row0 + tok) * K::DV;
+#pragma unroll
+    for (int et = E0; et < E1; ++et) {
+      if (et * 16 >= K::DV) continue;  // the z / padding tile
+      *reinterpret_cast<uint2*>(orow + et * 16 + 4 * g) =
+          pack4(acc[et - E0][0] * rden, acc[et - E0][1] * rden, acc[et - E0][2] * rden, acc[et - E0][3] * rden);
+    }
+  }
+}
+
+template <class K, int IB, int H>
+__device__ __forceinline__ void consumer_step(const Params& p, int64_t row0, int n, const uint16_t* sPq,
+                                              const uint16_t* sPk, const uint16_t* sVc, const uint16_t* sSt,
+                                              float* sDen, const RowOff<K, K::LDV>& vo, const RowOff<K, K::LDF>& so,
+                                              int lane, f32x4 (&acc0)[K::ESPLIT]) {
+  if constexpr (H == 0) {
+    consumer_task<K, IB, 0, K::ESPLIT>(sPq, sPk, sVc, sSt, vo, so, lane, acc0);
+  } else {
+    f32x4 acc1[K::NE - K::ESPLIT];
+    consumer_task<K, IB, K::ESPLIT, K::NE>(sPq, sPk, sVc, sSt, vo, so, lane, acc1);
+    // den of token col: element (row DV, column col) of the last tile
+    const int col = lane & 15;
+    const float den = __shfl(acc1[K::NE - 1 - K::ESPLIT][0], col, 64);
+    if (lane < 16) sDen[IB * 16 + lane] = den;
+    consumer_out<K, IB, K::ESPLIT, K::NE>(p, row0, n, lane, __builtin_amdgcn_rcpf(den), acc1);
+  }
+}
+
+template <class K>
+__global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  auto sQ = [&](int b) { return reinterpret_cast<uint16_t*>(lds + K::kSQ + b * K::kXt); };
+  auto sK = [&](int b) { return reinterpret_cast<uint16_t*>(lds + K::kSK + b * K::kXt); };
+  auto sV = [&](int b) { return reinterpret_cast<uint16_t*>(lds + K::kSV + b * K::kVbuf); };
+  auto sPq = [&](int b) { return reinterpret_cast<uint16_t*>(lds + K::kSPq + b * K::kPt); };
+  auto sPk = [&](int b) { return reinterpret_cast<uint16_t*>(lds + K::kSPk + b * K::kPt); };
+  auto sInv = [&](int b, int w) { return reinterpret_cast<float*>(lds + K::kSInv) + (b * 4 + w) * K::C; };
+  uint16_t* sSt = reinterpret_cast<uint16_t*>(lds + K::kSSt);
+  float* sDen = reinterpret_cast<float*>(lds + K::kSDen);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const bool producer = wave < K::NP;
+  const int cw = wave - K::NP;           // consumer index: token block cw >> 1, column half cw & 1
+  const int ctid = threadIdx.x - K::NP * 64;  // thread index among the consumers
+  const int64_t head = blockIdx.x / p.n_seg;
+  const int seg = (int)(blockIdx.x - head * p.n_seg);
+  const int set = (int)(head % p.n_draw_sets);
+  const int fb0 = (producer ? wave : 0) * K::FBW;
+
+  const RowOff<K, K::LDV> vo(col);
+  const RowOff<K, K::LDF> so(col);
+  for (int b = 0; b < 3; ++b) init_vconst<K, K::NTW>(threadIdx.x, sV(b));
+  for (int t = threadIdx.x; t < K::LDF; t += K::NTW) sSt[(K::DV + 1) * K::LDF + t] = 0;
+  const int64_t t0 = (int64_t)seg * p.seg_len;
+  const int64_t t1 = min<int64_t>(p.L, t0 + p.seg_len);
+  const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
+
+  // Producers and consumers run separate code (so each keeps only its own
+  // registers live); both execute the same barriers: two in the prologue and
+  // two per chunk.
+  if (producer) {
+    bf16x8 pa[K::FBW][K::NKS], pg[K::FBW][K::NKS];
+    float c1[K::FBW], c0[K::FBW];
+    f32x4 st[K::FBW][K::NE];
+    bf16x8 kf[K::FBW][K::NTS] = {};
+    load_p<K>(p, set, fb0, lane, pa, pg, c1, c0);
+    load_state<K>(p, head, seg, fb0, lane, st);
+    write_st<K>(sSt, so, wave, lane, st);
+    __syncthreads();  // chunks 0 and 1 staged
+    phase_k<K, true, false>(sK(0), sInv(0, 2), sInv(0, 3), sPk(0), fb0, lane, pa, pg, c1, c0, kf, nullptr, vo, kf, st);
+    phase_q<K>(sQ(0), sInv(0, 0), sInv(0, 1), sPq(0), wave, lane, pa, pg, c1, c0);
+    __syncthreads();  // phi of chunk 0 in LDS
+    for (int c = 0; c < nch; ++c) {
+      const int bn = (c & 1) ^ 1;
+      const uint16_t* sVc = sV(c % 3);
+      // ---- [A] phi of chunk c+1, state update by chunk c ----
+      if (c + 1 < nch) {
+        phase_k<K, true, true>(sK(bn), sInv(bn, 2), sInv(bn, 3), sPk(bn), fb0, lane, pa, pg, c1, c0, kf, sVc, vo, kf,
+                               st);
+        phase_q<K>(sQ(bn), sInv(bn, 0), sInv(bn, 1), sPq(bn), wave, lane, pa, pg, c1, c0);
+      } else {  // last chunk: its state update only
+#pragma unroll
+        for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sVc, vo, lane, s_, kf, st);
+      }
+      __syncthreads();  // B
+      // ---- [B] S'^T copy of the state after chunk c ----
+      write_st<K>(sSt, so, wave, lane, st);
+      __syncthreads();  // A
+    }
+    if (seg == p.n_seg - 1 && (p.S_out || p.z_out)) store_state_out<K>(p, head, fb0, lane, st);
+  } else {
+    // The SIMD issues from the highest-priority ready wave first: consumers
+    // (MFMA and LDS, little VALU) go ahead of the VALU-heavy producers, which
+    // fill the issue slots the consumers leave while they wait on LDS.
+    __builtin_amdgcn_s_setprio(2);
+    Prefetch<K, K::NC * 64> pf;
+    auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
+      const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
+      issue_loads<K, K::NC * 64>(ctid, p, head, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
+    };
+    auto stage = [&](int bx, int bv) {
+      store_x<K, K::NC * 64>(ctid, pf.q, sQ(bx), sInv(bx, 0), sInv(bx, 1));
+      store_x<K, K::NC * 64>(ctid, pf.k, sK(bx), sInv(bx, 2), sInv(bx, 3));
+      store_v<K, K::NC * 64>(ctid, pf.v0, pf.v1, sV(bv));
+    };
+    // prologue: chunks 0 and 1 staged, chunk 2 in flight
+    load_chunk(0);
+    stage(0, 0);
+    load_chunk(1);
+    stage(1, 1);
+    load_chunk(2);
+    __syncthreads();
+    __syncthreads();
+    // one loop per consumer role, so each keeps only its own addresses live
+    auto consumer_loop = [&](auto ib_c, auto h_c) {
+      constexpr int IB = decltype(ib_c)::value, H = decltype(h_c)::value;
+      for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        const int64_t row0 = head * p.L + t0 + (int64_t)c * K::C;
+        const int n = (int)min<int64_t>(K::C, t1 - (t0 + (int64_t)c * K::C));
+        f32x4 acc0[K::ESPLIT];
+        // ---- [A] contractions of chunk c; staging of chunk c+2 ----
+        consumer_step<K, IB, H>(p, row0, n, sPq(b), sPk(b), sV(c % 3), sSt, sDen, vo, so, lane, acc0);
+        stage(b, (c + 2) % 3);  // chunk c+2 (a repeat of the last past the end; never read then)
+        load_chunk(c + 3);
+        __syncthreads();  // B
+        // ---- [B] first column half: outputs with the other half's denominators ----
+        if constexpr (H == 0) {
+          const float rden = __builtin_amdgcn_rcpf(sDen[IB * 16 + col]);
+          consumer_out<K, IB, 0, K::ESPLIT>(p, row0, n, lane, rden, acc0);
+        }
+        __syncthreads();  // A
+      }
+    };
+    switch (cw) {  // wave-uniform
+      case 0: consumer_loop(std::integral_constant<int, 0>(), std::integral_constant<int, 0>()); break;
+      case 1: consumer_loop(std::integral_constant<int, 0>(), std::integral_constant<int, 1>()); break;
+      case 2: consumer_loop(std::integral_constant<int, 1>(), std::integral_constant<int, 0>()); break;
+      default: consumer_loop(std::integral_constant<int, 1>(), std::integral_constant<int, 1>()); break;
+    }
+  }
+}
+
+typedef Cfg<64, 64, 64, 8, 2> CfgF256;
+typedef Cfg<64, 64, 64, 8, 1> CfgF128;
+typedef Cfg<64, 64, 64, 6, 1> CfgF96;
+typedef Cfg<64, 64, 64, 4, 1> CfgF64;
+
+// Main-pass configuration per segment-pass configuration: the warp-specialized
+// kernel where one is compiled, else the two-phase pass2_kernel.  Both use the
+// same segments and the same fragment-ordered workspace.
+template <class K>
+struct MainPass {
+  using type = void;
+};
+template <>
+struct MainPass<CfgF256> {
+  using type = CfgS<64, 64, 8, 2>;
+};
 
 template <class K>
 int pick_segments(const ChunkedArgs& a) {
@@ -894,17 +1173,20 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
     e = launch_scan(sa, s);
     if (e != hipSuccess) return e;
   }
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass2_kernel<K>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pass2_kernel<K>, dim3((unsigned)(a.n_heads * n_seg)), dim3(K::NT), K::kLds, s, p);
+  using KS = typename MainPass<K>::type;
+  if constexpr (!std::is_void_v<KS>) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass2s_kernel<KS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, KS::kLdsS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pass2s_kernel<KS>, dim3((unsigned)(a.n_heads * n_seg)), dim3(KS::NTW), KS::kLdsS, s, p);
+  } else {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass2_kernel<K>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pass2_kernel<K>, dim3((unsigned)(a.n_heads * n_seg)), dim3(K::NT), K::kLds, s, p);
+  }
   return hipGetLastError();
 }
-
-typedef Cfg<64, 64, 64, 8, 2> CfgF256;
-typedef Cfg<64, 64, 64, 8, 1> CfgF128;
-typedef Cfg<64, 64, 64, 6, 1> CfgF96;
-typedef Cfg<64, 64, 64, 4, 1> CfgF64;
 
 template <typename Fn>
 bool dispatch(const ChunkedArgs& a, Fn&& fn) {
