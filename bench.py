@@ -78,7 +78,7 @@ def read_traffic(kind: str):
 
 TRAFFIC_UNITS = {
     # summary name: (kernel-name fragments counted once per launch of the unit, description)
-    "fused_fwd_h16_l16k_bf16": (("pass1_kernel", "scan_kernel", "pass2_kernel<"),
+    "fused_fwd_h16_l16k_bf16": (("pass1", "scan_kernel", "pass2"),
                                 "one causal forward, B1 H16 L16384 bf16 (segment states + scan + main pass)"),
     "featmap_h16_l16k_bf16": (("featmap_kernel<unsigned short, unsigned short",),
                               "one feature-map launch over 262144 bf16 rows, F = 256"),

@@ -90,6 +90,8 @@ struct Cfg {
   static constexpr int FS1 = 1;
   // phi projections of block tb+1 issued before the epilogue of block tb
   static constexpr bool PIPE = true;
+  // pass 1 with dedicated stager waves (pass1s_kernel)
+  static constexpr bool STAGERS1 = (NW == 8);
 };
 
 struct Params {
@@ -293,6 +295,18 @@ __device__ __forceinline__ bf16x8 vfrag(const uint16_t* sv, const RowOff<K, K::L
   const uint2 lo = *reinterpret_cast<const uint2*>(row);
   const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Scheduling hint for the preceding straight-line code: alternate one MFMA
+// with NV VALU instructions, NM times, so the matrix pipe works while the
+// wave issues its VALU epilogue (the scheduler keeps dependencies).
+template <int NM, int NV>
+__device__ __forceinline__ void mfma_valu_interleave() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+  }
 }
 
 // Projection accumulators of one 16-token block: y_a (anchor) and y_g (PRF)
@@ -719,6 +733,97 @@ __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
       *reinterpret_cast<f32x4*>(out + frag_off<K>(fb0 + j, et, lane)) = st[j][et];
 }
 
+// Pass 1 with 4 stager waves beside the NW feature waves: the stagers load
+// and stage k and v'^T (and the row scales of k); the feature waves only run
+// phi(k) and the state update.  Same buffers and one barrier per chunk as
+// pass1_kernel: in the interval of chunk c the stagers write chunk c+1 and
+// load chunk c+2 while the feature waves process chunk c.
+template <class K>
+__global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
+  constexpr int NS = 256;  // stager threads
+  extern __shared__ __align__(16) unsigned char lds[];
+  auto sK = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * K::kKbuf1); };
+  auto sInv = [&](int b) { return reinterpret_cast<float*>(lds + b * K::kKbuf1 + K::C * K::LDX * 2); };
+  auto sV = [&](int b) { return reinterpret_cast<uint16_t*>(lds + 2 * K::kKbuf1 + b * K::kVbuf); };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nsub = (p.n_seg - 1) * p.sub;  // sub-segments covered by pass 1
+  const int n_items = nsub + 1;
+  const int64_t head = blockIdx.x / nsub;
+  const int seg = (int)(blockIdx.x - head * nsub);
+  const int set = (int)(head % p.n_draw_sets);
+  const int64_t sub_len = p.seg_len / p.sub;
+  const int64_t t0 = (int64_t)seg * sub_len;
+  const int64_t t1 = min<int64_t>(p.L, t0 + sub_len);
+  const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
+
+  for (int t = threadIdx.x; t < K::DV * K::LDV / 2; t += K::NT + NS) reinterpret_cast<uint32_t*>(sV(2))[t] = 0u;
+  for (int b = 0; b < 3; ++b) init_vconst<K, K::NT + NS>(threadIdx.x, sV(b));
+
+  if (wave < K::NW) {  // feature waves
+    const int fb0 = wave * K::FBW;
+    bf16x8 pa[K::FBW][K::NKS], pg[K::FBW][K::NKS];
+    float c1[K::FBW], c0[K::FBW];
+    load_p<K>(p, set, fb0, lane, pa, pg, c1, c0);
+    f32x4 st[K::FBW][K::NE];
+#pragma unroll
+    for (int j = 0; j < K::FBW; ++j)
+#pragma unroll
+      for (int et = 0; et < K::NE; ++et) st[j][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // phi(k) of the current and the previous chunk; the "previous" of chunk 0
+    // is zero and meets the zeroed value rows of v'^T buffer 2
+    bf16x8 kfa[K::FBW][K::NTS] = {}, kfb[K::FBW][K::NTS] = {};
+    const RowOff<K, K::LDV> vo(lane & 15);
+    __syncthreads();  // chunk 0 staged
+    auto step = [&](int c, bf16x8(&kf_cur)[K::FBW][K::NTS], const bf16x8(&kf_prev)[K::FBW][K::NTS]) {
+      const int b = c & 1;
+      phase_k<K, false, true>(sK(b), sInv(b), sInv(b) + K::C, nullptr, fb0, lane, pa, pg, c1, c0, kf_cur,
+                              sV((c + 2) % 3), vo, kf_prev, st);
+      mfma_valu_interleave<K::NTB * K::FBW * K::NKS * 2 + K::NTS * K::NE * K::FBW, 3>();
+      __syncthreads();
+    };
+    for (int c = 0; c < nch; c += 2) {
+      step(c, kfa, kfb);
+      if (c + 1 < nch) step(c + 1, kfb, kfa);
+    }
+    const uint16_t* sv_last = sV((nch - 1) % 3);
+    if (nch & 1) {
+#pragma unroll
+      for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sv_last, vo, lane, s_, kfa, st);
+    } else {
+#pragma unroll
+      for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sv_last, vo, lane, s_, kfb, st);
+    }
+    float* out = p.ws + (head * n_items + seg) * (int64_t)K::F * K::DVP;
+#pragma unroll
+    for (int j = 0; j < K::FBW; ++j)
+#pragma unroll
+      for (int et = 0; et < K::NE; ++et)
+        *reinterpret_cast<f32x4*>(out + frag_off<K>(fb0 + j, et, lane)) = st[j][et];
+  } else {  // stagers
+    const int stid = threadIdx.x - K::NT;
+    Prefetch<K, NS> pf;
+    auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
+      const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
+      issue_loads<K, NS>(stid, p, head, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
+    };
+    load_chunk(0);
+    store_x<K, NS>(stid, pf.k, sK(0), sInv(0), sInv(0) + K::C);
+    store_v<K, NS>(stid, pf.v0, pf.v1, sV(0));
+    load_chunk(1);
+    __syncthreads();  // chunk 0 staged
+    for (int c = 0; c < nch; ++c) {
+      const int bn = (c + 1) & 1;
+      // chunk c+1 (a repeat of the last past the end; never read then)
+      store_x<K, NS>(stid, pf.k, sK(bn), sInv(bn), sInv(bn) + K::C);
+      store_v<K, NS>(stid, pf.v0, pf.v1, sV((c + 1) % 3));
+      load_chunk(c + 2);
+      __syncthreads();
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // pass 2: the segment's chunks in order, state on chip.  Two barriers per
 // chunk c:
@@ -1014,6 +1119,7 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
         phase_k<K, true, true>(sK(bn), sInv(bn, 2), sInv(bn, 3), sPk(bn), fb0, lane, pa, pg, c1, c0, kf, sVc, vo, kf,
                                st);
         phase_q<K>(sQ(bn), sInv(bn, 0), sInv(bn, 1), sPq(bn), wave, lane, pa, pg, c1, c0);
+        mfma_valu_interleave<K::NTB * K::FBW * K::NKS * 4 + K::NTS * K::NE * K::FBW, 4>();
       } else {  // last chunk: its state update only
 #pragma unroll
         for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sVc, vo, lane, s_, kf, st);
@@ -1150,12 +1256,20 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
   p.z_out = a.z_out;
   hipError_t e;
   if (n_seg > 1) {
-    constexpr int FS = K::FS1;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K, FS>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((pass1_kernel<K, FS>), dim3((unsigned)(a.n_heads * (n_seg - 1) * kSub * FS)),
-                       dim3(K::NT / FS), K::kLds1, s, p);
+    if constexpr (K::STAGERS1) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * (n_seg - 1) * kSub)), dim3(K::NT + 256),
+                         K::kLds1, s, p);
+    } else {
+      constexpr int FS = K::FS1;
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K, FS>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((pass1_kernel<K, FS>), dim3((unsigned)(a.n_heads * (n_seg - 1) * kSub * FS)),
+                         dim3(K::NT / FS), K::kLds1, s, p);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     ScanArgs sa{};
