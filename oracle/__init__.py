@@ -72,6 +72,9 @@ def _load():
         lib.orc_attn_rows.argtypes = [_I64, ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_int,
                                       _D, _D, _D, _D]
         lib.orc_attn_rows.restype = None
+        lib.orc_slay_noncausal.argtypes = [_I64, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_double, _D, _D, _D, _D, _D, _I64, _D, _D,
+                                           _D, _D, _D]
         _lib = lib
         return lib
 
@@ -214,6 +217,39 @@ def slay_causal(q, k, v, anchors, prf, eps: float, R: int, m: int, form: str = "
     _check(lib.orc_slay_causal(nh, L, d, dv, int(R), int(m), float(eps), _p(q), _p(k), _p(v), _p(a),
                                _p(g), stride, FORMS[form], int(chunk), _p(S0p), _p(z0p), _p(o), _p(S),
                                _p(z)), "slay_causal")
+    return o, S, z
+
+
+def slay_noncausal(q, k, v, anchors, prf, eps: float, R: int, m: int, S0=None, z0=None,
+                   per_head_draws: bool = False):
+    """Non-causal SLAY over heads: every query attends to every key.
+
+    q: [..., Lq, d]; k: [..., Lk, d]; v: [..., Lk, dv] (same leading dims).
+    Returns (o [..., Lq, dv], S [nh, F, dv], z [nh, F]) with S, z the final
+    state (S0, z0 plus every key).
+    """
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lead = q.shape[:-2]
+    Lq, d = q.shape[-2:]
+    Lk = k.shape[-2]
+    dv = v.shape[-1]
+    nh = int(np.prod(lead)) if lead else 1
+    F = R * m
+    a = _f64(anchors)
+    g = _f64(prf)
+    stride = F * d if per_head_draws else 0
+    if per_head_draws:
+        assert a.size == nh * F * d and g.size == nh * F * d
+    else:
+        assert a.size == F * d and g.size == F * d
+    S0p = None if S0 is None else _f64(S0).reshape(nh, F, dv)
+    z0p = None if z0 is None else _f64(z0).reshape(nh, F)
+    o = np.zeros(lead + (Lq, dv))
+    S = np.zeros((nh, F, dv))
+    z = np.zeros((nh, F))
+    _check(lib.orc_slay_noncausal(nh, Lq, Lk, d, dv, int(R), int(m), float(eps), _p(q), _p(k), _p(v), _p(a),
+                                  _p(g), stride, _p(S0p), _p(z0p), _p(o), _p(S), _p(z)), "slay_noncausal")
     return o, S, z
 
 

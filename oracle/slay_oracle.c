@@ -383,3 +383,68 @@ void orc_attn_rows(int64_t n_rows, const int64_t* rows, int F, int dv, const dou
     for (int e = 0; e < dv; ++e) orow[e] /= den;
   }
 }
+
+/* Non-causal SLAY: every query attends to every key,
+ *   o_i = (sum_j s_ij v_j + phq_i^T S0) / (sum_j s_ij + phq_i^T z0),
+ *   s_ij = phq_i . phk_j,
+ * the standard linear-attention contraction of [SLAY-rev] "Proposed method"
+ * bullet 6 taken over all keys (READING: the pages' vision and extreme-
+ * classification settings, "Motivation and goals" bullet 5 and "Main
+ * results" bullet 4, attend bidirectionally).  Written as the score sums,
+ * brute force over (i, j); the initial state (S0, z0), when given, adds to
+ * every query.  The final state is S0 + sum_j phk_j v_j^T, z0 + sum_j phk_j.
+ * Draws of head h start at a + h * draw_head_stride (0: shared).            */
+int orc_slay_noncausal(int64_t nh, int64_t Lq, int64_t Lk, int d, int dv, int R, int m, double eps,
+                       const double* q, const double* k, const double* v, const double* a,
+                       const double* g, int64_t draw_head_stride, const double* S0, const double* z0,
+                       double* o, double* S_out, double* z_out) {
+  if (nh < 0 || Lq < 0 || Lk < 0 || d < 1 || dv < 1 || R < 1 || m < 1) return ORC_BAD;
+  const int F = R * m;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t h = 0; h < nh; ++h) {
+    const double* ah = a + (draw_head_stride > 0 ? h * draw_head_stride : 0);
+    const double* gh = g + (draw_head_stride > 0 ? h * draw_head_stride : 0);
+    double* phq = (double*)malloc(sizeof(double) * (size_t)(Lq * F + 1));
+    double* phk = (double*)malloc(sizeof(double) * (size_t)(Lk * F + 1));
+    if (!phq || !phk) { bad |= 1; free(phq); free(phk); continue; }
+    bad |= orc_featmap(Lq, d, R, m, eps, q + h * Lq * d, ah, gh, phq);
+    bad |= orc_featmap(Lk, d, R, m, eps, k + h * Lk * d, ah, gh, phk);
+    const double* vh = v + h * Lk * dv;
+    const double* S0h = S0 ? S0 + h * (int64_t)F * dv : NULL;
+    const double* z0h = z0 ? z0 + h * (int64_t)F : NULL;
+    for (int64_t i = 0; i < Lq; ++i) {
+      const double* qf = phq + i * F;
+      double den = 0.0;
+      double* orow = o + (h * Lq + i) * dv;
+      for (int e = 0; e < dv; ++e) orow[e] = 0.0;
+      for (int64_t j = 0; j < Lk; ++j) {
+        double s = 0.0;
+        for (int f = 0; f < F; ++f) s += qf[f] * phk[j * F + f];
+        den += s;
+        for (int e = 0; e < dv; ++e) orow[e] += s * vh[j * dv + e];
+      }
+      if (z0h)
+        for (int f = 0; f < F; ++f) den += qf[f] * z0h[f];
+      if (S0h)
+        for (int e = 0; e < dv; ++e)
+          for (int f = 0; f < F; ++f) orow[e] += qf[f] * S0h[(size_t)f * dv + e];
+      for (int e = 0; e < dv; ++e) orow[e] /= den;
+    }
+    if (S_out || z_out) {
+      for (int f = 0; f < F; ++f) {
+        for (int e = 0; e < dv; ++e) {
+          double acc = S0h ? S0h[(size_t)f * dv + e] : 0.0;
+          for (int64_t j = 0; j < Lk; ++j) acc += phk[j * F + f] * vh[j * dv + e];
+          if (S_out) S_out[(h * F + f) * (int64_t)dv + e] = acc;
+        }
+        double zacc = z0h ? z0h[f] : 0.0;
+        for (int64_t j = 0; j < Lk; ++j) zacc += phk[j * F + f];
+        if (z_out) z_out[h * F + f] = zacc;
+      }
+    }
+    free(phq);
+    free(phk);
+  }
+  return bad ? ORC_BAD : ORC_OK;
+}

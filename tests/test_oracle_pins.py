@@ -363,3 +363,82 @@ def test_yat_exact_sanity(orc):
     lo = np.minimum.accumulate(v[0], axis=0)
     hi = np.maximum.accumulate(v[0], axis=0)
     assert np.all(o[0] >= lo - 1e-12) and np.all(o[0] <= hi + 1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Non-causal SLAY (review, "Proposed method" bullet 6, over every key)
+
+def _nc_inputs(rng, nh=2, Lq=7, Lk=11, d=8, dv=3, R=2, m=4):
+    q = rng.standard_normal((nh, Lq, d))
+    k = rng.standard_normal((nh, Lk, d))
+    v = rng.standard_normal((nh, Lk, dv))
+    A = rng.standard_normal((R * m, d))
+    G = rng.standard_normal((R * m, d))
+    return q, k, v, A, G, R, m
+
+
+def test_noncausal_last_query_equals_causal_last_row(orc):
+    # the causal output at the last position sees every key: the non-causal
+    # output of that query over the same keys must be the same number
+    rng = np.random.default_rng(21)
+    q, k, v, A, G, R, m = _nc_inputs(rng, Lq=11, Lk=11)
+    oc = orc.slay_causal(q, k, v, A, G, EPS, R, m, form="brute")[0]
+    on = orc.slay_noncausal(q[:, -1:], k, v, A, G, EPS, R, m)[0]
+    np.testing.assert_allclose(on[:, 0], oc[:, -1], rtol=1e-12, atol=1e-13)
+    # and the final states agree with the causal pass over the same keys
+    _, Sc, zc = orc.slay_causal(q, k, v, A, G, EPS, R, m, form="recurrent")
+    _, Sn, zn = orc.slay_noncausal(q, k, v, A, G, EPS, R, m)
+    np.testing.assert_allclose(Sn, Sc, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(zn, zc, rtol=1e-12)
+
+
+def test_noncausal_key_permutation_invariance(orc):
+    rng = np.random.default_rng(22)
+    q, k, v, A, G, R, m = _nc_inputs(rng)
+    perm = rng.permutation(k.shape[1])
+    o1 = orc.slay_noncausal(q, k, v, A, G, EPS, R, m)[0]
+    o2 = orc.slay_noncausal(q, k[:, perm], v[:, perm], A, G, EPS, R, m)[0]
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+
+
+def test_noncausal_identical_keys_give_mean(orc):
+    # every key the same: every score of a query is equal, o = mean of v
+    rng = np.random.default_rng(23)
+    q, k, v, A, G, R, m = _nc_inputs(rng)
+    k[:] = k[:, :1]
+    o = orc.slay_noncausal(q, k, v, A, G, EPS, R, m)[0]
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=1, keepdims=True), o.shape), rtol=1e-12, atol=1e-13)
+
+
+def test_noncausal_factored_form_and_hull(orc):
+    # phi(Q) (phi(K)^T V) / phi(Q) (phi(K)^T 1), built from the pinned feature
+    # map with numpy products, against the oracle's score-sum form
+    rng = np.random.default_rng(24)
+    q, k, v, A, G, R, m = _nc_inputs(rng, Lq=9, Lk=13)
+    o, S, z = orc.slay_noncausal(q, k, v, A, G, EPS, R, m)
+    for h in range(q.shape[0]):
+        pq = orc.featmap(q[h], A, G, EPS, R, m)
+        pk = orc.featmap(k[h], A, G, EPS, R, m)
+        Sh = pk.T @ v[h]
+        zh = pk.sum(0)
+        np.testing.assert_allclose(S[h], Sh, rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(z[h], zh, rtol=1e-12)
+        np.testing.assert_allclose(o[h], (pq @ Sh) / (pq @ zh)[:, None], rtol=1e-11, atol=1e-12)
+        # positive scores: each output inside the hull of the values
+        assert np.all(o[h] >= v[h].min(0) - 1e-12) and np.all(o[h] <= v[h].max(0) + 1e-12)
+
+
+def test_noncausal_initial_state(orc):
+    # keys split in two: the state of the first part as S0, z0 for the second
+    rng = np.random.default_rng(25)
+    q, k, v, A, G, R, m = _nc_inputs(rng, Lk=12)
+    o_all, S_all, z_all = orc.slay_noncausal(q, k, v, A, G, EPS, R, m)
+    _, S1, z1 = orc.slay_noncausal(q, k[:, :5], v[:, :5], A, G, EPS, R, m)
+    o2, S2, z2 = orc.slay_noncausal(q, k[:, 5:], v[:, 5:], A, G, EPS, R, m, S0=S1, z0=z1)
+    np.testing.assert_allclose(o2, o_all, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S2, S_all, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z2, z_all, rtol=1e-12)
+    # no keys at all: the output is the readout of the initial state
+    o0 = orc.slay_noncausal(q, k[:, :0], v[:, :0], A, G, EPS, R, m, S0=S1, z0=z1)[0]
+    o1 = orc.slay_noncausal(q, k[:, :5], v[:, :5], A, G, EPS, R, m)[0]
+    np.testing.assert_allclose(o0, o1, rtol=1e-12, atol=1e-13)
