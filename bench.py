@@ -46,6 +46,12 @@ def fwd_flops_per_token_head(w) -> int:
     return 8 * d * F + 4 * F * dv + 3 * F + (C + 1) * (F + dv) + (C + 1) // 2
 
 
+def noncausal_flops_per_token_head(w) -> int:
+    """Non-causal forward with Lq = Lk: q and k feature maps (4dF each), the
+    state phi(k) [v | 1]^T (2F(dv+1)) and the readout phi(q)^T [S | z] (2F(dv+1))."""
+    return 8 * w.d * w.F + 4 * w.F * (w.dv + 1)
+
+
 def featmap_bytes_per_row(w) -> int:
     return 2 * w.d + 2 * w.F  # bf16 row in, bf16 features out
 
@@ -174,7 +180,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per head of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["all", "fwd", "featmap", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "fwd", "featmap", "noncausal", "decode"], default="all")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (scale for HBM byte counters)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -270,6 +276,23 @@ def main():
                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("featmap_h16_l16k_bf16"),
                                   "algorithmic_bytes_per_launch": nbytes}})
+    if args.only in ("all", "noncausal"):
+        wsn = torch.empty(max(ops.noncausal_fwd_workspace_size(fm, w.B, w.H, w.L, w.L, w.dv, torch.bfloat16), 16),
+                          dtype=torch.uint8, device=dev)
+
+        def nc():
+            ops.noncausal_fwd(fm, qd, kd, vd, out=out, workspace=wsn)
+
+        for _ in range(args.warmup):
+            nc()
+        ms = event_time_ms(nc, args.steps, stream)
+        flops = noncausal_flops_per_token_head(w) * w.B * w.H * w.L
+        achieved = flops / (ms * 1e-3) / 1e12
+        also.append({"name": "noncausal_h16_l16k_bf16", "ms_per_step": ms, "tokens_per_s": w.B * w.L / (ms * 1e-3),
+                     "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                                  "traffic": read_traffic("noncausal_h16_l16k_bf16"),
+                                  "algorithmic_flops_per_launch": flops}})
     if args.only in ("all", "decode"):
         wd = ss.WORKLOADS[DECODE]
         nh = wd.n_heads

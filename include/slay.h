@@ -114,6 +114,34 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
                                     int32_t chunk, const float* S0, const float* z0, void* o, float* S_out,
                                     float* z_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes slay_attn_noncausal_fwd needs for this shape (0 is possible). */
+size_t slay_attn_noncausal_fwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t Lq,
+                                              int64_t Lk, int32_t dv, slay_dtype_t io_dtype);
+
+/* Non-causal SLAY forward: every query attends to every key, the standard
+ * linear-attention contraction (review, "Proposed method" bullet 6) over all
+ * keys, as used for the vision and extreme-classification settings (review,
+ * "Motivation and goals" bullet 5, "Main results" bullet 4):
+ *   o_i = phi(q_i)^T S / phi(q_i)^T z,  S = S0 + sum_j phi(k_j) v_j^T,
+ *   z = z0 + sum_j phi(k_j).
+ *   q, o : device [B][H][Lq][d], [B][H][Lq][dv];  k, v : device [B][H][Lk][d],
+ *          [B][H][Lk][dv];  dtype io_dtype (must equal the draw dtype); bf16
+ *          accumulates in fp32 and rounds the outputs to bf16 (RNE).
+ *   S0, z0     : nullable device fp32 initial state [B*H][R*m][dv], [B*H][R*m];
+ *   S_out, z_out: nullable device fp32 final state S, z (same shapes; may
+ *                alias S0, z0).
+ *   workspace  : device scratch of at least
+ *                slay_attn_noncausal_fwd_workspace_size(...) bytes (NULL if 0).
+ * Lq and Lk are independent (Lq = 0 only produces the state).  Lk = 0 needs
+ * z0 when Lq > 0 (SLAY_E_INVALID otherwise: the denominators would be 0).
+ * bf16 with d = dv = 64 and R*m in {64, 96, 128, 256} runs the fused MFMA
+ * kernels (segment states of the keys, their sum, a readout pass over the
+ * queries); every other accepted shape runs the general kernels. */
+slay_status_t slay_attn_noncausal_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                      slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t Lq, int64_t Lk,
+                                      int32_t dv, const float* S0, const float* z0, void* o, float* S_out,
+                                      float* z_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes slay_attn_recurrent_step needs (2 * n_heads * R*m * 4). */
 size_t slay_attn_recurrent_step_workspace_size(const slay_params_t* params, int64_t n_heads, int32_t dv,
                                                slay_dtype_t io_dtype);

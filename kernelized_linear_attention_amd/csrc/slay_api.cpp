@@ -21,6 +21,8 @@ namespace {
 
 thread_local std::string g_last_error;
 
+constexpr int32_t kNoncausalChunk = 64;  // token chunk of both non-causal paths
+
 slay_status_t fail(slay_status_t st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -181,8 +183,10 @@ slay::ChunkedArgs chunked_args(const slay_params_t* p, const void* q, const void
   a.k = k;
   a.v = v;
   a.io_bf16 = dt == SLAY_BF16;
+  a.causal = true;
   a.n_heads = (int64_t)B * H;
   a.L = L;
+  a.Lq = L;
   a.d = p->d;
   a.dv = dv;
   a.F = p->R * p->m;
@@ -289,6 +293,69 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
   if (nh == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   return device_status(fused ? slay::launch_fused(a, s) : slay::launch_generic(a, s), "slay_attn_chunked_fwd launch");
+}
+
+size_t slay_attn_noncausal_fwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t Lq,
+                                               int64_t Lk, int32_t dv, slay_dtype_t io_dtype) {
+  if (check_params(params) != SLAY_OK || B < 0 || H < 0 || Lq < 0 || Lk < 0 || dv < 1) return 0;
+  slay::ChunkedArgs a = chunked_args(params, nullptr, nullptr, nullptr, io_dtype, B, H, Lk, dv, kNoncausalChunk);
+  a.causal = false;
+  a.Lq = Lq;
+  if (a.n_heads == 0) return 0;
+  if (slay::fused_supported(a)) return slay::fused_workspace_bytes(a);
+  return slay::generic_workspace_bytes(a);
+}
+
+slay_status_t slay_attn_noncausal_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                      slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t Lq, int64_t Lk,
+                                      int32_t dv, const float* S0, const float* z0, void* o, float* S_out,
+                                      float* z_out, void* workspace, size_t workspace_bytes, void* stream) {
+  slay_status_t st = check_params(params);
+  if (st != SLAY_OK) return st;
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return fail(SLAY_E_INVALID, "B, H, Lq, Lk must be >= 0");
+  if (dv < 1) return fail(SLAY_E_INVALID, "dv must be >= 1");
+  if (io_dtype != SLAY_F32 && io_dtype != SLAY_BF16) return fail(SLAY_E_INVALID, "bad io dtype");
+  if (io_dtype != params->draw_dtype) return fail(SLAY_E_UNSUPPORTED, "io dtype must equal the draw dtype");
+  const int64_t nh = (int64_t)B * H;
+  const int F = params->R * params->m;
+  const int64_t Lmax = std::max(Lq, Lk);
+  if (!mul_ok(nh, Lmax) || !mul_ok(nh * Lmax, std::max<int64_t>(params->d, dv)) || !mul_ok(nh * Lmax, F))
+    return fail(SLAY_E_INVALID, "problem size overflows");
+  if (nh > 0 && Lq > 0 && Lk == 0 && !z0)
+    return fail(SLAY_E_INVALID, "no keys and no initial state: every denominator would be zero");
+  const int es = io_dtype == SLAY_BF16 ? 2 : 4;
+  if (nh > 0 && (Lq > 0 || Lk > 0) && ((dv * es) % 16 != 0 || (params->d * es) % 16 != 0))
+    return fail(SLAY_E_UNSUPPORTED, "rows of q/k/v must be whole 16-byte vectors (dv = %d)", dv);
+  if (nh > 0 && Lq > 0) {
+    if (!q || !o) return fail(SLAY_E_INVALID, "q/o pointer is NULL");
+    if (!aligned16(q) || !aligned16(o)) return fail(SLAY_E_INVALID, "q/o must be 16-byte aligned");
+  }
+  if (nh > 0 && Lk > 0) {
+    if (!k || !v) return fail(SLAY_E_INVALID, "k/v pointer is NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(SLAY_E_INVALID, "k/v must be 16-byte aligned");
+  }
+  slay::ChunkedArgs a = chunked_args(params, q, k, v, io_dtype, B, H, Lk, dv, kNoncausalChunk);
+  a.causal = false;
+  a.Lq = Lq;
+  a.nc = node_consts(params->R, params->m, params->eps);
+  a.S0 = S0;
+  a.z0 = z0;
+  a.o = o;
+  a.S_out = S_out;
+  a.z_out = z_out;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  const bool fused = slay::fused_supported(a);
+  if (!fused && !slay::generic_supported(a))
+    return fail(SLAY_E_UNSUPPORTED, "shape not supported (d=%d dv=%d F=%d)", params->d, dv, F);
+  const size_t need = nh == 0 ? 0 : (fused ? slay::fused_workspace_bytes(a) : slay::generic_workspace_bytes(a));
+  if (workspace_bytes < need) return fail(SLAY_E_INVALID, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (need > 0 && !workspace) return fail(SLAY_E_INVALID, "workspace is NULL");
+  if (need > 0 && !aligned16(workspace)) return fail(SLAY_E_INVALID, "workspace must be 16-byte aligned");
+  if (nh == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return device_status(fused ? slay::launch_fused(a, s) : slay::launch_generic(a, s),
+                       "slay_attn_noncausal_fwd launch");
 }
 
 namespace {

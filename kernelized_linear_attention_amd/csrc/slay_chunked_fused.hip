@@ -109,8 +109,14 @@ struct Params {
   int64_t draw_set_stride;
   int n_draw_sets;
   NodeConsts nc;
-  float* ws;         // [n_heads][n_items][F/16][NE][64][4] fragment-ordered states,
-                     // n_items = (n_seg - 1) * sub + 1; item s * sub is the prefix of segment s
+  float* ws;         // [n_heads][p1_items][F/16][NE][64][4] fragment-ordered states:
+                     // after the scan, item s * sub is the prefix of segment s and
+                     // item p1_segs the total
+  int p1_segs;       // segments the segment-state pass covers per head (of the keys)
+  int p1_items;      // p1_segs + 1
+  int64_t Lq;        // queries per head (non-causal; the causal path has Lq = L)
+  int64_t qseg_len;  // queries per workgroup of the non-causal output pass
+  int n_qseg;
   const float* S0;   // used when there is a single segment
   const float* z0;
   float* S_out;
@@ -528,16 +534,14 @@ __device__ __forceinline__ int64_t frag_off(int fb, int et, int lane) {
   return ((int64_t)(fb * K::NE + et) * 64 + lane) * 4;
 }
 
-// Initial state of segment seg for the wave's feature blocks fb0..fb0+FBW-1:
-// the scanned prefix from the workspace, or S0/z0 (zero when absent) when the
-// head is one segment.
+// State for the wave's feature blocks fb0..fb0+FBW-1: workspace item `item`
+// of the head when from_ws, else S0/z0 (zero when absent).
 template <class K>
-__device__ __forceinline__ void load_state(const Params& p, int64_t head, int seg, int fb0, int lane,
-                                           f32x4 (&st)[K::FBW][K::NE]) {
+__device__ __forceinline__ void load_state_item(const Params& p, int64_t head, bool from_ws, int64_t item, int fb0,
+                                                int lane, f32x4 (&st)[K::FBW][K::NE]) {
   const int g = lane >> 4, col = lane & 15;
-  if (p.n_seg > 1) {
-    const int64_t n_items = (int64_t)(p.n_seg - 1) * p.sub + 1;
-    const float* in = p.ws + (head * n_items + (int64_t)seg * p.sub) * (int64_t)K::F * K::DVP;
+  if (from_ws) {
+    const float* in = p.ws + (head * p.p1_items + item) * (int64_t)K::F * K::DVP;
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
@@ -561,6 +565,14 @@ __device__ __forceinline__ void load_state(const Params& p, int64_t head, int se
         }
       }
   }
+}
+
+// Initial state of causal segment seg: the scanned prefix from the workspace,
+// or S0/z0 when the head is one segment.
+template <class K>
+__device__ __forceinline__ void load_state(const Params& p, int64_t head, int seg, int fb0, int lane,
+                                           f32x4 (&st)[K::FBW][K::NE]) {
+  load_state_item<K>(p, head, p.n_seg > 1, (int64_t)seg * p.sub, fb0, lane, st);
 }
 
 // Final state of the head (last segment only) for the wave's feature blocks.
@@ -661,8 +673,8 @@ __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
   auto sV = [&](int b) { return reinterpret_cast<uint16_t*>(lds + 2 * K::kKbuf1 + b * K::kVbuf); };
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nsub = (p.n_seg - 1) * p.sub;  // sub-segments covered by pass 1
-  const int n_items = nsub + 1;
+  const int nsub = p.p1_segs;  // sub-segments covered by pass 1
+  const int n_items = p.p1_items;
   const int fs = (int)(blockIdx.x % FS);
   const int64_t hs = blockIdx.x / FS;
   const int64_t head = hs / nsub;
@@ -748,8 +760,8 @@ __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nsub = (p.n_seg - 1) * p.sub;  // sub-segments covered by pass 1
-  const int n_items = nsub + 1;
+  const int nsub = p.p1_segs;  // sub-segments covered by pass 1
+  const int n_items = p.p1_items;
   const int64_t head = blockIdx.x / nsub;
   const int seg = (int)(blockIdx.x - head * nsub);
   const int set = (int)(head % p.n_draw_sets);
@@ -1183,6 +1195,110 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Non-causal output pass: o = phi(q)^T S' / phi(q)^T z over the state of all
+// keys (the total from the workspace, or S0/z0 when there are no keys).  One
+// workgroup per (head, query segment); each wave keeps its feature slice of P
+// in registers and writes its slice of the bf16 S'^T copy once.  Per chunk c
+// of 64 queries, one barrier: the inter tasks of chunk c (one per (16-query
+// block, column half)) beside phi(q) of chunk c+1 and the staging of c+2.
+
+// Inter task for query block IB, column half H of num'^T = S'^T phi(q)^T,
+// then o = num / den for that half; each half also computes the denominator
+// tile (the z row), so the halves need no exchange.
+template <class K, int H>
+__device__ __forceinline__ void nc_task(const Params& p, int64_t row0, int n, int ib, const uint16_t* sPq,
+                                        const uint16_t* sSt, const RowOff<K, K::LDF>& so, int lane) {
+  constexpr int NV = K::NE - 1;         // value tiles
+  constexpr int NH = NV / 2 + 1;        // tiles of this half, the last one the denominator tile
+  const int g = lane >> 4, col = lane & 15;
+  auto tile = [](int i) { return i < NH - 1 ? H * (NV / 2) + i : K::NE - 1; };
+  f32x4 acc[NH];
+  const uint16_t* q0 = sPq + (ib * 16 + col) * K::LDF + 8 * g;
+#pragma unroll
+  for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
+    const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(q0 + kf_ * 32));
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const bf16x8 as = as_bf16x8(*reinterpret_cast<const uint4*>(sSt + so.off[tile(i)] + kf_ * 32 + 8 * g));
+      acc[i] = mfma_bf16(as, bq, kf_ == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i]);
+    }
+  }
+  const float rden = __builtin_amdgcn_rcpf(__shfl(acc[NH - 1][0], col, 64));
+  const int tok = ib * 16 + col;
+  if (tok < n) {
+    uint16_t* orow = p.o + (row0 + tok) * K::DV;
+#pragma unroll
+    for (int i = 0; i < NH - 1; ++i)
+      *reinterpret_cast<uint2*>(orow + tile(i) * 16 + 4 * g) =
+          pack4(acc[i][0] * rden, acc[i][1] * rden, acc[i][2] * rden, acc[i][3] * rden);
+  }
+}
+
+template <class K>
+__global__ __launch_bounds__(K::NT) void ncout_kernel(Params p) {
+  constexpr int kXt = K::C * K::LDX * 2, kPt = K::C * K::LDF * 2;
+  extern __shared__ __align__(16) unsigned char lds[];
+  auto sQ = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * kXt); };
+  auto sInv = [&](int b) { return reinterpret_cast<float*>(lds + 2 * kXt) + b * 2 * K::C; };
+  auto sPq = [&](int b) { return reinterpret_cast<uint16_t*>(lds + 2 * kXt + 4 * K::C * 4 + b * kPt); };
+  uint16_t* sSt = reinterpret_cast<uint16_t*>(lds + 2 * kXt + 4 * K::C * 4 + 2 * kPt);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;
+  const int64_t head = blockIdx.x / p.n_qseg;
+  const int qs = (int)(blockIdx.x - head * p.n_qseg);
+  const int set = (int)(head % p.n_draw_sets);
+  const int fb0 = wave * K::FBW;
+
+  bf16x8 pa[K::FBW][K::NKS], pg[K::FBW][K::NKS];
+  float c1[K::FBW], c0[K::FBW];
+  load_p<K>(p, set, fb0, lane, pa, pg, c1, c0);
+  const RowOff<K, K::LDF> so(col);
+  {
+    f32x4 st[K::FBW][K::NE];
+    load_state_item<K>(p, head, p.L > 0, p.p1_items - 1, fb0, lane, st);
+    write_st<K>(sSt, so, wave, lane, st);
+  }
+  for (int t = threadIdx.x; t < K::LDF; t += K::NT) sSt[(K::DV + 1) * K::LDF + t] = 0;
+
+  const int64_t t0 = (int64_t)qs * p.qseg_len;
+  const int64_t t1 = min<int64_t>(p.Lq, t0 + p.qseg_len);
+  const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
+  Prefetch<K> pf;
+  auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
+    const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
+    load_x<K>(threadIdx.x, p.q + (head * p.Lq + c2) * K::D, (int)min<int64_t>(K::C, t1 - c2), pf.q);
+  };
+  load_chunk(0);
+  store_x<K>(threadIdx.x, pf.q, sQ(0), sInv(0), sInv(0) + K::C);
+  load_chunk(1);
+  __syncthreads();
+  phase_q<K>(sQ(0), sInv(0), sInv(0) + K::C, sPq(0), wave, lane, pa, pg, c1, c0);
+  store_x<K>(threadIdx.x, pf.q, sQ(1), sInv(1), sInv(1) + K::C);
+  load_chunk(2);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    const int64_t row0 = head * p.Lq + t0 + (int64_t)c * K::C;
+    const int n = (int)min<int64_t>(K::C, t1 - (t0 + (int64_t)c * K::C));
+    for (int t = wave; t < 2 * K::NTB; t += K::NW) {  // wave-uniform task loop
+      if (t & 1) nc_task<K, 1>(p, row0, n, t >> 1, sPq(b), sSt, so, lane);
+      else nc_task<K, 0>(p, row0, n, t >> 1, sPq(b), sSt, so, lane);
+    }
+    if (c + 1 < nch) phase_q<K>(sQ(b ^ 1), sInv(b ^ 1), sInv(b ^ 1) + K::C, sPq(b ^ 1), wave, lane, pa, pg, c1, c0);
+    store_x<K>(threadIdx.x, pf.q, sQ(b), sInv(b), sInv(b) + K::C);  // chunk c+2 (a repeat past the end)
+    load_chunk(c + 3);
+    __syncthreads();
+  }
+}
+
+template <class K>
+constexpr int ncout_lds() {
+  return 2 * K::C * K::LDX * 2 + 4 * K::C * 4 + 2 * K::C * K::LDF * 2 + K::VROWS * K::LDF * 2;
+}
+
 typedef Cfg<64, 64, 64, 8, 2> CfgF256;
 typedef Cfg<64, 64, 64, 8, 1> CfgF128;
 typedef Cfg<64, 64, 64, 6, 1> CfgF96;
@@ -1200,10 +1316,12 @@ struct MainPass<CfgF256> {
   using type = CfgS<64, 64, 8, 2>;
 };
 
+// Segments per head for n_heads heads of L tokens: enough workgroups to fill
+// the chip (about 256), each an even number of chunks.
 template <class K>
-int pick_segments(const ChunkedArgs& a) {
-  const int64_t n_chunks = (a.L + K::C - 1) / K::C;
-  int64_t want = (256 + a.n_heads - 1) / a.n_heads;
+int pick_segments(int64_t n_heads, int64_t L) {
+  const int64_t n_chunks = (L + K::C - 1) / K::C;
+  int64_t want = (256 + n_heads - 1) / n_heads;
   if (want > n_chunks) want = n_chunks;
   if (want < 1) want = 1;
   const int64_t cps = (n_chunks + want - 1) / want;  // chunks per segment
@@ -1211,16 +1329,26 @@ int pick_segments(const ChunkedArgs& a) {
 }
 
 template <class K>
-int64_t seg_len_of(const ChunkedArgs& a, int n_seg) {
-  const int64_t n_chunks = (a.L + K::C - 1) / K::C;
+int64_t seg_len_of(int64_t L, int n_seg) {
+  const int64_t n_chunks = (L + K::C - 1) / K::C;
   const int64_t cps = (n_chunks + n_seg - 1) / n_seg;
-  return ((cps + 1) / 2) * 2 * K::C;  // an even number of chunks: pass 1 halves each segment
+  return ((cps + 1) / 2) * 2 * K::C;  // an even number of chunks
+}
+
+template <class K>
+int64_t seg_len_for(int64_t n_heads, int64_t L) {
+  return seg_len_of<K>(L, pick_segments<K>(n_heads, L));
+}
+
+template <class K>
+int segments_of(int64_t n_heads, int64_t L) {
+  const int64_t seg_len = seg_len_for<K>(n_heads, L);
+  return (int)((L + seg_len - 1) / seg_len);
 }
 
 template <class K>
 int segments_of(const ChunkedArgs& a) {
-  const int64_t seg_len = seg_len_of<K>(a, pick_segments<K>(a));
-  return (int)((a.L + seg_len - 1) / seg_len);
+  return segments_of<K>(a.n_heads, a.L);
 }
 
 constexpr int kSub = 1;  // pass-1 sub-segments per segment
@@ -1241,8 +1369,11 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
   p.o = static_cast<uint16_t*>(a.o);
   p.L = a.L;
   p.n_seg = n_seg;
-  p.seg_len = seg_len_of<K>(a, pick_segments<K>(a));
+  p.seg_len = seg_len_for<K>(a.n_heads, a.L);
   p.sub = kSub;
+  p.p1_segs = (n_seg - 1) * kSub;
+  p.p1_items = p.p1_segs + 1;
+  p.Lq = a.L;
   p.m = a.m;
   p.anchors = static_cast<const uint16_t*>(a.anchors);
   p.prf = static_cast<const uint16_t*>(a.prf);
@@ -1317,6 +1448,90 @@ bool dispatch(const ChunkedArgs& a, Fn&& fn) {
   }
 }
 
+// Non-causal: segment-state pass over every key segment, scan to the total
+// (item p1_segs), then the output pass over query segments.
+template <class K>
+size_t ws_bytes_nc_t(const ChunkedArgs& a) {
+  if (a.L == 0) return 0;
+  const int n_seg = segments_of<K>(a);
+  return sizeof(float) * (size_t)a.n_heads * (n_seg * kSub + 1) * K::F * K::DVP;
+}
+
+template <class K>
+hipError_t launch_nc_t(const ChunkedArgs& a, hipStream_t s) {
+  Params p{};
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<uint16_t*>(a.o);
+  p.L = a.L;
+  p.Lq = a.Lq;
+  p.sub = kSub;
+  p.m = a.m;
+  p.anchors = static_cast<const uint16_t*>(a.anchors);
+  p.prf = static_cast<const uint16_t*>(a.prf);
+  p.draw_set_stride = a.draw_set_stride;
+  p.n_draw_sets = a.n_draw_sets;
+  p.nc = a.nc;
+  p.ws = static_cast<float*>(a.ws);
+  p.S0 = a.S0;
+  p.z0 = a.z0;
+  hipError_t e;
+  ScanArgs sa{};
+  sa.n_heads = a.n_heads;
+  sa.F = K::F;
+  sa.dv = K::DV;
+  sa.S0 = a.S0;
+  sa.z0 = a.z0;
+  sa.S_out = a.S_out;
+  sa.z_out = a.z_out;
+  if (a.L > 0) {
+    const int n_seg = segments_of<K>(a);
+    p.n_seg = n_seg;
+    p.seg_len = seg_len_for<K>(a.n_heads, a.L);
+    p.p1_segs = n_seg * kSub;
+    p.p1_items = p.p1_segs + 1;
+    if constexpr (K::STAGERS1) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT + 256), K::kLds1, s,
+                         p);
+    } else {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K, 1>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((pass1_kernel<K, 1>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT), K::kLds1, s, p);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    sa.states = p.ws;
+    sa.n_items = p.p1_items;
+    sa.n_terms = p.p1_segs;
+    sa.layout = 1;
+  } else {  // no keys: the state is S0/z0 (the output pass reads them directly)
+    p.p1_items = 1;
+    sa.states = nullptr;
+    sa.n_items = 0;
+    sa.n_terms = 0;
+    sa.layout = 0;
+  }
+  if (sa.n_items > 0 || sa.S_out || sa.z_out) {
+    e = launch_scan(sa, s);
+    if (e != hipSuccess) return e;
+  }
+  if (a.Lq == 0) return hipSuccess;
+  p.n_qseg = segments_of<K>(a.n_heads, a.Lq);
+  p.qseg_len = seg_len_for<K>(a.n_heads, a.Lq);
+  constexpr int lds = ncout_lds<K>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ncout_kernel<K>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ncout_kernel<K>, dim3((unsigned)(a.n_heads * p.n_qseg)), dim3(K::NT), lds, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool fused_supported(const ChunkedArgs& a) {
@@ -1325,14 +1540,18 @@ bool fused_supported(const ChunkedArgs& a) {
 
 size_t fused_workspace_bytes(const ChunkedArgs& a) {
   size_t r = 0;
-  dispatch(a, [&](auto k) { r = ws_bytes_t<decltype(k)>(a); });
+  dispatch(a, [&](auto k) { r = a.causal ? ws_bytes_t<decltype(k)>(a) : ws_bytes_nc_t<decltype(k)>(a); });
   return r;
 }
 
 hipError_t launch_fused(const ChunkedArgs& a, hipStream_t s) {
   if (a.n_heads == 0) return hipSuccess;
-  if (a.L == 0) return launch_generic(a, s);  // only the state passes through
   hipError_t e = hipErrorInvalidValue;
+  if (!a.causal) {
+    dispatch(a, [&](auto k) { e = launch_nc_t<decltype(k)>(a, s); });
+    return e;
+  }
+  if (a.L == 0) return launch_generic(a, s);  // only the state passes through
   dispatch(a, [&](auto k) { e = launch_t<decltype(k)>(a, s); });
   return e;
 }

@@ -223,6 +223,91 @@ hipError_t launch_generic_t(const ChunkedArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Non-causal output: o_i = phi(q_i)^T S / phi(q_i)^T z with the state of all
+// keys (S in columns 0..dv-1, z in column dv of the [F][dv+1] layout).
+template <typename TV>
+__global__ __launch_bounds__(kGThreads) void nc_out_kernel(const float* __restrict__ phiq, int64_t Lq, int F, int dv,
+                                                           const float* __restrict__ S, int64_t state_stride,
+                                                           TV* __restrict__ o) {
+  const int64_t h = blockIdx.y;
+  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  const int n = (int)min<int64_t>(64, Lq - i0);
+  const int E1 = dv + 1;
+  const float* pq = phiq + (h * Lq + i0) * F;
+  const float* Sh = S + h * state_stride;
+  for (int p = threadIdx.x; p < n * dv; p += kGThreads) {
+    const int i = p / dv, e = p - (p / dv) * dv;
+    float num = 0.f, den = 0.f;
+    for (int f = 0; f < F; ++f) {
+      const float qf = pq[(int64_t)i * F + f];
+      num = fmaf(qf, Sh[(int64_t)f * E1 + e], num);
+      den = fmaf(qf, Sh[(int64_t)f * E1 + dv], den);
+    }
+    store_out<TV>(o + (h * Lq + i0 + i) * dv + e, num / den);
+  }
+}
+
+// Non-causal general path: phi(q), phi(k) to the workspace, per-chunk states
+// of the keys, scan to the total (item n_chunks, S0/z0 included), readout.
+template <typename TV>
+hipError_t launch_generic_nc_t(const ChunkedArgs& a, hipStream_t s) {
+  const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+  float* phiq = static_cast<float*>(a.ws);
+  float* phik = phiq + a.n_heads * a.Lq * a.F;
+  float* states = phik + a.n_heads * a.L * a.F;
+
+  FeatmapArgs fa{};
+  fa.n_heads = a.n_heads;
+  fa.d = a.d;
+  fa.F = a.F;
+  fa.m = a.m;
+  fa.x_bf16 = a.io_bf16;
+  fa.anchors = a.anchors;
+  fa.prf = a.prf;
+  fa.draw_set_stride = a.draw_set_stride;
+  fa.n_draw_sets = a.n_draw_sets;
+  fa.nc = a.nc;
+  fa.phi_bf16 = false;
+  hipError_t e;
+  if (a.Lq > 0) {
+    fa.rows_per_head = a.Lq;
+    fa.x = a.q;
+    fa.phi = phiq;
+    e = launch_featmap(fa, s);
+    if (e != hipSuccess) return e;
+  }
+  if (a.L > 0) {
+    fa.rows_per_head = a.L;
+    fa.x = a.k;
+    fa.phi = phik;
+    e = launch_featmap(fa, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_state_kernel<TV>, dim3((unsigned)n_chunks, (unsigned)a.n_heads), dim3(kGThreads), 0, s,
+                       phik, static_cast<const TV*>(a.v), a.L, a.F, a.dv, a.chunk, n_chunks + 1, states);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ScanArgs sa{};
+  sa.states = states;
+  sa.n_heads = a.n_heads;
+  sa.n_items = n_chunks + 1;
+  sa.n_terms = n_chunks;
+  sa.F = a.F;
+  sa.dv = a.dv;
+  sa.layout = 0;
+  sa.S0 = a.S0;
+  sa.z0 = a.z0;
+  sa.S_out = a.S_out;
+  sa.z_out = a.z_out;
+  e = launch_scan(sa, s);
+  if (e != hipSuccess) return e;
+  if (a.Lq == 0) return hipSuccess;
+  const int64_t E = (int64_t)a.F * (a.dv + 1);
+  hipLaunchKernelGGL(nc_out_kernel<TV>, dim3((unsigned)((a.Lq + 63) / 64), (unsigned)a.n_heads), dim3(kGThreads), 0, s,
+                     phiq, a.Lq, a.F, a.dv, states + n_chunks * E, (n_chunks + 1) * E, static_cast<TV*>(a.o));
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int64_t scan_state_elems(int F, int dv, int layout) {
@@ -243,12 +328,19 @@ bool generic_supported(const ChunkedArgs& a) {
 }
 
 size_t generic_workspace_bytes(const ChunkedArgs& a) {
-  const int64_t nrow = a.n_heads * a.L;
   const int64_t n_chunks = (a.L + a.chunk - 1) / a.chunk;
+  if (!a.causal)  // phi(q), phi(k), per-chunk states and their total
+    return sizeof(float) * (size_t)((a.n_heads * (a.Lq + a.L)) * a.F +
+                                    a.n_heads * (n_chunks + 1) * (int64_t)a.F * (a.dv + 1));
+  const int64_t nrow = a.n_heads * a.L;
   return sizeof(float) * (size_t)(2 * nrow * a.F + a.n_heads * n_chunks * (int64_t)a.F * (a.dv + 1));
 }
 
 hipError_t launch_generic(const ChunkedArgs& a, hipStream_t s) {
+  if (!a.causal) {
+    if (a.n_heads == 0) return hipSuccess;
+    return a.io_bf16 ? launch_generic_nc_t<uint16_t>(a, s) : launch_generic_nc_t<float>(a, s);
+  }
   if (a.n_heads == 0 || a.L == 0) {
     // no tokens: the final state is the initial one
     ScanArgs sa{};

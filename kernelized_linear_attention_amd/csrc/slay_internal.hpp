@@ -29,13 +29,15 @@ struct FeatmapArgs {
 bool featmap_supported(int d);
 hipError_t launch_featmap(const FeatmapArgs& a, hipStream_t s);
 
-// Causal chunked forward over n_heads = B*H heads.
+// Chunked forward over n_heads = B*H heads: causal (Lq == L) or non-causal
+// (every query attends to all L keys; Lq queries per head).
 struct ChunkedArgs {
-  const void* q;  // [n_heads][L][d]
-  const void* k;
+  const void* q;  // [n_heads][Lq][d]
+  const void* k;  // [n_heads][L][d]
   const void* v;  // [n_heads][L][dv]
   bool io_bf16;
-  int64_t n_heads, L;
+  bool causal;
+  int64_t n_heads, L, Lq;
   int d, dv, F, m, R, chunk;
   const void* anchors;
   const void* prf;
@@ -44,7 +46,7 @@ struct ChunkedArgs {
   NodeConsts nc;
   const float* S0;  // nullable [n_heads][F][dv]
   const float* z0;  // nullable [n_heads][F]
-  void* o;          // [n_heads][L][dv]
+  void* o;          // [n_heads][Lq][dv]
   float* S_out;     // nullable
   float* z_out;     // nullable
   void* ws;

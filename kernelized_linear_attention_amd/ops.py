@@ -152,6 +152,52 @@ def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     return out
 
 
+def noncausal_fwd_workspace_size(fm: FeatureMap, B: int, H: int, Lq: int, Lk: int, dv: int,
+                                 dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.slay_attn_noncausal_fwd_workspace_size(fm.c_params(), B, H, Lq, Lk, dv, _dtype_code(dtype)))
+
+
+def noncausal_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  S0: torch.Tensor | None = None, z0: torch.Tensor | None = None, return_state: bool = False,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, S_out=None, z_out=None):
+    """Non-causal SLAY forward.  q [B, H, Lq, d]; k [B, H, Lk, d]; v [B, H, Lk, dv] -> o [B, H, Lq, dv].
+
+    Every query attends to every key.  S0, z0: optional fp32 initial state
+    [B*H, F, dv], [B*H, F].  With return_state the final state (S, z) is
+    returned as well.
+    """
+    lib = _lib.load()
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", (B, H, Lk, d), q.dtype)
+    _need(v, "v", (B, H, Lk, dv), q.dtype)
+    if out is None:
+        out = torch.empty((B, H, Lq, dv), dtype=q.dtype, device=q.device)
+    _need(out, "out", (B, H, Lq, dv), q.dtype)
+    for t, name, shp in ((S0, "S0", (B * H, fm.F, dv)), (z0, "z0", (B * H, fm.F))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
+    if return_state:
+        if S_out is None:
+            S_out = torch.empty((B * H, fm.F, dv), dtype=torch.float32, device=q.device)
+        if z_out is None:
+            z_out = torch.empty((B * H, fm.F), dtype=torch.float32, device=q.device)
+    nbytes = noncausal_fwd_workspace_size(fm, B, H, Lq, Lk, dv, q.dtype)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.slay_attn_noncausal_fwd(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype),
+                                     B, H, Lq, Lk, dv, _ptr(S0), _ptr(z0), out.data_ptr(), _ptr(S_out),
+                                     _ptr(z_out), _ptr(workspace), wsz, _stream(q))
+    _lib.check(st, "slay_attn_noncausal_fwd")
+    if return_state:
+        return out, S_out, z_out
+    return out
+
+
 def recurrent_step_workspace_size(fm: FeatureMap, n_heads: int, dv: int, dtype: torch.dtype) -> int:
     lib = _lib.load()
     return int(lib.slay_attn_recurrent_step_workspace_size(fm.c_params(), n_heads, dv, _dtype_code(dtype)))

@@ -153,3 +153,41 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def _nc(lib, p, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, dt=_lib.SLAY_BF16, B=1, H=16, Lq=16384, Lk=16384, dv=64, S0=None, z0=None,
+                o=FAKE, S_out=None, z_out=None, ws=None, ws_bytes=0)
+    args.update(kw)
+    return lib.slay_attn_noncausal_fwd(ctypes.byref(p) if p is not None else None, args["q"], args["k"], args["v"],
+                                       args["dt"], args["B"], args["H"], args["Lq"], args["Lk"], args["dv"],
+                                       args["S0"], args["z0"], args["o"], args["S_out"], args["z_out"], args["ws"],
+                                       args["ws_bytes"], None)
+
+
+def test_noncausal_validation_and_workspace(lib):
+    E_INV, E_UNS = _lib.SLAY_E_INVALID, _lib.SLAY_E_UNSUPPORTED
+    p = _params()
+    assert _nc(lib, None) == E_INV
+    assert _nc(lib, p, Lq=-1) == E_INV
+    assert _nc(lib, p, Lk=-1) == E_INV
+    assert _nc(lib, p, dv=0) == E_INV
+    assert _nc(lib, p, dt=_lib.SLAY_F32) == E_UNS
+    assert _nc(lib, p, Lk=0) == E_INV and b"no keys" in lib.slay_last_error()
+    assert _nc(lib, p, q=None) == E_INV
+    assert _nc(lib, p, k=None) == E_INV
+    assert _nc(lib, p, o=FAKE + 4) == E_INV
+    assert _nc(lib, p) == E_INV and b"workspace too small" in lib.slay_last_error()
+    # q and o are not needed without queries, k and v not without keys
+    need_k = lib.slay_attn_noncausal_fwd_workspace_size(ctypes.byref(p), 1, 16, 0, 16384, 64, _lib.SLAY_BF16)
+    assert _nc(lib, p, q=None, o=None, Lq=0, ws=FAKE, ws_bytes=need_k - 1) == E_INV
+    # fused path: 16 key segments per head, their states and the total
+    n = lib.slay_attn_noncausal_fwd_workspace_size(ctypes.byref(p), 1, 16, 16384, 16384, 64, _lib.SLAY_BF16)
+    assert n == 4 * 16 * 17 * 256 * (64 + 16)
+    assert lib.slay_attn_noncausal_fwd_workspace_size(ctypes.byref(p), 1, 16, 100, 0, 64, _lib.SLAY_BF16) == 0
+    # general path (fp32): phi(q), phi(k), four 64-key chunk states and their total
+    p32 = _params(R=2, m=16, dt=_lib.SLAY_F32)
+    n = lib.slay_attn_noncausal_fwd_workspace_size(ctypes.byref(p32), 1, 1, 100, 256, 64, _lib.SLAY_F32)
+    assert n == 4 * ((100 + 256) * 32 + 5 * 32 * 65)
+    # nothing to do
+    assert _nc(lib, p, B=0) == _lib.SLAY_OK
