@@ -84,11 +84,36 @@ def _finish(x: np.ndarray, dtype: str) -> np.ndarray:
     return bf16_round(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
 
 
-def make_draws(w: Workload, seed=None):
-    """Anchor and PRF draws, each [R*m, d] fp32 (bf16-exact for bf16 workloads)."""
+def orthogonal_gaussian_rows(rng, n: int, d: int) -> np.ndarray:
+    """n rows in consecutive blocks of d mutually orthogonal directions.
+
+    Each block is a Haar-random orthogonal matrix (QR of a Gaussian matrix
+    with the signs of R's diagonal folded in), each row scaled by an
+    independent chi(d) length, so every row is still marginally N(0, I_d)
+    while the rows of a block are orthogonal: the "positive orthogonal random
+    features" of the linearized 2-simplicial attention page's summary.
+    """
+    blocks = []
+    for _ in range((n + d - 1) // d):
+        Q, R = np.linalg.qr(rng.standard_normal((d, d)))
+        Q = Q * np.sign(np.diag(R))
+        lengths = np.linalg.norm(rng.standard_normal((d, d)), axis=1)
+        blocks.append(Q.T * lengths[:, None])
+    return np.concatenate(blocks)[:n]
+
+
+def make_draws(w: Workload, seed=None, orthogonal: bool = False):
+    """Anchor and PRF draws, each [R*m, d] fp32 (bf16-exact for bf16 workloads).
+
+    orthogonal: the PRF rows of every node come in orthogonal blocks of d
+    (orthogonal_gaussian_rows); anchors stay i.i.d. N(0, I).
+    """
     rng = np.random.default_rng([w.wid, 1] if seed is None else seed)
     a = rng.standard_normal((w.F, w.d), dtype=np.float32)
-    g = rng.standard_normal((w.F, w.d), dtype=np.float32)
+    if orthogonal:
+        g = np.concatenate([orthogonal_gaussian_rows(rng, w.m, w.d) for _ in range(w.R)]).astype(np.float32)
+    else:
+        g = rng.standard_normal((w.F, w.d), dtype=np.float32)
     return _finish(a, w.dtype), _finish(g, w.dtype)
 
 

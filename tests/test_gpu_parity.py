@@ -342,3 +342,22 @@ def test_decode_graph_replay_matches_eager(lib):
         for t in range(n_in):
             assert torch.equal(outs_g[t], outs_e[t]), (rep, t)
         assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e)
+
+
+@pytest.mark.parametrize("name,L", [("tiny_f32", 200), ("h16_l16k_bf16", 1000)])
+def test_orthogonal_draws_parity(lib, orc, name, L):
+    """Positive orthogonal random features change only the caller's PRF draws:
+    the same kernels, checked against the oracle on orthogonal draws."""
+    w = ss.WORKLOADS[name].with_(H=2, L=L)
+    _say(f"orthogonal draws parity {name} L={L}")
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w, orthogonal=True)
+    o = _run_fwd(lib, w, q, k, v, A, G)
+    ro = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m)[0]
+    err = rownorm_rel(o, ro)
+    _say(f"  causal o rownorm rel err {err:.3e}")
+    assert err < TOL[w.dtype]
+    fm = _fm(lib, w, A, G)
+    on = to_np(lib.noncausal_fwd(fm, to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype)))
+    rn = orc.slay_noncausal(q, k, v, A, G, w.eps, w.R, w.m)[0]
+    assert rownorm_rel(on, rn) < TOL[w.dtype]

@@ -442,3 +442,64 @@ def test_noncausal_initial_state(orc):
     o0 = orc.slay_noncausal(q, k[:, :0], v[:, :0], A, G, EPS, R, m, S0=S1, z0=z1)[0]
     o1 = orc.slay_noncausal(q, k[:, :5], v[:, :5], A, G, EPS, R, m)[0]
     np.testing.assert_allclose(o0, o1, rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# Positive orthogonal random features (linearized 2-simplicial attention page,
+# summary): PRF rows in orthogonal blocks, each row still marginally N(0, I)
+
+def test_orthogonal_draws_structure():
+    import slay_synth as ss
+
+    rng = np.random.default_rng(31)
+    d, n = 16, 16 * 500
+    G = ss.orthogonal_gaussian_rows(rng, n, d)
+    blocks = G.reshape(-1, d, d)
+    gram = np.einsum("bid,bjd->bij", blocks, blocks)
+    off = gram - np.einsum("bii->bi", gram)[:, :, None] * np.eye(d)
+    assert np.abs(off).max() < 1e-9 * np.abs(gram).max()  # orthogonal within a block
+    # marginally N(0, I): squared lengths ~ chi^2(d), coordinates ~ N(0, 1)
+    sq = (G ** 2).sum(1)
+    assert sq.mean() == pytest.approx(d, rel=0.02)
+    assert sq.var() == pytest.approx(2 * d, rel=0.1)
+    assert G.mean() == pytest.approx(0.0, abs=0.02) and G.var() == pytest.approx(1.0, rel=0.03)
+    w = ss.WORKLOADS["tiny_f32"]
+    A, Go = ss.make_draws(w, orthogonal=True)
+    node0 = Go[: w.m]
+    gram0 = node0 @ node0.T
+    assert np.abs(gram0 - np.diag(np.diag(gram0))).max() < 1e-4 * np.abs(gram0).max()
+
+
+@pytest.mark.parametrize("u", [-0.5, 0.0, 0.5])
+def test_orthogonal_prf_unbiased_and_lower_variance(orc, u):
+    """With orthogonal PRF blocks the node mean keeps its closed form (each
+    row is marginally Gaussian), and the variance of one block's estimate
+    over independent blocks is below that of i.i.d. rows (the point of
+    orthogonal features).  Every anchor row is the fixed a = e0 + e1, so the
+    anchor factor (a.q)^2 (a.k)^2 is a constant and all variance comes from
+    the PRF factor; PRF rows scaled to c*g with c = 0.5 keep its log-normal
+    tail light enough for the variance comparison."""
+    import slay_synth as ss
+
+    R, d, c, n_sets = 1, 16, 0.5, 20000
+    m = d * n_sets
+    q = np.zeros(d)
+    q[0] = 1.0
+    k = np.zeros(d)
+    k[0], k[1] = u, math.sqrt(1 - u * u)
+    a = np.zeros(d)
+    a[0] = a[1] = 1.0
+    anchor = (a @ q) ** 2 * (a @ k) ** 2
+    alpha, beta = _params(orc, R)
+    want = anchor * math.exp(beta[0] * c * c * (1 + u) - beta[0])
+    A = np.tile(a, (m, 1))
+    var = {}
+    for kind in ("iid", "orth"):
+        rng = np.random.default_rng([41, int(10 * (u + 1)), kind == "orth"])
+        G = c * (ss.orthogonal_gaussian_rows(rng, m, d) if kind == "orth" else rng.standard_normal((m, d)))
+        phi = orc.featmap(np.stack([q, k]), A, G, EPS, R, m)
+        samples = phi[0] * phi[1] * m / alpha[0]
+        z = (samples.mean() - want) / (samples.std(ddof=1) / math.sqrt(m))
+        assert abs(z) < 4.5, (kind, samples.mean(), want, z)
+        var[kind] = samples.reshape(n_sets, d).mean(1).var()
+    assert var["orth"] < 0.95 * var["iid"], var
