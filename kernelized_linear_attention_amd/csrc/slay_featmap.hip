@@ -17,7 +17,8 @@
 // square / exp2 / scale epilogue straight from the accumulators.  The 1/|x|
 // scale is applied to the fp32 accumulator, (x/|x|).P = (x.P)/|x|, so bf16
 // inputs are never rounded twice.  The tile's features are written back from
-// an LDS staging copy with coalesced 16-byte stores.
+// an LDS staging copy with coalesced 16-byte stores (non-temporal for
+// large launches).
 #include "slay_device.hpp"
 #include "slay_internal.hpp"
 
@@ -27,6 +28,8 @@ namespace {
 
 constexpr int kTileRows = 64;  // rows per tile of large launches
 constexpr int kThreads = 256;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename TI>
 struct XStage {
@@ -217,9 +220,17 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
       const int ppr = fcols * (int)sizeof(TO) / 16;
       for (int pc = threadIdx.x; pc < TR * PPR; pc += kThreads) {
         const int rr = pc / PPR, q = pc - (pc / PPR) * PPR;
-        if (rr < nrow && q < ppr)
-          *reinterpret_cast<uint4*>(reinterpret_cast<char*>(pt + (int64_t)rr * F + blockIdx.y * FWS) + q * 16) =
-              *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(so + rr * LDO) + q * 16);
+        if (rr < nrow && q < ppr) {
+          const u32x4 val = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(so + rr * LDO) + q * 16);
+          u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(pt + (int64_t)rr * F + blockIdx.y * FWS) + q * 16);
+          // Large launches write phi once and never read it back here, so
+          // they stream it with non-temporal stores; small ones (a decode
+          // step's phi(q)) are read by the next kernel and stay cached.
+          if constexpr (TR == kTileRows)
+            __builtin_nontemporal_store(val, dst);
+          else
+            *dst = val;
+        }
       }
     }
     __syncthreads();
