@@ -75,6 +75,11 @@ def _load():
         lib.orc_slay_noncausal.argtypes = [_I64, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_double, _D, _D, _D, _D, _D, _I64, _D, _D,
                                            _D, _D, _D]
+        lib.orc_featmap_vjp.argtypes = [_I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                        _D, _D, _D, _D, _D]
+        lib.orc_slay_causal_bwd.argtypes = [_I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_double, _D, _D, _D, _D, _D, _I64, ctypes.c_int, _D, _D, _D,
+                                            _D, _D, _D, _D, _D, _D, _D]
         _lib = lib
         return lib
 
@@ -292,3 +297,58 @@ def attn_rows(rows, phq_rows, phk, v) -> np.ndarray:
     lib.orc_attn_rows(rows.size, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), F, dv, _p(phq_rows),
                       _p(phk), _p(v), _p(o))
     return o
+
+
+def featmap_vjp(x, anchors, prf, dphi, eps: float, R: int, m: int) -> np.ndarray:
+    """dx = J_phi(x)^T dphi for rows x [n, d] (the feature map's backward)."""
+    lib = _load()
+    x = _f64(x)
+    d = x.shape[-1]
+    x2 = x.reshape(-1, d)
+    a = _f64(anchors).reshape(R * m, d)
+    g = _f64(prf).reshape(R * m, d)
+    dphi = _f64(dphi).reshape(x2.shape[0], R * m)
+    out = np.zeros_like(x2)
+    _check(lib.orc_featmap_vjp(x2.shape[0], d, int(R), int(m), float(eps), _p(x2), _p(a), _p(g), _p(dphi),
+                               _p(out)), "featmap_vjp")
+    return out.reshape(x.shape)
+
+
+BWD_FORMS = {"brute": 0, "recurrent": 1}
+
+
+def slay_causal_bwd(q, k, v, dout, anchors, prf, eps: float, R: int, m: int, form: str = "recurrent",
+                    S0=None, z0=None, dS_T=None, dz_T=None, per_head_draws: bool = False):
+    """Backward of the causal SLAY forward over heads.
+
+    dout: [..., L, dv], the loss gradient with respect to o; dS_T [nh, F, dv],
+    dz_T [nh, F] (optional): with respect to the final state.
+    Returns (dq, dk, dv, dS0 [nh, F, dv], dz0 [nh, F]).
+    """
+    lib = _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    lead = q.shape[:-2]
+    L, d = q.shape[-2:]
+    dv = v.shape[-1]
+    nh = int(np.prod(lead)) if lead else 1
+    F = R * m
+    a = _f64(anchors)
+    g = _f64(prf)
+    stride = F * d if per_head_draws else 0
+    if per_head_draws:
+        assert a.size == nh * F * d and g.size == nh * F * d
+    else:
+        assert a.size == F * d and g.size == F * d
+    assert dout.shape == v.shape
+    opt = lambda t, shape: None if t is None else _f64(t).reshape(shape)
+    S0p, z0p = opt(S0, (nh, F, dv)), opt(z0, (nh, F))
+    dSTp, dzTp = opt(dS_T, (nh, F, dv)), opt(dz_T, (nh, F))
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dvv = np.zeros(v.shape)
+    dS0 = np.zeros((nh, F, dv))
+    dz0 = np.zeros((nh, F))
+    _check(lib.orc_slay_causal_bwd(nh, L, d, dv, int(R), int(m), float(eps), _p(q), _p(k), _p(v), _p(a), _p(g),
+                                   stride, BWD_FORMS[form], _p(S0p), _p(z0p), _p(dout), _p(dSTp), _p(dzTp),
+                                   _p(dq), _p(dk), _p(dvv), _p(dS0), _p(dz0)), "slay_causal_bwd")
+    return dq, dk, dvv, dS0, dz0

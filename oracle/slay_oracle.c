@@ -448,3 +448,270 @@ int orc_slay_noncausal(int64_t nh, int64_t Lq, int64_t Lk, int d, int dv, int R,
   }
   return bad ? ORC_BAD : ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the causal forward.  The gradient of a scalar loss whose
+ * derivative with respect to o is dout (and, optionally, dS_T / dz_T with
+ * respect to the final state) is the chain rule applied to the definitions
+ * above; the pages define only the forward ([SLAY-rev] Proposed method,
+ * bullets 1-6), so every step below is that forward differentiated.          */
+
+/* Vector-Jacobian product of the feature map: dx = J_phi(x)^T dphi.
+ * With y_a = a.xh, y_g = g.xh, e = exp(sqrt(beta) y_g - beta/2) and
+ * phi = sqrt(alpha/m) y_a^2 e:
+ *   d phi / d xh = sqrt(alpha/m) e (2 y_a a + sqrt(beta) y_a^2 g),
+ * and for xh = x / max(|x|, 1e-12):
+ *   d xh / d x = (I - xh xh^T) / |x|   if |x| >= 1e-12,   I / 1e-12 otherwise.  */
+int orc_featmap_vjp(int64_t n, int d, int R, int m, double eps, const double* x,
+                    const double* a, const double* g, const double* dphi, double* dx) {
+  if (n < 0 || d < 1 || R < 1 || m < 1) return ORC_BAD;
+  double* alpha = (double*)malloc(sizeof(double) * (size_t)R);
+  double* beta = (double*)malloc(sizeof(double) * (size_t)R);
+  if (!alpha || !beta) { free(alpha); free(beta); return ORC_BAD; }
+  int st = orc_node_params(R, eps, alpha, beta);
+  if (st != ORC_OK) { free(alpha); free(beta); return st; }
+  const int F = R * m;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t i = 0; i < n; ++i) {
+    const double* xi = x + i * d;
+    double* dxi = dx + i * d;
+    double* xh = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dxh = (double*)calloc((size_t)d, sizeof(double));
+    if (!xh || !dxh) { bad |= 1; free(xh); free(dxh); continue; }
+    double nrm = 0.0;
+    for (int c = 0; c < d; ++c) nrm += xi[c] * xi[c];
+    nrm = sqrt(nrm);
+    const int clamped = nrm < 1e-12;
+    const double nu = clamped ? 1e-12 : nrm;
+    for (int c = 0; c < d; ++c) xh[c] = xi[c] / nu;
+    for (int r = 0; r < R; ++r) {
+      for (int t = 0; t < m; ++t) {
+        const double* ar = a + (size_t)(r * m + t) * d;
+        const double* gr = g + (size_t)(r * m + t) * d;
+        double ya = 0.0, yg = 0.0;
+        for (int c = 0; c < d; ++c) {
+          ya += ar[c] * xh[c];
+          yg += gr[c] * xh[c];
+        }
+        const double scale = sqrt(alpha[r] / m);
+        const double e = exp(sqrt(beta[r]) * yg - 0.5 * beta[r]);
+        const double df = dphi[i * F + r * m + t];
+        for (int c = 0; c < d; ++c)
+          dxh[c] += df * scale * e * (2.0 * ya * ar[c] + sqrt(beta[r]) * ya * ya * gr[c]);
+      }
+    }
+    if (clamped) {
+      for (int c = 0; c < d; ++c) dxi[c] = dxh[c] / nu;
+    } else {
+      double proj = 0.0;
+      for (int c = 0; c < d; ++c) proj += xh[c] * dxh[c];
+      for (int c = 0; c < d; ++c) dxi[c] = (dxh[c] - xh[c] * proj) / nu;
+    }
+    free(xh);
+    free(dxh);
+  }
+  free(alpha);
+  free(beta);
+  return bad ? ORC_BAD : ORC_OK;
+}
+
+/* Feature-space backward of one head.  Forward: s_ij = phq_i . phk_j,
+ * den_i = sum_{j<=i} s_ij + phq_i . z0, num_i = sum_{j<=i} s_ij v_j + S0^T phq_i,
+ * o_i = num_i / den_i, and the final state S_T = S0 + sum_j phk_j v_j^T,
+ * z_T = z0 + sum_j phk_j.  With g_i = dout_i / den_i and
+ * h_i = -(dout_i . o_i) / den_i (the derivatives through num_i and den_i),
+ * ds_ij = g_i . v_j + h_i for j <= i, and
+ *   dphq_i = sum_{j<=i} ds_ij phk_j + S0 g_i + z0 h_i
+ *   dphk_j = sum_{i>=j} ds_ij phq_i + dS_T v_j + dz_T
+ *   dv_j   = sum_{i>=j} s_ij g_i + dS_T^T phk_j
+ *   dS0    = sum_i phq_i g_i^T + dS_T,   dz0 = sum_i phq_i h_i + dz_T.
+ * S0, z0, dS_T, dz_T may be NULL (zero).  Two forms, written independently:
+ * (0) brute force over the pairs (i, j); (1) recurrent: a forward sweep with
+ * the running (S, z) gives o_i, g_i, h_i and dphq_i = S_i g_i + z_i h_i, and
+ * a reverse sweep with U_j = dS_T + sum_{i>=j} phq_i g_i^T,
+ * u_j = dz_T + sum_{i>=j} phq_i h_i gives dphk_j = U_j v_j + u_j and
+ * dv_j = U_j^T phk_j.                                                        */
+static int attn_bwd_head(int form, int64_t L, int F, int dv, const double* phq, const double* phk,
+                         const double* v, const double* S0, const double* z0, const double* dout,
+                         const double* dST, const double* dzT, double* dphq, double* dphk,
+                         double* dvv, double* dS0, double* dz0) {
+  double* g = (double*)malloc(sizeof(double) * (size_t)(L * dv + 1));
+  double* hh = (double*)malloc(sizeof(double) * (size_t)(L + 1));
+  double* S = (double*)calloc((size_t)F * dv, sizeof(double));
+  double* z = (double*)calloc((size_t)F, sizeof(double));
+  double* o = (double*)malloc(sizeof(double) * (size_t)dv);
+  if (!g || !hh || !S || !z || !o) { free(g); free(hh); free(S); free(z); free(o); return ORC_BAD; }
+  if (form == 0) {
+    for (int64_t i = 0; i < L; ++i) {
+      double den = 0.0;
+      for (int e = 0; e < dv; ++e) o[e] = 0.0;
+      for (int64_t j = 0; j <= i; ++j) {
+        double s = 0.0;
+        for (int f = 0; f < F; ++f) s += phq[i * F + f] * phk[j * F + f];
+        den += s;
+        for (int e = 0; e < dv; ++e) o[e] += s * v[j * dv + e];
+      }
+      for (int f = 0; f < F; ++f) {
+        if (z0) den += phq[i * F + f] * z0[f];
+        if (S0)
+          for (int e = 0; e < dv; ++e) o[e] += phq[i * F + f] * S0[(size_t)f * dv + e];
+      }
+      double dot = 0.0;
+      for (int e = 0; e < dv; ++e) {
+        o[e] /= den;
+        dot += dout[i * dv + e] * o[e];
+        g[i * dv + e] = dout[i * dv + e] / den;
+      }
+      hh[i] = -dot / den;
+    }
+    for (int64_t i = 0; i < L; ++i) {
+      for (int f = 0; f < F; ++f) {
+        double acc = 0.0;
+        for (int64_t j = 0; j <= i; ++j) {
+          double ds = hh[i];
+          for (int e = 0; e < dv; ++e) ds += g[i * dv + e] * v[j * dv + e];
+          acc += ds * phk[j * F + f];
+        }
+        if (S0)
+          for (int e = 0; e < dv; ++e) acc += S0[(size_t)f * dv + e] * g[i * dv + e];
+        if (z0) acc += z0[f] * hh[i];
+        dphq[i * F + f] = acc;
+      }
+    }
+    for (int64_t j = 0; j < L; ++j) {
+      for (int f = 0; f < F; ++f) {
+        double acc = 0.0;
+        for (int64_t i = j; i < L; ++i) {
+          double ds = hh[i];
+          for (int e = 0; e < dv; ++e) ds += g[i * dv + e] * v[j * dv + e];
+          acc += ds * phq[i * F + f];
+        }
+        if (dST)
+          for (int e = 0; e < dv; ++e) acc += dST[(size_t)f * dv + e] * v[j * dv + e];
+        if (dzT) acc += dzT[f];
+        dphk[j * F + f] = acc;
+      }
+      for (int e = 0; e < dv; ++e) {
+        double acc = 0.0;
+        for (int64_t i = j; i < L; ++i) {
+          double s = 0.0;
+          for (int f = 0; f < F; ++f) s += phq[i * F + f] * phk[j * F + f];
+          acc += s * g[i * dv + e];
+        }
+        if (dST)
+          for (int f = 0; f < F; ++f) acc += dST[(size_t)f * dv + e] * phk[j * F + f];
+        dvv[j * dv + e] = acc;
+      }
+    }
+    for (int f = 0; f < F; ++f) {
+      for (int e = 0; e < dv; ++e) {
+        double acc = dST ? dST[(size_t)f * dv + e] : 0.0;
+        for (int64_t i = 0; i < L; ++i) acc += phq[i * F + f] * g[i * dv + e];
+        if (dS0) dS0[(size_t)f * dv + e] = acc;
+      }
+      double acc = dzT ? dzT[f] : 0.0;
+      for (int64_t i = 0; i < L; ++i) acc += phq[i * F + f] * hh[i];
+      if (dz0) dz0[f] = acc;
+    }
+  } else {
+    if (S0) memcpy(S, S0, sizeof(double) * (size_t)F * dv);
+    if (z0) memcpy(z, z0, sizeof(double) * (size_t)F);
+    for (int64_t i = 0; i < L; ++i) {
+      for (int f = 0; f < F; ++f) {
+        const double kf = phk[i * F + f];
+        for (int e = 0; e < dv; ++e) S[(size_t)f * dv + e] += kf * v[i * dv + e];
+        z[f] += kf;
+      }
+      double den = 0.0;
+      for (int f = 0; f < F; ++f) den += phq[i * F + f] * z[f];
+      double dot = 0.0;
+      for (int e = 0; e < dv; ++e) {
+        double num = 0.0;
+        for (int f = 0; f < F; ++f) num += phq[i * F + f] * S[(size_t)f * dv + e];
+        dot += dout[i * dv + e] * (num / den);
+        g[i * dv + e] = dout[i * dv + e] / den;
+      }
+      hh[i] = -dot / den;
+      for (int f = 0; f < F; ++f) {
+        double acc = z[f] * hh[i];
+        for (int e = 0; e < dv; ++e) acc += S[(size_t)f * dv + e] * g[i * dv + e];
+        dphq[i * F + f] = acc;
+      }
+    }
+    /* reverse sweep: S, z now hold U, u */
+    for (int f = 0; f < F; ++f) {
+      for (int e = 0; e < dv; ++e) S[(size_t)f * dv + e] = dST ? dST[(size_t)f * dv + e] : 0.0;
+      z[f] = dzT ? dzT[f] : 0.0;
+    }
+    for (int64_t j = L - 1; j >= 0; --j) {
+      for (int f = 0; f < F; ++f) {
+        const double qf = phq[j * F + f];
+        for (int e = 0; e < dv; ++e) S[(size_t)f * dv + e] += qf * g[j * dv + e];
+        z[f] += qf * hh[j];
+      }
+      for (int f = 0; f < F; ++f) {
+        double acc = z[f];
+        for (int e = 0; e < dv; ++e) acc += S[(size_t)f * dv + e] * v[j * dv + e];
+        dphk[j * F + f] = acc;
+      }
+      for (int e = 0; e < dv; ++e) {
+        double acc = 0.0;
+        for (int f = 0; f < F; ++f) acc += S[(size_t)f * dv + e] * phk[j * F + f];
+        dvv[j * dv + e] = acc;
+      }
+    }
+    if (dS0) memcpy(dS0, S, sizeof(double) * (size_t)F * dv);
+    if (dz0) memcpy(dz0, z, sizeof(double) * (size_t)F);
+  }
+  free(g);
+  free(hh);
+  free(S);
+  free(z);
+  free(o);
+  return ORC_OK;
+}
+
+/* Whole causal SLAY backward over nh heads (parallel over heads): given the
+ * forward's inputs and dout [nh][L][dv] (and nullable dS_T [nh][F][dv],
+ * dz_T [nh][F]), returns dq, dk [nh][L][d], dv [nh][L][dv] and nullable
+ * dS0 [nh][F][dv], dz0 [nh][F].  The draws are constants (random features
+ * are not trained).  form: 0 brute force, 1 recurrent.                       */
+int orc_slay_causal_bwd(int64_t nh, int64_t L, int d, int dv, int R, int m, double eps,
+                        const double* q, const double* k, const double* v, const double* a,
+                        const double* g, int64_t draw_head_stride, int form, const double* S0,
+                        const double* z0, const double* dout, const double* dS_T, const double* dz_T,
+                        double* dq, double* dk, double* dvv, double* dS0, double* dz0) {
+  if (nh < 0 || L < 0 || d < 1 || dv < 1 || R < 1 || m < 1 || (form != 0 && form != 1)) return ORC_BAD;
+  const int F = R * m;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t h = 0; h < nh; ++h) {
+    const double* ah = a + (draw_head_stride > 0 ? h * draw_head_stride : 0);
+    const double* gh = g + (draw_head_stride > 0 ? h * draw_head_stride : 0);
+    const size_t nf = (size_t)(L * F + 1);
+    double* phq = (double*)malloc(sizeof(double) * nf);
+    double* phk = (double*)malloc(sizeof(double) * nf);
+    double* dphq = (double*)malloc(sizeof(double) * nf);
+    double* dphk = (double*)malloc(sizeof(double) * nf);
+    if (!phq || !phk || !dphq || !dphk) {
+      bad |= 1;
+      free(phq); free(phk); free(dphq); free(dphk);
+      continue;
+    }
+    bad |= orc_featmap(L, d, R, m, eps, q + h * L * d, ah, gh, phq);
+    bad |= orc_featmap(L, d, R, m, eps, k + h * L * d, ah, gh, phk);
+    const int64_t sF = (int64_t)F * dv;
+    bad |= attn_bwd_head(form, L, F, dv, phq, phk, v + h * L * dv, S0 ? S0 + h * sF : NULL,
+                         z0 ? z0 + h * (int64_t)F : NULL, dout + h * L * dv, dS_T ? dS_T + h * sF : NULL,
+                         dz_T ? dz_T + h * (int64_t)F : NULL, dphq, dphk, dvv + h * L * dv,
+                         dS0 ? dS0 + h * sF : NULL, dz0 ? dz0 + h * (int64_t)F : NULL);
+    bad |= orc_featmap_vjp(L, d, R, m, eps, q + h * L * d, ah, gh, dphq, dq + h * L * d);
+    bad |= orc_featmap_vjp(L, d, R, m, eps, k + h * L * d, ah, gh, dphk, dk + h * L * d);
+    free(phq);
+    free(phk);
+    free(dphq);
+    free(dphk);
+  }
+  return bad ? ORC_BAD : ORC_OK;
+}

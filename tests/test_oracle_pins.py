@@ -503,3 +503,135 @@ def test_orthogonal_prf_unbiased_and_lower_variance(orc, u):
         assert abs(z) < 4.5, (kind, samples.mean(), want, z)
         var[kind] = samples.reshape(n_sets, d).mean(1).var()
     assert var["orth"] < 0.95 * var["iid"], var
+
+
+# ----------------------------------------------------------------------------
+# Backward of the causal forward (review, "Proposed method" bullets 1-6,
+# differentiated).  Pinned to the forward by central finite differences on
+# every argument, to closed forms of degenerate inputs, and to invariants.
+
+def _bwd_inputs(seed, nh=2, L=7, d=4, dv=3, R=2, m=2):
+    rng = np.random.default_rng(seed)
+    F = R * m
+    t = dict(q=rng.standard_normal((nh, L, d)), k=rng.standard_normal((nh, L, d)),
+             v=rng.standard_normal((nh, L, dv)), a=rng.standard_normal((F, d)), g=rng.standard_normal((F, d)),
+             S0=np.abs(rng.standard_normal((nh, F, dv))), z0=np.abs(rng.standard_normal((nh, F))),
+             do=rng.standard_normal((nh, L, dv)), dST=rng.standard_normal((nh, F, dv)),
+             dzT=rng.standard_normal((nh, F)))
+    return rng, t, R, m
+
+
+@pytest.mark.parametrize("form", ["brute", "recurrent"])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_backward_matches_finite_differences(orc, form, with_state):
+    rng, t, R, m = _bwd_inputs(51 + with_state)
+    S0, z0 = (t["S0"], t["z0"]) if with_state else (None, None)
+    dST, dzT = (t["dST"], t["dzT"]) if with_state else (None, None)
+
+    def loss(q, k, v, S0_, z0_):
+        o, S, z = orc.slay_causal(q, k, v, t["a"], t["g"], EPS, R, m, "recurrent", S0=S0_, z0=z0_)
+        val = float((o * t["do"]).sum())
+        if with_state:
+            val += float((S * dST).sum() + (z * dzT).sum())
+        return val
+
+    grads = orc.slay_causal_bwd(t["q"], t["k"], t["v"], t["do"], t["a"], t["g"], EPS, R, m, form, S0=S0, z0=z0,
+                                dS_T=dST, dz_T=dzT)
+    args = [t["q"], t["k"], t["v"], t["S0"], t["z0"]]
+    n_args = 5 if with_state else 3
+    if not with_state:  # without a given initial state the loss still has a gradient w.r.t. a zero one
+        args[3], args[4] = np.zeros_like(t["S0"]), np.zeros_like(t["z0"])
+        # a zero z0 keeps den > 0 only for positive perturbations: check dS0, dz0 by one-sided steps below
+    h = 1e-5
+    for idx in range(n_args):
+        for _ in range(2):
+            dirn = rng.standard_normal(args[idx].shape)
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[idx] += h * dirn
+            am[idx] -= h * dirn
+            fd = (loss(*ap) - loss(*am)) / (2 * h)
+            an = float((grads[idx] * dirn).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (form, idx, fd, an)
+    if not with_state:
+        # gradient with respect to a zero initial state, by a small one-sided positive step
+        dS0, dz0 = grads[3], grads[4]
+        for idx, gr in ((3, dS0), (4, dz0)):
+            dirn = np.abs(rng.standard_normal(args[idx].shape))
+            ap = [x.copy() for x in args]
+            ap[idx] = ap[idx] + 1e-7 * dirn
+            ap2 = [x.copy() for x in args]
+            ap2[idx] = ap2[idx] + 2e-7 * dirn
+            base = loss(*args)
+            fd = (4 * loss(*ap) - loss(*ap2) - 3 * base) / (2 * 1e-7)  # second-order one-sided difference
+            an = float((gr * dirn).sum())
+            assert abs(fd - an) <= 1e-5 * max(1.0, abs(an)), (idx, fd, an)
+
+
+def test_featmap_vjp_finite_differences(orc):
+    rng = np.random.default_rng(57)
+    R, m, d, n = 3, 4, 6, 9
+    F = R * m
+    x = rng.standard_normal((n, d)) * rng.uniform(0.1, 5.0, (n, 1))
+    x[0] *= 1e-14 / np.linalg.norm(x[0])  # below the 1e-12 norm clamp: phi is a function of x / 1e-12
+    a, g = rng.standard_normal((F, d)), rng.standard_normal((F, d))
+    dphi = rng.standard_normal((n, F))
+    dx = orc.featmap_vjp(x, a, g, dphi, EPS, R, m)
+    for i in range(n):
+        h = 1e-6 * np.linalg.norm(x[i])
+        for _ in range(3):
+            dirn = rng.standard_normal(d)
+            fp = orc.featmap(x[i:i + 1] + h * dirn, a, g, EPS, R, m)
+            fm = orc.featmap(x[i:i + 1] - h * dirn, a, g, EPS, R, m)
+            fd = float(((fp - fm) * dphi[i]).sum()) / (2 * h)
+            an = float(dx[i] @ dirn)
+            assert abs(fd - an) <= 1e-6 * np.abs(dx[i]).sum() * np.abs(dirn).max() + 1e-300, (i, fd, an)
+    # away from the clamp phi depends on x / |x| only: the gradient is orthogonal to x
+    cos = np.abs((dx[1:] * x[1:]).sum(1)) / (np.linalg.norm(dx[1:], axis=1) * np.linalg.norm(x[1:], axis=1))
+    assert cos.max() < 1e-12
+
+
+def test_backward_forms_agree(orc):
+    rng, t, R, m = _bwd_inputs(53, nh=3, L=40, d=8, dv=5, R=3, m=4)
+    outs = [orc.slay_causal_bwd(t["q"], t["k"], t["v"], t["do"], t["a"], t["g"], EPS, R, m, form,
+                                S0=t["S0"], z0=t["z0"], dS_T=t["dST"], dz_T=t["dzT"])
+            for form in ("brute", "recurrent")]
+    for x, y in zip(*outs):
+        assert np.abs(x - y).max() <= 1e-11 * np.abs(x).max()
+
+
+def test_backward_identical_keys(orc):
+    """All keys equal, no initial state: every score of row i is the same, so
+    o_i is the prefix mean of v whatever q is.  Then dq = 0,
+    dv_j = sum_{i>=j} dout_i/(i+1), and moving every key together leaves o
+    unchanged, so sum_j dk_j = 0."""
+    rng = np.random.default_rng(55)
+    nh, L, d, dv, R, m = 2, 9, 5, 3, 2, 4
+    F = R * m
+    q = rng.standard_normal((nh, L, d))
+    k = np.repeat(rng.standard_normal((nh, 1, d)), L, axis=1)
+    v = rng.standard_normal((nh, L, dv))
+    do = rng.standard_normal((nh, L, dv))
+    a, g = rng.standard_normal((F, d)), rng.standard_normal((F, d))
+    dq, dk, dvv, _, _ = orc.slay_causal_bwd(q, k, v, do, a, g, EPS, R, m)
+    assert np.abs(dq).max() <= 1e-12 * np.abs(do).max()
+    want = np.flip(np.cumsum(np.flip(do / np.arange(1, L + 1)[None, :, None], 1), 1), 1)
+    np.testing.assert_allclose(dvv, want, rtol=1e-12, atol=1e-14)
+    assert np.abs(dk.sum(1)).max() <= 1e-11 * np.abs(dk).max()
+
+
+def test_backward_homogeneity(orc):
+    """o and the final state S_T are linear in (v, S0) and do not depend on
+    the lengths of q and k rows: Euler's identity gives
+    sum dv.v + sum dS0.S0 = sum dout.o + sum dS_T.S_T, and each row of dq, dk
+    is orthogonal to its row of q, k."""
+    rng, t, R, m = _bwd_inputs(59, nh=2, L=12, d=6, dv=4, R=2, m=4)
+    dq, dk, dvv, dS0, dz0 = orc.slay_causal_bwd(t["q"], t["k"], t["v"], t["do"], t["a"], t["g"], EPS, R, m,
+                                                S0=t["S0"], z0=t["z0"], dS_T=t["dST"], dz_T=t["dzT"])
+    o, S, _ = orc.slay_causal(t["q"], t["k"], t["v"], t["a"], t["g"], EPS, R, m, S0=t["S0"], z0=t["z0"])
+    lhs = (dvv * t["v"]).sum() + (dS0 * t["S0"]).sum()
+    rhs = (t["do"] * o).sum() + (t["dST"] * S).sum()
+    assert abs(lhs - rhs) <= 1e-12 * (abs(lhs) + abs(rhs))
+    for dx, x in ((dq, t["q"]), (dk, t["k"])):
+        dots = np.abs((dx * x).sum(-1)) / (np.linalg.norm(dx, axis=-1) * np.linalg.norm(x, axis=-1))
+        assert dots.max() < 1e-12
