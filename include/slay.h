@@ -114,6 +114,42 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
                                     int32_t chunk, const float* S0, const float* z0, void* o, float* S_out,
                                     float* z_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes slay_attn_chunked_bwd needs for this shape (0 is possible). */
+size_t slay_attn_chunked_bwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t L,
+                                            int32_t dv, int32_t chunk, slay_dtype_t io_dtype);
+
+/* Backward of slay_attn_chunked_fwd: the gradients of a scalar loss with
+ * respect to q, k, v and the initial state, given its gradients with
+ * respect to o and (optionally) the final state.  The pages define the
+ * forward (review, "Proposed method" bullets 1-6); this is that forward
+ * differentiated.  With g_i = dout_i / den_i and h_i = -(dout_i . o_i) / den_i
+ * (den_i = phi(q_i)^T z_i):
+ *   dphi(q_i) = S_i g_i + z_i h_i,
+ *   dphi(k_j) = U_j v_j + u_j,  dv_j = U_j^T phi(k_j),
+ *   U_j = dS_T + sum_{i>=j} phi(q_i) g_i^T,  u_j = dz_T + sum_{i>=j} phi(q_i) h_i,
+ *   dS0 = U_0, dz0 = u_0,
+ * and dq, dk through the feature map's Jacobian (including the projection
+ * onto the sphere).  The draws are constants: no gradient is returned for them.
+ *   q, k, dq, dk : device [B][H][L][d];  v, dout, dv : device [B][H][L][dv];
+ *          dtype io_dtype (must equal the draw dtype); fp32 accumulation,
+ *          gradients rounded to io_dtype (RNE).
+ *   S0, z0     : nullable device fp32 initial state of the forward (as given to it);
+ *   dS_T, dz_T : nullable device fp32 gradients of the final state [B*H][R*m][dv],
+ *                [B*H][R*m] (NULL = zero);
+ *   dS0, dz0   : nullable device fp32 outputs, gradients of the initial state
+ *                (same shapes; may alias dS_T, dz_T);
+ *   workspace  : device scratch of at least
+ *                slay_attn_chunked_bwd_workspace_size(...) bytes (NULL if 0).
+ * chunk in [1, 128] only changes the summation order; dv <= 256.  L = 0 sets
+ * dS0 = dS_T and dz0 = dz_T (zero where those are NULL).
+ * Unfused general kernels (the feature map to the workspace, per-chunk
+ * states with a forward prefix and a reverse suffix, FMA contractions). */
+slay_status_t slay_attn_chunked_bwd(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                    const void* dout, slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L,
+                                    int32_t dv, int32_t chunk, const float* S0, const float* z0, const float* dS_T,
+                                    const float* dz_T, void* dq, void* dk, void* dv_out, float* dS0, float* dz0,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes slay_attn_noncausal_fwd needs for this shape (0 is possible). */
 size_t slay_attn_noncausal_fwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t Lq,
                                               int64_t Lk, int32_t dv, slay_dtype_t io_dtype);

@@ -295,6 +295,88 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
   return device_status(fused ? slay::launch_fused(a, s) : slay::launch_generic(a, s), "slay_attn_chunked_fwd launch");
 }
 
+}  // extern "C"
+
+namespace {
+slay::BackwardArgs backward_args(const slay_params_t* p, slay_dtype_t dt, int32_t B, int32_t H, int64_t L,
+                                 int32_t dv, int32_t chunk) {
+  slay::BackwardArgs a{};
+  a.io_bf16 = dt == SLAY_BF16;
+  a.n_heads = (int64_t)B * H;
+  a.L = L;
+  a.d = p->d;
+  a.dv = dv;
+  a.F = p->R * p->m;
+  a.m = p->m;
+  a.R = p->R;
+  a.chunk = chunk;
+  a.anchors = p->anchors;
+  a.prf = p->prf;
+  a.draw_set_stride = p->draw_set_stride;
+  a.n_draw_sets = p->n_draw_sets;
+  return a;
+}
+}  // namespace
+
+extern "C" {
+
+size_t slay_attn_chunked_bwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t L,
+                                            int32_t dv, int32_t chunk, slay_dtype_t io_dtype) {
+  if (check_params(params) != SLAY_OK || B < 0 || H < 0 || L < 0 || dv < 1 || chunk < 1) return 0;
+  return slay::backward_workspace_bytes(backward_args(params, io_dtype, B, H, L, dv, chunk));
+}
+
+slay_status_t slay_attn_chunked_bwd(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                    const void* dout, slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L,
+                                    int32_t dv, int32_t chunk, const float* S0, const float* z0, const float* dS_T,
+                                    const float* dz_T, void* dq, void* dk, void* dv_out, float* dS0, float* dz0,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  slay_status_t st = check_params(params);
+  if (st != SLAY_OK) return st;
+  if (B < 0 || H < 0 || L < 0) return fail(SLAY_E_INVALID, "B, H, L must be >= 0");
+  if (dv < 1) return fail(SLAY_E_INVALID, "dv must be >= 1");
+  if (chunk < 1 || chunk > 128) return fail(SLAY_E_INVALID, "chunk = %d outside [1, 128]", chunk);
+  if (io_dtype != SLAY_F32 && io_dtype != SLAY_BF16) return fail(SLAY_E_INVALID, "bad io dtype");
+  if (io_dtype != params->draw_dtype) return fail(SLAY_E_UNSUPPORTED, "io dtype must equal the draw dtype");
+  const int64_t nh = (int64_t)B * H;
+  const int F = params->R * params->m;
+  if (!mul_ok(nh, L) || !mul_ok(nh * L, std::max<int64_t>(params->d, dv)) || !mul_ok(nh * L, 4 * F))
+    return fail(SLAY_E_INVALID, "problem size overflows");
+  const bool tokens = nh > 0 && L > 0;
+  if (tokens) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv_out) return fail(SLAY_E_INVALID, "q/k/v/dout/dq/dk/dv pointer is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv_out))
+      return fail(SLAY_E_INVALID, "q/k/v/dout/dq/dk/dv must be 16-byte aligned");
+  }
+  slay::BackwardArgs a = backward_args(params, io_dtype, B, H, L, dv, chunk);
+  if (!slay::backward_supported(a))
+    return fail(SLAY_E_UNSUPPORTED, "backward shape not supported (d=%d dv=%d F=%d chunk=%d)", params->d, dv, F,
+                chunk);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.nc = node_consts(params->R, params->m, params->eps);
+  a.S0 = S0;
+  a.z0 = z0;
+  a.dS_T = dS_T;
+  a.dz_T = dz_T;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv_out = dv_out;
+  a.dS0 = dS0;
+  a.dz0 = dz0;
+  a.ws = workspace;
+  a.ws_bytes = workspace_bytes;
+  const size_t need = slay::backward_workspace_bytes(a);
+  if (workspace_bytes < need) return fail(SLAY_E_INVALID, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (need > 0 && !workspace) return fail(SLAY_E_INVALID, "workspace is NULL");
+  if (need > 0 && !aligned16(workspace)) return fail(SLAY_E_INVALID, "workspace must be 16-byte aligned");
+  if (nh == 0) return ok();
+  return device_status(slay::launch_backward(a, static_cast<hipStream_t>(stream)), "slay_attn_chunked_bwd launch");
+}
+
 size_t slay_attn_noncausal_fwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t Lq,
                                                int64_t Lk, int32_t dv, slay_dtype_t io_dtype) {
   if (check_params(params) != SLAY_OK || B < 0 || H < 0 || Lq < 0 || Lk < 0 || dv < 1) return 0;

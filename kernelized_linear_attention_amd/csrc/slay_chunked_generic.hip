@@ -40,7 +40,8 @@ __device__ __forceinline__ void scan_map(int64_t idx, int F, int dv, int layout,
   }
 }
 
-// In-place exclusive prefix over items: item i <- init + sum_{i' < i} delta_i'.
+// In-place exclusive prefix over items: item i <- init + sum_{i' < i} delta_i'
+// (or, reversed, the exclusive suffix init + sum_{i' > i} delta_i').
 __global__ __launch_bounds__(kGThreads) void scan_kernel(ScanArgs a, int64_t E) {
   const int64_t h = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
@@ -53,16 +54,18 @@ __global__ __launch_bounds__(kGThreads) void scan_kernel(ScanArgs a, int64_t E) 
   } else if (e == a.dv) {
     if (a.z0) run = a.z0[h * a.F + f];
   }
-  float* st = a.states + h * a.n_items * E + idx;
+  // a reverse scan walks the items from the last one: item i at st[(n_items - 1 - i) * step]
+  const int64_t step = a.reverse ? -E : E;
+  float* st = a.states + h * a.n_items * E + idx + (a.reverse ? (a.n_items - 1) * E : 0);
   // loads of a batch of items are issued together, then the running sums stored
   constexpr int kBatch = 16;
   for (int64_t i0 = 0; i0 < a.n_items; i0 += kBatch) {
     float d[kBatch];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) d[b] = (i0 + b < a.n_terms) ? st[(i0 + b) * E] : 0.f;
+    for (int b = 0; b < kBatch; ++b) d[b] = (i0 + b < a.n_terms) ? st[(i0 + b) * step] : 0.f;
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      if (i0 + b < a.n_items) st[(i0 + b) * E] = run;
+      if (i0 + b < a.n_items) st[(i0 + b) * step] = run;
       run += d[b];
     }
   }
@@ -309,6 +312,20 @@ hipError_t launch_generic_nc_t(const ChunkedArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_chunk_state(const float* phik, const void* v, bool v_bf16, int64_t n_heads, int64_t L, int F,
+                              int dv, int C, int64_t item_stride, float* states, hipStream_t s) {
+  const int64_t n_chunks = (L + C - 1) / C;
+  if (n_heads == 0 || n_chunks == 0) return hipSuccess;
+  const dim3 grid((unsigned)n_chunks, (unsigned)n_heads);
+  if (v_bf16)
+    hipLaunchKernelGGL(chunk_state_kernel<uint16_t>, grid, dim3(kGThreads), 0, s, phik,
+                       static_cast<const uint16_t*>(v), L, F, dv, C, item_stride, states);
+  else
+    hipLaunchKernelGGL(chunk_state_kernel<float>, grid, dim3(kGThreads), 0, s, phik, static_cast<const float*>(v),
+                       L, F, dv, C, item_stride, states);
+  return hipGetLastError();
+}
 
 int64_t scan_state_elems(int F, int dv, int layout) {
   return layout == 0 ? (int64_t)F * (dv + 1) : (int64_t)F * (dv + 16);

@@ -76,9 +76,45 @@ struct ScanArgs {
   const float* z0;
   float* S_out;       // nullable: init + sum of all n_terms items
   float* z_out;
+  bool reverse;       // suffix instead of prefix: item i <- init + sum_{i' > i} item i' (n_terms == n_items)
 };
 int64_t scan_state_elems(int F, int dv, int layout);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+
+// Per-chunk states dS_c = phi(k_c)^T [v_c | 1] of the general path, fp32
+// [n_heads][item_stride][F][dv+1] (chunk c at item c).
+hipError_t launch_chunk_state(const float* phik, const void* v, bool v_bf16, int64_t n_heads, int64_t L, int F,
+                              int dv, int C, int64_t item_stride, float* states, hipStream_t s);
+
+// Backward of the causal chunked forward.
+struct BackwardArgs {
+  const void* q;     // [n_heads][L][d]
+  const void* k;
+  const void* v;     // [n_heads][L][dv]
+  const void* dout;  // [n_heads][L][dv]
+  bool io_bf16;
+  int64_t n_heads, L;
+  int d, dv, F, m, R, chunk;
+  const void* anchors;
+  const void* prf;
+  int64_t draw_set_stride;
+  int n_draw_sets;
+  NodeConsts nc;
+  const float* S0;    // nullable [n_heads][F][dv]
+  const float* z0;    // nullable [n_heads][F]
+  const float* dS_T;  // nullable gradient of the final state
+  const float* dz_T;
+  void* dq;           // [n_heads][L][d]
+  void* dk;
+  void* dv_out;       // [n_heads][L][dv]
+  float* dS0;         // nullable [n_heads][F][dv]
+  float* dz0;         // nullable [n_heads][F]
+  void* ws;
+  size_t ws_bytes;
+};
+bool backward_supported(const BackwardArgs& a);
+size_t backward_workspace_bytes(const BackwardArgs& a);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 
 // Recurrent decode step.
 struct DecodeArgs {

@@ -152,6 +152,55 @@ def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     return out
 
 
+def chunked_bwd_workspace_size(fm: FeatureMap, B: int, H: int, L: int, dv: int, chunk: int,
+                               dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.slay_attn_chunked_bwd_workspace_size(fm.c_params(), B, H, L, dv, chunk, _dtype_code(dtype)))
+
+
+def chunked_bwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor, chunk: int,
+                S0: torch.Tensor | None = None, z0: torch.Tensor | None = None, dS_T: torch.Tensor | None = None,
+                dz_T: torch.Tensor | None = None, state_grad: bool = False, workspace: torch.Tensor | None = None,
+                dq=None, dk=None, dv=None, dS0=None, dz0=None):
+    """Backward of chunked_fwd.  Given dout [B, H, L, dv] (and optionally the
+    gradient of the final state dS_T [B*H, F, dv], dz_T [B*H, F]), returns
+    (dq, dk, dv), plus (dS0, dz0) when state_grad is set."""
+    lib = _lib.load()
+    B, H, L, d = q.shape
+    dvn = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.shape, q.dtype)
+    _need(v, "v", (B, H, L, dvn), q.dtype)
+    _need(dout, "dout", (B, H, L, dvn), q.dtype)
+    for t, name, shp in ((S0, "S0", (B * H, fm.F, dvn)), (z0, "z0", (B * H, fm.F)),
+                         (dS_T, "dS_T", (B * H, fm.F, dvn)), (dz_T, "dz_T", (B * H, fm.F))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", q.shape, q.dtype)
+    _need(dk, "dk", q.shape, q.dtype)
+    _need(dv, "dv", v.shape, q.dtype)
+    if state_grad:
+        if dS0 is None:
+            dS0 = torch.empty((B * H, fm.F, dvn), dtype=torch.float32, device=q.device)
+        if dz0 is None:
+            dz0 = torch.empty((B * H, fm.F), dtype=torch.float32, device=q.device)
+    nbytes = chunked_bwd_workspace_size(fm, B, H, L, dvn, chunk, q.dtype)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.slay_attn_chunked_bwd(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                   _dtype_code(q.dtype), B, H, L, dvn, chunk, _ptr(S0), _ptr(z0), _ptr(dS_T),
+                                   _ptr(dz_T), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _ptr(dS0), _ptr(dz0),
+                                   _ptr(workspace), wsz, _stream(q))
+    _lib.check(st, "slay_attn_chunked_bwd")
+    if state_grad:
+        return dq, dk, dv, dS0, dz0
+    return dq, dk, dv
+
+
 def noncausal_fwd_workspace_size(fm: FeatureMap, B: int, H: int, Lq: int, Lk: int, dv: int,
                                  dtype: torch.dtype) -> int:
     lib = _lib.load()

@@ -11,7 +11,8 @@ available; these synthetic inputs stand in for them):
   in fp32 and, for bf16 workloads, rounded to bf16 (RNE).  The anchor and PRF
   draws are i.i.d. N(0, 1) of shape [R*m, d] (row r*m + t), rounded to bf16
   for bf16 workloads.  Seeds: inputs use ``default_rng([workload_id, 0])``,
-  draws ``[workload_id, 1]``, decode step t ``[workload_id, 2, t]``.
+  draws ``[workload_id, 1]``, decode step t ``[workload_id, 2, t]``, loss
+gradients for the backward ``[workload_id, 3]``.
 """
 from __future__ import annotations
 
@@ -142,3 +143,14 @@ def make_decode_step(w: Workload, t: int, n_heads: int | None = None):
     k = rng.standard_normal((nh, w.d), dtype=np.float32)
     v = rng.standard_normal((nh, w.dv), dtype=np.float32)
     return _finish(_unit_rows(q), w.dtype), _finish(_unit_rows(k), w.dtype), _finish(v, w.dtype)
+
+
+def make_grads(w: Workload, seed=None):
+    """Loss gradients for the backward: dout [B, H, L, dv] ~ N(0, 1) (bf16-exact
+    for bf16 workloads) and final-state gradients dS_T [B*H, F, dv],
+    dz_T [B*H, F] ~ N(0, 1) in fp32."""
+    rng = np.random.default_rng([w.wid, 3] if seed is None else seed)
+    dout = rng.standard_normal((w.B, w.H, w.L, w.dv), dtype=np.float32)
+    dS = rng.standard_normal((w.n_heads, w.F, w.dv), dtype=np.float32)
+    dz = rng.standard_normal((w.n_heads, w.F), dtype=np.float32)
+    return _finish(dout, w.dtype), dS, dz

@@ -191,3 +191,38 @@ def test_noncausal_validation_and_workspace(lib):
     assert n == 4 * ((100 + 256) * 32 + 5 * 32 * 65)
     # nothing to do
     assert _nc(lib, p, B=0) == _lib.SLAY_OK
+
+
+def _bwd(lib, p, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, do=FAKE, dt=_lib.SLAY_BF16, B=1, H=16, L=16384, dv=64, chunk=64, S0=None,
+                z0=None, dST=None, dzT=None, dq=FAKE, dk=FAKE, dvo=FAKE, dS0=None, dz0=None, ws=None, ws_bytes=0)
+    args.update(kw)
+    a = args
+    return lib.slay_attn_chunked_bwd(ctypes.byref(p) if p is not None else None, a["q"], a["k"], a["v"], a["do"],
+                                     a["dt"], a["B"], a["H"], a["L"], a["dv"], a["chunk"], a["S0"], a["z0"], a["dST"],
+                                     a["dzT"], a["dq"], a["dk"], a["dvo"], a["dS0"], a["dz0"], a["ws"], a["ws_bytes"],
+                                     None)
+
+
+def test_backward_validation_and_workspace(lib):
+    E_INV, E_UNS = _lib.SLAY_E_INVALID, _lib.SLAY_E_UNSUPPORTED
+    p = _params()
+    assert _bwd(lib, None) == E_INV
+    assert _bwd(lib, p, L=-1) == E_INV
+    assert _bwd(lib, p, dv=0) == E_INV
+    assert _bwd(lib, p, chunk=0) == E_INV and _bwd(lib, p, chunk=129) == E_INV
+    assert _bwd(lib, p, dt=_lib.SLAY_F32) == E_UNS
+    assert _bwd(lib, p, dv=512) == E_UNS
+    for name in ("q", "k", "v", "do", "dq", "dk", "dvo"):
+        assert _bwd(lib, p, **{name: None}) == E_INV, name
+        assert _bwd(lib, p, **{name: FAKE + 4}) == E_INV, name
+    assert _bwd(lib, p) == E_INV and b"workspace too small" in lib.slay_last_error()
+    # phi(q), phi(k), dphi(q), dphi(k), g' per token, one state per 64-token chunk
+    n = lib.slay_attn_chunked_bwd_workspace_size(ctypes.byref(p), 1, 16, 16384, 64, 64, _lib.SLAY_BF16)
+    rows = 16 * 16384
+    assert n == 4 * (4 * rows * 256 + rows * 65 + 16 * 256 * 256 * 65)
+    assert _bwd(lib, p, ws=FAKE, ws_bytes=n - 1) == E_INV
+    assert _bwd(lib, p, ws=None, ws_bytes=n) == E_INV
+    # nothing to do, and no tokens (only the state gradient passes through; no pointers needed)
+    assert lib.slay_attn_chunked_bwd_workspace_size(ctypes.byref(p), 1, 16, 0, 64, 64, _lib.SLAY_BF16) == 0
+    assert _bwd(lib, p, B=0) == _lib.SLAY_OK
