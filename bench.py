@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 WORKLOAD = "h16_l16k_bf16"
 DECODE = "decode_256x16_f32"
 KERNEL_SOURCES = ("slay_chunked_fused.hip", "slay_chunked_generic.hip", "slay_featmap.hip", "slay_decode.hip",
-                  "slay_device.hpp")
+                  "slay_backward.hip", "slay_device.hpp")
 
 
 def fwd_flops_per_token_head(w) -> int:
@@ -50,6 +50,20 @@ def noncausal_flops_per_token_head(w) -> int:
     """Non-causal forward with Lq = Lk: q and k feature maps (4dF each), the
     state phi(k) [v | 1]^T (2F(dv+1)) and the readout phi(q)^T [S | z] (2F(dv+1))."""
     return 8 * w.d * w.F + 4 * w.F * (w.dv + 1)
+
+
+def bwd_flops_per_token_head(w) -> int:
+    """Algorithmic flops of the causal backward per (token, head), each product once.
+
+    feature maps of q and k (8dF) and their VJPs dxh = P^T w (8dF);
+    F x (dv+1) products per token: the chunk states phi(k) v'^T, the readout
+    phi(q) S', dphi(q) = S' g', the reverse state phi(q) g'^T, dphi(k) = U v'
+    (5 x 2F(dv+1)) and dv = U^T phi(k) (2F dv);
+    causal halves of the C x C blocks: A = phi(Q) phi(K)^T, D^T phi(Q) and
+    D phi(K) ((C+1)F each), A V' and D = G' V'^T ((C+1)(dv+1) each), A^T G ((C+1)dv).
+    """
+    F, d, dv, C = w.F, w.d, w.dv, w.chunk
+    return 16 * d * F + 10 * F * (dv + 1) + 2 * F * dv + 3 * (C + 1) * F + 2 * (C + 1) * (dv + 1) + (C + 1) * dv
 
 
 def featmap_bytes_per_row(w) -> int:
@@ -180,7 +194,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per head of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["all", "fwd", "featmap", "noncausal", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "fwd", "featmap", "noncausal", "backward", "decode"], default="all")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (scale for HBM byte counters)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -293,6 +307,26 @@ def main():
                                   "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                                   "traffic": read_traffic("noncausal_h16_l16k_bf16"),
                                   "algorithmic_flops_per_launch": flops}})
+    if args.only in ("all", "backward"):
+        dout = dev_bf16(ss.make_grads(w)[0])
+        dq, dk, dvv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        wsb = torch.empty(max(ops.chunked_bwd_workspace_size(fm, w.B, w.H, w.L, w.dv, w.chunk, torch.bfloat16), 16),
+                          dtype=torch.uint8, device=dev)
+
+        def bwd():
+            ops.chunked_bwd(fm, qd, kd, vd, dout, w.chunk, workspace=wsb, dq=dq, dk=dk, dv=dvv)
+
+        for _ in range(max(1, args.warmup // 5)):
+            bwd()
+        ms = event_time_ms(bwd, max(1, args.steps // 5), stream)
+        flops = bwd_flops_per_token_head(w) * w.B * w.H * w.L
+        achieved = flops / (ms * 1e-3) / 1e12
+        also.append({"name": "backward_h16_l16k_bf16", "ms_per_step": ms, "tokens_per_s": w.B * w.L / (ms * 1e-3),
+                     "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                                  "traffic": read_traffic("backward_h16_l16k_bf16"),
+                                  "algorithmic_flops_per_launch": flops}})
+        del wsb
     if args.only in ("all", "decode"):
         wd = ss.WORKLOADS[DECODE]
         nh = wd.n_heads

@@ -323,7 +323,9 @@ extern "C" {
 size_t slay_attn_chunked_bwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t L,
                                             int32_t dv, int32_t chunk, slay_dtype_t io_dtype) {
   if (check_params(params) != SLAY_OK || B < 0 || H < 0 || L < 0 || dv < 1 || chunk < 1) return 0;
-  return slay::backward_workspace_bytes(backward_args(params, io_dtype, B, H, L, dv, chunk));
+  const slay::BackwardArgs a = backward_args(params, io_dtype, B, H, L, dv, chunk);
+  return slay::backward_fused_supported(a) ? slay::backward_fused_workspace_bytes(a)
+                                           : slay::backward_workspace_bytes(a);
 }
 
 slay_status_t slay_attn_chunked_bwd(const slay_params_t* params, const void* q, const void* k, const void* v,
@@ -350,7 +352,8 @@ slay_status_t slay_attn_chunked_bwd(const slay_params_t* params, const void* q, 
       return fail(SLAY_E_INVALID, "q/k/v/dout/dq/dk/dv must be 16-byte aligned");
   }
   slay::BackwardArgs a = backward_args(params, io_dtype, B, H, L, dv, chunk);
-  if (!slay::backward_supported(a))
+  const bool fused = slay::backward_fused_supported(a);
+  if (!fused && !slay::backward_supported(a))
     return fail(SLAY_E_UNSUPPORTED, "backward shape not supported (d=%d dv=%d F=%d chunk=%d)", params->d, dv, F,
                 chunk);
   a.q = q;
@@ -369,12 +372,14 @@ slay_status_t slay_attn_chunked_bwd(const slay_params_t* params, const void* q, 
   a.dz0 = dz0;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
-  const size_t need = slay::backward_workspace_bytes(a);
+  const size_t need = fused ? slay::backward_fused_workspace_bytes(a) : slay::backward_workspace_bytes(a);
   if (workspace_bytes < need) return fail(SLAY_E_INVALID, "workspace too small: %zu < %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(SLAY_E_INVALID, "workspace is NULL");
   if (need > 0 && !aligned16(workspace)) return fail(SLAY_E_INVALID, "workspace must be 16-byte aligned");
   if (nh == 0) return ok();
-  return device_status(slay::launch_backward(a, static_cast<hipStream_t>(stream)), "slay_attn_chunked_bwd launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return device_status(fused ? slay::launch_backward_fused(a, s) : slay::launch_backward(a, s),
+                       "slay_attn_chunked_bwd launch");
 }
 
 size_t slay_attn_noncausal_fwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t Lq,

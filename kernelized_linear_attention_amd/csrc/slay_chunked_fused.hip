@@ -1532,7 +1532,77 @@ hipError_t launch_nc_t(const ChunkedArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Prefix states of every key segment, the input of the fused backward: the
+// segment-state pass over segments 0..n_seg-2 and the scan, after which item s
+// of ws (fragment order, [n_heads][n_seg][F/16][NE][64][4]) holds S0 plus the
+// states of all keys before segment s.
+template <class K>
+hipError_t segment_prefix_t(const ChunkedArgs& a, float* ws, hipStream_t s) {
+  const int n_seg = segments_of<K>(a);
+  Params p{};
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.L = a.L;
+  p.Lq = a.L;
+  p.sub = kSub;
+  p.m = a.m;
+  p.anchors = static_cast<const uint16_t*>(a.anchors);
+  p.prf = static_cast<const uint16_t*>(a.prf);
+  p.draw_set_stride = a.draw_set_stride;
+  p.n_draw_sets = a.n_draw_sets;
+  p.nc = a.nc;
+  p.ws = ws;
+  p.n_seg = n_seg;
+  p.seg_len = seg_len_for<K>(a.n_heads, a.L);
+  p.p1_segs = (n_seg - 1) * kSub;
+  p.p1_items = p.p1_segs + 1;
+  hipError_t e;
+  if (n_seg > 1) {
+    if constexpr (K::STAGERS1) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT + 256), K::kLds1, s,
+                         p);
+    } else {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K, 1>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((pass1_kernel<K, 1>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT), K::kLds1, s, p);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ScanArgs sa{};
+  sa.states = ws;
+  sa.n_heads = a.n_heads;
+  sa.n_items = p.p1_items;
+  sa.n_terms = p.p1_segs;
+  sa.F = K::F;
+  sa.dv = K::DV;
+  sa.layout = 1;
+  sa.S0 = a.S0;
+  sa.z0 = a.z0;
+  return launch_scan(sa, s);
+}
+
 }  // namespace
+
+int fused_segment_count(const ChunkedArgs& a, int64_t* seg_len) {
+  int n = 0;
+  dispatch(a, [&](auto k) {
+    using K = decltype(k);
+    n = segments_of<K>(a);
+    *seg_len = seg_len_for<K>(a.n_heads, a.L);
+  });
+  return n;
+}
+
+hipError_t launch_segment_prefix(const ChunkedArgs& a, float* ws, hipStream_t s) {
+  hipError_t e = hipErrorInvalidValue;
+  dispatch(a, [&](auto k) { e = segment_prefix_t<decltype(k)>(a, ws, s); });
+  return e;
+}
 
 bool fused_supported(const ChunkedArgs& a) {
   return dispatch(a, [](auto) {});

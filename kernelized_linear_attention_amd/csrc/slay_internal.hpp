@@ -58,6 +58,12 @@ bool fused_supported(const ChunkedArgs& a);
 size_t fused_workspace_bytes(const ChunkedArgs& a);
 hipError_t launch_fused(const ChunkedArgs& a, hipStream_t s);
 
+// Segment geometry of the fused path (0 segments if the shape has no fused
+// variant) and the prefix states of every key segment in its fragment-ordered
+// layout [n_heads][n_seg][F/16][(dv+16)/16][64][4] (the backward's input).
+int fused_segment_count(const ChunkedArgs& a, int64_t* seg_len);
+hipError_t launch_segment_prefix(const ChunkedArgs& a, float* ws, hipStream_t s);
+
 // Generic path (any supported dtype/shape; unfused, plain FMA).
 bool generic_supported(const ChunkedArgs& a);
 size_t generic_workspace_bytes(const ChunkedArgs& a);
@@ -113,6 +119,10 @@ struct BackwardArgs {
   size_t ws_bytes;
 };
 bool backward_supported(const BackwardArgs& a);
+// MFMA path of the backward (bf16, d = dv = 64, F = 256, chunk 64).
+bool backward_fused_supported(const BackwardArgs& a);
+size_t backward_fused_workspace_bytes(const BackwardArgs& a);
+hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s);
 size_t backward_workspace_bytes(const BackwardArgs& a);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t s);
 

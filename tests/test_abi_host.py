@@ -217,10 +217,15 @@ def test_backward_validation_and_workspace(lib):
         assert _bwd(lib, p, **{name: None}) == E_INV, name
         assert _bwd(lib, p, **{name: FAKE + 4}) == E_INV, name
     assert _bwd(lib, p) == E_INV and b"workspace too small" in lib.slay_last_error()
-    # phi(q), phi(k), dphi(q), dphi(k), g' per token, one state per 64-token chunk
+    # MFMA path: one fp32 state per (head, 1024-token segment), bf16 phi(q), phi(k), dphi(q), dphi(k)
+    # and an 80-column g' per token
     n = lib.slay_attn_chunked_bwd_workspace_size(ctypes.byref(p), 1, 16, 16384, 64, 64, _lib.SLAY_BF16)
     rows = 16 * 16384
-    assert n == 4 * (4 * rows * 256 + rows * 65 + 16 * 256 * 256 * 65)
+    assert n == 4 * 16 * 16 * 256 * 80 + 4 * 2 * rows * 256 + 2 * rows * 80
+    # general path (fp32): fp32 phi(q), phi(k), dphi(q), dphi(k), g' and one state per chunk
+    p32 = _params(R=2, m=16, dt=_lib.SLAY_F32)
+    n32 = lib.slay_attn_chunked_bwd_workspace_size(ctypes.byref(p32), 1, 2, 100, 64, 32, _lib.SLAY_F32)
+    assert n32 == 4 * (4 * 200 * 32 + 200 * 65 + 2 * 4 * 32 * 65)
     assert _bwd(lib, p, ws=FAKE, ws_bytes=n - 1) == E_INV
     assert _bwd(lib, p, ws=None, ws_bytes=n) == E_INV
     # nothing to do, and no tokens (only the state gradient passes through; no pointers needed)

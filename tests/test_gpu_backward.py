@@ -78,7 +78,8 @@ def _compare(got, ref, dtype, tag):
 @pytest.mark.parametrize("name,B,H,L,chunk,with_state", [
     ("tiny_f32", 1, 2, 100, 32, False),             # fp32, ragged tail
     ("tiny_f32", 1, 2, 77, 16, True),               # fp32 with initial state and final-state gradient
-    ("h16_l16k_bf16", 1, 2, 300, 64, True),         # bf16, F = 256
+    ("h16_l16k_bf16", 1, 2, 300, 64, True),         # MFMA path: F = 256, three segments, ragged tail
+    ("h16_l16k_bf16", 1, 1, 4000, 64, True),        # MFMA path: 32 segments walked in 32-token steps
     ("b4h8_l2k_bf16", 2, 1, 257, 64, False),        # bf16, F = 96, ragged tail of one token
     ("h8_l128k_d128_bf16", 1, 1, 200, 128, True),   # bf16, d = dv = 128, F = 512, chunk 128
 ])
@@ -114,7 +115,7 @@ def test_backward_chunk_invariance(lib):
 def test_backward_per_head_draws(lib, orc):
     import torch
 
-    w = ss.WORKLOADS["h16_l16k_bf16"].with_(H=2, L=130)
+    w = ss.WORKLOADS["h16_l16k_bf16"].with_(H=2, L=256)  # whole 128-row tiles per head: the MFMA path
     q, k, v = ss.make_qkv(w)
     A0, G0 = ss.make_draws(w)
     A1, G1 = ss.make_draws(w, seed=[3, 99])
