@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 WORKLOAD = "h16_l16k_bf16"
 DECODE = "decode_256x16_f32"
 KERNEL_SOURCES = ("slay_chunked_fused.hip", "slay_chunked_generic.hip", "slay_featmap.hip", "slay_decode.hip",
-                  "slay_backward.hip", "slay_device.hpp")
+                  "slay_backward.hip", "slay_backward_fused.hip", "slay_device.hpp")
 
 
 def fwd_flops_per_token_head(w) -> int:

@@ -98,6 +98,7 @@ struct BwdK {
   static constexpr int kLds = oN + C * LN * 4;
   static_assert(kLds <= 160 * 1024, "LDS budget");
   static_assert(NF % 2 == 0, "two feature blocks per wave");
+  static_assert(NT == 512 && F == 256 && C == 32, "the staging maps 512 threads onto 32 x 256 tiles");
 };
 
 struct BwdParams {
@@ -164,43 +165,128 @@ __device__ void zero_constant_regions(const Lds& s, int tid) {
   }
 }
 
-// Stage one chunk (rows row0 .. row0+n-1; rows beyond n are zero).
-template <class K, bool TK, bool TV, bool LOADG>
-__device__ void stage_chunk(const BwdParams& p, const Lds& s, int64_t row0, int n, int tid) {
-  constexpr int P8 = K::F / 8;
-  for (int idx = tid; idx < K::C * P8; idx += K::NT) {
-    const int r = idx / P8, c8 = (idx - r * P8) * 8;
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (r < n) {
-      a = *reinterpret_cast<const uint4*>(p.phiq + (row0 + r) * K::F + c8);
-      b = *reinterpret_cast<const uint4*>(p.phik + (row0 + r) * K::F + c8);
-    }
-    *reinterpret_cast<uint4*>(s.Q + r * K::LQ + c8) = a;
-    *reinterpret_cast<uint4*>(s.K + r * K::LQ + c8) = b;
-    scatter8(s.QT + c8 * K::LT + r, K::LT, a);
-    if (TK) scatter8(s.KT + c8 * K::LT + r, K::LT, b);
+// Chunk staging, software-pipelined: the global loads of chunk c+1 are issued
+// into registers right after chunk c is written to LDS, so they are in flight
+// while chunk c is computed.  A thread moves one 4-row x 8-column block of a
+// feature tile: four 16-byte row pieces, written as rows and, transposed in
+// registers (v_perm), as eight 8-byte column pieces of the transposed tile.
+__device__ __forceinline__ void transpose4x8(const uint4 (&in)[4], uint2 (&out)[8]) {
+  const uint32_t w[4][4] = {{in[0].x, in[0].y, in[0].z, in[0].w},
+                            {in[1].x, in[1].y, in[1].z, in[1].w},
+                            {in[2].x, in[2].y, in[2].z, in[2].w},
+                            {in[3].x, in[3].y, in[3].z, in[3].w}};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    out[2 * u] = make_uint2(lo16_pair(w[0][u], w[1][u]), lo16_pair(w[2][u], w[3][u]));
+    out[2 * u + 1] = make_uint2(hi16_pair(w[0][u], w[1][u]), hi16_pair(w[2][u], w[3][u]));
   }
-  for (int idx = tid; idx < K::C * 8; idx += K::NT) {
-    const int r = idx >> 3, c8 = (idx & 7) * 8;
-    uint4 a = make_uint4(0, 0, 0, 0);
-    if (r < n) a = *reinterpret_cast<const uint4*>(p.v + (row0 + r) * K::DV + c8);
-    *reinterpret_cast<uint4*>(s.V + r * K::LV + c8) = a;
-    if (TV) scatter8(s.VT + c8 * K::LT + r, K::LT, a);
-  }
-  for (int r = tid; r < K::C; r += K::NT) {  // the ones column counts valid rows only
+}
+
+__device__ __forceinline__ uint4 ld_row(const uint16_t* p, bool ok) {
+  return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+}
+
+// block u of a [C][width] tile: rows 4(u % 8) .. +3, columns 8(u / 8) .. +7
+template <class K>
+__device__ __forceinline__ void load_block(const uint16_t* src, int width, int64_t row0, int n, int u,
+                                           uint4 (&blk)[4]) {
+  const int r = 4 * (u & 7), c = 8 * (u >> 3);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) blk[t] = ld_row(src + (row0 + r + t) * width + c, r + t < n);
+}
+
+template <class K>
+__device__ __forceinline__ void store_block(uint16_t* rows, int ld_rows, uint16_t* cols, int u, const uint4 (&blk)[4]) {
+  const int r = 4 * (u & 7), c = 8 * (u >> 3);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) *reinterpret_cast<uint4*>(rows + (r + t) * ld_rows + c) = blk[t];
+  uint2 tr[8];
+  transpose4x8(blk, tr);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) *reinterpret_cast<uint2*>(cols + (c + t) * K::LT + r) = tr[t];
+}
+
+// the ones column of V' (and V'^T) counts the chunk's valid rows only
+template <class K, bool TV>
+__device__ __forceinline__ void store_ones(const Lds& s, int n, int tid) {
+  for (int r = tid; r < K::C; r += K::NT) {
     const uint16_t one = r < n ? kOneBf16 : (uint16_t)0;
     s.V[r * K::LV + K::DV] = one;
     if (TV) s.VT[K::DV * K::LT + r] = one;
   }
-  if (LOADG) {  // g' rows (80 columns) and their transpose
-    for (int idx = tid; idx < K::C * (K::E / 8); idx += K::NT) {
-      const int r = idx / (K::E / 8), c8 = (idx - r * (K::E / 8)) * 8;
-      uint4 a = make_uint4(0, 0, 0, 0);
-      if (r < n) a = *reinterpret_cast<const uint4*>(p.g + (row0 + r) * K::E + c8);
-      *reinterpret_cast<uint4*>(s.G + r * K::LV + c8) = a;
-      scatter8(s.GT + c8 * K::LT + r, K::LT, a);
+}
+
+// bwd_q: threads < 256 move a phi(Q) block, the others a phi(K) block; threads
+// < 256 also one 16-byte piece of v (row t/8, columns 8(t%8)..) and of dout.
+struct PrefQ {
+  uint4 blk[4];
+  uint4 v, dout;
+};
+
+template <class K>
+__device__ __forceinline__ void load_q(const BwdParams& p, int64_t row0, int n, int tid, PrefQ& pf) {
+  load_block<K>(tid < 256 ? p.phiq : p.phik, K::F, row0, n, tid & 255, pf.blk);
+  const int r = (tid & 255) >> 3, c = 8 * (tid & 7);
+  pf.v = ld_row(p.v + (row0 + r) * K::DV + c, tid < 256 && r < n);
+  pf.dout = ld_row(p.dout + (row0 + r) * K::DV + c, tid < 256 && r < n);
+}
+
+template <class K>
+__device__ __forceinline__ void store_q(const Lds& s, const PrefQ& pf, int n, int tid) {
+  store_block<K>(tid < 256 ? s.Q : s.K, K::LQ, tid < 256 ? s.QT : s.KT, tid & 255, pf.blk);
+  if (tid < 256) {
+    const int r = tid >> 3, c = 8 * (tid & 7);
+    *reinterpret_cast<uint4*>(s.V + r * K::LV + c) = pf.v;
+    scatter8(s.VT + c * K::LT + r, K::LT, pf.v);
+  }
+  store_ones<K, true>(s, n, tid);
+}
+
+// bwd_kv: threads < 256 move a phi(Q) block (rows and transposed) and one
+// piece of v; the others four row pieces of phi(K) and, for the first 80, a
+// block of g' (rows and transposed).
+struct PrefKV {
+  uint4 blk[4];
+  uint4 gb[4];
+  uint4 v;
+};
+
+template <class K>
+__device__ __forceinline__ void load_kv(const BwdParams& p, int64_t row0, int n, int tid, PrefKV& pf) {
+  const int u = tid & 255;
+  const bool lo = tid < 256;
+  if (lo) {
+    load_block<K>(p.phiq, K::F, row0, n, u, pf.blk);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int idx = u + 256 * t, r = idx >> 5, c = 8 * (idx & 31);
+      pf.blk[t] = ld_row(p.phik + (row0 + r) * K::F + c, r < n);
     }
   }
+  const int r = u >> 3, c = 8 * (u & 7);
+  pf.v = ld_row(p.v + (row0 + r) * K::DV + c, lo && r < n);
+  // g' blocks on threads 256 .. 335 (80 blocks of 4 rows x 8 columns); the rest load nothing
+  const bool gok = !lo && u < 8 * (K::E / 8);
+  load_block<K>(p.g, K::E, row0, gok ? n : 0, gok ? u : 0, pf.gb);
+}
+
+template <class K>
+__device__ __forceinline__ void store_kv(const Lds& s, const PrefKV& pf, int n, int tid) {
+  if (tid < 256) {
+    store_block<K>(s.Q, K::LQ, s.QT, tid, pf.blk);
+    const int r = tid >> 3, c = 8 * (tid & 7);
+    *reinterpret_cast<uint4*>(s.V + r * K::LV + c) = pf.v;
+  } else {
+    const int u = tid - 256;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int idx = u + 256 * t, r = idx >> 5, c = 8 * (idx & 31);
+      *reinterpret_cast<uint4*>(s.K + r * K::LQ + c) = pf.blk[t];
+    }
+    if (u < 8 * (K::E / 8)) store_block<K>(s.G, K::LV, s.GT, u, pf.gb);
+  }
+  store_ones<K, false>(s, n, tid);
 }
 
 // Fragment-ordered state item: element (f, e) of tile (f/16, e/16) sits at
@@ -255,11 +341,15 @@ __global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
     }
   write_state_copy<K>(s, ST, wave, g, c16);
 
+  PrefQ pf;
+  load_q<K>(p, h * p.L + t_begin, (int)min<int64_t>(K::C, t_end - t_begin), tid, pf);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += K::C) {
     const int n = (int)min<int64_t>(K::C, t_end - t0);
     const int64_t row0 = h * p.L + t0;
     __syncthreads();
-    stage_chunk<K, true, true, false>(p, s, row0, n, tid);
+    store_q<K>(s, pf, n, tid);
+    const uint4 dcur = pf.dout;
+    if (t0 + K::C < t_end) load_q<K>(p, row0 + K::C, (int)min<int64_t>(K::C, t_end - t0 - K::C), tid, pf);
     __syncthreads();
     // [1] A^T blocks (masked, to s.A as A[i][j]) and phi(Q) S' (to s.N as num'[i][e])
     for (int it = wave; it < K::NA + K::NI * K::NE; it += K::NW) {
@@ -294,10 +384,11 @@ __global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
     }
     __syncthreads();
     // [3] g' = [dout / den | -(dout . num) / den^2 | 0]: eight threads per token
-    for (int idx = tid; idx < K::C * 8; idx += K::NT) {
+    static_assert(K::NT >= K::C * 8, "one pass: thread t holds the dout piece of token t/8");
+    if (tid < K::C * 8) {
+      const int idx = tid;
       const int r = idx >> 3, e0 = (idx & 7) * 8;
-      uint4 dr = make_uint4(0, 0, 0, 0);
-      if (r < n) dr = *reinterpret_cast<const uint4*>(p.dout + (row0 + r) * K::DV + e0);
+      const uint4 dr = dcur;  // this thread's piece of dout, staged with the chunk
       const uint32_t dw[4] = {dr.x, dr.y, dr.z, dr.w};
       float dn[8];
 #pragma unroll
@@ -419,12 +510,16 @@ __global__ __launch_bounds__(K::NT) void bwd_kv_kernel(BwdParams p) {
   write_state_copy<K>(s, UT, wave, g, c16);
 
   const int n_steps = (int)((t_end - t_begin + K::C - 1) / K::C);
+  auto rows_of = [&](int cs) { return (int)min<int64_t>(K::C, t_end - (t_begin + (int64_t)cs * K::C)); };
+  PrefKV pf;
+  load_kv<K>(p, h * p.L + t_begin + (int64_t)(n_steps - 1) * K::C, rows_of(n_steps - 1), tid, pf);
   for (int cs = n_steps - 1; cs >= 0; --cs) {
     const int64_t t0 = t_begin + (int64_t)cs * K::C;
-    const int n = (int)min<int64_t>(K::C, t_end - t0);
+    const int n = rows_of(cs);
     const int64_t row0 = h * p.L + t0;
     __syncthreads();
-    stage_chunk<K, false, false, true>(p, s, row0, n, tid);
+    store_kv<K>(s, pf, n, tid);
+    if (cs > 0) load_kv<K>(p, row0 - K::C, K::C, tid, pf);
     __syncthreads();
     // [1] A^T and D^T (masked, as [j][i]); dV^T = U^T phi(K)^T (to s.N as [j][e])
     for (int it = wave; it < 2 * K::NA + (K::DV / 16) * K::NI; it += K::NW) {
@@ -533,6 +628,36 @@ struct VjpParams {
   NodeConsts nc;
 };
 
+// One tile's global inputs for one lane, loaded a tile ahead: x as the MFMA
+// B-operand (row l%16 of each 16-row block, columns 8(l/16).. and 32+8(l/16)..),
+// x again as the four column pieces the final projection needs, and dphi of
+// every feature block (columns 16 fb + 4(l/16) ..).
+template <class K>
+struct VjpPref {
+  uint4 xb[K::RB][2];
+  uint2 xo[K::RB][K::D / 16];
+  uint2 dp[K::NF][K::RB];
+};
+
+template <class K>
+__device__ __forceinline__ void vjp_load(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dphi,
+                                         int64_t n_rows, int64_t r0, int wave, int g, int c16, VjpPref<K>& pf) {
+#pragma unroll
+  for (int rb = 0; rb < K::RB; ++rb) {
+    const int64_t row = r0 + (wave * K::RB + rb) * 16 + c16;
+    const bool ok = row < n_rows;
+    const uint16_t* xr = x + row * K::D;
+    pf.xb[rb][0] = ok ? *reinterpret_cast<const uint4*>(xr + 8 * g) : make_uint4(0, 0, 0, 0);
+    pf.xb[rb][1] = ok ? *reinterpret_cast<const uint4*>(xr + 32 + 8 * g) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < K::D / 16; ++cb)
+      pf.xo[rb][cb] = ok ? *reinterpret_cast<const uint2*>(xr + cb * 16 + 4 * g) : make_uint2(0, 0);
+#pragma unroll
+    for (int fb = 0; fb < K::NF; ++fb)
+      pf.dp[fb][rb] = ok ? *reinterpret_cast<const uint2*>(dphi + row * K::F + fb * 16 + 4 * g) : make_uint2(0, 0);
+  }
+}
+
 template <class K>
 __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   extern __shared__ __align__(16) char lds_raw[];
@@ -546,6 +671,8 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   uint16_t* __restrict__ dx = p.dx[side];
   const int64_t n_tiles = (p.n_rows + K::ROWS - 1) / K::ROWS;
   int set = -1;
+  VjpPref<K> pf;
+  if ((int64_t)blockIdx.x < n_tiles) vjp_load<K>(x, dphi, p.n_rows, blockIdx.x * (int64_t)K::ROWS, wave, g, c16, pf);
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     const int64_t r0 = tile * K::ROWS;
     const int tset = (int)((r0 / p.rows_per_head) % p.n_draw_sets);  // a tile never spans two draw sets
@@ -562,6 +689,8 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       }
       __syncthreads();
     }
+    const VjpPref<K> cur = pf;
+    if (tile + gridDim.x < n_tiles) vjp_load<K>(x, dphi, p.n_rows, (tile + gridDim.x) * K::ROWS, wave, g, c16, pf);
     bf16x8 xb[K::RB][2];
     float inv[K::RB];
     bool clamp[K::RB];
@@ -569,13 +698,8 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
 #pragma unroll
     for (int rb = 0; rb < K::RB; ++rb) {
       row[rb] = r0 + (wave * K::RB + rb) * 16 + c16;
-      uint4 a = make_uint4(0, 0, 0, 0), b = a;
-      if (row[rb] < p.n_rows) {
-        a = *reinterpret_cast<const uint4*>(x + row[rb] * K::D + 8 * g);
-        b = *reinterpret_cast<const uint4*>(x + row[rb] * K::D + 32 + 8 * g);
-      }
-      xb[rb][0] = __builtin_bit_cast(bf16x8, a);
-      xb[rb][1] = __builtin_bit_cast(bf16x8, b);
+      xb[rb][0] = __builtin_bit_cast(bf16x8, cur.xb[rb][0]);
+      xb[rb][1] = __builtin_bit_cast(bf16x8, cur.xb[rb][1]);
       float ss = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -592,6 +716,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
     for (int rb = 0; rb < K::RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < K::D / 16; ++cb) dX[rb][cb] = kZero4;
+#pragma unroll
     for (int fb = 0; fb < K::NF; ++fb) {
       const int node = (fb * 16) / p.m;
       const float c1 = p.nc.c1[node], c0 = p.nc.c0[node];
@@ -606,8 +731,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
         ya = mfma_bf16(pa1, xb[rb][1], ya);
         f32x4 yg = mfma_bf16(pg0, xb[rb][0], kZero4);
         yg = mfma_bf16(pg1, xb[rb][1], yg);
-        uint2 dr = make_uint2(0, 0);
-        if (row[rb] < p.n_rows) dr = *reinterpret_cast<const uint2*>(dphi + row[rb] * K::F + fb * 16 + 4 * g);
+        const uint2 dr = cur.dp[fb][rb];
         const float dp[4] = {__uint_as_float(dr.x << 16), __uint_as_float(dr.x & 0xFFFF0000u),
                              __uint_as_float(dr.y << 16), __uint_as_float(dr.y & 0xFFFF0000u)};
         f32x4 wa, wg;
@@ -634,8 +758,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       float proj = 0.f;
 #pragma unroll
       for (int cb = 0; cb < K::D / 16; ++cb) {
-        uint2 xr = make_uint2(0, 0);
-        if (row[rb] < p.n_rows) xr = *reinterpret_cast<const uint2*>(x + row[rb] * K::D + cb * 16 + 4 * g);
+        const uint2 xr = cur.xo[rb][cb];
         xh[cb][0] = __uint_as_float(xr.x << 16) * inv[rb];
         xh[cb][1] = __uint_as_float(xr.x & 0xFFFF0000u) * inv[rb];
         xh[cb][2] = __uint_as_float(xr.y << 16) * inv[rb];
