@@ -114,6 +114,36 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
                                     int32_t chunk, const float* S0, const float* z0, void* o, float* S_out,
                                     float* z_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes slay_attn_varlen_fwd needs (0 for unsupported shapes). */
+size_t slay_attn_varlen_fwd_workspace_size(const slay_params_t* params, int32_t n_seqs, int32_t H,
+                                           int64_t total_tokens, int32_t dv, slay_dtype_t io_dtype);
+
+/* Causal SLAY forward over a batch of sequences of different lengths (the
+ * same contraction as slay_attn_chunked_fwd, review "Proposed method" bullet
+ * 6, applied to each sequence on its own; bounded-state streaming of mixed
+ * lengths, review "Motivation and goals").  The sequences are packed along one
+ * token axis per head: sequence s holds tokens cu_seqlens[s] ..
+ * cu_seqlens[s+1] - 1 of every head.
+ *   q, k : device [H][total_tokens][d];  v, o : device [H][total_tokens][dv];
+ *          bf16 (must equal the draw dtype); fp32 accumulation.
+ *   cu_seqlens : device int64 [n_seqs + 1], non-decreasing from 0 to
+ *          total_tokens (read on the device; offsets that break this rule
+ *          make the call compute nothing: o is left as it was and the final
+ *          states equal the initial ones).
+ *   S0, z0     : nullable device fp32 initial states [n_seqs][H][R*m][dv],
+ *                [n_seqs][H][R*m] (NULL = zero);
+ *   S_out, z_out: nullable device fp32 final states, same shapes (may alias
+ *                S0, z0): a prefill's hand-off to slay_attn_recurrent_step.
+ *   workspace  : device scratch of slay_attn_varlen_fwd_workspace_size() bytes.
+ * Supported: d = dv = 64, R*m = 256 with m a multiple of 32 (the fused MFMA
+ * kernels; other shapes return SLAY_E_UNSUPPORTED).  One launch each of a
+ * work-list kernel, the segment-state pass, the per-sequence scan and the
+ * main pass, whatever the number of sequences. */
+slay_status_t slay_attn_varlen_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                   slay_dtype_t io_dtype, int32_t n_seqs, int32_t H, const int64_t* cu_seqlens,
+                                   int64_t total_tokens, int32_t dv, const float* S0, const float* z0, void* o,
+                                   float* S_out, float* z_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes slay_attn_chunked_bwd needs for this shape (0 is possible). */
 size_t slay_attn_chunked_bwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t L,
                                             int32_t dv, int32_t chunk, slay_dtype_t io_dtype);

@@ -13,6 +13,7 @@ SLAY_F32, SLAY_BF16 = 0, 1
 
 # every function include/slay.h declares
 EXPORTS = ("slay_featmap", "slay_attn_chunked_fwd_workspace_size", "slay_attn_chunked_fwd",
+           "slay_attn_varlen_fwd_workspace_size", "slay_attn_varlen_fwd",
            "slay_attn_chunked_bwd_workspace_size", "slay_attn_chunked_bwd",
            "slay_attn_noncausal_fwd_workspace_size", "slay_attn_noncausal_fwd",
            "slay_attn_recurrent_step_workspace_size", "slay_attn_recurrent_step", "slay_gl_table",
@@ -63,6 +64,11 @@ def load() -> ctypes.CDLL:
         lib.slay_attn_chunked_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int, i32, i32, i64, i32, i32, fp, fp, vp, fp,
                                               fp, vp, sz, vp]
         lib.slay_attn_chunked_fwd.restype = ctypes.c_int
+        lib.slay_attn_varlen_fwd_workspace_size.argtypes = [P, i32, i32, i64, i32, ctypes.c_int]
+        lib.slay_attn_varlen_fwd_workspace_size.restype = sz
+        lib.slay_attn_varlen_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int, i32, i32, vp, i64, i32, fp, fp, vp, fp, fp,
+                                             vp, sz, vp]
+        lib.slay_attn_varlen_fwd.restype = ctypes.c_int
         lib.slay_attn_chunked_bwd_workspace_size.argtypes = [P, i32, i32, i64, i32, i32, ctypes.c_int]
         lib.slay_attn_chunked_bwd_workspace_size.restype = sz
         lib.slay_attn_chunked_bwd.argtypes = [P, vp, vp, vp, vp, ctypes.c_int, i32, i32, i64, i32, i32, fp, fp, fp,

@@ -382,6 +382,57 @@ slay_status_t slay_attn_chunked_bwd(const slay_params_t* params, const void* q, 
                        "slay_attn_chunked_bwd launch");
 }
 
+size_t slay_attn_varlen_fwd_workspace_size(const slay_params_t* params, int32_t n_seqs, int32_t H,
+                                           int64_t total_tokens, int32_t dv, slay_dtype_t io_dtype) {
+  if (check_params(params) != SLAY_OK || n_seqs < 0 || H < 0 || total_tokens < 0 || dv < 1) return 0;
+  slay::VarlenArgs a{};
+  a.c = chunked_args(params, nullptr, nullptr, nullptr, io_dtype, 1, H, total_tokens, dv, 64);
+  a.n_seqs = n_seqs;
+  return slay::varlen_supported(a) ? slay::varlen_workspace_bytes(a) : 0;
+}
+
+slay_status_t slay_attn_varlen_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                   slay_dtype_t io_dtype, int32_t n_seqs, int32_t H, const int64_t* cu_seqlens,
+                                   int64_t total_tokens, int32_t dv, const float* S0, const float* z0, void* o,
+                                   float* S_out, float* z_out, void* workspace, size_t workspace_bytes, void* stream) {
+  slay_status_t st = check_params(params);
+  if (st != SLAY_OK) return st;
+  if (n_seqs < 0 || H < 0 || total_tokens < 0) return fail(SLAY_E_INVALID, "n_seqs, H, total_tokens must be >= 0");
+  if (dv < 1) return fail(SLAY_E_INVALID, "dv must be >= 1");
+  if (io_dtype != SLAY_F32 && io_dtype != SLAY_BF16) return fail(SLAY_E_INVALID, "bad io dtype");
+  if (io_dtype != params->draw_dtype) return fail(SLAY_E_UNSUPPORTED, "io dtype must equal the draw dtype");
+  const int F = params->R * params->m;
+  if (!mul_ok(H, total_tokens) || !mul_ok((int64_t)H * total_tokens, std::max<int64_t>(params->d, dv)) ||
+      total_tokens > (int64_t)INT32_MAX * 64)
+    return fail(SLAY_E_INVALID, "problem size overflows");
+  slay::VarlenArgs a{};
+  a.c = chunked_args(params, q, k, v, io_dtype, 1, H, total_tokens, dv, 64);
+  a.n_seqs = n_seqs;
+  a.cu = cu_seqlens;
+  if (!slay::varlen_supported(a))
+    return fail(SLAY_E_UNSUPPORTED, "variable-length batches need bf16, d = dv = 64 and R*m = 256 (m a multiple of 32); "
+                "got d=%d dv=%d F=%d", params->d, dv, F);
+  if (H == 0 || n_seqs == 0) return ok();
+  if (!cu_seqlens) return fail(SLAY_E_INVALID, "cu_seqlens is NULL");
+  if (total_tokens > 0) {
+    if (!q || !k || !v || !o) return fail(SLAY_E_INVALID, "q/k/v/o pointer is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+      return fail(SLAY_E_INVALID, "q/k/v/o must be 16-byte aligned");
+  }
+  a.c.nc = node_consts(params->R, params->m, params->eps);
+  a.c.S0 = S0;
+  a.c.z0 = z0;
+  a.c.o = o;
+  a.c.S_out = S_out;
+  a.c.z_out = z_out;
+  a.c.ws = workspace;
+  a.c.ws_bytes = workspace_bytes;
+  const size_t need = slay::varlen_workspace_bytes(a);
+  if (workspace_bytes < need) return fail(SLAY_E_INVALID, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (!workspace || !aligned16(workspace)) return fail(SLAY_E_INVALID, "workspace must be non-NULL and 16-byte aligned");
+  return device_status(slay::launch_varlen(a, static_cast<hipStream_t>(stream)), "slay_attn_varlen_fwd launch");
+}
+
 size_t slay_attn_noncausal_fwd_workspace_size(const slay_params_t* params, int32_t B, int32_t H, int64_t Lq,
                                                int64_t Lk, int32_t dv, slay_dtype_t io_dtype) {
   if (check_params(params) != SLAY_OK || B < 0 || H < 0 || Lq < 0 || Lk < 0 || dv < 1) return 0;

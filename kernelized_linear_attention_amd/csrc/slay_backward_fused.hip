@@ -605,15 +605,23 @@ __global__ __launch_bounds__(K::NT) void bwd_kv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Feature-map VJP on MFMA: 4 waves, each 32 rows (two 16-row blocks) of a
-// 128-row tile; P = [anchors; prf] ([2F][d]) and its transpose in LDS.
+// Feature-map VJP on MFMA.  Each wave owns two 16-feature blocks and keeps
+// their rows of P = [anchors; prf] in registers, both as the A-operand of
+// y^T = P x^T (rows f, 8 consecutive d per lane) and, transposed, as the
+// A-operand of dxh^T = P^T w (rows d, the k order of the two accumulator tiles
+// that hold w).  Per 32-row tile: x staged in LDS; every wave forms its
+// features' y, the weights w and its partial dxh over those features into its
+// own fp32 LDS tile; then, summing the waves' partials, the projection
+// dx = (dxh - xh (xh . dxh)) / |x|, 16 lanes per row.  x and dphi of the
+// next three tiles are in flight while the current one is computed.
 template <int NF_>
 struct VjpK {
   static constexpr int NF = NF_, F = NF * 16, D = 64;
-  static constexpr int NW = 4, NT = 256, RB = 2, ROWS = NW * RB * 16;
-  static constexpr int LP = D + 8, LPT = 2 * F + 8;
-  static constexpr int oP = 0, oPT = 2 * F * LP * 2, kLds = oPT + D * LPT * 2;
-  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static constexpr int NW = NF / 2, NT = NW * 64;
+  static constexpr int RT = 32, NRB = RT / 16;  // rows per tile
+  static constexpr int LX = D + 8, LR = D + 4;
+  static constexpr int oX = 0, oR = RT * LX * 2, kLds = oR + NW * RT * LR * 4;  // x tile, per-wave partials
+  static_assert(NT >= RT * 8 && NT >= RT * 16, "one x piece and one output piece per thread");
 };
 
 struct VjpParams {
@@ -628,156 +636,166 @@ struct VjpParams {
   NodeConsts nc;
 };
 
-// One tile's global inputs for one lane, loaded a tile ahead: x as the MFMA
-// B-operand (row l%16 of each 16-row block, columns 8(l/16).. and 32+8(l/16)..),
-// x again as the four column pieces the final projection needs, and dphi of
-// every feature block (columns 16 fb + 4(l/16) ..).
 template <class K>
 struct VjpPref {
-  uint4 xb[K::RB][2];
-  uint2 xo[K::RB][K::D / 16];
-  uint2 dp[K::NF][K::RB];
+  uint4 x;                  // threads < 8 RT: row t/8, columns 8(t%8) ..
+  uint2 dp[K::NRB][2];      // dphi of row 16 rb + l%16, features 16 fb_j + 4(l/16) ..
 };
 
 template <class K>
 __device__ __forceinline__ void vjp_load(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dphi,
-                                         int64_t n_rows, int64_t r0, int wave, int g, int c16, VjpPref<K>& pf) {
+                                         int64_t n_rows, int64_t r0, int tid, int wave, int g, int c16,
+                                         VjpPref<K>& pf) {
+  const int64_t xr = r0 + (tid >> 3);
+  pf.x = (tid < K::RT * 8 && xr < n_rows) ? *reinterpret_cast<const uint4*>(x + xr * K::D + 8 * (tid & 7))
+                                          : make_uint4(0, 0, 0, 0);
 #pragma unroll
-  for (int rb = 0; rb < K::RB; ++rb) {
-    const int64_t row = r0 + (wave * K::RB + rb) * 16 + c16;
-    const bool ok = row < n_rows;
-    const uint16_t* xr = x + row * K::D;
-    pf.xb[rb][0] = ok ? *reinterpret_cast<const uint4*>(xr + 8 * g) : make_uint4(0, 0, 0, 0);
-    pf.xb[rb][1] = ok ? *reinterpret_cast<const uint4*>(xr + 32 + 8 * g) : make_uint4(0, 0, 0, 0);
+  for (int rb = 0; rb < K::NRB; ++rb) {
+    const int64_t row = r0 + rb * 16 + c16;
 #pragma unroll
-    for (int cb = 0; cb < K::D / 16; ++cb)
-      pf.xo[rb][cb] = ok ? *reinterpret_cast<const uint2*>(xr + cb * 16 + 4 * g) : make_uint2(0, 0);
-#pragma unroll
-    for (int fb = 0; fb < K::NF; ++fb)
-      pf.dp[fb][rb] = ok ? *reinterpret_cast<const uint2*>(dphi + row * K::F + fb * 16 + 4 * g) : make_uint2(0, 0);
+    for (int j = 0; j < 2; ++j)
+      pf.dp[rb][j] = row < n_rows
+                         ? *reinterpret_cast<const uint2*>(dphi + row * K::F + (2 * wave + j) * 16 + 4 * g)
+                         : make_uint2(0, 0);
   }
 }
 
 template <class K>
 __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   extern __shared__ __align__(16) char lds_raw[];
-  uint16_t* sP = reinterpret_cast<uint16_t*>(lds_raw + K::oP);
-  uint16_t* sPT = reinterpret_cast<uint16_t*>(lds_raw + K::oPT);
+  uint16_t* sX = reinterpret_cast<uint16_t*>(lds_raw + K::oX);
+  float* sR = reinterpret_cast<float*>(lds_raw + K::oR);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int side = blockIdx.y;
   const uint16_t* __restrict__ x = p.x[side];
   const uint16_t* __restrict__ dphi = p.dphi[side];
   uint16_t* __restrict__ dx = p.dx[side];
-  const int64_t n_tiles = (p.n_rows + K::ROWS - 1) / K::ROWS;
+  const int64_t n_tiles = (p.n_rows + K::RT - 1) / K::RT;
+
+  bf16x8 pa[2][2], pg[2][2], pt[2][K::D / 16];
+  float c1[2], c0[2], sb[2];
   int set = -1;
-  VjpPref<K> pf;
-  if ((int64_t)blockIdx.x < n_tiles) vjp_load<K>(x, dphi, p.n_rows, blockIdx.x * (int64_t)K::ROWS, wave, g, c16, pf);
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int64_t r0 = tile * K::ROWS;
+  // three tiles in flight: pf0 is the next tile to compute, pf1 and pf2 the two after it
+  VjpPref<K> pf0, pf1, pf2;
+  const int64_t gs = gridDim.x;
+  auto load_tile = [&](int64_t t, VjpPref<K>& dst) {
+    if (t < n_tiles) vjp_load<K>(x, dphi, p.n_rows, t * K::RT, tid, wave, g, c16, dst);
+  };
+  load_tile(blockIdx.x, pf0);
+  load_tile(blockIdx.x + gs, pf1);
+  load_tile(blockIdx.x + 2 * gs, pf2);
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gs) {
+    const int64_t r0 = tile * K::RT;
     const int tset = (int)((r0 / p.rows_per_head) % p.n_draw_sets);  // a tile never spans two draw sets
-    if (tset != set) {
-      __syncthreads();
+    if (tset != set) {  // this wave's rows of P, as both operands
       set = tset;
       const uint16_t* A = p.anchors + set * p.draw_set_stride;
       const uint16_t* G = p.prf + set * p.draw_set_stride;
-      for (int idx = tid; idx < 2 * K::F * (K::D / 8); idx += K::NT) {
-        const int f = idx / (K::D / 8), c8 = (idx - f * (K::D / 8)) * 8;
-        const uint4 a = *reinterpret_cast<const uint4*>((f < K::F ? A + f * K::D : G + (f - K::F) * K::D) + c8);
-        *reinterpret_cast<uint4*>(sP + f * K::LP + c8) = a;
-        scatter8(sPT + c8 * K::LPT + f, K::LPT, a);
-      }
-      __syncthreads();
-    }
-    const VjpPref<K> cur = pf;
-    if (tile + gridDim.x < n_tiles) vjp_load<K>(x, dphi, p.n_rows, (tile + gridDim.x) * K::ROWS, wave, g, c16, pf);
-    bf16x8 xb[K::RB][2];
-    float inv[K::RB];
-    bool clamp[K::RB];
-    int64_t row[K::RB];
 #pragma unroll
-    for (int rb = 0; rb < K::RB; ++rb) {
-      row[rb] = r0 + (wave * K::RB + rb) * 16 + c16;
-      xb[rb][0] = __builtin_bit_cast(bf16x8, cur.xb[rb][0]);
-      xb[rb][1] = __builtin_bit_cast(bf16x8, cur.xb[rb][1]);
+      for (int j = 0; j < 2; ++j) {
+        const int fb = 2 * wave + j;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          pa[j][kk] = ld8(A + (fb * 16 + c16) * K::D + kk * 32 + 8 * g);
+          pg[j][kk] = ld8(G + (fb * 16 + c16) * K::D + kk * 32 + 8 * g);
+        }
+#pragma unroll
+        for (int cb = 0; cb < K::D / 16; ++cb) {
+          uint16_t e[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            e[i] = A[(fb * 16 + 4 * g + i) * K::D + cb * 16 + c16];
+            e[4 + i] = G[(fb * 16 + 4 * g + i) * K::D + cb * 16 + c16];
+          }
+          pt[j][cb] = __builtin_bit_cast(bf16x8, make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
+                                                            e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)));
+        }
+        const int node = (fb * 16) / p.m;
+        c1[j] = p.nc.c1[node];
+        c0[j] = p.nc.c0[node];
+        sb[j] = c1[j] * 0.6931471805599453f;  // sqrt(beta_r)
+      }
+    }
+    __syncthreads();  // the previous tile's readers of sX and sR are done
+    const VjpPref<K> cur = pf0;
+    pf0 = pf1;
+    pf1 = pf2;
+    load_tile(tile + 3 * gs, pf2);
+    if (tid < K::RT * 8) *reinterpret_cast<uint4*>(sX + (tid >> 3) * K::LX + 8 * (tid & 7)) = cur.x;
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < K::NRB; ++rb) {
+      const bf16x8 xb0 = ld8(sX + (rb * 16 + c16) * K::LX + 8 * g);
+      const bf16x8 xb1 = ld8(sX + (rb * 16 + c16) * K::LX + 32 + 8 * g);
       float ss = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float u = (float)xb[rb][0][t], w = (float)xb[rb][1][t];
+        const float u = (float)xb0[t], w = (float)xb1[t];
         ss = fmaf(u, u, fmaf(w, w, ss));
       }
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
-      clamp[rb] = ss < 1e-24f;
-      inv[rb] = clamp[rb] ? 1e12f : __builtin_amdgcn_rsqf(ss);
-    }
-    f32x4 dX[K::RB][K::D / 16];
+      const float inv = ss < 1e-24f ? 1e12f : __builtin_amdgcn_rsqf(ss);
+      f32x4 dX[K::D / 16];
 #pragma unroll
-    for (int rb = 0; rb < K::RB; ++rb)
+      for (int cb = 0; cb < K::D / 16; ++cb) dX[cb] = kZero4;
 #pragma unroll
-      for (int cb = 0; cb < K::D / 16; ++cb) dX[rb][cb] = kZero4;
-#pragma unroll
-    for (int fb = 0; fb < K::NF; ++fb) {
-      const int node = (fb * 16) / p.m;
-      const float c1 = p.nc.c1[node], c0 = p.nc.c0[node];
-      const float sb = c1 * 0.6931471805599453f;  // sqrt(beta_r)
-      const bf16x8 pa0 = ld8(sP + (fb * 16 + c16) * K::LP + 8 * g), pa1 = ld8(sP + (fb * 16 + c16) * K::LP + 32 + 8 * g);
-      const bf16x8 pg0 = ld8(sP + (K::F + fb * 16 + c16) * K::LP + 8 * g);
-      const bf16x8 pg1 = ld8(sP + (K::F + fb * 16 + c16) * K::LP + 32 + 8 * g);
-#pragma unroll
-      for (int rb = 0; rb < K::RB; ++rb) {
-        // y[f = fb*16 + 4g + r][row]: anchors and prf of the same four features
-        f32x4 ya = mfma_bf16(pa0, xb[rb][0], kZero4);
-        ya = mfma_bf16(pa1, xb[rb][1], ya);
-        f32x4 yg = mfma_bf16(pg0, xb[rb][0], kZero4);
-        yg = mfma_bf16(pg1, xb[rb][1], yg);
-        const uint2 dr = cur.dp[fb][rb];
+      for (int j = 0; j < 2; ++j) {
+        // y[f = 16 fb + 4g + r][row 16 rb + l%16] for the anchors and the prf of the same four features
+        f32x4 ya = mfma_bf16(pa[j][0], xb0, kZero4);
+        ya = mfma_bf16(pa[j][1], xb1, ya);
+        f32x4 yg = mfma_bf16(pg[j][0], xb0, kZero4);
+        yg = mfma_bf16(pg[j][1], xb1, yg);
+        const uint2 dr = cur.dp[rb][j];
         const float dp[4] = {__uint_as_float(dr.x << 16), __uint_as_float(dr.x & 0xFFFF0000u),
                              __uint_as_float(dr.y << 16), __uint_as_float(dr.y & 0xFFFF0000u)};
         f32x4 wa, wg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float a = ya[r] * inv[rb];
-          const float e = fast_exp2(fmaf(yg[r] * inv[rb], c1, c0));
+          const float a = ya[r] * inv;
+          const float e = fast_exp2(fmaf(yg[r] * inv, c1[j], c0[j]));
           const float ae = a * e;
           wa[r] = dp[r] * 2.f * ae;
-          wg[r] = dp[r] * a * ae * sb;
+          wg[r] = dp[r] * a * ae * sb[j];
         }
         const bf16x8 w = pk_pair(wa, wg);
 #pragma unroll
-        for (int cb = 0; cb < K::D / 16; ++cb) {
-          const uint16_t* pr = sPT + (cb * 16 + c16) * K::LPT + fb * 16 + 4 * g;
-          dX[rb][cb] = mfma_bf16(ld4x2(pr, pr + K::F), w, dX[rb][cb]);
-        }
+        for (int cb = 0; cb < K::D / 16; ++cb) dX[cb] = mfma_bf16(pt[j][cb], w, dX[cb]);
       }
+      // dX[cb][r] = this wave's part of dxh[row 16 rb + l%16][c = 16 cb + 4g + r]
+#pragma unroll
+      for (int cb = 0; cb < K::D / 16; ++cb)
+        *reinterpret_cast<f32x4*>(sR + (wave * K::RT + rb * 16 + c16) * K::LR + cb * 16 + 4 * g) = dX[cb];
     }
-    // dX[rb][cb][r] = dxh[row][c = cb*16 + 4g + r]
+    __syncthreads();
+    if (tid < K::RT * 16) {  // 16 lanes per row, four columns each
+      const int rr = tid >> 4, c = 4 * (tid & 15);
+      const int64_t row = r0 + rr;
+      const uint2 xr = *reinterpret_cast<const uint2*>(sX + rr * K::LX + c);
+      const float xv[4] = {__uint_as_float(xr.x << 16), __uint_as_float(xr.x & 0xFFFF0000u),
+                           __uint_as_float(xr.y << 16), __uint_as_float(xr.y & 0xFFFF0000u)};
+      f32x4 dh = kZero4;
 #pragma unroll
-    for (int rb = 0; rb < K::RB; ++rb) {
-      float xh[K::D / 16][4];
-      float proj = 0.f;
+      for (int w = 0; w < K::NW; ++w) dh += *reinterpret_cast<const f32x4*>(sR + (w * K::RT + rr) * K::LR + c);
+      float ss = 0.f, pr = 0.f;
 #pragma unroll
-      for (int cb = 0; cb < K::D / 16; ++cb) {
-        const uint2 xr = cur.xo[rb][cb];
-        xh[cb][0] = __uint_as_float(xr.x << 16) * inv[rb];
-        xh[cb][1] = __uint_as_float(xr.x & 0xFFFF0000u) * inv[rb];
-        xh[cb][2] = __uint_as_float(xr.y << 16) * inv[rb];
-        xh[cb][3] = __uint_as_float(xr.y & 0xFFFF0000u) * inv[rb];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) proj = fmaf(xh[cb][r], dX[rb][cb][r], proj);
+      for (int r = 0; r < 4; ++r) {
+        ss = fmaf(xv[r], xv[r], ss);
+        pr = fmaf(xv[r], dh[r], pr);
       }
-      proj += __shfl_xor(proj, 16, 64);
-      proj += __shfl_xor(proj, 32, 64);
-      if (clamp[rb]) proj = 0.f;
-      if (row[rb] < p.n_rows) {
 #pragma unroll
-        for (int cb = 0; cb < K::D / 16; ++cb) {
-          f32x4 o;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (dX[rb][cb][r] - xh[cb][r] * proj) * inv[rb];
-          *reinterpret_cast<uint2*>(dx + row[rb] * K::D + cb * 16 + 4 * g) = pk4(o);
-        }
+      for (int o = 1; o < 16; o <<= 1) {
+        ss += __shfl_xor(ss, o, 64);
+        pr += __shfl_xor(pr, o, 64);
       }
+      const bool clamp = ss < 1e-24f;
+      const float inv = clamp ? 1e12f : __builtin_amdgcn_rsqf(ss);
+      const float proj = clamp ? 0.f : pr * inv;  // xh . dxh
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = (dh[r] - xv[r] * inv * proj) * inv;
+      if (row < p.n_rows) *reinterpret_cast<uint2*>(dx + row * K::D + c) = pk4(o);
     }
   }
 }
@@ -844,7 +862,7 @@ ChunkedArgs forward_args(const BackwardArgs& a) {
 bool backward_fused_supported(const BackwardArgs& a) {
   if (a.n_heads == 0 || a.L == 0) return false;  // nothing for the MFMA kernels: the general launcher handles it
   if (!a.io_bf16 || a.d != 64 || a.dv != 64 || a.F != K256::F || a.chunk != 64 || a.m % 32 != 0) return false;
-  if (a.n_draw_sets > 1 && a.L % V256::ROWS != 0) return false;  // a VJP tile must not span two draw sets
+  if (a.n_draw_sets > 1 && a.L % V256::RT != 0) return false;  // a VJP tile must not span two draw sets
   int64_t seg_len = 0;
   return fused_segment_count(forward_args(a), &seg_len) > 0 && seg_len % K256::C == 0;
 }
@@ -947,8 +965,8 @@ hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&vjp_kernel<V256>), hipFuncAttributeMaxDynamicSharedMemorySize,
                           V256::kLds);
   if (e != hipSuccess) return e;
-  const int64_t n_tiles = (vp.n_rows + V256::ROWS - 1) / V256::ROWS;
-  const unsigned gx = (unsigned)(n_tiles < 512 ? n_tiles : 512);
+  const int64_t n_tiles = (vp.n_rows + V256::RT - 1) / V256::RT;
+  const unsigned gx = (unsigned)(n_tiles < 128 ? n_tiles : 128);  // one workgroup per CU over both sides
   hipLaunchKernelGGL(vjp_kernel<V256>, dim3(gx, 2), dim3(V256::NT), V256::kLds, s, vp);
   return hipGetLastError();
 }

@@ -121,7 +121,55 @@ struct Params {
   const float* z0;
   float* S_out;
   float* z_out;
+  // Variable-length batches (vl_tab non-null): the packed token axis of each
+  // head holds sequences s at tokens cu[s] .. cu[s+1] (T tokens per head); work
+  // item g of a head is segment vl_tab[2g+1] of sequence vl_tab[2g] and owns
+  // state item g; work items g >= *vl_count exit at once.
+  const int* vl_tab;
+  const int* vl_count;
+  const int64_t* cu;
+  int64_t T;
+  int g_max;         // work items per head
 };
+
+// Where a workgroup's tokens lie: the packed row of its sequence's token 0,
+// its token range in the sequence and its state item.
+struct Geo {
+  int64_t head;
+  int64_t row0;
+  int64_t t0, t1;
+  int64_t item;
+  int seg;
+  bool valid;
+};
+
+// per_head: work items per head of a dense launch; items_per_head: state
+// items per head in the workspace (dense).
+__device__ __forceinline__ Geo geo_of(const Params& p, int per_head, int64_t seg_len, int64_t items_per_head) {
+  Geo g;
+  const int64_t w = blockIdx.x;
+  if (!p.vl_tab) {
+    g.head = w / per_head;
+    g.seg = (int)(w - g.head * per_head);
+    g.row0 = g.head * p.L;
+    g.t0 = (int64_t)g.seg * seg_len;
+    g.t1 = min<int64_t>(p.L, g.t0 + seg_len);
+    g.item = g.head * items_per_head + g.seg;
+    g.valid = true;
+  } else {
+    g.head = w / p.g_max;
+    const int gi = (int)(w - g.head * p.g_max);
+    g.valid = gi < *p.vl_count;
+    const int sq = g.valid ? p.vl_tab[2 * gi] : 0;
+    g.seg = g.valid ? p.vl_tab[2 * gi + 1] : 0;
+    const int64_t b = p.cu[sq], e = p.cu[sq + 1];
+    g.row0 = g.head * p.T + b;
+    g.t0 = (int64_t)g.seg * seg_len;
+    g.t1 = min<int64_t>(e - b, g.t0 + seg_len);
+    g.item = g.head * p.g_max + gi;
+  }
+  return g;
+}
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
   uint2 r;
@@ -228,11 +276,12 @@ __device__ __forceinline__ void load_v(int tid, const uint16_t* __restrict__ v, 
 }
 
 template <class K, int NT = K::NT>
-__device__ __forceinline__ void issue_loads(int tid, const Params& p, int64_t head, int64_t c0t, int n, bool want_q,
+// row0: packed row of token 0 of the sequence; c0t: the chunk's first token in it
+__device__ __forceinline__ void issue_loads(int tid, const Params& p, int64_t row0, int64_t c0t, int n, bool want_q,
                                             Prefetch<K, NT>& pf) {
-  if (want_q) load_x<K, NT>(tid, p.q + (head * p.L + c0t) * K::D, n, pf.q);
-  load_x<K, NT>(tid, p.k + (head * p.L + c0t) * K::D, n, pf.k);
-  load_v<K, NT>(tid, p.v + (head * p.L + c0t) * K::DV, n, pf.v0, pf.v1);
+  if (want_q) load_x<K, NT>(tid, p.q + (row0 + c0t) * K::D, n, pf.q);
+  load_x<K, NT>(tid, p.k + (row0 + c0t) * K::D, n, pf.k);
+  load_v<K, NT>(tid, p.v + (row0 + c0t) * K::DV, n, pf.v0, pf.v1);
 }
 
 // Write staged q or k vectors to LDS (padded rows) with, per row,
@@ -534,14 +583,14 @@ __device__ __forceinline__ int64_t frag_off(int fb, int et, int lane) {
   return ((int64_t)(fb * K::NE + et) * 64 + lane) * 4;
 }
 
-// State for the wave's feature blocks fb0..fb0+FBW-1: workspace item `item`
-// of the head when from_ws, else S0/z0 (zero when absent).
+// State for the wave's feature blocks fb0..fb0+FBW-1: workspace state item
+// `item` (absolute index) when from_ws, else S0/z0 of the head (zero when absent).
 template <class K>
 __device__ __forceinline__ void load_state_item(const Params& p, int64_t head, bool from_ws, int64_t item, int fb0,
                                                 int lane, f32x4 (&st)[K::FBW][K::NE]) {
   const int g = lane >> 4, col = lane & 15;
   if (from_ws) {
-    const float* in = p.ws + (head * p.p1_items + item) * (int64_t)K::F * K::DVP;
+    const float* in = p.ws + item * (int64_t)K::F * K::DVP;
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
@@ -572,7 +621,7 @@ __device__ __forceinline__ void load_state_item(const Params& p, int64_t head, b
 template <class K>
 __device__ __forceinline__ void load_state(const Params& p, int64_t head, int seg, int fb0, int lane,
                                            f32x4 (&st)[K::FBW][K::NE]) {
-  load_state_item<K>(p, head, p.n_seg > 1, (int64_t)seg * p.sub, fb0, lane, st);
+  load_state_item<K>(p, head, p.n_seg > 1, head * p.p1_items + (int64_t)seg * p.sub, fb0, lane, st);
 }
 
 // Final state of the head (last segment only) for the wave's feature blocks.
@@ -706,7 +755,7 @@ __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
   Prefetch<K, NT1> pf;
   auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
     const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-    issue_loads<K, NT1>(threadIdx.x, p, head, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
+    issue_loads<K, NT1>(threadIdx.x, p, head * p.L, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
   };
   load_chunk(0);
   store_x<K, NT1>(threadIdx.x, pf.k, sK(0), sInv(0), sInv(0) + K::C);
@@ -760,14 +809,11 @@ __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nsub = p.p1_segs;  // sub-segments covered by pass 1
-  const int n_items = p.p1_items;
-  const int64_t head = blockIdx.x / nsub;
-  const int seg = (int)(blockIdx.x - head * nsub);
+  const Geo geo = geo_of(p, p.p1_segs, p.seg_len / p.sub, p.p1_items);
+  if (!geo.valid) return;  // a variable-length launch's spare work item (whole workgroup)
+  const int64_t head = geo.head;
   const int set = (int)(head % p.n_draw_sets);
-  const int64_t sub_len = p.seg_len / p.sub;
-  const int64_t t0 = (int64_t)seg * sub_len;
-  const int64_t t1 = min<int64_t>(p.L, t0 + sub_len);
+  const int64_t t0 = geo.t0, t1 = geo.t1;
   const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
 
   for (int t = threadIdx.x; t < K::DV * K::LDV / 2; t += K::NT + NS) reinterpret_cast<uint32_t*>(sV(2))[t] = 0u;
@@ -807,7 +853,7 @@ __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
 #pragma unroll
       for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sv_last, vo, lane, s_, kfb, st);
     }
-    float* out = p.ws + (head * n_items + seg) * (int64_t)K::F * K::DVP;
+    float* out = p.ws + geo.item * (int64_t)K::F * K::DVP;
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
@@ -818,7 +864,7 @@ __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
     Prefetch<K, NS> pf;
     auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
       const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-      issue_loads<K, NS>(stid, p, head, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
+      issue_loads<K, NS>(stid, p, geo.row0, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
     };
     load_chunk(0);
     store_x<K, NS>(stid, pf.k, sK(0), sInv(0), sInv(0) + K::C);
@@ -897,7 +943,7 @@ __global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
   Prefetch<K> pf;
   auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
     const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-    issue_loads<K>(threadIdx.x, p, head, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
+    issue_loads<K>(threadIdx.x, p, head * p.L, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
   };
   load_chunk(0);
   store_x<K>(threadIdx.x, pf.q, sQ, sinvq, slgq);
@@ -1095,8 +1141,10 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
   const bool producer = wave < K::NP;
   const int cw = wave - K::NP;           // consumer index: token block cw >> 1, column half cw & 1
   const int ctid = threadIdx.x - K::NP * 64;  // thread index among the consumers
-  const int64_t head = blockIdx.x / p.n_seg;
-  const int seg = (int)(blockIdx.x - head * p.n_seg);
+  const Geo geo = geo_of(p, p.n_seg, p.seg_len, p.p1_items);
+  if (!geo.valid) return;  // a variable-length launch's spare work item (whole workgroup)
+  const int64_t head = geo.head;
+  const int seg = geo.seg;
   const int set = (int)(head % p.n_draw_sets);
   const int fb0 = (producer ? wave : 0) * K::FBW;
 
@@ -1104,8 +1152,7 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
   const RowOff<K, K::LDF> so(col);
   for (int b = 0; b < 3; ++b) init_vconst<K, K::NTW>(threadIdx.x, sV(b));
   for (int t = threadIdx.x; t < K::LDF; t += K::NTW) sSt[(K::DV + 1) * K::LDF + t] = 0;
-  const int64_t t0 = (int64_t)seg * p.seg_len;
-  const int64_t t1 = min<int64_t>(p.L, t0 + p.seg_len);
+  const int64_t t0 = geo.t0, t1 = geo.t1;
   const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
 
   // Producers and consumers run separate code (so each keeps only its own
@@ -1117,7 +1164,7 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
     f32x4 st[K::FBW][K::NE];
     bf16x8 kf[K::FBW][K::NTS] = {};
     load_p<K>(p, set, fb0, lane, pa, pg, c1, c0);
-    load_state<K>(p, head, seg, fb0, lane, st);
+    load_state_item<K>(p, head, p.vl_tab || p.n_seg > 1, geo.item, fb0, lane, st);
     write_st<K>(sSt, so, wave, lane, st);
     __syncthreads();  // chunks 0 and 1 staged
     phase_k<K, true, false>(sK(0), sInv(0, 2), sInv(0, 3), sPk(0), fb0, lane, pa, pg, c1, c0, kf, nullptr, vo, kf, st);
@@ -1141,7 +1188,7 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
       write_st<K>(sSt, so, wave, lane, st);
       __syncthreads();  // A
     }
-    if (seg == p.n_seg - 1 && (p.S_out || p.z_out)) store_state_out<K>(p, head, fb0, lane, st);
+    if (!p.vl_tab && seg == p.n_seg - 1 && (p.S_out || p.z_out)) store_state_out<K>(p, head, fb0, lane, st);
   } else {
     // The SIMD issues from the highest-priority ready wave first: consumers
     // (MFMA and LDS, little VALU) go ahead of the VALU-heavy producers, which
@@ -1150,7 +1197,7 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
     Prefetch<K, K::NC * 64> pf;
     auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
       const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-      issue_loads<K, K::NC * 64>(ctid, p, head, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
+      issue_loads<K, K::NC * 64>(ctid, p, geo.row0, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
     };
     auto stage = [&](int bx, int bv) {
       store_x<K, K::NC * 64>(ctid, pf.q, sQ(bx), sInv(bx, 0), sInv(bx, 1));
@@ -1170,7 +1217,7 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
       constexpr int IB = decltype(ib_c)::value, H = decltype(h_c)::value;
       for (int c = 0; c < nch; ++c) {
         const int b = c & 1;
-        const int64_t row0 = head * p.L + t0 + (int64_t)c * K::C;
+        const int64_t row0 = geo.row0 + t0 + (int64_t)c * K::C;
         const int n = (int)min<int64_t>(K::C, t1 - (t0 + (int64_t)c * K::C));
         f32x4 acc0[K::ESPLIT];
         // ---- [A] contractions of chunk c; staging of chunk c+2 ----
@@ -1258,7 +1305,7 @@ __global__ __launch_bounds__(K::NT) void ncout_kernel(Params p) {
   const RowOff<K, K::LDF> so(col);
   {
     f32x4 st[K::FBW][K::NE];
-    load_state_item<K>(p, head, p.L > 0, p.p1_items - 1, fb0, lane, st);
+    load_state_item<K>(p, head, p.L > 0, head * p.p1_items + p.p1_items - 1, fb0, lane, st);
     write_st<K>(sSt, so, wave, lane, st);
   }
   for (int t = threadIdx.x; t < K::LDF; t += K::NT) sSt[(K::DV + 1) * K::LDF + t] = 0;
@@ -1587,6 +1634,158 @@ hipError_t segment_prefix_t(const ChunkedArgs& a, float* ws, hipStream_t s) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Variable-length batches (F = 256 configuration).
+namespace {
+
+// Work list (one workgroup): each sequence's segment count, their exclusive
+// prefix (the sequence's first work item) and the (sequence, segment) pair of
+// every work item.  Offsets that do not rise from 0 to T without decreasing
+// give no work items (and zero segments for every sequence).
+__global__ __launch_bounds__(256) void vl_setup_kernel(const int64_t* __restrict__ cu, int n_seqs, int64_t T,
+                                                       int64_t seg_len, int g_max, int* __restrict__ tab,
+                                                       int* __restrict__ first, int* __restrict__ nseg,
+                                                       int* __restrict__ count) {
+  __shared__ int part[256];
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) bad = (cu[0] != 0 || cu[n_seqs] != T) ? 1 : 0;
+  __syncthreads();
+  const int per = (n_seqs + 255) / 256;
+  const int s0 = min(n_seqs, tid * per), s1 = min(n_seqs, s0 + per);
+  int local = 0;
+  for (int sq = s0; sq < s1; ++sq) {
+    const int64_t len = cu[sq + 1] - cu[sq];
+    if (len < 0) atomicOr(&bad, 1);
+    local += (int)((max<int64_t>(len, 0) + seg_len - 1) / seg_len);
+  }
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int v = part[t];
+      part[t] = run;
+      run += v;
+    }
+    if (run > g_max) bad = 1;
+    *count = bad ? 0 : run;
+  }
+  __syncthreads();
+  const bool ok = bad == 0;
+  int base = part[tid];
+  for (int sq = s0; sq < s1; ++sq) {
+    const int ns = ok ? (int)((cu[sq + 1] - cu[sq] + seg_len - 1) / seg_len) : 0;
+    first[sq] = ok ? base : 0;
+    nseg[sq] = ns;
+    for (int j = 0; j < ns; ++j) {
+      tab[2 * (base + j)] = sq;
+      tab[2 * (base + j) + 1] = j;
+    }
+    base += ns;
+  }
+}
+
+// Tokens per work item: about 256 work items over the chip, a multiple of two chunks.
+int64_t vl_seg_len(int64_t H, int64_t T) {
+  const int64_t want = (H * T + 255) / 256;
+  const int64_t sl = ((want + 127) / 128) * 128;
+  return sl < 128 ? 128 : sl;
+}
+
+// Work items per head: every sequence adds at most one partial segment.
+int vl_g_max(int64_t T, int n_seqs, int64_t seg_len) { return (int)(T / seg_len + n_seqs); }
+
+struct VlWs {
+  int *tab, *first, *nseg, *count;
+  float* states;
+  size_t bytes;
+};
+
+VlWs vl_ws(const VarlenArgs& a, int g_max, void* base) {
+  VlWs w{};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    char* q = p ? p + off : nullptr;
+    off += (b + 255) & ~(size_t)255;
+    return q;
+  };
+  w.states = reinterpret_cast<float*>(take(sizeof(float) * (size_t)a.c.n_heads * g_max * CfgF256::F * CfgF256::DVP));
+  w.tab = reinterpret_cast<int*>(take(sizeof(int) * 2 * (size_t)g_max));
+  w.first = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
+  w.nseg = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
+  w.count = reinterpret_cast<int*>(take(sizeof(int)));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+bool varlen_supported(const VarlenArgs& a) {
+  return a.c.io_bf16 && a.c.d == 64 && a.c.dv == 64 && a.c.F == CfgF256::F && a.c.m % 32 == 0;
+}
+
+size_t varlen_workspace_bytes(const VarlenArgs& a) {
+  if (a.c.n_heads == 0 || a.n_seqs == 0) return 0;
+  return vl_ws(a, vl_g_max(a.c.L, a.n_seqs, vl_seg_len(a.c.n_heads, a.c.L)), nullptr).bytes;
+}
+
+hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s) {
+  using K = CfgF256;
+  using KS = typename MainPass<K>::type;
+  const int64_t H = a.c.n_heads, T = a.c.L;
+  if (H == 0 || a.n_seqs == 0) return hipSuccess;
+  const int64_t seg_len = vl_seg_len(H, T);
+  const int g_max = vl_g_max(T, a.n_seqs, seg_len);
+  const VlWs w = vl_ws(a, g_max, a.c.ws);
+  hipLaunchKernelGGL(vl_setup_kernel, dim3(1), dim3(256), 0, s, a.cu, a.n_seqs, T, seg_len, g_max, w.tab, w.first,
+                     w.nseg, w.count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  Params p{};
+  p.q = static_cast<const uint16_t*>(a.c.q);
+  p.k = static_cast<const uint16_t*>(a.c.k);
+  p.v = static_cast<const uint16_t*>(a.c.v);
+  p.o = static_cast<uint16_t*>(a.c.o);
+  p.L = T;
+  p.Lq = T;
+  p.seg_len = seg_len;
+  p.n_seg = g_max;
+  p.sub = kSub;
+  p.p1_segs = g_max;
+  p.p1_items = g_max;
+  p.m = a.c.m;
+  p.anchors = static_cast<const uint16_t*>(a.c.anchors);
+  p.prf = static_cast<const uint16_t*>(a.c.prf);
+  p.draw_set_stride = a.c.draw_set_stride;
+  p.n_draw_sets = a.c.n_draw_sets;
+  p.nc = a.c.nc;
+  p.ws = w.states;
+  p.vl_tab = w.tab;
+  p.vl_count = w.count;
+  p.cu = a.cu;
+  p.T = T;
+  p.g_max = g_max;
+  const unsigned grid = (unsigned)(H * g_max);
+  if (T > 0) {  // every segment's state (the last ones too: their sums are the final states)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            K::kLds1);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((pass1s_kernel<K>), dim3(grid), dim3(K::NT + 256), K::kLds1, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  e = launch_scan_varlen(w.states, H, a.n_seqs, g_max, w.first, w.nseg, K::F, K::DV, a.c.S0, a.c.z0, a.c.S_out,
+                         a.c.z_out, s);
+  if (e != hipSuccess || T == 0) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass2s_kernel<KS>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          KS::kLdsS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pass2s_kernel<KS>, dim3(grid), dim3(KS::NTW), KS::kLdsS, s, p);
+  return hipGetLastError();
+}
 
 int fused_segment_count(const ChunkedArgs& a, int64_t* seg_len) {
   int n = 0;

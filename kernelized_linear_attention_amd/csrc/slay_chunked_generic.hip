@@ -313,6 +313,39 @@ hipError_t launch_generic_nc_t(const ChunkedArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Variable-length batches: per (sequence s, head h) and state element, the
+// exclusive prefix over the sequence's segment items (first[s] .. +nseg[s]) of
+// head h, from S0 of (s, h); the total goes to S_out.  States are fragment
+// ordered (layout 1); S0/S_out are [n_seqs][H][F][dv].
+__global__ __launch_bounds__(kGThreads) void vl_scan_kernel(float* states, int64_t H, int g_max, const int* first,
+                                                            const int* nseg, int F, int dv, const float* S0,
+                                                            const float* z0, float* S_out, float* z_out, int64_t E) {
+  const int64_t sh = blockIdx.y;  // s * H + h
+  const int64_t h = sh % H, sq = sh / H;
+  const int64_t idx = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
+  if (idx >= E) return;
+  int f, e;
+  scan_map(idx, F, dv, 1, f, e);
+  float run = 0.f;
+  if (e < dv) {
+    if (S0) run = S0[(sh * F + f) * dv + e];
+  } else if (e == dv) {
+    if (z0) run = z0[sh * F + f];
+  }
+  const int n = nseg[sq];
+  float* st = states + (h * g_max + first[sq]) * E + idx;
+  for (int j = 0; j < n; ++j) {
+    const float d = st[(int64_t)j * E];
+    st[(int64_t)j * E] = run;
+    run += d;
+  }
+  if (e < dv) {
+    if (S_out) S_out[(sh * F + f) * dv + e] = run;
+  } else if (e == dv) {
+    if (z_out) z_out[sh * F + f] = run;
+  }
+}
+
 hipError_t launch_chunk_state(const float* phik, const void* v, bool v_bf16, int64_t n_heads, int64_t L, int F,
                               int dv, int C, int64_t item_stride, float* states, hipStream_t s) {
   const int64_t n_chunks = (L + C - 1) / C;
@@ -324,6 +357,16 @@ hipError_t launch_chunk_state(const float* phik, const void* v, bool v_bf16, int
   else
     hipLaunchKernelGGL(chunk_state_kernel<float>, grid, dim3(kGThreads), 0, s, phik, static_cast<const float*>(v),
                        L, F, dv, C, item_stride, states);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, const int* first, const int* nseg,
+                              int F, int dv, const float* S0, const float* z0, float* S_out, float* z_out,
+                              hipStream_t s) {
+  const int64_t E = scan_state_elems(F, dv, 1);
+  if (H == 0 || n_seqs == 0) return hipSuccess;
+  hipLaunchKernelGGL(vl_scan_kernel, dim3((unsigned)((E + kGThreads - 1) / kGThreads), (unsigned)(H * n_seqs)),
+                     dim3(kGThreads), 0, s, states, H, g_max, first, nseg, F, dv, S0, z0, S_out, z_out, E);
   return hipGetLastError();
 }
 

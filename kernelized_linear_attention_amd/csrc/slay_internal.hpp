@@ -86,6 +86,22 @@ struct ScanArgs {
 };
 int64_t scan_state_elems(int F, int dv, int layout);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, const int* first, const int* nseg,
+                              int F, int dv, const float* S0, const float* z0, float* S_out, float* z_out,
+                              hipStream_t s);
+
+// Variable-length batch of the causal forward: n_seqs sequences packed along
+// the token axis of each of H heads (q, k [H][T][d], v, o [H][T][dv]),
+// sequence s at tokens cu[s] .. cu[s+1] (device int64, n_seqs + 1 entries);
+// states [n_seqs][H][F][dv].
+struct VarlenArgs {
+  ChunkedArgs c;  // q, k, v, o, dtypes, d, dv, F, m, R, draws, nc, S0, z0, S_out, z_out, ws (n_heads = H, L = T)
+  int n_seqs;
+  const int64_t* cu;
+};
+bool varlen_supported(const VarlenArgs& a);
+size_t varlen_workspace_bytes(const VarlenArgs& a);
+hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s);
 
 // Per-chunk states dS_c = phi(k_c)^T [v_c | 1] of the general path, fp32
 // [n_heads][item_stride][F][dv+1] (chunk c at item c).

@@ -152,6 +152,54 @@ def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     return out
 
 
+def varlen_fwd_workspace_size(fm: FeatureMap, n_seqs: int, H: int, total_tokens: int, dv: int,
+                              dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.slay_attn_varlen_fwd_workspace_size(fm.c_params(), n_seqs, H, total_tokens, dv, _dtype_code(dtype)))
+
+
+def varlen_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+               S0: torch.Tensor | None = None, z0: torch.Tensor | None = None, return_state: bool = False,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, S_out=None, z_out=None):
+    """Causal SLAY forward over sequences of different lengths packed per head.
+
+    q, k [H, T, d]; v [H, T, dv]; cu_seqlens int64 [n_seqs + 1] on the GPU
+    (sequence s = tokens cu[s] .. cu[s+1] - 1 of every head) -> o [H, T, dv].
+    S0, z0: optional fp32 initial states [n_seqs, H, F, dv], [n_seqs, H, F];
+    with return_state the final states are returned as well.
+    """
+    lib = _lib.load()
+    H, T, d = q.shape
+    dv = v.shape[-1]
+    n_seqs = cu_seqlens.numel() - 1
+    _need(q, "q")
+    _need(k, "k", q.shape, q.dtype)
+    _need(v, "v", (H, T, dv), q.dtype)
+    _need(cu_seqlens, "cu_seqlens", None, torch.int64)
+    if out is None:
+        out = torch.empty((H, T, dv), dtype=q.dtype, device=q.device)
+    _need(out, "out", (H, T, dv), q.dtype)
+    for t, name, shp in ((S0, "S0", (n_seqs, H, fm.F, dv)), (z0, "z0", (n_seqs, H, fm.F))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
+    if return_state:
+        if S_out is None:
+            S_out = torch.empty((n_seqs, H, fm.F, dv), dtype=torch.float32, device=q.device)
+        if z_out is None:
+            z_out = torch.empty((n_seqs, H, fm.F), dtype=torch.float32, device=q.device)
+    nbytes = varlen_fwd_workspace_size(fm, n_seqs, H, T, dv, q.dtype)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.slay_attn_varlen_fwd(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype),
+                                  n_seqs, H, cu_seqlens.data_ptr(), T, dv, _ptr(S0), _ptr(z0), out.data_ptr(),
+                                  _ptr(S_out), _ptr(z_out), _ptr(workspace), wsz, _stream(q))
+    _lib.check(st, "slay_attn_varlen_fwd")
+    if return_state:
+        return out, S_out, z_out
+    return out
+
+
 def chunked_bwd_workspace_size(fm: FeatureMap, B: int, H: int, L: int, dv: int, chunk: int,
                                dtype: torch.dtype) -> int:
     lib = _lib.load()

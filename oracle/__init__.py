@@ -352,3 +352,32 @@ def slay_causal_bwd(q, k, v, dout, anchors, prf, eps: float, R: int, m: int, for
                                    stride, BWD_FORMS[form], _p(S0p), _p(z0p), _p(dout), _p(dSTp), _p(dzTp),
                                    _p(dq), _p(dk), _p(dvv), _p(dS0), _p(dz0)), "slay_causal_bwd")
     return dq, dk, dvv, dS0, dz0
+
+
+def slay_causal_varlen(q, k, v, cu_seqlens, anchors, prf, eps: float, R: int, m: int, S0=None, z0=None,
+                       form: str = "recurrent"):
+    """Causal SLAY over sequences packed along the token axis of every head.
+
+    q, k: [H, T, d]; v: [H, T, dv]; cu_seqlens: [n_seqs + 1] offsets (sequence
+    s = tokens cu[s] .. cu[s+1] - 1 of each head); S0, z0: optional initial
+    states [n_seqs, H, F, dv], [n_seqs, H, F].  Each sequence is its own causal
+    problem, started from its own state.  Returns (o [H, T, dv],
+    S [n_seqs, H, F, dv], z [n_seqs, H, F]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    H, T, _ = q.shape
+    dv = v.shape[-1]
+    F = R * m
+    n = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T and all(b <= e for b, e in zip(cu[:-1], cu[1:]))
+    o = np.zeros((H, T, dv))
+    S = np.zeros((n, H, F, dv))
+    z = np.zeros((n, H, F))
+    for s in range(n):
+        b, e = cu[s], cu[s + 1]
+        o_s, S_s, z_s = slay_causal(q[:, b:e], k[:, b:e], v[:, b:e], anchors, prf, eps, R, m, form=form,
+                                    S0=None if S0 is None else _f64(S0)[s], z0=None if z0 is None else _f64(z0)[s])
+        o[:, b:e] = o_s
+        S[s], z[s] = S_s, z_s
+    return o, S, z

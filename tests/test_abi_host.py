@@ -231,3 +231,37 @@ def test_backward_validation_and_workspace(lib):
     # nothing to do, and no tokens (only the state gradient passes through; no pointers needed)
     assert lib.slay_attn_chunked_bwd_workspace_size(ctypes.byref(p), 1, 16, 0, 64, 64, _lib.SLAY_BF16) == 0
     assert _bwd(lib, p, B=0) == _lib.SLAY_OK
+
+
+def _vl(lib, p, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dt=_lib.SLAY_BF16, n=4, H=16, cu=FAKE, T=16384, dv=64, S0=None, z0=None,
+             o=FAKE, S_out=None, z_out=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.slay_attn_varlen_fwd(ctypes.byref(p) if p is not None else None, a["q"], a["k"], a["v"], a["dt"],
+                                    a["n"], a["H"], a["cu"], a["T"], a["dv"], a["S0"], a["z0"], a["o"], a["S_out"],
+                                    a["z_out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_varlen_validation_and_workspace(lib):
+    E_INV, E_UNS = _lib.SLAY_E_INVALID, _lib.SLAY_E_UNSUPPORTED
+    p = _params()
+    assert _vl(lib, None) == E_INV
+    assert _vl(lib, p, n=-1) == E_INV and _vl(lib, p, H=-1) == E_INV and _vl(lib, p, T=-1) == E_INV
+    assert _vl(lib, p, dv=0) == E_INV
+    assert _vl(lib, p, dt=_lib.SLAY_F32) == E_UNS
+    assert _vl(lib, p, dv=128) == E_UNS and b"variable-length" in lib.slay_last_error()
+    assert _vl(lib, _params(R=3, m=32)) == E_UNS
+    assert _vl(lib, p, cu=None) == E_INV
+    for name in ("q", "k", "v", "o"):
+        assert _vl(lib, p, **{name: None}) == E_INV, name
+        assert _vl(lib, p, **{name: FAKE + 4}) == E_INV, name
+    assert _vl(lib, p) == E_INV and b"workspace too small" in lib.slay_last_error()
+    # one state per (head, work item), the work list (two ints per item), per-sequence first item and count
+    n = lib.slay_attn_varlen_fwd_workspace_size(ctypes.byref(p), 4, 16, 16384, 64, _lib.SLAY_BF16)
+    g_max = 16384 // 1024 + 4
+    r = lambda b: (b + 255) // 256 * 256
+    assert n == r(4 * 16 * g_max * 256 * 80) + r(8 * g_max) + 2 * r(16) + r(4)
+    assert _vl(lib, p, ws=FAKE, ws_bytes=n - 1) == E_INV
+    # nothing to do
+    assert _vl(lib, p, n=0) == _lib.SLAY_OK and _vl(lib, p, H=0) == _lib.SLAY_OK
+    assert lib.slay_attn_varlen_fwd_workspace_size(ctypes.byref(p), 0, 16, 0, 64, _lib.SLAY_BF16) == 0

@@ -1,0 +1,167 @@
+"""GPU parity of the variable-length causal forward (sequences of different
+lengths packed per head) through the C ABI against the fp64 oracle, which
+runs each sequence on its own.  Bar as for the causal forward: 2e-2
+row-normwise for bf16, the final states normwise per (sequence, head).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import slay_synth as ss
+from helpers import TOL, headnorm_rel, rownorm_rel, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+W = ss.WORKLOADS["h16_l16k_bf16"]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from kernelized_linear_attention_amd import ops
+
+    return ops
+
+
+def _packed(H, lengths, seed):
+    """q, k [H, T, d], v [H, T, dv] (bf16-exact) and the offsets of the sequences."""
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T = int(cu[-1])
+    q, k, v = ss.make_qkv(W.with_(B=1, H=H, L=max(T, 1)), seed=seed)
+    return q[0, :, :T], k[0, :, :T], v[0, :, :T], cu
+
+
+def _states(n, H, seed):
+    rng = np.random.default_rng(seed)
+    S0 = np.abs(rng.standard_normal((n, H, W.F, W.dv))).astype(np.float32)
+    z0 = (rng.random((n, H, W.F)) + 0.5).astype(np.float32)
+    return S0, z0
+
+
+def _run(lib, q, k, v, cu, A, G, S0=None, z0=None, out=None):
+    import torch
+
+    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), W.R, W.m, W.eps)
+    f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    o, S, z = lib.varlen_fwd(fm, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                             torch.from_numpy(cu).cuda(), S0=f32(S0), z0=f32(z0), return_state=True, out=out)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(S), to_np(z)
+
+
+@pytest.mark.parametrize("H,lengths,with_state", [
+    (2, [300, 0, 1, 1000, 77, 2049, 128], True),   # empty, one-token, ragged and multi-segment sequences
+    (3, [64, 64, 64], False),
+    (1, [5000], True),
+])
+def test_varlen_parity(lib, orc, H, lengths, with_state):
+    _say(f"varlen parity H={H} lengths={lengths} state={with_state}")
+    q, k, v, cu = _packed(H, lengths, [3, 70, len(lengths)])
+    A, G = ss.make_draws(W)
+    S0, z0 = _states(len(lengths), H, 5) if with_state else (None, None)
+    o, S, z = _run(lib, q, k, v, cu, A, G, S0, z0)
+    ro, rS, rz = orc.slay_causal_varlen(q, k, v, cu, A, G, W.eps, W.R, W.m, S0=S0, z0=z0)
+    nz = [s for s, n in enumerate(lengths) if n > 0]
+    err = rownorm_rel(o, ro) if cu[-1] > 0 else 0.0
+    s_err = headnorm_rel(S.reshape(-1, W.F * W.dv), rS.reshape(-1, W.F * W.dv))
+    z_err = headnorm_rel(z.reshape(-1, W.F), rz.reshape(-1, W.F))
+    _say(f"  o rownorm {err:.3e}; S {s_err:.3e} z {z_err:.3e} (non-empty sequences {nz})")
+    assert err < TOL["bf16"] and s_err < TOL["bf16"] and z_err < TOL["bf16"]
+    for s, n in enumerate(lengths):  # an empty sequence passes its state through unchanged
+        if n == 0:
+            assert np.array_equal(S[s], np.float32(S0[s]) if with_state else np.zeros_like(S[s]))
+
+
+def test_varlen_equal_lengths_match_dense(lib):
+    """Equal lengths are a dense batch: the packed call matches slay_attn_chunked_fwd on [B][H][L]."""
+    import torch
+
+    B, H, L = 4, 2, 512
+    q, k, v, cu = _packed(H, [L] * B, [3, 71])
+    A, G = ss.make_draws(W)
+    o, S, z = _run(lib, q, k, v, cu, A, G)
+    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), W.R, W.m, W.eps)
+    dense = lambda x: to_dev(np.ascontiguousarray(x.reshape(H, B, L, -1).transpose(1, 0, 2, 3)), "bf16")
+    od, Sd, zd = lib.chunked_fwd(fm, dense(q), dense(k), dense(v), 64, return_state=True)
+    torch.cuda.synchronize()
+    od = to_np(od).transpose(1, 0, 2, 3).reshape(H, B * L, -1)
+    assert rownorm_rel(o, od) < 1e-2
+    assert headnorm_rel(S.reshape(B * H, -1), to_np(Sd).reshape(B * H, -1)) < 1e-4
+
+
+def test_varlen_prefill_then_decode(lib, orc):
+    """The final states of a mixed-length prefill are the decode state of every (sequence, head)."""
+    import torch
+
+    H, lengths = 2, [200, 37, 513]
+    q, k, v, cu = _packed(H, lengths, [3, 72])
+    A, G = ss.make_draws(W)
+    _, S, z = _run(lib, q, k, v, cu, A, G)
+    n = len(lengths) * H
+    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), W.R, W.m, W.eps)
+    Sd = torch.from_numpy(np.float32(S.reshape(n, W.F, W.dv))).cuda()
+    zd = torch.from_numpy(np.float32(z.reshape(n, W.F))).cuda()
+    rng = np.random.default_rng(9)
+    steps = [tuple(ss.bf16_round(rng.standard_normal((n, x)).astype(np.float32)) for x in (W.d, W.d, W.dv))
+             for _ in range(5)]
+    for qs, ks, vs in steps:
+        o_last = lib.recurrent_step(fm, to_dev(qs, "bf16"), to_dev(ks, "bf16"), to_dev(vs, "bf16"), Sd, zd)
+    torch.cuda.synchronize()
+    # oracle: each sequence's prompt plus the five decode tokens as one causal sequence
+    for s, L in enumerate(lengths):
+        b = int(cu[s])
+        for h in range(H):
+            row = s * H + h
+            qq = np.concatenate([q[h, b:b + L]] + [st[0][row:row + 1] for st in steps])
+            kk = np.concatenate([k[h, b:b + L]] + [st[1][row:row + 1] for st in steps])
+            vv = np.concatenate([v[h, b:b + L]] + [st[2][row:row + 1] for st in steps])
+            ro, _, _ = orc.slay_causal(qq[None], kk[None], vv[None], A, G, W.eps, W.R, W.m)
+            assert rownorm_rel(to_np(o_last)[row:row + 1], ro[0, -1:]) < TOL["bf16"]
+
+
+def test_varlen_many_short_sequences(lib, orc):
+    rng = np.random.default_rng(11)
+    lengths = [int(x) for x in rng.integers(0, 90, 300)]
+    H = 1
+    q, k, v, cu = _packed(H, lengths, [3, 73])
+    A, G = ss.make_draws(W)
+    o, S, z = _run(lib, q, k, v, cu, A, G)
+    ro, rS, _ = orc.slay_causal_varlen(q, k, v, cu, A, G, W.eps, W.R, W.m)
+    assert rownorm_rel(o, ro) < TOL["bf16"]
+    assert headnorm_rel(S.reshape(-1, W.F * W.dv), rS.reshape(-1, W.F * W.dv)) < TOL["bf16"]
+
+
+def test_varlen_bad_offsets_compute_nothing(lib):
+    """Offsets that decrease, or do not end at the token count, give no work:
+    o keeps its contents and the final states are the initial ones."""
+    import torch
+
+    H = 2
+    q, k, v, _ = _packed(H, [100, 100], [3, 74])
+    A, G = ss.make_draws(W)
+    S0, z0 = _states(2, H, 6)
+    for cu in (np.array([0, 150, 120], np.int64), np.array([0, 100, 150], np.int64)):
+        out = torch.full((H, 200, W.dv), 7.0, dtype=torch.bfloat16, device="cuda")
+        o, S, z = _run(lib, q, k, v, cu, A, G, S0, z0, out=out)
+        assert np.all(o == 7.0)
+        assert np.array_equal(S, np.float32(S0)) and np.array_equal(z, np.float32(z0))
+
+
+def test_varlen_no_sequences_and_unsupported(lib):
+    import torch
+
+    fm = lib.FeatureMap(to_dev(np.zeros((W.F, W.d)), "bf16"), to_dev(np.zeros((W.F, W.d)), "bf16"), W.R, W.m, W.eps)
+    e = torch.empty(2, 0, W.d, dtype=torch.bfloat16, device="cuda")
+    lib.varlen_fwd(fm, e, e, e, torch.zeros(1, dtype=torch.int64, device="cuda"))
+    fm96 = lib.FeatureMap(to_dev(np.zeros((96, W.d)), "bf16"), to_dev(np.zeros((96, W.d)), "bf16"), 3, 32, W.eps)
+    x = torch.zeros(1, 64, W.d, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(Exception, match="variable-length"):
+        lib.varlen_fwd(fm96, x, x, x, torch.tensor([0, 64], dtype=torch.int64, device="cuda"))

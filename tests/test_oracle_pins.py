@@ -635,3 +635,40 @@ def test_backward_homogeneity(orc):
     for dx, x in ((dq, t["q"]), (dk, t["k"])):
         dots = np.abs((dx * x).sum(-1)) / (np.linalg.norm(dx, axis=-1) * np.linalg.norm(x, axis=-1))
         assert dots.max() < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# Variable-length batches: every sequence is its own causal problem.
+
+def test_varlen_equal_lengths_match_dense_batch(orc):
+    rng = np.random.default_rng(61)
+    B, H, L, d, dv, R, m = 3, 2, 20, 6, 4, 2, 4
+    F = R * m
+    q, k, v = (rng.standard_normal((B, H, L, x)) for x in (d, d, dv))
+    a, g = rng.standard_normal((F, d)), rng.standard_normal((F, d))
+    S0 = np.abs(rng.standard_normal((B, H, F, dv)))
+    z0 = np.abs(rng.standard_normal((B, H, F))) + 0.5
+    dense = orc.slay_causal(q, k, v, a, g, EPS, R, m, S0=S0.reshape(B * H, F, dv), z0=z0.reshape(B * H, F))
+    pack = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(H, B * L, -1))
+    o, S, z = orc.slay_causal_varlen(pack(q), pack(k), pack(v), [0, L, 2 * L, 3 * L], a, g, EPS, R, m, S0=S0, z0=z0)
+    np.testing.assert_allclose(o, pack(dense[0]), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(S.reshape(B * H, F, dv), dense[1], rtol=1e-13)
+    np.testing.assert_allclose(z.reshape(B * H, F), dense[2], rtol=1e-13)
+
+
+def test_varlen_chained_sequences_equal_one(orc):
+    """Two sequences where the second starts from the first's final state are
+    one sequence split in two; an empty sequence passes its state through."""
+    rng = np.random.default_rng(63)
+    H, T, d, dv, R, m = 2, 29, 5, 3, 2, 4
+    F = R * m
+    q, k, v = (rng.standard_normal((H, T, x)) for x in (d, d, dv))
+    a, g = rng.standard_normal((F, d)), rng.standard_normal((F, d))
+    whole = orc.slay_causal_varlen(q, k, v, [0, T], a, g, EPS, R, m)
+    cut = 11
+    first = orc.slay_causal_varlen(q[:, :cut], k[:, :cut], v[:, :cut], [0, cut], a, g, EPS, R, m)
+    second = orc.slay_causal_varlen(q[:, cut:], k[:, cut:], v[:, cut:], [0, 0, T - cut], a, g, EPS, R, m,
+                                    S0=np.stack([first[1][0], first[1][0]]), z0=np.stack([first[2][0], first[2][0]]))
+    np.testing.assert_allclose(np.concatenate([first[0], second[0]], 1), whole[0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(second[1][1], whole[1][0], rtol=1e-12)
+    np.testing.assert_allclose(second[1][0], first[1][0], rtol=0, atol=0)  # the empty sequence
