@@ -194,7 +194,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per head of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["all", "fwd", "featmap", "noncausal", "backward", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "fwd", "featmap", "noncausal", "varlen", "backward", "decode"],
+                    default="all")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (scale for HBM byte counters)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -306,6 +307,30 @@ def main():
                      "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                                   "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                                   "traffic": read_traffic("noncausal_h16_l16k_bf16"),
+                                  "algorithmic_flops_per_launch": flops}})
+    if args.only in ("all", "varlen"):
+        # eight sequences of mixed lengths packed per head (16384 tokens per head, 16 heads)
+        lengths = [6144, 4096, 2048, 2048, 1024, 512, 256, 256]
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64, device=dev)
+        T = int(sum(lengths))
+        qv, kv, vv = (x.reshape(w.H, T, -1) for x in (qd, kd, vd))  # the same values, read as a packed batch
+        ov = torch.empty_like(vv)
+        wsv = torch.empty(max(ops.varlen_fwd_workspace_size(fm, len(lengths), w.H, T, w.dv, torch.bfloat16), 16),
+                          dtype=torch.uint8, device=dev)
+
+        def vl():
+            ops.varlen_fwd(fm, qv, kv, vv, cu, out=ov, workspace=wsv)
+
+        for _ in range(args.warmup):
+            vl()
+        ms = event_time_ms(vl, args.steps, stream)
+        flops = fwd_flops_per_token_head(w) * w.H * T
+        achieved = flops / (ms * 1e-3) / 1e12
+        also.append({"name": "varlen_h16_8seqs_16k_bf16", "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+                     "lengths": lengths,
+                     "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                                  "traffic": read_traffic("varlen_h16_8seqs_16k_bf16"),
                                   "algorithmic_flops_per_launch": flops}})
     if args.only in ("all", "backward"):
         dout = dev_bf16(ss.make_grads(w)[0])

@@ -122,14 +122,16 @@ struct Params {
   float* S_out;
   float* z_out;
   // Variable-length batches (vl_tab non-null): the packed token axis of each
-  // head holds sequences s at tokens cu[s] .. cu[s+1] (T tokens per head); work
-  // item g of a head is segment vl_tab[2g+1] of sequence vl_tab[2g] and owns
-  // state item g; work items g >= *vl_count exit at once.
+  // head holds sequences s at tokens cu[s] .. cu[s+1] (T tokens per head).
+  // Workgroup w takes work item g = w / n_heads of head w % n_heads (so the
+  // heads' items of one g run side by side): segment vl_tab[2g+1] of sequence
+  // vl_tab[2g], owning state item g of the head; items g >= *vl_count exit.
   const int* vl_tab;
   const int* vl_count;
   const int64_t* cu;
   int64_t T;
   int g_max;         // work items per head
+  int64_t n_heads;
 };
 
 // Where a workgroup's tokens lie: the packed row of its sequence's token 0,
@@ -157,8 +159,9 @@ __device__ __forceinline__ Geo geo_of(const Params& p, int per_head, int64_t seg
     g.item = g.head * items_per_head + g.seg;
     g.valid = true;
   } else {
-    g.head = w / p.g_max;
-    const int gi = (int)(w - g.head * p.g_max);
+    const int64_t nh = p.n_heads;
+    const int gi = (int)(w / nh);
+    g.head = w - (int64_t)gi * nh;
     g.valid = gi < *p.vl_count;
     const int sq = g.valid ? p.vl_tab[2 * gi] : 0;
     g.seg = g.valid ? p.vl_tab[2 * gi + 1] : 0;
@@ -1639,51 +1642,67 @@ hipError_t segment_prefix_t(const ChunkedArgs& a, float* ws, hipStream_t s) {
 // Variable-length batches (F = 256 configuration).
 namespace {
 
-// Work list (one workgroup): each sequence's segment count, their exclusive
-// prefix (the sequence's first work item) and the (sequence, segment) pair of
-// every work item.  Offsets that do not rise from 0 to T without decreasing
-// give no work items (and zero segments for every sequence).
+// Work list (one workgroup).  The whole segments of every sequence come
+// first (so they start together), then the sequences' shorter tails, which
+// fill the compute units the whole segments leave free.  Per sequence: its
+// first whole-segment item, the number of whole segments and the tail's item
+// (-1 if none); per item: (sequence, segment).  Offsets that do not rise from
+// 0 to T without decreasing give no work items.
 __global__ __launch_bounds__(256) void vl_setup_kernel(const int64_t* __restrict__ cu, int n_seqs, int64_t T,
                                                        int64_t seg_len, int g_max, int* __restrict__ tab,
-                                                       int* __restrict__ first, int* __restrict__ nseg,
-                                                       int* __restrict__ count) {
-  __shared__ int part[256];
-  __shared__ int bad;
+                                                       int* __restrict__ first, int* __restrict__ nfull,
+                                                       int* __restrict__ tail, int* __restrict__ count) {
+  __shared__ int pf[256], pt[256];
+  __shared__ int bad, n_full_all;
   const int tid = threadIdx.x;
   if (tid == 0) bad = (cu[0] != 0 || cu[n_seqs] != T) ? 1 : 0;
   __syncthreads();
   const int per = (n_seqs + 255) / 256;
   const int s0 = min(n_seqs, tid * per), s1 = min(n_seqs, s0 + per);
-  int local = 0;
+  int lf = 0, lt = 0;
   for (int sq = s0; sq < s1; ++sq) {
     const int64_t len = cu[sq + 1] - cu[sq];
     if (len < 0) atomicOr(&bad, 1);
-    local += (int)((max<int64_t>(len, 0) + seg_len - 1) / seg_len);
+    const int64_t l = max<int64_t>(len, 0);
+    lf += (int)(l / seg_len);
+    lt += (l % seg_len) != 0;
   }
-  part[tid] = local;
+  pf[tid] = lf;
+  pt[tid] = lt;
   __syncthreads();
   if (tid == 0) {
-    int run = 0;
+    int rf = 0, rt = 0;
     for (int t = 0; t < 256; ++t) {
-      const int v = part[t];
-      part[t] = run;
-      run += v;
+      const int a = pf[t], b = pt[t];
+      pf[t] = rf;
+      pt[t] = rt;
+      rf += a;
+      rt += b;
     }
-    if (run > g_max) bad = 1;
-    *count = bad ? 0 : run;
+    if (rf + rt > g_max) bad = 1;
+    n_full_all = rf;
+    *count = bad ? 0 : rf + rt;
   }
   __syncthreads();
   const bool ok = bad == 0;
-  int base = part[tid];
+  int bf = pf[tid], bt = n_full_all + pt[tid];
   for (int sq = s0; sq < s1; ++sq) {
-    const int ns = ok ? (int)((cu[sq + 1] - cu[sq] + seg_len - 1) / seg_len) : 0;
-    first[sq] = ok ? base : 0;
-    nseg[sq] = ns;
-    for (int j = 0; j < ns; ++j) {
-      tab[2 * (base + j)] = sq;
-      tab[2 * (base + j) + 1] = j;
+    const int64_t len = ok ? cu[sq + 1] - cu[sq] : 0;
+    const int nf = (int)(len / seg_len);
+    const bool has_tail = (len % seg_len) != 0;
+    first[sq] = bf;
+    nfull[sq] = nf;
+    tail[sq] = has_tail ? bt : -1;
+    for (int j = 0; j < nf; ++j) {
+      tab[2 * (bf + j)] = sq;
+      tab[2 * (bf + j) + 1] = j;
     }
-    base += ns;
+    if (has_tail) {
+      tab[2 * bt] = sq;
+      tab[2 * bt + 1] = nf;
+      ++bt;
+    }
+    bf += nf;
   }
 }
 
@@ -1698,7 +1717,7 @@ int64_t vl_seg_len(int64_t H, int64_t T) {
 int vl_g_max(int64_t T, int n_seqs, int64_t seg_len) { return (int)(T / seg_len + n_seqs); }
 
 struct VlWs {
-  int *tab, *first, *nseg, *count;
+  int *tab, *first, *nfull, *tail, *count;
   float* states;
   size_t bytes;
 };
@@ -1715,7 +1734,8 @@ VlWs vl_ws(const VarlenArgs& a, int g_max, void* base) {
   w.states = reinterpret_cast<float*>(take(sizeof(float) * (size_t)a.c.n_heads * g_max * CfgF256::F * CfgF256::DVP));
   w.tab = reinterpret_cast<int*>(take(sizeof(int) * 2 * (size_t)g_max));
   w.first = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
-  w.nseg = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
+  w.nfull = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
+  w.tail = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
   w.count = reinterpret_cast<int*>(take(sizeof(int)));
   w.bytes = off;
   return w;
@@ -1741,7 +1761,7 @@ hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s) {
   const int g_max = vl_g_max(T, a.n_seqs, seg_len);
   const VlWs w = vl_ws(a, g_max, a.c.ws);
   hipLaunchKernelGGL(vl_setup_kernel, dim3(1), dim3(256), 0, s, a.cu, a.n_seqs, T, seg_len, g_max, w.tab, w.first,
-                     w.nseg, w.count);
+                     w.nfull, w.tail, w.count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   Params p{};
@@ -1768,6 +1788,7 @@ hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s) {
   p.cu = a.cu;
   p.T = T;
   p.g_max = g_max;
+  p.n_heads = H;
   const unsigned grid = (unsigned)(H * g_max);
   if (T > 0) {  // every segment's state (the last ones too: their sums are the final states)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1777,8 +1798,8 @@ hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  e = launch_scan_varlen(w.states, H, a.n_seqs, g_max, w.first, w.nseg, K::F, K::DV, a.c.S0, a.c.z0, a.c.S_out,
-                         a.c.z_out, s);
+  e = launch_scan_varlen(w.states, H, a.n_seqs, g_max, w.first, w.nfull, w.tail, K::F, K::DV, a.c.S0, a.c.z0,
+                         a.c.S_out, a.c.z_out, s);
   if (e != hipSuccess || T == 0) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass2s_kernel<KS>), hipFuncAttributeMaxDynamicSharedMemorySize,
                           KS::kLdsS);

@@ -314,12 +314,14 @@ hipError_t launch_generic_nc_t(const ChunkedArgs& a, hipStream_t s) {
 }  // namespace
 
 // Variable-length batches: per (sequence s, head h) and state element, the
-// exclusive prefix over the sequence's segment items (first[s] .. +nseg[s]) of
-// head h, from S0 of (s, h); the total goes to S_out.  States are fragment
-// ordered (layout 1); S0/S_out are [n_seqs][H][F][dv].
+// exclusive prefix over the sequence's segment items in segment order (its
+// whole segments first[s] .. +nfull[s], then its tail item, if any) of head h,
+// from S0 of (s, h); the total goes to S_out.  States are fragment ordered
+// (layout 1); S0/S_out are [n_seqs][H][F][dv].
 __global__ __launch_bounds__(kGThreads) void vl_scan_kernel(float* states, int64_t H, int g_max, const int* first,
-                                                            const int* nseg, int F, int dv, const float* S0,
-                                                            const float* z0, float* S_out, float* z_out, int64_t E) {
+                                                            const int* nfull, const int* tail, int F, int dv,
+                                                            const float* S0, const float* z0, float* S_out,
+                                                            float* z_out, int64_t E) {
   const int64_t sh = blockIdx.y;  // s * H + h
   const int64_t h = sh % H, sq = sh / H;
   const int64_t idx = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
@@ -332,11 +334,13 @@ __global__ __launch_bounds__(kGThreads) void vl_scan_kernel(float* states, int64
   } else if (e == dv) {
     if (z0) run = z0[sh * F + f];
   }
-  const int n = nseg[sq];
-  float* st = states + (h * g_max + first[sq]) * E + idx;
-  for (int j = 0; j < n; ++j) {
-    const float d = st[(int64_t)j * E];
-    st[(int64_t)j * E] = run;
+  float* base = states + h * g_max * E + idx;
+  const int n = nfull[sq], t = tail[sq];
+  for (int j = 0; j <= n; ++j) {
+    const int64_t item = j < n ? first[sq] + j : t;
+    if (item < 0) break;  // no tail
+    const float d = base[item * E];
+    base[item * E] = run;
     run += d;
   }
   if (e < dv) {
@@ -360,13 +364,13 @@ hipError_t launch_chunk_state(const float* phik, const void* v, bool v_bf16, int
   return hipGetLastError();
 }
 
-hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, const int* first, const int* nseg,
-                              int F, int dv, const float* S0, const float* z0, float* S_out, float* z_out,
-                              hipStream_t s) {
+hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, const int* first, const int* nfull,
+                              const int* tail, int F, int dv, const float* S0, const float* z0, float* S_out,
+                              float* z_out, hipStream_t s) {
   const int64_t E = scan_state_elems(F, dv, 1);
   if (H == 0 || n_seqs == 0) return hipSuccess;
   hipLaunchKernelGGL(vl_scan_kernel, dim3((unsigned)((E + kGThreads - 1) / kGThreads), (unsigned)(H * n_seqs)),
-                     dim3(kGThreads), 0, s, states, H, g_max, first, nseg, F, dv, S0, z0, S_out, z_out, E);
+                     dim3(kGThreads), 0, s, states, H, g_max, first, nfull, tail, F, dv, S0, z0, S_out, z_out, E);
   return hipGetLastError();
 }
 

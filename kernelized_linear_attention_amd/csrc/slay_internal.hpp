@@ -86,9 +86,9 @@ struct ScanArgs {
 };
 int64_t scan_state_elems(int F, int dv, int layout);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
-hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, const int* first, const int* nseg,
-                              int F, int dv, const float* S0, const float* z0, float* S_out, float* z_out,
-                              hipStream_t s);
+hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, const int* first, const int* nfull,
+                              const int* tail, int F, int dv, const float* S0, const float* z0, float* S_out,
+                              float* z_out, hipStream_t s);
 
 // Variable-length batch of the causal forward: n_seqs sequences packed along
 // the token axis of each of H heads (q, k [H][T][d], v, o [H][T][dv]),
