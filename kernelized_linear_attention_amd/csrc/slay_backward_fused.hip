@@ -298,15 +298,26 @@ __device__ __forceinline__ int item_index(int fb, int eb, int g, int c16, int r)
   return ((fb * K::NE + eb) * 64 + (4 * g + r) + 16 * (c16 >> 2)) * 4 + (c16 & 3);
 }
 
+// bf16 copy of the state, [e][f] rows.  Lanes l, l^1 hold features f, f+1
+// of rows e..e+3: the even lane writes the (f, f+1) words of rows e, e+1, the
+// odd lane those of e+2, e+3 (one 4-byte store per row instead of two 2-byte
+// ones); v_perm takes bytes 0-3 from this lane's word, 4-7 from the neighbour's.
 template <class K>
 __device__ __forceinline__ void write_state_copy(const Lds& s, const f32x4 (&T)[K::NE][2], int wave, int g, int c16) {
+  const bool odd = c16 & 1;
+  const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;
+  const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;
 #pragma unroll
   for (int eb = 0; eb < K::NE; ++eb)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int fb = 2 * wave + j;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s.S[(eb * 16 + 4 * g + r) * K::LS + fb * 16 + c16] = f32_to_bf16(T[eb][j][r]);
+      const uint2 pk = pk4(T[eb][j]);
+      const uint32_t mine = odd ? pk.y : pk.x;
+      const uint32_t recv = swap_lane_pair(odd ? pk.x : pk.y);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(s.S + (eb * 16 + 4 * g + (odd ? 2 : 0)) * K::LS + fb * 16 + (c16 & ~1));
+      dst[0] = __builtin_amdgcn_perm(recv, mine, sel0);
+      dst[K::LS / 2] = __builtin_amdgcn_perm(recv, mine, sel1);
     }
 }
 
@@ -339,7 +350,6 @@ __global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
       for (int r = 0; r < 4; ++r) ST[eb][j][r] = item[item_index<K>(2 * wave + j, eb, g, c16, r)];
       UT[eb][j] = kZero4;
     }
-  write_state_copy<K>(s, ST, wave, g, c16);
 
   PrefQ pf;
   load_q<K>(p, h * p.L + t_begin, (int)min<int64_t>(K::C, t_end - t_begin), tid, pf);
@@ -347,6 +357,9 @@ __global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
     const int n = (int)min<int64_t>(K::C, t_end - t0);
     const int64_t row0 = h * p.L + t0;
     __syncthreads();
+    // the state before this chunk, as the bf16 copy [1] reads (written here, a
+    // phase after the update, so the update's MFMAs are done by now)
+    write_state_copy<K>(s, ST, wave, g, c16);
     store_q<K>(s, pf, n, tid);
     const uint4 dcur = pf.dout;
     if (t0 + K::C < t_end) load_q<K>(p, row0 + K::C, (int)min<int64_t>(K::C, t_end - t0 - K::C), tid, pf);
@@ -463,7 +476,6 @@ __global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
         ST[eb][j] = mfma_bf16(vt, ld8(s.KT + (fb * 16 + c16) * K::LT + 8 * g), ST[eb][j]);
       }
     }
-    write_state_copy<K>(s, ST, wave, g, c16);
     __syncthreads();
     // [5] dphi(Q)^T += phi(K)^T D^T; write dphi(Q)
 #pragma unroll
@@ -507,7 +519,6 @@ __global__ __launch_bounds__(K::NT) void bwd_kv_kernel(BwdParams p) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) UT[eb][j][r] = item[item_index<K>(2 * wave + j, eb, g, c16, r)];
-  write_state_copy<K>(s, UT, wave, g, c16);
 
   const int n_steps = (int)((t_end - t_begin + K::C - 1) / K::C);
   auto rows_of = [&](int cs) { return (int)min<int64_t>(K::C, t_end - (t_begin + (int64_t)cs * K::C)); };
@@ -518,6 +529,7 @@ __global__ __launch_bounds__(K::NT) void bwd_kv_kernel(BwdParams p) {
     const int n = rows_of(cs);
     const int64_t row0 = h * p.L + t0;
     __syncthreads();
+    write_state_copy<K>(s, UT, wave, g, c16);  // U after this chunk, as the bf16 copy [1] reads
     store_kv<K>(s, pf, n, tid);
     if (cs > 0) load_kv<K>(p, row0 - K::C, K::C, tid, pf);
     __syncthreads();
@@ -600,7 +612,6 @@ __global__ __launch_bounds__(K::NT) void bwd_kv_kernel(BwdParams p) {
       for (int j = 0; j < 2; ++j)
         UT[eb][j] = mfma_bf16(gt, ld8(s.QT + ((2 * wave + j) * 16 + c16) * K::LT + 8 * g), UT[eb][j]);
     }
-    write_state_copy<K>(s, UT, wave, g, c16);
   }
 }
 
