@@ -97,19 +97,29 @@ def read_traffic(kind: str):
 
 
 TRAFFIC_UNITS = {
-    # summary name: (kernel-name fragments counted once per launch of the unit, description)
-    "fused_fwd_h16_l16k_bf16": (("pass1", "scan_kernel", "pass2"),
+    # summary name: (bench --only part, kernel-name fragments with their dispatches per launch of the unit,
+    # description); the counters of each unit come from runs of that part alone
+    "fused_fwd_h16_l16k_bf16": ("fwd", (("pass1s", 1), ("scan_kernel", 1), ("pass2s", 1)),
                                 "one causal forward, B1 H16 L16384 bf16 (segment states + scan + main pass)"),
-    "featmap_h16_l16k_bf16": (("featmap_kernel<unsigned short, unsigned short",),
+    "featmap_h16_l16k_bf16": ("featmap", (("featmap_kernel<unsigned short, unsigned short", 1),),
                               "one feature-map launch over 262144 bf16 rows, F = 256"),
-    "decode_256x16_f32": (("featmap_kernel<float, float", "stream_kernel"),
+    "noncausal_h16_l16k_bf16": ("noncausal", (("pass1s", 1), ("scan_kernel", 1), ("ncout_kernel", 1)),
+                                "one non-causal forward, B1 H16 Lq = Lk = 16384 bf16"),
+    "varlen_h16_8seqs_16k_bf16": ("varlen", (("vl_setup", 1), ("pass1s", 1), ("vl_scan", 1), ("pass2s", 1)),
+                                  "one variable-length forward, 16 heads x 8 sequences (16384 tokens) bf16"),
+    "backward_h16_l16k_bf16": ("backward", (("featmap_kernel<unsigned short, unsigned short", 1), ("pass1s", 1),
+                                            ("scan_kernel", 2), ("bwd_q_kernel", 1), ("bwd_kv_kernel", 1),
+                                            ("vjp_kernel", 1)),
+                               "one causal backward, B1 H16 L16384 bf16"),
+    "decode_256x16_f32": ("decode", (("featmap_kernel<float, float", 1), ("stream_kernel", 1)),
                           "one decode step for 4096 heads (q/k feature map + state stream)"),
 }
 CALIB_KERNEL = "copyBuffer"  # the device-to-device copy of --calib-copy-mib MiB
 
 
-def traffic_summary(fetch_dir: str, write_dir: str, calib_mib: int, command: str) -> None:
-    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_*.txt."""
+def traffic_summary(fetch_dir: str, write_dir: str, calib_mib: int, command: str, part: str) -> None:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of `bench.py --only part` into
+    profiles/traffic_*.txt for the units of that part."""
     import collections
     import csv
     import glob
@@ -138,20 +148,24 @@ def traffic_summary(fetch_dir: str, write_dir: str, calib_mib: int, command: str
 
     f_scale = calib_kib / pick(fetch, CALIB_KERNEL)
     w_scale = calib_kib / pick(write, CALIB_KERNEL)
-    for name, (frags, desc) in TRAFFIC_UNITS.items():
-        f_kib = sum(pick(fetch, fr) or 0.0 for fr in frags)
-        w_kib = sum(pick(write, fr) or 0.0 for fr in frags)
+    for name, (unit_part, frags, desc) in TRAFFIC_UNITS.items():
+        if unit_part != part:
+            continue
+        f_kib = sum((pick(fetch, fr) or 0.0) * k for fr, k in frags)
+        w_kib = sum((pick(write, fr) or 0.0) * k for fr, k in frags)
         total = (f_kib * f_scale + w_kib * w_scale) * 1024.0
         lines = [f"# HBM traffic per launch: {name}", "", f"unit: {desc}", "",
                  "commands (from the repository root on the GPU box):", "",
                  f"    {command.replace('COUNTER', 'FETCH_SIZE')}",
                  f"    {command.replace('COUNTER', 'WRITE_SIZE')}",
-                 f"    python bench.py --traffic-summary <FETCH_SIZE dir> <WRITE_SIZE dir> --calib-copy-mib {calib_mib}", "",
+                 f"    python bench.py --only {part} --traffic-summary <FETCH_SIZE dir> <WRITE_SIZE dir> "
+                 f"--calib-copy-mib {calib_mib}", "",
                  f"calibration: a {calib_mib} MiB device copy reads FETCH_SIZE x{1 / f_scale:.3f} and WRITE_SIZE "
                  f"x{1 / w_scale:.3f} of its bytes; factors {f_scale:.3f} and {w_scale:.3f}", "",
-                 "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch |", "|---|---|---|"]
-        for fr in frags:
-            lines.append(f"| {fr} | {pick(fetch, fr) or 0.0:.0f} | {pick(write, fr) or 0.0:.0f} |")
+                 "| kernel | dispatches per launch | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch |",
+                 "|---|---|---|---|"]
+        for fr, k in frags:
+            lines.append(f"| {fr} | {k} | {pick(fetch, fr) or 0.0:.0f} | {pick(write, fr) or 0.0:.0f} |")
         lines += ["", f"hbm_bytes_per_launch: {total:.6e}", f"sources_sha256_16: {sources_digest()}"]
         with open(os.path.join(ROOT, "profiles", f"traffic_{name}.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
@@ -201,11 +215,11 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_*.txt from two rocprofv3 --pmc runs and exit (no GPU)")
     ap.add_argument("--traffic-command", default="rocprofv3 --pmc COUNTER --output-format csv -d <dir> -o run -- "
-                    "python3 bench.py --steps 5 --warmup 1 --decode-steps 32 --no-cpu --calib-copy-mib 512")
+                    "python3 bench.py --only PART --steps 5 --warmup 1 --decode-steps 32 --no-cpu --calib-copy-mib 512")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.calib_copy_mib or 512,
-                        args.traffic_command)
+                        args.traffic_command.replace("PART", args.only), args.only)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))

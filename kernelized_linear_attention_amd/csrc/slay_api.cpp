@@ -8,6 +8,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <set>
+#include <utility>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -575,3 +578,20 @@ const char* slay_last_error(void) { return g_last_error.c_str(); }
 int32_t slay_version(void) { return 100; }
 
 }  // extern "C"
+
+namespace slay {
+
+hipError_t set_max_lds(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({kernel, dev});
+  return e;
+}
+
+}  // namespace slay

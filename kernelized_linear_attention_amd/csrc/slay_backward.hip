@@ -345,8 +345,7 @@ hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
 
   const size_t lds = bwd_lds_bytes(a);
   const dim3 grid((unsigned)n_chunks, (unsigned)a.n_heads);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_q_kernel<TV>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds);
+  e = set_max_lds(reinterpret_cast<const void*>(&bwd_q_kernel<TV>), (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_q_kernel<TV>, grid, dim3(kBThreads), lds, s, w.phiq, w.phik, static_cast<const TV*>(a.v),
                      static_cast<const TV*>(a.dout), a.L, a.F, a.dv, a.chunk, n_chunks, w.states, w.gh, w.dphiq);
@@ -369,8 +368,7 @@ hipError_t launch_backward_t(const BackwardArgs& a, hipStream_t s) {
   e = launch_scan(ra, s);
   if (e != hipSuccess) return e;
 
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv_kernel<TV>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  e = set_max_lds(reinterpret_cast<const void*>(&bwd_kv_kernel<TV>), (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_kv_kernel<TV>, grid, dim3(kBThreads), lds, s, w.phiq, w.phik, static_cast<const TV*>(a.v),
                      a.L, a.F, a.dv, a.chunk, n_chunks, w.states, w.gh, w.dphik, static_cast<TV*>(a.dv_out));

@@ -928,8 +928,7 @@ hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   p.dphik = w.dphik;
   p.dv = static_cast<uint16_t*>(a.dv_out);
   const dim3 grid((unsigned)(a.n_heads * n_seg));
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_q_kernel<K256>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          K256::kLds);
+  e = set_max_lds(reinterpret_cast<const void*>(&bwd_q_kernel<K256>), K256::kLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_q_kernel<K256>, grid, dim3(K256::NT), K256::kLds, s, p);
   e = hipGetLastError();
@@ -951,8 +950,7 @@ hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   e = launch_scan(ra, s);
   if (e != hipSuccess) return e;
 
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_kv_kernel<K256>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, K256::kLds);
+  e = set_max_lds(reinterpret_cast<const void*>(&bwd_kv_kernel<K256>), K256::kLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_kv_kernel<K256>, grid, dim3(K256::NT), K256::kLds, s, p);
   e = hipGetLastError();
@@ -973,8 +971,7 @@ hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   vp.prf = static_cast<const uint16_t*>(a.prf);
   vp.draw_set_stride = a.draw_set_stride;
   vp.nc = a.nc;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&vjp_kernel<V256>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          V256::kLds);
+  e = set_max_lds(reinterpret_cast<const void*>(&vjp_kernel<V256>), V256::kLds);
   if (e != hipSuccess) return e;
   const int64_t n_tiles = (vp.n_rows + V256::RT - 1) / V256::RT;
   const unsigned gx = (unsigned)(n_tiles < 128 ? n_tiles : 128);  // one workgroup per CU over both sides

@@ -1438,15 +1438,13 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
   hipError_t e;
   if (n_seg > 1) {
     if constexpr (K::STAGERS1) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K>), K::kLds1);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * (n_seg - 1) * kSub)), dim3(K::NT + 256),
                          K::kLds1, s, p);
     } else {
       constexpr int FS = K::FS1;
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K, FS>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1_kernel<K, FS>), K::kLds1);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((pass1_kernel<K, FS>), dim3((unsigned)(a.n_heads * (n_seg - 1) * kSub * FS)),
                          dim3(K::NT / FS), K::kLds1, s, p);
@@ -1470,13 +1468,11 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
   }
   using KS = typename MainPass<K>::type;
   if constexpr (!std::is_void_v<KS>) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass2s_kernel<KS>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, KS::kLdsS);
+    e = set_max_lds(reinterpret_cast<const void*>(&pass2s_kernel<KS>), KS::kLdsS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pass2s_kernel<KS>, dim3((unsigned)(a.n_heads * n_seg)), dim3(KS::NTW), KS::kLdsS, s, p);
   } else {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass2_kernel<K>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds);
+    e = set_max_lds(reinterpret_cast<const void*>(&pass2_kernel<K>), K::kLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pass2_kernel<K>, dim3((unsigned)(a.n_heads * n_seg)), dim3(K::NT), K::kLds, s, p);
   }
@@ -1542,14 +1538,12 @@ hipError_t launch_nc_t(const ChunkedArgs& a, hipStream_t s) {
     p.p1_segs = n_seg * kSub;
     p.p1_items = p.p1_segs + 1;
     if constexpr (K::STAGERS1) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K>), K::kLds1);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT + 256), K::kLds1, s,
                          p);
     } else {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K, 1>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1_kernel<K, 1>), K::kLds1);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((pass1_kernel<K, 1>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT), K::kLds1, s, p);
     }
@@ -1575,8 +1569,7 @@ hipError_t launch_nc_t(const ChunkedArgs& a, hipStream_t s) {
   p.qseg_len = seg_len_for<K>(a.n_heads, a.Lq);
   constexpr int lds = ncout_lds<K>();
   static_assert(lds <= 160 * 1024, "LDS budget");
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ncout_kernel<K>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          lds);
+  e = set_max_lds(reinterpret_cast<const void*>(&ncout_kernel<K>), lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ncout_kernel<K>, dim3((unsigned)(a.n_heads * p.n_qseg)), dim3(K::NT), lds, s, p);
   return hipGetLastError();
@@ -1609,14 +1602,12 @@ hipError_t segment_prefix_t(const ChunkedArgs& a, float* ws, hipStream_t s) {
   hipError_t e;
   if (n_seg > 1) {
     if constexpr (K::STAGERS1) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K>), K::kLds1);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT + 256), K::kLds1, s,
                          p);
     } else {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1_kernel<K, 1>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1_kernel<K, 1>), K::kLds1);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((pass1_kernel<K, 1>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT), K::kLds1, s, p);
     }
@@ -1667,22 +1658,41 @@ __global__ __launch_bounds__(256) void vl_setup_kernel(const int64_t* __restrict
     lf += (int)(l / seg_len);
     lt += (l % seg_len) != 0;
   }
-  pf[tid] = lf;
-  pt[tid] = lt;
-  __syncthreads();
-  if (tid == 0) {
-    int rf = 0, rt = 0;
-    for (int t = 0; t < 256; ++t) {
-      const int a = pf[t], b = pt[t];
-      pf[t] = rf;
-      pt[t] = rt;
-      rf += a;
-      rt += b;
+  // exclusive prefix of the per-thread counts: inclusive scan within each wave
+  // (shuffles), then the four wave totals
+  int sf = lf, st = lt;
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int uf = __shfl_up(sf, o, 64), ut = __shfl_up(st, o, 64);
+    if (lane >= o) {
+      sf += uf;
+      st += ut;
     }
+  }
+  if (lane == 63) {
+    pf[wv] = sf;
+    pt[wv] = st;
+  }
+  __syncthreads();
+  int bf0 = 0, bt0 = 0, rf = 0, rt = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wv) {
+      bf0 += pf[w];
+      bt0 += pt[w];
+    }
+    rf += pf[w];
+    rt += pt[w];
+  }
+  __syncthreads();  // every wave has read the wave totals
+  if (tid == 0) {
     if (rf + rt > g_max) bad = 1;
     n_full_all = rf;
     *count = bad ? 0 : rf + rt;
   }
+  pf[tid] = bf0 + sf - lf;  // exclusive prefix of this thread
+  pt[tid] = bt0 + st - lt;
   __syncthreads();
   const bool ok = bad == 0;
   int bf = pf[tid], bt = n_full_all + pt[tid];
@@ -1791,8 +1801,7 @@ hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s) {
   p.n_heads = H;
   const unsigned grid = (unsigned)(H * g_max);
   if (T > 0) {  // every segment's state (the last ones too: their sums are the final states)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass1s_kernel<K>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            K::kLds1);
+    e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K>), K::kLds1);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((pass1s_kernel<K>), dim3(grid), dim3(K::NT + 256), K::kLds1, s, p);
     e = hipGetLastError();
@@ -1801,8 +1810,7 @@ hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s) {
   e = launch_scan_varlen(w.states, H, a.n_seqs, g_max, w.first, w.nfull, w.tail, K::F, K::DV, a.c.S0, a.c.z0,
                          a.c.S_out, a.c.z_out, s);
   if (e != hipSuccess || T == 0) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pass2s_kernel<KS>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          KS::kLdsS);
+  e = set_max_lds(reinterpret_cast<const void*>(&pass2s_kernel<KS>), KS::kLdsS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pass2s_kernel<KS>, dim3(grid), dim3(KS::NTW), KS::kLdsS, s, p);
   return hipGetLastError();

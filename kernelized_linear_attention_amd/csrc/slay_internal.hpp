@@ -9,6 +9,11 @@
 
 namespace slay {
 
+// Raise a kernel's dynamic-LDS limit once per (kernel, device): the setting
+// persists on the device, so later launches make no call besides the launch
+// itself (they may be under stream capture).
+hipError_t set_max_lds(const void* kernel, int bytes);
+
 struct FeatmapArgs {
   const void* x;          // [n_heads * rows_per_head][d]
   const void* x2;         // nullable: a second input of the same shape (phi2 <- phi(x2)), same launch
