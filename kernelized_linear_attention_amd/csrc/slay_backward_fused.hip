@@ -739,11 +739,16 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
     for (int rb = 0; rb < K::NRB; ++rb) {
       const bf16x8 xb0 = ld8(sX + (rb * 16 + c16) * K::LX + 8 * g);
       const bf16x8 xb1 = ld8(sX + (rb * 16 + c16) * K::LX + 32 + 8 * g);
+      // |x|^2 with the bf16 dot instruction (products of bf16 values are exact in fp32)
       float ss = 0.f;
+      {
+        const uint4 u0 = __builtin_bit_cast(uint4, xb0), u1 = __builtin_bit_cast(uint4, xb1);
+        const uint32_t wds[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float u = (float)xb0[t], w = (float)xb1[t];
-        ss = fmaf(u, u, fmaf(w, w, ss));
+        for (int t = 0; t < 8; ++t) {
+          const bf16x2 h2 = __builtin_bit_cast(bf16x2, wds[t]);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, ss, false);
+        }
       }
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
