@@ -31,8 +31,9 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 WORKLOAD = "h16_l16k_bf16"
 DECODE = "decode_256x16_f32"
-KERNEL_SOURCES = ("slay_chunked_fused.hip", "slay_chunked_generic.hip", "slay_featmap.hip", "slay_decode.hip",
-                  "slay_backward.hip", "slay_backward_fused.hip", "slay_device.hpp")
+LONG = "h8_l128k_d128_bf16"
+KERNEL_SOURCES = ("slay_chunked_fused.hip", "slay_chunked_generic.hip", "slay_chunked_wide.hip", "slay_featmap.hip",
+                  "slay_decode.hip", "slay_backward.hip", "slay_backward_fused.hip", "slay_device.hpp")
 
 
 def fwd_flops_per_token_head(w) -> int:
@@ -111,6 +112,9 @@ TRAFFIC_UNITS = {
                                             ("scan_kernel", 2), ("bwd_q_kernel", 1), ("bwd_kv_kernel", 1),
                                             ("vjp_kernel", 1)),
                                "one causal backward, B1 H16 L16384 bf16"),
+    "long_h8_l128k_d128_bf16": ("long", (("featmap_kernel<unsigned short, unsigned short", 1), ("wstate", 1),
+                                         ("scan_kernel", 1), ("wout", 1)),
+                                "one causal forward, B1 H8 L131072 d=dv=128 F=512 bf16 (wide path)"),
     "decode_256x16_f32": ("decode", (("featmap_kernel<float, float", 1), ("stream_kernel", 1)),
                           "one decode step for 4096 heads (q/k feature map + state stream)"),
 }
@@ -208,7 +212,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per head of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["all", "fwd", "featmap", "noncausal", "varlen", "backward", "decode"],
+    ap.add_argument("--only", choices=["all", "fwd", "featmap", "noncausal", "varlen", "backward", "long", "decode"],
                     default="all")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (scale for HBM byte counters)")
@@ -366,6 +370,33 @@ def main():
                                   "traffic": read_traffic("backward_h16_l16k_bf16"),
                                   "algorithmic_flops_per_launch": flops}})
         del wsb
+    if args.only in ("all", "long"):
+        # B1 H8 L131072, d = dv = 128, F = 512: feature maps in HBM, state on chip
+        wl = ss.WORKLOADS[LONG]
+        ql, kl, vl_ = ss.make_qkv(wl)
+        Al, Gl = ss.make_draws(wl)
+        fml = ops.FeatureMap(dev_bf16(Al), dev_bf16(Gl), wl.R, wl.m, wl.eps)
+        qld, kld, vld = dev_bf16(ql), dev_bf16(kl), dev_bf16(vl_)
+        del ql, kl, vl_
+        oll = torch.empty_like(vld)
+        wsl = torch.empty(max(ops.chunked_fwd_workspace_size(fml, wl.B, wl.H, wl.L, wl.dv, wl.chunk, torch.bfloat16),
+                              16), dtype=torch.uint8, device=dev)
+
+        def lfwd():
+            ops.chunked_fwd(fml, qld, kld, vld, wl.chunk, out=oll, workspace=wsl)
+
+        for _ in range(max(1, args.warmup // 2)):
+            lfwd()
+        ms = event_time_ms(lfwd, max(1, args.steps // 2), stream)
+        flops = fwd_flops_per_token_head(wl) * wl.B * wl.H * wl.L
+        achieved = flops / (ms * 1e-3) / 1e12
+        also.append({"name": "long_h8_l128k_d128_bf16", "ms_per_step": ms,
+                     "tokens_per_s": wl.B * wl.L / (ms * 1e-3),
+                     "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                                  "traffic": read_traffic("long_h8_l128k_d128_bf16"),
+                                  "algorithmic_flops_per_launch": flops}})
+        del qld, kld, vld, oll, wsl
     if args.only in ("all", "decode"):
         wd = ss.WORKLOADS[DECODE]
         nh = wd.n_heads

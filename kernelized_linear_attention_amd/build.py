@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libslay.so")
-SOURCES = ["slay_api.cpp", "slay_featmap.hip", "slay_chunked_generic.hip", "slay_chunked_fused.hip",
+SOURCES = ["slay_api.cpp", "slay_featmap.hip", "slay_chunked_generic.hip", "slay_chunked_fused.hip", "slay_chunked_wide.hip",
            "slay_decode.hip", "slay_backward.hip", "slay_backward_fused.hip"]
 ARCH = os.environ.get("SLAY_OFFLOAD_ARCH", "gfx950")
 

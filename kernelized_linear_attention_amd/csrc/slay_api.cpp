@@ -250,6 +250,7 @@ size_t slay_attn_chunked_fwd_workspace_size(const slay_params_t* params, int32_t
   slay::ChunkedArgs a = chunked_args(params, nullptr, nullptr, nullptr, io_dtype, B, H, L, dv, chunk);
   if (a.n_heads == 0 || L == 0) return 0;
   if (slay::fused_supported(a)) return slay::fused_workspace_bytes(a);
+  if (slay::wide_supported(a)) return slay::wide_workspace_bytes(a);
   return slay::generic_workspace_bytes(a);
 }
 
@@ -286,16 +287,23 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
   a.z_out = z_out;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
-  const bool fused = slay::fused_supported(a);
-  if (!fused && !slay::generic_supported(a))
+  // kernel family: fused (feature map on chip), wide (feature maps in HBM,
+  // state on chip), generic (plain FMA, any accepted shape and dtype)
+  const int path = slay::fused_supported(a) ? 0 : (slay::wide_supported(a) ? 1 : 2);
+  if (path == 2 && !slay::generic_supported(a))
     return fail(SLAY_E_UNSUPPORTED, "shape not supported (d=%d dv=%d F=%d chunk=%d)", params->d, dv, F, chunk);
-  const size_t need = (!tokens) ? 0 : (fused ? slay::fused_workspace_bytes(a) : slay::generic_workspace_bytes(a));
+  const size_t need = (!tokens) ? 0
+                      : path == 0 ? slay::fused_workspace_bytes(a)
+                      : path == 1 ? slay::wide_workspace_bytes(a)
+                                  : slay::generic_workspace_bytes(a);
   if (workspace_bytes < need) return fail(SLAY_E_INVALID, "workspace too small: %zu < %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(SLAY_E_INVALID, "workspace is NULL");
   if (need > 0 && !aligned16(workspace)) return fail(SLAY_E_INVALID, "workspace must be 16-byte aligned");
   if (nh == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return device_status(fused ? slay::launch_fused(a, s) : slay::launch_generic(a, s), "slay_attn_chunked_fwd launch");
+  const hipError_t e = path == 0 ? slay::launch_fused(a, s) : path == 1 ? slay::launch_wide(a, s)
+                                                                        : slay::launch_generic(a, s);
+  return device_status(e, "slay_attn_chunked_fwd launch");
 }
 
 }  // extern "C"

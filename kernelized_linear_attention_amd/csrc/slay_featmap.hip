@@ -56,7 +56,7 @@ template <typename TI, typename TO, int D, int FBW, int TR>
 __global__ __launch_bounds__(kThreads) void featmap_kernel(
     const TI* __restrict__ x_a, const TI* __restrict__ x_b, int64_t rows_per_head, int64_t n_heads,
     const TI* __restrict__ anchors, const TI* __restrict__ prf, int64_t draw_set_stride, int n_draw_sets, int F,
-    int m, NodeConsts nc, TO* __restrict__ phi_a, TO* __restrict__ phi_b) {
+    int m, NodeConsts nc, TO* __restrict__ phi_a, TO* __restrict__ phi_b, int gx) {
   // blockIdx.z selects the input: z = 1 maps the second input in the same launch
   const TI* __restrict__ x = blockIdx.z ? x_b : x_a;
   TO* __restrict__ phi = blockIdx.z ? phi_b : phi_a;
@@ -79,7 +79,15 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
   const int g = lane >> 4;
   const int col = lane & 15;
   const int n_fblk = F / 16;
-  const int fblk0 = blockIdx.y * (4 * FBW) + wave * FBW;
+  // Workgroup id -> (row-tile walker bx, feature slice by): the gy slices of
+  // the same walker get ids that are equal modulo 8, so they run on one XCD
+  // and start together, and the later slices read each x tile from that
+  // XCD's L2 rather than from HBM.
+  const int gy = (F + FWS - 1) / FWS;
+  const int grp = (int)blockIdx.x / (8 * gy), rem = (int)blockIdx.x - grp * 8 * gy;
+  const int by = rem >> 3, bx = grp * 8 + (rem & 7);
+  if (bx >= gx) return;
+  const int fblk0 = by * (4 * FBW) + wave * FBW;
 
   const int tiles_per_head = (int)((rows_per_head + TR - 1) / TR);
   const int n_tiles = tiles_per_head * (int)n_heads;
@@ -106,9 +114,9 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
       if (r < nr) xr[i] = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + c);
     }
   };
-  if ((int)blockIdx.x < n_tiles) load_tile(blockIdx.x);
+  if (bx < n_tiles) load_tile(bx);
 
-  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+  for (int t = bx; t < n_tiles; t += gx) {
     const int h = t / tiles_per_head;
     const int64_t row0 = (int64_t)(t - h * tiles_per_head) * TR;  // row within head
     const int64_t nrow = min<int64_t>(TR, rows_per_head - row0);
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
       slg[threadIdx.x / TPR] = 2.0f * __builtin_amdgcn_logf(inv);  // log2(inv^2)
     }
     __syncthreads();
-    if (t + (int)gridDim.x < n_tiles) load_tile(t + gridDim.x);
+    if (t + gx < n_tiles) load_tile(t + gx);
 
 #pragma unroll
     for (int tb = 0; tb < TR / 16; ++tb) {
@@ -216,13 +224,13 @@ __global__ __launch_bounds__(kThreads) void featmap_kernel(
     // coalesced write-out of the tile's feature slice: 16-byte pieces of each row
     {
       constexpr int PPR = FWS * (int)sizeof(TO) / 16;  // 16-byte pieces per row of the slice
-      const int fcols = min(FWS, F - (int)blockIdx.y * FWS);
+      const int fcols = min(FWS, F - by * FWS);
       const int ppr = fcols * (int)sizeof(TO) / 16;
       for (int pc = threadIdx.x; pc < TR * PPR; pc += kThreads) {
         const int rr = pc / PPR, q = pc - (pc / PPR) * PPR;
         if (rr < nrow && q < ppr) {
           const u32x4 val = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(so + rr * LDO) + q * 16);
-          u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(pt + (int64_t)rr * F + blockIdx.y * FWS) + q * 16);
+          u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(pt + (int64_t)rr * F + by * FWS) + q * 16);
           // Large launches write phi once and never read it back here, so
           // they stream it with non-temporal stores; small ones (a decode
           // step's phi(q)) are read by the next kernel and stay cached.
@@ -247,10 +255,11 @@ hipError_t launch_t(const FeatmapArgs& a, hipStream_t s) {
   if (gx > tiles) gx = tiles;
   if (tiles == 0) return hipSuccess;
   const int gz = a.x2 ? 2 : 1;
-  hipLaunchKernelGGL((featmap_kernel<TI, TO, D, FBW, TR>), dim3((unsigned)gx, gy, gz), dim3(kThreads), 0, s,
+  const unsigned n_groups = (unsigned)((gx + 7) / 8);  // walkers in groups of 8, one id per (walker, slice)
+  hipLaunchKernelGGL((featmap_kernel<TI, TO, D, FBW, TR>), dim3(n_groups * 8 * gy, 1, gz), dim3(kThreads), 0, s,
                      static_cast<const TI*>(a.x), static_cast<const TI*>(a.x2), a.rows_per_head, a.n_heads,
                      static_cast<const TI*>(a.anchors), static_cast<const TI*>(a.prf), a.draw_set_stride,
-                     a.n_draw_sets, a.F, a.m, a.nc, static_cast<TO*>(a.phi), static_cast<TO*>(a.phi2));
+                     a.n_draw_sets, a.F, a.m, a.nc, static_cast<TO*>(a.phi), static_cast<TO*>(a.phi2), (int)gx);
   return hipGetLastError();
 }
 

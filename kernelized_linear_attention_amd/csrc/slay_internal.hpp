@@ -69,6 +69,12 @@ hipError_t launch_fused(const ChunkedArgs& a, hipStream_t s);
 int fused_segment_count(const ChunkedArgs& a, int64_t* seg_len);
 hipError_t launch_segment_prefix(const ChunkedArgs& a, float* ws, hipStream_t s);
 
+// Wide MFMA path (bf16, causal, F in {128, 256, 384, 512}, dv in {64, 128}):
+// feature maps materialised in bf16, the state kept on chip per segment.
+bool wide_supported(const ChunkedArgs& a);
+size_t wide_workspace_bytes(const ChunkedArgs& a);
+hipError_t launch_wide(const ChunkedArgs& a, hipStream_t s);
+
 // Generic path (any supported dtype/shape; unfused, plain FMA).
 bool generic_supported(const ChunkedArgs& a);
 size_t generic_workspace_bytes(const ChunkedArgs& a);

@@ -98,7 +98,8 @@ def _run_fwd(lib, w, q, k, v, A, G, chunk=None, S0=None, z0=None, state=False):
     ("tiny_f32", 97, 128),       # one partial chunk
     ("b4h8_l2k_bf16", 2048, 64),  # fused MFMA path, F = 96
     ("h16_l16k_bf16", 1000, 64),  # fused MFMA path, F = 256, ragged tail, 1 segment per head
-    ("h16_l16k_bf16", 1000, 32),  # general path in bf16
+    ("h16_l16k_bf16", 1000, 32),  # wide MFMA path (feature maps in HBM), F = 256
+    ("b4h8_l2k_bf16", 500, 32),   # general path in bf16 (F = 96 has no wide variant)
 ])
 def test_chunked_parity(lib, orc, name, L, chunk):
     w = ss.WORKLOADS[name].with_(L=L, chunk=chunk)
@@ -118,6 +119,43 @@ def test_chunked_parity(lib, orc, name, L, chunk):
     assert rownorm_rel(S.reshape(-1, w.dv), rS.reshape(-1, w.dv)) < TOL[w.dtype]
     assert np.max(np.abs(z - rz) / rz) < TOL[w.dtype]
     np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], rtol=TOL[w.dtype], atol=TOL[w.dtype])  # o_1 = v_1
+
+
+@pytest.mark.parametrize("d,dv,R,m,H,L", [
+    (128, 128, 4, 128, 2, 1000),  # the long-sequence shape's head geometry; 32 segments, ragged tail
+    (64, 128, 3, 128, 2, 333),    # F = 384
+    (128, 64, 2, 64, 3, 77),      # F = 128, dv = 64 (four feature slices per column group)
+    (32, 64, 4, 128, 1, 513),     # d = 32, F = 512, dv = 64
+    (128, 128, 4, 128, 1, 20),    # one segment, one partial chunk
+])
+def test_wide_parity(lib, orc, d, dv, R, m, H, L):
+    """The wide MFMA path (feature maps written once in bf16, state kept on chip per segment)."""
+    w = ss.WORKLOADS["h8_l128k_d128_bf16"].with_(H=H, L=L, d=d, dv=dv, R=R, m=m)
+    _say(f"wide parity d={d} dv={dv} F={w.F} H={H} L={L}")
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    o, S, z = _run_fwd(lib, w, q, k, v, A, G, state=True)
+    ro, rS, rz = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m, form="recurrent")
+    err = rownorm_rel(o, ro)
+    s_err = rownorm_rel(S.reshape(-1, w.dv), rS.reshape(-1, w.dv))
+    z_err = float(np.max(np.abs(z - rz) / rz))
+    _say(f"  o rownorm rel err {err:.3e}; S {s_err:.3e} z {z_err:.3e}")
+    assert err < TOL["bf16"] and s_err < TOL["bf16"] and z_err < TOL["bf16"]
+    np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], rtol=TOL["bf16"], atol=TOL["bf16"])  # o_1 = v_1
+
+
+def test_wide_initial_state_and_handoff(lib, orc):
+    """Wide path: [0, L1) then [L1, L) with the state carried equals one pass."""
+    w = ss.WORKLOADS["h8_l128k_d128_bf16"].with_(H=2, L=900)
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    cut = 416
+    o1, S1, z1 = _run_fwd(lib, w, q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], A, G, state=True)
+    o2, S2, z2 = _run_fwd(lib, w, q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], A, G, S0=S1, z0=z1, state=True)
+    ro, rS, rz = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m, form="recurrent")
+    assert rownorm_rel(np.concatenate([o1, o2], axis=2), ro) < TOL["bf16"]
+    assert rownorm_rel(S2.reshape(-1, w.dv), rS.reshape(-1, w.dv)) < TOL["bf16"]
+    assert np.max(np.abs(z2 - rz) / rz) < TOL["bf16"]
 
 
 def test_chunked_initial_state_and_handoff(lib, orc):
