@@ -107,8 +107,15 @@ size_t slay_attn_chunked_fwd_workspace_size(const slay_params_t* params, int32_t
  *                slay_attn_chunked_fwd_workspace_size(...) bytes (NULL if 0).
  * L need not be a multiple of chunk (the tail chunk is masked); L = 0 only
  * copies S0/z0 to S_out/z_out.  chunk in [1, 128].
- * bf16 with d = dv = 64, chunk = 64 and R*m in {64, 96, 128, 256} runs the
- * fused MFMA kernels; every other accepted shape runs the general kernels. */
+ * Kernel families, chosen from the shape:
+ *   bf16, d = dv = 64, chunk = 64, R*m in {64, 96, 128, 256}: fused MFMA
+ *     kernels (the feature map computed on chip);
+ *   otherwise bf16, d in {32, 64, 128}, dv in {64, 128}, chunk a multiple of
+ *     32, R*m in {128, 256, 384, 512}: wide MFMA kernels (phi(q), phi(k)
+ *     written once to the workspace in bf16, the state kept on chip);
+ *   every other accepted shape (fp32 included): the general kernels.
+ * All three compute the same quantity; the chunk size changes only the
+ * order of summation. */
 slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
                                     slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L, int32_t dv,
                                     int32_t chunk, const float* S0, const float* z0, void* o, float* S_out,
