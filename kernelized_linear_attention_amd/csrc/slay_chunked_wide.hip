@@ -31,9 +31,11 @@
 // features 4g..4g+3 and 16+4g..16+4g+3 of one column; phi(q) is read in the
 // same feature order), then the state update with phi(K)^T and V^T staged
 // token-contiguous in LDS.  The partials of a token tile meet in LDS and the
-// wave (cg, it) finishes tile it: num^T += V^T A^T, divide, store.  z stays
-// in fp32 on the VALU: wave w owns features [w F/8, (w+1) F/8) of z, adds
-// phi(k) over the chunk and forms its part of phi(q) . z for every token.
+// wave (cg, it) finishes tile it: num^T += V^T A^T, divide, store.  z is
+// summed in fp32 on the VALU: wave w owns features [w F/8, (w+1) F/8) of z,
+// adds phi(k) over the chunk (bf16 dot products with ones) and forms its part
+// of phi(q) . z for every token from a bf16 copy of z (as S enters the
+// readout in bf16).
 // The three causal 16x16 tiles of A^T are formed by waves 0..2, rounded to
 // bf16 (the same values feed A V and A 1) and shared through LDS.
 #include "slay_device.hpp"
@@ -200,20 +202,28 @@ __device__ __forceinline__ void w_update(const uint16_t* sKt, const uint16_t* sV
 }
 
 // z[f] += sum over the chunk's tokens of phi(k)[f] for the wave's features
-// (lane f - w*ZPW), fp32.
+// (lane f - w*ZPW), accumulated in fp32 (bf16 dot products with ones); a bf16
+// copy of z goes to sZb for the denominators when sZb is set.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 template <class K>
-__device__ __forceinline__ void w_zupdate(const uint16_t* sKt, float* sZ, int zf, int lane, float& zreg) {
+__device__ __forceinline__ void w_zupdate(const uint16_t* sKt, uint16_t* sZb, int zf, int lane, float& zreg) {
+  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
   if (lane < K::ZPW) {
     const uint16_t* kr = sKt + zf * K::LT;
-    float s = 0.f;
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int x = 0; x < K::C / 8; ++x) {
       const uint4 kv = *reinterpret_cast<const uint4*>(kr + 8 * x);
-      s += (lo_f(kv.x) + hi_f(kv.x)) + (lo_f(kv.y) + hi_f(kv.y)) + (lo_f(kv.z) + hi_f(kv.z)) +
-           (lo_f(kv.w) + hi_f(kv.w));
+      s0 = dot2(kv.x, kOnes, s0);
+      s1 = dot2(kv.y, kOnes, s1);
+      s0 = dot2(kv.z, kOnes, s0);
+      s1 = dot2(kv.w, kOnes, s1);
     }
-    zreg += s;
-    if (sZ) sZ[zf] = zreg;
+    zreg += s0 + s1;
+    if (sZb) sZb[zf] = f32_to_bf16(zreg);
   }
 }
 
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(K::NT) void wout_kernel(WParams p) {
   uint16_t* sA = reinterpret_cast<uint16_t*>(lds + K::oA);
   float* sP = reinterpret_cast<float*>(lds + K::oP);
   float* sDen = reinterpret_cast<float*>(lds + K::oDen);
-  float* sZ = reinterpret_cast<float*>(lds + K::oZ);
+  uint16_t* sZb = reinterpret_cast<uint16_t*>(lds + K::oZ);  // bf16 copy of z (denominators)
   uint16_t* sO = reinterpret_cast<uint16_t*>(lds + K::oO);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, col = lane & 15;
   const int cg = wave % K::NCG, fs = wave / K::NCG;
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(K::NT) void wout_kernel(WParams p) {
   float zreg = 0.f;
   if (lane < K::ZPW) {
     zreg = st[((zf >> 4) * K::NE + K::NE - 1) * 256 + 64 * ((zf & 15) >> 2) + (zf & 3)];
-    sZ[zf] = zreg;
+    sZb[zf] = f32_to_bf16(zreg);
   }
   for (int x = tid; x < K::C * K::LA / 2; x += K::NT) reinterpret_cast<uint32_t*>(sA)[x] = 0u;
   for (int x = tid; x < K::C * K::LD; x += K::NT) sDen[x] = 0.f;
@@ -380,25 +390,21 @@ __global__ __launch_bounds__(K::NT) void wout_kernel(WParams p) {
       const int i = lane & 31, hf = lane >> 5;
       const int f0 = wave * K::ZPW + hf * (K::ZPW / 2);
       const uint16_t* qr = sQ + i * K::LQ + f0;
-      float d = 0.f;
+      float d0 = 0.f, d1 = 0.f;
 #pragma unroll
       for (int x = 0; x < K::ZPW / 2; x += 8) {
         const uint4 qv = *reinterpret_cast<const uint4*>(qr + x);
-        const f32x4 za = *reinterpret_cast<const f32x4*>(sZ + f0 + x);
-        const f32x4 zb = *reinterpret_cast<const f32x4*>(sZ + f0 + x + 4);
-        d = fmaf(lo_f(qv.x), za[0], d);
-        d = fmaf(hi_f(qv.x), za[1], d);
-        d = fmaf(lo_f(qv.y), za[2], d);
-        d = fmaf(hi_f(qv.y), za[3], d);
-        d = fmaf(lo_f(qv.z), zb[0], d);
-        d = fmaf(hi_f(qv.z), zb[1], d);
-        d = fmaf(lo_f(qv.w), zb[2], d);
-        d = fmaf(hi_f(qv.w), zb[3], d);
+        const uint4 zv = *reinterpret_cast<const uint4*>(sZb + f0 + x);
+        d0 = dot2(qv.x, zv.x, d0);
+        d1 = dot2(qv.y, zv.y, d1);
+        d0 = dot2(qv.z, zv.z, d0);
+        d1 = dot2(qv.w, zv.w, d1);
       }
+      float d = d0 + d1;
       d += __shfl_xor(d, 32, 64);
       if (hf == 0) sDen[i * K::LD + wave] = d;
     }
-    w_zupdate<K>(sKt, sZ, zf, lane, zreg);
+    w_zupdate<K>(sKt, sZb, zf, lane, zreg);
 
     // partial num^T = S^T phi(Q)^T over the wave's features
     f32x4 num[2][2];
