@@ -207,8 +207,10 @@ def cpu_baseline(w, q, k, v, A, G, L_sample: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # timings settle only after ~100 forwards (~15 ms of GPU work): the
+    # default warm-up covers that; fewer warm-up steps measure a cold GPU
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per head of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
