@@ -114,6 +114,29 @@ def test_workspace_sizes(lib):
     assert lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p), 1, 16, 0, 64, 64, _lib.SLAY_BF16) == 0
 
 
+def test_wide_path_workspace(lib):
+    """bf16 shapes the fused kernels do not cover take the wide path: phi(q) and
+    phi(k) in bf16 (256-byte aligned each) plus one fp32 state of F x (dv+16)
+    per (head, segment), segments of whole 32-token chunks, about 512 of them
+    over the batch."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    p = _params(d=128, R=4, m=128)
+    # B1 H8 L131072 d=dv=128 F=512, chunk 128: segments of 2048 tokens, 64 per head
+    n = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p), 1, 8, 131072, 128, 128, _lib.SLAY_BF16)
+    assert n == 2 * r256(8 * 131072 * 512 * 2) + 4 * 8 * 64 * 512 * 144
+    # a short ragged sequence: segments of one chunk (32 tokens), ceil(1000 / 32) = 32 of them
+    n = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p), 1, 2, 1000, 128, 32, _lib.SLAY_BF16)
+    assert n == 2 * r256(2 * 1000 * 512 * 2) + 4 * 2 * 32 * 512 * 144
+    # dv = 64 with F = 256 at chunk 32 (the fused kernels need chunk 64): 32-token segments, 32 per head
+    p64 = _params(R=4, m=64)
+    n = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p64), 1, 3, 1000, 64, 32, _lib.SLAY_BF16)
+    assert n == 2 * r256(3 * 1000 * 256 * 2) + 4 * 3 * 32 * 256 * 80
+    # F = 96 has no wide variant: the general path (fp32 phi and per-chunk states)
+    p96 = _params(R=3, m=32)
+    n = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p96), 1, 1, 500, 64, 32, _lib.SLAY_BF16)
+    assert n == 4 * (2 * 500 * 96 + 16 * 96 * 65)
+
+
 def test_featmap_and_decode_validation(lib):
     p = _params()
     assert lib.slay_featmap(None, FAKE, _lib.SLAY_BF16, 10, 0, FAKE, _lib.SLAY_BF16, None) == _lib.SLAY_E_INVALID
