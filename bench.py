@@ -159,7 +159,7 @@ def traffic_summary(fetch_dir: str, write_dir: str, calib_mib: int, command: str
         w_kib = sum((pick(write, fr) or 0.0) * k for fr, k in frags)
         total = (f_kib * f_scale + w_kib * w_scale) * 1024.0
         lines = [f"# HBM traffic per launch: {name}", "", f"unit: {desc}", "",
-                 "commands (from the repository root on the GPU box):", "",
+                 "commands (from the repository root, on the machine with the GPU):", "",
                  f"    {command.replace('COUNTER', 'FETCH_SIZE')}",
                  f"    {command.replace('COUNTER', 'WRITE_SIZE')}",
                  f"    python bench.py --only {part} --traffic-summary <FETCH_SIZE dir> <WRITE_SIZE dir> "
@@ -228,7 +228,7 @@ def main():
                         args.traffic_command.replace("PART", args.only), args.only)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import torch
