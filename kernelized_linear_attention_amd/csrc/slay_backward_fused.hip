@@ -631,7 +631,8 @@ struct VjpK {
   static constexpr int NW = NF / 2, NT = NW * 64;
   static constexpr int RT = 32, NRB = RT / 16;  // rows per tile
   static constexpr int LX = D + 8, LR = D + 4;
-  static constexpr int oX = 0, oR = RT * LX * 2, kLds = oR + NW * RT * LR * 4;  // x tile, per-wave partials
+  // x tile, per-wave partials, 1/|x| per row (negative where |x| is clamped)
+  static constexpr int oX = 0, oR = RT * LX * 2, oI = oR + NW * RT * LR * 4, kLds = oI + RT * 4;
   static_assert(NT >= RT * 8 && NT >= RT * 16, "one x piece and one output piece per thread");
 };
 
@@ -676,6 +677,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   extern __shared__ __align__(16) char lds_raw[];
   uint16_t* sX = reinterpret_cast<uint16_t*>(lds_raw + K::oX);
   float* sR = reinterpret_cast<float*>(lds_raw + K::oR);
+  float* sI = reinterpret_cast<float*>(lds_raw + K::oI);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int side = blockIdx.y;
@@ -733,26 +735,26 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
     pf0 = pf1;
     pf1 = pf2;
     load_tile(tile + 3 * gs, pf2);
-    if (tid < K::RT * 8) *reinterpret_cast<uint4*>(sX + (tid >> 3) * K::LX + 8 * (tid & 7)) = cur.x;
+    if (tid < K::RT * 8) {  // x rows, and 1/|x| once per row (eight threads per row)
+      *reinterpret_cast<uint4*>(sX + (tid >> 3) * K::LX + 8 * (tid & 7)) = cur.x;
+      const uint32_t wds[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
+      float ss = 0.f;  // bf16 products are exact in fp32
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x2 h2 = __builtin_bit_cast(bf16x2, wds[t]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, ss, false);
+      }
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      if ((tid & 7) == 0) sI[tid >> 3] = ss < 1e-24f ? -1e12f : __builtin_amdgcn_rsqf(ss);
+    }
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < K::NRB; ++rb) {
       const bf16x8 xb0 = ld8(sX + (rb * 16 + c16) * K::LX + 8 * g);
       const bf16x8 xb1 = ld8(sX + (rb * 16 + c16) * K::LX + 32 + 8 * g);
-      // |x|^2 with the bf16 dot instruction (products of bf16 values are exact in fp32)
-      float ss = 0.f;
-      {
-        const uint4 u0 = __builtin_bit_cast(uint4, xb0), u1 = __builtin_bit_cast(uint4, xb1);
-        const uint32_t wds[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x2 h2 = __builtin_bit_cast(bf16x2, wds[t]);
-          ss = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, ss, false);
-        }
-      }
-      ss += __shfl_xor(ss, 16, 64);
-      ss += __shfl_xor(ss, 32, 64);
-      const float inv = ss < 1e-24f ? 1e12f : __builtin_amdgcn_rsqf(ss);
+      const float inv = fabsf(sI[rb * 16 + c16]);
       f32x4 dX[K::D / 16];
 #pragma unroll
       for (int cb = 0; cb < K::D / 16; ++cb) dX[cb] = kZero4;
@@ -766,14 +768,16 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
         const uint2 dr = cur.dp[rb][j];
         const float dp[4] = {__uint_as_float(dr.x << 16), __uint_as_float(dr.x & 0xFFFF0000u),
                              __uint_as_float(dr.y << 16), __uint_as_float(dr.y & 0xFFFF0000u)};
+        // u = dphi * a * e: w_a = 2u, w_g = u a sqrt(beta)
+        const float s1 = inv * c1[j];
         f32x4 wa, wg;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float a = ya[r] * inv;
-          const float e = fast_exp2(fmaf(yg[r] * inv, c1[j], c0[j]));
-          const float ae = a * e;
-          wa[r] = dp[r] * 2.f * ae;
-          wg[r] = dp[r] * a * ae * sb[j];
+          const float e = fast_exp2(fmaf(yg[r], s1, c0[j]));
+          const float u = dp[r] * (a * e);
+          wa[r] = u + u;
+          wg[r] = (u * a) * sb[j];
         }
         const bf16x8 w = pk_pair(wa, wg);
 #pragma unroll
@@ -794,19 +798,14 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       f32x4 dh = kZero4;
 #pragma unroll
       for (int w = 0; w < K::NW; ++w) dh += *reinterpret_cast<const f32x4*>(sR + (w * K::RT + rr) * K::LR + c);
-      float ss = 0.f, pr = 0.f;
+      float pr = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ss = fmaf(xv[r], xv[r], ss);
-        pr = fmaf(xv[r], dh[r], pr);
-      }
+      for (int r = 0; r < 4; ++r) pr = fmaf(xv[r], dh[r], pr);
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        ss += __shfl_xor(ss, o, 64);
-        pr += __shfl_xor(pr, o, 64);
-      }
-      const bool clamp = ss < 1e-24f;
-      const float inv = clamp ? 1e12f : __builtin_amdgcn_rsqf(ss);
+      for (int o = 1; o < 16; o <<= 1) pr += __shfl_xor(pr, o, 64);
+      const float si = sI[rr];
+      const bool clamp = si < 0.f;
+      const float inv = fabsf(si);
       const float proj = clamp ? 0.f : pr * inv;  // xh . dxh
       f32x4 o;
 #pragma unroll
