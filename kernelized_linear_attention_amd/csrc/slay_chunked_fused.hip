@@ -17,25 +17,17 @@
 // so appending a ones column to v (v' = [v | 1 | 0]) makes every contraction
 // with v' produce the numerator and the denominator together.
 //
-// Inside a workgroup (NW waves): wave w owns FBW blocks of 16 features.  It
-// keeps its slice of P = [anchors | prf] in registers as MFMA operands and
-// its F-slice of S' as fp32 accumulators for the whole segment.  Per chunk
-// of C tokens:
-//   stage    q, k tiles -> LDS (padded rows) with 1/|x| per row; v -> v'^T in LDS
-//   phase A  (all waves, own features)  phi(k): projection with tokens as the
-//            MFMA M dimension, so each lane's accumulator holds 4 consecutive
-//            tokens of one feature -- exactly the A-operand of the state
-//            update, kept in registers; also written to LDS as phi(k)[j][f].
-//            phi(q): projection with features as M, written to LDS as
-//            phi(q)[i][f] with 8-byte stores.
-//   phase B1 intra(ib): A^T = phi(k) phi(q)^T on the causal 16x16 blocks of
-//            query block ib, masked, rounded to bf16 and used in registers as
-//            the B-operand of num'^T += v'^T A^T;  inter(ib): num'^T +=
-//            S'^T phi(q)^T from the bf16 copy of S'^T in LDS.  Separate waves
-//            when there are enough, combined through LDS.
-//   phase B2 o = num / den (den is row dv of num'^T), 8-byte stores; each
-//            wave adds phi(k)^T v' to its S' slice and refreshes its rows of
-//            the bf16 S'^T copy for the next chunk.
+// Feature waves: wave w owns FBW blocks of 16 features.  It keeps its slice
+// of P = [anchors | prf] in registers as MFMA operands and its F-slice of S'
+// as fp32 accumulators for the whole segment.  phi(k) is projected with
+// tokens as the MFMA M dimension, so each lane's accumulator holds 4
+// consecutive tokens of one feature -- exactly the A-operand of the state
+// update, kept in registers (and, in pass 2, also written to LDS as
+// phi(k)[j][f]); phi(q) is projected with features as M and written to LDS as
+// phi(q)[i][f].  Pass 2 adds four consumer waves that run the contractions of
+// chunk c (the causal blocks A^T = phi(k) phi(q)^T, masked and rounded to
+// bf16, then v'^T A^T; and S'^T phi(q)^T from a bf16 copy of S'^T in LDS)
+// while the feature waves map chunk c+1 (see pass2s_kernel).
 // The contraction over tokens uses a fixed permutation of the 32 tokens of
 // an MFMA k-step (lane group g holds tokens 4g..4g+3 and 16+4g..16+4g+3) on
 // both operands, which leaves the sum unchanged and lets accumulators feed
@@ -68,21 +60,8 @@ struct Cfg {
   static constexpr int LDX = D + 8;        // padded row strides (elements)
   static constexpr int LDV = C + 4;        // 34 dwords: 16 lanes x 8 bytes hit 32 distinct banks
   static constexpr int LDF = F + 8;
-  static constexpr int NINTER = (NW - NTB) < NTB ? (NW - NTB) : NTB;  // inter tasks on their own wave
   static_assert(C % 32 == 0 && D % 32 == 0 && DV % 16 == 0, "tile sizes");
-  static_assert(NW >= NTB, "one intra task per wave at most");
-  // pass 2 LDS (bytes); v'^T is double-buffered
-  static constexpr int kQ = 0;
-  static constexpr int kK = kQ + C * LDX * 2;
-  static constexpr int kV = kK + C * LDX * 2;
-  static constexpr int kVbuf = VROWS * LDV * 2;
-  static constexpr int kPq = kV + 2 * kVbuf;
-  static constexpr int kPk = kPq + C * LDF * 2;
-  static constexpr int kSt = kPk + C * LDF * 2;
-  static constexpr int kX = kSt + VROWS * LDF * 2;
-  static constexpr int kInv = kX + (NINTER > 0 ? NINTER : 1) * NE * 64 * 16;
-  static constexpr int kLds = kInv + 4 * C * 4;  // inv and log2 scale of q and k rows
-  static_assert(kLds <= 160 * 1024, "LDS budget");
+  static constexpr int kVbuf = VROWS * LDV * 2;  // one v'^T buffer (bytes)
   // pass 1 LDS: k tile with its row scales (two buffers), v'^T (three buffers)
   static constexpr int kKbuf1 = C * LDX * 2 + 2 * C * 4;
   static constexpr int kLds1 = 2 * kKbuf1 + 3 * kVbuf;
@@ -649,65 +628,6 @@ __device__ __forceinline__ void store_state_out(const Params& p, int64_t head, i
     }
 }
 
-// intra(IB): A^T = phi(k) phi(q)^T on the causal 16x16 blocks (jb, IB),
-// jb <= IB, masked on the diagonal, rounded to bf16 and used in registers as
-// the B-operand of num'^T += v'^T A^T.  acc starts from zero.
-template <class K, int IB>
-__device__ __forceinline__ void intra_task(const uint16_t* sPq, const uint16_t* sPk, const uint16_t* sVc,
-                                           const RowOff<K, K::LDV>& vo, int lane, f32x4 (&acc)[K::NE]) {
-  if constexpr (IB < K::NTB) {
-    const int g = lane >> 4, col = lane & 15;
-    f32x4 at[IB + 1];
-#pragma unroll
-    for (int jb = 0; jb <= IB; ++jb) at[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
-      const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(sPq + (IB * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
-#pragma unroll
-      for (int jb = 0; jb <= IB; ++jb) {
-        const bf16x8 ak = as_bf16x8(*reinterpret_cast<const uint4*>(sPk + (jb * 16 + col) * K::LDF + kf_ * 32 + 8 * g));
-        at[jb] = mfma_bf16(ak, bq, at[jb]);
-      }
-    }
-    // causal mask on the diagonal block: keep j <= i (row 4g+i, column col)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * g + i > col) at[IB][i] = 0.f;
-#pragma unroll
-    for (int s = 0; 2 * s <= IB; ++s) {
-      const uint2 lo = pack4(at[2 * s][0], at[2 * s][1], at[2 * s][2], at[2 * s][3]);
-      uint2 hi = make_uint2(0, 0);
-      if constexpr (true) {
-        if (2 * s + 1 <= IB)
-          hi = pack4(at[(2 * s + 1) % (IB + 1)][0], at[(2 * s + 1) % (IB + 1)][1], at[(2 * s + 1) % (IB + 1)][2],
-                     at[(2 * s + 1) % (IB + 1)][3]);
-      }
-      const bf16x8 ab = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-      for (int et = 0; et < K::NE; ++et)
-        acc[et] = mfma_bf16(vfrag<K>(sVc, vo, et, s, lane), ab, s == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[et]);
-    }
-  }
-}
-
-// inter(ib): num'^T += S'^T phi(q)^T from the bf16 copy of S'^T in LDS
-// (num'^T = S'^T phi(q)^T when ZERO).
-template <class K, bool ZERO>
-__device__ __forceinline__ void inter_task(const uint16_t* sPq, const uint16_t* sSt, const RowOff<K, K::LDF>& so,
-                                           int ib, int lane, f32x4 (&acc)[K::NE]) {
-  const int g = lane >> 4, col = lane & 15;
-  const uint16_t* q0 = sPq + (ib * 16 + col) * K::LDF + 8 * g;
-#pragma unroll
-  for (int kf_ = 0; kf_ < K::NFK; ++kf_) {
-    const bf16x8 bq = as_bf16x8(*reinterpret_cast<const uint4*>(q0 + kf_ * 32));
-#pragma unroll
-    for (int et = 0; et < K::NE; ++et) {
-      const bf16x8 as = as_bf16x8(*reinterpret_cast<const uint4*>(sSt + so.off[et] + kf_ * 32 + 8 * g));
-      acc[et] = mfma_bf16(as, bq, (ZERO && kf_ == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[et]);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // pass 1: per-segment state deltas.  Every workgroup stages the whole chunk;
 // the F features are split over FS workgroups of NW/FS waves.  One barrier
@@ -883,140 +803,6 @@ __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
       __syncthreads();
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// pass 2: the segment's chunks in order, state on chip.  Two barriers per
-// chunk c:
-//   [X] before: B1(c) -- intra / inter contractions -- beside the staging of
-//       chunk c+1 (q, k tiles, v'^T into the other buffer, loads of c+2);
-//   [Y] before: B2(c) -- output of c, then phase A(c+1): phi(k), phi(q) of
-//       chunk c+1 with the state update by phi(k) of c spread through the
-//       phi(k) pipeline, and the refresh of the S'^T copy.
-// In the last step the staging works on a repeat of the last chunk (its
-// result is never read) and phase A is skipped.
-template <class K>
-__global__ __launch_bounds__(K::NT) void pass2_kernel(Params p) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(lds + K::kQ);
-  uint16_t* sK = reinterpret_cast<uint16_t*>(lds + K::kK);
-  auto sV = [&](int b) { return reinterpret_cast<uint16_t*>(lds + K::kV + b * K::kVbuf); };
-  uint16_t* sPq = reinterpret_cast<uint16_t*>(lds + K::kPq);
-  uint16_t* sPk = reinterpret_cast<uint16_t*>(lds + K::kPk);
-  uint16_t* sSt = reinterpret_cast<uint16_t*>(lds + K::kSt);
-  f32x4* sX = reinterpret_cast<f32x4*>(lds + K::kX);
-  float* sinvq = reinterpret_cast<float*>(lds + K::kInv);
-  float* slgq = sinvq + K::C;
-  float* sinvk = slgq + K::C;
-  float* slgk = sinvk + K::C;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, col = lane & 15;
-  const int64_t head = blockIdx.x / p.n_seg;
-  const int seg = (int)(blockIdx.x - head * p.n_seg);
-  const int set = (int)(head % p.n_draw_sets);
-
-  bf16x8 pa[K::FBW][K::NKS], pg[K::FBW][K::NKS];
-  float c1[K::FBW], c0[K::FBW];
-  load_p<K>(p, set, wave * K::FBW, lane, pa, pg, c1, c0);
-
-  f32x4 st[K::FBW][K::NE];
-  load_state<K>(p, head, seg, wave * K::FBW, lane, st);
-  init_vconst<K>(threadIdx.x, sV(0));
-  init_vconst<K>(threadIdx.x, sV(1));
-  // the zero row of the S'^T copy (padding columns DV+1..DV+15)
-  for (int t = threadIdx.x; t < K::LDF; t += K::NT) sSt[(K::DV + 1) * K::LDF + t] = 0;
-  const RowOff<K, K::LDV> vo(col);
-  const RowOff<K, K::LDF> so(col);
-  write_st<K>(sSt, so, wave, lane, st);
-  bf16x8 kf[K::FBW][K::NTS] = {};
-
-  const int role = __builtin_amdgcn_readfirstlane(wave < K::NTB ? wave : -1);
-  const bool intra_wave = wave < K::NTB;
-  const int ib_intra = wave;
-  const bool inter_wave = (wave >= K::NTB) && (wave - K::NTB < K::NINTER);
-  const int ib_inter = wave - K::NTB;
-  const bool self_inter = intra_wave && (wave >= K::NINTER);  // intra wave also does its inter
-
-  const int64_t t0 = (int64_t)seg * p.seg_len;
-  const int64_t t1 = min<int64_t>(p.L, t0 + p.seg_len);
-  const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
-
-  // prologue: stage chunk 0, phase A of chunk 0
-  Prefetch<K> pf;
-  auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
-    const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-    issue_loads<K>(threadIdx.x, p, head * p.L, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
-  };
-  load_chunk(0);
-  store_x<K>(threadIdx.x, pf.q, sQ, sinvq, slgq);
-  store_x<K>(threadIdx.x, pf.k, sK, sinvk, slgk);
-  store_v<K>(threadIdx.x, pf.v0, pf.v1, sV(0));
-  load_chunk(1);
-  __syncthreads();
-  phase_k<K, true, false>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf, nullptr, vo, kf, st);
-  phase_q<K>(sQ, sinvq, slgq, sPq, wave, lane, pa, pg, c1, c0);
-  __syncthreads();
-
-  for (int c = 0; c < nch; ++c) {
-    const int b = c & 1;
-    const int64_t c0t = t0 + (int64_t)c * K::C;
-    const int n = (int)min<int64_t>(K::C, t1 - c0t);
-    const uint16_t* sVc = sV(b);
-
-    // ---- B1(c): contractions; staging of chunk c+1 ----
-    f32x4 acc[K::NE];  // set by the intra task or, on inter waves, the inter task
-    switch (role) {  // wave-uniform (scalar) dispatch
-      case 0: intra_task<K, 0>(sPq, sPk, sVc, vo, lane, acc); break;
-      case 1: intra_task<K, 1>(sPq, sPk, sVc, vo, lane, acc); break;
-      case 2: intra_task<K, 2>(sPq, sPk, sVc, vo, lane, acc); break;
-      case 3: intra_task<K, 3>(sPq, sPk, sVc, vo, lane, acc); break;
-      default: break;
-    }
-    if (inter_wave) {
-      inter_task<K, true>(sPq, sSt, so, ib_inter, lane, acc);
-#pragma unroll
-      for (int et = 0; et < K::NE; ++et) sX[(ib_inter * K::NE + et) * 64 + lane] = acc[et];
-    } else if (self_inter) {
-      inter_task<K, false>(sPq, sSt, so, ib_intra, lane, acc);
-    }
-    store_x<K>(threadIdx.x, pf.q, sQ, sinvq, slgq);
-    store_x<K>(threadIdx.x, pf.k, sK, sinvk, slgk);
-    store_v<K>(threadIdx.x, pf.v0, pf.v1, sV(b ^ 1));
-    load_chunk(c + 2);
-    __syncthreads();  // X
-
-    // ---- B2(c): output and state update; phase A(c+1) ----
-    if (intra_wave) {
-      const int ib = ib_intra;
-      if (!self_inter) {
-#pragma unroll
-        for (int et = 0; et < K::NE; ++et) acc[et] += sX[(ib * K::NE + et) * 64 + lane];
-      }
-      // den of token col = element (row dv, column col): lane col (g = 0), i = 0 of tile NE-1
-      const float den = __shfl(acc[K::NE - 1][0], col, 64);
-      const float rden = __builtin_amdgcn_rcpf(den);
-      const int tok = ib * 16 + col;
-      if (tok < n) {
-        uint16_t* orow = p.o + (head * p.L + c0t + tok) * K::DV;
-#pragma unroll
-        for (int et = 0; et < K::NE - 1; ++et)
-          *reinterpret_cast<uint2*>(orow + et * 16 + 4 * g) =
-              pack4(acc[et][0] * rden, acc[et][1] * rden, acc[et][2] * rden, acc[et][3] * rden);
-      }
-    }
-    if (c + 1 < nch) {
-      phase_k<K, true, true>(sK, sinvk, slgk, sPk, wave * K::FBW, lane, pa, pg, c1, c0, kf, sVc, vo, kf, st);
-      write_st<K>(sSt, so, wave, lane, st);
-      phase_q<K>(sQ, sinvq, slgq, sPq, wave, lane, pa, pg, c1, c0);
-    } else {  // last chunk: its state update only
-#pragma unroll
-      for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sVc, vo, lane, s_, kf, st);
-    }
-    __syncthreads();  // Y
-  }
-
-  if (seg == p.n_seg - 1 && (p.S_out || p.z_out)) store_state_out<K>(p, head, wave * K::FBW, lane, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1354,16 +1140,12 @@ typedef Cfg<64, 64, 64, 8, 1> CfgF128;
 typedef Cfg<64, 64, 64, 6, 1> CfgF96;
 typedef Cfg<64, 64, 64, 4, 1> CfgF64;
 
-// Main-pass configuration per segment-pass configuration: the warp-specialized
-// kernel where one is compiled, else the two-phase pass2_kernel.  Both use the
-// same segments and the same fragment-ordered workspace.
+// Main-pass configuration for a segment-pass configuration: the same feature
+// waves as producers, 32-token chunks; both use the same segments and the
+// same fragment-ordered workspace.
 template <class K>
 struct MainPass {
-  using type = void;
-};
-template <>
-struct MainPass<CfgF256> {
-  using type = CfgS<64, 64, 8, 2>;
+  using type = CfgS<K::D, K::DV, K::NW, K::FBW>;
 };
 
 // Segments per head for n_heads heads of L tokens: enough workgroups to fill
@@ -1467,15 +1249,9 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   using KS = typename MainPass<K>::type;
-  if constexpr (!std::is_void_v<KS>) {
-    e = set_max_lds(reinterpret_cast<const void*>(&pass2s_kernel<KS>), KS::kLdsS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pass2s_kernel<KS>, dim3((unsigned)(a.n_heads * n_seg)), dim3(KS::NTW), KS::kLdsS, s, p);
-  } else {
-    e = set_max_lds(reinterpret_cast<const void*>(&pass2_kernel<K>), K::kLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pass2_kernel<K>, dim3((unsigned)(a.n_heads * n_seg)), dim3(K::NT), K::kLds, s, p);
-  }
+  e = set_max_lds(reinterpret_cast<const void*>(&pass2s_kernel<KS>), KS::kLdsS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pass2s_kernel<KS>, dim3((unsigned)(a.n_heads * n_seg)), dim3(KS::NTW), KS::kLdsS, s, p);
   return hipGetLastError();
 }
 
