@@ -1,4 +1,4 @@
-"""The forward, variable-length forward and backward captured in HIP graphs.
+"""The forward (fused and wide paths), variable-length forward and backward captured in HIP graphs.
 
 Each call is captured once (with its workspace and outputs preallocated) and
 the graph replayed several times, with eager calls of the same entry point
@@ -104,3 +104,23 @@ def test_backward_graph(lib):
                         state_grad=True)
 
     _replay_matches(lambda: run(g), lambda: run(e), g, e)
+
+
+def test_wide_forward_graph(lib):
+    """The wide path (feature maps in the workspace, d = dv = 128, F = 512)."""
+    import torch
+
+    w = ss.WORKLOADS["h8_l128k_d128_bf16"].with_(H=2, L=1500)
+    q, k, v = (to_dev(x, "bf16") for x in ss.make_qkv(w))
+    A, G = ss.make_draws(w)
+    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), w.R, w.m, w.eps)
+    ws = torch.empty(lib.chunked_fwd_workspace_size(fm, 1, 2, w.L, w.dv, w.chunk, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    og, oe = torch.empty_like(v), torch.empty_like(v)
+    Sg, Se = (torch.empty(2, w.F, w.dv, device="cuda") for _ in range(2))
+    zg, ze = (torch.empty(2, w.F, device="cuda") for _ in range(2))
+    _replay_matches(lambda: lib.chunked_fwd(fm, q, k, v, w.chunk, out=og, workspace=ws, return_state=True, S_out=Sg,
+                                            z_out=zg),
+                    lambda: lib.chunked_fwd(fm, q, k, v, w.chunk, out=oe, workspace=ws, return_state=True, S_out=Se,
+                                            z_out=ze),
+                    [og, Sg, zg], [oe, Se, ze])
