@@ -179,8 +179,14 @@ size_t slay_attn_chunked_bwd_workspace_size(const slay_params_t* params, int32_t
  *                slay_attn_chunked_bwd_workspace_size(...) bytes (NULL if 0).
  * chunk in [1, 128] only changes the summation order; dv <= 256.  L = 0 sets
  * dS0 = dS_T and dz0 = dz_T (zero where those are NULL).
- * Unfused general kernels (the feature map to the workspace, per-chunk
- * states with a forward prefix and a reverse suffix, FMA contractions). */
+ * Kernel families, chosen from the shape:
+ *   bf16, d = dv = 64, chunk = 64, m a multiple of 32, R*m <= 256: MFMA
+ *     kernels (phi written once in bf16, per-segment states, 32-token steps);
+ *     R*m below 256 runs them on features zero-padded to 256, which changes
+ *     no result (the padded features and their gradients are exactly zero);
+ *   every other accepted shape: general kernels (the feature map to the
+ *     workspace, per-chunk states with a forward prefix and a reverse
+ *     suffix, FMA contractions). */
 slay_status_t slay_attn_chunked_bwd(const slay_params_t* params, const void* q, const void* k, const void* v,
                                     const void* dout, slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L,
                                     int32_t dv, int32_t chunk, const float* S0, const float* z0, const float* dS_T,

@@ -872,25 +872,93 @@ ChunkedArgs forward_args(const BackwardArgs& a) {
   return c;
 }
 
+// Feature counts below 256 run the F = 256 kernels on zero-padded features:
+// the draws get zero rows f >= F (so phi_f = 0 and every contraction with it
+// vanishes, and the node constants beyond R are zero, so the feature map and
+// its VJP stay finite there), the states and their gradients zero rows.
+// dst[b][r][:] = src[b][r][:] for r < rows_src and 0 for rows_src <= r < rows_dst.
+template <typename T>
+__global__ __launch_bounds__(256) void pad_rows_kernel(T* __restrict__ dst, const T* __restrict__ src,
+                                                       int64_t n_blocks, int64_t rows_src, int64_t rows_dst,
+                                                       int64_t row_elems, int64_t src_stride, int64_t dst_stride) {
+  const int64_t per = rows_dst * row_elems;
+  const int64_t total = n_blocks * per;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t b = i / per, rem = i - b * per, r = rem / row_elems, e = rem - r * row_elems;
+    dst[b * dst_stride + r * row_elems + e] = r < rows_src ? src[b * src_stride + r * row_elems + e] : T(0);
+  }
+}
+
+template <typename T>
+hipError_t pad_rows(T* dst, const T* src, int64_t n_blocks, int64_t rows_src, int64_t rows_dst, int64_t row_elems,
+                    int64_t src_stride, int64_t dst_stride, hipStream_t s) {
+  const int64_t total = n_blocks * rows_dst * row_elems;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(pad_rows_kernel<T>, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, dst, src,
+                     n_blocks, rows_src, rows_dst, row_elems, src_stride, dst_stride);
+  return hipGetLastError();
+}
+
+// Workspace of the padded call after the F = 256 one: padded draws and states.
+struct PadWs {
+  uint16_t *anchors, *prf;
+  float *S0, *z0, *dS_T, *dz_T, *dS0, *dz0;
+  size_t bytes;
+};
+
+PadWs pad_ws(const BackwardArgs& a, char* base) {
+  PadWs w{};
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    char* q = base ? base + off : nullptr;
+    off += (b + 255) & ~(size_t)255;
+    return q;
+  };
+  const size_t nd = (size_t)a.n_draw_sets * K256::F * a.d * 2;
+  const size_t ns = (size_t)a.n_heads * K256::F * a.dv * 4, nz = (size_t)a.n_heads * K256::F * 4;
+  w.anchors = reinterpret_cast<uint16_t*>(take(nd));
+  w.prf = reinterpret_cast<uint16_t*>(take(nd));
+  w.S0 = reinterpret_cast<float*>(take(ns));
+  w.z0 = reinterpret_cast<float*>(take(nz));
+  w.dS_T = reinterpret_cast<float*>(take(ns));
+  w.dz_T = reinterpret_cast<float*>(take(nz));
+  w.dS0 = reinterpret_cast<float*>(take(ns));
+  w.dz0 = reinterpret_cast<float*>(take(nz));
+  w.bytes = off;
+  return w;
+}
+
+BackwardArgs padded_args(const BackwardArgs& a) {
+  BackwardArgs p = a;
+  p.F = K256::F;
+  return p;
+}
+
 }  // namespace
 
 bool backward_fused_supported(const BackwardArgs& a) {
   if (a.n_heads == 0 || a.L == 0) return false;  // nothing for the MFMA kernels: the general launcher handles it
-  if (!a.io_bf16 || a.d != 64 || a.dv != 64 || a.F != K256::F || a.chunk != 64 || a.m % 32 != 0) return false;
+  // F < 256 runs on zero-padded features (a multiple of 32, as the m % 32 rule gives)
+  if (!a.io_bf16 || a.d != 64 || a.dv != 64 || a.F > K256::F || a.F % 32 != 0 || a.chunk != 64 || a.m % 32 != 0)
+    return false;
   if (a.n_draw_sets > 1 && a.L % V256::RT != 0) return false;  // a VJP tile must not span two draw sets
   int64_t seg_len = 0;
-  return fused_segment_count(forward_args(a), &seg_len) > 0 && seg_len % K256::C == 0;
+  return fused_segment_count(forward_args(padded_args(a)), &seg_len) > 0 && seg_len % K256::C == 0;
 }
 
 size_t backward_fused_workspace_bytes(const BackwardArgs& a) {
   if (a.n_heads == 0 || a.L == 0) return 0;
+  const BackwardArgs ap = padded_args(a);
   int64_t seg_len = 0;
-  const int n_seg = fused_segment_count(forward_args(a), &seg_len);
-  return fused_ws(a, n_seg, nullptr).bytes;
+  const int n_seg = fused_segment_count(forward_args(ap), &seg_len);
+  const size_t base = fused_ws(ap, n_seg, nullptr).bytes;
+  return a.F == K256::F ? base : base + pad_ws(a, nullptr).bytes;
 }
 
-hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
-  if (a.n_heads == 0 || a.L == 0) return launch_backward(a, s);  // only the state gradient passes through
+namespace {
+
+hipError_t launch_backward_fused_256(const BackwardArgs& a, hipStream_t s) {
   const ChunkedArgs fa = forward_args(a);
   int64_t seg_len = 0;
   const int n_seg = fused_segment_count(fa, &seg_len);
@@ -981,6 +1049,47 @@ hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   const unsigned gx = (unsigned)(n_tiles < 128 ? n_tiles : 128);  // one workgroup per CU over both sides
   hipLaunchKernelGGL(vjp_kernel<V256>, dim3(gx, 2), dim3(V256::NT), V256::kLds, s, vp);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
+  if (a.n_heads == 0 || a.L == 0) return launch_backward(a, s);  // only the state gradient passes through
+  if (a.F == K256::F) return launch_backward_fused_256(a, s);
+  BackwardArgs ap = padded_args(a);
+  int64_t seg_len = 0;
+  const int n_seg = fused_segment_count(forward_args(ap), &seg_len);
+  const PadWs w = pad_ws(a, static_cast<char*>(a.ws) + fused_ws(ap, n_seg, nullptr).bytes);
+  const int64_t nh = a.n_heads, F = a.F, P = K256::F, d = a.d, dv = a.dv;
+  hipError_t e = pad_rows<uint16_t>(w.anchors, static_cast<const uint16_t*>(a.anchors), a.n_draw_sets, F, P, d,
+                                    a.draw_set_stride, P * d, s);
+  if (e == hipSuccess)
+    e = pad_rows<uint16_t>(w.prf, static_cast<const uint16_t*>(a.prf), a.n_draw_sets, F, P, d, a.draw_set_stride,
+                           P * d, s);
+  if (e != hipSuccess) return e;
+  ap.anchors = w.anchors;
+  ap.prf = w.prf;
+  ap.draw_set_stride = P * d;
+  // padded inputs (read before anything is written: a gradient output may alias its input)
+  struct In {
+    const float* src;
+    float* dst;
+    int64_t row_elems;
+    const float** slot;
+  } ins[4] = {{a.S0, w.S0, dv, &ap.S0}, {a.z0, w.z0, 1, &ap.z0}, {a.dS_T, w.dS_T, dv, &ap.dS_T}, {a.dz_T, w.dz_T, 1, &ap.dz_T}};
+  for (const In& in : ins) {
+    if (!in.src) continue;
+    e = pad_rows<float>(in.dst, in.src, nh, F, P, in.row_elems, F * in.row_elems, P * in.row_elems, s);
+    if (e != hipSuccess) return e;
+    *in.slot = in.dst;
+  }
+  ap.dS0 = a.dS0 ? w.dS0 : nullptr;
+  ap.dz0 = a.dz0 ? w.dz0 : nullptr;
+  e = launch_backward_fused_256(ap, s);
+  if (e != hipSuccess) return e;
+  if (a.dS0) e = pad_rows<float>(a.dS0, w.dS0, nh, F, F, dv, P * dv, F * dv, s);
+  if (e == hipSuccess && a.dz0) e = pad_rows<float>(a.dz0, w.dz0, nh, F, F, 1, P, F, s);
+  return e;
 }
 
 }  // namespace slay

@@ -146,7 +146,8 @@ struct BackwardArgs {
   size_t ws_bytes;
 };
 bool backward_supported(const BackwardArgs& a);
-// MFMA path of the backward (bf16, d = dv = 64, F = 256, chunk 64).
+// MFMA path of the backward (bf16, d = dv = 64, chunk 64, F <= 256 a multiple
+// of 32; F below 256 on zero-padded features).
 bool backward_fused_supported(const BackwardArgs& a);
 size_t backward_fused_workspace_bytes(const BackwardArgs& a);
 hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s);

@@ -80,7 +80,7 @@ def _compare(got, ref, dtype, tag):
     ("tiny_f32", 1, 2, 77, 16, True),               # fp32 with initial state and final-state gradient
     ("h16_l16k_bf16", 1, 2, 300, 64, True),         # MFMA path: F = 256, three segments, ragged tail
     ("h16_l16k_bf16", 1, 1, 4000, 64, True),        # MFMA path: 32 segments walked in 32-token steps
-    ("b4h8_l2k_bf16", 2, 1, 257, 64, False),        # bf16, F = 96, ragged tail of one token
+    ("b4h8_l2k_bf16", 2, 1, 257, 64, False),        # MFMA path on zero-padded features: F = 96, tail of one token
     ("h8_l128k_d128_bf16", 1, 1, 200, 128, True),   # bf16, d = dv = 128, F = 512, chunk 128
 ])
 def test_backward_parity(lib, orc, name, B, H, L, chunk, with_state):
@@ -97,6 +97,48 @@ def test_backward_parity(lib, orc, name, B, H, L, chunk, with_state):
     for t in got:
         assert np.all(np.isfinite(t))
     _compare(got, ref, w.dtype, name)
+
+
+@pytest.mark.parametrize("R,m,H,L", [
+    (3, 32, 2, 700),   # F = 96 (the B4 H8 L2048 workload's features), three segments
+    (1, 32, 1, 300),   # F = 32
+    (2, 32, 3, 129),   # F = 64
+    (7, 32, 1, 1000),  # F = 224
+])
+def test_backward_padded_features(lib, orc, R, m, H, L):
+    """F < 256 runs the F = 256 MFMA kernels on zero-padded features: the
+    padding must change nothing, initial state and final-state gradient included."""
+    w = ss.WORKLOADS["b4h8_l2k_bf16"].with_(B=1, H=H, L=L, R=R, m=m)
+    _say(f"backward padded features F={w.F} H={H} L={L}")
+    q, k, v = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    dout, dST, dzT = ss.make_grads(w)
+    S0, z0 = _state(w, 8)
+    got = _run_bwd(lib, w, q, k, v, dout, A, G, 64, S0, z0, dST, dzT)
+    ref = orc.slay_causal_bwd(q, k, v, dout, A, G, w.eps, w.R, w.m, S0=S0, z0=z0, dS_T=dST, dz_T=dzT)
+    for t in got:
+        assert np.all(np.isfinite(t))
+    assert got[3].shape == (H, w.F, w.dv) and got[4].shape == (H, w.F)
+    _compare(got, ref, w.dtype, f"F={w.F}")
+
+
+def test_backward_padded_per_head_draws(lib, orc):
+    """Padded features with one draw set per head (the padding is per set)."""
+    import torch
+
+    w = ss.WORKLOADS["b4h8_l2k_bf16"].with_(B=1, H=2, L=256)
+    q, k, v = ss.make_qkv(w)
+    A0, G0 = ss.make_draws(w)
+    A1, G1 = ss.make_draws(w, seed=[3, 98])
+    A, G = np.stack([A0, A1]), np.stack([G0, G1])
+    dout, _, _ = ss.make_grads(w)
+    fm = lib.FeatureMap(to_dev(A, w.dtype), to_dev(G, w.dtype), w.R, w.m, w.eps)
+    res = lib.chunked_bwd(fm, to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), to_dev(dout, w.dtype), 64,
+                          state_grad=True)
+    torch.cuda.synchronize()
+    got = tuple(to_np(t) for t in res)
+    ref = orc.slay_causal_bwd(q, k, v, dout, A, G, w.eps, w.R, w.m, per_head_draws=True)
+    _compare(got, ref, w.dtype, "padded, per-head draws")
 
 
 def test_backward_chunk_invariance(lib):
