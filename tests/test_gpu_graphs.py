@@ -124,3 +124,30 @@ def test_wide_forward_graph(lib):
                     lambda: lib.chunked_fwd(fm, q, k, v, w.chunk, out=oe, workspace=ws, return_state=True, S_out=Se,
                                             z_out=ze),
                     [og, Sg, zg], [oe, Se, ze])
+
+
+def test_padded_backward_graph(lib):
+    """The backward at F = 96 (features zero-padded to 256, with the padding
+    copies of the draws and of the states inside the graph)."""
+    import torch
+
+    w = ss.WORKLOADS["b4h8_l2k_bf16"].with_(B=1, H=2, L=700)
+    q, k, v = (to_dev(x, "bf16") for x in ss.make_qkv(w))
+    dout, dST, dzT = ss.make_grads(w)
+    dout = to_dev(dout, "bf16")
+    dST, dzT = (torch.from_numpy(np.float32(x)).cuda() for x in (dST, dzT))
+    S0 = torch.rand(2, w.F, w.dv, device="cuda")
+    z0 = torch.rand(2, w.F, device="cuda") + 0.5
+    A, G = ss.make_draws(w)
+    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), w.R, w.m, w.eps)
+    ws = torch.empty(lib.chunked_bwd_workspace_size(fm, 1, 2, w.L, w.dv, 64, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    g = [torch.empty_like(x) for x in (q, k, v)] + [torch.empty(2, w.F, w.dv, device="cuda"),
+                                                    torch.empty(2, w.F, device="cuda")]
+    e = [torch.empty_like(x) for x in g]
+
+    def run(o):
+        lib.chunked_bwd(fm, q, k, v, dout, 64, S0=S0, z0=z0, dS_T=dST, dz_T=dzT, workspace=ws, dq=o[0], dk=o[1],
+                        dv=o[2], dS0=o[3], dz0=o[4], state_grad=True)
+
+    _replay_matches(lambda: run(g), lambda: run(e), g, e)
