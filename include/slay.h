@@ -108,8 +108,10 @@ size_t slay_attn_chunked_fwd_workspace_size(const slay_params_t* params, int32_t
  * L need not be a multiple of chunk (the tail chunk is masked); L = 0 only
  * copies S0/z0 to S_out/z_out.  chunk in [1, 128].
  * Kernel families, chosen from the shape:
- *   bf16, d = dv = 64, chunk = 64, R*m in {64, 96, 128, 256}: fused MFMA
- *     kernels (the feature map computed on chip);
+ *   bf16, d = dv = 64, chunk = 64, R*m <= 256: fused MFMA kernels (the
+ *     feature map computed on chip), built for R*m in {64, 96, 128, 256};
+ *     other R*m run the next built count on zero-padded features (no result
+ *     changes; R*m above 128 needs m a multiple of 32);
  *   otherwise bf16, d in {32, 64, 128}, dv in {64, 128}, chunk a multiple of
  *     32, R*m in {128, 256, 384, 512}: wide MFMA kernels (phi(q), phi(k)
  *     written once to the workspace in bf16, the state kept on chip);
@@ -142,8 +144,9 @@ size_t slay_attn_varlen_fwd_workspace_size(const slay_params_t* params, int32_t 
  *   S_out, z_out: nullable device fp32 final states, same shapes (may alias
  *                S0, z0): a prefill's hand-off to slay_attn_recurrent_step.
  *   workspace  : device scratch of slay_attn_varlen_fwd_workspace_size() bytes.
- * Supported: d = dv = 64, R*m = 256 with m a multiple of 32 (the fused MFMA
- * kernels; other shapes return SLAY_E_UNSUPPORTED).  One launch each of a
+ * Supported: bf16, d = dv = 64, R*m <= 256 with m a multiple of 32 (the
+ * fused MFMA kernels; R*m below 256 on features zero-padded to 256, which
+ * changes no result; other shapes return SLAY_E_UNSUPPORTED).  One launch each of a
  * work-list kernel, the segment-state pass, the per-sequence scan and the
  * main pass, whatever the number of sequences. */
 slay_status_t slay_attn_varlen_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
@@ -213,9 +216,10 @@ size_t slay_attn_noncausal_fwd_workspace_size(const slay_params_t* params, int32
  *                slay_attn_noncausal_fwd_workspace_size(...) bytes (NULL if 0).
  * Lq and Lk are independent (Lq = 0 only produces the state).  Lk = 0 needs
  * z0 when Lq > 0 (SLAY_E_INVALID otherwise: the denominators would be 0).
- * bf16 with d = dv = 64 and R*m in {64, 96, 128, 256} runs the fused MFMA
- * kernels (segment states of the keys, their sum, a readout pass over the
- * queries); every other accepted shape runs the general kernels. */
+ * bf16 with d = dv = 64 and R*m <= 256 runs the fused MFMA kernels (segment
+ * states of the keys, their sum, a readout pass over the queries; R*m not in
+ * {64, 96, 128, 256} on zero-padded features, R*m above 128 with m a multiple
+ * of 32); every other accepted shape runs the general kernels. */
 slay_status_t slay_attn_noncausal_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
                                       slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t Lq, int64_t Lk,
                                       int32_t dv, const float* S0, const float* z0, void* o, float* S_out,

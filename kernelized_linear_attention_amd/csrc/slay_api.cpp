@@ -421,7 +421,7 @@ slay_status_t slay_attn_varlen_fwd(const slay_params_t* params, const void* q, c
   a.n_seqs = n_seqs;
   a.cu = cu_seqlens;
   if (!slay::varlen_supported(a))
-    return fail(SLAY_E_UNSUPPORTED, "variable-length batches need bf16, d = dv = 64 and R*m = 256 (m a multiple of 32); "
+    return fail(SLAY_E_UNSUPPORTED, "variable-length batches need bf16, d = dv = 64 and R*m <= 256 (m a multiple of 32); "
                 "got d=%d dv=%d F=%d", params->d, dv, F);
   if (H == 0 || n_seqs == 0) return ok();
   if (!cu_seqlens) return fail(SLAY_E_INVALID, "cu_seqlens is NULL");

@@ -876,30 +876,6 @@ ChunkedArgs forward_args(const BackwardArgs& a) {
 // the draws get zero rows f >= F (so phi_f = 0 and every contraction with it
 // vanishes, and the node constants beyond R are zero, so the feature map and
 // its VJP stay finite there), the states and their gradients zero rows.
-// dst[b][r][:] = src[b][r][:] for r < rows_src and 0 for rows_src <= r < rows_dst.
-template <typename T>
-__global__ __launch_bounds__(256) void pad_rows_kernel(T* __restrict__ dst, const T* __restrict__ src,
-                                                       int64_t n_blocks, int64_t rows_src, int64_t rows_dst,
-                                                       int64_t row_elems, int64_t src_stride, int64_t dst_stride) {
-  const int64_t per = rows_dst * row_elems;
-  const int64_t total = n_blocks * per;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t b = i / per, rem = i - b * per, r = rem / row_elems, e = rem - r * row_elems;
-    dst[b * dst_stride + r * row_elems + e] = r < rows_src ? src[b * src_stride + r * row_elems + e] : T(0);
-  }
-}
-
-template <typename T>
-hipError_t pad_rows(T* dst, const T* src, int64_t n_blocks, int64_t rows_src, int64_t rows_dst, int64_t row_elems,
-                    int64_t src_stride, int64_t dst_stride, hipStream_t s) {
-  const int64_t total = n_blocks * rows_dst * row_elems;
-  if (total == 0) return hipSuccess;
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(pad_rows_kernel<T>, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, dst, src,
-                     n_blocks, rows_src, rows_dst, row_elems, src_stride, dst_stride);
-  return hipGetLastError();
-}
-
 // Workspace of the padded call after the F = 256 one: padded draws and states.
 struct PadWs {
   uint16_t *anchors, *prf;
@@ -1061,10 +1037,10 @@ hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   const int n_seg = fused_segment_count(forward_args(ap), &seg_len);
   const PadWs w = pad_ws(a, static_cast<char*>(a.ws) + fused_ws(ap, n_seg, nullptr).bytes);
   const int64_t nh = a.n_heads, F = a.F, P = K256::F, d = a.d, dv = a.dv;
-  hipError_t e = pad_rows<uint16_t>(w.anchors, static_cast<const uint16_t*>(a.anchors), a.n_draw_sets, F, P, d,
+  hipError_t e = pad_rows(w.anchors, static_cast<const uint16_t*>(a.anchors), a.n_draw_sets, F, P, d,
                                     a.draw_set_stride, P * d, s);
   if (e == hipSuccess)
-    e = pad_rows<uint16_t>(w.prf, static_cast<const uint16_t*>(a.prf), a.n_draw_sets, F, P, d, a.draw_set_stride,
+    e = pad_rows(w.prf, static_cast<const uint16_t*>(a.prf), a.n_draw_sets, F, P, d, a.draw_set_stride,
                            P * d, s);
   if (e != hipSuccess) return e;
   ap.anchors = w.anchors;
@@ -1079,7 +1055,7 @@ hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   } ins[4] = {{a.S0, w.S0, dv, &ap.S0}, {a.z0, w.z0, 1, &ap.z0}, {a.dS_T, w.dS_T, dv, &ap.dS_T}, {a.dz_T, w.dz_T, 1, &ap.dz_T}};
   for (const In& in : ins) {
     if (!in.src) continue;
-    e = pad_rows<float>(in.dst, in.src, nh, F, P, in.row_elems, F * in.row_elems, P * in.row_elems, s);
+    e = pad_rows(in.dst, in.src, nh, F, P, in.row_elems, F * in.row_elems, P * in.row_elems, s);
     if (e != hipSuccess) return e;
     *in.slot = in.dst;
   }
@@ -1087,8 +1063,8 @@ hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   ap.dz0 = a.dz0 ? w.dz0 : nullptr;
   e = launch_backward_fused_256(ap, s);
   if (e != hipSuccess) return e;
-  if (a.dS0) e = pad_rows<float>(a.dS0, w.dS0, nh, F, F, dv, P * dv, F * dv, s);
-  if (e == hipSuccess && a.dz0) e = pad_rows<float>(a.dz0, w.dz0, nh, F, F, 1, P, F, s);
+  if (a.dS0) e = pad_rows(a.dS0, w.dS0, nh, F, F, dv, P * dv, F * dv, s);
+  if (e == hipSuccess && a.dz0) e = pad_rows(a.dz0, w.dz0, nh, F, F, 1, P, F, s);
   return e;
 }
 

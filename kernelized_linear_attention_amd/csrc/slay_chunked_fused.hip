@@ -1529,16 +1529,124 @@ VlWs vl_ws(const VarlenArgs& a, int g_max, void* base) {
 
 }  // namespace
 
+// Feature counts the fused kernels are not built for run a built count's
+// kernels on zero-padded features: the draws get zero rows f >= F (phi_f = 0,
+// and the node constants beyond R are zero, so the exponent stays finite),
+// the initial states zero rows, and the first F rows of the final states are
+// copied out.  No result changes; the padded work is the cost.
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// F itself when kernels are built for it, else the smallest built count it
+// can be padded to; 0 when there is none.
+int fused_target_F(const ChunkedArgs& a) {
+  if (!a.io_bf16 || a.d != 64 || a.dv != 64 || a.chunk != 64 || a.m % 16 != 0) return 0;
+  for (const int Fb : {CfgF64::F, CfgF96::F, CfgF128::F, CfgF256::F}) {
+    if (Fb < a.F) continue;
+    if (Fb == CfgF256::F && a.m % 32 != 0) continue;  // a wave's two feature blocks must share a node
+    if ((Fb - 1) / a.m >= kMaxNodes) continue;        // node of every padded feature in the table
+    return Fb;
+  }
+  return 0;
+}
+
+// Padded copies: draws [n_sets][Fp][d], states [n_state][Fp][dv] and [n_state][Fp].
+struct FPad {
+  uint16_t *anchors, *prf;
+  float *S0, *z0, *S_out, *z_out;
+  size_t bytes;
+};
+
+FPad fpad_ws(const ChunkedArgs& a, int Fp, int64_t n_state, char* base) {
+  FPad w{};
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    char* q = base ? base + off : nullptr;
+    off += align256(b);
+    return q;
+  };
+  const size_t nd = (size_t)a.n_draw_sets * Fp * a.d * 2;
+  const size_t ns = (size_t)n_state * Fp * a.dv * 4, nz = (size_t)n_state * Fp * 4;
+  w.anchors = reinterpret_cast<uint16_t*>(take(nd));
+  w.prf = reinterpret_cast<uint16_t*>(take(nd));
+  w.S0 = reinterpret_cast<float*>(take(ns));
+  w.z0 = reinterpret_cast<float*>(take(nz));
+  w.S_out = reinterpret_cast<float*>(take(ns));
+  w.z_out = reinterpret_cast<float*>(take(nz));
+  w.bytes = off;
+  return w;
+}
+
+// Fill the padded inputs and point ap (a copy of a with F = Fp) at them.  The
+// inputs are copied before anything is written: S_out may alias S0.
+hipError_t pad_inputs(const ChunkedArgs& a, int Fp, int64_t n_state, const FPad& w, ChunkedArgs& ap, hipStream_t s) {
+  const int64_t F = a.F, d = a.d, dv = a.dv;
+  hipError_t e = pad_rows(w.anchors, static_cast<const uint16_t*>(a.anchors), a.n_draw_sets, F, Fp, d,
+                          a.draw_set_stride, (int64_t)Fp * d, s);
+  if (e == hipSuccess)
+    e = pad_rows(w.prf, static_cast<const uint16_t*>(a.prf), a.n_draw_sets, F, Fp, d, a.draw_set_stride,
+                 (int64_t)Fp * d, s);
+  if (e == hipSuccess && a.S0) e = pad_rows(w.S0, a.S0, n_state, F, Fp, dv, F * dv, (int64_t)Fp * dv, s);
+  if (e == hipSuccess && a.z0) e = pad_rows(w.z0, a.z0, n_state, F, Fp, 1, F, Fp, s);
+  if (e != hipSuccess) return e;
+  ap = a;
+  ap.F = Fp;
+  ap.anchors = w.anchors;
+  ap.prf = w.prf;
+  ap.draw_set_stride = (int64_t)Fp * d;
+  ap.S0 = a.S0 ? w.S0 : nullptr;
+  ap.z0 = a.z0 ? w.z0 : nullptr;
+  ap.S_out = a.S_out ? w.S_out : nullptr;
+  ap.z_out = a.z_out ? w.z_out : nullptr;
+  return hipSuccess;
+}
+
+hipError_t pad_outputs(const ChunkedArgs& a, int Fp, int64_t n_state, const FPad& w, hipStream_t s) {
+  const int64_t F = a.F, dv = a.dv;
+  hipError_t e = hipSuccess;
+  if (a.S_out) e = pad_rows(a.S_out, w.S_out, n_state, F, F, dv, (int64_t)Fp * dv, F * dv, s);
+  if (e == hipSuccess && a.z_out) e = pad_rows(a.z_out, w.z_out, n_state, F, F, 1, Fp, F, s);
+  return e;
+}
+
+size_t varlen_bytes_exact(const VarlenArgs& a) {
+  return vl_ws(a, vl_g_max(a.c.L, a.n_seqs, vl_seg_len(a.c.n_heads, a.c.L)), nullptr).bytes;
+}
+
+hipError_t launch_varlen_exact(const VarlenArgs& a, hipStream_t s);
+
+}  // namespace
+
 bool varlen_supported(const VarlenArgs& a) {
-  return a.c.io_bf16 && a.c.d == 64 && a.c.dv == 64 && a.c.F == CfgF256::F && a.c.m % 32 == 0;
+  // F <= 256 (below 256 on zero-padded features); m % 32 == 0 keeps a wave's two feature blocks on one node
+  return a.c.io_bf16 && a.c.d == 64 && a.c.dv == 64 && a.c.F <= CfgF256::F && a.c.m % 32 == 0;
 }
 
 size_t varlen_workspace_bytes(const VarlenArgs& a) {
   if (a.c.n_heads == 0 || a.n_seqs == 0) return 0;
-  return vl_ws(a, vl_g_max(a.c.L, a.n_seqs, vl_seg_len(a.c.n_heads, a.c.L)), nullptr).bytes;
+  if (a.c.F == CfgF256::F) return varlen_bytes_exact(a);
+  VarlenArgs ap = a;
+  ap.c.F = CfgF256::F;
+  return align256(varlen_bytes_exact(ap)) + fpad_ws(a.c, CfgF256::F, (int64_t)a.n_seqs * a.c.n_heads, nullptr).bytes;
 }
 
 hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s) {
+  if (a.c.F == CfgF256::F || a.c.n_heads == 0 || a.n_seqs == 0) return launch_varlen_exact(a, s);
+  VarlenArgs ap = a;
+  ap.c.F = CfgF256::F;
+  const int64_t n_state = (int64_t)a.n_seqs * a.c.n_heads;
+  const FPad w = fpad_ws(a.c, CfgF256::F, n_state, static_cast<char*>(a.c.ws) + align256(varlen_bytes_exact(ap)));
+  hipError_t e = pad_inputs(a.c, CfgF256::F, n_state, w, ap.c, s);
+  if (e != hipSuccess) return e;
+  e = launch_varlen_exact(ap, s);
+  if (e != hipSuccess) return e;
+  return pad_outputs(a.c, CfgF256::F, n_state, w, s);
+}
+
+namespace {
+
+hipError_t launch_varlen_exact(const VarlenArgs& a, hipStream_t s) {
   using K = CfgF256;
   using KS = typename MainPass<K>::type;
   const int64_t H = a.c.n_heads, T = a.c.L;
@@ -1592,6 +1700,8 @@ hipError_t launch_varlen(const VarlenArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+}  // namespace
+
 int fused_segment_count(const ChunkedArgs& a, int64_t* seg_len) {
   int n = 0;
   dispatch(a, [&](auto k) {
@@ -1608,18 +1718,41 @@ hipError_t launch_segment_prefix(const ChunkedArgs& a, float* ws, hipStream_t s)
   return e;
 }
 
-bool fused_supported(const ChunkedArgs& a) {
-  return dispatch(a, [](auto) {});
-}
+bool fused_supported(const ChunkedArgs& a) { return fused_target_F(a) != 0; }
 
-size_t fused_workspace_bytes(const ChunkedArgs& a) {
+namespace {
+
+size_t fused_bytes_exact(const ChunkedArgs& a) {
   size_t r = 0;
   dispatch(a, [&](auto k) { r = a.causal ? ws_bytes_t<decltype(k)>(a) : ws_bytes_nc_t<decltype(k)>(a); });
   return r;
 }
 
+}  // namespace
+
+size_t fused_workspace_bytes(const ChunkedArgs& a) {
+  const int Fp = fused_target_F(a);
+  if (Fp == 0) return 0;
+  if (Fp == a.F) return fused_bytes_exact(a);
+  ChunkedArgs ap = a;
+  ap.F = Fp;
+  return align256(fused_bytes_exact(ap)) + fpad_ws(a, Fp, a.n_heads, nullptr).bytes;
+}
+
 hipError_t launch_fused(const ChunkedArgs& a, hipStream_t s) {
   if (a.n_heads == 0) return hipSuccess;
+  const int Fp = fused_target_F(a);
+  if (Fp != a.F) {  // zero-padded features
+    if (a.causal && a.L == 0) return launch_generic(a, s);  // only the state passes through
+    ChunkedArgs ap = a;
+    ap.F = Fp;
+    const FPad w = fpad_ws(a, Fp, a.n_heads, static_cast<char*>(a.ws) + align256(fused_bytes_exact(ap)));
+    hipError_t e = pad_inputs(a, Fp, a.n_heads, w, ap, s);
+    if (e != hipSuccess) return e;
+    e = launch_fused(ap, s);
+    if (e != hipSuccess) return e;
+    return pad_outputs(a, Fp, a.n_heads, w, s);
+  }
   hipError_t e = hipErrorInvalidValue;
   if (!a.causal) {
     dispatch(a, [&](auto k) { e = launch_nc_t<decltype(k)>(a, s); });

@@ -386,6 +386,44 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+
+// dst[b][r][:] = src[b][r][:] for r < rows_src and 0 for rows_src <= r < rows_dst.
+template <typename T>
+__global__ __launch_bounds__(256) void pad_rows_kernel(T* __restrict__ dst, const T* __restrict__ src,
+                                                       int64_t n_blocks, int64_t rows_src, int64_t rows_dst,
+                                                       int64_t row_elems, int64_t src_stride, int64_t dst_stride) {
+  const int64_t per = rows_dst * row_elems;
+  const int64_t total = n_blocks * per;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t b = i / per, rem = i - b * per, r = rem / row_elems, e = rem - r * row_elems;
+    dst[b * dst_stride + r * row_elems + e] = r < rows_src ? src[b * src_stride + r * row_elems + e] : T(0);
+  }
+}
+
+template <typename T>
+hipError_t pad_rows_t(T* dst, const T* src, int64_t n_blocks, int64_t rows_src, int64_t rows_dst, int64_t row_elems,
+                      int64_t src_stride, int64_t dst_stride, hipStream_t s) {
+  const int64_t total = n_blocks * rows_dst * row_elems;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(pad_rows_kernel<T>, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s, dst, src,
+                     n_blocks, rows_src, rows_dst, row_elems, src_stride, dst_stride);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t pad_rows(uint16_t* dst, const uint16_t* src, int64_t n_blocks, int64_t rows_src, int64_t rows_dst,
+                    int64_t row_elems, int64_t src_stride, int64_t dst_stride, hipStream_t s) {
+  return pad_rows_t(dst, src, n_blocks, rows_src, rows_dst, row_elems, src_stride, dst_stride, s);
+}
+
+hipError_t pad_rows(float* dst, const float* src, int64_t n_blocks, int64_t rows_src, int64_t rows_dst,
+                    int64_t row_elems, int64_t src_stride, int64_t dst_stride, hipStream_t s) {
+  return pad_rows_t(dst, src, n_blocks, rows_src, rows_dst, row_elems, src_stride, dst_stride, s);
+}
+
 bool generic_supported(const ChunkedArgs& a) {
   return featmap_supported(a.d) && a.F % 16 == 0 && a.m % 16 == 0 && a.chunk >= 1 && a.chunk <= 128 &&
          a.dv >= 1 && a.dv <= 1024;

@@ -80,6 +80,15 @@ bool generic_supported(const ChunkedArgs& a);
 size_t generic_workspace_bytes(const ChunkedArgs& a);
 hipError_t launch_generic(const ChunkedArgs& a, hipStream_t s);
 
+// Zero-padded copies of row blocks on the stream: dst[b][r][:] = src[b][r][:]
+// for r < rows_src, 0 for rows_src <= r < rows_dst (row_elems elements per
+// row; strides in elements).  Feature counts the MFMA kernels are not built
+// for run a larger count's kernels on zero-padded draws and states.
+hipError_t pad_rows(uint16_t* dst, const uint16_t* src, int64_t n_blocks, int64_t rows_src, int64_t rows_dst,
+                    int64_t row_elems, int64_t src_stride, int64_t dst_stride, hipStream_t s);
+hipError_t pad_rows(float* dst, const float* src, int64_t n_blocks, int64_t rows_src, int64_t rows_dst,
+                    int64_t row_elems, int64_t src_stride, int64_t dst_stride, hipStream_t s);
+
 // Prefix scan of per-item states (shared by both paths).
 // layout 0: plain [F][dv+1] (z in column dv); layout 1: MFMA fragment order
 // with dv+16 columns (z in column dv), see slay_chunked_fused.hip.

@@ -273,7 +273,8 @@ def test_varlen_validation_and_workspace(lib):
     assert _vl(lib, p, dv=0) == E_INV
     assert _vl(lib, p, dt=_lib.SLAY_F32) == E_UNS
     assert _vl(lib, p, dv=128) == E_UNS and b"variable-length" in lib.slay_last_error()
-    assert _vl(lib, _params(R=3, m=32)) == E_UNS
+    assert _vl(lib, _params(R=4, m=16)) == E_UNS  # m must be a multiple of 32
+    assert _vl(lib, _params(R=5, m=64)) == E_UNS  # R*m above 256
     assert _vl(lib, p, cu=None) == E_INV
     for name in ("q", "k", "v", "o"):
         assert _vl(lib, p, **{name: None}) == E_INV, name
@@ -289,3 +290,9 @@ def test_varlen_validation_and_workspace(lib):
     # nothing to do
     assert _vl(lib, p, n=0) == _lib.SLAY_OK and _vl(lib, p, H=0) == _lib.SLAY_OK
     assert lib.slay_attn_varlen_fwd_workspace_size(ctypes.byref(p), 0, 16, 0, 64, _lib.SLAY_BF16) == 0
+    # R*m = 96 runs the F = 256 kernels on zero-padded features: the F = 256
+    # workspace, then the padded draws (two [1][256][64] bf16) and the padded
+    # initial and final states ([4*16][256][64] and [4*16][256] fp32, twice)
+    p96 = _params(R=3, m=32)
+    n96 = lib.slay_attn_varlen_fwd_workspace_size(ctypes.byref(p96), 4, 16, 16384, 64, _lib.SLAY_BF16)
+    assert n96 == r(n) + 2 * r(256 * 64 * 2) + 2 * (r(64 * 256 * 64 * 4) + r(64 * 256 * 4))

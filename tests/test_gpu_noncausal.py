@@ -103,6 +103,30 @@ def test_noncausal_initial_state_and_split(lib, orc):
         assert headnorm_rel(to_np(S), rS) < TOL[w.dtype]
 
 
+@pytest.mark.parametrize("R,m,per_head", [(5, 16, False), (7, 32, True)])
+def test_noncausal_padded_features(lib, orc, R, m, per_head):
+    """F = 80 and F = 224 on zero-padded features, with an initial state and the final state out."""
+    w = ss.WORKLOADS["h16_l16k_bf16"].with_(B=1, H=2, R=R, m=m)
+    _say(f"noncausal padded F={w.F} per_head={per_head}")
+    q, k, v = _inputs(w, 300, 900)
+    if per_head:
+        draws = [ss.make_draws(w, seed=[3, 60 + h]) for h in range(w.H)]
+        A, G = np.stack([a for a, _ in draws]), np.stack([g for _, g in draws])
+    else:
+        A, G = ss.make_draws(w)
+    rng = np.random.default_rng(12)
+    S0 = np.abs(rng.standard_normal((w.H, w.F, w.dv))).astype(np.float32)
+    z0 = (rng.random((w.H, w.F)) + 0.5).astype(np.float32)
+    o, S, z = _run(lib, w, q, k, v, A, G, S0=S0, z0=z0, state=True)
+    ro, rS, rz = orc.slay_noncausal(q, k, v, A, G, w.eps, w.R, w.m, S0=S0, z0=z0, per_head_draws=per_head)
+    err = rownorm_rel(o, ro)
+    s_err = headnorm_rel(S.reshape(w.H, -1), rS.reshape(w.H, -1))
+    z_err = headnorm_rel(z.reshape(w.H, -1), rz.reshape(w.H, -1))
+    _say(f"  o rownorm {err:.3e}; S {s_err:.3e} z {z_err:.3e}")
+    assert S.shape == (w.H, w.F, w.dv)
+    assert err < TOL["bf16"] and s_err < TOL["bf16"] and z_err < TOL["bf16"]
+
+
 def test_noncausal_edge_cases(lib, orc):
     import torch
     from kernelized_linear_attention_amd import _lib

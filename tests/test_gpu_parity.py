@@ -144,6 +144,45 @@ def test_wide_parity(lib, orc, d, dv, R, m, H, L):
     np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], rtol=TOL["bf16"], atol=TOL["bf16"])  # o_1 = v_1
 
 
+@pytest.mark.parametrize("R,m,per_head", [
+    (2, 16, False),   # F = 32 on the F = 64 kernels
+    (3, 16, True),    # F = 48 -> 64, one draw set per head
+    (5, 16, False),   # F = 80 -> 96
+    (1, 128, False),  # F = 128, built: no padding
+    (5, 32, True),    # F = 160 -> 256
+    (7, 32, False),   # F = 224 -> 256
+])
+def test_fused_padded_features(lib, orc, R, m, per_head):
+    """Feature counts the fused kernels are not built for run on zero-padded
+    features; the state handoff is at the caller's F (S_out aliasing S0 too)."""
+    import torch
+
+    w = ss.WORKLOADS["h16_l16k_bf16"].with_(H=2, L=700, R=R, m=m)
+    _say(f"fused padded F={w.F} per_head={per_head}")
+    q, k, v = ss.make_qkv(w)
+    if per_head:
+        draws = [ss.make_draws(w, seed=[3, 80 + h]) for h in range(w.B * w.H)]
+        A, G = np.stack([a for a, _ in draws]), np.stack([g for _, g in draws])
+    else:
+        A, G = ss.make_draws(w)
+    cut = 333
+    o1, S1, z1 = _run_fwd(lib, w, q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], A, G, state=True)
+    assert S1.shape == (w.B * w.H, w.F, w.dv) and z1.shape == (w.B * w.H, w.F)
+    fm = _fm(lib, w, A, G)
+    S = torch.from_numpy(np.float32(S1)).cuda()
+    z = torch.from_numpy(np.float32(z1)).cuda()
+    o2 = lib.chunked_fwd(fm, to_dev(q[:, :, cut:], w.dtype), to_dev(k[:, :, cut:], w.dtype),
+                         to_dev(v[:, :, cut:], w.dtype), 64, S0=S, z0=z, S_out=S, z_out=z, return_state=True)[0]
+    torch.cuda.synchronize()
+    ro, rS, rz = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m, form="recurrent", per_head_draws=per_head)
+    err = rownorm_rel(np.concatenate([o1, to_np(o2)], axis=2), ro)
+    S2, z2 = to_np(S), to_np(z)
+    s_err = rownorm_rel(S2.reshape(-1, w.dv), rS.reshape(-1, w.dv))
+    z_err = float(np.max(np.abs(z2 - rz) / rz))
+    _say(f"  o rownorm rel err {err:.3e}; S {s_err:.3e} z {z_err:.3e}")
+    assert err < TOL["bf16"] and s_err < TOL["bf16"] and z_err < TOL["bf16"]
+
+
 def test_wide_initial_state_and_handoff(lib, orc):
     """Wide path: [0, L1) then [L1, L) with the state carried equals one pass."""
     w = ss.WORKLOADS["h8_l128k_d128_bf16"].with_(H=2, L=900)

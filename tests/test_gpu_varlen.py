@@ -161,7 +161,48 @@ def test_varlen_no_sequences_and_unsupported(lib):
     fm = lib.FeatureMap(to_dev(np.zeros((W.F, W.d)), "bf16"), to_dev(np.zeros((W.F, W.d)), "bf16"), W.R, W.m, W.eps)
     e = torch.empty(2, 0, W.d, dtype=torch.bfloat16, device="cuda")
     lib.varlen_fwd(fm, e, e, e, torch.zeros(1, dtype=torch.int64, device="cuda"))
-    fm96 = lib.FeatureMap(to_dev(np.zeros((96, W.d)), "bf16"), to_dev(np.zeros((96, W.d)), "bf16"), 3, 32, W.eps)
+    fm64 = lib.FeatureMap(to_dev(np.zeros((64, W.d)), "bf16"), to_dev(np.zeros((64, W.d)), "bf16"), 4, 16, W.eps)
     x = torch.zeros(1, 64, W.d, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(Exception, match="variable-length"):
-        lib.varlen_fwd(fm96, x, x, x, torch.tensor([0, 64], dtype=torch.int64, device="cuda"))
+    with pytest.raises(Exception, match="variable-length"):  # m = 16: a wave's feature blocks would span two nodes
+        lib.varlen_fwd(fm64, x, x, x, torch.tensor([0, 64], dtype=torch.int64, device="cuda"))
+
+
+@pytest.mark.parametrize("R,m,per_head", [(3, 32, False), (5, 32, True), (1, 32, False)])
+def test_varlen_padded_features(lib, orc, R, m, per_head):
+    """Feature counts below 256 run on zero-padded features: initial states in,
+    final states out at the caller's F, one draw set per head or shared."""
+    import torch
+
+    w = W.with_(R=R, m=m)
+    H, lengths = 2, [300, 0, 77, 1500, 64]
+    _say(f"varlen padded F={w.F} per_head={per_head}")
+    q, k, v, cu = _packed(H, lengths, [3, 75])
+    if per_head:
+        draws = [ss.make_draws(w, seed=[3, 90 + h]) for h in range(H)]
+        A, G = np.stack([a for a, _ in draws]), np.stack([g for _, g in draws])
+    else:
+        A, G = ss.make_draws(w)
+    rng = np.random.default_rng(8)
+    S0 = np.abs(rng.standard_normal((len(lengths), H, w.F, w.dv))).astype(np.float32)
+    z0 = (rng.random((len(lengths), H, w.F)) + 0.5).astype(np.float32)
+    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), R, m, w.eps)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    o, S, z = lib.varlen_fwd(fm, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                             torch.from_numpy(cu).cuda(), S0=f32(S0), z0=f32(z0), return_state=True)
+    torch.cuda.synchronize()
+    o, S, z = to_np(o), to_np(S), to_np(z)
+    assert S.shape == (len(lengths), H, w.F, w.dv) and z.shape == (len(lengths), H, w.F)
+    if per_head:  # the oracle takes one head's draws at a time
+        outs = [orc.slay_causal_varlen(q[h:h + 1], k[h:h + 1], v[h:h + 1], cu, A[h], G[h], w.eps, R, m,
+                                       S0=S0[:, h:h + 1], z0=z0[:, h:h + 1]) for h in range(H)]
+        ro = np.concatenate([x[0] for x in outs], axis=0)
+        rS = np.concatenate([x[1] for x in outs], axis=1)
+        rz = np.concatenate([x[2] for x in outs], axis=1)
+    else:
+        ro, rS, rz = orc.slay_causal_varlen(q, k, v, cu, A, G, w.eps, R, m, S0=S0, z0=z0)
+    err = rownorm_rel(o, ro)
+    s_err = headnorm_rel(S.reshape(-1, w.F * w.dv), rS.reshape(-1, w.F * w.dv))
+    z_err = headnorm_rel(z.reshape(-1, w.F), rz.reshape(-1, w.F))
+    _say(f"  o rownorm {err:.3e}; S {s_err:.3e} z {z_err:.3e}")
+    assert err < TOL["bf16"] and s_err < TOL["bf16"] and z_err < TOL["bf16"]
+    assert np.array_equal(S[1], S0[1]) and np.array_equal(z[1], z0[1])  # the empty sequence
