@@ -9,7 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
-#include <set>
+#include <map>
 #include <utility>
 #include <cstdarg>
 #include <cstdio>
@@ -593,12 +593,15 @@ hipError_t set_max_lds(const void* kernel, int bytes) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  // the largest limit set so far per (kernel, device): a kernel whose LDS
+  // size depends on the shape gets its limit raised when a call needs more
   static std::mutex mu;
-  static std::set<std::pair<const void*, int>> done;
+  static std::map<std::pair<const void*, int>, int> limit;
   std::lock_guard<std::mutex> lock(mu);
-  if (done.count({kernel, dev})) return hipSuccess;
+  const auto it = limit.find({kernel, dev});
+  if (it != limit.end() && it->second >= bytes) return hipSuccess;
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) done.insert({kernel, dev});
+  if (e == hipSuccess) limit[{kernel, dev}] = bytes;
   return e;
 }
 
