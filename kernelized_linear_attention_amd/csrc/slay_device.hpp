@@ -55,6 +55,11 @@ __device__ __forceinline__ uint32_t hi16_pair(uint32_t lo, uint32_t hi) { return
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8).  Vector loads and
+// stores retire in issue order and share this counter.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

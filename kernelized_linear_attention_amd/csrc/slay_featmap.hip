@@ -77,7 +77,9 @@ __global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 1) vo
   __shared__ float sinv[TR], slg[TR];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform, so the node constants below are scalar loads and no vector
+  // load of them is left for the tile loop to wait on
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int col = lane & 15;
   const int n_fblk = F / 16;
@@ -112,11 +114,18 @@ __global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 1) vo
       const int v = threadIdx.x * PER_T + i;
       const int r = v / VPR;
       const int c = (v - r * VPR) * VEC;
-      xr[i] = make_uint4(0, 0, 0, 0);
-      if (r < nr) xr[i] = *reinterpret_cast<const uint4*>(src + (int64_t)r * D + c);
+      // unconditional load of a row inside the tile (rows past its end repeat
+      // its last row; their features are never stored): a conditional load
+      // lets the compiler move work on the loaded value next to the load,
+      // which then waits on it at once
+      const int64_t rc = r < nr ? r : nr - 1;
+      xr[i] = *reinterpret_cast<const uint4*>(src + rc * D + c);
     }
   };
   if (bx < n_tiles) load_tile(bx);
+  // the tile loop below then starts with no load in flight, so its staging
+  // needs no wait on the counter that the stores also use
+  wait_vmem();
 
   for (int t = bx; t < n_tiles; t += gx) {
     const int h = t / tiles_per_head;
@@ -153,6 +162,10 @@ __global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 1) vo
           }
         }
       }
+      // wait here, where the reload is rare, so that the first MFMA of the
+      // tile does not wait for every load in flight (the next tile's prefetch
+      // included) to learn that P has arrived
+      wait_vmem();
     }
 
     // stage the x tile in LDS and compute 1/max(|x|, 1e-12) per row
@@ -223,6 +236,12 @@ __global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 1) vo
       }
     }
     __syncthreads();
+    // Loads and stores retire in issue order and share one counter, so the
+    // next tile's staging, which needs the prefetched rows, would otherwise
+    // also wait for every store issued below.  Waiting here (the prefetch was
+    // issued before the projection) leaves the stores to drain while the
+    // next tile is staged and computed.
+    wait_vmem();
     // coalesced write-out of the tile's feature slice: 16-byte pieces of each row
     {
       constexpr int PPR = FWS * (int)sizeof(TO) / 16;  // 16-byte pieces per row of the slice
