@@ -353,6 +353,11 @@ __global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
 
   PrefQ pf;
   load_q<K>(p, h * p.L + t_begin, (int)min<int64_t>(K::C, t_end - t_begin), tid, pf);
+  // Vector loads and stores retire in issue order and share one counter.  The
+  // step loop starts with no load in flight and waits for its prefetch once,
+  // before its own stores; a wait for the prefetch issued later would also
+  // wait for the previous step's stores.
+  wait_vmem();
   for (int64_t t0 = t_begin; t0 < t_end; t0 += K::C) {
     const int n = (int)min<int64_t>(K::C, t_end - t0);
     const int64_t row0 = h * p.L + t0;
@@ -396,6 +401,7 @@ __global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
       *pn = mfma_bf16(ld8(s.VT + (eb * 16 + c16) * K::LT + 8 * g), ld8(s.A + (ib * 16 + c16) * K::LA + 8 * g), *pn);
     }
     __syncthreads();
+    wait_vmem();  // the next chunk's prefetch, before this step's stores
     // [3] g' = [dout / den | -(dout . num) / den^2 | 0]: eight threads per token
     static_assert(K::NT >= K::C * 8, "one pass: thread t holds the dout piece of token t/8");
     if (tid < K::C * 8) {
@@ -524,6 +530,7 @@ __global__ __launch_bounds__(K::NT) void bwd_kv_kernel(BwdParams p) {
   auto rows_of = [&](int cs) { return (int)min<int64_t>(K::C, t_end - (t_begin + (int64_t)cs * K::C)); };
   PrefKV pf;
   load_kv<K>(p, h * p.L + t_begin + (int64_t)(n_steps - 1) * K::C, rows_of(n_steps - 1), tid, pf);
+  wait_vmem();  // as in bwd_q_kernel: no load in flight when the step loop starts
   for (int cs = n_steps - 1; cs >= 0; --cs) {
     const int64_t t0 = t_begin + (int64_t)cs * K::C;
     const int n = rows_of(cs);
@@ -585,6 +592,7 @@ __global__ __launch_bounds__(K::NT) void bwd_kv_kernel(BwdParams p) {
       }
     }
     __syncthreads();
+    wait_vmem();  // the next chunk's prefetch, before this step's stores
     // [2] dphi(K)^T += phi(Q)^T D; dV^T += G^T A; U^T += G'^T phi(Q)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -689,15 +697,18 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   bf16x8 pa[2][2], pg[2][2], pt[2][K::D / 16];
   float c1[2], c0[2], sb[2];
   int set = -1;
-  // three tiles in flight: pf0 is the next tile to compute, pf1 and pf2 the two after it
-  VjpPref<K> pf0, pf1, pf2;
+  // The next tile's rows are loaded while this one is computed.  Vector loads
+  // and stores retire in issue order and share one counter, so the loop
+  // starts with no load in flight and waits for the prefetch once, before
+  // the tile's stores: a deeper prefetch (or one rotated through registers)
+  // would make each wait for it also wait for the stores issued since.
+  VjpPref<K> pf;
   const int64_t gs = gridDim.x;
   auto load_tile = [&](int64_t t, VjpPref<K>& dst) {
     if (t < n_tiles) vjp_load<K>(x, dphi, p.n_rows, t * K::RT, tid, wave, g, c16, dst);
   };
-  load_tile(blockIdx.x, pf0);
-  load_tile(blockIdx.x + gs, pf1);
-  load_tile(blockIdx.x + 2 * gs, pf2);
+  load_tile(blockIdx.x, pf);
+  wait_vmem();
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gs) {
     const int64_t r0 = tile * K::RT;
     const int tset = (int)((r0 / p.rows_per_head) % p.n_draw_sets);  // a tile never spans two draw sets
@@ -729,12 +740,11 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
         c0[j] = p.nc.c0[node];
         sb[j] = c1[j] * 0.6931471805599453f;  // sqrt(beta_r)
       }
+      wait_vmem();  // here, where the reload is rare, rather than at the first use
     }
     __syncthreads();  // the previous tile's readers of sX and sR are done
-    const VjpPref<K> cur = pf0;
-    pf0 = pf1;
-    pf1 = pf2;
-    load_tile(tile + 3 * gs, pf2);
+    const VjpPref<K> cur = pf;
+    load_tile(tile + gs, pf);
     if (tid < K::RT * 8) {  // x rows, and 1/|x| once per row (eight threads per row)
       *reinterpret_cast<uint4*>(sX + (tid >> 3) * K::LX + 8 * (tid & 7)) = cur.x;
       const uint32_t wds[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
@@ -789,6 +799,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
         *reinterpret_cast<f32x4*>(sR + (wave * K::RT + rb * 16 + c16) * K::LR + cb * 16 + 4 * g) = dX[cb];
     }
     __syncthreads();
+    wait_vmem();  // the next tile's prefetch, before this tile's stores
     if (tid < K::RT * 16) {  // 16 lanes per row, four columns each
       const int rr = tid >> 4, c = 4 * (tid & 15);
       const int64_t row = r0 + rr;

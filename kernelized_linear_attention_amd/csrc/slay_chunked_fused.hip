@@ -1119,13 +1119,19 @@ __global__ __launch_bounds__(K::NT) void ncout_kernel(Params p) {
     const int b = c & 1;
     const int64_t row0 = head * p.Lq + t0 + (int64_t)c * K::C;
     const int n = (int)min<int64_t>(K::C, t1 - (t0 + (int64_t)c * K::C));
+    // Vector loads and stores retire in issue order and share one counter:
+    // the rows of chunk c+2 (loaded before the previous chunk's feature map)
+    // are waited for here, before this chunk's output stores, so that their
+    // staging below does not also wait for those stores.
+    wait_vmem();
     for (int t = wave; t < 2 * K::NTB; t += K::NW) {  // wave-uniform task loop
       if (t & 1) nc_task<K, 1>(p, row0, n, t >> 1, sPq(b), sSt, so, lane);
       else nc_task<K, 0>(p, row0, n, t >> 1, sPq(b), sSt, so, lane);
     }
-    if (c + 1 < nch) phase_q<K>(sQ(b ^ 1), sInv(b ^ 1), sInv(b ^ 1) + K::C, sPq(b ^ 1), wave, lane, pa, pg, c1, c0);
-    store_x<K>(threadIdx.x, pf.q, sQ(b), sInv(b), sInv(b) + K::C);  // chunk c+2 (a repeat past the end)
+    // chunk c+2 into the x buffer chunk c used (phase_q below reads the other)
+    store_x<K>(threadIdx.x, pf.q, sQ(b), sInv(b), sInv(b) + K::C);  // a repeat past the end
     load_chunk(c + 3);
+    if (c + 1 < nch) phase_q<K>(sQ(b ^ 1), sInv(b ^ 1), sInv(b ^ 1) + K::C, sPq(b ^ 1), wave, lane, pa, pg, c1, c0);
     __syncthreads();
   }
 }

@@ -117,34 +117,42 @@ struct WPref {
 // at or beyond `n` read as zero (the ragged tail of a sequence).
 template <class K, bool WANT_Q>
 __device__ __forceinline__ void w_load(const WParams& p, int64_t row0, int n, int tid, WPref<K>& pf) {
+  // Each address is a wave-uniform row base plus one 32-bit lane offset in
+  // bytes (the same offset for the four rows of a thread), so the loads take
+  // the scalar-base form and few registers hold addresses.
   const uint4 z4 = {0u, 0u, 0u, 0u};
   if constexpr (WANT_Q) {
+    // piece u of thread tid is 8 elements at row-major offset 8 (tid + u NT)
+    const char* base = reinterpret_cast<const char*>(p.phiq + row0 * K::F);
+    const uint32_t off = 16u * (uint32_t)tid;
 #pragma unroll
     for (int u = 0; u < K::QPT; ++u) {
-      const int piece = tid + u * K::NT;
-      const int r = piece / (K::F / 8), c8 = piece % (K::F / 8);
+      const int r = (tid + u * K::NT) / (K::F / 8);
       pf.q[u] = z4;
-      if (r < n) pf.q[u] = *reinterpret_cast<const uint4*>(p.phiq + (row0 + r) * K::F + 8 * c8);
+      if (r < n) pf.q[u] = *reinterpret_cast<const uint4*>(base + (size_t)u * K::NT * 16 + off);
     }
   }
   if (tid < K::F) {
     const int r4 = tid % 8, c8 = tid / 8;
+    const uint32_t off = 2u * (uint32_t)(4 * r4 * K::F + 8 * c8);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int r = 4 * r4 + x;
+      const char* base = reinterpret_cast<const char*>(p.phik + (row0 + x) * K::F);
       pf.k[x] = z4;
-      if (r < n) pf.k[x] = *reinterpret_cast<const uint4*>(p.phik + (row0 + r) * K::F + 8 * c8);
+      if (4 * r4 + x < n) pf.k[x] = *reinterpret_cast<const uint4*>(base + off);
     }
   }
   if (tid < 4 * K::DV) {
     const int r4 = tid / (K::DV / 2), c2 = tid % (K::DV / 2);
+    const uint32_t off = 2u * (uint32_t)(4 * r4 * K::DV + 2 * c2);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int r = 4 * r4 + x;
+      const char* base = reinterpret_cast<const char*>(p.v + (row0 + x) * K::DV);
       pf.v[x] = 0u;
-      if (r < n) pf.v[x] = *reinterpret_cast<const uint32_t*>(p.v + (row0 + r) * K::DV + 2 * c2);
+      if (4 * r4 + x < n) pf.v[x] = *reinterpret_cast<const uint32_t*>(base + off);
     }
   }
+
 }
 
 // Write a chunk to LDS: phi(q), phi(k) as rows (when ROWS), phi(k)^T and v^T
@@ -452,6 +460,10 @@ __global__ __launch_bounds__(K::NT) void wout_kernel(WParams p) {
     else if (fs == 1)
       w_finish<K, 1>(sP, sA, sDen, sO, cg, fs, lane, num[1], bv);
     if (more) w_store<K, true>(sQ, sK, sKt, sVt, tid, pf);
+    // Loads and stores retire in issue order and share one counter: with the
+    // prefetch known complete here, the next chunk's prefetch does not wait
+    // for the output stores below.
+    wait_vmem();
     __syncthreads();
     // whole output rows of the chunk, 16 bytes per thread (read before the
     // next chunk's phase 2 writes the staging rows again)
