@@ -1335,6 +1335,7 @@ hipError_t launch_nc_t(const ChunkedArgs& a, hipStream_t s) {
     sa.n_items = p.p1_items;
     sa.n_terms = p.p1_segs;
     sa.layout = 1;
+    sa.total_only = true;  // the output pass reads only the total (the last item)
   } else {  // no keys: the state is S0/z0 (the output pass reads them directly)
     p.p1_items = 1;
     sa.states = nullptr;

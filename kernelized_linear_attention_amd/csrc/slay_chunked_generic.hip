@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kGThreads) void scan_kernel(ScanArgs a, int64_t E) 
     for (int b = 0; b < kBatch; ++b) d[b] = (i0 + b < a.n_terms) ? st[(i0 + b) * step] : 0.f;
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      if (i0 + b < a.n_items) st[(i0 + b) * step] = run;
+      if (i0 + b < a.n_items && (!a.total_only || i0 + b == a.n_items - 1)) st[(i0 + b) * step] = run;
       run += d[b];
     }
   }

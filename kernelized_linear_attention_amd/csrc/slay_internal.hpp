@@ -103,6 +103,7 @@ struct ScanArgs {
   float* S_out;       // nullable: init + sum of all n_terms items
   float* z_out;
   bool reverse;       // suffix instead of prefix: item i <- init + sum_{i' > i} item i' (n_terms == n_items)
+  bool total_only;    // write only the last item (the total), not the prefixes before it
 };
 int64_t scan_state_elems(int F, int dv, int layout);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
