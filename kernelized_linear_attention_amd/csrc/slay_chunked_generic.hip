@@ -48,15 +48,21 @@ __global__ __launch_bounds__(kGThreads) void scan_kernel(ScanArgs a, int64_t E) 
   if (idx >= E) return;
   int f, e;
   scan_map(idx, a.F, a.dv, a.layout, f, e);
+  // a reverse scan walks the items from the last one: item i at st[(n_items - 1 - i) * step]
+  const int64_t step = a.reverse ? -E : E;
+  float* st = a.states + h * a.n_items * E + idx + (a.reverse ? (a.n_items - 1) * E : 0);
+  if (e > a.dv) {
+    // padding column of the fragment layout: zero in every delta item, so every
+    // prefix is zero too; only the items no delta was written to are stored
+    for (int64_t i = a.n_terms; i < a.n_items; ++i) st[i * step] = 0.f;
+    return;
+  }
   float run = 0.f;
   if (e < a.dv) {
     if (a.S0) run = a.S0[(h * a.F + f) * a.dv + e];
   } else if (e == a.dv) {
     if (a.z0) run = a.z0[h * a.F + f];
   }
-  // a reverse scan walks the items from the last one: item i at st[(n_items - 1 - i) * step]
-  const int64_t step = a.reverse ? -E : E;
-  float* st = a.states + h * a.n_items * E + idx + (a.reverse ? (a.n_items - 1) * E : 0);
   // loads of a batch of items are issued together, then the running sums stored
   constexpr int kBatch = 16;
   for (int64_t i0 = 0; i0 < a.n_items; i0 += kBatch) {
