@@ -197,6 +197,31 @@ def test_wide_initial_state_and_handoff(lib, orc):
     assert np.max(np.abs(z2 - rz) / rz) < TOL["bf16"]
 
 
+def test_wide_per_head_draws_in_place(lib, orc):
+    """Wide path with one draw set per head, the state handed over in place (S_out aliases S0)."""
+    import torch
+
+    w = ss.WORKLOADS["h8_l128k_d128_bf16"].with_(H=3, L=700)
+    _say(f"wide per-head draws in place F={w.F} H={w.H} L={w.L}")
+    q, k, v = ss.make_qkv(w)
+    draws = [ss.make_draws(w, seed=[6, 70 + h]) for h in range(w.H)]
+    A, G = np.stack([a for a, _ in draws]), np.stack([g for _, g in draws])
+    cut = 288
+    o1, S1, z1 = _run_fwd(lib, w, q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], A, G, state=True)
+    fm = _fm(lib, w, A, G)
+    S = torch.from_numpy(np.float32(S1)).cuda()
+    z = torch.from_numpy(np.float32(z1)).cuda()
+    o2 = lib.chunked_fwd(fm, to_dev(q[:, :, cut:], w.dtype), to_dev(k[:, :, cut:], w.dtype),
+                         to_dev(v[:, :, cut:], w.dtype), w.chunk, S0=S, z0=z, S_out=S, z_out=z, return_state=True)[0]
+    torch.cuda.synchronize()
+    ro, rS, rz = orc.slay_causal(q, k, v, A, G, w.eps, w.R, w.m, form="recurrent", per_head_draws=True)
+    err = rownorm_rel(np.concatenate([o1, to_np(o2)], axis=2), ro)
+    s_err = rownorm_rel(to_np(S).reshape(-1, w.dv), rS.reshape(-1, w.dv))
+    z_err = float(np.max(np.abs(to_np(z) - rz) / rz))
+    _say(f"  o rownorm rel err {err:.3e}; S {s_err:.3e} z {z_err:.3e}")
+    assert err < TOL["bf16"] and s_err < TOL["bf16"] and z_err < TOL["bf16"]
+
+
 def test_chunked_initial_state_and_handoff(lib, orc):
     """Running [0, L1) then [L1, L) with the state carried equals one pass; S_out may alias S0."""
     import torch
@@ -357,6 +382,33 @@ def test_decode_parity(lib, orc, n_heads, steps):
     assert s_err < TOL["f32"]
     assert z_err < TOL["f32"]
     np.testing.assert_allclose(got[:, 0], v[:, 0], rtol=1e-5, atol=1e-5)  # first step from zero state returns v
+
+
+def test_decode_per_head_draws(lib, orc):
+    """Decode with draw sets shared by head groups: head h uses set h % 3."""
+    import torch
+
+    w = ss.WORKLOADS["decode_256x16_f32"]
+    n_heads, steps, n_sets = 48, 16, 3
+    _say(f"decode per-head draws heads={n_heads} steps={steps} sets={n_sets}")
+    draws = [ss.make_draws(w, seed=[5, 40 + i]) for i in range(n_sets)]
+    A, G = np.stack([a for a, _ in draws]), np.stack([g for _, g in draws])
+    q, k, v = _decode_inputs(w, n_heads, steps)
+    fm = _fm(lib, w, A, G)
+    S = torch.zeros(n_heads, w.F, w.dv, device="cuda")
+    z = torch.zeros(n_heads, w.F, device="cuda")
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    outs = torch.empty(n_heads, steps, w.dv, device="cuda")
+    for t in range(steps):
+        outs[:, t] = lib.recurrent_step(fm, qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(), S, z)
+    torch.cuda.synchronize()
+    Ah = np.stack([A[h % n_sets] for h in range(n_heads)])
+    Gh = np.stack([G[h % n_sets] for h in range(n_heads)])
+    ro, rS, rz = orc.slay_causal(q, k, v, Ah, Gh, w.eps, w.R, w.m, form="recurrent", per_head_draws=True)
+    err = rownorm_rel(to_np(outs), ro)
+    s_err, z_err = headnorm_rel(to_np(S), rS), headnorm_rel(to_np(z), rz)
+    _say(f"  o rownorm rel err {err:.3e}; S {s_err:.3e}; z {z_err:.3e}")
+    assert err < TOL["f32"] and s_err < TOL["f32"] and z_err < TOL["f32"]
 
 
 def test_decode_continues_prefill(lib, orc):
