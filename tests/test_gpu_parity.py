@@ -127,6 +127,9 @@ def test_chunked_parity(lib, orc, name, L, chunk):
     (128, 64, 2, 64, 3, 77),      # F = 128, dv = 64 (four feature slices per column group)
     (32, 64, 4, 128, 1, 513),     # d = 32, F = 512, dv = 64
     (128, 128, 4, 128, 1, 20),    # one segment, one partial chunk
+    (64, 128, 2, 64, 2, 451),     # F = 128, dv = 128
+    (32, 128, 4, 64, 2, 390),     # F = 256, dv = 128
+    (128, 64, 3, 128, 2, 333),    # F = 384, dv = 64
 ])
 def test_wide_parity(lib, orc, d, dv, R, m, H, L):
     """The wide MFMA path (feature maps written once in bf16, state kept on chip per segment)."""
