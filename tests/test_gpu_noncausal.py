@@ -103,9 +103,10 @@ def test_noncausal_initial_state_and_split(lib, orc):
         assert headnorm_rel(to_np(S), rS) < TOL[w.dtype]
 
 
-@pytest.mark.parametrize("R,m,per_head", [(5, 16, False), (7, 32, True)])
+@pytest.mark.parametrize("R,m,per_head", [(5, 16, False), (7, 32, True), (4, 16, False), (2, 64, True)])
 def test_noncausal_padded_features(lib, orc, R, m, per_head):
-    """F = 80 and F = 224 on zero-padded features, with an initial state and the final state out."""
+    """F = 80 and F = 224 on zero-padded features, F = 64 and F = 128 on their own kernels, with an
+    initial state and the final state out."""
     w = ss.WORKLOADS["h16_l16k_bf16"].with_(B=1, H=2, R=R, m=m)
     _say(f"noncausal padded F={w.F} per_head={per_head}")
     q, k, v = _inputs(w, 300, 900)
