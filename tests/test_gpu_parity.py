@@ -59,6 +59,42 @@ def test_featmap_parity(lib, orc, name, out):
     assert np.all(got > 0)  # strictly positive features
 
 
+@pytest.mark.parametrize("base,d,R,m,out", [
+    ("h16_l16k_bf16", 64, 4, 64, "bf16"),        # bf16 -> bf16, d = 64 (the forward's and backward's map)
+    ("h16_l16k_bf16", 32, 4, 64, "bf16"),        # d = 32, four feature blocks per wave
+    ("h8_l128k_d128_bf16", 128, 4, 128, "bf16"),  # d = 128, F = 512
+    ("h16_l16k_bf16", 64, 4, 64, "f32"),         # bf16 -> fp32
+    ("tiny_f32", 64, 4, 64, "f32"),              # fp32 -> fp32, d = 64
+    ("tiny_f32", 128, 4, 128, "f32"),            # fp32 -> fp32, d = 128
+])
+def test_featmap_large_launches(lib, orc, base, d, R, m, out):
+    """Launches past the small-launch size (64-row tiles walked by each workgroup), ragged last tile."""
+    import torch
+
+    w = ss.WORKLOADS[base].with_(B=1, H=1, L=40961, d=d, R=R, m=m)
+    _say(f"featmap large launch {w.dtype} -> {out} d={d} F={w.F} rows={w.L}")
+    q, _, _ = ss.make_qkv(w)
+    A, G = ss.make_draws(w)
+    fm = _fm(lib, w, A, G)
+    x = q.reshape(-1, w.d)
+    phi = lib.featmap(fm, to_dev(x, w.dtype), torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    ref = orc.featmap(x, A, G, w.eps, w.R, w.m)
+    got = to_np(phi)
+    err = rownorm_rel(got, ref)
+    _say(f"  rownorm rel err {err:.3e}")
+    assert err < (TOL["bf16"] if out == "bf16" else 1e-4)
+    # Positive up to rounding: where |a.xh| is below what the fp32 sum of the
+    # bf16 products resolves (about |a| 2^-24), the anchor factor, and with it
+    # phi, can come out exactly 0; the true value there is negligible in its row.
+    assert np.all(got >= 0)
+    zero = got == 0
+    if zero.any():
+        rel = (ref / ref.max(axis=1, keepdims=True))[zero]
+        _say(f"  {int(zero.sum())} exact zeros of {got.size}, oracle there <= {rel.max():.1e} of its row's largest")
+        assert rel.max() < 1e-12
+
+
 def test_featmap_per_head_draws(lib, orc):
     import torch
 
