@@ -132,9 +132,10 @@ def test_noncausal_edge_cases(lib, orc):
     import torch
     from kernelized_linear_attention_amd import _lib
 
-    for name in ("tiny_f32", "h16_l16k_bf16"):
-        w = ss.WORKLOADS[name].with_(H=2)
-        _say(f"noncausal edge cases {name}")
+    # the last case runs F = 80 on zero-padded features
+    for name, extra in (("tiny_f32", {}), ("h16_l16k_bf16", {}), ("h16_l16k_bf16", {"R": 5, "m": 16})):
+        w = ss.WORKLOADS[name].with_(H=2, **extra)
+        _say(f"noncausal edge cases {name} F={w.F}")
         q, k, v = _inputs(w, 130, 200)
         A, G = ss.make_draws(w)
         _, S1, z1 = orc.slay_noncausal(q, k, v, A, G, w.eps, w.R, w.m)

@@ -299,10 +299,11 @@ def test_chunked_chunk_size_invariance(lib):
         assert rownorm_rel(o, outs[0]) < 1e-5
 
 
-def test_chunked_edge_cases(lib):
+@pytest.mark.parametrize("R,m", [(4, 64), (5, 16)])  # F = 256, and F = 80 on zero-padded features
+def test_chunked_edge_cases(lib, R, m):
     import torch
 
-    w = ss.WORKLOADS["h16_l16k_bf16"].with_(H=2, L=64)
+    w = ss.WORKLOADS["h16_l16k_bf16"].with_(H=2, L=64, R=R, m=m)
     q, k, v = ss.make_qkv(w)
     A, G = ss.make_draws(w)
     fm = _fm(lib, w, A, G)
