@@ -39,17 +39,17 @@ def _packed(H, lengths, seed):
     return q[0, :, :T], k[0, :, :T], v[0, :, :T], cu
 
 
-def _states(n, H, seed):
+def _states(n, H, seed, w=W):
     rng = np.random.default_rng(seed)
-    S0 = np.abs(rng.standard_normal((n, H, W.F, W.dv))).astype(np.float32)
-    z0 = (rng.random((n, H, W.F)) + 0.5).astype(np.float32)
+    S0 = np.abs(rng.standard_normal((n, H, w.F, w.dv))).astype(np.float32)
+    z0 = (rng.random((n, H, w.F)) + 0.5).astype(np.float32)
     return S0, z0
 
 
-def _run(lib, q, k, v, cu, A, G, S0=None, z0=None, out=None):
+def _run(lib, q, k, v, cu, A, G, S0=None, z0=None, out=None, w=W):
     import torch
 
-    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), W.R, W.m, W.eps)
+    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), w.R, w.m, w.eps)
     f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
     o, S, z = lib.varlen_fwd(fm, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
                              torch.from_numpy(cu).cuda(), S0=f32(S0), z0=f32(z0), return_state=True, out=out)
@@ -139,18 +139,20 @@ def test_varlen_many_short_sequences(lib, orc):
     assert headnorm_rel(S.reshape(-1, W.F * W.dv), rS.reshape(-1, W.F * W.dv)) < TOL["bf16"]
 
 
-def test_varlen_bad_offsets_compute_nothing(lib):
+@pytest.mark.parametrize("R,m", [(4, 64), (3, 32)])  # F = 256, and F = 96 on zero-padded features
+def test_varlen_bad_offsets_compute_nothing(lib, R, m):
     """Offsets that decrease, or do not end at the token count, give no work:
     o keeps its contents and the final states are the initial ones."""
     import torch
 
+    w = W.with_(R=R, m=m)
     H = 2
     q, k, v, _ = _packed(H, [100, 100], [3, 74])
-    A, G = ss.make_draws(W)
-    S0, z0 = _states(2, H, 6)
+    A, G = ss.make_draws(w)
+    S0, z0 = _states(2, H, 6, w)
     for cu in (np.array([0, 150, 120], np.int64), np.array([0, 100, 150], np.int64)):
-        out = torch.full((H, 200, W.dv), 7.0, dtype=torch.bfloat16, device="cuda")
-        o, S, z = _run(lib, q, k, v, cu, A, G, S0, z0, out=out)
+        out = torch.full((H, 200, w.dv), 7.0, dtype=torch.bfloat16, device="cuda")
+        o, S, z = _run(lib, q, k, v, cu, A, G, S0, z0, out=out, w=w)
         assert np.all(o == 7.0)
         assert np.array_equal(S, np.float32(S0)) and np.array_equal(z, np.float32(z0))
 
