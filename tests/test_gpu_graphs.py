@@ -45,10 +45,11 @@ def _replay_matches(fn_graph, fn_eager, outs_graph, outs_eager, reps=3):
             assert torch.equal(a, b), rep
 
 
-def test_forward_graph(lib):
+@pytest.mark.parametrize("R,m", [(4, 64), (5, 32)])  # F = 256, and F = 160 on zero-padded features
+def test_forward_graph(lib, R, m):
     import torch
 
-    w = W.with_(H=4, L=2000)
+    w = W.with_(H=4, L=2000, R=R, m=m)
     q, k, v = (to_dev(x, "bf16") for x in ss.make_qkv(w))
     A, G = ss.make_draws(w)
     fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), w.R, w.m, w.eps)
@@ -61,6 +62,28 @@ def test_forward_graph(lib):
                                             z_out=zg),
                     lambda: lib.chunked_fwd(fm, q, k, v, 64, out=oe, workspace=ws, return_state=True, S_out=Se,
                                             z_out=ze),
+                    [og, Sg, zg], [oe, Se, ze])
+
+
+@pytest.mark.parametrize("R,m", [(4, 64), (5, 16)])  # F = 256, and F = 80 on zero-padded features
+def test_noncausal_graph(lib, R, m):
+    import torch
+
+    w = W.with_(H=3, L=1500, R=R, m=m)
+    q, k, v = (to_dev(x, "bf16") for x in ss.make_qkv(w))
+    qq = q[:, :, :700].contiguous()
+    A, G = ss.make_draws(w)
+    fm = lib.FeatureMap(to_dev(A, "bf16"), to_dev(G, "bf16"), w.R, w.m, w.eps)
+    ws = torch.empty(lib.noncausal_fwd_workspace_size(fm, 1, 3, 700, w.L, w.dv, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    og = torch.empty(1, 3, 700, w.dv, dtype=torch.bfloat16, device="cuda")
+    oe = torch.empty_like(og)
+    Sg, Se = (torch.empty(3, w.F, w.dv, device="cuda") for _ in range(2))
+    zg, ze = (torch.empty(3, w.F, device="cuda") for _ in range(2))
+    _replay_matches(lambda: lib.noncausal_fwd(fm, qq, k, v, out=og, workspace=ws, S_out=Sg, z_out=zg,
+                                              return_state=True),
+                    lambda: lib.noncausal_fwd(fm, qq, k, v, out=oe, workspace=ws, S_out=Se, z_out=ze,
+                                              return_state=True),
                     [og, Sg, zg], [oe, Se, ze])
 
 
