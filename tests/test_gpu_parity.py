@@ -166,6 +166,7 @@ def test_chunked_parity(lib, orc, name, L, chunk):
     (64, 128, 2, 64, 2, 451),     # F = 128, dv = 128
     (32, 128, 4, 64, 2, 390),     # F = 256, dv = 128
     (128, 64, 3, 128, 2, 333),    # F = 384, dv = 64
+    (64, 64, 16, 16, 2, 300),     # the most nodes, R = 16 (m = 16 keeps F = 256 off the fused kernels)
 ])
 def test_wide_parity(lib, orc, d, dv, R, m, H, L):
     """The wide MFMA path (feature maps written once in bf16, state kept on chip per segment)."""
