@@ -191,6 +191,7 @@ def test_wide_parity(lib, orc, d, dv, R, m, H, L):
     (1, 128, False),  # F = 128, built: no padding
     (5, 32, True),    # F = 160 -> 256
     (7, 32, False),   # F = 224 -> 256
+    (8, 32, True),    # F = 256, built: eight nodes, one per producer wave
 ])
 def test_fused_padded_features(lib, orc, R, m, per_head):
     """Feature counts the fused kernels are not built for run on zero-padded
