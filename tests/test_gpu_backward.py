@@ -104,10 +104,12 @@ def test_backward_parity(lib, orc, name, B, H, L, chunk, with_state):
     (1, 32, 1, 300),   # F = 32
     (2, 32, 3, 129),   # F = 64
     (7, 32, 1, 1000),  # F = 224
+    (8, 32, 2, 400),   # F = 256 itself with eight nodes (no padding)
 ])
 def test_backward_padded_features(lib, orc, R, m, H, L):
     """F < 256 runs the F = 256 MFMA kernels on zero-padded features: the
-    padding must change nothing, initial state and final-state gradient included."""
+    padding must change nothing, initial state and final-state gradient included
+    (the last case is F = 256 itself, with eight nodes)."""
     w = ss.WORKLOADS["b4h8_l2k_bf16"].with_(B=1, H=H, L=L, R=R, m=m)
     _say(f"backward padded features F={w.F} H={H} L={L}")
     q, k, v = ss.make_qkv(w)
