@@ -118,31 +118,67 @@ def make_draws(w: Workload, seed=None, orthogonal: bool = False):
     return _finish(a, w.dtype), _finish(g, w.dtype)
 
 
-def make_qkv(w: Workload, seed=None, near_pairs: float = 0.0):
+def make_qkv(w: Workload, seed=None, near_pairs=None, qk_scale=None, zero_k=()):
     """q, k [B, H, L, d] and v [B, H, L, dv] fp32 (bf16-exact for bf16 workloads).
 
-    near_pairs > 0 builds a stress set with large q.k: k = unit(q + near_pairs * noise).
+    The defaults give the workload recipe (q, k on the unit sphere).  Stress
+    options, each drawn from its own seeded stream so the default arrays do
+    not change:
+      near_pairs = (u_lo, u_hi): every k_i is rebuilt as u_i q_i + sqrt(1-u_i^2) e_i
+          with e_i a unit vector orthogonal to q_i and u_i ~ U(u_lo, u_hi), so
+          q_i . k_i = u_i (up to rounding) -- the high-alignment set;
+      qk_scale = (lo, hi): each q and k row is then multiplied by its own
+          log-uniform factor in [lo, hi] (rows off the unit sphere);
+      zero_k: token indices whose k rows are set to exactly zero.
     """
-    rng = np.random.default_rng([w.wid, 0] if seed is None else seed)
+    base = [w.wid, 0] if seed is None else seed
+    base = list(base) if isinstance(base, (list, tuple)) else [int(base)]
+    rng = np.random.default_rng(base)
     shp = (w.B, w.H, w.L)
     q = rng.standard_normal(shp + (w.d,), dtype=np.float32)
     k = rng.standard_normal(shp + (w.d,), dtype=np.float32)
     v = rng.standard_normal(shp + (w.dv,), dtype=np.float32)
     q = _unit_rows(q)
-    if near_pairs > 0:
-        k = q + np.float32(near_pairs) * k
+    if near_pairs is not None:
+        lo, hi = near_pairs
+        r2 = np.random.default_rng(base + [101])
+        u = r2.uniform(lo, hi, shp + (1,)).astype(np.float64)
+        q64 = q.astype(np.float64)
+        e = k.astype(np.float64)
+        e = e - np.sum(e * q64, axis=-1, keepdims=True) * q64
+        e = e / np.linalg.norm(e, axis=-1, keepdims=True)
+        k = (u * q64 + np.sqrt(1.0 - u * u) * e).astype(np.float32)
     k = _unit_rows(k)
+    if qk_scale is not None:
+        lo, hi = qk_scale
+        r3 = np.random.default_rng(base + [102])
+        sq = np.exp(r3.uniform(np.log(lo), np.log(hi), shp + (1,))).astype(np.float32)
+        sk = np.exp(r3.uniform(np.log(lo), np.log(hi), shp + (1,))).astype(np.float32)
+        q = q * sq
+        k = k * sk
+    if len(zero_k):
+        k[:, :, np.asarray(zero_k, dtype=np.int64)] = 0.0
     return _finish(q, w.dtype), _finish(k, w.dtype), _finish(v, w.dtype)
 
 
-def make_decode_step(w: Workload, t: int, n_heads: int | None = None):
-    """Single-token q, k [n_heads, d] and v [n_heads, dv] for decode step t (fp32)."""
+def make_decode_step(w: Workload, t: int, n_heads: int | None = None, qk_scale=None):
+    """Single-token q, k [n_heads, d] and v [n_heads, dv] for decode step t (fp32).
+
+    qk_scale = (lo, hi) multiplies each q and k row by its own log-uniform
+    factor in [lo, hi] (drawn from a separate stream; the default arrays are
+    unchanged)."""
     nh = w.n_heads if n_heads is None else n_heads
     rng = np.random.default_rng([w.wid, 2, int(t)])
     q = rng.standard_normal((nh, w.d), dtype=np.float32)
     k = rng.standard_normal((nh, w.d), dtype=np.float32)
     v = rng.standard_normal((nh, w.dv), dtype=np.float32)
-    return _finish(_unit_rows(q), w.dtype), _finish(_unit_rows(k), w.dtype), _finish(v, w.dtype)
+    q, k = _unit_rows(q), _unit_rows(k)
+    if qk_scale is not None:
+        lo, hi = qk_scale
+        r3 = np.random.default_rng([w.wid, 2, int(t), 102])
+        q = q * np.exp(r3.uniform(np.log(lo), np.log(hi), (nh, 1))).astype(np.float32)
+        k = k * np.exp(r3.uniform(np.log(lo), np.log(hi), (nh, 1))).astype(np.float32)
+    return _finish(q, w.dtype), _finish(k, w.dtype), _finish(v, w.dtype)
 
 
 def make_grads(w: Workload, seed=None):

@@ -19,15 +19,37 @@ def rownorm_rel(got, ref) -> float:
     return float(np.max(num / np.maximum(den, 1e-300)))
 
 
-def headnorm_rel(got, ref) -> float:
-    """Max over heads (leading axis) of the relative Frobenius error of one head's array.
+def rowfloor_rel(got, ref, heads: int = 1, floor_frac: float = 0.1) -> float:
+    """Per-row relative error with a floor: max over rows i of
+    |got_i - ref_i|_2 / max(|ref_i|_2, floor_frac * rms_i |ref_i|_2),
+    the rms taken over the rows of the same head (the leading `heads` rows
+    blocks of the flattened array, equal sizes).
 
-    Used for recurrent states after few tokens: a state row of feature f is
-    then a handful of phi_f values, whose fp32 relative error is unbounded
-    where (a.xh)^2 cancels (a nearly orthogonal to xh), so a per-row ratio is
-    ill-posed the same way an elementwise one is; the head's whole state is
-    the well-conditioned unit.
+    The gate for arrays whose rows can legitimately be tiny next to their
+    neighbours: rows of a state after few tokens (a feature row holds a
+    handful of phi values, each with the fp32 cancellation of (a.xh)^2 when a
+    is nearly orthogonal to xh), or rows of dq, dk (the projection
+    (I - xh xh^T) of a feature-space gradient nearly parallel to xh).  Such a
+    row is measured against a tenth of the head's typical row, while every
+    row of ordinary size -- and any row that is wholly wrong -- is held to the
+    full relative bar.
     """
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = got.shape[-1] if got.ndim > 1 else 1
+    g = got.reshape(heads, -1, d)
+    r = ref.reshape(heads, -1, d)
+    num = np.linalg.norm(g - r, axis=2)
+    den = np.linalg.norm(r, axis=2)
+    rms = np.sqrt(np.mean(den * den, axis=1, keepdims=True))
+    if num.size == 0:
+        return 0.0
+    return float(np.max(num / np.maximum(np.maximum(den, floor_frac * rms), 1e-300)))
+
+
+def headnorm_rel(got, ref) -> float:
+    """Max over heads (leading axis) of the relative Frobenius error of one head's array
+    (reported beside the per-row gate; not a gate by itself)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     g = got.reshape(got.shape[0], -1)
