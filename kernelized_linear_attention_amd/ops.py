@@ -45,6 +45,12 @@ def _need(t: torch.Tensor, name: str, shape=None, dtype=None) -> None:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def _need_d(t: torch.Tensor, name: str, d: int) -> None:
+    """The last axis of q/k/x must be the draws' d (the kernels read d columns per row)."""
+    if t.dim() < 1 or t.shape[-1] != d:
+        raise ValueError(f"{name} has last dimension {t.shape[-1] if t.dim() else None}, the draws have d = {d}")
+
+
 @dataclass
 class FeatureMap:
     """Anchor and PRF draws plus the Gauss-Laguerre mixture settings.
@@ -95,6 +101,7 @@ def featmap(fm: FeatureMap, x: torch.Tensor, out_dtype: torch.dtype | None = Non
             rows_per_head: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
     """phi(x) for rows x [..., d]; returns [..., R*m] in out_dtype (default x.dtype)."""
     lib = _lib.load()
+    _need_d(x, "x", fm.d)
     _need(x, "x")
     out_dtype = out_dtype or x.dtype
     n = x.numel() // fm.d
@@ -114,18 +121,14 @@ def chunked_fwd_workspace_size(fm: FeatureMap, B: int, H: int, L: int, dv: int, 
     return int(lib.slay_attn_chunked_fwd_workspace_size(fm.c_params(), B, H, L, dv, chunk, _dtype_code(dtype)))
 
 
-def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk: int,
-                S0: torch.Tensor | None = None, z0: torch.Tensor | None = None, return_state: bool = False,
-                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, S_out=None, z_out=None):
-    """Causal SLAY forward.  q, k [B, H, L, d]; v [B, H, L, dv] -> o [B, H, L, dv].
-
-    S0, z0: optional fp32 initial state [B*H, F, dv], [B*H, F].  With
-    return_state the final state (S, z) is returned as well.
-    """
-    lib = _lib.load()
-    B, H, L, d = q.shape
-    dv = v.shape[-1]
+def _fwd_outputs(fm: FeatureMap, q, k, v, S0, z0, return_state, out, S_out, z_out):
+    """Validate the causal forward's tensors and create the outputs the caller did not pass."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    _need_d(q, "q", fm.d)
     _need(q, "q")
+    B, H, L, _ = q.shape
+    dv = v.shape[-1]
     _need(k, "k", q.shape, q.dtype)
     _need(v, "v", (B, H, L, dv), q.dtype)
     if out is None:
@@ -139,9 +142,27 @@ def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
             S_out = torch.empty((B * H, fm.F, dv), dtype=torch.float32, device=q.device)
         if z_out is None:
             z_out = torch.empty((B * H, fm.F), dtype=torch.float32, device=q.device)
+    for t, name, shp in ((S_out, "S_out", (B * H, fm.F, dv)), (z_out, "z_out", (B * H, fm.F))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
+    return B, H, L, dv, out, S_out, z_out
+
+
+def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk: int,
+                S0: torch.Tensor | None = None, z0: torch.Tensor | None = None, return_state: bool = False,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, S_out=None, z_out=None):
+    """Causal SLAY forward.  q, k [B, H, L, d]; v [B, H, L, dv] -> o [B, H, L, dv].
+
+    S0, z0: optional fp32 initial state [B*H, F, dv], [B*H, F].  With
+    return_state the final state (S, z) is returned as well.
+    """
+    lib = _lib.load()
+    B, H, L, dv, out, S_out, z_out = _fwd_outputs(fm, q, k, v, S0, z0, return_state, out, S_out, z_out)
     nbytes = chunked_fwd_workspace_size(fm, B, H, L, dv, chunk, q.dtype)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.slay_attn_chunked_fwd(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype), B,
                                    H, L, dv, chunk, _ptr(S0), _ptr(z0), out.data_ptr(), _ptr(S_out), _ptr(z_out),
@@ -169,10 +190,13 @@ def varlen_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     with return_state the final states are returned as well.
     """
     lib = _lib.load()
-    H, T, d = q.shape
+    if q.dim() != 3:
+        raise ValueError("q must be [H, T, d]")
+    _need_d(q, "q", fm.d)
+    _need(q, "q")
+    H, T, _ = q.shape
     dv = v.shape[-1]
     n_seqs = cu_seqlens.numel() - 1
-    _need(q, "q")
     _need(k, "k", q.shape, q.dtype)
     _need(v, "v", (H, T, dv), q.dtype)
     _need(cu_seqlens, "cu_seqlens", None, torch.int64)
@@ -187,9 +211,14 @@ def varlen_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
             S_out = torch.empty((n_seqs, H, fm.F, dv), dtype=torch.float32, device=q.device)
         if z_out is None:
             z_out = torch.empty((n_seqs, H, fm.F), dtype=torch.float32, device=q.device)
+    for t, name, shp in ((S_out, "S_out", (n_seqs, H, fm.F, dv)), (z_out, "z_out", (n_seqs, H, fm.F))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
     nbytes = varlen_fwd_workspace_size(fm, n_seqs, H, T, dv, q.dtype)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.slay_attn_varlen_fwd(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype),
                                   n_seqs, H, cu_seqlens.data_ptr(), T, dv, _ptr(S0), _ptr(z0), out.data_ptr(),
@@ -214,9 +243,12 @@ def chunked_bwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     gradient of the final state dS_T [B*H, F, dv], dz_T [B*H, F]), returns
     (dq, dk, dv), plus (dS0, dz0) when state_grad is set."""
     lib = _lib.load()
-    B, H, L, d = q.shape
-    dvn = v.shape[-1]
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, L, d]")
+    _need_d(q, "q", fm.d)
     _need(q, "q")
+    B, H, L, _ = q.shape
+    dvn = v.shape[-1]
     _need(k, "k", q.shape, q.dtype)
     _need(v, "v", (B, H, L, dvn), q.dtype)
     _need(dout, "dout", (B, H, L, dvn), q.dtype)
@@ -235,9 +267,14 @@ def chunked_bwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
             dS0 = torch.empty((B * H, fm.F, dvn), dtype=torch.float32, device=q.device)
         if dz0 is None:
             dz0 = torch.empty((B * H, fm.F), dtype=torch.float32, device=q.device)
+    for t, name, shp in ((dS0, "dS0", (B * H, fm.F, dvn)), (dz0, "dz0", (B * H, fm.F))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
     nbytes = chunked_bwd_workspace_size(fm, B, H, L, dvn, chunk, q.dtype)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.slay_attn_chunked_bwd(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                                    _dtype_code(q.dtype), B, H, L, dvn, chunk, _ptr(S0), _ptr(z0), _ptr(dS_T),
@@ -265,10 +302,13 @@ def noncausal_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     returned as well.
     """
     lib = _lib.load()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k must be [B, H, L, d]")
+    _need_d(q, "q", fm.d)
+    _need(q, "q")
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
     dv = v.shape[-1]
-    _need(q, "q")
     _need(k, "k", (B, H, Lk, d), q.dtype)
     _need(v, "v", (B, H, Lk, dv), q.dtype)
     if out is None:
@@ -282,9 +322,14 @@ def noncausal_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
             S_out = torch.empty((B * H, fm.F, dv), dtype=torch.float32, device=q.device)
         if z_out is None:
             z_out = torch.empty((B * H, fm.F), dtype=torch.float32, device=q.device)
+    for t, name, shp in ((S_out, "S_out", (B * H, fm.F, dv)), (z_out, "z_out", (B * H, fm.F))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
     nbytes = noncausal_fwd_workspace_size(fm, B, H, Lq, Lk, dv, q.dtype)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.slay_attn_noncausal_fwd(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype),
                                      B, H, Lq, Lk, dv, _ptr(S0), _ptr(z0), out.data_ptr(), _ptr(S_out),
@@ -305,18 +350,24 @@ def recurrent_step(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Te
                    workspace: torch.Tensor | None = None) -> torch.Tensor:
     """One decode step for n heads: q, k [n, d], v [n, dv]; S [n, F, dv], z [n, F] fp32 in place."""
     lib = _lib.load()
-    n, d = q.shape
-    dv = v.shape[-1]
+    if q.dim() != 2:
+        raise ValueError("q must be [n_heads, d]")
+    _need_d(q, "q", fm.d)
     _need(q, "q")
+    n = q.shape[0]
+    dv = v.shape[-1]
     _need(k, "k", q.shape, q.dtype)
     _need(v, "v", (n, dv), q.dtype)
     _need(S, "S", (n, fm.F, dv), torch.float32)
     _need(z, "z", (n, fm.F), torch.float32)
     if out is None:
         out = torch.empty((n, dv), dtype=q.dtype, device=q.device)
+    _need(out, "out", (n, dv), q.dtype)
     nbytes = recurrent_step_workspace_size(fm, n, dv, q.dtype)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need(workspace, "workspace")
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.slay_attn_recurrent_step(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q.dtype),
                                       n, dv, S.data_ptr(), z.data_ptr(), out.data_ptr(), _ptr(workspace), wsz,

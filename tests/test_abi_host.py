@@ -296,3 +296,29 @@ def test_varlen_validation_and_workspace(lib):
     p96 = _params(R=3, m=32)
     n96 = lib.slay_attn_varlen_fwd_workspace_size(ctypes.byref(p96), 4, 16, 16384, 64, _lib.SLAY_BF16)
     assert n96 == r(n) + 2 * r(256 * 64 * 2) + 2 * (r(64 * 256 * 64 * 4) + r(64 * 256 * 4))
+
+
+def test_binding_rejects_mismatched_d_before_launch():
+    """Every wrapper compares the last axis of q/k/x with the draws' d before it
+    touches the device (a mismatch would make the kernels read or write past
+    the tensors)."""
+    import types
+
+    import torch
+
+    from kernelized_linear_attention_amd import ops
+
+    fm = types.SimpleNamespace(d=64, F=256, R=4, m=64, n_sets=1)
+    x = torch.zeros(2, 3, 5, 48)
+    v = torch.zeros(2, 3, 5, 64)
+    calls = [
+        lambda: ops.featmap(fm, x[0, 0]),
+        lambda: ops.chunked_fwd(fm, x, x, v, 64),
+        lambda: ops.chunked_bwd(fm, x, x, v, v, 64),
+        lambda: ops.noncausal_fwd(fm, x, x, v),
+        lambda: ops.varlen_fwd(fm, x[0], x[0], v[0], torch.zeros(2, dtype=torch.int64)),
+        lambda: ops.recurrent_step(fm, x[0, 0], x[0, 0], v[0, 0], torch.zeros(5, 256, 64), torch.zeros(5, 256)),
+    ]
+    for c in calls:
+        with pytest.raises(ValueError, match="d = 64"):
+            c()
