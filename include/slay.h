@@ -123,6 +123,28 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
                                     int32_t chunk, const float* S0, const float* z0, void* o, float* S_out,
                                     float* z_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the fixed device scratch behind slay_attn_chunked_fwd_noalloc. */
+#define SLAY_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* slay_attn_chunked_fwd for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, hosts that forbid
+ * allocation).  Same arguments, semantics and kernels as
+ * slay_attn_chunked_fwd, without the workspace: the library uses its own
+ * fixed device array of SLAY_NOALLOC_SCRATCH_BYTES bytes instead (32 MiB,
+ * held on every GPU the library runs on until the process ends).  Calls whose
+ * workspace would exceed it -- slay_attn_chunked_fwd_workspace_size(...) >
+ * SLAY_NOALLOC_SCRATCH_BYTES -- return SLAY_E_UNSUPPORTED with nothing
+ * enqueued.  Nothing is allocated or freed: not by the library, not through
+ * a library it calls.  The scratch carries no state between calls (no
+ * kernel reads what an earlier call left in it), but every call on one GPU
+ * shares it: calls that overlap in time on one GPU (different streams or
+ * threads) race and give wrong results; serialise them.  The scratch's
+ * device address is looked up once per device on the first call there. */
+slay_status_t slay_attn_chunked_fwd_noalloc(const slay_params_t* params, const void* q, const void* k,
+                                            const void* v, slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L,
+                                            int32_t dv, int32_t chunk, const float* S0, const float* z0, void* o,
+                                            float* S_out, float* z_out, void* stream);
+
 /* Workspace bytes slay_attn_varlen_fwd needs (0 for unsupported shapes). */
 size_t slay_attn_varlen_fwd_workspace_size(const slay_params_t* params, int32_t n_seqs, int32_t H,
                                            int64_t total_tokens, int32_t dv, slay_dtype_t io_dtype);

@@ -10,9 +10,10 @@ LIB_PATH = os.path.join(_PKG, "libslay.so")
 
 SLAY_OK, SLAY_E_INVALID, SLAY_E_UNSUPPORTED, SLAY_E_DEVICE = 0, 1, 2, 3
 SLAY_F32, SLAY_BF16 = 0, 1
+SLAY_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/slay.h
 
 # every function include/slay.h declares
-EXPORTS = ("slay_featmap", "slay_attn_chunked_fwd_workspace_size", "slay_attn_chunked_fwd",
+EXPORTS = ("slay_featmap", "slay_attn_chunked_fwd_workspace_size", "slay_attn_chunked_fwd", "slay_attn_chunked_fwd_noalloc",
            "slay_attn_varlen_fwd_workspace_size", "slay_attn_varlen_fwd",
            "slay_attn_chunked_bwd_workspace_size", "slay_attn_chunked_bwd",
            "slay_attn_noncausal_fwd_workspace_size", "slay_attn_noncausal_fwd",
@@ -64,6 +65,9 @@ def load() -> ctypes.CDLL:
         lib.slay_attn_chunked_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int, i32, i32, i64, i32, i32, fp, fp, vp, fp,
                                               fp, vp, sz, vp]
         lib.slay_attn_chunked_fwd.restype = ctypes.c_int
+        lib.slay_attn_chunked_fwd_noalloc.argtypes = [P, vp, vp, vp, ctypes.c_int, i32, i32, i64, i32, i32, fp, fp,
+                                                      vp, fp, fp, vp]
+        lib.slay_attn_chunked_fwd_noalloc.restype = ctypes.c_int
         lib.slay_attn_varlen_fwd_workspace_size.argtypes = [P, i32, i32, i64, i32, ctypes.c_int]
         lib.slay_attn_varlen_fwd_workspace_size.restype = sz
         lib.slay_attn_varlen_fwd.argtypes = [P, vp, vp, vp, ctypes.c_int, i32, i32, vp, i64, i32, fp, fp, vp, fp, fp,

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libslay.so")
 SOURCES = ["slay_api.cpp", "slay_featmap.hip", "slay_chunked_generic.hip", "slay_chunked_fused.hip", "slay_chunked_wide.hip",
-           "slay_decode.hip", "slay_backward.hip", "slay_backward_fused.hip"]
+           "slay_decode.hip", "slay_backward.hip", "slay_backward_fused.hip", "slay_noalloc.hip"]
 ARCH = os.environ.get("SLAY_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU instructions are kept out of the device code.

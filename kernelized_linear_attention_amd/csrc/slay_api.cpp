@@ -258,6 +258,18 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
                                     slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L, int32_t dv,
                                     int32_t chunk, const float* S0, const float* z0, void* o, float* S_out,
                                     float* z_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return slay::chunked_fwd_entry(params, q, k, v, io_dtype, B, H, L, dv, chunk, S0, z0, o, S_out, z_out, workspace,
+                                 workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace slay {
+
+slay_status_t chunked_fwd_entry(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L, int32_t dv, int32_t chunk,
+                                const float* S0, const float* z0, void* o, float* S_out, float* z_out,
+                                void* workspace, size_t workspace_bytes, void* stream, ScratchFn scratch) {
   slay_status_t st = check_params(params);
   if (st != SLAY_OK) return st;
   if (B < 0 || H < 0 || L < 0) return fail(SLAY_E_INVALID, "B, H, L must be >= 0");
@@ -296,17 +308,25 @@ slay_status_t slay_attn_chunked_fwd(const slay_params_t* params, const void* q, 
                       : path == 0 ? slay::fused_workspace_bytes(a)
                       : path == 1 ? slay::wide_workspace_bytes(a)
                                   : slay::generic_workspace_bytes(a);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (scratch && need > 0) {  // the caller's fixed scratch, looked up only once every argument is checked
+    if (need > workspace_bytes)
+      return fail(SLAY_E_UNSUPPORTED, "workspace of %zu bytes exceeds the fixed scratch of %zu bytes", need,
+                  workspace_bytes);
+    const hipError_t e = scratch(s, &workspace);
+    if (e != hipSuccess) return device_status(e, "scratch lookup");
+    a.ws = workspace;
+  }
   if (workspace_bytes < need) return fail(SLAY_E_INVALID, "workspace too small: %zu < %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(SLAY_E_INVALID, "workspace is NULL");
   if (need > 0 && !aligned16(workspace)) return fail(SLAY_E_INVALID, "workspace must be 16-byte aligned");
   if (nh == 0) return ok();
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = path == 0 ? slay::launch_fused(a, s) : path == 1 ? slay::launch_wide(a, s)
                                                                         : slay::launch_generic(a, s);
   return device_status(e, "slay_attn_chunked_fwd launch");
 }
 
-}  // extern "C"
+}  // namespace slay
 
 namespace {
 slay::BackwardArgs backward_args(const slay_params_t* p, slay_dtype_t dt, int32_t B, int32_t H, int64_t L,

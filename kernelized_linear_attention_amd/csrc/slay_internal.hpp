@@ -5,9 +5,21 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "slay.h"
 #include "slay_device.hpp"
 
 namespace slay {
+
+// slay_attn_chunked_fwd's checks and launch.  With `scratch` set, the call
+// uses a fixed device scratch of workspace_bytes bytes instead of `workspace`:
+// once every argument has passed its checks, scratch(stream, &ptr) supplies
+// its device address, and a shape whose workspace exceeds the scratch is
+// refused (SLAY_E_UNSUPPORTED).
+typedef hipError_t (*ScratchFn)(hipStream_t stream, void** ptr);
+slay_status_t chunked_fwd_entry(const slay_params_t* params, const void* q, const void* k, const void* v,
+                                slay_dtype_t io_dtype, int32_t B, int32_t H, int64_t L, int32_t dv, int32_t chunk,
+                                const float* S0, const float* z0, void* o, float* S_out, float* z_out,
+                                void* workspace, size_t workspace_bytes, void* stream, ScratchFn scratch);
 
 // Raise a kernel's dynamic-LDS limit once per (kernel, device): the setting
 // persists on the device, so later launches make no call besides the launch

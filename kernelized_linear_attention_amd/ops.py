@@ -173,6 +173,23 @@ def chunked_fwd(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     return out
 
 
+def chunked_fwd_noalloc(fm: FeatureMap, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk: int,
+                        S0: torch.Tensor | None = None, z0: torch.Tensor | None = None, return_state: bool = False,
+                        out: torch.Tensor | None = None, S_out=None, z_out=None):
+    """chunked_fwd through slay_attn_chunked_fwd_noalloc: the library's fixed
+    device scratch replaces the workspace, so the C call allocates nothing (the
+    outputs are created here unless the caller passes them)."""
+    lib = _lib.load()
+    B, H, L, dv, out, S_out, z_out = _fwd_outputs(fm, q, k, v, S0, z0, return_state, out, S_out, z_out)
+    st = lib.slay_attn_chunked_fwd_noalloc(fm.c_params(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           _dtype_code(q.dtype), B, H, L, dv, chunk, _ptr(S0), _ptr(z0),
+                                           out.data_ptr(), _ptr(S_out), _ptr(z_out), _stream(q))
+    _lib.check(st, "slay_attn_chunked_fwd_noalloc")
+    if return_state:
+        return out, S_out, z_out
+    return out
+
+
 def varlen_fwd_workspace_size(fm: FeatureMap, n_seqs: int, H: int, total_tokens: int, dv: int,
                               dtype: torch.dtype) -> int:
     lib = _lib.load()

@@ -298,6 +298,30 @@ def test_varlen_validation_and_workspace(lib):
     assert n96 == r(n) + 2 * r(256 * 64 * 2) + 2 * (r(64 * 256 * 64 * 4) + r(64 * 256 * 4))
 
 
+def test_noalloc_rejects_before_any_launch(lib):
+    """slay_attn_chunked_fwd_noalloc: a workspace beyond the fixed scratch is
+    refused on the host (UNSUPPORTED, with the sizes in the message), and bad
+    arguments get the same checks as slay_attn_chunked_fwd."""
+    E_INV, E_UNS = _lib.SLAY_E_INVALID, _lib.SLAY_E_UNSUPPORTED
+
+    def call(p, B=1, H=8, L=131072, dv=128, chunk=128, q=FAKE):
+        return lib.slay_attn_chunked_fwd_noalloc(ctypes.byref(p) if p is not None else None, q, FAKE, FAKE,
+                                                 _lib.SLAY_BF16, B, H, L, dv, chunk, None, None, FAKE, None, None,
+                                                 None)
+
+    big = _params(d=128, R=4, m=128)
+    need = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(big), 1, 8, 131072, 128, 128, _lib.SLAY_BF16)
+    assert need > _lib.SLAY_NOALLOC_SCRATCH_BYTES
+    assert call(big) == E_UNS
+    assert b"exceeds the fixed scratch" in lib.slay_last_error()
+    assert call(None) == E_INV
+    assert call(_params(), H=16, L=16384, dv=64, chunk=0) == E_INV
+    assert call(_params(), H=16, L=16384, dv=64, chunk=64, q=None) == E_INV
+    # the headline shape's workspace fits the scratch
+    fits = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(_params()), 1, 16, 16384, 64, 64, _lib.SLAY_BF16)
+    assert 0 < fits <= _lib.SLAY_NOALLOC_SCRATCH_BYTES
+
+
 def test_binding_rejects_mismatched_d_before_launch():
     """Every wrapper compares the last axis of q/k/x with the draws' d before it
     touches the device (a mismatch would make the kernels read or write past
@@ -314,6 +338,7 @@ def test_binding_rejects_mismatched_d_before_launch():
     calls = [
         lambda: ops.featmap(fm, x[0, 0]),
         lambda: ops.chunked_fwd(fm, x, x, v, 64),
+        lambda: ops.chunked_fwd_noalloc(fm, x, x, v, 64),
         lambda: ops.chunked_bwd(fm, x, x, v, v, 64),
         lambda: ops.noncausal_fwd(fm, x, x, v),
         lambda: ops.varlen_fwd(fm, x[0], x[0], v[0], torch.zeros(2, dtype=torch.int64)),
