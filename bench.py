@@ -7,9 +7,16 @@ the chunked contraction, segment states, prefix scan) over B1 H16 L16384,
 d = dv = 64, R = 4 Gauss-Laguerre nodes x m = 64 features (F = 256), chunk
 64, bf16 in / fp32 accumulate / bf16 out, on seeded synthetic inputs already
 resident in HBM.  Prints one JSON line.  Beside the forward it times the
-standalone feature map on the same q and k (HBM-bound) and one recurrent
-decode step for 256 sequences x 16 heads (HBM-bound on the fp32 state), and
-the fp64 CPU oracle on a bounded prefix of the same workload.
+standalone feature map on the same q and k (HBM-bound), the causal forward of
+B4 H8 L2048 (F = 96), the non-causal, variable-length, backward and
+long-sequence forwards, one recurrent decode step for 256 sequences x 16
+heads (HBM-bound on the fp32 state), and the fp64 CPU oracle on bounded
+samples of the workloads.
+
+Warm-up: the W requested steps run first; then, if they amounted to less than
+SETTLE_MS of GPU time, more untimed steps run until that much has passed
+(the shader clock and the timings settle only after ~15 ms of sustained
+work).  The extra steps are reported as "settle_steps".
 """
 from __future__ import annotations
 
@@ -30,10 +37,26 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 WORKLOAD = "h16_l16k_bf16"
+SMALL = "b4h8_l2k_bf16"
 DECODE = "decode_256x16_f32"
 LONG = "h8_l128k_d128_bf16"
+SETTLE_MS = 200.0  # minimum GPU time of untimed work before each timed loop
 KERNEL_SOURCES = ("slay_chunked_fused.hip", "slay_chunked_generic.hip", "slay_chunked_wide.hip", "slay_featmap.hip",
                   "slay_decode.hip", "slay_backward.hip", "slay_backward_fused.hip", "slay_device.hpp")
+# the sources whose kernels each measured unit launches (a counter summary is
+# current while their digest matches the one it records)
+_FWD = ("slay_chunked_fused.hip", "slay_chunked_generic.hip", "slay_device.hpp")
+UNIT_SOURCES = {
+    "fused_fwd_h16_l16k_bf16": _FWD,
+    "fused_fwd_b4h8_l2k_bf16": _FWD,
+    "noncausal_h16_l16k_bf16": _FWD,
+    "varlen_h16_8seqs_16k_bf16": _FWD,
+    "featmap_h16_l16k_bf16": ("slay_featmap.hip", "slay_device.hpp"),
+    "backward_h16_l16k_bf16": ("slay_backward_fused.hip", "slay_featmap.hip") + _FWD,
+    "long_h8_l128k_d128_bf16": ("slay_chunked_wide.hip", "slay_featmap.hip", "slay_chunked_generic.hip",
+                                "slay_device.hpp"),
+    "decode_256x16_f32": ("slay_decode.hip", "slay_featmap.hip", "slay_device.hpp"),
+}
 
 
 def fwd_flops_per_token_head(w) -> int:
@@ -67,6 +90,11 @@ def bwd_flops_per_token_head(w) -> int:
     return 16 * d * F + 10 * F * (dv + 1) + 2 * F * dv + 3 * (C + 1) * F + 2 * (C + 1) * (dv + 1) + (C + 1) * dv
 
 
+def fwd_bytes_per_token_head(w) -> int:
+    """Algorithmic HBM bytes of the fused causal forward: q, k, v read and o written once (bf16)."""
+    return 2 * (2 * w.d + 2 * w.dv)
+
+
 def featmap_bytes_per_row(w) -> int:
     return 2 * w.d + 2 * w.F  # bf16 row in, bf16 features out
 
@@ -76,9 +104,9 @@ def decode_bytes_per_head(w) -> int:
     return 4 * 2 * (w.F * w.dv + w.F) + 4 * (2 * w.d + 2 * w.dv)
 
 
-def sources_digest() -> str:
+def sources_digest(names=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, "kernelized_linear_attention_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -92,7 +120,7 @@ def read_traffic(kind: str):
     txt = open(path).read()
     m_src = re.search(r"^sources_sha256_16:\s*(\w+)", txt, re.M)
     m_val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
-    if not m_src or not m_val or m_src.group(1) != sources_digest():
+    if not m_src or not m_val or m_src.group(1) != sources_digest(UNIT_SOURCES[kind]):
         return None
     return float(m_val.group(1))
 
@@ -102,6 +130,8 @@ TRAFFIC_UNITS = {
     # description); the counters of each unit come from runs of that part alone
     "fused_fwd_h16_l16k_bf16": ("fwd", (("pass1s", 1), ("scan_kernel", 1), ("pass2s", 1)),
                                 "one causal forward, B1 H16 L16384 bf16 (segment states + scan + main pass)"),
+    "fused_fwd_b4h8_l2k_bf16": ("small", (("pass1s", 1), ("scan_kernel", 1), ("pass2s", 1)),
+                                "one causal forward, B4 H8 L2048 F = 96 bf16 (segment states + scan + main pass)"),
     "featmap_h16_l16k_bf16": ("featmap", (("featmap_kernel<unsigned short, unsigned short", 1),),
                               "one feature-map launch over 262144 bf16 rows, F = 256"),
     "noncausal_h16_l16k_bf16": ("noncausal", (("pass1s", 1), ("scan_kernel", 1), ("ncout_kernel", 1)),
@@ -170,7 +200,9 @@ def traffic_summary(fetch_dir: str, write_dir: str, calib_mib: int, command: str
                  "|---|---|---|---|"]
         for fr, k in frags:
             lines.append(f"| {fr} | {k} | {pick(fetch, fr) or 0.0:.0f} | {pick(write, fr) or 0.0:.0f} |")
-        lines += ["", f"hbm_bytes_per_launch: {total:.6e}", f"sources_sha256_16: {sources_digest()}"]
+        lines += ["", f"hbm_bytes_per_launch: {total:.6e}",
+                  f"sources ({', '.join(UNIT_SOURCES[name])}):",
+                  f"sources_sha256_16: {sources_digest(UNIT_SOURCES[name])}"]
         with open(os.path.join(ROOT, "profiles", f"traffic_{name}.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
         print(name, f"{total / 1e6:.1f} MB per launch")
@@ -190,6 +222,50 @@ def event_time_ms(fn, steps: int, stream) -> float:
     return start.elapsed_time(end) / steps
 
 
+def warm_up(fn, steps: int, stream) -> int:
+    """Run `steps` untimed calls, then more until at least SETTLE_MS of GPU time
+    has passed in this warm-up; returns the number of extra calls."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    spent = start.elapsed_time(end) if steps > 0 else 0.0
+    extra = 0
+    while spent < SETTLE_MS:
+        n = 8 if extra == 0 else extra  # doubling batches
+        start.record(stream)
+        for _ in range(n):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        spent += start.elapsed_time(end)
+        extra += n
+    return extra
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_threads() -> int:
+    """Threads the oracle's OpenMP loops use (its own report)."""
+    import oracle
+
+    return int(oracle.max_threads())
+
+
 def cpu_baseline(w, q, k, v, A, G, L_sample: int):
     import oracle
 
@@ -198,10 +274,49 @@ def cpu_baseline(w, q, k, v, A, G, L_sample: int):
     t0 = time.perf_counter()
     oracle.slay_causal(qs, ks, vs, A, G, w.eps, w.R, w.m, form="recurrent")
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    return {"value": w.B * L_sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 recurrent form, all {w.H} heads x first {L_sample} of {w.L} tokens "
-                      f"({dt:.2f} s wall); per-token cost is independent of L"}
+    return {"value": w.B * L_sample / dt, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"fp64 recurrent form, all {w.B * w.H} heads x first {L_sample} of {w.L} tokens "
+                      f"({dt:.2f} s wall); per-token cost is independent of L",
+            "cpu_model": cpu_model()}
+
+
+def cpu_baselines_other():
+    """The oracle on bounded samples of the other workloads (reported beside the headline one)."""
+    import oracle
+
+    import slay_synth as ss
+
+    out = []
+    w2 = ss.WORKLOADS[SMALL]
+    q, k, v = ss.make_qkv(w2)
+    A, G = ss.make_draws(w2)
+    t0 = time.perf_counter()
+    oracle.slay_causal(q, k, v, A, G, w2.eps, w2.R, w2.m, form="recurrent")
+    dt = time.perf_counter() - t0
+    out.append({"workload": SMALL, "value": w2.B * w2.L / dt, "unit": "tokens/s", "wall_s": dt,
+                "sample": "the whole workload (B4 H8 L2048, F = 96), fp64 recurrent form"})
+    wl = ss.WORKLOADS[LONG]
+    Ls = 2048
+    q, k, v = ss.make_qkv(wl.with_(L=Ls))
+    A, G = ss.make_draws(wl)
+    t0 = time.perf_counter()
+    oracle.slay_causal(q, k, v, A, G, wl.eps, wl.R, wl.m, form="recurrent")
+    dt = time.perf_counter() - t0
+    out.append({"workload": LONG, "value": wl.B * Ls / dt, "unit": "tokens/s", "wall_s": dt,
+                "sample": f"all {wl.H} heads x first {Ls} of {wl.L} tokens (d = dv = 128, F = 512), fp64 recurrent "
+                          "form; per-token cost is independent of L"})
+    wd = ss.WORKLOADS[DECODE]
+    n_steps = 16
+    qs, ks, vs = zip(*(ss.make_decode_step(wd, t) for t in range(n_steps)))
+    qd, kd, vd = (np.stack(x, 1) for x in (qs, ks, vs))  # [heads, steps, d]
+    A, G = ss.make_draws(wd)
+    t0 = time.perf_counter()
+    oracle.slay_causal(qd, kd, vd, A, G, wd.eps, wd.R, wd.m, form="recurrent")
+    dt = time.perf_counter() - t0
+    out.append({"workload": DECODE, "value": wd.B * n_steps / dt, "unit": "tokens/s", "wall_s": dt,
+                "sample": f"{n_steps} decode steps of all {wd.n_heads} heads (256 sequences x 16), fp64 recurrent "
+                          "form (the state carried in memory as the GPU does)"})
+    return out
 
 
 def main():
@@ -214,7 +329,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per head of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--only", choices=["all", "fwd", "featmap", "noncausal", "varlen", "backward", "long", "decode"],
+    ap.add_argument("--only", choices=["all", "fwd", "small", "featmap", "noncausal", "varlen", "backward", "long",
+                                       "decode"],
                     default="all")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (scale for HBM byte counters)")
@@ -263,10 +379,9 @@ def main():
         ops.chunked_fwd(fm, qd, kd, vd, w.chunk, out=out, workspace=ws)
 
     result = {}
+    settle = {}
     if args.only in ("all", "fwd"):
-        for _ in range(args.warmup):
-            fwd()
-        torch.cuda.synchronize()
+        settle["fwd"] = warm_up(fwd, args.warmup, stream)
         t0 = time.perf_counter()
         ms = event_time_ms(fwd, args.steps, stream)
         wall = (time.perf_counter() - t0) / args.steps * 1e3
@@ -292,8 +407,36 @@ def main():
                          "kernel": "fused causal forward: segment-state pass + prefix scan + main pass, one stream",
                          "algorithmic_flops_per_launch": flops},
             "wall_ms_per_step": wall,
+            "settle_steps": settle["fwd"],
         }
     also = []
+    if args.only in ("all", "small"):
+        # B4 H8 L2048, F = 96 (R = 3, m = 32), chunk 64: the fused kernels at a small feature count
+        w2 = ss.WORKLOADS[SMALL]
+        q2, k2, v2 = ss.make_qkv(w2)
+        A2, G2 = ss.make_draws(w2)
+        fm2 = ops.FeatureMap(dev_bf16(A2), dev_bf16(G2), w2.R, w2.m, w2.eps)
+        q2d, k2d, v2d = dev_bf16(q2), dev_bf16(k2), dev_bf16(v2)
+        o2 = torch.empty_like(v2d)
+        ws2 = torch.empty(max(ops.chunked_fwd_workspace_size(fm2, w2.B, w2.H, w2.L, w2.dv, w2.chunk, torch.bfloat16),
+                              16), dtype=torch.uint8, device=dev)
+
+        def sfwd():
+            ops.chunked_fwd(fm2, q2d, k2d, v2d, w2.chunk, out=o2, workspace=ws2)
+
+        settle["small"] = warm_up(sfwd, args.warmup, stream)
+        ms = event_time_ms(sfwd, args.steps, stream)
+        nbytes = fwd_bytes_per_token_head(w2) * w2.B * w2.H * w2.L
+        flops = fwd_flops_per_token_head(w2) * w2.B * w2.H * w2.L
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        also.append({"name": "fwd_b4h8_l2k_bf16", "ms_per_step": ms, "tokens_per_s": w2.B * w2.L / (ms * 1e-3),
+                     "config": {"B": w2.B, "H": w2.H, "L": w2.L, "d": w2.d, "dv": w2.dv, "R": w2.R, "m": w2.m,
+                                "F": w2.F, "chunk": w2.chunk},
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic("fused_fwd_b4h8_l2k_bf16"),
+                                  "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+                                  "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}})
+        del q2d, k2d, v2d, o2, ws2
     if args.only in ("all", "featmap"):
         phi = torch.empty(w.B, w.H, w.L, w.F, dtype=torch.bfloat16, device=dev)
 
@@ -301,8 +444,7 @@ def main():
             for x in (qd, kd):
                 ops.featmap(fm, x, torch.bfloat16, out=phi)
 
-        for _ in range(args.warmup):
-            fmap()
+        settle["featmap"] = warm_up(fmap, args.warmup, stream)
         ms = event_time_ms(fmap, args.steps, stream) / 2  # per launch
         rows = w.B * w.H * w.L
         nbytes = rows * featmap_bytes_per_row(w)
@@ -318,8 +460,7 @@ def main():
         def nc():
             ops.noncausal_fwd(fm, qd, kd, vd, out=out, workspace=wsn)
 
-        for _ in range(args.warmup):
-            nc()
+        settle["noncausal"] = warm_up(nc, args.warmup, stream)
         ms = event_time_ms(nc, args.steps, stream)
         flops = noncausal_flops_per_token_head(w) * w.B * w.H * w.L
         achieved = flops / (ms * 1e-3) / 1e12
@@ -341,8 +482,7 @@ def main():
         def vl():
             ops.varlen_fwd(fm, qv, kv, vv, cu, out=ov, workspace=wsv)
 
-        for _ in range(args.warmup):
-            vl()
+        settle["varlen"] = warm_up(vl, args.warmup, stream)
         ms = event_time_ms(vl, args.steps, stream)
         flops = fwd_flops_per_token_head(w) * w.H * T
         achieved = flops / (ms * 1e-3) / 1e12
@@ -361,8 +501,7 @@ def main():
         def bwd():
             ops.chunked_bwd(fm, qd, kd, vd, dout, w.chunk, workspace=wsb, dq=dq, dk=dk, dv=dvv)
 
-        for _ in range(max(1, args.warmup // 5)):
-            bwd()
+        settle["backward"] = warm_up(bwd, max(1, args.warmup // 5), stream)
         ms = event_time_ms(bwd, max(1, args.steps // 5), stream)
         flops = bwd_flops_per_token_head(w) * w.B * w.H * w.L
         achieved = flops / (ms * 1e-3) / 1e12
@@ -387,8 +526,7 @@ def main():
         def lfwd():
             ops.chunked_fwd(fml, qld, kld, vld, wl.chunk, out=oll, workspace=wsl)
 
-        for _ in range(max(1, args.warmup // 2)):
-            lfwd()
+        settle["long"] = warm_up(lfwd, max(1, args.warmup // 2), stream)
         ms = event_time_ms(lfwd, max(1, args.steps // 2), stream)
         flops = fwd_flops_per_token_head(wl) * wl.B * wl.H * wl.L
         achieved = flops / (ms * 1e-3) / 1e12
@@ -427,8 +565,7 @@ def main():
         with torch.cuda.graph(graph):
             steps()
         reps = max(1, args.decode_steps // n_in)
-        for _ in range(max(1, args.warmup // n_in)):
-            graph.replay()
+        settle["decode"] = n_in * warm_up(graph.replay, max(1, args.warmup // n_in), stream)
         ms = event_time_ms(graph.replay, reps, stream) / n_in
         nbytes = nh * decode_bytes_per_head(wd)
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -441,6 +578,9 @@ def main():
         result["also"] = also
     if args.only in ("all", "fwd") and not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, A, G, min(args.cpu_tokens, w.L))
+        if args.only == "all":
+            result["cpu_baseline_other"] = cpu_baselines_other()
+    result["settle_steps"] = settle
     result["sources_sha256_16"] = sources_digest()
     print(json.dumps(result))
 

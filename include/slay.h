@@ -4,10 +4,10 @@
  *
  * Method sources (web pages; cited by title and section):
  *   - "SLAY: Geometry-Aware Spherical Linearized Attention with Yat-Kernel",
- *     arXiv 2602.04915, English abstract: queries and keys on the unit
- *     sphere; the spherical Yat kernel written (Bernstein's theorem) as a
- *     nonnegative mixture of polynomial x exponential kernels; a strictly
- *     positive random-feature approximation giving O(L) attention.
+ *     arXiv 2602.04915, English abstract: q and k are normalised onto the
+ *     sphere; K is written, via Bernstein's theorem, as a positive sum of
+ *     u^2 exp(beta u) terms, which positive random features approximate, so
+ *     attention costs O(L).
  *   - nubint.ai review of that paper, "Proposed method" (six bullets):
  *     (1) Yat kernel as a spherical similarity on unit-norm q, k; (2) the
  *     denominator linearised through its Laplace representation; (3) anchor
@@ -271,6 +271,23 @@ slay_status_t slay_attn_recurrent_step(const slay_params_t* params, const void* 
  * library, alpha[r] = w_r/(2+eps), beta[r] = 2 x_r/(2+eps) (fp64, R <= 16).
  * Returns SLAY_OK or SLAY_E_INVALID. */
 slay_status_t slay_gl_table(int32_t R, double eps, double* alpha, double* beta);
+
+/* Host-only: positive orthogonal random-feature draws (the linearized
+ * 2-simplicial attention page's summary: positive orthogonal random features,
+ * a variance-reduced alternative to i.i.d. PRF draws at the same F).  Rows
+ * come in blocks of d: within a block they are mutually orthogonal, and each
+ * row is marginally N(0, I_d) -- the block is the Haar-random orthogonal
+ * factor of a Gaussian matrix (Householder QR with the signs fixed so that R
+ * has a positive diagonal), row i scaled by the length of an independent
+ * Gaussian vector.  The randomness is the caller's:
+ *   gauss : [ceil(n_rows/d)][d][d] fp64, i.i.d. N(0, 1) (block b's matrix);
+ *   chi   : [ceil(n_rows/d)][d][d] fp64, i.i.d. N(0, 1) (row i of block b has
+ *           length |chi[b][i]|);
+ *   out   : [n_rows][d] fp32, the first n_rows rows of the blocks in order.
+ * For SLAY's PRF draws [R*m][d], call it once per node on that node's m rows
+ * (orthogonal within the node), then copy to the device.  Returns SLAY_OK or
+ * SLAY_E_INVALID (NULL pointer, d outside [1, 4096], non-finite input). */
+slay_status_t slay_orthogonal_draws(int32_t n_rows, int32_t d, const double* gauss, const double* chi, float* out);
 
 /* Static description of a status code. */
 const char* slay_status_string(slay_status_t status);

@@ -17,7 +17,7 @@ EXPORTS = ("slay_featmap", "slay_attn_chunked_fwd_workspace_size", "slay_attn_ch
            "slay_attn_varlen_fwd_workspace_size", "slay_attn_varlen_fwd",
            "slay_attn_chunked_bwd_workspace_size", "slay_attn_chunked_bwd",
            "slay_attn_noncausal_fwd_workspace_size", "slay_attn_noncausal_fwd",
-           "slay_attn_recurrent_step_workspace_size", "slay_attn_recurrent_step", "slay_gl_table",
+           "slay_attn_recurrent_step_workspace_size", "slay_attn_recurrent_step", "slay_gl_table", "slay_orthogonal_draws",
            "slay_status_string", "slay_last_error", "slay_version")
 
 
@@ -90,6 +90,9 @@ def load() -> ctypes.CDLL:
         lib.slay_gl_table.argtypes = [i32, ctypes.c_double, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_double)]
         lib.slay_gl_table.restype = ctypes.c_int
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.slay_orthogonal_draws.argtypes = [i32, i32, dp, dp, ctypes.POINTER(ctypes.c_float)]
+        lib.slay_orthogonal_draws.restype = ctypes.c_int
         lib.slay_status_string.argtypes = [ctypes.c_int]
         lib.slay_status_string.restype = ctypes.c_char_p
         lib.slay_last_error.argtypes = []

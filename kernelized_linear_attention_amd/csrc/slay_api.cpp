@@ -172,6 +172,61 @@ slay_status_t check_params(const slay_params_t* p) {
   return SLAY_OK;
 }
 
+// One block of positive orthogonal random-feature directions (the
+// linearized 2-simplicial attention page's summary: positive orthogonal
+// random features), fp64.  The d x d Gaussian matrix G is factored G = QR by
+// Householder reflections; with the columns of Q multiplied by sign(R_ii) the
+// factor is the unique one with a positive diagonal of R, which makes it
+// Haar-distributed over the orthogonal group.  Row i of the block is column i
+// of that Q times |c_i|, the length of an independent Gaussian vector c_i
+// (chi-distributed with d degrees of freedom), so every row is marginally
+// N(0, I_d) while the rows of the block are mutually orthogonal.
+// g, c: [d][d] row-major; out: rows_out <= d rows of d values.
+void orthogonal_block(int d, const double* g, const double* c, int rows_out, float* out) {
+  std::vector<double> a(g, g + (size_t)d * d);  // reduced in place to R
+  std::vector<double> vs((size_t)d * d, 0.0);   // Householder vectors, v_k in vs[k][k..]
+  std::vector<double> rdiag(d);
+  for (int k = 0; k < d; ++k) {
+    double nrm = 0.0;
+    for (int i = k; i < d; ++i) nrm += a[(size_t)i * d + k] * a[(size_t)i * d + k];
+    nrm = std::sqrt(nrm);
+    const double x0 = a[(size_t)k * d + k];
+    const double alpha = x0 >= 0.0 ? -nrm : nrm;  // reflect x onto alpha e_k, away from x0 (no cancellation)
+    double* v = &vs[(size_t)k * d];
+    for (int i = k; i < d; ++i) v[i] = a[(size_t)i * d + k];
+    v[k] -= alpha;
+    double vn = 0.0;
+    for (int i = k; i < d; ++i) vn += v[i] * v[i];
+    if (vn > 0.0) {
+      const double inv = 1.0 / std::sqrt(vn);
+      for (int i = k; i < d; ++i) v[i] *= inv;
+      for (int j = k; j < d; ++j) {  // a[k.., j] -= 2 v (v . a[k.., j])
+        double dot = 0.0;
+        for (int i = k; i < d; ++i) dot += v[i] * a[(size_t)i * d + j];
+        for (int i = k; i < d; ++i) a[(size_t)i * d + j] -= 2.0 * v[i] * dot;
+      }
+    }
+    rdiag[k] = a[(size_t)k * d + k];
+  }
+  // Q = H_0 H_1 ... H_{d-1}: apply the reflections to the identity, last one first
+  std::vector<double> q((size_t)d * d, 0.0);
+  for (int i = 0; i < d; ++i) q[(size_t)i * d + i] = 1.0;
+  for (int k = d - 1; k >= 0; --k) {
+    const double* v = &vs[(size_t)k * d];
+    for (int j = 0; j < d; ++j) {
+      double dot = 0.0;
+      for (int i = k; i < d; ++i) dot += v[i] * q[(size_t)i * d + j];
+      for (int i = k; i < d; ++i) q[(size_t)i * d + j] -= 2.0 * v[i] * dot;
+    }
+  }
+  for (int i = 0; i < rows_out; ++i) {  // row i = sign(R_ii) Q[:, i] |c_i|
+    double len = 0.0;
+    for (int t = 0; t < d; ++t) len += c[(size_t)i * d + t] * c[(size_t)i * d + t];
+    const double sc = (rdiag[i] < 0.0 ? -1.0 : 1.0) * std::sqrt(len);
+    for (int t = 0; t < d; ++t) out[(size_t)i * d + t] = (float)(q[(size_t)t * d + i] * sc);
+  }
+}
+
 bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / a; }
 
 slay_status_t device_status(hipError_t e, const char* what) {
@@ -588,6 +643,22 @@ slay_status_t slay_gl_table(int32_t R, double eps, double* alpha, double* beta) 
   if (R < 1 || R > slay::kMaxNodes || !alpha || !beta || !(eps > 0.0) || !std::isfinite(eps))
     return fail(SLAY_E_INVALID, "slay_gl_table: R in [1, 16], eps > 0, non-NULL outputs");
   node_params(R, eps, alpha, beta);
+  return ok();
+}
+
+slay_status_t slay_orthogonal_draws(int32_t n_rows, int32_t d, const double* gauss, const double* chi, float* out) {
+  if (n_rows < 0 || d < 1 || d > 4096) return fail(SLAY_E_INVALID, "slay_orthogonal_draws: n_rows >= 0, d in [1, 4096]");
+  if (n_rows == 0) return ok();
+  if (!gauss || !chi || !out) return fail(SLAY_E_INVALID, "slay_orthogonal_draws: NULL pointer");
+  const int32_t n_blocks = (n_rows + d - 1) / d;
+  for (int32_t b = 0; b < n_blocks; ++b) {
+    const size_t off = (size_t)b * d * d;
+    const int rows = std::min<int32_t>(d, n_rows - b * d);
+    for (size_t i = 0; i < (size_t)d * d; ++i)
+      if (!std::isfinite(gauss[off + i]) || !std::isfinite(chi[off + i]))
+        return fail(SLAY_E_INVALID, "slay_orthogonal_draws: non-finite input");
+    orthogonal_block(d, gauss + off, chi + off, rows, out + (size_t)b * d * d);
+  }
   return ok();
 }
 

@@ -33,9 +33,10 @@
 // side by side are the eight consecutive k-values one lane feeds a 16x16x32
 // MFMA, provided the other operand is read with the same k order.  All
 // contractions use the one 16x16x32 bf16 shape, the 80-column ones as two full
-// steps plus a tail step whose second half is zero: a chain that fed a
-// 16x16x16 result into the next MFMA's accumulator gave wrong values in its
-// first two accumulator registers on gfx950.
+// steps plus a tail step whose second half is zero.  (An earlier tail step in
+// the 16x16x16 shape gave wrong results for a reason never established --
+// possibly an operand-layout mistake in that code; the one shape whose lane
+// layout is checked is used instead.)
 #include "slay_device.hpp"
 #include "slay_internal.hpp"
 

@@ -97,6 +97,23 @@ def gl_table(R: int, eps: float):
     return np.array(a[:]), np.array(b[:])
 
 
+def orthogonal_draws(n_rows: int, d: int, gauss: np.ndarray, chi: np.ndarray) -> np.ndarray:
+    """Rows in orthogonal blocks of d, each marginally N(0, I_d), from the
+    caller's Gaussian matrices gauss, chi [ceil(n_rows/d), d, d] (host, fp64);
+    returns [n_rows, d] float32 on the host (slay_orthogonal_draws)."""
+    lib = _lib.load()
+    nb = (n_rows + d - 1) // d
+    g = np.ascontiguousarray(gauss, dtype=np.float64)
+    c = np.ascontiguousarray(chi, dtype=np.float64)
+    if g.shape != (nb, d, d) or c.shape != (nb, d, d):
+        raise ValueError(f"gauss and chi must be [{nb}, {d}, {d}]")
+    out = np.empty((n_rows, d), dtype=np.float32)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _lib.check(lib.slay_orthogonal_draws(n_rows, d, g.ctypes.data_as(dp), c.ctypes.data_as(dp),
+                                         out.ctypes.data_as(ctypes.POINTER(ctypes.c_float))), "slay_orthogonal_draws")
+    return out
+
+
 def featmap(fm: FeatureMap, x: torch.Tensor, out_dtype: torch.dtype | None = None,
             rows_per_head: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
     """phi(x) for rows x [..., d]; returns [..., R*m] in out_dtype (default x.dtype)."""

@@ -80,6 +80,8 @@ def _load():
         lib.orc_slay_causal_bwd.argtypes = [_I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_double, _D, _D, _D, _D, _D, _I64, ctypes.c_int, _D, _D, _D,
                                             _D, _D, _D, _D, _D, _D, _D]
+        lib.orc_max_threads.argtypes = []
+        lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -97,6 +99,11 @@ def _p(a):
 def _check(status: int, what: str) -> None:
     if status != 0:
         raise ValueError(f"oracle {what} rejected its arguments (status {status})")
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_max_threads())
 
 
 # --------------------------------------------------------------------------

@@ -30,6 +30,7 @@
  *   - zero rows are normalised as x / max(|x|, 1e-12).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -715,3 +716,6 @@ int orc_slay_causal_bwd(int64_t nh, int64_t L, int d, int dv, int R, int m, doub
   }
   return bad ? ORC_BAD : ORC_OK;
 }
+
+/* Threads the OpenMP loops above use (the CPU baseline reports it). */
+int orc_max_threads(void) { return omp_get_max_threads(); }

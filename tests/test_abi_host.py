@@ -347,3 +347,39 @@ def test_binding_rejects_mismatched_d_before_launch():
     for c in calls:
         with pytest.raises(ValueError, match="d = 64"):
             c()
+
+
+def test_orthogonal_draws_library(lib):
+    """slay_orthogonal_draws: rows orthogonal within blocks of d with the
+    lengths of the caller's chi vectors; equal (to fp32 rounding) to the
+    sign-fixed QR factor numpy gives for the same Gaussian matrices, and to the
+    test inputs' generator fed the same stream."""
+    import slay_synth as ss
+    from kernelized_linear_attention_amd import ops
+
+    for d, n in ((64, 150), (32, 32), (128, 100)):
+        rng = np.random.default_rng([7, d])
+        nb = (n + d - 1) // d
+        blocks = [(rng.standard_normal((d, d)), rng.standard_normal((d, d))) for _ in range(nb)]
+        g = np.stack([b[0] for b in blocks])
+        c = np.stack([b[1] for b in blocks])
+        out = ops.orthogonal_draws(n, d, g, c).astype(np.float64)
+        ref = []
+        for b in range(nb):
+            Q, R = np.linalg.qr(g[b])
+            ref.append((Q * np.sign(np.diag(R))).T * np.linalg.norm(c[b], axis=1)[:, None])
+        ref = np.concatenate(ref)[:n]
+        np.testing.assert_allclose(out, ref, rtol=0, atol=2e-6 * np.abs(ref).max())
+        for b in range(nb):
+            blk = out[b * d:(b + 1) * d]
+            lens = np.linalg.norm(c[b], axis=1)[:blk.shape[0]]
+            np.testing.assert_allclose(np.linalg.norm(blk, axis=1), lens, rtol=1e-6)
+            gram = (blk / lens[:, None]) @ (blk / lens[:, None]).T
+            np.testing.assert_allclose(gram, np.eye(blk.shape[0]), atol=1e-6)
+        synth = ss.orthogonal_gaussian_rows(np.random.default_rng([7, d]), n, d)
+        np.testing.assert_allclose(out, synth, rtol=0, atol=2e-6 * np.abs(ref).max())
+    a = (ctypes.c_double * 4)()
+    f = (ctypes.c_float * 4)()
+    assert lib.slay_orthogonal_draws(4, 2, None, a, f) == _lib.SLAY_E_INVALID
+    assert lib.slay_orthogonal_draws(4, 0, a, a, f) == _lib.SLAY_E_INVALID
+    assert lib.slay_orthogonal_draws(0, 2, None, None, None) == _lib.SLAY_OK
