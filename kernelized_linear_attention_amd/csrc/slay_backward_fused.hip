@@ -1,5 +1,6 @@
-// slay_backward_fused.hip -- MFMA backward of the causal SLAY forward (bf16,
-// d = dv = 64, F = 256).
+// slay_backward_fused.hip -- MFMA backward of the causal SLAY forward (bf16
+// inputs and gradients, d = dv = 64, F = 256; smaller F on zero-padded
+// features).
 //
 // The forward ("SLAY: Geometry-Aware Spherical Linearized Attention with
 // Yat-Kernel", abstract; nubint.ai review, "Proposed method" bullets 1-6)
@@ -9,34 +10,46 @@
 //   U_j = [dS_T | dz_T] + sum_{i>=j} phi(q_i) g'_i^T,  [dS0 | dz0] = U_0,
 // then dq, dk through the feature map's Jacobian.
 //
-// Launches (one stream):
-//   1. the feature map writes phi(q), phi(k) to the workspace in bf16;
-//   2. the forward's segment-state pass and scan give S' before every segment;
-//   3. bwd_q_kernel, one workgroup per (head, segment), walks the segment's
-//      32-token chunks forward with S'^T in MFMA accumulators (each wave two
-//      16-feature blocks) and a bf16 copy in LDS: the masked block
-//      A = tril(phi(Q) phi(K)^T), num' = A V' + phi(Q) S', g', the masked block
-//      D = tril(G' V'^T), dphi(Q) = D phi(K) + G' S'^T, the segment's
-//      sum phi(Q)^T G' (written over its prefix state) and the state update;
-//   4. the reverse scan of those sums from [dS_T | dz_T] gives U after every
-//      segment, and its total [dS0 | dz0];
-//   5. bwd_kv_kernel walks each segment's chunks backward with U^T in
-//      accumulators: dphi(K) = D^T phi(Q) + V' U^T, dV = A^T G + phi(K) U,
-//      then U += phi(Q)^T G';
-//   6. vjp_kernel maps dphi back to dq and dk: y = P x (MFMA), the weights
-//      w_a = dphi 2 y_a E / |x|, w_g = dphi phi sqrt(beta) from the epilogue,
-//      dxh = P^T w (MFMA, the weights straight from the accumulators), then
-//      dx = (dxh - xh (xh . dxh)) / |x|.
-// Every MFMA operand comes from LDS tiles with rows padded to an odd multiple
-// of 16 bytes, or from accumulators of an earlier MFMA: a 16x16 accumulator
-// tile gives each lane four consecutive rows of one column, so two tiles
-// side by side are the eight consecutive k-values one lane feeds a 16x16x32
-// MFMA, provided the other operand is read with the same k order.  All
-// contractions use the one 16x16x32 bf16 shape, the 80-column ones as two full
-// steps plus a tail step whose second half is zero.  (An earlier tail step in
-// the 16x16x16 shape gave wrong results for a reason never established --
-// possibly an operand-layout mistake in that code; the one shape whose lane
-// layout is checked is used instead.)
+// Precision.  The gradient with respect to q is a small difference of large
+// terms: o_i depends on q_i only through how the scores of the i keys
+// before it change, so dq_i shrinks roughly like 1/sqrt(i) next to the
+// products S'_i g'_i it is formed from.  With bf16 operands (8 mantissa bits)
+// in those products the per-row error of dq grows to tens of percent at
+// L = 16384.  Every product that touches a state, g', phi or U therefore
+// runs on split operands: x = x_hi + x_lo, both bf16, so the pair carries 16
+// mantissa bits, and a product of two split values is taken as
+// x_hi y_hi + x_lo y_hi + x_hi y_lo (fp32 accumulation).  phi(q), phi(k) are
+// written once in fp32 by the feature map, the states and U live in fp32
+// MFMA accumulators, g' is formed and stored in fp32, and the masked
+// intra-chunk blocks A = tril(phi(Q) phi(K)^T) and D = tril(G' V'^T) are split
+// too where they feed the numerators and dphi (A only in bf16 for dV, whose
+// terms are all positive-weighted).  dphi leaves in bf16: its rounding does
+// not meet the cancellation.
+//
+// Token contractions run 16 tokens per step on the 16x16x32 bf16 MFMA: a
+// lane's eight k-slots hold four tokens' hi parts and the same four tokens'
+// lo parts, against the other operand's value for those tokens twice, so one
+// instruction applies a split operand exactly.  (The lane layouts of that
+// shape, checked on gfx950, are in slay_device.hpp.)
+//
+// Launches (one stream), one workgroup of 8 waves per (head, segment), wave
+// w owning features [32w, 32w + 32):
+//   1. the feature map writes phi(q), phi(k) in fp32;
+//   2. pb_state_kernel sums each segment's phi(K)^T V' (all but the last);
+//      the prefix scan turns them into S' before every segment (plus S0, z0);
+//   3. pb_g_kernel walks each segment with S' in accumulators, forms the
+//      numerators and denominators (per-wave partials over the wave's
+//      features, summed through LDS) and writes g' in fp32;
+//   4. pb_dq_kernel walks each segment again: dphi(Q) = D phi(K) + G' S'^T,
+//      and the segment's sum phi(Q)^T G' (written over its prefix state);
+//   5. the reverse scan gives U after every segment (plus dS_T, dz_T) and
+//      [dS0 | dz0];
+//   6. pb_dk_kernel walks each segment backward with U in accumulators:
+//      dphi(K) = D^T phi(Q) + V' U^T, dV = A^T G + phi(K) U (per-wave partials
+//      summed through LDS), then U += phi(Q)^T G';
+//   7. vjp_kernel maps dphi back to dq and dk.
+#include <algorithm>
+
 #include "slay_device.hpp"
 #include "slay_internal.hpp"
 
@@ -46,17 +59,6 @@ namespace {
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
-}
-// four values then four zeros: the 16-column tail block (columns 64..79) of
-// an 80-column contraction as one 16x16x32 step whose other half is zero
-__device__ __forceinline__ bf16x8 ld4z(const uint16_t* p) {
-  const uint2 a = *reinterpret_cast<const uint2*>(p);
-  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, 0u, 0u));
-}
-__device__ __forceinline__ bf16x8 ld4x2(const uint16_t* p0, const uint16_t* p1) {
-  const uint2 a = *reinterpret_cast<const uint2*>(p0);
-  const uint2 b = *reinterpret_cast<const uint2*>(p1);
-  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
 }
 __device__ __forceinline__ uint2 pk4(const f32x4& a) {
   return make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
@@ -68,347 +70,277 @@ __device__ __forceinline__ bf16x8 pk_pair(const f32x4& a, const f32x4& b) {
 }
 
 constexpr f32x4 kZero4 = {0.f, 0.f, 0.f, 0.f};
-constexpr uint16_t kOneBf16 = 0x3F80;
+constexpr uint2 kZero2 = {0u, 0u};
 
-template <int NF_>
-struct BwdK {
-  static constexpr int NF = NF_;          // 16-feature blocks
-  static constexpr int F = NF * 16;
-  static constexpr int C = 32;            // tokens per chunk step
-  static constexpr int NI = C / 16;       // 16-token blocks per chunk
-  static constexpr int DV = 64;
-  static constexpr int E = 80;            // [v | 1 | 0 ...] columns
-  static constexpr int NE = E / 16;
-  static constexpr int NA = NI * (NI + 1) / 2;  // causal 16x16 blocks of a C x C block
-  static constexpr int NW = NF / 2;       // waves: two feature blocks each
-  static constexpr int NT = NW * 64;
-  // LDS row strides in elements (odd multiples of 16 bytes)
-  static constexpr int LQ = F + 8, LT = C + 8, LV = E + 8, LS = F + 8, LA = C + 8, LN = E + 4;
-  static constexpr int oQ = 0;                    // phi(Q) [C][LQ]
-  static constexpr int oQT = oQ + C * LQ * 2;     // phi(Q)^T [F][LT]
-  static constexpr int oK = oQT + F * LT * 2;     // phi(K) [C][LQ]
-  static constexpr int oKT = oK + C * LQ * 2;     // phi(K)^T [F][LT]
-  static constexpr int oV = oKT + F * LT * 2;     // V' [C][LV]
-  static constexpr int oVT = oV + C * LV * 2;     // V'^T [E][LT]
-  static constexpr int oS = oVT + E * LT * 2;     // bf16 S'^T or U^T [E][LS]
-  static constexpr int oG = oS + E * LS * 2;      // G' [C][LV]
-  static constexpr int oGT = oG + C * LV * 2;     // G'^T [E][LT]
-  static constexpr int oA = oGT + E * LT * 2;     // masked A [C][LA] (bwd_q: A[i][j]; bwd_kv: A^T[j][i])
-  static constexpr int oD = oA + C * LA * 2;      // masked D (bwd_q: D[i][j]; bwd_kv: D^T[j][i])
-  static constexpr int oN = oD + C * LA * 2;      // fp32 [C][LN]: num' (bwd_q) or dV partials (bwd_kv)
-  static constexpr int kLds = oN + C * LN * 4;
-  static_assert(kLds <= 160 * 1024, "LDS budget");
-  static_assert(NF % 2 == 0, "two feature blocks per wave");
-  static_assert(NT == 512 && F == 256 && C == 32, "the staging maps 512 threads onto 32 x 256 tiles");
-};
+__device__ __forceinline__ bf16x8 cat(const uint2& a, const uint2& b) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+__device__ __forceinline__ f32x4 unpk4(const uint2& h) {
+  f32x4 r;
+  r[0] = __uint_as_float(h.x << 16);
+  r[1] = __uint_as_float(h.x & 0xFFFF0000u);
+  r[2] = __uint_as_float(h.y << 16);
+  r[3] = __uint_as_float(h.y & 0xFFFF0000u);
+  return r;
+}
+// x = hi + lo: hi the bf16 rounding of x, lo the bf16 rounding of the (exact) remainder
+__device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
+  hi = pk4(x);
+  lo = pk4(x - unpk4(hi));
+}
+// a split value as one operand: k-slots 0-3 the hi parts, 4-7 the lo parts
+__device__ __forceinline__ bf16x8 hilo(const f32x4& x) {
+  uint2 h, l;
+  split4(x, h, l);
+  return cat(h, l);
+}
 
-struct BwdParams {
-  const uint16_t* phiq;  // [n_heads * L][F] bf16
-  const uint16_t* phik;
+// ---------------------------------------------------------------------------
+// Precise segment kernels.
+constexpr int kT = 16;             // tokens per step
+constexpr int kF = 256;            // features
+constexpr int kE = 80;             // columns of v' and g' (dv + 1, padded to 16)
+constexpr int kNE = kE / 16;
+constexpr int kDV = 64;
+constexpr int kW = 8, kNT = kW * 64;  // waves; wave w owns feature blocks 2w, 2w + 1
+// LDS row strides in elements (odd multiples of 16 bytes)
+constexpr int kLT = kT + 8;        // [e][t] tiles
+constexpr int kLR = kE + 8;        // [t][e] tiles
+constexpr int kLP = kE + 4;        // fp32 partials [w][t][e]
+constexpr int kLPV = kDV + 4;
+
+struct PbParams {
+  const float* phiq;     // [n_heads * L][F] fp32
+  const float* phik;
   const uint16_t* v;     // [n_heads * L][64]
   const uint16_t* dout;  // [n_heads * L][64]
   int64_t L, seg_len;
   int n_seg;
-  float* states;         // [n_heads][n_seg][F/16][NE][64][4]
-  uint16_t* g;           // [n_heads * L][80]: [dout/den | h | 0 ...]
-  uint16_t* dphiq;       // [n_heads * L][F]
+  float* states;         // [n_heads][n_seg][F / 16][kNE][64][4]: element (f, e) at lane e%16 + 16 ((f%16)/4), slot f%4
+  float* g;              // [n_heads * L][80] fp32: [dout/den | h | 0 ...]
+  uint16_t* dphiq;       // [n_heads * L][F] bf16
   uint16_t* dphik;
   uint16_t* dv;          // [n_heads * L][64]
 };
 
-struct Lds {
-  uint16_t *Q, *QT, *K, *KT, *V, *VT, *S, *G, *GT, *A, *D;
-  float* N;
-};
-
-template <class K>
-__device__ __forceinline__ Lds lds_of(char* base) {
-  Lds l;
-  l.Q = reinterpret_cast<uint16_t*>(base + K::oQ);
-  l.QT = reinterpret_cast<uint16_t*>(base + K::oQT);
-  l.K = reinterpret_cast<uint16_t*>(base + K::oK);
-  l.KT = reinterpret_cast<uint16_t*>(base + K::oKT);
-  l.V = reinterpret_cast<uint16_t*>(base + K::oV);
-  l.VT = reinterpret_cast<uint16_t*>(base + K::oVT);
-  l.S = reinterpret_cast<uint16_t*>(base + K::oS);
-  l.G = reinterpret_cast<uint16_t*>(base + K::oG);
-  l.GT = reinterpret_cast<uint16_t*>(base + K::oGT);
-  l.A = reinterpret_cast<uint16_t*>(base + K::oA);
-  l.D = reinterpret_cast<uint16_t*>(base + K::oD);
-  l.N = reinterpret_cast<float*>(base + K::oN);
-  return l;
-}
-
-// 8 bf16 of a uint4 written down a column of a transposed tile
-__device__ __forceinline__ void scatter8(uint16_t* col, int stride, const uint4& x) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+// phi rows t0 + 4g + r (r < 4) of feature 16 fb + c: the "four tokens of a lane" layout of the token contractions
+__device__ __forceinline__ f32x4 load_tok4(const float* __restrict__ x, int64_t row0, int n, int fb, int g, int c) {
+  f32x4 r;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    col[(2 * t) * stride] = (uint16_t)(w[t] & 0xFFFFu);
-    col[(2 * t + 1) * stride] = (uint16_t)(w[t] >> 16);
-  }
+  for (int i = 0; i < 4; ++i) r[i] = (4 * g + i < n) ? x[(row0 + 4 * g + i) * kF + 16 * fb + c] : 0.f;
+  return r;
 }
-
-// Regions no chunk writes stay zero: columns 65..79 of V', G' (rows of their
-// transposes) and the blocks of the masked tiles above the diagonal.
-template <class K>
-__device__ void zero_constant_regions(const Lds& s, int tid) {
-  for (int idx = tid; idx < K::C * 15; idx += K::NT) {
-    const int r = idx / 15, e = 65 + idx % 15;
-    s.V[r * K::LV + e] = 0;
-    s.G[r * K::LV + e] = 0;
-    s.VT[e * K::LT + r] = 0;
-    s.GT[e * K::LT + r] = 0;
-  }
-  for (int idx = tid; idx < K::C * K::LA; idx += K::NT) {
-    s.A[idx] = 0;
-    s.D[idx] = 0;
-  }
-}
-
-// Chunk staging, software-pipelined: the global loads of chunk c+1 are issued
-// into registers right after chunk c is written to LDS, so they are in flight
-// while chunk c is computed.  A thread moves one 4-row x 8-column block of a
-// feature tile: four 16-byte row pieces, written as rows and, transposed in
-// registers (v_perm), as eight 8-byte column pieces of the transposed tile.
-__device__ __forceinline__ void transpose4x8(const uint4 (&in)[4], uint2 (&out)[8]) {
-  const uint32_t w[4][4] = {{in[0].x, in[0].y, in[0].z, in[0].w},
-                            {in[1].x, in[1].y, in[1].z, in[1].w},
-                            {in[2].x, in[2].y, in[2].z, in[2].w},
-                            {in[3].x, in[3].y, in[3].z, in[3].w}};
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    out[2 * u] = make_uint2(lo16_pair(w[0][u], w[1][u]), lo16_pair(w[2][u], w[3][u]));
-    out[2 * u + 1] = make_uint2(hi16_pair(w[0][u], w[1][u]), hi16_pair(w[2][u], w[3][u]));
-  }
-}
-
-__device__ __forceinline__ uint4 ld_row(const uint16_t* p, bool ok) {
-  return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-}
-
-// block u of a [C][width] tile: rows 4(u % 8) .. +3, columns 8(u / 8) .. +7
-template <class K>
-__device__ __forceinline__ void load_block(const uint16_t* src, int width, int64_t row0, int n, int u,
-                                           uint4 (&blk)[4]) {
-  const int r = 4 * (u & 7), c = 8 * (u >> 3);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) blk[t] = ld_row(src + (row0 + r + t) * width + c, r + t < n);
-}
-
-template <class K>
-__device__ __forceinline__ void store_block(uint16_t* rows, int ld_rows, uint16_t* cols, int u, const uint4 (&blk)[4]) {
-  const int r = 4 * (u & 7), c = 8 * (u >> 3);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) *reinterpret_cast<uint4*>(rows + (r + t) * ld_rows + c) = blk[t];
-  uint2 tr[8];
-  transpose4x8(blk, tr);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) *reinterpret_cast<uint2*>(cols + (c + t) * K::LT + r) = tr[t];
-}
-
-// the ones column of V' (and V'^T) counts the chunk's valid rows only
-template <class K, bool TV>
-__device__ __forceinline__ void store_ones(const Lds& s, int n, int tid) {
-  for (int r = tid; r < K::C; r += K::NT) {
-    const uint16_t one = r < n ? kOneBf16 : (uint16_t)0;
-    s.V[r * K::LV + K::DV] = one;
-    if (TV) s.VT[K::DV * K::LT + r] = one;
-  }
-}
-
-// bwd_q: threads < 256 move a phi(Q) block, the others a phi(K) block; threads
-// < 256 also one 16-byte piece of v (row t/8, columns 8(t%8)..) and of dout.
-struct PrefQ {
-  uint4 blk[4];
-  uint4 v, dout;
-};
-
-template <class K>
-__device__ __forceinline__ void load_q(const BwdParams& p, int64_t row0, int n, int tid, PrefQ& pf) {
-  load_block<K>(tid < 256 ? p.phiq : p.phik, K::F, row0, n, tid & 255, pf.blk);
-  const int r = (tid & 255) >> 3, c = 8 * (tid & 7);
-  pf.v = ld_row(p.v + (row0 + r) * K::DV + c, tid < 256 && r < n);
-  pf.dout = ld_row(p.dout + (row0 + r) * K::DV + c, tid < 256 && r < n);
-}
-
-template <class K>
-__device__ __forceinline__ void store_q(const Lds& s, const PrefQ& pf, int n, int tid) {
-  store_block<K>(tid < 256 ? s.Q : s.K, K::LQ, tid < 256 ? s.QT : s.KT, tid & 255, pf.blk);
-  if (tid < 256) {
-    const int r = tid >> 3, c = 8 * (tid & 7);
-    *reinterpret_cast<uint4*>(s.V + r * K::LV + c) = pf.v;
-    scatter8(s.VT + c * K::LT + r, K::LT, pf.v);
-  }
-  store_ones<K, true>(s, n, tid);
-}
-
-// bwd_kv: threads < 256 move a phi(Q) block (rows and transposed) and one
-// piece of v; the others four row pieces of phi(K) and, for the first 80, a
-// block of g' (rows and transposed).
-struct PrefKV {
-  uint4 blk[4];
-  uint4 gb[4];
-  uint4 v;
-};
-
-template <class K>
-__device__ __forceinline__ void load_kv(const BwdParams& p, int64_t row0, int n, int tid, PrefKV& pf) {
-  const int u = tid & 255;
-  const bool lo = tid < 256;
-  if (lo) {
-    load_block<K>(p.phiq, K::F, row0, n, u, pf.blk);
+// phi row t0 + c, features 32 w + 4g .. +3 and 32 w + 16 + 4g .. +3: a lane's k-slots of a contraction over the
+// wave's 32 features (the order of two accumulator tiles side by side)
+__device__ __forceinline__ void load_feat8(const float* __restrict__ x, int64_t row0, int n, int w, int g, int c,
+                                           f32x4& a, f32x4& b) {
+  if (c < n) {
+    const float* p = x + (row0 + c) * kF + 32 * w + 4 * g;
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 16);
   } else {
+    a = kZero4;
+    b = kZero4;
+  }
+}
+
+// V' = [v | 1 | 0] of the step's tokens (zero rows past n) as [t][e] rows and [e][t] columns
+__device__ __forceinline__ void stage_v(const uint16_t* __restrict__ v, int64_t row0, int n, uint16_t* VR,
+                                        uint16_t* VT, int tid) {
+  if (tid < kT * 8) {
+    const int t = tid >> 3, e0 = 8 * (tid & 7);
+    const uint4 x = t < n ? *reinterpret_cast<const uint4*>(v + (row0 + t) * kDV + e0) : make_uint4(0, 0, 0, 0);
+    if (VR) *reinterpret_cast<uint4*>(VR + t * kLR + e0) = x;
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int idx = u + 256 * t, r = idx >> 5, c = 8 * (idx & 31);
-      pf.blk[t] = ld_row(p.phik + (row0 + r) * K::F + c, r < n);
+    for (int i = 0; i < 4; ++i) {
+      VT[(e0 + 2 * i) * kLT + t] = (uint16_t)(w[i] & 0xFFFFu);
+      VT[(e0 + 2 * i + 1) * kLT + t] = (uint16_t)(w[i] >> 16);
+    }
+  } else if (tid < kT * 8 + kT) {
+    const int t = tid - kT * 8;
+    const uint16_t one = t < n ? (uint16_t)0x3F80 : (uint16_t)0;
+    if (VR) {
+      *reinterpret_cast<uint4*>(VR + t * kLR + kDV) = make_uint4(one, 0, 0, 0);
+      *reinterpret_cast<uint4*>(VR + t * kLR + kDV + 8) = make_uint4(0, 0, 0, 0);
+    }
+    VT[kDV * kLT + t] = one;
+#pragma unroll
+    for (int e = kDV + 1; e < kE; ++e) VT[e * kLT + t] = 0;
+  }
+}
+
+// g' of the step's tokens (fp32 in HBM) split into hi and lo bf16, as [t][e] rows and [e][t] columns
+__device__ __forceinline__ void stage_g(const float* __restrict__ gsrc, int64_t row0, int n, uint16_t* GRh,
+                                        uint16_t* GRl, uint16_t* GTh, uint16_t* GTl, int tid) {
+  if (tid < kT * (kE / 4)) {
+    const int t = tid / (kE / 4), e0 = 4 * (tid % (kE / 4));
+    const f32x4 x = t < n ? *reinterpret_cast<const f32x4*>(gsrc + (row0 + t) * kE + e0) : kZero4;
+    uint2 h, l;
+    split4(x, h, l);
+    *reinterpret_cast<uint2*>(GRh + t * kLR + e0) = h;
+    *reinterpret_cast<uint2*>(GRl + t * kLR + e0) = l;
+    const uint32_t hw[2] = {h.x, h.y}, lw[2] = {l.x, l.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      GTh[(e0 + 2 * i) * kLT + t] = (uint16_t)(hw[i] & 0xFFFFu);
+      GTh[(e0 + 2 * i + 1) * kLT + t] = (uint16_t)(hw[i] >> 16);
+      GTl[(e0 + 2 * i) * kLT + t] = (uint16_t)(lw[i] & 0xFFFFu);
+      GTl[(e0 + 2 * i + 1) * kLT + t] = (uint16_t)(lw[i] >> 16);
     }
   }
-  const int r = u >> 3, c = 8 * (u & 7);
-  pf.v = ld_row(p.v + (row0 + r) * K::DV + c, lo && r < n);
-  // g' blocks on threads 256 .. 335 (80 blocks of 4 rows x 8 columns); the rest load nothing
-  const bool gok = !lo && u < 8 * (K::E / 8);
-  load_block<K>(p.g, K::E, row0, gok ? n : 0, gok ? u : 0, pf.gb);
 }
 
-template <class K>
-__device__ __forceinline__ void store_kv(const Lds& s, const PrefKV& pf, int n, int tid) {
-  if (tid < 256) {
-    store_block<K>(s.Q, K::LQ, s.QT, tid, pf.blk);
-    const int r = tid >> 3, c = 8 * (tid & 7);
-    *reinterpret_cast<uint4*>(s.V + r * K::LV + c) = pf.v;
-  } else {
-    const int u = tid - 256;
+// four consecutive tokens of column e of an [e][t] tile: the lane's k-slots 4g .. 4g+3
+__device__ __forceinline__ uint2 col4(const uint16_t* T, int e, int g) {
+  return *reinterpret_cast<const uint2*>(T + e * kLT + 4 * g);
+}
+// columns 16 e0 + 4g .. +3 and 16 e1 + 4g .. +3 of row r of a [t][e] tile (e1 < 0: zeros)
+__device__ __forceinline__ bf16x8 row4x2(const uint16_t* R, int r, int e0, int e1, int g) {
+  const uint2 a = *reinterpret_cast<const uint2*>(R + r * kLR + 16 * e0 + 4 * g);
+  const uint2 b = e1 >= 0 ? *reinterpret_cast<const uint2*>(R + r * kLR + 16 * e1 + 4 * g) : kZero2;
+  return cat(a, b);
+}
+
+// state item of (head, seg) and its accumulator tiles: element (f = 16 fb + 4g + r, e = 16 eb + c) of the
+// tile (fb, eb) in lane 16 g + c, slot r ("C[f][e]" order: one 16-byte access per lane)
+__device__ __forceinline__ float* item_ptr(const PbParams& p, int64_t h, int seg) {
+  return p.states + (h * p.n_seg + seg) * (int64_t)(kF * kE);
+}
+__device__ __forceinline__ f32x4 load_fe(const float* item, int fb, int eb, int lane) {
+  return *reinterpret_cast<const f32x4*>(item + ((fb * kNE + eb) * 64 + lane) * 4);
+}
+__device__ __forceinline__ void store_fe(float* item, int fb, int eb, int lane, const f32x4& x) {
+  *reinterpret_cast<f32x4*>(item + ((fb * kNE + eb) * 64 + lane) * 4) = x;
+}
+// the transposed tile order ("C[e][f]"): element (e = 16 eb + 4g + r, f = 16 fb + c) in lane 16 g + c, slot r
+__device__ __forceinline__ f32x4 load_ef(const float* item, int fb, int eb, int g, int c) {
+  f32x4 x;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int idx = u + 256 * t, r = idx >> 5, c = 8 * (idx & 31);
-      *reinterpret_cast<uint4*>(s.K + r * K::LQ + c) = pf.blk[t];
-    }
-    if (u < 8 * (K::E / 8)) store_block<K>(s.G, K::LV, s.GT, u, pf.gb);
-  }
-  store_ones<K, false>(s, n, tid);
+  for (int r = 0; r < 4; ++r) x[r] = item[((fb * kNE + eb) * 64 + (4 * g + r) + 16 * (c >> 2)) * 4 + (c & 3)];
+  return x;
 }
 
-// Fragment-ordered state item: element (f, e) of tile (f/16, e/16) sits at
-// lane (e%16) + 16((f%16)/4), slot f%4.  The transposed accumulator
-// T[eb][j] (C[m = e][n = f], f in feature block fb = 2 wave + j) of this lane
-// holds (f = fb*16 + l%16, e = eb*16 + 4(l/16) + r).
-template <class K>
-__device__ __forceinline__ int item_index(int fb, int eb, int g, int c16, int r) {
-  return ((fb * K::NE + eb) * 64 + (4 * g + r) + 16 * (c16 >> 2)) * 4 + (c16 & 3);
-}
-
-// bf16 copy of the state, [e][f] rows.  Lanes l, l^1 hold features f, f+1
-// of rows e..e+3: the even lane writes the (f, f+1) words of rows e, e+1, the
-// odd lane those of e+2, e+3 (one 4-byte store per row instead of two 2-byte
-// ones); v_perm takes bytes 0-3 from this lane's word, 4-7 from the neighbour's.
-template <class K>
-__device__ __forceinline__ void write_state_copy(const Lds& s, const f32x4 (&T)[K::NE][2], int wave, int g, int c16) {
-  const bool odd = c16 & 1;
-  const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;
-  const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;
+// (1) sum over each segment's keys (all segments but the last) of phi(k) v'^T, in the item order
+__global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
+  __shared__ __align__(16) uint16_t VT[kE * kLT];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_items = p.n_seg - 1;
+  const int64_t h = blockIdx.x / n_items;
+  const int seg = (int)(blockIdx.x - h * n_items);
+  const int64_t t_begin = seg * p.seg_len;
+  const int64_t t_end = min<int64_t>(p.L, t_begin + p.seg_len);
+  f32x4 S[2][kNE];
 #pragma unroll
-  for (int eb = 0; eb < K::NE; ++eb)
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int eb = 0; eb < kNE; ++eb) S[j][eb] = kZero4;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kT) {
+    const int n = (int)min<int64_t>(kT, t_end - t0);
+    const int64_t row0 = h * p.L + t0;
+    f32x4 kt[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) kt[j] = load_tok4(p.phik, row0, n, 2 * w + j, g, c);
+    __syncthreads();
+    stage_v(p.v, row0, n, nullptr, VT, tid);
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int fb = 2 * wave + j;
-      const uint2 pk = pk4(T[eb][j]);
-      const uint32_t mine = odd ? pk.y : pk.x;
-      const uint32_t recv = swap_lane_pair(odd ? pk.x : pk.y);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(s.S + (eb * 16 + 4 * g + (odd ? 2 : 0)) * K::LS + fb * 16 + (c16 & ~1));
-      dst[0] = __builtin_amdgcn_perm(recv, mine, sel0);
-      dst[K::LS / 2] = __builtin_amdgcn_perm(recv, mine, sel1);
+      const bf16x8 a = hilo(kt[j]);
+#pragma unroll
+      for (int eb = 0; eb < kNE; ++eb) {
+        const uint2 v4 = col4(VT, 16 * eb + c, g);
+        S[j][eb] = mfma_bf16(a, cat(v4, v4), S[j][eb]);
+      }
     }
+  }
+  float* item = item_ptr(p, h, seg);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int eb = 0; eb < kNE; ++eb) store_fe(item, 2 * w + j, eb, lane, S[j][eb]);
 }
 
-// the causal 16x16 blocks (ib, jb), jb <= ib, in order (0,0), (1,0), (1,1), ...
-__device__ __forceinline__ void causal_block(int it, int& ib, int& jb) {
-  ib = 0;
-  while ((ib + 1) * (ib + 2) / 2 <= it) ++ib;
-  jb = it - ib * (ib + 1) / 2;
-}
-
-template <class K>
-__global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
-  extern __shared__ __align__(16) char lds_raw[];
-  const Lds s = lds_of<K>(lds_raw);
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// (3) numerators, denominators and g' of every token, with S' (the item: the state before the segment) in
+// accumulators
+__global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
+  __shared__ __align__(16) uint16_t VT[kE * kLT];
+  __shared__ __align__(16) float P[kW * kT * kLP];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t h = blockIdx.x / p.n_seg;
   const int seg = (int)(blockIdx.x - h * p.n_seg);
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = min<int64_t>(p.L, t_begin + p.seg_len);
-  float* item = p.states + (h * p.n_seg + seg) * (int64_t)(K::F * K::E);
-
-  zero_constant_regions<K>(s, tid);
-  f32x4 ST[K::NE][2], UT[K::NE][2];
+  const float* item = item_ptr(p, h, seg);
+  f32x4 S[2][kNE];
 #pragma unroll
-  for (int eb = 0; eb < K::NE; ++eb)
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int eb = 0; eb < kNE; ++eb) S[j][eb] = load_fe(item, 2 * w + j, eb, lane);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kT) {
+    const int n = (int)min<int64_t>(kT, t_end - t0);
+    const int64_t row0 = h * p.L + t0;
+    f32x4 qa, qb, ka, kb, kt[2];
+    load_feat8(p.phiq, row0, n, w, g, c, qa, qb);
+    load_feat8(p.phik, row0, n, w, g, c, ka, kb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) kt[j] = load_tok4(p.phik, row0, n, 2 * w + j, g, c);
+    __syncthreads();  // the previous step's readers of VT and P are done
+    stage_v(p.v, row0, n, nullptr, VT, tid);
+    __syncthreads();
+    // this wave's part of A^T[j][i] = sum_f phi(K_j)_f phi(Q_i)_f over its features (split phi), masked j <= i
+    uint2 qh0, ql0, qh1, ql1, kh0, kl0, kh1, kl1;
+    split4(qa, qh0, ql0);
+    split4(qb, qh1, ql1);
+    split4(ka, kh0, kl0);
+    split4(kb, kh1, kl1);
+    const bf16x8 qh = cat(qh0, qh1), ql = cat(ql0, ql1), kh = cat(kh0, kh1);
+    f32x4 at = mfma_bf16(kh, qh, kZero4);  // lane: j = 4g + r, i = c
+    at = mfma_bf16(cat(kl0, kl1), qh, at);
+    at = mfma_bf16(kh, ql, at);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) at[r] = (4 * g + r <= c && c < n) ? at[r] : 0.f;
+    const bf16x8 atb = hilo(at);  // A^T split: slots 0-3 hi, 4-7 lo of the same four keys
+    // num'^T[e][i] partial = V'^T A^T (this wave's A part) + S'^T phi(Q)^T over this wave's features
+#pragma unroll
+    for (int eb = 0; eb < kNE; ++eb) {
+      const uint2 v4 = col4(VT, 16 * eb + c, g);
+      f32x4 acc = mfma_bf16(cat(v4, v4), atb, kZero4);
+      uint2 s0h, s0l, s1h, s1l;
+      split4(S[0][eb], s0h, s0l);
+      split4(S[1][eb], s1h, s1l);
+      const bf16x8 sh = cat(s0h, s1h), sl = cat(s0l, s1l);
+      acc = mfma_bf16(sh, qh, acc);
+      acc = mfma_bf16(sl, qh, acc);
+      acc = mfma_bf16(sh, ql, acc);
+      *reinterpret_cast<f32x4*>(P + (w * kT + c) * kLP + 16 * eb + 4 * g) = acc;  // lane: e = 16 eb + 4g + r, i = c
+    }
+    // S' += phi(K)^T V' for this wave's features (after its use: S' is the state before the chunk)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+      const bf16x8 a = hilo(kt[j]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ST[eb][j][r] = item[item_index<K>(2 * wave + j, eb, g, c16, r)];
-      UT[eb][j] = kZero4;
-    }
-
-  PrefQ pf;
-  load_q<K>(p, h * p.L + t_begin, (int)min<int64_t>(K::C, t_end - t_begin), tid, pf);
-  // Vector loads and stores retire in issue order and share one counter.  The
-  // step loop starts with no load in flight and waits for its prefetch once,
-  // before its own stores; a wait for the prefetch issued later would also
-  // wait for the previous step's stores.
-  wait_vmem();
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += K::C) {
-    const int n = (int)min<int64_t>(K::C, t_end - t0);
-    const int64_t row0 = h * p.L + t0;
-    __syncthreads();
-    // the state before this chunk, as the bf16 copy [1] reads (written here, a
-    // phase after the update, so the update's MFMAs are done by now)
-    write_state_copy<K>(s, ST, wave, g, c16);
-    store_q<K>(s, pf, n, tid);
-    const uint4 dcur = pf.dout;
-    if (t0 + K::C < t_end) load_q<K>(p, row0 + K::C, (int)min<int64_t>(K::C, t_end - t0 - K::C), tid, pf);
-    __syncthreads();
-    // [1] A^T blocks (masked, to s.A as A[i][j]) and phi(Q) S' (to s.N as num'[i][e])
-    for (int it = wave; it < K::NA + K::NI * K::NE; it += K::NW) {
-      f32x4 acc = kZero4;
-      if (it < K::NA) {
-        int ib, jb;
-        causal_block(it, ib, jb);
-#pragma unroll
-        for (int kk = 0; kk < K::F; kk += 32)
-          acc = mfma_bf16(ld8(s.K + (jb * 16 + c16) * K::LQ + kk + 8 * g), ld8(s.Q + (ib * 16 + c16) * K::LQ + kk + 8 * g),
-                          acc);
-        const int i = ib * 16 + c16;
-        f32x4 m;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = (jb * 16 + 4 * g + r <= i) ? acc[r] : 0.f;
-        *reinterpret_cast<uint2*>(s.A + i * K::LA + jb * 16 + 4 * g) = pk4(m);
-      } else {
-        const int ib = (it - K::NA) / K::NE, eb = (it - K::NA) - ((it - K::NA) / K::NE) * K::NE;
-#pragma unroll
-        for (int kk = 0; kk < K::F; kk += 32)
-          acc = mfma_bf16(ld8(s.S + (eb * 16 + c16) * K::LS + kk + 8 * g), ld8(s.Q + (ib * 16 + c16) * K::LQ + kk + 8 * g),
-                          acc);
-        *reinterpret_cast<f32x4*>(s.N + (ib * 16 + c16) * K::LN + eb * 16 + 4 * g) = acc;
+      for (int eb = 0; eb < kNE; ++eb) {
+        const uint2 v4 = col4(VT, 16 * eb + c, g);
+        S[j][eb] = mfma_bf16(a, cat(v4, v4), S[j][eb]);
       }
     }
     __syncthreads();
-    // [2] num'^T += V'^T A^T over the chunk's keys
-    for (int it = wave; it < K::NI * K::NE; it += K::NW) {
-      const int ib = it / K::NE, eb = it - (it / K::NE) * K::NE;
-      f32x4* pn = reinterpret_cast<f32x4*>(s.N + (ib * 16 + c16) * K::LN + eb * 16 + 4 * g);
-      *pn = mfma_bf16(ld8(s.VT + (eb * 16 + c16) * K::LT + 8 * g), ld8(s.A + (ib * 16 + c16) * K::LA + 8 * g), *pn);
-    }
-    __syncthreads();
-    wait_vmem();  // the next chunk's prefetch, before this step's stores
-    // [3] g' = [dout / den | -(dout . num) / den^2 | 0]: eight threads per token
-    static_assert(K::NT >= K::C * 8, "one pass: thread t holds the dout piece of token t/8");
-    if (tid < K::C * 8) {
-      const int idx = tid;
-      const int r = idx >> 3, e0 = (idx & 7) * 8;
-      const uint4 dr = dcur;  // this thread's piece of dout, staged with the chunk
+    // g' = [dout / den | -(dout . num) / den^2 | 0]: eight threads per token, eight columns each
+    if (tid < kT * 8) {
+      const int i = tid >> 3, e0 = 8 * (tid & 7);
+      f32x4 n0 = kZero4, n1 = kZero4;
+      float den = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kW; ++ww) {
+        const float* pr = P + (ww * kT + i) * kLP;
+        n0 += *reinterpret_cast<const f32x4*>(pr + e0);
+        n1 += *reinterpret_cast<const f32x4*>(pr + e0 + 4);
+        den += pr[kDV];
+      }
+      const uint4 dr = i < n ? *reinterpret_cast<const uint4*>(p.dout + (row0 + i) * kDV + e0) : make_uint4(0, 0, 0, 0);
       const uint32_t dw[4] = {dr.x, dr.y, dr.z, dr.w};
       float dn[8];
 #pragma unroll
@@ -416,210 +348,246 @@ __global__ __launch_bounds__(K::NT) void bwd_q_kernel(BwdParams p) {
         dn[2 * t] = __uint_as_float(dw[t] << 16);
         dn[2 * t + 1] = __uint_as_float(dw[t] & 0xFFFF0000u);
       }
-      const float* nr = s.N + r * K::LN;
       float dot = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) dot = fmaf(dn[t], nr[e0 + t], dot);
+      for (int t = 0; t < 4; ++t) dot = fmaf(dn[t], n0[t], fmaf(dn[4 + t], n1[t], dot));
       dot += __shfl_xor(dot, 1, 64);
       dot += __shfl_xor(dot, 2, 64);
       dot += __shfl_xor(dot, 4, 64);
-      const float inv = r < n ? 1.f / nr[K::DV] : 0.f;
-      uint4 gv;
-      gv.x = pack_bf16x2(dn[0] * inv, dn[1] * inv);
-      gv.y = pack_bf16x2(dn[2] * inv, dn[3] * inv);
-      gv.z = pack_bf16x2(dn[4] * inv, dn[5] * inv);
-      gv.w = pack_bf16x2(dn[6] * inv, dn[7] * inv);
-      *reinterpret_cast<uint4*>(s.G + r * K::LV + e0) = gv;
-      scatter8(s.GT + e0 * K::LT + r, K::LT, gv);
-      if (r < n) *reinterpret_cast<uint4*>(p.g + (row0 + r) * K::E + e0) = gv;
-      if ((idx & 7) == 0) {
-        const uint16_t hb = f32_to_bf16(-dot * inv * inv);
-        s.G[r * K::LV + K::DV] = hb;
-        s.GT[K::DV * K::LT + r] = hb;
-        if (r < n) {
-          *reinterpret_cast<uint4*>(p.g + (row0 + r) * K::E + K::DV) = make_uint4(hb, 0, 0, 0);
-          *reinterpret_cast<uint4*>(p.g + (row0 + r) * K::E + K::DV + 8) = make_uint4(0, 0, 0, 0);
+      if (i < n) {
+        const float inv = 1.f / den;
+        float* gr = p.g + (row0 + i) * kE;
+        f32x4 g0, g1;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          g0[t] = dn[t] * inv;
+          g1[t] = dn[4 + t] * inv;
+        }
+        *reinterpret_cast<f32x4*>(gr + e0) = g0;
+        *reinterpret_cast<f32x4*>(gr + e0 + 4) = g1;
+        if ((tid & 7) == 0) {
+          const f32x4 hz = {-dot * inv * inv, 0.f, 0.f, 0.f};
+          *reinterpret_cast<f32x4*>(gr + kDV) = hz;
+          *reinterpret_cast<f32x4*>(gr + kDV + 4) = kZero4;
+          *reinterpret_cast<f32x4*>(gr + kDV + 8) = kZero4;
+          *reinterpret_cast<f32x4*>(gr + kDV + 12) = kZero4;
         }
       }
     }
-    __syncthreads();
-    // [4] D (masked, to s.D as D[i][j]); dphi(Q)^T = S' G'^T; sum phi(Q)^T G'; S' += phi(K)^T V'
-    for (int it = wave; it < K::NA; it += K::NW) {
-      int ib, jb;
-      causal_block(it, ib, jb);
-      const uint16_t* vr = s.V + (jb * 16 + c16) * K::LV;
-      const uint16_t* gr = s.G + (ib * 16 + c16) * K::LV;
-      f32x4 acc = mfma_bf16(ld8(vr + 8 * g), ld8(gr + 8 * g), kZero4);
-      acc = mfma_bf16(ld8(vr + 32 + 8 * g), ld8(gr + 32 + 8 * g), acc);
-      acc = mfma_bf16(ld4z(vr + 64 + 4 * g), ld4z(gr + 64 + 4 * g), acc);
-      const int i = ib * 16 + c16;
-      f32x4 m;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) m[r] = (jb * 16 + 4 * g + r <= i) ? acc[r] : 0.f;
-      *reinterpret_cast<uint2*>(s.D + i * K::LA + jb * 16 + 4 * g) = pk4(m);
-    }
-    f32x4 DQ[2][K::NI];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16x8 a01 = pk_pair(ST[0][j], ST[1][j]);
-      const bf16x8 a23 = pk_pair(ST[2][j], ST[3][j]);
-      const bf16x8 a4 = pk_pair(ST[4][j], kZero4);
-#pragma unroll
-      for (int ib = 0; ib < K::NI; ++ib) {
-        const uint16_t* gr = s.G + (ib * 16 + c16) * K::LV + 4 * g;
-        f32x4 acc = mfma_bf16(a01, ld4x2(gr, gr + 16), kZero4);
-        acc = mfma_bf16(a23, ld4x2(gr + 32, gr + 48), acc);
-        DQ[j][ib] = mfma_bf16(a4, ld4z(gr + 64), acc);
-      }
-    }
-#pragma unroll
-    for (int eb = 0; eb < K::NE; ++eb) {
-      const bf16x8 gt = ld8(s.GT + (eb * 16 + c16) * K::LT + 8 * g);
-      const bf16x8 vt = ld8(s.VT + (eb * 16 + c16) * K::LT + 8 * g);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int fb = 2 * wave + j;
-        UT[eb][j] = mfma_bf16(gt, ld8(s.QT + (fb * 16 + c16) * K::LT + 8 * g), UT[eb][j]);
-        ST[eb][j] = mfma_bf16(vt, ld8(s.KT + (fb * 16 + c16) * K::LT + 8 * g), ST[eb][j]);
-      }
-    }
-    __syncthreads();
-    // [5] dphi(Q)^T += phi(K)^T D^T; write dphi(Q)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int fb = 2 * wave + j;
-      const bf16x8 kt = ld8(s.KT + (fb * 16 + c16) * K::LT + 8 * g);
-#pragma unroll
-      for (int ib = 0; ib < K::NI; ++ib) {
-        const f32x4 acc = mfma_bf16(kt, ld8(s.D + (ib * 16 + c16) * K::LA + 8 * g), DQ[j][ib]);
-        const int i = ib * 16 + c16;
-        if (i < n) *reinterpret_cast<uint2*>(p.dphiq + (row0 + i) * K::F + fb * 16 + 4 * g) = pk4(acc);
-      }
-    }
   }
-  // the segment's sum of phi(Q)^T G' replaces its (consumed) prefix state
-#pragma unroll
-  for (int eb = 0; eb < K::NE; ++eb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) item[item_index<K>(2 * wave + j, eb, g, c16, r)] = UT[eb][j][r];
 }
 
-template <class K>
-__global__ __launch_bounds__(K::NT) void bwd_kv_kernel(BwdParams p) {
-  extern __shared__ __align__(16) char lds_raw[];
-  const Lds s = lds_of<K>(lds_raw);
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// (4) dphi(Q) = D phi(K) + G' S'^T for this wave's features, and the segment's sum phi(Q)^T G' (written over
+// the item once the walk is done)
+__global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
+  __shared__ __align__(16) uint16_t VT[kE * kLT];
+  __shared__ __align__(16) uint16_t VR[kT * kLR];
+  __shared__ __align__(16) uint16_t GRh[kT * kLR];
+  __shared__ __align__(16) uint16_t GRl[kT * kLR];
+  __shared__ __align__(16) uint16_t GTh[kE * kLT];
+  __shared__ __align__(16) uint16_t GTl[kE * kLT];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t h = blockIdx.x / p.n_seg;
   const int seg = (int)(blockIdx.x - h * p.n_seg);
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = min<int64_t>(p.L, t_begin + p.seg_len);
-  const float* item = p.states + (h * p.n_seg + seg) * (int64_t)(K::F * K::E);
-
-  zero_constant_regions<K>(s, tid);
-  f32x4 UT[K::NE][2];
+  float* item = item_ptr(p, h, seg);
+  f32x4 S[kNE][2], U[2][kNE];  // S' as C[e][f] (contractions over e), U as C[f][e]
 #pragma unroll
-  for (int eb = 0; eb < K::NE; ++eb)
+  for (int eb = 0; eb < kNE; ++eb)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) UT[eb][j][r] = item[item_index<K>(2 * wave + j, eb, g, c16, r)];
-
-  const int n_steps = (int)((t_end - t_begin + K::C - 1) / K::C);
-  auto rows_of = [&](int cs) { return (int)min<int64_t>(K::C, t_end - (t_begin + (int64_t)cs * K::C)); };
-  PrefKV pf;
-  load_kv<K>(p, h * p.L + t_begin + (int64_t)(n_steps - 1) * K::C, rows_of(n_steps - 1), tid, pf);
-  wait_vmem();  // as in bwd_q_kernel: no load in flight when the step loop starts
-  for (int cs = n_steps - 1; cs >= 0; --cs) {
-    const int64_t t0 = t_begin + (int64_t)cs * K::C;
-    const int n = rows_of(cs);
+    for (int j = 0; j < 2; ++j) {
+      S[eb][j] = load_ef(item, 2 * w + j, eb, g, c);
+      U[j][eb] = kZero4;
+    }
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kT) {
+    const int n = (int)min<int64_t>(kT, t_end - t0);
     const int64_t row0 = h * p.L + t0;
-    __syncthreads();
-    write_state_copy<K>(s, UT, wave, g, c16);  // U after this chunk, as the bf16 copy [1] reads
-    store_kv<K>(s, pf, n, tid);
-    if (cs > 0) load_kv<K>(p, row0 - K::C, K::C, tid, pf);
-    __syncthreads();
-    // [1] A^T and D^T (masked, as [j][i]); dV^T = U^T phi(K)^T (to s.N as [j][e])
-    for (int it = wave; it < 2 * K::NA + (K::DV / 16) * K::NI; it += K::NW) {
-      if (it < 2 * K::NA) {
-        int ib, jb;
-        causal_block(it % K::NA, ib, jb);
-        f32x4 acc = kZero4;
-        if (it < K::NA) {  // A[i][j] = phi(Q_i) . phi(K_j)
-#pragma unroll
-          for (int kk = 0; kk < K::F; kk += 32)
-            acc = mfma_bf16(ld8(s.Q + (ib * 16 + c16) * K::LQ + kk + 8 * g),
-                            ld8(s.K + (jb * 16 + c16) * K::LQ + kk + 8 * g), acc);
-        } else {  // D[i][j] = g'_i . v'_j
-          const uint16_t* gr = s.G + (ib * 16 + c16) * K::LV;
-          const uint16_t* vr = s.V + (jb * 16 + c16) * K::LV;
-          acc = mfma_bf16(ld8(gr + 8 * g), ld8(vr + 8 * g), acc);
-          acc = mfma_bf16(ld8(gr + 32 + 8 * g), ld8(vr + 32 + 8 * g), acc);
-          acc = mfma_bf16(ld4z(gr + 64 + 4 * g), ld4z(vr + 64 + 4 * g), acc);
-        }
-        // acc[r] = X[i = ib*16 + 4g + r][j = jb*16 + l%16] -> [j][i], masked i >= j
-        const int j = jb * 16 + c16;
-        f32x4 m;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m[r] = (ib * 16 + 4 * g + r >= j) ? acc[r] : 0.f;
-        uint16_t* dst = it < K::NA ? s.A : s.D;
-        *reinterpret_cast<uint2*>(dst + j * K::LA + ib * 16 + 4 * g) = pk4(m);
-      } else {
-        const int k2 = it - 2 * K::NA;
-        const int eb = k2 / K::NI, jb = k2 - (k2 / K::NI) * K::NI;
-        f32x4 acc = kZero4;
-#pragma unroll
-        for (int kk = 0; kk < K::F; kk += 32)
-          acc = mfma_bf16(ld8(s.S + (eb * 16 + c16) * K::LS + kk + 8 * g), ld8(s.K + (jb * 16 + c16) * K::LQ + kk + 8 * g),
-                          acc);
-        *reinterpret_cast<f32x4*>(s.N + (jb * 16 + c16) * K::LN + eb * 16 + 4 * g) = acc;
-      }
-    }
-    // dphi(K)^T = U V'^T for own feature blocks
-    f32x4 DK[2][K::NI];
+    f32x4 qt[2], kt[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const bf16x8 a01 = pk_pair(UT[0][j], UT[1][j]);
-      const bf16x8 a23 = pk_pair(UT[2][j], UT[3][j]);
-      const bf16x8 a4 = pk_pair(UT[4][j], kZero4);
+      qt[j] = load_tok4(p.phiq, row0, n, 2 * w + j, g, c);
+      kt[j] = load_tok4(p.phik, row0, n, 2 * w + j, g, c);
+    }
+    __syncthreads();
+    stage_v(p.v, row0, n, VR, VT, tid);
+    stage_g(p.g, row0, n, GRh, GRl, GTh, GTl, (tid + 256) & (kNT - 1));
+    __syncthreads();
+    // D^T[j][i] = v'_j . g'_i (split g'), masked j <= i < n; every wave forms it (lane: j = 4g + r, i = c)
+    f32x4 dt = kZero4;
 #pragma unroll
-      for (int jb = 0; jb < K::NI; ++jb) {
-        const uint16_t* vr = s.V + (jb * 16 + c16) * K::LV + 4 * g;
-        f32x4 acc = mfma_bf16(a01, ld4x2(vr, vr + 16), kZero4);
-        acc = mfma_bf16(a23, ld4x2(vr + 32, vr + 48), acc);
-        DK[j][jb] = mfma_bf16(a4, ld4z(vr + 64), acc);
+    for (int kk = 0; kk < 64; kk += 32) {
+      const bf16x8 vr = ld8(VR + c * kLR + kk + 8 * g);
+      dt = mfma_bf16(vr, ld8(GRh + c * kLR + kk + 8 * g), dt);
+      dt = mfma_bf16(vr, ld8(GRl + c * kLR + kk + 8 * g), dt);
+    }
+    {
+      const bf16x8 vr = row4x2(VR, c, 4, -1, g);
+      dt = mfma_bf16(vr, row4x2(GRh, c, 4, -1, g), dt);
+      dt = mfma_bf16(vr, row4x2(GRl, c, 4, -1, g), dt);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dt[r] = (4 * g + r <= c && c < n) ? dt[r] : 0.f;
+    uint2 d4, d4l;
+    split4(dt, d4, d4l);
+    // dphi(Q)^T[f][i] for this wave's features
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int fb = 2 * w + j;
+      f32x4 acc = mfma_bf16(hilo(kt[j]), cat(d4, d4), kZero4);
+      acc = mfma_bf16(cat(pk4(kt[j]), kZero2), cat(d4l, kZero2), acc);
+#pragma unroll
+      for (int e0 = 0; e0 < kNE; e0 += 2) {
+        const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
+        uint2 a0h, a0l, a1h = kZero2, a1l = kZero2;
+        split4(S[e0][j], a0h, a0l);
+        if (e1 >= 0) split4(S[e1][j], a1h, a1l);
+        const bf16x8 sh = cat(a0h, a1h), sl = cat(a0l, a1l);
+        const bf16x8 gh = row4x2(GRh, c, e0, e1, g), gl = row4x2(GRl, c, e0, e1, g);
+        acc = mfma_bf16(sh, gh, acc);
+        acc = mfma_bf16(sl, gh, acc);
+        acc = mfma_bf16(sh, gl, acc);
+      }
+      if (c < n) *reinterpret_cast<uint2*>(p.dphiq + (row0 + c) * kF + 16 * fb + 4 * g) = pk4(acc);
+    }
+    // U += phi(Q)^T G' and S' += V'^T phi(K) for this wave's features
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x8 aq = hilo(qt[j]);
+      const bf16x8 aqh = cat(pk4(qt[j]), kZero2);
+      const bf16x8 bk = hilo(kt[j]);
+#pragma unroll
+      for (int eb = 0; eb < kNE; ++eb) {
+        const uint2 gh = col4(GTh, 16 * eb + c, g), gl = col4(GTl, 16 * eb + c, g);
+        U[j][eb] = mfma_bf16(aq, cat(gh, gh), U[j][eb]);
+        U[j][eb] = mfma_bf16(aqh, cat(gl, kZero2), U[j][eb]);
+        const uint2 v4 = col4(VT, 16 * eb + c, g);
+        S[eb][j] = mfma_bf16(cat(v4, v4), bk, S[eb][j]);
+      }
+    }
+  }
+  __syncthreads();  // every wave has read its part of the item (loaded at the start) long before; keep order simple
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int eb = 0; eb < kNE; ++eb) store_fe(item, 2 * w + j, eb, lane, U[j][eb]);
+}
+
+// (6) dphi(K) = D^T phi(Q) + V' U^T for this wave's features, dV = A^T G + phi(K) U[:, :dv] (per-wave partials
+// summed through LDS), walking the segment backward with U (the item: U after the segment) in accumulators
+__global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
+  __shared__ __align__(16) uint16_t VR[kT * kLR];
+  __shared__ __align__(16) uint16_t VT[kE * kLT];
+  __shared__ __align__(16) uint16_t GRh[kT * kLR];
+  __shared__ __align__(16) uint16_t GRl[kT * kLR];
+  __shared__ __align__(16) uint16_t GTh[kE * kLT];
+  __shared__ __align__(16) uint16_t GTl[kE * kLT];
+  __shared__ __align__(16) float P[kW * kT * kLPV];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t h = blockIdx.x / p.n_seg;
+  const int seg = (int)(blockIdx.x - h * p.n_seg);
+  const int64_t t_begin = seg * p.seg_len;
+  const int64_t t_end = min<int64_t>(p.L, t_begin + p.seg_len);
+  const float* item = item_ptr(p, h, seg);
+  f32x4 UA[2][kNE], UB[kNE][2];  // U as C[f][e] (contraction over f: dV) and as C[e][f] (over e: dphi(K))
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int eb = 0; eb < kNE; ++eb) {
+      UA[j][eb] = load_fe(item, 2 * w + j, eb, lane);
+      UB[eb][j] = load_ef(item, 2 * w + j, eb, g, c);
+    }
+  const int n_steps = (int)((t_end - t_begin + kT - 1) / kT);
+  for (int st = n_steps - 1; st >= 0; --st) {
+    const int64_t t0 = t_begin + (int64_t)st * kT;
+    const int n = (int)min<int64_t>(kT, t_end - t0);
+    const int64_t row0 = h * p.L + t0;
+    f32x4 qa, qb, ka, kb, qt[2];
+    load_feat8(p.phiq, row0, n, w, g, c, qa, qb);
+    load_feat8(p.phik, row0, n, w, g, c, ka, kb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) qt[j] = load_tok4(p.phiq, row0, n, 2 * w + j, g, c);
+    __syncthreads();
+    stage_v(p.v, row0, n, VR, VT, tid);
+    stage_g(p.g, row0, n, GRh, GRl, GTh, GTl, (tid + 256) & (kNT - 1));
+    __syncthreads();
+    // this wave's part of A[i][j] over its features, masked i >= j (lane: i = 4g + r, j = c)
+    f32x4 aw = mfma_bf16(pk_pair(qa, qb), pk_pair(ka, kb), kZero4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) aw[r] = (4 * g + r >= c && 4 * g + r < n) ? aw[r] : 0.f;
+    const bf16x8 awb = cat(pk4(aw), kZero2);
+    // D[i][j] = g'_i . v'_j (split g'), masked i >= j (lane: i = 4g + r, j = c)
+    f32x4 dm = kZero4;
+#pragma unroll
+    for (int kk = 0; kk < 64; kk += 32) {
+      const bf16x8 vr = ld8(VR + c * kLR + kk + 8 * g);
+      dm = mfma_bf16(ld8(GRh + c * kLR + kk + 8 * g), vr, dm);
+      dm = mfma_bf16(ld8(GRl + c * kLR + kk + 8 * g), vr, dm);
+    }
+    {
+      const bf16x8 vr = row4x2(VR, c, 4, -1, g);
+      dm = mfma_bf16(row4x2(GRh, c, 4, -1, g), vr, dm);
+      dm = mfma_bf16(row4x2(GRl, c, 4, -1, g), vr, dm);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dm[r] = (4 * g + r >= c && 4 * g + r < n) ? dm[r] : 0.f;
+    uint2 d4, d4l;
+    split4(dm, d4, d4l);
+    // dphi(K)^T[f][j] for this wave's features
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int fb = 2 * w + j;
+      f32x4 acc = mfma_bf16(hilo(qt[j]), cat(d4, d4), kZero4);
+      acc = mfma_bf16(cat(pk4(qt[j]), kZero2), cat(d4l, kZero2), acc);
+#pragma unroll
+      for (int e0 = 0; e0 < kNE; e0 += 2) {
+        const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
+        uint2 a0h, a0l, a1h = kZero2, a1l = kZero2;
+        split4(UB[e0][j], a0h, a0l);
+        if (e1 >= 0) split4(UB[e1][j], a1h, a1l);
+        const bf16x8 vr = row4x2(VR, c, e0, e1, g);
+        acc = mfma_bf16(cat(a0h, a1h), vr, acc);
+        acc = mfma_bf16(cat(a0l, a1l), vr, acc);
+      }
+      if (c < n) *reinterpret_cast<uint2*>(p.dphik + (row0 + c) * kF + 16 * fb + 4 * g) = pk4(acc);
+    }
+    // dV^T[e][j] partial (e < dv): G^T A over this wave's A part, and U^T phi(K)^T over its features
+#pragma unroll
+    for (int eb = 0; eb < kDV / 16; ++eb) {
+      f32x4 acc = mfma_bf16(cat(col4(GTh, 16 * eb + c, g), kZero2), awb, kZero4);
+      acc = mfma_bf16(pk_pair(UA[0][eb], UA[1][eb]), pk_pair(ka, kb), acc);
+      *reinterpret_cast<f32x4*>(P + (w * kT + c) * kLPV + 16 * eb + 4 * g) = acc;  // lane: e = 16 eb + 4g + r, j = c
+    }
+    // U += phi(Q)^T G' (both orders) for the earlier chunks
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x8 aq = hilo(qt[j]);
+      const bf16x8 aqh = cat(pk4(qt[j]), kZero2);
+#pragma unroll
+      for (int eb = 0; eb < kNE; ++eb) {
+        const uint2 gh = col4(GTh, 16 * eb + c, g), gl = col4(GTl, 16 * eb + c, g);
+        UA[j][eb] = mfma_bf16(aq, cat(gh, gh), UA[j][eb]);
+        UA[j][eb] = mfma_bf16(aqh, cat(gl, kZero2), UA[j][eb]);
+        UB[eb][j] = mfma_bf16(cat(gh, gh), aq, UB[eb][j]);
+        UB[eb][j] = mfma_bf16(cat(gl, kZero2), aqh, UB[eb][j]);
       }
     }
     __syncthreads();
-    wait_vmem();  // the next chunk's prefetch, before this step's stores
-    // [2] dphi(K)^T += phi(Q)^T D; dV^T += G^T A; U^T += G'^T phi(Q)
+    if (tid < kT * 8) {  // dV rows: sum of the waves' partials, eight columns per thread
+      const int jj = tid >> 3, e0 = 8 * (tid & 7);
+      f32x4 a0 = kZero4, a1 = kZero4;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int fb = 2 * wave + j;
-      const bf16x8 qt = ld8(s.QT + (fb * 16 + c16) * K::LT + 8 * g);
-#pragma unroll
-      for (int jb = 0; jb < K::NI; ++jb) {
-        const f32x4 acc = mfma_bf16(qt, ld8(s.D + (jb * 16 + c16) * K::LA + 8 * g), DK[j][jb]);
-        const int jj = jb * 16 + c16;
-        if (jj < n) *reinterpret_cast<uint2*>(p.dphik + (row0 + jj) * K::F + fb * 16 + 4 * g) = pk4(acc);
+      for (int ww = 0; ww < kW; ++ww) {
+        const float* pr = P + (ww * kT + jj) * kLPV + e0;
+        a0 += *reinterpret_cast<const f32x4*>(pr);
+        a1 += *reinterpret_cast<const f32x4*>(pr + 4);
       }
-    }
-    for (int it = wave; it < (K::DV / 16) * K::NI; it += K::NW) {
-      const int eb = it / K::NI, jb = it - (it / K::NI) * K::NI;
-      const f32x4 part = *reinterpret_cast<const f32x4*>(s.N + (jb * 16 + c16) * K::LN + eb * 16 + 4 * g);
-      const f32x4 acc = mfma_bf16(ld8(s.GT + (eb * 16 + c16) * K::LT + 8 * g), ld8(s.A + (jb * 16 + c16) * K::LA + 8 * g),
-                                  part);
-      const int jj = jb * 16 + c16;
-      if (jj < n) *reinterpret_cast<uint2*>(p.dv + (row0 + jj) * K::DV + eb * 16 + 4 * g) = pk4(acc);
-    }
-#pragma unroll
-    for (int eb = 0; eb < K::NE; ++eb) {
-      const bf16x8 gt = ld8(s.GT + (eb * 16 + c16) * K::LT + 8 * g);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        UT[eb][j] = mfma_bf16(gt, ld8(s.QT + ((2 * wave + j) * 16 + c16) * K::LT + 8 * g), UT[eb][j]);
+      if (jj < n) {
+        const uint2 lo = pk4(a0), hi = pk4(a1);
+        *reinterpret_cast<uint4*>(p.dv + (row0 + jj) * kDV + e0) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
     }
   }
 }
@@ -828,19 +796,24 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
 }
 
 // ---------------------------------------------------------------------------
-using K256 = BwdK<16>;
 using V256 = VjpK<16>;
 
-struct FusedWs {
-  uint16_t *phiq, *phik, *dphiq, *dphik, *g;
-  float* states;
+// Segments of the precise kernels: about 1024 workgroups over all heads (four
+// per compute unit), whole 16-token steps, at least 64 tokens each.
+int64_t pb_seg_len(int64_t n_heads, int64_t L) {
+  const int64_t want = (L * n_heads + 1023) / 1024;
+  return std::max<int64_t>(64, (want + kT - 1) / kT * kT);
+}
+
+struct PbWs {
+  float *states, *phiq, *phik, *g;
+  uint16_t *dphiq, *dphik;
   size_t bytes;
 };
 
-FusedWs fused_ws(const BackwardArgs& a, int n_seg, void* base) {
+PbWs pb_ws(const BackwardArgs& a, int n_seg, void* base) {
   const int64_t rows = a.n_heads * a.L;
-  const size_t nphi = (size_t)rows * a.F * 2;
-  FusedWs w{};
+  PbWs w{};
   char* p = static_cast<char*>(base);
   size_t off = 0;
   auto take = [&](size_t b) {
@@ -848,40 +821,14 @@ FusedWs fused_ws(const BackwardArgs& a, int n_seg, void* base) {
     off += (b + 255) & ~(size_t)255;
     return q;
   };
-  w.states = reinterpret_cast<float*>(take(sizeof(float) * (size_t)a.n_heads * n_seg * K256::F * K256::E));
-  w.phiq = reinterpret_cast<uint16_t*>(take(nphi));
-  w.phik = reinterpret_cast<uint16_t*>(take(nphi));
-  w.dphiq = reinterpret_cast<uint16_t*>(take(nphi));
-  w.dphik = reinterpret_cast<uint16_t*>(take(nphi));
-  w.g = reinterpret_cast<uint16_t*>(take((size_t)rows * K256::E * 2));
+  w.states = reinterpret_cast<float*>(take(sizeof(float) * (size_t)a.n_heads * n_seg * kF * kE));
+  w.phiq = reinterpret_cast<float*>(take(sizeof(float) * (size_t)rows * kF));
+  w.phik = reinterpret_cast<float*>(take(sizeof(float) * (size_t)rows * kF));
+  w.g = reinterpret_cast<float*>(take(sizeof(float) * (size_t)rows * kE));
+  w.dphiq = reinterpret_cast<uint16_t*>(take(2 * (size_t)rows * kF));
+  w.dphik = reinterpret_cast<uint16_t*>(take(2 * (size_t)rows * kF));
   w.bytes = off;
   return w;
-}
-
-ChunkedArgs forward_args(const BackwardArgs& a) {
-  ChunkedArgs c{};
-  c.q = a.q;
-  c.k = a.k;
-  c.v = a.v;
-  c.io_bf16 = a.io_bf16;
-  c.causal = true;
-  c.n_heads = a.n_heads;
-  c.L = a.L;
-  c.Lq = a.L;
-  c.d = a.d;
-  c.dv = a.dv;
-  c.F = a.F;
-  c.m = a.m;
-  c.R = a.R;
-  c.chunk = a.chunk;
-  c.anchors = a.anchors;
-  c.prf = a.prf;
-  c.draw_set_stride = a.draw_set_stride;
-  c.n_draw_sets = a.n_draw_sets;
-  c.nc = a.nc;
-  c.S0 = a.S0;
-  c.z0 = a.z0;
-  return c;
 }
 
 // Feature counts below 256 run the F = 256 kernels on zero-padded features:
@@ -903,8 +850,8 @@ PadWs pad_ws(const BackwardArgs& a, char* base) {
     off += (b + 255) & ~(size_t)255;
     return q;
   };
-  const size_t nd = (size_t)a.n_draw_sets * K256::F * a.d * 2;
-  const size_t ns = (size_t)a.n_heads * K256::F * a.dv * 4, nz = (size_t)a.n_heads * K256::F * 4;
+  const size_t nd = (size_t)a.n_draw_sets * kF * a.d * 2;
+  const size_t ns = (size_t)a.n_heads * kF * a.dv * 4, nz = (size_t)a.n_heads * kF * 4;
   w.anchors = reinterpret_cast<uint16_t*>(take(nd));
   w.prf = reinterpret_cast<uint16_t*>(take(nd));
   w.S0 = reinterpret_cast<float*>(take(ns));
@@ -919,7 +866,7 @@ PadWs pad_ws(const BackwardArgs& a, char* base) {
 
 BackwardArgs padded_args(const BackwardArgs& a) {
   BackwardArgs p = a;
-  p.F = K256::F;
+  p.F = kF;
   return p;
 }
 
@@ -928,29 +875,27 @@ BackwardArgs padded_args(const BackwardArgs& a) {
 bool backward_fused_supported(const BackwardArgs& a) {
   if (a.n_heads == 0 || a.L == 0) return false;  // nothing for the MFMA kernels: the general launcher handles it
   // F < 256 runs on zero-padded features (a multiple of 32, as the m % 32 rule gives)
-  if (!a.io_bf16 || a.d != 64 || a.dv != 64 || a.F > K256::F || a.F % 32 != 0 || a.chunk != 64 || a.m % 32 != 0)
+  if (!a.io_bf16 || a.d != 64 || a.dv != 64 || a.F > kF || a.F % 32 != 0 || a.chunk != 64 || a.m % 32 != 0)
     return false;
   if (a.n_draw_sets > 1 && a.L % V256::RT != 0) return false;  // a VJP tile must not span two draw sets
-  int64_t seg_len = 0;
-  return fused_segment_count(forward_args(padded_args(a)), &seg_len) > 0 && seg_len % K256::C == 0;
+  return true;
 }
 
 size_t backward_fused_workspace_bytes(const BackwardArgs& a) {
   if (a.n_heads == 0 || a.L == 0) return 0;
   const BackwardArgs ap = padded_args(a);
-  int64_t seg_len = 0;
-  const int n_seg = fused_segment_count(forward_args(ap), &seg_len);
-  const size_t base = fused_ws(ap, n_seg, nullptr).bytes;
-  return a.F == K256::F ? base : base + pad_ws(a, nullptr).bytes;
+  const int64_t seg_len = pb_seg_len(a.n_heads, a.L);
+  const int n_seg = (int)((a.L + seg_len - 1) / seg_len);
+  const size_t base = pb_ws(ap, n_seg, nullptr).bytes;
+  return a.F == kF ? base : base + pad_ws(a, nullptr).bytes;
 }
 
 namespace {
 
 hipError_t launch_backward_fused_256(const BackwardArgs& a, hipStream_t s) {
-  const ChunkedArgs fa = forward_args(a);
-  int64_t seg_len = 0;
-  const int n_seg = fused_segment_count(fa, &seg_len);
-  const FusedWs w = fused_ws(a, n_seg, a.ws);
+  const int64_t seg_len = pb_seg_len(a.n_heads, a.L);
+  const int n_seg = (int)((a.L + seg_len - 1) / seg_len);
+  const PbWs w = pb_ws(a, n_seg, a.ws);
 
   FeatmapArgs fm{};
   fm.x = a.q;
@@ -968,13 +913,11 @@ hipError_t launch_backward_fused_256(const BackwardArgs& a, hipStream_t s) {
   fm.nc = a.nc;
   fm.phi = w.phiq;
   fm.phi2 = w.phik;
-  fm.phi_bf16 = true;
+  fm.phi_bf16 = false;
   hipError_t e = launch_featmap(fm, s);
   if (e != hipSuccess) return e;
-  e = launch_segment_prefix(fa, w.states, s);
-  if (e != hipSuccess) return e;
 
-  BwdParams p{};
+  PbParams p{};
   p.phiq = w.phiq;
   p.phik = w.phik;
   p.v = static_cast<const uint16_t*>(a.v);
@@ -987,19 +930,32 @@ hipError_t launch_backward_fused_256(const BackwardArgs& a, hipStream_t s) {
   p.dphiq = w.dphiq;
   p.dphik = w.dphik;
   p.dv = static_cast<uint16_t*>(a.dv_out);
+  if (n_seg > 1) {
+    hipLaunchKernelGGL(pb_state_kernel, dim3((unsigned)(a.n_heads * (n_seg - 1))), dim3(kNT), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  ScanArgs fa{};  // S' before every segment: S0 + the earlier segments' sums
+  fa.states = w.states;
+  fa.n_heads = a.n_heads;
+  fa.n_items = n_seg;
+  fa.n_terms = n_seg - 1;
+  fa.F = kF;
+  fa.dv = a.dv;
+  fa.layout = 1;
+  fa.S0 = a.S0;
+  fa.z0 = a.z0;
+  if ((e = launch_scan(fa, s)) != hipSuccess) return e;
   const dim3 grid((unsigned)(a.n_heads * n_seg));
-  e = set_max_lds(reinterpret_cast<const void*>(&bwd_q_kernel<K256>), K256::kLds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_q_kernel<K256>, grid, dim3(K256::NT), K256::kLds, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  ScanArgs ra{};
+  hipLaunchKernelGGL(pb_g_kernel, grid, dim3(kNT), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(pb_dq_kernel, grid, dim3(kNT), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  ScanArgs ra{};  // U after every segment: [dS_T | dz_T] + the later segments' sums; the total is [dS0 | dz0]
   ra.states = w.states;
   ra.n_heads = a.n_heads;
   ra.n_items = n_seg;
   ra.n_terms = n_seg;
-  ra.F = a.F;
+  ra.F = kF;
   ra.dv = a.dv;
   ra.layout = 1;
   ra.S0 = a.dS_T;
@@ -1007,14 +963,9 @@ hipError_t launch_backward_fused_256(const BackwardArgs& a, hipStream_t s) {
   ra.S_out = a.dS0;
   ra.z_out = a.dz0;
   ra.reverse = true;
-  e = launch_scan(ra, s);
-  if (e != hipSuccess) return e;
-
-  e = set_max_lds(reinterpret_cast<const void*>(&bwd_kv_kernel<K256>), K256::kLds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_kv_kernel<K256>, grid, dim3(K256::NT), K256::kLds, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = launch_scan(ra, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(pb_dk_kernel, grid, dim3(kNT), 0, s, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
 
   VjpParams vp{};
   vp.x[0] = static_cast<const uint16_t*>(a.q);
@@ -1043,12 +994,12 @@ hipError_t launch_backward_fused_256(const BackwardArgs& a, hipStream_t s) {
 
 hipError_t launch_backward_fused(const BackwardArgs& a, hipStream_t s) {
   if (a.n_heads == 0 || a.L == 0) return launch_backward(a, s);  // only the state gradient passes through
-  if (a.F == K256::F) return launch_backward_fused_256(a, s);
+  if (a.F == kF) return launch_backward_fused_256(a, s);
   BackwardArgs ap = padded_args(a);
-  int64_t seg_len = 0;
-  const int n_seg = fused_segment_count(forward_args(ap), &seg_len);
-  const PadWs w = pad_ws(a, static_cast<char*>(a.ws) + fused_ws(ap, n_seg, nullptr).bytes);
-  const int64_t nh = a.n_heads, F = a.F, P = K256::F, d = a.d, dv = a.dv;
+  const int64_t seg_len = pb_seg_len(a.n_heads, a.L);
+  const int n_seg = (int)((a.L + seg_len - 1) / seg_len);
+  const PadWs w = pad_ws(a, static_cast<char*>(a.ws) + pb_ws(ap, n_seg, nullptr).bytes);
+  const int64_t nh = a.n_heads, F = a.F, P = kF, d = a.d, dv = a.dv;
   hipError_t e = pad_rows(w.anchors, static_cast<const uint16_t*>(a.anchors), a.n_draw_sets, F, P, d,
                                     a.draw_set_stride, P * d, s);
   if (e == hipSuccess)

@@ -4,10 +4,12 @@ The backward is the causal forward (review of "SLAY: Geometry-Aware
 Spherical Linearized Attention with Yat-Kernel", "Proposed method" bullets
 1-6) differentiated; the oracle's backward is pinned to finite differences of
 its forward.  Bar as for the forward: 1e-4 for fp32 inputs, 2e-2 for bf16.
-dv is compared row by row; dq and dk per head (normwise), because a row of
-dq is the projection (I - qh qh^T) of the feature-space gradient, which
-cancels where that gradient is nearly parallel to qh; the state gradients
-per head as well.
+Every gradient is gated row by row (helpers.rowfloor_rel): a row's error
+relative to its own norm, floored at a tenth of the head's rms row norm.  The
+floor is for rows of dq and dk that are legitimately small -- a row of dq is
+the projection (I - qh qh^T) of the feature-space gradient, which cancels
+where that gradient is nearly parallel to qh -- and for state-gradient rows
+of features that carry little weight; a wholly wrong row still fails.
 """
 import sys
 
@@ -15,7 +17,7 @@ import numpy as np
 import pytest
 
 import slay_synth as ss
-from helpers import TOL, headnorm_rel, rownorm_rel, to_dev, to_np
+from helpers import TOL, headnorm_rel, rowfloor_rel, rownorm_rel, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -63,14 +65,15 @@ def _compare(got, ref, dtype, tag):
     rq, rk, rv, rS0, rz0 = ref
     nh = dq.shape[0] * dq.shape[1]
     errs = {
-        "dq": headnorm_rel(dq.reshape(nh, -1), rq.reshape(nh, -1)),
-        "dk": headnorm_rel(dk.reshape(nh, -1), rk.reshape(nh, -1)),
-        "dv": rownorm_rel(dv, rv),
-        "dS0": headnorm_rel(dS0, rS0),
-        "dz0": headnorm_rel(dz0, rz0),
+        "dq": rowfloor_rel(dq, rq, heads=nh),
+        "dk": rowfloor_rel(dk, rk, heads=nh),
+        "dv": rowfloor_rel(dv, rv, heads=nh),
+        "dS0": rowfloor_rel(dS0, rS0, heads=nh),
+        "dz0": rowfloor_rel(dz0[..., None], rz0[..., None], heads=nh),
     }
     _say(f"  {tag}: " + " ".join(f"{k} {e:.3e}" for k, e in errs.items())
-         + f" (rownorm dq {rownorm_rel(dq, rq):.3e} dk {rownorm_rel(dk, rk):.3e})")
+         + f" (unfloored rownorm dq {rownorm_rel(dq, rq):.3e} dk {rownorm_rel(dk, rk):.3e};"
+         + f" headnorm dq {headnorm_rel(dq.reshape(nh, -1), rq.reshape(nh, -1)):.3e})")
     for name, e in errs.items():
         assert e < TOL[dtype], (name, e)
 
@@ -153,7 +156,10 @@ def test_backward_chunk_invariance(lib):
     outs = [_run_bwd(lib, w, q, k, v, dout, A, G, c, S0, z0, dST, dzT) for c in (1, 7, 64, 128)]
     for other in outs[1:]:
         for x, y in zip(outs[0], other):
-            assert headnorm_rel(y.reshape(y.shape[0], -1), x.reshape(x.shape[0], -1)) < 1e-5
+            nh = x.shape[0] * (x.shape[1] if x.ndim == 4 else 1)
+            xr = x[..., None] if x.ndim == 2 else x
+            yr = y[..., None] if y.ndim == 2 else y
+            assert rowfloor_rel(yr, xr, heads=nh) < 1e-5
 
 
 def test_backward_per_head_draws(lib, orc):

@@ -297,3 +297,55 @@ def test_decode_stress_inputs(lib, orc):
     z_err = rowfloor_rel(to_np(z)[..., None], rz[..., None], heads=n_heads)
     _say(f"decode off-sphere: o rownorm {err:.3e}; S per-row {s_err:.3e}; z per-row {z_err:.3e}")
     assert err < TOL["f32"] and s_err < TOL["f32"] and z_err < TOL["f32"]
+# ----------------------------------------------------------------------------
+# backward: the sphere projection's Jacobian (I - xh xh^T)/|x| and the clamp
+
+BWD_CASES = [
+    ("h16_l16k_bf16", dict(H=2, L=1500), 64, "MFMA F=256"),
+    ("b4h8_l2k_bf16", dict(B=1, H=2, L=700), 64, "MFMA F=96 padded"),
+    ("h8_l128k_d128_bf16", dict(H=1, L=300), 128, "general bf16 d=128"),
+    ("tiny_f32", dict(H=2, L=200), 32, "general fp32"),
+]
+
+
+@pytest.mark.parametrize("name,over,chunk,label", BWD_CASES)
+@pytest.mark.parametrize("stress", ["scaled", "near_scaled"])
+def test_backward_stress_inputs(lib, orc, name, over, chunk, label, stress):
+    import torch
+
+    w = ss.WORKLOADS[name].with_(**over)
+    _say(f"backward {stress} {label}: H={w.H} L={w.L} F={w.F}")
+    kw = dict(qk_scale=SCALE, zero_k=_zero_keys(w.L))
+    if stress == "near_scaled":
+        kw.update(near_pairs=NEAR)
+    q, k, v = ss.make_qkv(w, **kw)
+    A, G = ss.make_draws(w)
+    dout, dST, dzT = ss.make_grads(w)
+    rng = np.random.default_rng(17)
+    S0 = np.abs(rng.standard_normal((w.n_heads, w.F, w.dv))).astype(np.float32)
+    z0 = (rng.random((w.n_heads, w.F)) + 0.5).astype(np.float32)
+    fm = _fm(lib, w, A, G)
+    res = lib.chunked_bwd(fm, to_dev(q, w.dtype), to_dev(k, w.dtype), to_dev(v, w.dtype), to_dev(dout, w.dtype),
+                          chunk, S0=_f32(S0), z0=_f32(z0), dS_T=_f32(dST), dz_T=_f32(dzT), state_grad=True)
+    torch.cuda.synchronize()
+    dq, dk, dv, dS0, dz0 = (to_np(t) for t in res)
+    rq, rk, rv, rS0, rz0 = orc.slay_causal_bwd(q, k, v, dout, A, G, w.eps, w.R, w.m, S0=S0, z0=z0, dS_T=dST,
+                                                dz_T=dzT)
+    nh = w.n_heads
+    nq = np.linalg.norm(q.astype(np.float64), axis=-1, keepdims=True)
+    nk = np.linalg.norm(k.astype(np.float64), axis=-1, keepdims=True)
+    zero = nk[..., 0] == 0
+    errs = {
+        "dq": rowfloor_rel(nq * dq, nq * rq, heads=nh),
+        "dk": rowfloor_rel(nk * dk, nk * rk, heads=nh),
+        "dv": rowfloor_rel(dv, rv, heads=nh),
+        "dS0": rowfloor_rel(dS0, rS0, heads=nh),
+        "dz0": rowfloor_rel(dz0[..., None], rz0[..., None], heads=nh),
+    }
+    _say("  " + " ".join(f"{n} {e:.3e}" for n, e in errs.items())
+         + f"; dk on zero keys max {np.abs(dk[zero]).max() if zero.any() else 0:.1e}")
+    for t in (dq, dk, dv, dS0, dz0):
+        assert np.all(np.isfinite(t))
+    assert np.all(rk[zero] == 0) and np.all(dk[zero] == 0)
+    for n, e in errs.items():
+        assert e < TOL[w.dtype], (n, e)
