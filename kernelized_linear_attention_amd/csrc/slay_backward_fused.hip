@@ -19,8 +19,9 @@
 // runs on split operands: x = x_hi + x_lo, both bf16, so the pair carries 16
 // mantissa bits, and a product of two split values is taken as
 // x_hi y_hi + x_lo y_hi + x_hi y_lo (fp32 accumulation).  phi(q), phi(k) are
-// written once in fp32 by the feature map, the states and U live in fp32
-// MFMA accumulators, g' is formed and stored in fp32, and the masked
+// recomputed on chip in fp32 wherever a kernel needs them (the projection
+// P x on MFMA, exact bf16 products), the states and U live in fp32 MFMA
+// accumulators, g' is formed and stored in fp32, and the masked
 // intra-chunk blocks A = tril(phi(Q) phi(K)^T) and D = tril(G' V'^T) are split
 // too where they feed the numerators and dphi (A only in bf16 for dV, whose
 // terms are all positive-weighted).  dphi leaves in bf16: its rounding does
@@ -33,21 +34,22 @@
 // shape, checked on gfx950, are in slay_device.hpp.)
 //
 // Launches (one stream), one workgroup of 8 waves per (head, segment), wave
-// w owning features [32w, 32w + 32):
-//   1. the feature map writes phi(q), phi(k) in fp32;
-//   2. pb_state_kernel sums each segment's phi(K)^T V' (all but the last);
+// w owning features [32w, 32w + 32) and keeping their rows of the projection
+// P = [anchors; prf] in registers, from which it forms phi of its features for
+// each 16-token step:
+//   1. pb_state_kernel sums each segment's phi(K)^T V' (all but the last);
 //      the prefix scan turns them into S' before every segment (plus S0, z0);
-//   3. pb_g_kernel walks each segment with S' in accumulators, forms the
+//   2. pb_g_kernel walks each segment with S' in accumulators, forms the
 //      numerators and denominators (per-wave partials over the wave's
 //      features, summed through LDS) and writes g' in fp32;
-//   4. pb_dq_kernel walks each segment again: dphi(Q) = D phi(K) + G' S'^T,
+//   3. pb_dq_kernel walks each segment again: dphi(Q) = D phi(K) + G' S'^T,
 //      and the segment's sum phi(Q)^T G' (written over its prefix state);
-//   5. the reverse scan gives U after every segment (plus dS_T, dz_T) and
+//   4. the reverse scan gives U after every segment (plus dS_T, dz_T) and
 //      [dS0 | dz0];
-//   6. pb_dk_kernel walks each segment backward with U in accumulators:
+//   5. pb_dk_kernel walks each segment backward with U in accumulators:
 //      dphi(K) = D^T phi(Q) + V' U^T, dV = A^T G + phi(K) U (per-wave partials
 //      summed through LDS), then U += phi(Q)^T G';
-//   7. vjp_kernel maps dphi back to dq and dk.
+//   6. vjp_kernel maps dphi back to dq and dk.
 #include <algorithm>
 
 #include "slay_device.hpp"
@@ -94,6 +96,11 @@ __device__ __forceinline__ bf16x8 hilo(const f32x4& x) {
   split4(x, h, l);
   return cat(h, l);
 }
+// the hi parts of a split operand alone (k-slots 4-7 zero)
+__device__ __forceinline__ bf16x8 hi_only(const bf16x8& x) {
+  const uint4 u = __builtin_bit_cast(uint4, x);
+  return __builtin_bit_cast(bf16x8, make_uint4(u.x, u.y, 0u, 0u));
+}
 
 // ---------------------------------------------------------------------------
 // Precise segment kernels.
@@ -110,8 +117,13 @@ constexpr int kLP = kE + 4;        // fp32 partials [w][t][e]
 constexpr int kLPV = kDV + 4;
 
 struct PbParams {
-  const float* phiq;     // [n_heads * L][F] fp32
-  const float* phik;
+  const uint16_t* q;     // [n_heads * L][64]
+  const uint16_t* k;
+  const uint16_t* anchors;  // [n_draw_sets][F][64] (draw set of head h: h % n_draw_sets)
+  const uint16_t* prf;
+  int64_t draw_set_stride;
+  int n_draw_sets, m;
+  NodeConsts nc;
   const uint16_t* v;     // [n_heads * L][64]
   const uint16_t* dout;  // [n_heads * L][64]
   int64_t L, seg_len;
@@ -123,33 +135,137 @@ struct PbParams {
   uint16_t* dv;          // [n_heads * L][64]
 };
 
-// phi rows t0 + 4g + r (r < 4) of feature 16 fb + c: the "four tokens of a lane" layout of the token contractions
-__device__ __forceinline__ f32x4 load_tok4(const float* __restrict__ x, int64_t row0, int n, int fb, int g, int c) {
-  f32x4 r;
+// The feature map of the step's tokens for this wave's features, on chip:
+// y = P x (bf16 products, fp32 accumulation) for the anchor and PRF rows of
+// the wave's two feature blocks, then phi = (y_a / |x|)^2 exp2(y_g c1 / |x| + c0)
+// in fp32 (c1 = sqrt(beta_r) log2 e, c0 = -beta_r/2 log2 e + log2 sqrt(alpha_r/m)),
+// with |x| clamped at 1e-12.  The same registers serve both operand orders.
+struct Proj {
+  bf16x8 a[2][2], p[2][2];  // [feature block j][k-step]: rows 16 fb + c, columns 32 kk + 8g ..
+  float c1[2], c0[2];
+};
+
+__device__ __forceinline__ void load_proj(Proj& P, const PbParams& p, int64_t h, int w, int g, int c) {
+  const int64_t set = h % p.n_draw_sets;
+  const uint16_t* A = p.anchors + set * p.draw_set_stride;
+  const uint16_t* G = p.prf + set * p.draw_set_stride;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (4 * g + i < n) ? x[(row0 + 4 * g + i) * kF + 16 * fb + c] : 0.f;
-  return r;
-}
-// phi row t0 + c, features 32 w + 4g .. +3 and 32 w + 16 + 4g .. +3: a lane's k-slots of a contraction over the
-// wave's 32 features (the order of two accumulator tiles side by side)
-__device__ __forceinline__ void load_feat8(const float* __restrict__ x, int64_t row0, int n, int w, int g, int c,
-                                           f32x4& a, f32x4& b) {
-  if (c < n) {
-    const float* p = x + (row0 + c) * kF + 32 * w + 4 * g;
-    a = *reinterpret_cast<const f32x4*>(p);
-    b = *reinterpret_cast<const f32x4*>(p + 16);
-  } else {
-    a = kZero4;
-    b = kZero4;
+  for (int j = 0; j < 2; ++j) {
+    const int fb = 2 * w + j;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      P.a[j][kk] = ld8(A + (16 * fb + c) * kDV + 32 * kk + 8 * g);
+      P.p[j][kk] = ld8(G + (16 * fb + c) * kDV + 32 * kk + 8 * g);
+    }
+    const int node = (16 * fb) / p.m;
+    P.c1[j] = p.nc.c1[node];
+    P.c0[j] = p.nc.c0[node];
   }
 }
 
+// rows t0 + c of x (zero past n), with 1/|x| and log2(1/|x|^2) of that row
+struct XRows {
+  bf16x8 x0, x1;
+  float inv, lg;
+};
+
+// Global inputs of one 16-token step.  The q and k rows are issued one step
+// ahead of their use; the v, dout and g' pieces at the top of their own step,
+// ahead of the feature map that runs before they are staged.  Rows past the
+// step's n read its last row (an unconditional load: a select between
+// addresses would go through a private zero copy) and are zeroed where used.
+struct StepIn {
+  uint4 qa, qb, ka, kb;  // rows t0 + c of q and k: columns 8g .. and 32 + 8g ..
+};
+struct StepAux {
+  uint4 v;               // threads < 128: v row t0 + tid/8, columns 8 (tid % 8) ..
+  uint4 d;               // threads < 128: the same piece of dout
+  f32x4 gp;              // staging thread u = (tid + 256) % 512 < 320: g' row t0 + u/20, columns 4 (u % 20) ..
+};
+
+template <bool Q, bool K>
+__device__ __forceinline__ void load_step(StepIn& s, const PbParams& p, int64_t row0, int n, int g, int c) {
+  const int64_t rx = row0 + min(c, n - 1);
+  if (Q) {
+    s.qa = *reinterpret_cast<const uint4*>(p.q + rx * kDV + 8 * g);
+    s.qb = *reinterpret_cast<const uint4*>(p.q + rx * kDV + 32 + 8 * g);
+  }
+  if (K) {
+    s.ka = *reinterpret_cast<const uint4*>(p.k + rx * kDV + 8 * g);
+    s.kb = *reinterpret_cast<const uint4*>(p.k + rx * kDV + 32 + 8 * g);
+  }
+}
+
+template <bool D, bool G>
+__device__ __forceinline__ StepAux load_aux(const PbParams& p, int64_t row0, int n, int tid) {
+  StepAux s;
+  if (tid < kT * 8) {
+    const int64_t rv = row0 + min(tid >> 3, n - 1);
+    s.v = *reinterpret_cast<const uint4*>(p.v + rv * kDV + 8 * (tid & 7));
+    if (D) s.d = *reinterpret_cast<const uint4*>(p.dout + rv * kDV + 8 * (tid & 7));
+  }
+  if (G) {
+    const int u = (tid + 256) & (kNT - 1);
+    if (u < kT * (kE / 4)) {
+      const int64_t rg = row0 + min(u / (kE / 4), n - 1);
+      s.gp = *reinterpret_cast<const f32x4*>(p.g + rg * kE + 4 * (u % (kE / 4)));
+    }
+  }
+  return s;
+}
+
+__device__ __forceinline__ XRows finish_x(uint4 a, uint4 b, bool valid) {
+  if (!valid) a = b = make_uint4(0, 0, 0, 0);
+  XRows X;
+  X.x0 = __builtin_bit_cast(bf16x8, a);
+  X.x1 = __builtin_bit_cast(bf16x8, b);
+  const uint32_t wd[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float ss = 0.f;  // bf16 products are exact in fp32
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const bf16x2 h2 = __builtin_bit_cast(bf16x2, wd[t]);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, ss, false);
+  }
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  X.inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+  X.lg = 2.0f * __builtin_amdgcn_logf(X.inv);  // log2(inv^2)
+  return X;
+}
+
+// phi[t0 + c][16 fb + 4g + r] (r < 4): a lane's k-slots over the wave's features, tokens on lanes
+__device__ __forceinline__ f32x4 phi_feat(const Proj& P, const XRows& X, int j) {
+  f32x4 ya = mfma_bf16(P.a[j][0], X.x0, kZero4);
+  ya = mfma_bf16(P.a[j][1], X.x1, ya);
+  f32x4 yg = mfma_bf16(P.p[j][0], X.x0, kZero4);
+  yg = mfma_bf16(P.p[j][1], X.x1, yg);
+  const float s1 = X.inv * P.c1[j], c0 = P.c0[j] + X.lg;
+  f32x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = ya[r] * ya[r] * fast_exp2(fmaf(yg[r], s1, c0));
+  return o;
+}
+
+// phi[t0 + 4g + r][16 fb + c] (r < 4): four tokens per lane, features on lanes
+__device__ __forceinline__ f32x4 phi_tok(const Proj& P, const XRows& X, int j, int g) {
+  f32x4 ya = mfma_bf16(X.x0, P.a[j][0], kZero4);
+  ya = mfma_bf16(X.x1, P.a[j][1], ya);
+  f32x4 yg = mfma_bf16(X.x0, P.p[j][0], kZero4);
+  yg = mfma_bf16(X.x1, P.p[j][1], yg);
+  f32x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float inv = __shfl(X.inv, 4 * g + r, 64), lg = __shfl(X.lg, 4 * g + r, 64);
+    o[r] = ya[r] * ya[r] * fast_exp2(fmaf(yg[r], inv * P.c1[j], P.c0[j] + lg));
+  }
+  return o;
+}
+
 // V' = [v | 1 | 0] of the step's tokens (zero rows past n) as [t][e] rows and [e][t] columns
-__device__ __forceinline__ void stage_v(const uint16_t* __restrict__ v, int64_t row0, int n, uint16_t* VR,
-                                        uint16_t* VT, int tid) {
+__device__ __forceinline__ void stage_v(uint4 x, int n, uint16_t* VR, uint16_t* VT, int tid) {
   if (tid < kT * 8) {
     const int t = tid >> 3, e0 = 8 * (tid & 7);
-    const uint4 x = t < n ? *reinterpret_cast<const uint4*>(v + (row0 + t) * kDV + e0) : make_uint4(0, 0, 0, 0);
+    if (t >= n) x = make_uint4(0, 0, 0, 0);
     if (VR) *reinterpret_cast<uint4*>(VR + t * kLR + e0) = x;
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -170,12 +286,13 @@ __device__ __forceinline__ void stage_v(const uint16_t* __restrict__ v, int64_t 
   }
 }
 
-// g' of the step's tokens (fp32 in HBM) split into hi and lo bf16, as [t][e] rows and [e][t] columns
-__device__ __forceinline__ void stage_g(const float* __restrict__ gsrc, int64_t row0, int n, uint16_t* GRh,
-                                        uint16_t* GRl, uint16_t* GTh, uint16_t* GTl, int tid) {
-  if (tid < kT * (kE / 4)) {
-    const int t = tid / (kE / 4), e0 = 4 * (tid % (kE / 4));
-    const f32x4 x = t < n ? *reinterpret_cast<const f32x4*>(gsrc + (row0 + t) * kE + e0) : kZero4;
+// g' of the step's tokens split into hi and lo bf16, as [t][e] rows and [e][t] columns
+__device__ __forceinline__ void stage_g(f32x4 x, int n, uint16_t* GRh, uint16_t* GRl, uint16_t* GTh, uint16_t* GTl,
+                                        int tid) {
+  const int u = (tid + 256) & (kNT - 1);
+  if (u < kT * (kE / 4)) {
+    const int t = u / (kE / 4), e0 = 4 * (u % (kE / 4));
+    if (t >= n) x = kZero4;
     uint2 h, l;
     split4(x, h, l);
     *reinterpret_cast<uint2*>(GRh + t * kLR + e0) = h;
@@ -221,6 +338,38 @@ __device__ __forceinline__ f32x4 load_ef(const float* item, int fb, int eb, int 
   return x;
 }
 
+// A segment's steps.  The body takes the step's q, k rows (issued during the
+// previous step), its token range, and a callback that issues the next
+// step's rows into the same registers once the body has consumed them.
+template <bool REV, class LOAD, class BODY>
+__device__ __forceinline__ void walk_steps(int64_t t_begin, int64_t t_end, LOAD load, BODY body) {
+  const int n_steps = (int)((t_end - t_begin + kT - 1) / kT);
+  auto geom = [&](int i, int64_t& t0, int& n) {
+    const int st = REV ? n_steps - 1 - i : i;
+    t0 = t_begin + (int64_t)st * kT;
+    n = (int)min<int64_t>(kT, t_end - t0);
+  };
+  StepIn in;
+  int64_t t0;
+  int n;
+  geom(0, t0, n);
+  load(in, t0, n);
+  for (int i = 0; i < n_steps; ++i) {
+    int64_t tc;
+    int nc;
+    geom(i, tc, nc);
+    auto prefetch = [&]() {
+      if (i + 1 < n_steps) {
+        int64_t tn;
+        int nn;
+        geom(i + 1, tn, nn);
+        load(in, tn, nn);
+      }
+    };
+    body(in, tc, nc, prefetch);
+  }
+}
+
 // (1) sum over each segment's keys (all segments but the last) of phi(k) v'^T, in the item order
 __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
   __shared__ __align__(16) uint16_t VT[kE * kLT];
@@ -231,30 +380,36 @@ __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
   const int seg = (int)(blockIdx.x - h * n_items);
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = min<int64_t>(p.L, t_begin + p.seg_len);
+  Proj P;
+  load_proj(P, p, h, w, g, c);
   f32x4 S[2][kNE];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int eb = 0; eb < kNE; ++eb) S[j][eb] = kZero4;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kT) {
-    const int n = (int)min<int64_t>(kT, t_end - t0);
-    const int64_t row0 = h * p.L + t0;
-    f32x4 kt[2];
+  walk_steps<false>(
+      t_begin, t_end,
+      [&](StepIn& in, int64_t t0, int n) { load_step<false, true>(in, p, h * p.L + t0, n, g, c); },
+      [&](StepIn& in, int64_t t0, int n, auto prefetch) {
+        const StepAux ax = load_aux<false, false>(p, h * p.L + t0, n, tid);
+        const XRows xk = finish_x(in.ka, in.kb, c < n);
+        prefetch();
+        f32x4 kt[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) kt[j] = load_tok4(p.phik, row0, n, 2 * w + j, g, c);
-    __syncthreads();
-    stage_v(p.v, row0, n, nullptr, VT, tid);
-    __syncthreads();
+        for (int j = 0; j < 2; ++j) kt[j] = phi_tok(P, xk, j, g);
+        __syncthreads();
+        stage_v(ax.v, n, nullptr, VT, tid);
+        __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16x8 a = hilo(kt[j]);
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8 a = hilo(kt[j]);
 #pragma unroll
-      for (int eb = 0; eb < kNE; ++eb) {
-        const uint2 v4 = col4(VT, 16 * eb + c, g);
-        S[j][eb] = mfma_bf16(a, cat(v4, v4), S[j][eb]);
-      }
-    }
-  }
+          for (int eb = 0; eb < kNE; ++eb) {
+            const uint2 v4 = col4(VT, 16 * eb + c, g);
+            S[j][eb] = mfma_bf16(a, cat(v4, v4), S[j][eb]);
+          }
+        }
+      });
   float* item = item_ptr(p, h, seg);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -262,7 +417,7 @@ __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
     for (int eb = 0; eb < kNE; ++eb) store_fe(item, 2 * w + j, eb, lane, S[j][eb]);
 }
 
-// (3) numerators, denominators and g' of every token, with S' (the item: the state before the segment) in
+// (2) numerators, denominators and g' of every token, with S' (the item: the state before the segment) in
 // accumulators
 __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
   __shared__ __align__(16) uint16_t VT[kE * kLT];
@@ -274,110 +429,117 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = min<int64_t>(p.L, t_begin + p.seg_len);
   const float* item = item_ptr(p, h, seg);
+  Proj Pj;
+  load_proj(Pj, p, h, w, g, c);
   f32x4 S[2][kNE];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int eb = 0; eb < kNE; ++eb) S[j][eb] = load_fe(item, 2 * w + j, eb, lane);
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kT) {
-    const int n = (int)min<int64_t>(kT, t_end - t0);
-    const int64_t row0 = h * p.L + t0;
-    f32x4 qa, qb, ka, kb, kt[2];
-    load_feat8(p.phiq, row0, n, w, g, c, qa, qb);
-    load_feat8(p.phik, row0, n, w, g, c, ka, kb);
+  walk_steps<false>(
+      t_begin, t_end,
+      [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
+      [&](StepIn& in, int64_t t0, int n, auto prefetch) {
+        const int64_t row0 = h * p.L + t0;
+        const StepAux ax = load_aux<true, false>(p, row0, n, tid);
+        const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
+        prefetch();
+        const f32x4 qa = phi_feat(Pj, xq, 0), qb = phi_feat(Pj, xq, 1);
+        const f32x4 ka = phi_feat(Pj, xk, 0), kb = phi_feat(Pj, xk, 1);
+        f32x4 kt[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) kt[j] = load_tok4(p.phik, row0, n, 2 * w + j, g, c);
-    __syncthreads();  // the previous step's readers of VT and P are done
-    stage_v(p.v, row0, n, nullptr, VT, tid);
-    __syncthreads();
-    // this wave's part of A^T[j][i] = sum_f phi(K_j)_f phi(Q_i)_f over its features (split phi), masked j <= i
-    uint2 qh0, ql0, qh1, ql1, kh0, kl0, kh1, kl1;
-    split4(qa, qh0, ql0);
-    split4(qb, qh1, ql1);
-    split4(ka, kh0, kl0);
-    split4(kb, kh1, kl1);
-    const bf16x8 qh = cat(qh0, qh1), ql = cat(ql0, ql1), kh = cat(kh0, kh1);
-    f32x4 at = mfma_bf16(kh, qh, kZero4);  // lane: j = 4g + r, i = c
-    at = mfma_bf16(cat(kl0, kl1), qh, at);
-    at = mfma_bf16(kh, ql, at);
+        for (int j = 0; j < 2; ++j) kt[j] = phi_tok(Pj, xk, j, g);
+        __syncthreads();  // the previous step's readers of VT and P are done
+        stage_v(ax.v, n, nullptr, VT, tid);
+        __syncthreads();
+        // this wave's part of A^T[j][i] = sum_f phi(K_j)_f phi(Q_i)_f over its features (split phi), masked j <= i
+        uint2 qh0, ql0, qh1, ql1, kh0, kl0, kh1, kl1;
+        split4(qa, qh0, ql0);
+        split4(qb, qh1, ql1);
+        split4(ka, kh0, kl0);
+        split4(kb, kh1, kl1);
+        const bf16x8 qh = cat(qh0, qh1), ql = cat(ql0, ql1), kh = cat(kh0, kh1);
+        f32x4 at = mfma_bf16(kh, qh, kZero4);  // lane: j = 4g + r, i = c
+        at = mfma_bf16(cat(kl0, kl1), qh, at);
+        at = mfma_bf16(kh, ql, at);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) at[r] = (4 * g + r <= c && c < n) ? at[r] : 0.f;
-    const bf16x8 atb = hilo(at);  // A^T split: slots 0-3 hi, 4-7 lo of the same four keys
-    // num'^T[e][i] partial = V'^T A^T (this wave's A part) + S'^T phi(Q)^T over this wave's features
+        for (int r = 0; r < 4; ++r) at[r] = (4 * g + r <= c && c < n) ? at[r] : 0.f;
+        const bf16x8 atb = hilo(at);  // A^T split: slots 0-3 hi, 4-7 lo of the same four keys
+        // num'^T[e][i] partial = V'^T A^T (this wave's A part) + S'^T phi(Q)^T over this wave's features
 #pragma unroll
-    for (int eb = 0; eb < kNE; ++eb) {
-      const uint2 v4 = col4(VT, 16 * eb + c, g);
-      f32x4 acc = mfma_bf16(cat(v4, v4), atb, kZero4);
-      uint2 s0h, s0l, s1h, s1l;
-      split4(S[0][eb], s0h, s0l);
-      split4(S[1][eb], s1h, s1l);
-      const bf16x8 sh = cat(s0h, s1h), sl = cat(s0l, s1l);
-      acc = mfma_bf16(sh, qh, acc);
-      acc = mfma_bf16(sl, qh, acc);
-      acc = mfma_bf16(sh, ql, acc);
-      *reinterpret_cast<f32x4*>(P + (w * kT + c) * kLP + 16 * eb + 4 * g) = acc;  // lane: e = 16 eb + 4g + r, i = c
-    }
-    // S' += phi(K)^T V' for this wave's features (after its use: S' is the state before the chunk)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16x8 a = hilo(kt[j]);
-#pragma unroll
-      for (int eb = 0; eb < kNE; ++eb) {
-        const uint2 v4 = col4(VT, 16 * eb + c, g);
-        S[j][eb] = mfma_bf16(a, cat(v4, v4), S[j][eb]);
-      }
-    }
-    __syncthreads();
-    // g' = [dout / den | -(dout . num) / den^2 | 0]: eight threads per token, eight columns each
-    if (tid < kT * 8) {
-      const int i = tid >> 3, e0 = 8 * (tid & 7);
-      f32x4 n0 = kZero4, n1 = kZero4;
-      float den = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kW; ++ww) {
-        const float* pr = P + (ww * kT + i) * kLP;
-        n0 += *reinterpret_cast<const f32x4*>(pr + e0);
-        n1 += *reinterpret_cast<const f32x4*>(pr + e0 + 4);
-        den += pr[kDV];
-      }
-      const uint4 dr = i < n ? *reinterpret_cast<const uint4*>(p.dout + (row0 + i) * kDV + e0) : make_uint4(0, 0, 0, 0);
-      const uint32_t dw[4] = {dr.x, dr.y, dr.z, dr.w};
-      float dn[8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        dn[2 * t] = __uint_as_float(dw[t] << 16);
-        dn[2 * t + 1] = __uint_as_float(dw[t] & 0xFFFF0000u);
-      }
-      float dot = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) dot = fmaf(dn[t], n0[t], fmaf(dn[4 + t], n1[t], dot));
-      dot += __shfl_xor(dot, 1, 64);
-      dot += __shfl_xor(dot, 2, 64);
-      dot += __shfl_xor(dot, 4, 64);
-      if (i < n) {
-        const float inv = 1.f / den;
-        float* gr = p.g + (row0 + i) * kE;
-        f32x4 g0, g1;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          g0[t] = dn[t] * inv;
-          g1[t] = dn[4 + t] * inv;
+        for (int eb = 0; eb < kNE; ++eb) {
+          const uint2 v4 = col4(VT, 16 * eb + c, g);
+          f32x4 acc = mfma_bf16(cat(v4, v4), atb, kZero4);
+          uint2 s0h, s0l, s1h, s1l;
+          split4(S[0][eb], s0h, s0l);
+          split4(S[1][eb], s1h, s1l);
+          const bf16x8 sh = cat(s0h, s1h), sl = cat(s0l, s1l);
+          acc = mfma_bf16(sh, qh, acc);
+          acc = mfma_bf16(sl, qh, acc);
+          acc = mfma_bf16(sh, ql, acc);
+          *reinterpret_cast<f32x4*>(P + (w * kT + c) * kLP + 16 * eb + 4 * g) = acc;  // lane: e = 16 eb + 4g + r, i = c
         }
-        *reinterpret_cast<f32x4*>(gr + e0) = g0;
-        *reinterpret_cast<f32x4*>(gr + e0 + 4) = g1;
-        if ((tid & 7) == 0) {
-          const f32x4 hz = {-dot * inv * inv, 0.f, 0.f, 0.f};
-          *reinterpret_cast<f32x4*>(gr + kDV) = hz;
-          *reinterpret_cast<f32x4*>(gr + kDV + 4) = kZero4;
-          *reinterpret_cast<f32x4*>(gr + kDV + 8) = kZero4;
-          *reinterpret_cast<f32x4*>(gr + kDV + 12) = kZero4;
+        // S' += phi(K)^T V' for this wave's features (after its use: S' is the state before the chunk)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8 a = hilo(kt[j]);
+#pragma unroll
+          for (int eb = 0; eb < kNE; ++eb) {
+            const uint2 v4 = col4(VT, 16 * eb + c, g);
+            S[j][eb] = mfma_bf16(a, cat(v4, v4), S[j][eb]);
+          }
         }
-      }
-    }
-  }
+        __syncthreads();
+        // g' = [dout / den | -(dout . num) / den^2 | 0]: eight threads per token, eight columns each
+        if (tid < kT * 8) {
+          const int i = tid >> 3, e0 = 8 * (tid & 7);
+          f32x4 n0 = kZero4, n1 = kZero4;
+          float den = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < kW; ++ww) {
+            const float* pr = P + (ww * kT + i) * kLP;
+            n0 += *reinterpret_cast<const f32x4*>(pr + e0);
+            n1 += *reinterpret_cast<const f32x4*>(pr + e0 + 4);
+            den += pr[kDV];
+          }
+          const uint4 dr = i < n ? ax.d : make_uint4(0, 0, 0, 0);
+          const uint32_t dw[4] = {dr.x, dr.y, dr.z, dr.w};
+          float dn[8];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            dn[2 * t] = __uint_as_float(dw[t] << 16);
+            dn[2 * t + 1] = __uint_as_float(dw[t] & 0xFFFF0000u);
+          }
+          float dot = 0.f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) dot = fmaf(dn[t], n0[t], fmaf(dn[4 + t], n1[t], dot));
+          dot += __shfl_xor(dot, 1, 64);
+          dot += __shfl_xor(dot, 2, 64);
+          dot += __shfl_xor(dot, 4, 64);
+          if (i < n) {
+            const float inv = 1.f / den;
+            float* gr = p.g + (row0 + i) * kE;
+            f32x4 g0, g1;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              g0[t] = dn[t] * inv;
+              g1[t] = dn[4 + t] * inv;
+            }
+            *reinterpret_cast<f32x4*>(gr + e0) = g0;
+            *reinterpret_cast<f32x4*>(gr + e0 + 4) = g1;
+            if ((tid & 7) == 0) {
+              const f32x4 hz = {-dot * inv * inv, 0.f, 0.f, 0.f};
+              *reinterpret_cast<f32x4*>(gr + kDV) = hz;
+              *reinterpret_cast<f32x4*>(gr + kDV + 4) = kZero4;
+              *reinterpret_cast<f32x4*>(gr + kDV + 8) = kZero4;
+              *reinterpret_cast<f32x4*>(gr + kDV + 12) = kZero4;
+            }
+          }
+        }
+      });
 }
 
-// (4) dphi(Q) = D phi(K) + G' S'^T for this wave's features, and the segment's sum phi(Q)^T G' (written over
+// (3) dphi(Q) = D phi(K) + G' S'^T for this wave's features, and the segment's sum phi(Q)^T G' (written over
 // the item once the walk is done)
 __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
   __shared__ __align__(16) uint16_t VT[kE * kLT];
@@ -393,6 +555,8 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = min<int64_t>(p.L, t_begin + p.seg_len);
   float* item = item_ptr(p, h, seg);
+  Proj P;
+  load_proj(P, p, h, w, g, c);
   f32x4 S[kNE][2], U[2][kNE];  // S' as C[e][f] (contractions over e), U as C[f][e]
 #pragma unroll
   for (int eb = 0; eb < kNE; ++eb)
@@ -401,80 +565,82 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
       S[eb][j] = load_ef(item, 2 * w + j, eb, g, c);
       U[j][eb] = kZero4;
     }
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kT) {
-    const int n = (int)min<int64_t>(kT, t_end - t0);
-    const int64_t row0 = h * p.L + t0;
-    f32x4 qt[2], kt[2];
+  walk_steps<false>(
+      t_begin, t_end,
+      [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
+      [&](StepIn& in, int64_t t0, int n, auto prefetch) {
+        const int64_t row0 = h * p.L + t0;
+        const StepAux ax = load_aux<false, true>(p, row0, n, tid);
+        const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
+        prefetch();
+        bf16x8 qt[2], kt[2];  // split phi of the step's tokens, four per lane
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      qt[j] = load_tok4(p.phiq, row0, n, 2 * w + j, g, c);
-      kt[j] = load_tok4(p.phik, row0, n, 2 * w + j, g, c);
-    }
-    __syncthreads();
-    stage_v(p.v, row0, n, VR, VT, tid);
-    stage_g(p.g, row0, n, GRh, GRl, GTh, GTl, (tid + 256) & (kNT - 1));
-    __syncthreads();
-    // D^T[j][i] = v'_j . g'_i (split g'), masked j <= i < n; every wave forms it (lane: j = 4g + r, i = c)
-    f32x4 dt = kZero4;
+        for (int j = 0; j < 2; ++j) {
+          qt[j] = hilo(phi_tok(P, xq, j, g));
+          kt[j] = hilo(phi_tok(P, xk, j, g));
+        }
+        __syncthreads();
+        stage_v(ax.v, n, VR, VT, tid);
+        stage_g(ax.gp, n, GRh, GRl, GTh, GTl, tid);
+        __syncthreads();
+        // D^T[j][i] = v'_j . g'_i (split g'), masked j <= i < n; every wave forms it (lane: j = 4g + r, i = c)
+        f32x4 dt = kZero4;
 #pragma unroll
-    for (int kk = 0; kk < 64; kk += 32) {
-      const bf16x8 vr = ld8(VR + c * kLR + kk + 8 * g);
-      dt = mfma_bf16(vr, ld8(GRh + c * kLR + kk + 8 * g), dt);
-      dt = mfma_bf16(vr, ld8(GRl + c * kLR + kk + 8 * g), dt);
-    }
-    {
-      const bf16x8 vr = row4x2(VR, c, 4, -1, g);
-      dt = mfma_bf16(vr, row4x2(GRh, c, 4, -1, g), dt);
-      dt = mfma_bf16(vr, row4x2(GRl, c, 4, -1, g), dt);
-    }
+        for (int kk = 0; kk < 64; kk += 32) {
+          const bf16x8 vr = ld8(VR + c * kLR + kk + 8 * g);
+          dt = mfma_bf16(vr, ld8(GRh + c * kLR + kk + 8 * g), dt);
+          dt = mfma_bf16(vr, ld8(GRl + c * kLR + kk + 8 * g), dt);
+        }
+        {
+          const bf16x8 vr = row4x2(VR, c, 4, -1, g);
+          dt = mfma_bf16(vr, row4x2(GRh, c, 4, -1, g), dt);
+          dt = mfma_bf16(vr, row4x2(GRl, c, 4, -1, g), dt);
+        }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dt[r] = (4 * g + r <= c && c < n) ? dt[r] : 0.f;
-    uint2 d4, d4l;
-    split4(dt, d4, d4l);
-    // dphi(Q)^T[f][i] for this wave's features
+        for (int r = 0; r < 4; ++r) dt[r] = (4 * g + r <= c && c < n) ? dt[r] : 0.f;
+        uint2 d4, d4l;
+        split4(dt, d4, d4l);
+        // dphi(Q)^T[f][i] for this wave's features
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int fb = 2 * w + j;
-      f32x4 acc = mfma_bf16(hilo(kt[j]), cat(d4, d4), kZero4);
-      acc = mfma_bf16(cat(pk4(kt[j]), kZero2), cat(d4l, kZero2), acc);
+        for (int j = 0; j < 2; ++j) {
+          const int fb = 2 * w + j;
+          f32x4 acc = mfma_bf16(kt[j], cat(d4, d4), kZero4);
+          acc = mfma_bf16(hi_only(kt[j]), cat(d4l, kZero2), acc);
 #pragma unroll
-      for (int e0 = 0; e0 < kNE; e0 += 2) {
-        const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
-        uint2 a0h, a0l, a1h = kZero2, a1l = kZero2;
-        split4(S[e0][j], a0h, a0l);
-        if (e1 >= 0) split4(S[e1][j], a1h, a1l);
-        const bf16x8 sh = cat(a0h, a1h), sl = cat(a0l, a1l);
-        const bf16x8 gh = row4x2(GRh, c, e0, e1, g), gl = row4x2(GRl, c, e0, e1, g);
-        acc = mfma_bf16(sh, gh, acc);
-        acc = mfma_bf16(sl, gh, acc);
-        acc = mfma_bf16(sh, gl, acc);
-      }
-      if (c < n) *reinterpret_cast<uint2*>(p.dphiq + (row0 + c) * kF + 16 * fb + 4 * g) = pk4(acc);
-    }
-    // U += phi(Q)^T G' and S' += V'^T phi(K) for this wave's features
+          for (int e0 = 0; e0 < kNE; e0 += 2) {
+            const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
+            uint2 a0h, a0l, a1h = kZero2, a1l = kZero2;
+            split4(S[e0][j], a0h, a0l);
+            if (e1 >= 0) split4(S[e1][j], a1h, a1l);
+            const bf16x8 sh = cat(a0h, a1h), sl = cat(a0l, a1l);
+            const bf16x8 gh = row4x2(GRh, c, e0, e1, g), gl = row4x2(GRl, c, e0, e1, g);
+            acc = mfma_bf16(sh, gh, acc);
+            acc = mfma_bf16(sl, gh, acc);
+            acc = mfma_bf16(sh, gl, acc);
+          }
+          if (c < n) *reinterpret_cast<uint2*>(p.dphiq + (row0 + c) * kF + 16 * fb + 4 * g) = pk4(acc);
+        }
+        // U += phi(Q)^T G' and S' += V'^T phi(K) for this wave's features
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16x8 aq = hilo(qt[j]);
-      const bf16x8 aqh = cat(pk4(qt[j]), kZero2);
-      const bf16x8 bk = hilo(kt[j]);
+        for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int eb = 0; eb < kNE; ++eb) {
-        const uint2 gh = col4(GTh, 16 * eb + c, g), gl = col4(GTl, 16 * eb + c, g);
-        U[j][eb] = mfma_bf16(aq, cat(gh, gh), U[j][eb]);
-        U[j][eb] = mfma_bf16(aqh, cat(gl, kZero2), U[j][eb]);
-        const uint2 v4 = col4(VT, 16 * eb + c, g);
-        S[eb][j] = mfma_bf16(cat(v4, v4), bk, S[eb][j]);
-      }
-    }
-  }
-  __syncthreads();  // every wave has read its part of the item (loaded at the start) long before; keep order simple
+          for (int eb = 0; eb < kNE; ++eb) {
+            const uint2 gh = col4(GTh, 16 * eb + c, g), gl = col4(GTl, 16 * eb + c, g);
+            U[j][eb] = mfma_bf16(qt[j], cat(gh, gh), U[j][eb]);
+            U[j][eb] = mfma_bf16(hi_only(qt[j]), cat(gl, kZero2), U[j][eb]);
+            const uint2 v4 = col4(VT, 16 * eb + c, g);
+            S[eb][j] = mfma_bf16(cat(v4, v4), kt[j], S[eb][j]);
+          }
+        }
+      });
+  // every wave read only its own feature blocks of the item, at the start
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int eb = 0; eb < kNE; ++eb) store_fe(item, 2 * w + j, eb, lane, U[j][eb]);
 }
 
-// (6) dphi(K) = D^T phi(Q) + V' U^T for this wave's features, dV = A^T G + phi(K) U[:, :dv] (per-wave partials
+// (5) dphi(K) = D^T phi(Q) + V' U^T for this wave's features, dV = A^T G + phi(K) U[:, :dv] (per-wave partials
 // summed through LDS), walking the segment backward with U (the item: U after the segment) in accumulators
 __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
   __shared__ __align__(16) uint16_t VR[kT * kLR];
@@ -491,6 +657,8 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = min<int64_t>(p.L, t_begin + p.seg_len);
   const float* item = item_ptr(p, h, seg);
+  Proj Pj;
+  load_proj(Pj, p, h, w, g, c);
   f32x4 UA[2][kNE], UB[kNE][2];  // U as C[f][e] (contraction over f: dV) and as C[e][f] (over e: dphi(K))
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -499,97 +667,99 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
       UA[j][eb] = load_fe(item, 2 * w + j, eb, lane);
       UB[eb][j] = load_ef(item, 2 * w + j, eb, g, c);
     }
-  const int n_steps = (int)((t_end - t_begin + kT - 1) / kT);
-  for (int st = n_steps - 1; st >= 0; --st) {
-    const int64_t t0 = t_begin + (int64_t)st * kT;
-    const int n = (int)min<int64_t>(kT, t_end - t0);
-    const int64_t row0 = h * p.L + t0;
-    f32x4 qa, qb, ka, kb, qt[2];
-    load_feat8(p.phiq, row0, n, w, g, c, qa, qb);
-    load_feat8(p.phik, row0, n, w, g, c, ka, kb);
+  walk_steps<true>(
+      t_begin, t_end,
+      [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
+      [&](StepIn& in, int64_t t0, int n, auto prefetch) {
+        const int64_t row0 = h * p.L + t0;
+        const StepAux ax = load_aux<false, true>(p, row0, n, tid);
+        const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
+        prefetch();
+        const f32x4 qa = phi_feat(Pj, xq, 0), qb = phi_feat(Pj, xq, 1);
+        const f32x4 ka = phi_feat(Pj, xk, 0), kb = phi_feat(Pj, xk, 1);
+        bf16x8 qt[2];  // split phi(q) of the step's tokens, four per lane
 #pragma unroll
-    for (int j = 0; j < 2; ++j) qt[j] = load_tok4(p.phiq, row0, n, 2 * w + j, g, c);
-    __syncthreads();
-    stage_v(p.v, row0, n, VR, VT, tid);
-    stage_g(p.g, row0, n, GRh, GRl, GTh, GTl, (tid + 256) & (kNT - 1));
-    __syncthreads();
-    // this wave's part of A[i][j] over its features, masked i >= j (lane: i = 4g + r, j = c)
-    f32x4 aw = mfma_bf16(pk_pair(qa, qb), pk_pair(ka, kb), kZero4);
+        for (int j = 0; j < 2; ++j) qt[j] = hilo(phi_tok(Pj, xq, j, g));
+        __syncthreads();
+        stage_v(ax.v, n, VR, VT, tid);
+        stage_g(ax.gp, n, GRh, GRl, GTh, GTl, tid);
+        __syncthreads();
+        // this wave's part of A[i][j] over its features, masked i >= j (lane: i = 4g + r, j = c)
+        f32x4 aw = mfma_bf16(pk_pair(qa, qb), pk_pair(ka, kb), kZero4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) aw[r] = (4 * g + r >= c && 4 * g + r < n) ? aw[r] : 0.f;
-    const bf16x8 awb = cat(pk4(aw), kZero2);
-    // D[i][j] = g'_i . v'_j (split g'), masked i >= j (lane: i = 4g + r, j = c)
-    f32x4 dm = kZero4;
+        for (int r = 0; r < 4; ++r) aw[r] = (4 * g + r >= c && 4 * g + r < n) ? aw[r] : 0.f;
+        const bf16x8 awb = cat(pk4(aw), kZero2);
+        // D[i][j] = g'_i . v'_j (split g'), masked i >= j (lane: i = 4g + r, j = c)
+        f32x4 dm = kZero4;
 #pragma unroll
-    for (int kk = 0; kk < 64; kk += 32) {
-      const bf16x8 vr = ld8(VR + c * kLR + kk + 8 * g);
-      dm = mfma_bf16(ld8(GRh + c * kLR + kk + 8 * g), vr, dm);
-      dm = mfma_bf16(ld8(GRl + c * kLR + kk + 8 * g), vr, dm);
-    }
-    {
-      const bf16x8 vr = row4x2(VR, c, 4, -1, g);
-      dm = mfma_bf16(row4x2(GRh, c, 4, -1, g), vr, dm);
-      dm = mfma_bf16(row4x2(GRl, c, 4, -1, g), vr, dm);
-    }
+        for (int kk = 0; kk < 64; kk += 32) {
+          const bf16x8 vr = ld8(VR + c * kLR + kk + 8 * g);
+          dm = mfma_bf16(ld8(GRh + c * kLR + kk + 8 * g), vr, dm);
+          dm = mfma_bf16(ld8(GRl + c * kLR + kk + 8 * g), vr, dm);
+        }
+        {
+          const bf16x8 vr = row4x2(VR, c, 4, -1, g);
+          dm = mfma_bf16(row4x2(GRh, c, 4, -1, g), vr, dm);
+          dm = mfma_bf16(row4x2(GRl, c, 4, -1, g), vr, dm);
+        }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dm[r] = (4 * g + r >= c && 4 * g + r < n) ? dm[r] : 0.f;
-    uint2 d4, d4l;
-    split4(dm, d4, d4l);
-    // dphi(K)^T[f][j] for this wave's features
+        for (int r = 0; r < 4; ++r) dm[r] = (4 * g + r >= c && 4 * g + r < n) ? dm[r] : 0.f;
+        uint2 d4, d4l;
+        split4(dm, d4, d4l);
+        // dphi(K)^T[f][j] for this wave's features
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int fb = 2 * w + j;
-      f32x4 acc = mfma_bf16(hilo(qt[j]), cat(d4, d4), kZero4);
-      acc = mfma_bf16(cat(pk4(qt[j]), kZero2), cat(d4l, kZero2), acc);
+        for (int j = 0; j < 2; ++j) {
+          const int fb = 2 * w + j;
+          f32x4 acc = mfma_bf16(qt[j], cat(d4, d4), kZero4);
+          acc = mfma_bf16(hi_only(qt[j]), cat(d4l, kZero2), acc);
 #pragma unroll
-      for (int e0 = 0; e0 < kNE; e0 += 2) {
-        const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
-        uint2 a0h, a0l, a1h = kZero2, a1l = kZero2;
-        split4(UB[e0][j], a0h, a0l);
-        if (e1 >= 0) split4(UB[e1][j], a1h, a1l);
-        const bf16x8 vr = row4x2(VR, c, e0, e1, g);
-        acc = mfma_bf16(cat(a0h, a1h), vr, acc);
-        acc = mfma_bf16(cat(a0l, a1l), vr, acc);
-      }
-      if (c < n) *reinterpret_cast<uint2*>(p.dphik + (row0 + c) * kF + 16 * fb + 4 * g) = pk4(acc);
-    }
-    // dV^T[e][j] partial (e < dv): G^T A over this wave's A part, and U^T phi(K)^T over its features
+          for (int e0 = 0; e0 < kNE; e0 += 2) {
+            const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
+            uint2 a0h, a0l, a1h = kZero2, a1l = kZero2;
+            split4(UB[e0][j], a0h, a0l);
+            if (e1 >= 0) split4(UB[e1][j], a1h, a1l);
+            const bf16x8 vr = row4x2(VR, c, e0, e1, g);
+            acc = mfma_bf16(cat(a0h, a1h), vr, acc);
+            acc = mfma_bf16(cat(a0l, a1l), vr, acc);
+          }
+          if (c < n) *reinterpret_cast<uint2*>(p.dphik + (row0 + c) * kF + 16 * fb + 4 * g) = pk4(acc);
+        }
+        // dV^T[e][j] partial (e < dv): G^T A over this wave's A part, and U^T phi(K)^T over its features
 #pragma unroll
-    for (int eb = 0; eb < kDV / 16; ++eb) {
-      f32x4 acc = mfma_bf16(cat(col4(GTh, 16 * eb + c, g), kZero2), awb, kZero4);
-      acc = mfma_bf16(pk_pair(UA[0][eb], UA[1][eb]), pk_pair(ka, kb), acc);
-      *reinterpret_cast<f32x4*>(P + (w * kT + c) * kLPV + 16 * eb + 4 * g) = acc;  // lane: e = 16 eb + 4g + r, j = c
-    }
-    // U += phi(Q)^T G' (both orders) for the earlier chunks
+        for (int eb = 0; eb < kDV / 16; ++eb) {
+          f32x4 acc = mfma_bf16(cat(col4(GTh, 16 * eb + c, g), kZero2), awb, kZero4);
+          acc = mfma_bf16(pk_pair(UA[0][eb], UA[1][eb]), pk_pair(ka, kb), acc);
+          *reinterpret_cast<f32x4*>(P + (w * kT + c) * kLPV + 16 * eb + 4 * g) = acc;  // lane: e = 16 eb + 4g + r, j = c
+        }
+        // U += phi(Q)^T G' (both orders) for the earlier chunks
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16x8 aq = hilo(qt[j]);
-      const bf16x8 aqh = cat(pk4(qt[j]), kZero2);
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8 aqh = hi_only(qt[j]);
 #pragma unroll
-      for (int eb = 0; eb < kNE; ++eb) {
-        const uint2 gh = col4(GTh, 16 * eb + c, g), gl = col4(GTl, 16 * eb + c, g);
-        UA[j][eb] = mfma_bf16(aq, cat(gh, gh), UA[j][eb]);
-        UA[j][eb] = mfma_bf16(aqh, cat(gl, kZero2), UA[j][eb]);
-        UB[eb][j] = mfma_bf16(cat(gh, gh), aq, UB[eb][j]);
-        UB[eb][j] = mfma_bf16(cat(gl, kZero2), aqh, UB[eb][j]);
-      }
-    }
-    __syncthreads();
-    if (tid < kT * 8) {  // dV rows: sum of the waves' partials, eight columns per thread
-      const int jj = tid >> 3, e0 = 8 * (tid & 7);
-      f32x4 a0 = kZero4, a1 = kZero4;
+          for (int eb = 0; eb < kNE; ++eb) {
+            const uint2 gh = col4(GTh, 16 * eb + c, g), gl = col4(GTl, 16 * eb + c, g);
+            UA[j][eb] = mfma_bf16(qt[j], cat(gh, gh), UA[j][eb]);
+            UA[j][eb] = mfma_bf16(aqh, cat(gl, kZero2), UA[j][eb]);
+            UB[eb][j] = mfma_bf16(cat(gh, gh), qt[j], UB[eb][j]);
+            UB[eb][j] = mfma_bf16(cat(gl, kZero2), aqh, UB[eb][j]);
+          }
+        }
+        __syncthreads();
+        if (tid < kT * 8) {  // dV rows: sum of the waves' partials, eight columns per thread
+          const int jj = tid >> 3, e0 = 8 * (tid & 7);
+          f32x4 a0 = kZero4, a1 = kZero4;
 #pragma unroll
-      for (int ww = 0; ww < kW; ++ww) {
-        const float* pr = P + (ww * kT + jj) * kLPV + e0;
-        a0 += *reinterpret_cast<const f32x4*>(pr);
-        a1 += *reinterpret_cast<const f32x4*>(pr + 4);
-      }
-      if (jj < n) {
-        const uint2 lo = pk4(a0), hi = pk4(a1);
-        *reinterpret_cast<uint4*>(p.dv + (row0 + jj) * kDV + e0) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      }
-    }
-  }
+          for (int ww = 0; ww < kW; ++ww) {
+            const float* pr = P + (ww * kT + jj) * kLPV + e0;
+            a0 += *reinterpret_cast<const f32x4*>(pr);
+            a1 += *reinterpret_cast<const f32x4*>(pr + 4);
+          }
+          if (jj < n) {
+            const uint2 lo = pk4(a0), hi = pk4(a1);
+            *reinterpret_cast<uint4*>(p.dv + (row0 + jj) * kDV + e0) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          }
+        }
+      });
 }
 
 // ---------------------------------------------------------------------------
@@ -798,15 +968,18 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
 // ---------------------------------------------------------------------------
 using V256 = VjpK<16>;
 
-// Segments of the precise kernels: about 1024 workgroups over all heads (four
-// per compute unit), whole 16-token steps, at least 64 tokens each.
+// Segments of the precise kernels: about PB_WG workgroups over all heads, whole
+// 16-token steps, at least 64 tokens each.
+#ifndef PB_WG
+#define PB_WG 512
+#endif
 int64_t pb_seg_len(int64_t n_heads, int64_t L) {
-  const int64_t want = (L * n_heads + 1023) / 1024;
+  const int64_t want = (L * n_heads + PB_WG - 1) / PB_WG;
   return std::max<int64_t>(64, (want + kT - 1) / kT * kT);
 }
 
 struct PbWs {
-  float *states, *phiq, *phik, *g;
+  float *states, *g;
   uint16_t *dphiq, *dphik;
   size_t bytes;
 };
@@ -822,8 +995,6 @@ PbWs pb_ws(const BackwardArgs& a, int n_seg, void* base) {
     return q;
   };
   w.states = reinterpret_cast<float*>(take(sizeof(float) * (size_t)a.n_heads * n_seg * kF * kE));
-  w.phiq = reinterpret_cast<float*>(take(sizeof(float) * (size_t)rows * kF));
-  w.phik = reinterpret_cast<float*>(take(sizeof(float) * (size_t)rows * kF));
   w.g = reinterpret_cast<float*>(take(sizeof(float) * (size_t)rows * kE));
   w.dphiq = reinterpret_cast<uint16_t*>(take(2 * (size_t)rows * kF));
   w.dphik = reinterpret_cast<uint16_t*>(take(2 * (size_t)rows * kF));
@@ -897,29 +1068,15 @@ hipError_t launch_backward_fused_256(const BackwardArgs& a, hipStream_t s) {
   const int n_seg = (int)((a.L + seg_len - 1) / seg_len);
   const PbWs w = pb_ws(a, n_seg, a.ws);
 
-  FeatmapArgs fm{};
-  fm.x = a.q;
-  fm.x2 = a.k;
-  fm.rows_per_head = a.L;
-  fm.n_heads = a.n_heads;
-  fm.d = a.d;
-  fm.F = a.F;
-  fm.m = a.m;
-  fm.x_bf16 = true;
-  fm.anchors = a.anchors;
-  fm.prf = a.prf;
-  fm.draw_set_stride = a.draw_set_stride;
-  fm.n_draw_sets = a.n_draw_sets;
-  fm.nc = a.nc;
-  fm.phi = w.phiq;
-  fm.phi2 = w.phik;
-  fm.phi_bf16 = false;
-  hipError_t e = launch_featmap(fm, s);
-  if (e != hipSuccess) return e;
-
   PbParams p{};
-  p.phiq = w.phiq;
-  p.phik = w.phik;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.anchors = static_cast<const uint16_t*>(a.anchors);
+  p.prf = static_cast<const uint16_t*>(a.prf);
+  p.draw_set_stride = a.draw_set_stride;
+  p.n_draw_sets = a.n_draw_sets;
+  p.m = a.m;
+  p.nc = a.nc;
   p.v = static_cast<const uint16_t*>(a.v);
   p.dout = static_cast<const uint16_t*>(a.dout);
   p.L = a.L;
@@ -930,6 +1087,7 @@ hipError_t launch_backward_fused_256(const BackwardArgs& a, hipStream_t s) {
   p.dphiq = w.dphiq;
   p.dphik = w.dphik;
   p.dv = static_cast<uint16_t*>(a.dv_out);
+  hipError_t e = hipSuccess;
   if (n_seg > 1) {
     hipLaunchKernelGGL(pb_state_kernel, dim3((unsigned)(a.n_heads * (n_seg - 1))), dim3(kNT), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
