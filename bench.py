@@ -52,7 +52,7 @@ UNIT_SOURCES = {
     "noncausal_h16_l16k_bf16": _FWD,
     "varlen_h16_8seqs_16k_bf16": _FWD,
     "featmap_h16_l16k_bf16": ("slay_featmap.hip", "slay_device.hpp"),
-    "backward_h16_l16k_bf16": ("slay_backward_fused.hip", "slay_featmap.hip") + _FWD,
+    "backward_h16_l16k_bf16": ("slay_backward_fused.hip", "slay_chunked_generic.hip", "slay_device.hpp"),
     "long_h8_l128k_d128_bf16": ("slay_chunked_wide.hip", "slay_featmap.hip", "slay_chunked_generic.hip",
                                 "slay_device.hpp"),
     "decode_256x16_f32": ("slay_decode.hip", "slay_featmap.hip", "slay_device.hpp"),
@@ -138,9 +138,8 @@ TRAFFIC_UNITS = {
                                 "one non-causal forward, B1 H16 Lq = Lk = 16384 bf16"),
     "varlen_h16_8seqs_16k_bf16": ("varlen", (("vl_setup", 1), ("pass1s", 1), ("vl_scan", 1), ("pass2s", 1)),
                                   "one variable-length forward, 16 heads x 8 sequences (16384 tokens) bf16"),
-    "backward_h16_l16k_bf16": ("backward", (("featmap_kernel<unsigned short, unsigned short", 1), ("pass1s", 1),
-                                            ("scan_kernel", 2), ("bwd_q_kernel", 1), ("bwd_kv_kernel", 1),
-                                            ("vjp_kernel", 1)),
+    "backward_h16_l16k_bf16": ("backward", (("pb_state", 1), ("scan_kernel", 2), ("pb_g", 1), ("pb_dq", 1),
+                                            ("pb_dk", 1), ("vjp_kernel", 1)),
                                "one causal backward, B1 H16 L16384 bf16"),
     "long_h8_l128k_d128_bf16": ("long", (("featmap_kernel<unsigned short, unsigned short", 1), ("wstate", 1),
                                          ("scan_kernel", 1), ("wout", 1)),
@@ -208,6 +207,128 @@ def traffic_summary(fetch_dir: str, write_dir: str, calib_mib: int, command: str
         print(name, f"{total / 1e6:.1f} MB per launch")
 
 
+COUNTER_UNITS = {
+    # bench --only part: (summary name, kernel-name fragments, description)
+    "fwd": ("fused_fwd_h16_l16k_bf16", ("pass1s", "scan_kernel", "pass2s"),
+            "causal forward, B1 H16 L16384 d=dv=64 F=256 bf16"),
+    "small": ("fused_fwd_b4h8_l2k_bf16", ("pass1s", "scan_kernel", "pass2s"),
+              "causal forward, B4 H8 L2048 d=dv=64 F=96 bf16"),
+    "featmap": ("featmap_h16_l16k_bf16", ("featmap_kernel",), "feature map of 262144 bf16 rows, F = 256"),
+    "backward": ("backward_h16_l16k_bf16", ("pb_state", "scan_kernel", "pb_g", "pb_dq", "pb_dk", "vjp"),
+                 "causal backward, B1 H16 L16384 bf16"),
+    "varlen": ("varlen_h16_8seqs_16k_bf16", ("vl_setup", "pass1s", "vl_scan", "pass2s"),
+               "variable-length causal forward, 16 heads x 8 sequences (16384 tokens) bf16"),
+    "long": ("long_h8_l128k_d128_bf16", ("featmap_kernel", "wstate", "scan_kernel", "wout"),
+             "causal forward, B1 H8 L131072 d=dv=128 F=512 bf16 (wide path)"),
+    "noncausal": ("noncausal_h16_l16k_bf16", ("pass1s", "scan_kernel", "ncout"),
+                  "non-causal forward, B1 H16 L16384 bf16"),
+    "decode": ("decode_256x16_f32", ("featmap_kernel", "stream_kernel"), "decode step, 4096 heads, fp32"),
+}
+
+
+def counter_summary(pmc_dir: str, command: str, part: str) -> None:
+    """profiles/counters_<unit>.md from one rocprofv3 --pmc run (with --kernel-trace) of `bench.py --only part`:
+    per kernel, the averages over its dispatches of MFMA and VALU busy (% of the kernel's time on all SIMDs),
+    LDS utilisation, LDS bank-conflict cycles per active LDS instruction cycle and the bf16 MFMA work executed."""
+    import collections
+    import csv
+    import glob
+
+    name, frags, desc = COUNTER_UNITS[part]
+    path = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)[0]
+    vals = collections.defaultdict(lambda: collections.defaultdict(float))
+    kname = {}
+    for r in csv.DictReader(open(path)):
+        vals[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        kname[r["Dispatch_Id"]] = r["Kernel_Name"]
+    dur = {}
+    tr = glob.glob(os.path.join(pmc_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if tr:
+        for r in csv.DictReader(open(tr[0])):
+            dur[r["Dispatch_Id"]] = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3  # us
+    per = collections.defaultdict(list)
+    for did, cv in vals.items():
+        kn = kname[did]
+        if any(f in kn for f in frags):
+            per[kn].append((cv, dur.get(did)))
+    lines = [f"# rocprofv3 counters: {name}", "", f"unit: {desc}", "",
+             "command (from the repository root, on the machine with the GPU):", "", f"    {command}",
+             f"    python bench.py --only {part} --counter-summary <dir>", "",
+             "Per kernel, averages over its dispatches.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs for the "
+             "kernel's time (rocprofv3's MfmaUtil); VALU busy = rocprofv3's VALUBusy (SQ_ACTIVE_INST_VALU per CU "
+             "over the kernel's time); LDS util = LdsUtil; LDS conflict ratio = SQ_LDS_BANK_CONFLICT / "
+             "SQ_ACTIVE_INST_LDS (bank-conflict stall cycles per cycle of active LDS instructions); MFMA-VALU "
+             "co-issue = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; bf16 MFMA work = "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops, executed (recomputation included), and its rate over "
+             "the dispatch's traced duration (the counters serialise dispatches, so durations here run longer "
+             "than in the timing runs).", "",
+             "| kernel | dispatches | MFMA busy % | VALU busy % | LDS util % | LDS conflict ratio | MFMA-VALU co-issue |"
+             " bf16 MFMA GFLOP / dispatch | executed TFLOP/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for kn, rows in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        n = len(rows)
+        avg = lambda c: sum(r[0].get(c, 0.0) for r in rows) / n  # noqa: E731
+        lds_act = avg("SQ_ACTIVE_INST_LDS")
+        busy = avg("SQ_VALU_MFMA_BUSY_CYCLES")
+        gflop = avg("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / 1e9
+        ds = [r[1] for r in rows if r[1]]
+        rate = gflop / (sum(ds) / len(ds)) * 1e3 if ds else float("nan")  # GFLOP per us -> TFLOP/s
+        lines.append(f"| {kn[:70]} | {n} | {avg('MfmaUtil'):.1f} | {avg('VALUBusy'):.1f} | {avg('LdsUtil'):.1f} | "
+                     f"{(avg('SQ_LDS_BANK_CONFLICT') / lds_act) if lds_act else 0.0:.2f} | "
+                     f"{(avg('SQ_VALU_MFMA_COEXEC_CYCLES') / busy) if busy else 0.0:.2f} | {gflop:.2f} | "
+                     f"{rate:.0f} |")
+    lines += ["", f"sources ({', '.join(UNIT_SOURCES[name])}):",
+              f"sources_sha256_16: {sources_digest(UNIT_SOURCES[name])}"]
+    with open(os.path.join(ROOT, "profiles", f"counters_{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats_summary(trace_dir: str, command: str, part: str) -> None:
+    """profiles/<unit>.md from one rocprofv3 --kernel-trace --stats run of `bench.py --only part` with as many
+    warm-up steps as timed ones and no settle steps: per kernel, the average duration over all its dispatches
+    and over the later half (the timed calls)."""
+    import collections
+    import csv
+    import glob
+
+    name, frags, desc = COUNTER_UNITS[part]
+    path = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if any(f in r["Kernel_Name"] for f in frags):
+            per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
+    lines = [f"# rocprofv3 kernel statistics: {name}", "", f"workload: {desc}", "",
+             "command (from the repository root, on the machine with the GPU):", "", f"    {command}",
+             f"    python bench.py --only {part} --stats-summary <dir>", "",
+             "bench.py runs as many warm-up calls as timed ones here (it scales both per part) and no settle "
+             "steps, so the later half of each kernel's dispatches are the timed calls. `average` is over every "
+             "call, `timed average` over the timed calls only.", "",
+             "| kernel | calls | average (us) | timed average (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
+    total = 0.0
+    rows = []
+    for kn, ds in per.items():
+        ds.sort()
+        d = [x[1] for x in ds]
+        timed = d[len(d) // 2:]
+        rows.append((sum(timed) / len(timed), kn, len(d), sum(d) / len(d), min(d), max(d)))
+    n_units = None
+    for ta, kn, n, avg, mn, mx in sorted(rows, reverse=True):
+        short = re.sub(r"slay::\(anonymous namespace\)::", "", kn)
+        short = re.sub(r"^void ", "", short)
+        short = re.sub(r"\(.*\)$", "", short)
+        lines.append(f"| {short[:80]} | {n} | {avg:.2f} | {ta:.2f} | {mn:.2f} | {mx:.2f} |")
+        total += ta * n
+        n_units = n if n_units is None else min(n_units, n)
+    if n_units:
+        lines += ["", f"sum of the timed averages per launch of the unit: {total / n_units:.1f} us"]
+    lines += ["", f"sources ({', '.join(UNIT_SOURCES[name])}):",
+              f"sources_sha256_16: {sources_digest(UNIT_SOURCES[name])}"]
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def event_time_ms(fn, steps: int, stream) -> float:
     import torch
 
@@ -227,6 +348,8 @@ def warm_up(fn, steps: int, stream) -> int:
     has passed in this warm-up; returns the number of extra calls."""
     import torch
 
+    settle_ms = SETTLE_MS  # set from --settle-ms
+
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -237,7 +360,7 @@ def warm_up(fn, steps: int, stream) -> int:
     torch.cuda.synchronize()
     spent = start.elapsed_time(end) if steps > 0 else 0.0
     extra = 0
-    while spent < SETTLE_MS:
+    while spent < settle_ms:
         n = 8 if extra == 0 else extra  # doubling batches
         start.record(stream)
         for _ in range(n):
@@ -320,6 +443,7 @@ def cpu_baselines_other():
 
 
 def main():
+    global SETTLE_MS
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -336,9 +460,30 @@ def main():
                     help="first run 3 plain device copies of this many MiB (scale for HBM byte counters)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_*.txt from two rocprofv3 --pmc runs and exit (no GPU)")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="minimum GPU time of untimed work before each timed loop (0: only the warm-up steps)")
+    ap.add_argument("--counter-summary", metavar="PMC_DIR",
+                    help="write profiles/counters_*.md from one rocprofv3 --pmc run of this part and exit (no GPU)")
+    ap.add_argument("--counter-command", default="rocprofv3 --pmc " + " ".join(
+        ["MfmaUtil", "VALUBusy", "LdsUtil", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
+         "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_COEXEC_CYCLES"]) +
+        " --kernel-trace --output-format csv -d <dir> -o run -- python3 bench.py --only PART --steps 5 --warmup 1 "
+        "--settle-ms 0 --decode-steps 32 --no-cpu")
     ap.add_argument("--traffic-command", default="rocprofv3 --pmc COUNTER --output-format csv -d <dir> -o run -- "
-                    "python3 bench.py --only PART --steps 5 --warmup 1 --decode-steps 32 --no-cpu --calib-copy-mib 512")
+                    "python3 bench.py --only PART --steps 5 --warmup 1 --settle-ms 0 --decode-steps 32 --no-cpu "
+                    "--calib-copy-mib 512")
+    ap.add_argument("--stats-summary", metavar="TRACE_DIR",
+                    help="write profiles/<unit>.md from one rocprofv3 --kernel-trace --stats run of this part and exit")
+    ap.add_argument("--stats-command", default="rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                    "python3 bench.py --only PART --steps 100 --warmup 100 --settle-ms 0 --decode-steps 64 --no-cpu")
     args = ap.parse_args()
+    SETTLE_MS = args.settle_ms
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.counter_command.replace("PART", args.only), args.only)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary, args.stats_command.replace("PART", args.only), args.only)
+        return
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.calib_copy_mib or 512,
                         args.traffic_command.replace("PART", args.only), args.only)
