@@ -128,21 +128,21 @@ def read_traffic(kind: str):
 TRAFFIC_UNITS = {
     # summary name: (bench --only part, kernel-name fragments with their dispatches per launch of the unit,
     # description); the counters of each unit come from runs of that part alone
-    "fused_fwd_h16_l16k_bf16": ("fwd", (("pass1s", 1), ("scan_kernel", 1), ("pass2s", 1)),
+    "fused_fwd_h16_l16k_bf16": ("fwd", (("pass1s", 1), ("scan4_kernel", 1), ("pass2s", 1)),
                                 "one causal forward, B1 H16 L16384 bf16 (segment states + scan + main pass)"),
-    "fused_fwd_b4h8_l2k_bf16": ("small", (("pass1_kernel", 1), ("scan_kernel", 1), ("pass2s", 1)),
+    "fused_fwd_b4h8_l2k_bf16": ("small", (("pass1_kernel", 1), ("scan4_kernel", 1), ("pass2s", 1)),
                                 "one causal forward, B4 H8 L2048 F = 96 bf16 (segment states + scan + main pass)"),
     "featmap_h16_l16k_bf16": ("featmap", (("featmap_kernel<unsigned short, unsigned short", 1),),
                               "one feature-map launch over 262144 bf16 rows, F = 256"),
-    "noncausal_h16_l16k_bf16": ("noncausal", (("pass1s", 1), ("scan_kernel", 1), ("ncout_kernel", 1)),
+    "noncausal_h16_l16k_bf16": ("noncausal", (("pass1s", 1), ("scan4_kernel", 1), ("ncout_kernel", 1)),
                                 "one non-causal forward, B1 H16 Lq = Lk = 16384 bf16"),
     "varlen_h16_8seqs_16k_bf16": ("varlen", (("vl_setup", 1), ("pass1s", 1), ("vl_scan", 1), ("pass2s", 1)),
                                   "one variable-length forward, 16 heads x 8 sequences (16384 tokens) bf16"),
-    "backward_h16_l16k_bf16": ("backward", (("pb_state", 1), ("scan_kernel", 2), ("pb_g", 1), ("pb_dq", 1),
+    "backward_h16_l16k_bf16": ("backward", (("pb_state", 1), ("scan4_kernel", 2), ("pb_g", 1), ("pb_dq", 1),
                                             ("pb_dk", 1), ("vjp_kernel", 1)),
                                "one causal backward, B1 H16 L16384 bf16"),
     "long_h8_l128k_d128_bf16": ("long", (("featmap_kernel<unsigned short, unsigned short", 1), ("wstate", 1),
-                                         ("scan_kernel", 1), ("wout", 1)),
+                                         ("scan4_kernel", 1), ("wout", 1)),
                                 "one causal forward, B1 H8 L131072 d=dv=128 F=512 bf16 (wide path)"),
     "decode_256x16_f32": ("decode", (("featmap_kernel<float, float", 1), ("stream_kernel", 1)),
                           "one decode step for 4096 heads (q/k feature map + state stream)"),
@@ -209,18 +209,18 @@ def traffic_summary(fetch_dir: str, write_dir: str, calib_mib: int, command: str
 
 COUNTER_UNITS = {
     # bench --only part: (summary name, kernel-name fragments, description)
-    "fwd": ("fused_fwd_h16_l16k_bf16", ("pass1s", "scan_kernel", "pass2s"),
+    "fwd": ("fused_fwd_h16_l16k_bf16", ("pass1s", "scan4_kernel", "pass2s"),
             "causal forward, B1 H16 L16384 d=dv=64 F=256 bf16"),
-    "small": ("fused_fwd_b4h8_l2k_bf16", ("pass1_kernel", "scan_kernel", "pass2s"),
+    "small": ("fused_fwd_b4h8_l2k_bf16", ("pass1_kernel", "scan4_kernel", "pass2s"),
               "causal forward, B4 H8 L2048 d=dv=64 F=96 bf16"),
     "featmap": ("featmap_h16_l16k_bf16", ("featmap_kernel",), "feature map of 262144 bf16 rows, F = 256"),
-    "backward": ("backward_h16_l16k_bf16", ("pb_state", "scan_kernel", "pb_g", "pb_dq", "pb_dk", "vjp"),
+    "backward": ("backward_h16_l16k_bf16", ("pb_state", "scan4_kernel", "pb_g", "pb_dq", "pb_dk", "vjp"),
                  "causal backward, B1 H16 L16384 bf16"),
     "varlen": ("varlen_h16_8seqs_16k_bf16", ("vl_setup", "pass1s", "vl_scan", "pass2s"),
                "variable-length causal forward, 16 heads x 8 sequences (16384 tokens) bf16"),
-    "long": ("long_h8_l128k_d128_bf16", ("featmap_kernel", "wstate", "scan_kernel", "wout"),
+    "long": ("long_h8_l128k_d128_bf16", ("featmap_kernel", "wstate", "scan4_kernel", "wout"),
              "causal forward, B1 H8 L131072 d=dv=128 F=512 bf16 (wide path)"),
-    "noncausal": ("noncausal_h16_l16k_bf16", ("pass1s", "scan_kernel", "ncout"),
+    "noncausal": ("noncausal_h16_l16k_bf16", ("pass1s", "scan4_kernel", "ncout"),
                   "non-causal forward, B1 H16 L16384 bf16"),
     "decode": ("decode_256x16_f32", ("featmap_kernel", "stream_kernel"), "decode step, 4096 heads, fp32"),
 }

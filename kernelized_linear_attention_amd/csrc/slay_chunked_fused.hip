@@ -1429,18 +1429,21 @@ __global__ __launch_bounds__(256) void vl_setup_kernel(const int64_t* __restrict
   __shared__ int pf[256], pt[256];
   __shared__ int bad, n_full_all;
   const int tid = threadIdx.x;
-  if (tid == 0) bad = (cu[0] != 0 || cu[n_seqs] != T) ? 1 : 0;
-  __syncthreads();
   const int per = (n_seqs + 255) / 256;
   const int s0 = min(n_seqs, tid * per), s1 = min(n_seqs, s0 + per);
-  int lf = 0, lt = 0;
+  // every thread's offsets are read in one round trip with the end checks
+  const bool ends_bad = tid == 0 && (cu[0] != 0 || cu[n_seqs] != T);
+  int lf = 0, lt = 0, lbad = ends_bad ? 1 : 0;
   for (int sq = s0; sq < s1; ++sq) {
     const int64_t len = cu[sq + 1] - cu[sq];
-    if (len < 0) atomicOr(&bad, 1);
+    lbad |= len < 0;
     const int64_t l = max<int64_t>(len, 0);
     lf += (int)(l / seg_len);
     lt += (l % seg_len) != 0;
   }
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  if (lbad) atomicOr(&bad, 1);
   // exclusive prefix of the per-thread counts: inclusive scan within each wave
   // (shuffles), then the four wave totals
   int sf = lf, st = lt;

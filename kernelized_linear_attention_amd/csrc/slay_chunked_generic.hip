@@ -82,6 +82,70 @@ __global__ __launch_bounds__(kGThreads) void scan_kernel(ScanArgs a, int64_t E) 
   }
 }
 
+// Initial value of state elements (f + i, e), i < 4: S0 / z0 of row `sh`, or 0.
+__device__ __forceinline__ float4 scan_init4(const float* S0, const float* z0, int64_t sh, int F, int dv, int f,
+                                             int e) {
+  float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (e < dv) {
+      if (S0) r[i] = S0[(sh * F + f + i) * dv + e];
+    } else if (z0) {
+      r[i] = z0[sh * F + f + i];
+    }
+  }
+  return make_float4(r[0], r[1], r[2], r[3]);
+}
+
+__device__ __forceinline__ void scan_out4(float* S_out, float* z_out, int64_t sh, int F, int dv, int f, int e,
+                                          float4 v) {
+  const float r[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (e < dv) {
+      if (S_out) S_out[(sh * F + f + i) * dv + e] = r[i];
+    } else if (z_out) {
+      z_out[sh * F + f + i] = r[i];
+    }
+  }
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// scan_kernel for the fragment layout, one 16-byte vector per thread: the four
+// elements of a vector share the column e (features f .. f+3), so a vector is
+// either all padding or all state.
+__global__ __launch_bounds__(kGThreads) void scan4_kernel(ScanArgs a, int64_t E) {
+  const int64_t h = blockIdx.y;
+  const int64_t idx = ((int64_t)blockIdx.x * kGThreads + threadIdx.x) * 4;
+  if (idx >= E) return;
+  int f, e;
+  scan_map(idx, a.F, a.dv, 1, f, e);
+  const int64_t step = a.reverse ? -E : E;
+  float4* st = reinterpret_cast<float4*>(a.states + h * a.n_items * E + idx + (a.reverse ? (a.n_items - 1) * E : 0));
+  const int64_t step4 = step / 4;
+  if (e > a.dv) {  // padding column: zero prefixes, stored only where no delta was written
+    for (int64_t i = a.n_terms; i < a.n_items; ++i) st[i * step4] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  float4 run = scan_init4(a.S0, a.z0, h, a.F, a.dv, f, e);
+  constexpr int kBatch = 16;
+  for (int64_t i0 = 0; i0 < a.n_items; i0 += kBatch) {
+    float4 d[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+      d[b] = (i0 + b < a.n_terms) ? st[(i0 + b) * step4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (i0 + b < a.n_items && (!a.total_only || i0 + b == a.n_items - 1)) st[(i0 + b) * step4] = run;
+      run = add4(run, d[b]);
+    }
+  }
+  scan_out4(a.S_out, a.z_out, h, a.F, a.dv, f, e, run);
+}
+
 // dS_c[f][e] = sum_{j in chunk} phik[j][f] * vx[j][e], with vx = [v | 1].
 // Each thread owns a 4 (f) x 4 (e) block of the (F, dv+1) state.
 template <typename TV>
@@ -324,36 +388,41 @@ hipError_t launch_generic_nc_t(const ChunkedArgs& a, hipStream_t s) {
 // whole segments first[s] .. +nfull[s], then its tail item, if any) of head h,
 // from S0 of (s, h); the total goes to S_out.  States are fragment ordered
 // (layout 1); S0/S_out are [n_seqs][H][F][dv].
+// One 16-byte vector (features f .. f+3 of one column) per thread; the
+// padding columns are zero in every delta item, and so in every prefix.
 __global__ __launch_bounds__(kGThreads) void vl_scan_kernel(float* states, int64_t H, int g_max, const int* first,
                                                             const int* nfull, const int* tail, int F, int dv,
                                                             const float* S0, const float* z0, float* S_out,
                                                             float* z_out, int64_t E) {
   const int64_t sh = blockIdx.y;  // s * H + h
   const int64_t h = sh % H, sq = sh / H;
-  const int64_t idx = (int64_t)blockIdx.x * kGThreads + threadIdx.x;
+  const int64_t idx = ((int64_t)blockIdx.x * kGThreads + threadIdx.x) * 4;
   if (idx >= E) return;
   int f, e;
   scan_map(idx, F, dv, 1, f, e);
-  float run = 0.f;
-  if (e < dv) {
-    if (S0) run = S0[(sh * F + f) * dv + e];
-  } else if (e == dv) {
-    if (z0) run = z0[sh * F + f];
+  if (e > dv) return;
+  float4 run = scan_init4(S0, z0, sh, F, dv, f, e);
+  float4* base = reinterpret_cast<float4*>(states + h * g_max * E + idx);
+  const int64_t E4 = E / 4;
+  const int n = nfull[sq], t = tail[sq], i0 = first[sq];
+  const int n_items = n + (t >= 0 ? 1 : 0);
+  // the loads of a batch of items are issued together, then the prefixes stored
+  constexpr int kBatch = 8;
+  for (int j0 = 0; j0 < n_items; j0 += kBatch) {
+    float4 d[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int j = j0 + b;
+      d[b] = j < n_items ? base[(int64_t)(j < n ? i0 + j : t) * E4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int j = j0 + b;
+      if (j < n_items) base[(int64_t)(j < n ? i0 + j : t) * E4] = run;
+      run = add4(run, d[b]);
+    }
   }
-  float* base = states + h * g_max * E + idx;
-  const int n = nfull[sq], t = tail[sq];
-  for (int j = 0; j <= n; ++j) {
-    const int64_t item = j < n ? first[sq] + j : t;
-    if (item < 0) break;  // no tail
-    const float d = base[item * E];
-    base[item * E] = run;
-    run += d;
-  }
-  if (e < dv) {
-    if (S_out) S_out[(sh * F + f) * dv + e] = run;
-  } else if (e == dv) {
-    if (z_out) z_out[sh * F + f] = run;
-  }
+  scan_out4(S_out, z_out, sh, F, dv, f, e, run);
 }
 
 hipError_t launch_chunk_state(const float* phik, const void* v, bool v_bf16, int64_t n_heads, int64_t L, int F,
@@ -375,7 +444,7 @@ hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, c
                               float* z_out, hipStream_t s) {
   const int64_t E = scan_state_elems(F, dv, 1);
   if (H == 0 || n_seqs == 0) return hipSuccess;
-  hipLaunchKernelGGL(vl_scan_kernel, dim3((unsigned)((E + kGThreads - 1) / kGThreads), (unsigned)(H * n_seqs)),
+  hipLaunchKernelGGL(vl_scan_kernel, dim3((unsigned)((E / 4 + kGThreads - 1) / kGThreads), (unsigned)(H * n_seqs)),
                      dim3(kGThreads), 0, s, states, H, g_max, first, nfull, tail, F, dv, S0, z0, S_out, z_out, E);
   return hipGetLastError();
 }
@@ -387,6 +456,11 @@ int64_t scan_state_elems(int F, int dv, int layout) {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   const int64_t E = scan_state_elems(a.F, a.dv, a.layout);
   if (a.n_heads == 0 || E == 0) return hipSuccess;
+  if (a.layout == 1) {  // E = F (dv + 16) is a multiple of 64: whole 16-byte vectors
+    dim3 grid((unsigned)((E / 4 + kGThreads - 1) / kGThreads), (unsigned)a.n_heads);
+    hipLaunchKernelGGL(scan4_kernel, grid, dim3(kGThreads), 0, s, a, E);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((E + kGThreads - 1) / kGThreads), (unsigned)a.n_heads);
   hipLaunchKernelGGL(scan_kernel, grid, dim3(kGThreads), 0, s, a, E);
   return hipGetLastError();
