@@ -168,9 +168,11 @@ size_t slay_attn_varlen_fwd_workspace_size(const slay_params_t* params, int32_t 
  *   workspace  : device scratch of slay_attn_varlen_fwd_workspace_size() bytes.
  * Supported: bf16, d = dv = 64, R*m <= 256 with m a multiple of 32 (the
  * fused MFMA kernels; R*m below 256 on features zero-padded to 256, which
- * changes no result; other shapes return SLAY_E_UNSUPPORTED).  One launch each of a
+ * changes no result; other shapes return SLAY_E_UNSUPPORTED), total_tokens
+ * below 2^31 - 64 (else SLAY_E_UNSUPPORTED).  One launch each of a
  * work-list kernel, the segment-state pass, the per-sequence scan and the
- * main pass, whatever the number of sequences. */
+ * main pass, whatever the number of sequences; the tails of several short
+ * sequences share one workgroup. */
 slay_status_t slay_attn_varlen_fwd(const slay_params_t* params, const void* q, const void* k, const void* v,
                                    slay_dtype_t io_dtype, int32_t n_seqs, int32_t H, const int64_t* cu_seqlens,
                                    int64_t total_tokens, int32_t dv, const float* S0, const float* z0, void* o,

@@ -488,9 +488,10 @@ slay_status_t slay_attn_varlen_fwd(const slay_params_t* params, const void* q, c
   if (io_dtype != SLAY_F32 && io_dtype != SLAY_BF16) return fail(SLAY_E_INVALID, "bad io dtype");
   if (io_dtype != params->draw_dtype) return fail(SLAY_E_UNSUPPORTED, "io dtype must equal the draw dtype");
   const int F = params->R * params->m;
-  if (!mul_ok(H, total_tokens) || !mul_ok((int64_t)H * total_tokens, std::max<int64_t>(params->d, dv)) ||
-      total_tokens > (int64_t)INT32_MAX * 64)
+  if (!mul_ok(H, total_tokens) || !mul_ok((int64_t)H * total_tokens, std::max<int64_t>(params->d, dv)))
     return fail(SLAY_E_INVALID, "problem size overflows");
+  if (total_tokens > (int64_t)INT32_MAX - 64)  // the work list holds token rows as 32-bit integers
+    return fail(SLAY_E_UNSUPPORTED, "total_tokens = %lld exceeds 2^31 - 65", (long long)total_tokens);
   slay::VarlenArgs a{};
   a.c = chunked_args(params, q, k, v, io_dtype, 1, H, total_tokens, dv, 64);
   a.n_seqs = n_seqs;

@@ -100,57 +100,132 @@ struct Params {
   const float* z0;
   float* S_out;
   float* z_out;
-  // Variable-length batches (vl_tab non-null): the packed token axis of each
-  // head holds sequences s at tokens cu[s] .. cu[s+1] (T tokens per head).
-  // Workgroup w takes work item g = w / n_heads of head w % n_heads (so the
-  // heads' items of one g run side by side): segment vl_tab[2g+1] of sequence
-  // vl_tab[2g], owning state item g of the head; items g >= *vl_count exit.
-  const int* vl_tab;
+  // Variable-length batches: the packed token axis of each head holds
+  // sequences s at tokens cu[s] .. cu[s+1] (T tokens per head).  Workgroup w
+  // takes work item g = w / n_heads of head w % n_heads (so the heads' items
+  // of one g run side by side).  The main pass has vl_count[0] items, the
+  // segment-state pass the first vl_count[1] of them: the whole segments that
+  // another segment of their sequence follows.  vl_item[g] = (chunks of 32
+  // tokens, chunks of 64, a, b): a whole segment (b < 0) of sequence -1 - b
+  // starting at row a of the head's packed axis, owning state slot g (the
+  // last piece of its sequence when g >= vl_count[1]); or a pack of sequence
+  // tails walked one after another (b >= 0) whose chunk descriptors start at
+  // vl_list32[a]: (row of the chunk's first token in the packed axis, tokens,
+  // state slot, kFirst | kLast | kSeqEnd | sequence << 3).  A pack walks at
+  // most vl_cap chunks.
   const int* vl_count;
+  const int4* vl_item;
+  const int4* vl_list32;
+  int vl_cap;
   const int64_t* cu;
   int64_t T;
   int g_max;         // work items per head
   int64_t n_heads;
 };
 
-// Where a workgroup's tokens lie: the packed row of its sequence's token 0,
-// its token range in the sequence and its state item.
+// Where a dense workgroup's tokens lie: the packed row of the head's token 0,
+// its token range and its state item.
 struct Geo {
   int64_t head;
   int64_t row0;
   int64_t t0, t1;
   int64_t item;
   int seg;
-  bool valid;
 };
 
-// per_head: work items per head of a dense launch; items_per_head: state
-// items per head in the workspace (dense).
+// per_head: work items per head; items_per_head: state items per head in the
+// workspace.
 __device__ __forceinline__ Geo geo_of(const Params& p, int per_head, int64_t seg_len, int64_t items_per_head) {
   Geo g;
   const int64_t w = blockIdx.x;
-  if (!p.vl_tab) {
-    g.head = w / per_head;
-    g.seg = (int)(w - g.head * per_head);
-    g.row0 = g.head * p.L;
-    g.t0 = (int64_t)g.seg * seg_len;
-    g.t1 = min<int64_t>(p.L, g.t0 + seg_len);
-    g.item = g.head * items_per_head + g.seg;
-    g.valid = true;
-  } else {
-    const int64_t nh = p.n_heads;
-    const int gi = (int)(w / nh);
-    g.head = w - (int64_t)gi * nh;
-    g.valid = gi < *p.vl_count;
-    const int sq = g.valid ? p.vl_tab[2 * gi] : 0;
-    g.seg = g.valid ? p.vl_tab[2 * gi + 1] : 0;
-    const int64_t b = p.cu[sq], e = p.cu[sq + 1];
-    g.row0 = g.head * p.T + b;
-    g.t0 = (int64_t)g.seg * seg_len;
-    g.t1 = min<int64_t>(e - b, g.t0 + seg_len);
-    g.item = g.head * p.g_max + gi;
-  }
+  g.head = w / per_head;
+  g.seg = (int)(w - g.head * per_head);
+  g.row0 = g.head * p.L;
+  g.t0 = (int64_t)g.seg * seg_len;
+  g.t1 = min<int64_t>(p.L, g.t0 + seg_len);
+  g.item = g.head * items_per_head + g.seg;
   return g;
+}
+
+// chunk flags: first / last chunk of its piece; the piece ends its sequence
+constexpr int kFirst = 1, kLast = 2, kSeqEnd = 4;
+
+// One chunk of a workgroup's walk.
+struct ChunkRef {
+  int64_t row;   // packed row of the chunk's first token
+  int n;         // tokens in the chunk (1 .. C)
+  int64_t item;  // state item of the chunk's piece
+  int flags;     // kFirst, kLast, kSeqEnd
+  int seq;       // variable-length: the piece's sequence
+};
+
+// The chunks a workgroup walks.  Dense (VL false): the whole chunks of one
+// (head, segment), a single piece.  Variable-length: a whole segment of one
+// sequence (one piece, whole chunks), or (main pass only) a pack of sequence
+// tails, one piece each, whose chunk descriptors every thread of the
+// workgroup copies to LDS before the workgroup's first barrier.
+template <class K, bool VL>
+struct Chunks {
+  int64_t head;
+  int nch;
+  bool valid;
+  Geo geo;            // dense, and a variable-length whole segment (row0, item)
+  bool pack;          // VL: a pack of tails
+  bool seq_end;       // VL whole segment: the last piece of its sequence
+  int seq;            // VL whole segment: its sequence
+  const int4* list;   // VL pack: descriptors in LDS
+  int64_t head_row, head_item;
+  __device__ __forceinline__ ChunkRef at(int c) const {
+    if (VL && pack) {  // the same descriptor in every lane: kept in scalar registers
+      const int4 e = list[c];
+      const int w = __builtin_amdgcn_readfirstlane(e.w);
+      return {head_row + __builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y),
+              head_item + __builtin_amdgcn_readfirstlane(e.z), w & 7, w >> 3};
+    }
+    const int64_t c0 = geo.t0 + (int64_t)c * K::C;
+    const bool last = c == nch - 1;
+    return {geo.row0 + c0, (int)min<int64_t>(K::C, geo.t1 - c0), geo.item,
+            (c == 0 ? kFirst : 0) | (last ? kLast : 0) | (last && seq_end ? kSeqEnd : 0), seq};
+  }
+};
+
+// per_head, seg_len, items_per_head as for geo_of (dense only); sl: LDS room
+// for vl_cap chunk descriptors (VL only); nt: threads of the workgroup.
+template <class K, bool VL>
+__device__ __forceinline__ Chunks<K, VL> chunks_of(const Params& p, int per_head, int64_t seg_len,
+                                                   int64_t items_per_head, int4* sl, int nt) {
+  Chunks<K, VL> c{};
+  if constexpr (VL) {
+    const int64_t nh = p.n_heads;
+    const int gi = (int)(blockIdx.x / nh);
+    c.head = blockIdx.x - (int64_t)gi * nh;
+    const int n_pass1 = p.vl_count[1];
+    c.valid = gi < (K::C == 64 ? n_pass1 : p.vl_count[0]);
+    if (!c.valid) return c;
+    const int4 info = p.vl_item[gi];
+    c.nch = K::C == 64 ? info.y : info.x;
+    c.head_row = c.head * p.T;
+    c.head_item = c.head * p.g_max;
+    c.pack = K::C != 64 && info.w >= 0;  // the segment-state pass sees whole segments only
+    if (c.pack) {
+      const int4* src = p.vl_list32 + info.z;
+      for (int t = threadIdx.x; t < c.nch; t += nt) sl[t] = src[t];
+      c.list = sl;
+    } else {
+      c.geo.row0 = c.head_row + info.z;
+      c.geo.t0 = 0;
+      c.geo.t1 = p.seg_len;
+      c.geo.item = c.head_item + gi;
+      c.seq = -1 - info.w;
+      c.seq_end = gi >= n_pass1;
+    }
+  } else {
+    c.geo = geo_of(p, per_head, seg_len, items_per_head);
+    c.head = c.geo.head;
+    c.valid = true;
+    c.nch = (int)((c.geo.t1 - c.geo.t0 + K::C - 1) / K::C);
+  }
+  return c;
 }
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
@@ -571,12 +646,14 @@ template <class K>
 __device__ __forceinline__ void load_state_item(const Params& p, int64_t head, bool from_ws, int64_t item, int fb0,
                                                 int lane, f32x4 (&st)[K::FBW][K::NE]) {
   const int g = lane >> 4, col = lane & 15;
-  if (from_ws) {
-    const float* in = p.ws + item * (int64_t)K::F * K::DVP;
+  if (from_ws) {  // a wave-uniform base plus one 32-bit lane offset
+    const float* in = p.ws + item * (int64_t)K::F * K::DVP + frag_off<K>(fb0, 0, 0);
+    const uint32_t off = (uint32_t)lane * 4;
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
-      for (int et = 0; et < K::NE; ++et) st[j][et] = *reinterpret_cast<const f32x4*>(in + frag_off<K>(fb0 + j, et, lane));
+      for (int et = 0; et < K::NE; ++et)
+        st[j][et] = *reinterpret_cast<const f32x4*>(in + (j * K::NE + et) * 256 + off);
   } else {
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j)
@@ -606,26 +683,33 @@ __device__ __forceinline__ void load_state(const Params& p, int64_t head, int se
   load_state_item<K>(p, head, p.n_seg > 1, head * p.p1_items + (int64_t)seg * p.sub, fb0, lane, st);
 }
 
-// Final state of the head (last segment only) for the wave's feature blocks.
+// Final state of state row `head` (a head; for a variable-length batch,
+// sequence * n_heads + head) for the wave's feature blocks.
 template <class K>
+// Addresses are a wave-uniform base plus one 32-bit lane offset, so the
+// stores add few live registers where they sit inside a chunk loop.
 __device__ __forceinline__ void store_state_out(const Params& p, int64_t head, int fb0, int lane,
                                                 const f32x4 (&st)[K::FBW][K::NE]) {
   const int g = lane >> 4, col = lane & 15;
+  const int64_t row0 = head * K::F + fb0 * 16;  // first feature row of the wave
+  if (p.S_out) {
+    float* base = p.S_out + row0 * K::DV;
+    const uint32_t off = (uint32_t)(4 * g * K::DV + col);
 #pragma unroll
-  for (int j = 0; j < K::FBW; ++j)
+    for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
-    for (int et = 0; et < K::NE; ++et) {
-      const int e = et * 16 + col;
+      for (int et = 0; et < K::NE - 1; ++et)  // tile NE-1 holds z and padding
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = (fb0 + j) * 16 + 4 * g + i;
-        if (e < K::DV) {
-          if (p.S_out) p.S_out[(head * K::F + f) * K::DV + e] = st[j][et][i];
-        } else if (e == K::DV) {
-          if (p.z_out) p.z_out[head * K::F + f] = st[j][et][i];
-        }
-      }
-    }
+        for (int i = 0; i < 4; ++i) base[(j * 16 + i) * K::DV + et * 16 + off] = st[j][et][i];
+  }
+  if (p.z_out && col == 0) {
+    float* base = p.z_out + row0;
+    const uint32_t off = (uint32_t)(4 * g);
+#pragma unroll
+    for (int j = 0; j < K::FBW; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base[j * 16 + i + off] = st[j][K::NE - 1][i];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -722,7 +806,7 @@ __global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
 // phi(k) and the state update.  Same buffers and one barrier per chunk as
 // pass1_kernel: in the interval of chunk c the stagers write chunk c+1 and
 // load chunk c+2 while the feature waves process chunk c.
-template <class K>
+template <class K, bool VL>
 __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
   constexpr int NS = 256;  // stager threads
   extern __shared__ __align__(16) unsigned char lds[];
@@ -732,12 +816,13 @@ __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Geo geo = geo_of(p, p.p1_segs, p.seg_len / p.sub, p.p1_items);
-  if (!geo.valid) return;  // a variable-length launch's spare work item (whole workgroup)
-  const int64_t head = geo.head;
+  const Chunks<K, VL> ch = chunks_of<K, VL>(p, p.p1_segs, p.seg_len / p.sub, p.p1_items,
+                                            reinterpret_cast<int4*>(lds + K::kLds1), K::NT + NS);
+  if (!ch.valid) return;  // a variable-length launch's spare work item (whole workgroup)
+  if constexpr (VL) __syncthreads();  // chunk list in LDS
+  const int64_t head = ch.head;
   const int set = (int)(head % p.n_draw_sets);
-  const int64_t t0 = geo.t0, t1 = geo.t1;
-  const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
+  const int nch = ch.nch;
 
   for (int t = threadIdx.x; t < K::DV * K::LDV / 2; t += K::NT + NS) reinterpret_cast<uint32_t*>(sV(2))[t] = 0u;
   for (int b = 0; b < 3; ++b) init_vconst<K, K::NT + NS>(threadIdx.x, sV(b));
@@ -776,7 +861,8 @@ __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
 #pragma unroll
       for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sv_last, vo, lane, s_, kfb, st);
     }
-    float* out = p.ws + geo.item * (int64_t)K::F * K::DVP;
+    // one piece per workgroup (variable-length packs never come here)
+    float* out = p.ws + ch.at(0).item * (int64_t)K::F * K::DVP;
 #pragma unroll
     for (int j = 0; j < K::FBW; ++j)
 #pragma unroll
@@ -786,8 +872,8 @@ __global__ __launch_bounds__(K::NT + 256) void pass1s_kernel(Params p) {
     const int stid = threadIdx.x - K::NT;
     Prefetch<K, NS> pf;
     auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
-      const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-      issue_loads<K, NS>(stid, p, geo.row0, c2, (int)min<int64_t>(K::C, t1 - c2), false, pf);
+      const ChunkRef r = ch.at(min(cc, nch - 1));
+      issue_loads<K, NS>(stid, p, r.row, 0, r.n, false, pf);
     };
     load_chunk(0);
     store_x<K, NS>(stid, pf.k, sK(0), sInv(0), sInv(0) + K::C);
@@ -912,7 +998,7 @@ __device__ __forceinline__ void consumer_step(const Params& p, int64_t row0, int
   }
 }
 
-template <class K>
+template <class K, bool VL>
 __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char lds[];
   auto sQ = [&](int b) { return reinterpret_cast<uint16_t*>(lds + K::kSQ + b * K::kXt); };
@@ -930,10 +1016,11 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
   const bool producer = wave < K::NP;
   const int cw = wave - K::NP;           // consumer index: token block cw >> 1, column half cw & 1
   const int ctid = threadIdx.x - K::NP * 64;  // thread index among the consumers
-  const Geo geo = geo_of(p, p.n_seg, p.seg_len, p.p1_items);
-  if (!geo.valid) return;  // a variable-length launch's spare work item (whole workgroup)
-  const int64_t head = geo.head;
-  const int seg = geo.seg;
+  const Chunks<K, VL> ch = chunks_of<K, VL>(p, p.n_seg, p.seg_len, p.p1_items,
+                                            reinterpret_cast<int4*>(lds + K::kLdsS), K::NTW);
+  if (!ch.valid) return;  // a variable-length launch's spare work item (whole workgroup)
+  if constexpr (VL) __syncthreads();  // chunk list in LDS
+  const int64_t head = ch.head;
   const int set = (int)(head % p.n_draw_sets);
   const int fb0 = (producer ? wave : 0) * K::FBW;
 
@@ -941,8 +1028,7 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
   const RowOff<K, K::LDF> so(col);
   for (int b = 0; b < 3; ++b) init_vconst<K, K::NTW>(threadIdx.x, sV(b));
   for (int t = threadIdx.x; t < K::LDF; t += K::NTW) sSt[(K::DV + 1) * K::LDF + t] = 0;
-  const int64_t t0 = geo.t0, t1 = geo.t1;
-  const int nch = (int)((t1 - t0 + K::C - 1) / K::C);
+  const int nch = ch.nch;
 
   // Producers and consumers run separate code (so each keeps only its own
   // registers live); both execute the same barriers: two in the prologue and
@@ -953,31 +1039,46 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
     f32x4 st[K::FBW][K::NE];
     bf16x8 kf[K::FBW][K::NTS] = {};
     load_p<K>(p, set, fb0, lane, pa, pg, c1, c0);
-    load_state_item<K>(p, head, p.vl_tab || p.n_seg > 1, geo.item, fb0, lane, st);
+    load_state_item<K>(p, head, VL || p.n_seg > 1, ch.at(0).item, fb0, lane, st);
     write_st<K>(sSt, so, wave, lane, st);
     __syncthreads();  // chunks 0 and 1 staged
     phase_k<K, true, false>(sK(0), sInv(0, 2), sInv(0, 3), sPk(0), fb0, lane, pa, pg, c1, c0, kf, nullptr, vo, kf, st);
     phase_q<K>(sQ(0), sInv(0, 0), sInv(0, 1), sPq(0), wave, lane, pa, pg, c1, c0);
     __syncthreads();  // phi of chunk 0 in LDS
-    for (int c = 0; c < nch; ++c) {
-      const int bn = (c & 1) ^ 1;
-      const uint16_t* sVc = sV(c % 3);
-      // ---- [A] phi of chunk c+1, state update by chunk c ----
-      if (c + 1 < nch) {
-        phase_k<K, true, true>(sK(bn), sInv(bn, 2), sInv(bn, 3), sPk(bn), fb0, lane, pa, pg, c1, c0, kf, sVc, vo, kf,
-                               st);
-        phase_q<K>(sQ(bn), sInv(bn, 0), sInv(bn, 1), sPq(bn), wave, lane, pa, pg, c1, c0);
-        mfma_valu_interleave<K::NTB * K::FBW * K::NKS * 4 + K::NTS * K::NE * K::FBW, 4>();
-      } else {  // last chunk: its state update only
-#pragma unroll
-        for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sVc, vo, lane, s_, kf, st);
-      }
+    // ---- [B] S'^T copy of the state before chunk c+1: the state after
+    // chunk c, or (variable-length) a new piece's initial state from the scan ----
+    auto interval_b = [&](int c) {
       __syncthreads();  // B
-      // ---- [B] S'^T copy of the state after chunk c ----
+      if constexpr (VL) {
+        const ChunkRef r = ch.at(c);  // the state after a sequence's last chunk is its final state
+        if ((r.flags & kSeqEnd) && (p.S_out || p.z_out))
+          store_state_out<K>(p, (int64_t)r.seq * p.n_heads + head, fb0, lane, st);
+        if (c + 1 < nch) {
+          const ChunkRef r1 = ch.at(c + 1);
+          if (r1.flags & kFirst) load_state_item<K>(p, head, true, r1.item, fb0, lane, st);
+        }
+      }
       write_st<K>(sSt, so, wave, lane, st);
       __syncthreads();  // A
+    };
+    // the last chunk is peeled off, so the loop body holds no branch that
+    // writes the state accumulators two ways
+    for (int c = 0; c < nch - 1; ++c) {
+      const int bn = (c & 1) ^ 1;
+      // ---- [A] phi of chunk c+1, state update by chunk c ----
+      phase_k<K, true, true>(sK(bn), sInv(bn, 2), sInv(bn, 3), sPk(bn), fb0, lane, pa, pg, c1, c0, kf, sV(c % 3), vo,
+                             kf, st);
+      phase_q<K>(sQ(bn), sInv(bn, 0), sInv(bn, 1), sPq(bn), wave, lane, pa, pg, c1, c0);
+      mfma_valu_interleave<K::NTB * K::FBW * K::NKS * 4 + K::NTS * K::NE * K::FBW, 4>();
+      interval_b(c);
     }
-    if (!p.vl_tab && seg == p.n_seg - 1 && (p.S_out || p.z_out)) store_state_out<K>(p, head, fb0, lane, st);
+    {  // [A] of the last chunk: its state update only
+      const uint16_t* sVc = sV((nch - 1) % 3);
+#pragma unroll
+      for (int s_ = 0; s_ < K::NTS; ++s_) state_update_step<K>(sVc, vo, lane, s_, kf, st);
+      interval_b(nch - 1);
+    }
+    if (!VL && ch.geo.seg == p.n_seg - 1 && (p.S_out || p.z_out)) store_state_out<K>(p, head, fb0, lane, st);
   } else {
     // The SIMD issues from the highest-priority ready wave first: consumers
     // (MFMA and LDS, little VALU) go ahead of the VALU-heavy producers, which
@@ -985,8 +1086,8 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
     __builtin_amdgcn_s_setprio(2);
     Prefetch<K, K::NC * 64> pf;
     auto load_chunk = [&](int cc) {  // chunk min(cc, nch-1): the last one again past the end
-      const int64_t c2 = t0 + (int64_t)min(cc, nch - 1) * K::C;
-      issue_loads<K, K::NC * 64>(ctid, p, geo.row0, c2, (int)min<int64_t>(K::C, t1 - c2), true, pf);
+      const ChunkRef r = ch.at(min(cc, nch - 1));
+      issue_loads<K, K::NC * 64>(ctid, p, r.row, 0, r.n, true, pf);
     };
     auto stage = [&](int bx, int bv) {
       store_x<K, K::NC * 64>(ctid, pf.q, sQ(bx), sInv(bx, 0), sInv(bx, 1));
@@ -1006,8 +1107,9 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
       constexpr int IB = decltype(ib_c)::value, H = decltype(h_c)::value;
       for (int c = 0; c < nch; ++c) {
         const int b = c & 1;
-        const int64_t row0 = geo.row0 + t0 + (int64_t)c * K::C;
-        const int n = (int)min<int64_t>(K::C, t1 - (t0 + (int64_t)c * K::C));
+        const ChunkRef r = ch.at(c);
+        const int64_t row0 = r.row;
+        const int n = r.n;
         f32x4 acc0[K::ESPLIT];
         // ---- [A] contractions of chunk c; staging of chunk c+2 ----
         consumer_step<K, IB, H>(p, row0, n, sPq(b), sPk(b), sV(c % 3), sSt, sDen, vo, so, lane, acc0);
@@ -1226,9 +1328,9 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
   hipError_t e;
   if (n_seg > 1) {
     if constexpr (K::STAGERS1) {
-      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K>), K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K, false>), K::kLds1);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * (n_seg - 1) * kSub)), dim3(K::NT + 256),
+      hipLaunchKernelGGL((pass1s_kernel<K, false>), dim3((unsigned)(a.n_heads * (n_seg - 1) * kSub)), dim3(K::NT + 256),
                          K::kLds1, s, p);
     } else {
       constexpr int FS = K::FS1;
@@ -1255,9 +1357,10 @@ hipError_t launch_t(const ChunkedArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   using KS = typename MainPass<K>::type;
-  e = set_max_lds(reinterpret_cast<const void*>(&pass2s_kernel<KS>), KS::kLdsS);
+  e = set_max_lds(reinterpret_cast<const void*>(&pass2s_kernel<KS, false>), KS::kLdsS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pass2s_kernel<KS>, dim3((unsigned)(a.n_heads * n_seg)), dim3(KS::NTW), KS::kLdsS, s, p);
+  hipLaunchKernelGGL((pass2s_kernel<KS, false>), dim3((unsigned)(a.n_heads * n_seg)), dim3(KS::NTW), KS::kLdsS, s,
+                     p);
   return hipGetLastError();
 }
 
@@ -1320,9 +1423,9 @@ hipError_t launch_nc_t(const ChunkedArgs& a, hipStream_t s) {
     p.p1_segs = n_seg * kSub;
     p.p1_items = p.p1_segs + 1;
     if constexpr (K::STAGERS1) {
-      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K>), K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K, false>), K::kLds1);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT + 256), K::kLds1, s,
+      hipLaunchKernelGGL((pass1s_kernel<K, false>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT + 256), K::kLds1, s,
                          p);
     } else {
       e = set_max_lds(reinterpret_cast<const void*>(&pass1_kernel<K, 1>), K::kLds1);
@@ -1385,9 +1488,9 @@ hipError_t segment_prefix_t(const ChunkedArgs& a, float* ws, hipStream_t s) {
   hipError_t e;
   if (n_seg > 1) {
     if constexpr (K::STAGERS1) {
-      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K>), K::kLds1);
+      e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K, false>), K::kLds1);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((pass1s_kernel<K>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT + 256), K::kLds1, s,
+      hipLaunchKernelGGL((pass1s_kernel<K, false>), dim3((unsigned)(a.n_heads * p.p1_segs)), dim3(K::NT + 256), K::kLds1, s,
                          p);
     } else {
       e = set_max_lds(reinterpret_cast<const void*>(&pass1_kernel<K, 1>), K::kLds1);
@@ -1416,104 +1519,168 @@ hipError_t segment_prefix_t(const ChunkedArgs& a, float* ws, hipStream_t s) {
 // Variable-length batches (F = 256 configuration).
 namespace {
 
-// Work list (one workgroup).  The whole segments of every sequence come
-// first (so they start together), then the sequences' shorter tails, which
-// fill the compute units the whole segments leave free.  Per sequence: its
-// first whole-segment item, the number of whole segments and the tail's item
-// (-1 if none); per item: (sequence, segment).  Offsets that do not rise from
-// 0 to T without decreasing give no work items.
+// Work list (one workgroup of 256 threads).  A sequence of len tokens is cut
+// into len / seg_len whole segments and a shorter tail; its last piece (the
+// tail, or else its last whole segment) needs no segment state, because no
+// later piece of the sequence starts from it: the main pass ends that piece
+// with the sequence's final state.  State slots, in order: the whole segments
+// that another piece follows (A: the segment-state pass covers them), the
+// whole segments that end their sequence (B), the tails (C).  Main-pass work
+// items: one per whole segment (item g owns slot g), then packs of
+// consecutive tails whose lengths rounded up to 32 tokens sum to at most
+// seg_len, walked one after another by one workgroup, so the tails of short
+// sequences do not each take a compute unit.  Threads own blocks of at least
+// 32 consecutive sequences and pack within their block.  Outputs: per
+// sequence its first A slot, its A count and the slot of its last piece (-1
+// if it is empty), for the scan; per item the descriptor of Params::vl_item;
+// the packs' chunk descriptors; the item counts of both passes.  Offsets
+// that do not rise from 0 to T without decreasing give no items.
 __global__ __launch_bounds__(256) void vl_setup_kernel(const int64_t* __restrict__ cu, int n_seqs, int64_t T,
-                                                       int64_t seg_len, int g_max, int* __restrict__ tab,
-                                                       int* __restrict__ first, int* __restrict__ nfull,
-                                                       int* __restrict__ tail, int* __restrict__ count) {
-  __shared__ int pf[256], pt[256];
-  __shared__ int bad, n_full_all;
+                                                       int64_t seg_len, int g_max, int* __restrict__ first,
+                                                       int* __restrict__ n_a, int* __restrict__ last,
+                                                       int* __restrict__ count, int4* __restrict__ item,
+                                                       int4* __restrict__ list32) {
+  constexpr int NV = 5;  // per-thread counts: slots A, B, C, packs, pack chunks
+  __shared__ int part[4][NV];
+  __shared__ int bad;
   const int tid = threadIdx.x;
-  const int per = (n_seqs + 255) / 256;
+  const int per = max(32, (n_seqs + 255) / 256);
   const int s0 = min(n_seqs, tid * per), s1 = min(n_seqs, s0 + per);
   // every thread's offsets are read in one round trip with the end checks
   const bool ends_bad = tid == 0 && (cu[0] != 0 || cu[n_seqs] != T);
-  int lf = 0, lt = 0, lbad = ends_bad ? 1 : 0;
-  for (int sq = s0; sq < s1; ++sq) {
-    const int64_t len = cu[sq + 1] - cu[sq];
-    lbad |= len < 0;
-    const int64_t l = max<int64_t>(len, 0);
-    lf += (int)(l / seg_len);
-    lt += (l % seg_len) != 0;
+  int v[NV] = {0, 0, 0, 0, 0};
+  int lbad = ends_bad ? 1 : 0;
+  {
+    int64_t fill = -1;  // tokens in this thread's open pack (-1: none)
+    for (int sq = s0; sq < s1; ++sq) {
+      const int64_t len = cu[sq + 1] - cu[sq];
+      lbad |= len < 0;
+      const int64_t l = max<int64_t>(len, 0);
+      const int nf = (int)(l / seg_len);
+      const int64_t r = l % seg_len;
+      if (r) {
+        v[0] += nf;
+        const int64_t pl = (r + 31) / 32 * 32;
+        if (fill < 0 || fill + pl > seg_len) {
+          ++v[3];
+          fill = 0;
+        }
+        fill += pl;
+        ++v[2];
+        v[4] += (int)((r + 31) / 32);
+      } else if (nf > 0) {
+        v[0] += nf - 1;
+        ++v[1];
+      }
+    }
   }
   if (tid == 0) bad = 0;
   __syncthreads();
   if (lbad) atomicOr(&bad, 1);
   // exclusive prefix of the per-thread counts: inclusive scan within each wave
   // (shuffles), then the four wave totals
-  int sf = lf, st = lt;
   const int lane = tid & 63, wv = tid >> 6;
+  int inc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) inc[i] = v[i];
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int uf = __shfl_up(sf, o, 64), ut = __shfl_up(st, o, 64);
-    if (lane >= o) {
-      sf += uf;
-      st += ut;
-    }
-  }
-  if (lane == 63) {
-    pf[wv] = sf;
-    pt[wv] = st;
-  }
-  __syncthreads();
-  int bf0 = 0, bt0 = 0, rf = 0, rt = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wv) {
-      bf0 += pf[w];
-      bt0 += pt[w];
+    for (int i = 0; i < NV; ++i) {
+      const int u = __shfl_up(inc[i], o, 64);
+      if (lane >= o) inc[i] += u;
     }
-    rf += pf[w];
-    rt += pt[w];
   }
-  __syncthreads();  // every wave has read the wave totals
-  if (tid == 0) {
-    if (rf + rt > g_max) bad = 1;
-    n_full_all = rf;
-    *count = bad ? 0 : rf + rt;
-  }
-  pf[tid] = bf0 + sf - lf;  // exclusive prefix of this thread
-  pt[tid] = bt0 + st - lt;
+  if (lane == 63)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) part[wv][i] = inc[i];
   __syncthreads();
-  const bool ok = bad == 0;
-  int bf = pf[tid], bt = n_full_all + pt[tid];
-  for (int sq = s0; sq < s1; ++sq) {
-    const int64_t len = ok ? cu[sq + 1] - cu[sq] : 0;
-    const int nf = (int)(len / seg_len);
-    const bool has_tail = (len % seg_len) != 0;
-    first[sq] = bf;
-    nfull[sq] = nf;
-    tail[sq] = has_tail ? bt : -1;
-    for (int j = 0; j < nf; ++j) {
-      tab[2 * (bf + j)] = sq;
-      tab[2 * (bf + j) + 1] = j;
+  int base[NV], tot[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    base[i] = inc[i] - v[i];
+    tot[i] = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w < wv) base[i] += part[w][i];
+      tot[i] += part[w][i];
     }
-    if (has_tail) {
-      tab[2 * bt] = sq;
-      tab[2 * bt + 1] = nf;
-      ++bt;
-    }
-    bf += nf;
   }
+  const int ra = tot[0], rb = tot[1], rc = tot[2], rp = tot[3];
+  if (tid == 0 && ra + rb + rc > g_max) atomicOr(&bad, 1);
+  __syncthreads();  // every wave has read the wave totals; bad is final
+  const bool ok = bad == 0;
+  if (tid == 0) {
+    count[0] = ok ? ra + rb + rp : 0;
+    count[1] = ok ? ra : 0;
+  }
+  if (!ok) {  // no pieces: the scan passes every sequence's initial state through
+    for (int sq = s0; sq < s1; ++sq) {
+      first[sq] = 0;
+      n_a[sq] = 0;
+      last[sq] = -1;
+    }
+    return;
+  }
+  const int S32 = (int)(seg_len / 32), S64 = (int)(seg_len / 64);
+  int slot_a = base[0], slot_b = ra + base[1], slot_c = ra + rb + base[2], pk = ra + rb + base[3];
+  int pos = base[4];
+  int open = -1, open0 = 0;  // this thread's open pack: item, first descriptor
+  int64_t fill = 0;
+  auto close = [&]() {
+    if (open >= 0) item[open] = make_int4(pos - open0, 0, open0, open0);
+  };
+  for (int sq = s0; sq < s1; ++sq) {
+    const int64_t c0 = cu[sq], len = cu[sq + 1] - c0;
+    const int nf = (int)(len / seg_len);
+    const int64_t r = len % seg_len;
+    const int na = r ? nf : max(nf - 1, 0);
+    first[sq] = slot_a;
+    n_a[sq] = na;
+    for (int j = 0; j < na; ++j) item[slot_a + j] = make_int4(S32, S64, (int)(c0 + j * seg_len), -1 - sq);
+    slot_a += na;
+    if (r) {
+      last[sq] = slot_c;
+      const int64_t pl = (r + 31) / 32 * 32;
+      if (open < 0 || fill + pl > seg_len) {
+        close();
+        open = pk++;
+        open0 = pos;
+        fill = 0;
+      }
+      fill += pl;
+      const int row = (int)(c0 + (int64_t)nf * seg_len);
+      const int n32 = (int)((r + 31) / 32);
+      for (int i = 0; i < n32; ++i)
+        list32[pos + i] = make_int4(row + 32 * i, (int)min<int64_t>(32, r - 32 * i), slot_c,
+                                    (i == 0 ? kFirst : 0) | (i == n32 - 1 ? kLast | kSeqEnd : 0) | (sq << 3));
+      pos += n32;
+      ++slot_c;
+    } else if (nf > 0) {
+      last[sq] = slot_b;
+      item[slot_b] = make_int4(S32, S64, (int)(c0 + (int64_t)na * seg_len), -1 - sq);
+      ++slot_b;
+    } else {
+      last[sq] = -1;
+    }
+  }
+  close();
 }
 
-// Tokens per work item: about 256 work items over the chip, a multiple of two chunks.
+// Tokens per work item: about 256 work items over the chip, a multiple of two
+// chunks, at most 8192 (so a pack's chunk descriptors take at most 4 KiB of LDS).
 int64_t vl_seg_len(int64_t H, int64_t T) {
   const int64_t want = (H * T + 255) / 256;
   const int64_t sl = ((want + 127) / 128) * 128;
-  return sl < 128 ? 128 : sl;
+  return sl < 128 ? 128 : (sl > 8192 ? 8192 : sl);
 }
 
 // Work items per head: every sequence adds at most one partial segment.
 int vl_g_max(int64_t T, int n_seqs, int64_t seg_len) { return (int)(T / seg_len + n_seqs); }
 
 struct VlWs {
-  int *tab, *first, *nfull, *tail, *count;
+  int *first, *n_a, *last, *count;
+  int4 *item, *list32;
   float* states;
   size_t bytes;
 };
@@ -1528,11 +1695,13 @@ VlWs vl_ws(const VarlenArgs& a, int g_max, void* base) {
     return q;
   };
   w.states = reinterpret_cast<float*>(take(sizeof(float) * (size_t)a.c.n_heads * g_max * CfgF256::F * CfgF256::DVP));
-  w.tab = reinterpret_cast<int*>(take(sizeof(int) * 2 * (size_t)g_max));
+  w.item = reinterpret_cast<int4*>(take(sizeof(int4) * (size_t)g_max));
+  // pack descriptors: every tail r takes ceil(r / 32) <= r / 32 + 1 of them
+  w.list32 = reinterpret_cast<int4*>(take(sizeof(int4) * (size_t)(a.c.L / 32 + a.n_seqs)));
   w.first = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
-  w.nfull = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
-  w.tail = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
-  w.count = reinterpret_cast<int*>(take(sizeof(int)));
+  w.n_a = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
+  w.last = reinterpret_cast<int*>(take(sizeof(int) * (size_t)a.n_seqs));
+  w.count = reinterpret_cast<int*>(take(2 * sizeof(int)));
   w.bytes = off;
   return w;
 }
@@ -1664,8 +1833,8 @@ hipError_t launch_varlen_exact(const VarlenArgs& a, hipStream_t s) {
   const int64_t seg_len = vl_seg_len(H, T);
   const int g_max = vl_g_max(T, a.n_seqs, seg_len);
   const VlWs w = vl_ws(a, g_max, a.c.ws);
-  hipLaunchKernelGGL(vl_setup_kernel, dim3(1), dim3(256), 0, s, a.cu, a.n_seqs, T, seg_len, g_max, w.tab, w.first,
-                     w.nfull, w.tail, w.count);
+  hipLaunchKernelGGL(vl_setup_kernel, dim3(1), dim3(256), 0, s, a.cu, a.n_seqs, T, seg_len, g_max, w.first,
+                     w.n_a, w.last, w.count, w.item, w.list32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   Params p{};
@@ -1687,26 +1856,31 @@ hipError_t launch_varlen_exact(const VarlenArgs& a, hipStream_t s) {
   p.n_draw_sets = a.c.n_draw_sets;
   p.nc = a.c.nc;
   p.ws = w.states;
-  p.vl_tab = w.tab;
   p.vl_count = w.count;
+  p.vl_item = w.item;
+  p.vl_list32 = w.list32;
+  p.vl_cap = (int)(seg_len / 32);
   p.cu = a.cu;
   p.T = T;
   p.g_max = g_max;
   p.n_heads = H;
   const unsigned grid = (unsigned)(H * g_max);
-  if (T > 0) {  // every segment's state (the last ones too: their sums are the final states)
-    e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K>), K::kLds1);
+  p.S_out = a.c.S_out;  // the main pass writes the final state of every non-empty sequence
+  p.z_out = a.c.z_out;
+  const int lds_list = (int)sizeof(int4) * p.vl_cap;  // a pack's chunk descriptors (main pass)
+  if (T > 0) {  // the states of the whole segments another piece follows
+    e = set_max_lds(reinterpret_cast<const void*>(&pass1s_kernel<K, true>), K::kLds1);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((pass1s_kernel<K>), dim3(grid), dim3(K::NT + 256), K::kLds1, s, p);
+    hipLaunchKernelGGL((pass1s_kernel<K, true>), dim3(grid), dim3(K::NT + 256), K::kLds1, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  e = launch_scan_varlen(w.states, H, a.n_seqs, g_max, w.first, w.nfull, w.tail, K::F, K::DV, a.c.S0, a.c.z0,
+  e = launch_scan_varlen(w.states, H, a.n_seqs, g_max, w.first, w.n_a, w.last, K::F, K::DV, a.c.S0, a.c.z0,
                          a.c.S_out, a.c.z_out, s);
   if (e != hipSuccess || T == 0) return e;
-  e = set_max_lds(reinterpret_cast<const void*>(&pass2s_kernel<KS>), KS::kLdsS);
+  e = set_max_lds(reinterpret_cast<const void*>(&pass2s_kernel<KS, true>), KS::kLdsS + lds_list);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pass2s_kernel<KS>, dim3(grid), dim3(KS::NTW), KS::kLdsS, s, p);
+  hipLaunchKernelGGL((pass2s_kernel<KS, true>), dim3(grid), dim3(KS::NTW), KS::kLdsS + lds_list, s, p);
   return hipGetLastError();
 }
 

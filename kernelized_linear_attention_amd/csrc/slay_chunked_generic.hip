@@ -384,14 +384,17 @@ hipError_t launch_generic_nc_t(const ChunkedArgs& a, hipStream_t s) {
 }  // namespace
 
 // Variable-length batches: per (sequence s, head h) and state element, the
-// exclusive prefix over the sequence's segment items in segment order (its
-// whole segments first[s] .. +nfull[s], then its tail item, if any) of head h,
-// from S0 of (s, h); the total goes to S_out.  States are fragment ordered
-// (layout 1); S0/S_out are [n_seqs][H][F][dv].
-// One 16-byte vector (features f .. f+3 of one column) per thread; the
-// padding columns are zero in every delta item, and so in every prefix.
+// exclusive prefixes from S0 of (s, h) over the state slots of the sequence's
+// pieces of head h, in order: n_a[s] whole segments from slot first[s] on,
+// whose deltas the segment-state pass wrote, then the slot of its last piece
+// last[s] (-1 for an empty sequence), which gets its prefix and contributes
+// no delta.  The main pass writes the final state of every non-empty
+// sequence; here only an empty one's (S0) goes to S_out.  States are fragment
+// ordered (layout 1); S0/S_out are [n_seqs][H][F][dv].  One 16-byte vector
+// (features f .. f+3 of one column) per thread; the padding columns are zero
+// in every delta, and so in every prefix.
 __global__ __launch_bounds__(kGThreads) void vl_scan_kernel(float* states, int64_t H, int g_max, const int* first,
-                                                            const int* nfull, const int* tail, int F, int dv,
+                                                            const int* n_a, const int* last, int F, int dv,
                                                             const float* S0, const float* z0, float* S_out,
                                                             float* z_out, int64_t E) {
   const int64_t sh = blockIdx.y;  // s * H + h
@@ -404,25 +407,24 @@ __global__ __launch_bounds__(kGThreads) void vl_scan_kernel(float* states, int64
   float4 run = scan_init4(S0, z0, sh, F, dv, f, e);
   float4* base = reinterpret_cast<float4*>(states + h * g_max * E + idx);
   const int64_t E4 = E / 4;
-  const int n = nfull[sq], t = tail[sq], i0 = first[sq];
-  const int n_items = n + (t >= 0 ? 1 : 0);
-  // the loads of a batch of items are issued together, then the prefixes stored
+  const int n = n_a[sq], i0 = first[sq], t = last[sq];
+  if (t < 0) {  // empty sequence: the state passes through
+    scan_out4(S_out, z_out, sh, F, dv, f, e, run);
+    return;
+  }
+  // the loads of a batch of deltas are issued together, then the prefixes stored
   constexpr int kBatch = 8;
-  for (int j0 = 0; j0 < n_items; j0 += kBatch) {
+  for (int j0 = 0; j0 < n; j0 += kBatch) {
     float4 d[kBatch];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int j = j0 + b;
-      d[b] = j < n_items ? base[(int64_t)(j < n ? i0 + j : t) * E4] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int b = 0; b < kBatch; ++b) d[b] = j0 + b < n ? base[(int64_t)(i0 + j0 + b) * E4] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      const int j = j0 + b;
-      if (j < n_items) base[(int64_t)(j < n ? i0 + j : t) * E4] = run;
+      if (j0 + b < n) base[(int64_t)(i0 + j0 + b) * E4] = run;
       run = add4(run, d[b]);
     }
   }
-  scan_out4(S_out, z_out, sh, F, dv, f, e, run);
+  base[(int64_t)t * E4] = run;
 }
 
 hipError_t launch_chunk_state(const float* phik, const void* v, bool v_bf16, int64_t n_heads, int64_t L, int F,
@@ -439,13 +441,13 @@ hipError_t launch_chunk_state(const float* phik, const void* v, bool v_bf16, int
   return hipGetLastError();
 }
 
-hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, const int* first, const int* nfull,
-                              const int* tail, int F, int dv, const float* S0, const float* z0, float* S_out,
+hipError_t launch_scan_varlen(float* states, int64_t H, int n_seqs, int g_max, const int* first, const int* n_a,
+                              const int* last, int F, int dv, const float* S0, const float* z0, float* S_out,
                               float* z_out, hipStream_t s) {
   const int64_t E = scan_state_elems(F, dv, 1);
   if (H == 0 || n_seqs == 0) return hipSuccess;
   hipLaunchKernelGGL(vl_scan_kernel, dim3((unsigned)((E / 4 + kGThreads - 1) / kGThreads), (unsigned)(H * n_seqs)),
-                     dim3(kGThreads), 0, s, states, H, g_max, first, nfull, tail, F, dv, S0, z0, S_out, z_out, E);
+                     dim3(kGThreads), 0, s, states, H, g_max, first, n_a, last, F, dv, S0, z0, S_out, z_out, E);
   return hipGetLastError();
 }
 

@@ -280,12 +280,15 @@ def test_varlen_validation_and_workspace(lib):
         assert _vl(lib, p, **{name: None}) == E_INV, name
         assert _vl(lib, p, **{name: FAKE + 4}) == E_INV, name
     assert _vl(lib, p) == E_INV and b"workspace too small" in lib.slay_last_error()
-    # one state per (head, work item), the work list (two ints per item), per-sequence first item,
-    # whole-segment count and tail item, and the item count
+    # one state per (head, state slot), one 16-byte descriptor per work item, the chunk
+    # descriptors of the tail packs (at most T / 32 + n_seqs), per-sequence first slot,
+    # slot count and last slot, and the item counts of the two passes
     n = lib.slay_attn_varlen_fwd_workspace_size(ctypes.byref(p), 4, 16, 16384, 64, _lib.SLAY_BF16)
     g_max = 16384 // 1024 + 4
     r = lambda b: (b + 255) // 256 * 256
-    assert n == r(4 * 16 * g_max * 256 * 80) + r(8 * g_max) + 3 * r(16) + r(4)
+    assert n == r(4 * 16 * g_max * 256 * 80) + r(16 * g_max) + r(16 * (16384 // 32 + 4)) + 3 * r(16) + r(8)
+    # more tokens than 2^31 - 65 per head are refused (the work list holds 32-bit token rows)
+    assert _vl(lib, p, T=2 ** 31) == E_UNS and b"exceeds" in lib.slay_last_error()
     assert _vl(lib, p, ws=FAKE, ws_bytes=n - 1) == E_INV
     # nothing to do
     assert _vl(lib, p, n=0) == _lib.SLAY_OK and _vl(lib, p, H=0) == _lib.SLAY_OK

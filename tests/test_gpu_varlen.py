@@ -73,6 +73,9 @@ def _run(lib, q, k, v, cu, A, G, S0=None, z0=None, out=None, w=W):
     (2, [300, 0, 1, 1000, 77, 2049, 128], True),   # empty, one-token, ragged and multi-segment sequences
     (3, [64, 64, 64], False),
     (1, [5000], True),
+    # 16 heads: segments of 1024 tokens; the tails 512, 256, 256 share one work item (a pack),
+    # and five sequences end with a whole segment that writes their final state
+    (16, [6144, 4096, 2048, 2048, 1024, 512, 256, 256], True),
 ])
 def test_varlen_parity(lib, orc, H, lengths, with_state):
     _say(f"varlen parity H={H} lengths={lengths} state={with_state}")
