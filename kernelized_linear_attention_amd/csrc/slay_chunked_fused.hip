@@ -1530,7 +1530,7 @@ namespace {
 // consecutive tails whose lengths rounded up to 32 tokens sum to at most
 // seg_len, walked one after another by one workgroup, so the tails of short
 // sequences do not each take a compute unit.  Threads own blocks of at least
-// 32 consecutive sequences and pack within their block.  Outputs: per
+// 4 consecutive sequences and pack within their block.  Outputs: per
 // sequence its first A slot, its A count and the slot of its last piece (-1
 // if it is empty), for the scan; per item the descriptor of Params::vl_item;
 // the packs' chunk descriptors; the item counts of both passes.  Offsets
@@ -1541,130 +1541,168 @@ __global__ __launch_bounds__(256) void vl_setup_kernel(const int64_t* __restrict
                                                        int* __restrict__ count, int4* __restrict__ item,
                                                        int4* __restrict__ list32) {
   constexpr int NV = 5;  // per-thread counts: slots A, B, C, packs, pack chunks
+  constexpr int kStage = 2048;  // offsets and tails of up to this many sequences are staged in LDS
   __shared__ int part[4][NV];
   __shared__ int bad;
+  __shared__ int64_t scu[kStage + 1];
+  __shared__ int4 stail[kStage];  // per tail: first descriptor, row, slot, sequence
   const int tid = threadIdx.x;
-  const int per = max(32, (n_seqs + 255) / 256);
+  const uint32_t sl = (uint32_t)seg_len;  // <= 8192
+  const int per = max(4, (n_seqs + 255) / 256);  // sequences per thread: the serial depth of the walk
   const int s0 = min(n_seqs, tid * per), s1 = min(n_seqs, s0 + per);
-  // every thread's offsets are read in one round trip with the end checks
-  const bool ends_bad = tid == 0 && (cu[0] != 0 || cu[n_seqs] != T);
-  int v[NV] = {0, 0, 0, 0, 0};
-  int lbad = ends_bad ? 1 : 0;
-  {
-    int64_t fill = -1;  // tokens in this thread's open pack (-1: none)
+  // The threads walk their sequences one after another; with the offsets in
+  // LDS (read by all threads together in one round trip) each step costs no
+  // memory round trip, and the tails' chunk descriptors are written after the
+  // walk by all threads together.  Larger batches read the offsets from
+  // memory and write the descriptors during the walk.
+  const bool staged = n_seqs <= kStage;
+  if (staged)
+    for (int i = tid; i <= n_seqs; i += 256) scu[i] = cu[i];
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  // the rest of the kernel, with the offsets read from LDS or from memory
+  // (one or the other at compile time: a pointer that may be either would
+  // make every read a flat access that waits for all stores in flight)
+  auto run = [&](auto staged_c) {
+    constexpr bool ST = decltype(staged_c)::value;
+    auto ofs_at = [&](int i) -> int64_t { return ST ? scu[i] : cu[i]; };
+    const bool ends_bad = tid == 0 && (ofs_at(0) != 0 || ofs_at(n_seqs) != T);
+    int v[NV] = {0, 0, 0, 0, 0};
+    int lbad = ends_bad ? 1 : 0;
+    {
+      int fill = -1;  // tokens in this thread's open pack (-1: none)
+      for (int sq = s0; sq < s1; ++sq) {
+        const int64_t len = ofs_at(sq + 1) - ofs_at(sq);
+        lbad |= len < 0;
+        const uint32_t l = (uint32_t)max<int64_t>(len, 0);  // T < 2^31: 32-bit arithmetic
+        const int nf = (int)(l / sl);
+        const int r = (int)(l - nf * sl);
+        if (r) {
+          v[0] += nf;
+          const int pl = (r + 31) / 32 * 32;
+          if (fill < 0 || fill + pl > (int)sl) {
+            ++v[3];
+            fill = 0;
+          }
+          fill += pl;
+          ++v[2];
+          v[4] += (r + 31) / 32;
+        } else if (nf > 0) {
+          v[0] += nf - 1;
+          ++v[1];
+        }
+      }
+    }
+    if (lbad) atomicOr(&bad, 1);
+    // exclusive prefix of the per-thread counts: inclusive scan within each wave
+    // (shuffles), then the four wave totals
+    const int lane = tid & 63, wv = tid >> 6;
+    int inc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) inc[i] = v[i];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int u = __shfl_up(inc[i], o, 64);
+        if (lane >= o) inc[i] += u;
+      }
+    }
+    if (lane == 63)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) part[wv][i] = inc[i];
+    __syncthreads();
+    int base[NV], tot[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      base[i] = inc[i] - v[i];
+      tot[i] = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (w < wv) base[i] += part[w][i];
+        tot[i] += part[w][i];
+      }
+    }
+    const int ra = tot[0], rb = tot[1], rc = tot[2], rp = tot[3];
+    if (tid == 0 && ra + rb + rc > g_max) atomicOr(&bad, 1);
+    __syncthreads();  // every wave has read the wave totals; bad is final
+    const bool ok = bad == 0;
+    if (tid == 0) {
+      count[0] = ok ? ra + rb + rp : 0;
+      count[1] = ok ? ra : 0;
+    }
+    if (!ok) {  // no pieces: the scan passes every sequence's initial state through
+      for (int sq = s0; sq < s1; ++sq) {
+        first[sq] = 0;
+        n_a[sq] = 0;
+        last[sq] = -1;
+      }
+      return;
+    }
+    const int S32 = (int)(sl / 32), S64 = (int)(sl / 64);
+    int slot_a = base[0], slot_b = ra + base[1], slot_c = ra + rb + base[2], pk = ra + rb + base[3];
+    int pos = base[4];
+    int open = -1, open0 = 0;  // this thread's open pack: item, first descriptor
+    int fill = 0;
+    auto close = [&]() {
+      if (open >= 0) item[open] = make_int4(pos - open0, 0, open0, open0);
+    };
     for (int sq = s0; sq < s1; ++sq) {
-      const int64_t len = cu[sq + 1] - cu[sq];
-      lbad |= len < 0;
-      const int64_t l = max<int64_t>(len, 0);
-      const int nf = (int)(l / seg_len);
-      const int64_t r = l % seg_len;
+      const int c0 = (int)ofs_at(sq);
+      const uint32_t len = (uint32_t)(ofs_at(sq + 1) - c0);
+      const int nf = (int)(len / sl);
+      const int r = (int)(len - nf * sl);
+      const int na = r ? nf : max(nf - 1, 0);
+      first[sq] = slot_a;
+      n_a[sq] = na;
+      for (int j = 0; j < na; ++j) item[slot_a + j] = make_int4(S32, S64, c0 + j * (int)sl, -1 - sq);
+      slot_a += na;
       if (r) {
-        v[0] += nf;
-        const int64_t pl = (r + 31) / 32 * 32;
-        if (fill < 0 || fill + pl > seg_len) {
-          ++v[3];
+        last[sq] = slot_c;
+        const int pl = (r + 31) / 32 * 32;
+        if (open < 0 || fill + pl > (int)sl) {
+          close();
+          open = pk++;
+          open0 = pos;
           fill = 0;
         }
         fill += pl;
-        ++v[2];
-        v[4] += (int)((r + 31) / 32);
+        const int row = c0 + nf * (int)sl;
+        const int n32 = (r + 31) / 32;
+        if constexpr (ST) {
+          stail[slot_c - ra - rb] = make_int4(pos, row, slot_c, sq);
+        } else {
+          for (int i = 0; i < n32; ++i)
+            list32[pos + i] = make_int4(row + 32 * i, min(32, r - 32 * i), slot_c,
+                                        (i == 0 ? kFirst : 0) | (i == n32 - 1 ? kLast | kSeqEnd : 0) | (sq << 3));
+        }
+        pos += n32;
+        ++slot_c;
       } else if (nf > 0) {
-        v[0] += nf - 1;
-        ++v[1];
+        last[sq] = slot_b;
+        item[slot_b] = make_int4(S32, S64, c0 + na * (int)sl, -1 - sq);
+        ++slot_b;
+      } else {
+        last[sq] = -1;
       }
     }
-  }
-  if (tid == 0) bad = 0;
-  __syncthreads();
-  if (lbad) atomicOr(&bad, 1);
-  // exclusive prefix of the per-thread counts: inclusive scan within each wave
-  // (shuffles), then the four wave totals
-  const int lane = tid & 63, wv = tid >> 6;
-  int inc[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) inc[i] = v[i];
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int u = __shfl_up(inc[i], o, 64);
-      if (lane >= o) inc[i] += u;
+    close();
+    if constexpr (!ST) return;
+    __syncthreads();  // every tail recorded
+    // one wave per tail, one lane per chunk
+    for (int t = tid >> 6; t < rc; t += 4) {
+      const int4 ti = stail[t];
+      const int r = (int)((uint32_t)(scu[ti.w + 1] - scu[ti.w]) % sl);
+      const int n32 = (r + 31) / 32;
+      for (int i = lane; i < n32; i += 64)
+        list32[ti.x + i] = make_int4(ti.y + 32 * i, min(32, r - 32 * i), ti.z,
+                                     (i == 0 ? kFirst : 0) | (i == n32 - 1 ? kLast | kSeqEnd : 0) | (ti.w << 3));
     }
-  }
-  if (lane == 63)
-#pragma unroll
-    for (int i = 0; i < NV; ++i) part[wv][i] = inc[i];
-  __syncthreads();
-  int base[NV], tot[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    base[i] = inc[i] - v[i];
-    tot[i] = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (w < wv) base[i] += part[w][i];
-      tot[i] += part[w][i];
-    }
-  }
-  const int ra = tot[0], rb = tot[1], rc = tot[2], rp = tot[3];
-  if (tid == 0 && ra + rb + rc > g_max) atomicOr(&bad, 1);
-  __syncthreads();  // every wave has read the wave totals; bad is final
-  const bool ok = bad == 0;
-  if (tid == 0) {
-    count[0] = ok ? ra + rb + rp : 0;
-    count[1] = ok ? ra : 0;
-  }
-  if (!ok) {  // no pieces: the scan passes every sequence's initial state through
-    for (int sq = s0; sq < s1; ++sq) {
-      first[sq] = 0;
-      n_a[sq] = 0;
-      last[sq] = -1;
-    }
-    return;
-  }
-  const int S32 = (int)(seg_len / 32), S64 = (int)(seg_len / 64);
-  int slot_a = base[0], slot_b = ra + base[1], slot_c = ra + rb + base[2], pk = ra + rb + base[3];
-  int pos = base[4];
-  int open = -1, open0 = 0;  // this thread's open pack: item, first descriptor
-  int64_t fill = 0;
-  auto close = [&]() {
-    if (open >= 0) item[open] = make_int4(pos - open0, 0, open0, open0);
   };
-  for (int sq = s0; sq < s1; ++sq) {
-    const int64_t c0 = cu[sq], len = cu[sq + 1] - c0;
-    const int nf = (int)(len / seg_len);
-    const int64_t r = len % seg_len;
-    const int na = r ? nf : max(nf - 1, 0);
-    first[sq] = slot_a;
-    n_a[sq] = na;
-    for (int j = 0; j < na; ++j) item[slot_a + j] = make_int4(S32, S64, (int)(c0 + j * seg_len), -1 - sq);
-    slot_a += na;
-    if (r) {
-      last[sq] = slot_c;
-      const int64_t pl = (r + 31) / 32 * 32;
-      if (open < 0 || fill + pl > seg_len) {
-        close();
-        open = pk++;
-        open0 = pos;
-        fill = 0;
-      }
-      fill += pl;
-      const int row = (int)(c0 + (int64_t)nf * seg_len);
-      const int n32 = (int)((r + 31) / 32);
-      for (int i = 0; i < n32; ++i)
-        list32[pos + i] = make_int4(row + 32 * i, (int)min<int64_t>(32, r - 32 * i), slot_c,
-                                    (i == 0 ? kFirst : 0) | (i == n32 - 1 ? kLast | kSeqEnd : 0) | (sq << 3));
-      pos += n32;
-      ++slot_c;
-    } else if (nf > 0) {
-      last[sq] = slot_b;
-      item[slot_b] = make_int4(S32, S64, (int)(c0 + (int64_t)na * seg_len), -1 - sq);
-      ++slot_b;
-    } else {
-      last[sq] = -1;
-    }
-  }
-  close();
+  if (staged)
+    run(std::true_type());
+  else
+    run(std::false_type());
 }
 
 // Tokens per work item: about 256 work items over the chip, a multiple of two

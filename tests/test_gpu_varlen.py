@@ -142,16 +142,23 @@ def test_varlen_prefill_then_decode(lib, orc):
             assert rownorm_rel(to_np(o_last)[row:row + 1], ro[0, -1:]) < TOL["bf16"]
 
 
-def test_varlen_many_short_sequences(lib, orc):
-    rng = np.random.default_rng(11)
-    lengths = [int(x) for x in rng.integers(0, 90, 300)]
-    H = 1
-    q, k, v, cu = _packed(H, lengths, [3, 73])
+@pytest.mark.parametrize("n_seqs,max_len,H", [
+    (300, 90, 1),    # the work list stages offsets and tails in LDS (up to 2048 sequences)
+    (2100, 9, 1),    # more sequences: the work list reads them from memory
+])
+def test_varlen_many_short_sequences(lib, orc, n_seqs, max_len, H):
+    """Many short sequences: their tails share work items (packs of many pieces)."""
+    _say(f"varlen many short sequences n={n_seqs} max_len={max_len} H={H}")
+    rng = np.random.default_rng([11, n_seqs])
+    lengths = [int(x) for x in rng.integers(0, max_len, n_seqs)]
+    q, k, v, cu = _packed(H, lengths, [3, 73, n_seqs])
     A, G = ss.make_draws(W)
-    o, S, z = _run(lib, q, k, v, cu, A, G)
-    ro, rS, _ = orc.slay_causal_varlen(q, k, v, cu, A, G, W.eps, W.R, W.m)
-    assert rownorm_rel(o, ro) < TOL["bf16"]
-    assert _srel(S, rS, W) < TOL["bf16"]
+    S0, z0 = _states(n_seqs, H, 7)
+    o, S, z = _run(lib, q, k, v, cu, A, G, S0, z0)
+    ro, rS, rz = orc.slay_causal_varlen(q, k, v, cu, A, G, W.eps, W.R, W.m, S0=S0, z0=z0)
+    err, s_err, z_err = rownorm_rel(o, ro), _srel(S, rS, W), _zrel(z, rz, W)
+    _say(f"  o rownorm {err:.3e}; S {s_err:.3e} z {z_err:.3e}")
+    assert err < TOL["bf16"] and s_err < TOL["bf16"] and z_err < TOL["bf16"]
 
 
 @pytest.mark.parametrize("R,m", [(4, 64), (3, 32)])  # F = 256, and F = 96 on zero-padded features
