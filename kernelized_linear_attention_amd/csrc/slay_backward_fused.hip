@@ -111,10 +111,10 @@ constexpr int kNE = kE / 16;
 constexpr int kDV = 64;
 constexpr int kW = 8, kNT = kW * 64;  // waves; wave w owns feature blocks 2w, 2w + 1
 // LDS row strides in elements (odd multiples of 16 bytes)
-constexpr int kLT = kT + 8;        // [e][t] tiles
+constexpr int kLT = kT + 4;        // [e][t] tiles: 40-byte rows keep the staging stores and 8-byte column reads apart in banks
 constexpr int kLR = kE + 8;        // [t][e] tiles
-constexpr int kLP = kE + 4;        // fp32 partials [w][t][e]
-constexpr int kLPV = kDV + 4;
+constexpr int kLP = kE + 8;        // fp32 partials [w][t][e] (row stride 32 mod 64 bytes: 16-byte accesses in one pass)
+constexpr int kLPV = kDV + 8;
 
 struct PbParams {
   const uint16_t* q;     // [n_heads * L][64]
@@ -261,28 +261,41 @@ __device__ __forceinline__ f32x4 phi_tok(const Proj& P, const XRows& X, int j, i
   return o;
 }
 
-// V' = [v | 1 | 0] of the step's tokens (zero rows past n) as [t][e] rows and [e][t] columns
+// V' = [v | 1 | 0] of the step's tokens (zero rows past n) as [t][e] rows and [e][t] columns.
+// The columns are written as token pairs: lanes t and t^1 (lane ^ 8) trade their
+// eight values, and the even token's lane writes four columns, the odd one's the
+// other four, one 4-byte store each.
 __device__ __forceinline__ void stage_v(uint4 x, int n, uint16_t* VR, uint16_t* VT, int tid) {
   if (tid < kT * 8) {
     const int t = tid >> 3, e0 = 8 * (tid & 7);
     if (t >= n) x = make_uint4(0, 0, 0, 0);
     if (VR) *reinterpret_cast<uint4*>(VR + t * kLR + e0) = x;
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};  // columns (e0 + 2i, e0 + 2i + 1) of token t
+    uint32_t o[4];                                // the same of token t ^ 1
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      VT[(e0 + 2 * i) * kLT + t] = (uint16_t)(w[i] & 0xFFFFu);
-      VT[(e0 + 2 * i + 1) * kLT + t] = (uint16_t)(w[i] >> 16);
+    for (int i = 0; i < 4; ++i) o[i] = (uint32_t)__shfl_xor((int)w[i], 8, 64);
+    const bool odd = t & 1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // columns e0 + 4 odd + r
+      const int i = 2 * (odd ? 1 : 0) + (r >> 1);
+      const int sh = 16 * (r & 1);
+      const uint32_t mine = (w[i] >> sh) & 0xFFFFu, other = (o[i] >> sh) & 0xFFFFu;
+      const uint32_t pair = odd ? (other | (mine << 16)) : (mine | (other << 16));  // even token in the low half
+      *reinterpret_cast<uint32_t*>(VT + (e0 + 4 * (odd ? 1 : 0) + r) * kLT + (t & ~1)) = pair;
     }
-  } else if (tid < kT * 8 + kT) {
-    const int t = tid - kT * 8;
-    const uint16_t one = t < n ? (uint16_t)0x3F80 : (uint16_t)0;
+  } else if (tid < kT * 8 + kT / 2) {  // the ones column and the zero columns, a token pair per thread
+    const int t = 2 * (tid - kT * 8);
+    const uint32_t one = (t < n ? 0x3F80u : 0u) | (t + 1 < n ? 0x3F800000u : 0u);
     if (VR) {
-      *reinterpret_cast<uint4*>(VR + t * kLR + kDV) = make_uint4(one, 0, 0, 0);
-      *reinterpret_cast<uint4*>(VR + t * kLR + kDV + 8) = make_uint4(0, 0, 0, 0);
-    }
-    VT[kDV * kLT + t] = one;
 #pragma unroll
-    for (int e = kDV + 1; e < kE; ++e) VT[e * kLT + t] = 0;
+      for (int u = 0; u < 2; ++u) {
+        *reinterpret_cast<uint4*>(VR + (t + u) * kLR + kDV) = make_uint4((one >> (16 * u)) & 0xFFFFu, 0, 0, 0);
+        *reinterpret_cast<uint4*>(VR + (t + u) * kLR + kDV + 8) = make_uint4(0, 0, 0, 0);
+      }
+    }
+    *reinterpret_cast<uint32_t*>(VT + kDV * kLT + t) = one;
+#pragma unroll
+    for (int e = kDV + 1; e < kE; ++e) *reinterpret_cast<uint32_t*>(VT + e * kLT + t) = 0u;
   }
 }
 
