@@ -208,7 +208,9 @@ size_t slay_attn_chunked_bwd_workspace_size(const slay_params_t* params, int32_t
  * dS0 = dS_T and dz0 = dz_T (zero where those are NULL).
  * Kernel families, chosen from the shape:
  *   bf16, d = dv = 64, chunk = 64, m a multiple of 32, R*m <= 256: MFMA
- *     kernels (phi written once in bf16, per-segment states, 32-token steps);
+ *     kernels (per-segment states, 16-token steps, phi recomputed on chip;
+ *     every product that touches a state, phi or g runs on split hi + lo
+ *     bf16 operands, because dq is a small difference of large terms);
  *     R*m below 256 runs them on features zero-padded to 256, which changes
  *     no result (the padded features and their gradients are exactly zero);
  *   every other accepted shape: general kernels (the feature map to the
