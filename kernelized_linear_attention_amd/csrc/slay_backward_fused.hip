@@ -352,8 +352,9 @@ __device__ __forceinline__ f32x4 load_ef(const float* item, int fb, int eb, int 
 }
 
 // A segment's steps.  The body takes the step's q, k rows (issued during the
-// previous step), its token range, and a callback that issues the next
-// step's rows into the same registers once the body has consumed them.
+// previous step), its token range, the step's index (its parity picks the
+// LDS buffers of the double-buffered tiles) and a callback that issues the
+// next step's rows into the same registers once the body has consumed them.
 template <bool REV, class LOAD, class BODY>
 __device__ __forceinline__ void walk_steps(int64_t t_begin, int64_t t_end, LOAD load, BODY body) {
   const int n_steps = (int)((t_end - t_begin + kT - 1) / kT);
@@ -379,13 +380,13 @@ __device__ __forceinline__ void walk_steps(int64_t t_begin, int64_t t_end, LOAD 
         load(in, tn, nn);
       }
     };
-    body(in, tc, nc, prefetch);
+    body(in, tc, nc, i, prefetch);
   }
 }
 
 // (1) sum over each segment's keys (all segments but the last) of phi(k) v'^T, in the item order
 __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
-  __shared__ __align__(16) uint16_t VT[kE * kLT];
+  __shared__ __align__(16) uint16_t VT2[2][kE * kLT];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n_items = p.n_seg - 1;
@@ -403,14 +404,16 @@ __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
   walk_steps<false>(
       t_begin, t_end,
       [&](StepIn& in, int64_t t0, int n) { load_step<false, true>(in, p, h * p.L + t0, n, g, c); },
-      [&](StepIn& in, int64_t t0, int n, auto prefetch) {
+      [&](StepIn& in, int64_t t0, int n, int step, auto prefetch) {
         const StepAux ax = load_aux<false, false>(p, h * p.L + t0, n, tid);
         const XRows xk = finish_x(in.ka, in.kb, c < n);
         prefetch();
         f32x4 kt[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) kt[j] = phi_tok(P, xk, j, g);
-        __syncthreads();
+        // double-buffered VT: the previous step's readers use the other buffer, and a
+        // buffer is written again only after every wave has passed the next step's barrier
+        uint16_t* VT = VT2[step & 1];
         stage_v(ax.v, n, nullptr, VT, tid);
         __syncthreads();
 #pragma unroll
@@ -433,8 +436,8 @@ __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
 // (2) numerators, denominators and g' of every token, with S' (the item: the state before the segment) in
 // accumulators
 __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
-  __shared__ __align__(16) uint16_t VT[kE * kLT];
-  __shared__ __align__(16) float P[kW * kT * kLP];
+  __shared__ __align__(16) uint16_t VT2[2][kE * kLT];
+  __shared__ __align__(16) float P2[2][kW * kT * kLP];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t h = blockIdx.x / p.n_seg;
@@ -452,7 +455,7 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
   walk_steps<false>(
       t_begin, t_end,
       [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
-      [&](StepIn& in, int64_t t0, int n, auto prefetch) {
+      [&](StepIn& in, int64_t t0, int n, int step, auto prefetch) {
         const int64_t row0 = h * p.L + t0;
         const StepAux ax = load_aux<true, false>(p, row0, n, tid);
         const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
@@ -462,7 +465,10 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
         f32x4 kt[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) kt[j] = phi_tok(Pj, xk, j, g);
-        __syncthreads();  // the previous step's readers of VT and P are done
+        // double-buffered VT and P: the previous step's readers use the other buffers, and a
+        // buffer is written again only after every wave has passed the next step's barriers
+        uint16_t* VT = VT2[step & 1];
+        float* P = P2[step & 1];
         stage_v(ax.v, n, nullptr, VT, tid);
         __syncthreads();
         // this wave's part of A^T[j][i] = sum_f phi(K_j)_f phi(Q_i)_f over its features (split phi), masked j <= i
@@ -555,12 +561,12 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
 // (3) dphi(Q) = D phi(K) + G' S'^T for this wave's features, and the segment's sum phi(Q)^T G' (written over
 // the item once the walk is done)
 __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
-  __shared__ __align__(16) uint16_t VT[kE * kLT];
-  __shared__ __align__(16) uint16_t VR[kT * kLR];
-  __shared__ __align__(16) uint16_t GRh[kT * kLR];
-  __shared__ __align__(16) uint16_t GRl[kT * kLR];
-  __shared__ __align__(16) uint16_t GTh[kE * kLT];
-  __shared__ __align__(16) uint16_t GTl[kE * kLT];
+  __shared__ __align__(16) uint16_t VT2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t VR2[2][kT * kLR];
+  __shared__ __align__(16) uint16_t GRh2[2][kT * kLR];
+  __shared__ __align__(16) uint16_t GRl2[2][kT * kLR];
+  __shared__ __align__(16) uint16_t GTh2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t GTl2[2][kE * kLT];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t h = blockIdx.x / p.n_seg;
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
   walk_steps<false>(
       t_begin, t_end,
       [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
-      [&](StepIn& in, int64_t t0, int n, auto prefetch) {
+      [&](StepIn& in, int64_t t0, int n, int step, auto prefetch) {
         const int64_t row0 = h * p.L + t0;
         const StepAux ax = load_aux<false, true>(p, row0, n, tid);
         const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
@@ -592,7 +598,10 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
           qt[j] = hilo(phi_tok(P, xq, j, g));
           kt[j] = hilo(phi_tok(P, xk, j, g));
         }
-        __syncthreads();
+        // double-buffered tiles: the previous step's readers use the other buffers, and a
+        // buffer is written again only after every wave has passed the next step's barrier
+        const int sb = step & 1;
+        uint16_t *VT = VT2[sb], *VR = VR2[sb], *GRh = GRh2[sb], *GRl = GRl2[sb], *GTh = GTh2[sb], *GTl = GTl2[sb];
         stage_v(ax.v, n, VR, VT, tid);
         stage_g(ax.gp, n, GRh, GRl, GTh, GTl, tid);
         __syncthreads();
@@ -656,13 +665,13 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
 // (5) dphi(K) = D^T phi(Q) + V' U^T for this wave's features, dV = A^T G + phi(K) U[:, :dv] (per-wave partials
 // summed through LDS), walking the segment backward with U (the item: U after the segment) in accumulators
 __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
-  __shared__ __align__(16) uint16_t VR[kT * kLR];
-  __shared__ __align__(16) uint16_t VT[kE * kLT];
-  __shared__ __align__(16) uint16_t GRh[kT * kLR];
-  __shared__ __align__(16) uint16_t GRl[kT * kLR];
-  __shared__ __align__(16) uint16_t GTh[kE * kLT];
-  __shared__ __align__(16) uint16_t GTl[kE * kLT];
-  __shared__ __align__(16) float P[kW * kT * kLPV];
+  __shared__ __align__(16) uint16_t VR2[2][kT * kLR];
+  __shared__ __align__(16) uint16_t VT2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t GRh2[2][kT * kLR];
+  __shared__ __align__(16) uint16_t GRl2[2][kT * kLR];
+  __shared__ __align__(16) uint16_t GTh2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t GTl2[2][kE * kLT];
+  __shared__ __align__(16) float P2[2][kW * kT * kLPV];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t h = blockIdx.x / p.n_seg;
@@ -683,7 +692,7 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
   walk_steps<true>(
       t_begin, t_end,
       [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
-      [&](StepIn& in, int64_t t0, int n, auto prefetch) {
+      [&](StepIn& in, int64_t t0, int n, int step, auto prefetch) {
         const int64_t row0 = h * p.L + t0;
         const StepAux ax = load_aux<false, true>(p, row0, n, tid);
         const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
@@ -693,7 +702,12 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
         bf16x8 qt[2];  // split phi(q) of the step's tokens, four per lane
 #pragma unroll
         for (int j = 0; j < 2; ++j) qt[j] = hilo(phi_tok(Pj, xq, j, g));
-        __syncthreads();
+        // double-buffered tiles and partials: the previous step's readers use the other
+        // buffers, and a buffer is written again only after every wave has passed the next
+        // step's barriers
+        const int sb = step & 1;
+        uint16_t *VT = VT2[sb], *VR = VR2[sb], *GRh = GRh2[sb], *GRl = GRl2[sb], *GTh = GTh2[sb], *GTl = GTl2[sb];
+        float* P = P2[sb];
         stage_v(ax.v, n, VR, VT, tid);
         stage_g(ax.gp, n, GRh, GRl, GTh, GTl, tid);
         __syncthreads();
