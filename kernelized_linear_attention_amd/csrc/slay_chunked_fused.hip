@@ -721,7 +721,7 @@ __device__ __forceinline__ void store_state_out(const Params& p, int64_t head, i
 // k tiles are double-buffered, v'^T triple-buffered (chunk c-1 is still read
 // while chunk c+1 is staged), and phi(k) alternates between two register sets.
 template <class K, int FS>
-__global__ __launch_bounds__(K::NT / FS) void pass1_kernel(Params p) {
+__global__ __launch_bounds__(K::NT / FS, 2) void pass1_kernel(Params p) {
   constexpr int NT1 = K::NT / FS;
   extern __shared__ __align__(16) unsigned char lds[];
   auto sK = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * K::kKbuf1); };
@@ -1174,7 +1174,7 @@ __device__ __forceinline__ void nc_task(const Params& p, int64_t row0, int n, in
 }
 
 template <class K>
-__global__ __launch_bounds__(K::NT) void ncout_kernel(Params p) {
+__global__ __launch_bounds__(K::NT, 2) void ncout_kernel(Params p) {
   constexpr int kXt = K::C * K::LDX * 2, kPt = K::C * K::LDF * 2;
   extern __shared__ __align__(16) unsigned char lds[];
   auto sQ = [&](int b) { return reinterpret_cast<uint16_t*>(lds + b * kXt); };

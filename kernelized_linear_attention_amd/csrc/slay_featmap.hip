@@ -55,7 +55,7 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, 
 // The d = 128 bf16 variant is held to 3 waves per SIMD: it otherwise takes
 // 164 registers and runs 2 waves per SIMD, with its memory latency exposed.
 template <typename TI, typename TO, int D, int FBW, int TR>
-__global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 1) void featmap_kernel(
+__global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 2) void featmap_kernel(
     const TI* __restrict__ x_a, const TI* __restrict__ x_b, int64_t rows_per_head, int64_t n_heads,
     const TI* __restrict__ anchors, const TI* __restrict__ prf, int64_t draw_set_stride, int n_draw_sets, int F,
     int m, NodeConsts nc, TO* __restrict__ phi_a, TO* __restrict__ phi_b, int gx) {
