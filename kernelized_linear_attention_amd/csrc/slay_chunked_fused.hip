@@ -720,6 +720,8 @@ __device__ __forceinline__ void store_state_out(const Params& p, int64_t head, i
 // chunk c-1 runs beside it, so MFMA and VALU work of two chunks overlap.
 // k tiles are double-buffered, v'^T triple-buffered (chunk c-1 is still read
 // while chunk c+1 is staged), and phi(k) alternates between two register sets.
+// At least 2 waves per SIMD are asked for (the 4-wave shape would otherwise
+// keep MFMA results in accumulator registers, each copied out by a VALU op).
 template <class K, int FS>
 __global__ __launch_bounds__(K::NT / FS, 2) void pass1_kernel(Params p) {
   constexpr int NT1 = K::NT / FS;
@@ -1173,6 +1175,7 @@ __device__ __forceinline__ void nc_task(const Params& p, int64_t row0, int n, in
   }
 }
 
+// (at least 2 waves per SIMD, for the reason given at pass1_kernel)
 template <class K>
 __global__ __launch_bounds__(K::NT, 2) void ncout_kernel(Params p) {
   constexpr int kXt = K::C * K::LDX * 2, kPt = K::C * K::LDF * 2;

@@ -52,8 +52,11 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, float a, float b, 
   *reinterpret_cast<uint2*>(p) = v;
 }
 
-// The d = 128 bf16 variant is held to 3 waves per SIMD: it otherwise takes
-// 164 registers and runs 2 waves per SIMD, with its memory latency exposed.
+// Every variant asks for at least 2 waves per SIMD: with 1 the compiler may
+// keep the MFMA results in accumulator registers and copy each one out with
+// a VALU instruction.  The d = 128 bf16 variant is held to 3: it otherwise
+// takes 164 registers and runs 2 waves per SIMD, with its memory latency
+// exposed.
 template <typename TI, typename TO, int D, int FBW, int TR>
 __global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 2) void featmap_kernel(
     const TI* __restrict__ x_a, const TI* __restrict__ x_b, int64_t rows_per_head, int64_t n_heads,
