@@ -17,8 +17,8 @@
 // square / exp2 / scale epilogue straight from the accumulators.  The 1/|x|
 // scale is applied to the fp32 accumulator, (x/|x|).P = (x.P)/|x|, so bf16
 // inputs are never rounded twice.  The tile's features are written back from
-// an LDS staging copy with coalesced 16-byte stores (non-temporal for
-// large launches).
+// an LDS staging copy with coalesced 16-byte buffer stores (non-temporal for
+// large launches) that stay in flight while the next tile is computed.
 #include "slay_device.hpp"
 #include "slay_internal.hpp"
 
@@ -239,33 +239,41 @@ __global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 2) vo
       }
     }
     __syncthreads();
-    // Loads and stores retire in issue order and share one counter, so the
-    // next tile's staging, which needs the prefetched rows, would otherwise
-    // also wait for every store issued below.  Waiting here (the prefetch was
-    // issued before the projection) leaves the stores to drain while the
-    // next tile is staged and computed.
-    wait_vmem();
-    // coalesced write-out of the tile's feature slice: 16-byte pieces of each row
+    // coalesced write-out of the tile's feature slice: 16-byte pieces of each
+    // row as buffer stores bounded by the tile's rows (pieces past its last row
+    // or past F are dropped by the bounds check), so every thread issues the
+    // same number of stores and the next tile's staging waits only for the
+    // prefetched rows, not for these stores
     {
       constexpr int PPR = FWS * (int)sizeof(TO) / 16;  // 16-byte pieces per row of the slice
+      constexpr int NPC = (TR * PPR + kThreads - 1) / kThreads;  // pieces per thread
       const int fcols = min(FWS, F - by * FWS);
       const int ppr = fcols * (int)sizeof(TO) / 16;
-      for (int pc = threadIdx.x; pc < TR * PPR; pc += kThreads) {
-        const int rr = pc / PPR, q = pc - (pc / PPR) * PPR;
-        if (rr < nrow && q < ppr) {
-          const u32x4 val = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(so + rr * LDO) + q * 16);
-          u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(pt + (int64_t)rr * F + by * FWS) + q * 16);
-          // Large launches write phi once and never read it back here, so
-          // they stream it with non-temporal stores; small ones (a decode
-          // step's phi(q)) are read by the next kernel and stay cached.
-          if constexpr (TR == kTileRows)
-            __builtin_nontemporal_store(val, dst);
-          else
-            *dst = val;
-        }
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          pt, (short)0, (int)(nrow * F * (int64_t)sizeof(TO)), 0x00020000);
+      u32x4 val[NPC];
+#pragma unroll
+      for (int i = 0; i < NPC; ++i) {
+        const int pc = min(threadIdx.x + i * kThreads, TR * PPR - 1);
+        const int rr = pc / PPR, q = pc - rr * PPR;
+        val[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(so + rr * LDO) + q * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < NPC; ++i) {
+        const int pc = threadIdx.x + i * kThreads;
+        const int rr = pc / PPR, q = pc - rr * PPR;
+        const bool ok = pc < TR * PPR && q < ppr;
+        const int off = ok ? rr * F * (int)sizeof(TO) + by * FWS * (int)sizeof(TO) + q * 16 : 0x7FFFFFF0;
+        // Large launches write phi once and never read it back here, so they
+        // stream it with non-temporal stores (cache policy 2); small ones (a
+        // decode step's phi(q)) are read by the next kernel and stay cached.
+        __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, TR == kTileRows ? 2 : 0);
       }
     }
-    __syncthreads();
+    // No barrier here: the next tile's staging writes sx, sinv and slg, whose
+    // last readers (this tile's projection) all finished before the barrier
+    // above, and its epilogue writes so only after the next staging barrier,
+    // which every thread reaches after reading its pieces of so.
   }
 }
 
@@ -274,7 +282,9 @@ hipError_t launch_t(const FeatmapArgs& a, hipStream_t s) {
   const int FW = 4 * FBW * 16;
   const int gy = (a.F + FW - 1) / FW;
   const int64_t tiles = ((a.rows_per_head + TR - 1) / TR) * a.n_heads;
-  int64_t gx = 2048 / gy;
+  // 1024 workgroups in all, one per (walker, slice): four per CU at the
+  // headline shape's occupancy, so every walker starts at once
+  int64_t gx = 1024 / gy;
   if (gx < 1) gx = 1;
   if (gx > tiles) gx = tiles;
   if (tiles == 0) return hipSuccess;
