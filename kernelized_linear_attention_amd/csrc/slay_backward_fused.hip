@@ -532,9 +532,7 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
           float dot = 0.f;
 #pragma unroll
           for (int t = 0; t < 4; ++t) dot = fmaf(dn[t], n0[t], fmaf(dn[4 + t], n1[t], dot));
-          dot += __shfl_xor(dot, 1, 64);
-          dot += __shfl_xor(dot, 2, 64);
-          dot += __shfl_xor(dot, 4, 64);
+          dot = sum_lanes8(dot);
           if (i < n) {
             const float inv = 1.f / den;
             float* gr = p.g + (row0 + i) * kE;
@@ -798,16 +796,18 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
 // features' y, the weights w and its partial dxh over those features into its
 // own fp32 LDS tile; then, summing the waves' partials, the projection
 // dx = (dxh - xh (xh . dxh)) / |x|, 16 lanes per row.  x and dphi of the
-// next three tiles are in flight while the current one is computed.
+// next two tiles are in flight while the current one is computed.
 template <int NF_>
 struct VjpK {
   static constexpr int NF = NF_, F = NF * 16, D = 64;
   static constexpr int NW = NF / 2, NT = NW * 64;
   static constexpr int RT = 32, NRB = RT / 16;  // rows per tile
   static constexpr int LX = D + 8, LR = D + 4;
-  // x tile, per-wave partials, 1/|x| per row (negative where |x| is clamped)
-  static constexpr int oX = 0, oR = RT * LX * 2, oI = oR + NW * RT * LR * 4, kLds = oI + RT * 4;
-  static_assert(NT >= RT * 8 && NT >= RT * 16, "one x piece and one output piece per thread");
+  // x tile, per-wave partials, 1/|x| per row (negative where |x| is clamped), and each
+  // thread's own dphi pieces ([piece][thread], 8 bytes each)
+  static constexpr int oX = 0, oR = RT * LX * 2, oI = oR + NW * RT * LR * 4, oD = oI + RT * 4;
+  static constexpr int kLds = oD + NRB * 2 * NT * 8;
+  static_assert(NT >= RT * 8 && NT == RT * 16, "one x piece per thread (some idle), one output piece per thread");
 };
 
 struct VjpParams {
@@ -828,22 +828,36 @@ struct VjpPref {
   uint2 dp[K::NRB][2];      // dphi of row 16 rb + l%16, features 16 fb_j + 4(l/16) ..
 };
 
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// Buffer resource over rows [r0, min(r0 + rt, n_rows)) of a row-major array:
+// accesses past those rows (or past the end, for a tile past the last) read
+// zeros and write nothing, so every thread issues the same memory
+// instructions for every tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int64_t r0, int64_t n_rows, int rt,
+                                                           int row_bytes) {
+  const int64_t nr = max<int64_t>(0, min<int64_t>(rt, n_rows - r0));
+  char* b = const_cast<char*>(static_cast<const char*>(base)) + (nr > 0 ? r0 : 0) * row_bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)(nr * row_bytes), 0x00020000);
+}
+constexpr int kOutOfRange = 0x7FFFFFF0;
+
 template <class K>
 __device__ __forceinline__ void vjp_load(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dphi,
                                          int64_t n_rows, int64_t r0, int tid, int wave, int g, int c16,
                                          VjpPref<K>& pf) {
-  const int64_t xr = r0 + (tid >> 3);
-  pf.x = (tid < K::RT * 8 && xr < n_rows) ? *reinterpret_cast<const uint4*>(x + xr * K::D + 8 * (tid & 7))
-                                          : make_uint4(0, 0, 0, 0);
+  const __amdgpu_buffer_rsrc_t rx = tile_rsrc(x, r0, n_rows, K::RT, K::D * 2);
+  const int xo = tid < K::RT * 8 ? (tid >> 3) * (K::D * 2) + 16 * (tid & 7) : kOutOfRange;
+  pf.x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0));
+  const __amdgpu_buffer_rsrc_t rd = tile_rsrc(dphi, r0, n_rows, K::RT, K::F * 2);
 #pragma unroll
-  for (int rb = 0; rb < K::NRB; ++rb) {
-    const int64_t row = r0 + rb * 16 + c16;
+  for (int rb = 0; rb < K::NRB; ++rb)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      pf.dp[rb][j] = row < n_rows
-                         ? *reinterpret_cast<const uint2*>(dphi + row * K::F + (2 * wave + j) * 16 + 4 * g)
-                         : make_uint2(0, 0);
-  }
+      pf.dp[rb][j] = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(rd, (rb * 16 + c16) * (K::F * 2) + ((2 * wave + j) * 16 + 4 * g) * 2,
+                                                      0, 0));
 }
 
 template <class K>
@@ -852,6 +866,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   uint16_t* sX = reinterpret_cast<uint16_t*>(lds_raw + K::oX);
   float* sR = reinterpret_cast<float*>(lds_raw + K::oR);
   float* sI = reinterpret_cast<float*>(lds_raw + K::oI);
+  uint2* sD = reinterpret_cast<uint2*>(lds_raw + K::oD);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int side = blockIdx.y;
@@ -863,22 +878,23 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   bf16x8 pa[2][2], pg[2][2], pt[2][K::D / 16];
   float c1[2], c0[2], sb[2];
   int set = -1;
-  // The next tile's rows are loaded while this one is computed.  Vector loads
-  // and stores retire in issue order and share one counter, so the loop
-  // starts with no load in flight and waits for the prefetch once, before
-  // the tile's stores: a deeper prefetch (or one rotated through registers)
-  // would make each wait for it also wait for the stores issued since.
-  VjpPref<K> pf;
+  // The two tiles after the one being computed are in flight, in two
+  // register sets that alternate (the loop body is taken twice per
+  // iteration, once per set); a tile's inputs move to LDS before its set is
+  // reloaded, so no loaded value is copied between registers.  Vector loads
+  // and stores retire in issue order and share one counter; every load and
+  // store here is a bounded buffer access issued by every thread for every
+  // tile (a tile past the last one reads zeros and writes nothing), so the
+  // compiler can count what is in flight and a tile's staging waits only for
+  // its own rows, not for the stores issued since.
   const int64_t gs = gridDim.x;
   auto load_tile = [&](int64_t t, VjpPref<K>& dst) {
-    if (t < n_tiles) vjp_load<K>(x, dphi, p.n_rows, t * K::RT, tid, wave, g, c16, dst);
+    vjp_load<K>(x, dphi, p.n_rows, t * K::RT, tid, wave, g, c16, dst);
   };
-  load_tile(blockIdx.x, pf);
-  wait_vmem();
-  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gs) {
+  auto tile_body = [&](int64_t tile, VjpPref<K>& pf) {
     const int64_t r0 = tile * K::RT;
     const int tset = (int)((r0 / p.rows_per_head) % p.n_draw_sets);  // a tile never spans two draw sets
-    if (tset != set) {  // this wave's rows of P, as both operands
+    if (tset != set && r0 < p.n_rows) {  // this wave's rows of P, as both operands
       set = tset;
       const uint16_t* A = p.anchors + set * p.draw_set_stride;
       const uint16_t* G = p.prf + set * p.draw_set_stride;
@@ -908,23 +924,24 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       }
       wait_vmem();  // here, where the reload is rare, rather than at the first use
     }
-    __syncthreads();  // the previous tile's readers of sX and sR are done
-    const VjpPref<K> cur = pf;
-    load_tile(tile + gs, pf);
+    __syncthreads();  // the previous tile's readers of sX, sR and sD are done
+#pragma unroll
+    for (int rb = 0; rb < K::NRB; ++rb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sD[(rb * 2 + j) * K::NT + tid] = pf.dp[rb][j];
     if (tid < K::RT * 8) {  // x rows, and 1/|x| once per row (eight threads per row)
-      *reinterpret_cast<uint4*>(sX + (tid >> 3) * K::LX + 8 * (tid & 7)) = cur.x;
-      const uint32_t wds[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
+      *reinterpret_cast<uint4*>(sX + (tid >> 3) * K::LX + 8 * (tid & 7)) = pf.x;
+      const uint32_t wds[4] = {pf.x.x, pf.x.y, pf.x.z, pf.x.w};
       float ss = 0.f;  // bf16 products are exact in fp32
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const bf16x2 h2 = __builtin_bit_cast(bf16x2, wds[t]);
         ss = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, ss, false);
       }
-      ss += __shfl_xor(ss, 1, 64);
-      ss += __shfl_xor(ss, 2, 64);
-      ss += __shfl_xor(ss, 4, 64);
+      ss = sum_lanes8(ss);
       if ((tid & 7) == 0) sI[tid >> 3] = ss < 1e-24f ? -1e12f : __builtin_amdgcn_rsqf(ss);
     }
+    load_tile(tile + 2 * gs, pf);
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < K::NRB; ++rb) {
@@ -941,7 +958,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
         ya = mfma_bf16(pa[j][1], xb1, ya);
         f32x4 yg = mfma_bf16(pg[j][0], xb0, kZero4);
         yg = mfma_bf16(pg[j][1], xb1, yg);
-        const uint2 dr = cur.dp[rb][j];
+        const uint2 dr = sD[(rb * 2 + j) * K::NT + tid];  // this thread's own piece
         const float dp[4] = {__uint_as_float(dr.x << 16), __uint_as_float(dr.x & 0xFFFF0000u),
                              __uint_as_float(dr.y << 16), __uint_as_float(dr.y & 0xFFFF0000u)};
         // u = dphi * a * e: w_a = 2u, w_g = u a sqrt(beta)
@@ -965,10 +982,9 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
         *reinterpret_cast<f32x4*>(sR + (wave * K::RT + rb * 16 + c16) * K::LR + cb * 16 + 4 * g) = dX[cb];
     }
     __syncthreads();
-    wait_vmem();  // the next tile's prefetch, before this tile's stores
-    if (tid < K::RT * 16) {  // 16 lanes per row, four columns each
+    const __amdgpu_buffer_rsrc_t ro = tile_rsrc(dx, r0, p.n_rows, K::RT, K::D * 2);
+    {  // 16 lanes per row, four columns each
       const int rr = tid >> 4, c = 4 * (tid & 15);
-      const int64_t row = r0 + rr;
       const uint2 xr = *reinterpret_cast<const uint2*>(sX + rr * K::LX + c);
       const float xv[4] = {__uint_as_float(xr.x << 16), __uint_as_float(xr.x & 0xFFFF0000u),
                            __uint_as_float(xr.y << 16), __uint_as_float(xr.y & 0xFFFF0000u)};
@@ -978,8 +994,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       float pr = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) pr = fmaf(xv[r], dh[r], pr);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) pr += __shfl_xor(pr, o, 64);
+      pr = sum_lanes16(pr);
       const float si = sI[rr];
       const bool clamp = si < 0.f;
       const float inv = fabsf(si);
@@ -987,8 +1002,15 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       f32x4 o;
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = (dh[r] - xv[r] * inv * proj) * inv;
-      if (row < p.n_rows) *reinterpret_cast<uint2*>(dx + row * K::D + c) = pk4(o);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, pk4(o)), ro, rr * (K::D * 2) + c * 2, 0, 0);
     }
+  };
+  VjpPref<K> pf0, pf1;
+  load_tile(blockIdx.x, pf0);
+  load_tile(blockIdx.x + gs, pf1);
+  for (int64_t tile = blockIdx.x; tile < n_tiles; tile += 2 * gs) {
+    tile_body(tile, pf0);
+    tile_body(tile + gs, pf1);  // past the last tile: zeros in, nothing out
   }
 }
 

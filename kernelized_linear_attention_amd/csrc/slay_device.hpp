@@ -60,6 +60,30 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // stores retire in issue order and share this counter.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Sums over groups of 4, 8 or 16 consecutive lanes by DPP moves, with no LDS
+// round trip: quad_perm [1,0,3,2] and [2,3,0,1] pair lanes inside each quad,
+// row_half_mirror lane i with 7-i and row_mirror lane i with 15-i of each
+// 16-lane row.  Each step adds two partial sums that the paired lanes hold in
+// swapped order, so every lane of a group ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float sum_lanes4(float x) {
+  x += dpp_mov<0xB1>(x);
+  return x + dpp_mov<0x4E>(x);
+}
+__device__ __forceinline__ float sum_lanes8(float x) { x = sum_lanes4(x); return x + dpp_mov<0x141>(x); }
+__device__ __forceinline__ float sum_lanes16(float x) { x = sum_lanes8(x); return x + dpp_mov<0x140>(x); }
+template <int N>
+__device__ __forceinline__ float sum_lanes(float x) {
+  static_assert(N == 1 || N == 4 || N == 8 || N == 16, "DPP sums cover groups of 4, 8 or 16 lanes");
+  if constexpr (N == 4) return sum_lanes4(x);
+  if constexpr (N == 8) return sum_lanes8(x);
+  if constexpr (N == 16) return sum_lanes16(x);
+  return x;
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

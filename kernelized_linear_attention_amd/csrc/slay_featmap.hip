@@ -186,8 +186,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 2) vo
         ss += f * f;
       }
     }
-#pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    ss = sum_lanes<TPR>(ss);
     if ((threadIdx.x % TPR) == 0) {
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
       sinv[threadIdx.x / TPR] = inv;
