@@ -534,7 +534,7 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
           for (int t = 0; t < 4; ++t) dot = fmaf(dn[t], n0[t], fmaf(dn[4 + t], n1[t], dot));
           dot = sum_lanes8(dot);
           if (i < n) {
-            const float inv = 1.f / den;
+            const float inv = __builtin_amdgcn_rcpf(den);  // v_rcp_f32, within 1 ulp
             float* gr = p.g + (row0 + i) * kE;
             f32x4 g0, g1;
 #pragma unroll
