@@ -17,8 +17,8 @@
 // square / exp2 / scale epilogue straight from the accumulators.  The 1/|x|
 // scale is applied to the fp32 accumulator, (x/|x|).P = (x.P)/|x|, so bf16
 // inputs are never rounded twice.  The tile's features are written back from
-// an LDS staging copy with coalesced 16-byte buffer stores (non-temporal for
-// large launches) that stay in flight while the next tile is computed.
+// an LDS staging copy with coalesced 16-byte non-temporal buffer stores that
+// stay in flight while the next tile is computed.
 #include "slay_device.hpp"
 #include "slay_internal.hpp"
 
@@ -263,10 +263,10 @@ __global__ __launch_bounds__(kThreads, (sizeof(TI) == 2 && D == 128) ? 3 : 2) vo
         const int rr = pc / PPR, q = pc - rr * PPR;
         const bool ok = pc < TR * PPR && q < ppr;
         const int off = ok ? rr * F * (int)sizeof(TO) + by * FWS * (int)sizeof(TO) + q * 16 : 0x7FFFFFF0;
-        // Large launches write phi once and never read it back here, so they
-        // stream it with non-temporal stores (cache policy 2); small ones (a
-        // decode step's phi(q)) are read by the next kernel and stay cached.
-        __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, TR == kTileRows ? 2 : 0);
+        // non-temporal (cache policy 2): phi is written once and not read
+        // back here; even a decode step, whose next kernel reads phi at once,
+        // measured slower with cached stores
+        __builtin_amdgcn_raw_buffer_store_b128(val[i], rs, off, 0, 2);
       }
     }
     // No barrier here: the next tile's staging writes sx, sinv and slg, whose
