@@ -179,7 +179,7 @@ struct StepIn {
 };
 struct StepAux {
   uint4 v;               // threads < 128: v row t0 + tid/8, columns 8 (tid % 8) ..
-  uint4 d;               // threads < 128: the same piece of dout
+  uint32_t d;            // every thread: dout row t0 + tid/32, columns 2(tid%32), 2(tid%32) + 1
   f32x4 gp;              // staging thread u = (tid + 256) % 512 < 320: g' row t0 + u/20, columns 4 (u % 20) ..
 };
 
@@ -202,7 +202,10 @@ __device__ __forceinline__ StepAux load_aux(const PbParams& p, int64_t row0, int
   if (tid < kT * 8) {
     const int64_t rv = row0 + min(tid >> 3, n - 1);
     s.v = *reinterpret_cast<const uint4*>(p.v + rv * kDV + 8 * (tid & 7));
-    if (D) s.d = *reinterpret_cast<const uint4*>(p.dout + rv * kDV + 8 * (tid & 7));
+  }
+  if (D) {
+    const int64_t rd = row0 + min(tid >> 5, n - 1);
+    s.d = *reinterpret_cast<const uint32_t*>(p.dout + rd * kDV + 2 * (tid & 31));
   }
   if (G) {
     const int u = (tid + 256) & (kNT - 1);
@@ -509,47 +512,32 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
           }
         }
         __syncthreads();
-        // g' = [dout / den | -(dout . num) / den^2 | 0]: eight threads per token, eight columns each
-        if (tid < kT * 8) {
-          const int i = tid >> 3, e0 = 8 * (tid & 7);
-          f32x4 n0 = kZero4, n1 = kZero4;
-          float den = 0.f;
+        // g' = [dout / den | -(dout . num) / den^2 | 0]: 32 threads per token (every wave), two columns each
+        {
+          static_assert(kNT == kT * 32 && kDV == 64, "32 threads per token, two columns each");
+          const int i = tid >> 5, e0 = 2 * (tid & 31);
+          float n0 = 0.f, n1 = 0.f, den = 0.f;
 #pragma unroll
           for (int ww = 0; ww < kW; ++ww) {
             const float* pr = P + (ww * kT + i) * kLP;
-            n0 += *reinterpret_cast<const f32x4*>(pr + e0);
-            n1 += *reinterpret_cast<const f32x4*>(pr + e0 + 4);
+            const float2 x = *reinterpret_cast<const float2*>(pr + e0);
+            n0 += x.x;
+            n1 += x.y;
             den += pr[kDV];
           }
-          const uint4 dr = i < n ? ax.d : make_uint4(0, 0, 0, 0);
-          const uint32_t dw[4] = {dr.x, dr.y, dr.z, dr.w};
-          float dn[8];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            dn[2 * t] = __uint_as_float(dw[t] << 16);
-            dn[2 * t + 1] = __uint_as_float(dw[t] & 0xFFFF0000u);
-          }
-          float dot = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) dot = fmaf(dn[t], n0[t], fmaf(dn[4 + t], n1[t], dot));
-          dot = sum_lanes8(dot);
+          const uint32_t dw = i < n ? ax.d : 0u;
+          const float d0 = __uint_as_float(dw << 16), d1 = __uint_as_float(dw & 0xFFFF0000u);
+          float dot = sum_lanes16(fmaf(d0, n0, d1 * n1));
+          dot += __shfl_xor(dot, 16, 64);  // the token's other 16 lanes
           if (i < n) {
             const float inv = __builtin_amdgcn_rcpf(den);  // v_rcp_f32, within 1 ulp
             float* gr = p.g + (row0 + i) * kE;
-            f32x4 g0, g1;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              g0[t] = dn[t] * inv;
-              g1[t] = dn[4 + t] * inv;
-            }
-            *reinterpret_cast<f32x4*>(gr + e0) = g0;
-            *reinterpret_cast<f32x4*>(gr + e0 + 4) = g1;
-            if ((tid & 7) == 0) {
-              const f32x4 hz = {-dot * inv * inv, 0.f, 0.f, 0.f};
-              *reinterpret_cast<f32x4*>(gr + kDV) = hz;
-              *reinterpret_cast<f32x4*>(gr + kDV + 4) = kZero4;
-              *reinterpret_cast<f32x4*>(gr + kDV + 8) = kZero4;
-              *reinterpret_cast<f32x4*>(gr + kDV + 12) = kZero4;
+            *reinterpret_cast<float2*>(gr + e0) = make_float2(d0 * inv, d1 * inv);
+            const int q = tid & 31;
+            if (q < (kE - kDV) / 4) {  // h and the zero columns, 16 bytes per thread
+              f32x4 hz = kZero4;
+              if (q == 0) hz[0] = -dot * inv * inv;
+              *reinterpret_cast<f32x4*>(gr + kDV + 4 * q) = hz;
             }
           }
         }
