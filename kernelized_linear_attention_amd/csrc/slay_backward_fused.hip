@@ -169,22 +169,22 @@ struct XRows {
   float inv, lg;
 };
 
-// Global inputs of one 16-token step.  The q and k rows are issued one step
-// ahead of their use; the v, dout and g' pieces at the top of their own step,
-// ahead of the feature map that runs before they are staged.  Rows past the
-// step's n read its last row (an unconditional load: a select between
-// addresses would go through a private zero copy) and are zeroed where used.
+// Global inputs of one 16-token step, all issued one step ahead of their
+// use into the registers the step has just consumed: its q, k rows (read by
+// the feature map) and the v and g' pieces (staged in LDS at the top of the
+// step, before the next step's loads reuse their registers).  dout is
+// loaded at the top of its own step: it is read only after the step's two
+// barriers.  Rows past the step's n read its last row (an unconditional
+// load: a select between addresses would go through a private zero copy)
+// and are zeroed where used.
 struct StepIn {
   uint4 qa, qb, ka, kb;  // rows t0 + c of q and k: columns 8g .. and 32 + 8g ..
-};
-struct StepAux {
   uint4 v;               // threads < 128: v row t0 + tid/8, columns 8 (tid % 8) ..
-  uint32_t d;            // every thread: dout row t0 + tid/32, columns 2(tid%32), 2(tid%32) + 1
   f32x4 gp;              // staging thread u = (tid + 256) % 512 < 320: g' row t0 + u/20, columns 4 (u % 20) ..
 };
 
-template <bool Q, bool K>
-__device__ __forceinline__ void load_step(StepIn& s, const PbParams& p, int64_t row0, int n, int g, int c) {
+template <bool Q, bool K, bool V, bool G>
+__device__ __forceinline__ void load_step(StepIn& s, const PbParams& p, int64_t row0, int n, int g, int c, int tid) {
   const int64_t rx = row0 + min(c, n - 1);
   if (Q) {
     s.qa = *reinterpret_cast<const uint4*>(p.q + rx * kDV + 8 * g);
@@ -194,18 +194,9 @@ __device__ __forceinline__ void load_step(StepIn& s, const PbParams& p, int64_t 
     s.ka = *reinterpret_cast<const uint4*>(p.k + rx * kDV + 8 * g);
     s.kb = *reinterpret_cast<const uint4*>(p.k + rx * kDV + 32 + 8 * g);
   }
-}
-
-template <bool D, bool G>
-__device__ __forceinline__ StepAux load_aux(const PbParams& p, int64_t row0, int n, int tid) {
-  StepAux s;
-  if (tid < kT * 8) {
+  if (V && tid < kT * 8) {
     const int64_t rv = row0 + min(tid >> 3, n - 1);
     s.v = *reinterpret_cast<const uint4*>(p.v + rv * kDV + 8 * (tid & 7));
-  }
-  if (D) {
-    const int64_t rd = row0 + min(tid >> 5, n - 1);
-    s.d = *reinterpret_cast<const uint32_t*>(p.dout + rd * kDV + 2 * (tid & 31));
   }
   if (G) {
     const int u = (tid + 256) & (kNT - 1);
@@ -214,7 +205,12 @@ __device__ __forceinline__ StepAux load_aux(const PbParams& p, int64_t row0, int
       s.gp = *reinterpret_cast<const f32x4*>(p.g + rg * kE + 4 * (u % (kE / 4)));
     }
   }
-  return s;
+}
+
+// every thread: dout row t0 + tid/32, columns 2(tid%32), 2(tid%32) + 1
+__device__ __forceinline__ uint32_t load_dout(const PbParams& p, int64_t row0, int n, int tid) {
+  const int64_t rd = row0 + min(tid >> 5, n - 1);
+  return *reinterpret_cast<const uint32_t*>(p.dout + rd * kDV + 2 * (tid & 31));
 }
 
 __device__ __forceinline__ XRows finish_x(uint4 a, uint4 b, bool valid) {
@@ -406,18 +402,17 @@ __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
     for (int eb = 0; eb < kNE; ++eb) S[j][eb] = kZero4;
   walk_steps<false>(
       t_begin, t_end,
-      [&](StepIn& in, int64_t t0, int n) { load_step<false, true>(in, p, h * p.L + t0, n, g, c); },
+      [&](StepIn& in, int64_t t0, int n) { load_step<false, true, true, false>(in, p, h * p.L + t0, n, g, c, tid); },
       [&](StepIn& in, int64_t t0, int n, int step, auto prefetch) {
-        const StepAux ax = load_aux<false, false>(p, h * p.L + t0, n, tid);
         const XRows xk = finish_x(in.ka, in.kb, c < n);
+        // double-buffered VT: the previous step's readers use the other buffer, and a
+        // buffer is written again only after every wave has passed the next step's barrier
+        uint16_t* VT = VT2[step & 1];
+        stage_v(in.v, n, nullptr, VT, tid);
         prefetch();
         f32x4 kt[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) kt[j] = phi_tok(P, xk, j, g);
-        // double-buffered VT: the previous step's readers use the other buffer, and a
-        // buffer is written again only after every wave has passed the next step's barrier
-        uint16_t* VT = VT2[step & 1];
-        stage_v(ax.v, n, nullptr, VT, tid);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -457,22 +452,22 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
     for (int eb = 0; eb < kNE; ++eb) S[j][eb] = load_fe(item, 2 * w + j, eb, lane);
   walk_steps<false>(
       t_begin, t_end,
-      [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
+      [&](StepIn& in, int64_t t0, int n) { load_step<true, true, true, false>(in, p, h * p.L + t0, n, g, c, tid); },
       [&](StepIn& in, int64_t t0, int n, int step, auto prefetch) {
         const int64_t row0 = h * p.L + t0;
-        const StepAux ax = load_aux<true, false>(p, row0, n, tid);
+        const uint32_t dout2 = load_dout(p, row0, n, tid);
         const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
+        // double-buffered VT and P: the previous step's readers use the other buffers, and a
+        // buffer is written again only after every wave has passed the next step's barriers
+        uint16_t* VT = VT2[step & 1];
+        float* P = P2[step & 1];
+        stage_v(in.v, n, nullptr, VT, tid);
         prefetch();
         const f32x4 qa = phi_feat(Pj, xq, 0), qb = phi_feat(Pj, xq, 1);
         const f32x4 ka = phi_feat(Pj, xk, 0), kb = phi_feat(Pj, xk, 1);
         f32x4 kt[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) kt[j] = phi_tok(Pj, xk, j, g);
-        // double-buffered VT and P: the previous step's readers use the other buffers, and a
-        // buffer is written again only after every wave has passed the next step's barriers
-        uint16_t* VT = VT2[step & 1];
-        float* P = P2[step & 1];
-        stage_v(ax.v, n, nullptr, VT, tid);
         __syncthreads();
         // this wave's part of A^T[j][i] = sum_f phi(K_j)_f phi(Q_i)_f over its features (split phi), masked j <= i
         uint2 qh0, ql0, qh1, ql1, kh0, kl0, kh1, kl1;
@@ -525,7 +520,7 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
             n1 += x.y;
             den += pr[kDV];
           }
-          const uint32_t dw = i < n ? ax.d : 0u;
+          const uint32_t dw = i < n ? dout2 : 0u;
           const float d0 = __uint_as_float(dw << 16), d1 = __uint_as_float(dw & 0xFFFF0000u);
           float dot = sum_lanes16(fmaf(d0, n0, d1 * n1));
           dot += __shfl_xor(dot, 16, 64);  // the token's other 16 lanes
@@ -572,11 +567,16 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
     }
   walk_steps<false>(
       t_begin, t_end,
-      [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
+      [&](StepIn& in, int64_t t0, int n) { load_step<true, true, true, true>(in, p, h * p.L + t0, n, g, c, tid); },
       [&](StepIn& in, int64_t t0, int n, int step, auto prefetch) {
         const int64_t row0 = h * p.L + t0;
-        const StepAux ax = load_aux<false, true>(p, row0, n, tid);
         const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
+        // double-buffered tiles: the previous step's readers use the other buffers, and a
+        // buffer is written again only after every wave has passed the next step's barrier
+        const int sb = step & 1;
+        uint16_t *VT = VT2[sb], *VR = VR2[sb], *GRh = GRh2[sb], *GRl = GRl2[sb], *GTh = GTh2[sb], *GTl = GTl2[sb];
+        stage_v(in.v, n, VR, VT, tid);
+        stage_g(in.gp, n, GRh, GRl, GTh, GTl, tid);
         prefetch();
         bf16x8 qt[2], kt[2];  // split phi of the step's tokens, four per lane
 #pragma unroll
@@ -584,12 +584,6 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
           qt[j] = hilo(phi_tok(P, xq, j, g));
           kt[j] = hilo(phi_tok(P, xk, j, g));
         }
-        // double-buffered tiles: the previous step's readers use the other buffers, and a
-        // buffer is written again only after every wave has passed the next step's barrier
-        const int sb = step & 1;
-        uint16_t *VT = VT2[sb], *VR = VR2[sb], *GRh = GRh2[sb], *GRl = GRl2[sb], *GTh = GTh2[sb], *GTl = GTl2[sb];
-        stage_v(ax.v, n, VR, VT, tid);
-        stage_g(ax.gp, n, GRh, GRl, GTh, GTl, tid);
         __syncthreads();
         // D^T[j][i] = v'_j . g'_i (split g'), masked j <= i < n; every wave forms it (lane: j = 4g + r, i = c)
         f32x4 dt = kZero4;
@@ -677,25 +671,24 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
     }
   walk_steps<true>(
       t_begin, t_end,
-      [&](StepIn& in, int64_t t0, int n) { load_step<true, true>(in, p, h * p.L + t0, n, g, c); },
+      [&](StepIn& in, int64_t t0, int n) { load_step<true, true, true, true>(in, p, h * p.L + t0, n, g, c, tid); },
       [&](StepIn& in, int64_t t0, int n, int step, auto prefetch) {
         const int64_t row0 = h * p.L + t0;
-        const StepAux ax = load_aux<false, true>(p, row0, n, tid);
         const XRows xq = finish_x(in.qa, in.qb, c < n), xk = finish_x(in.ka, in.kb, c < n);
-        prefetch();
-        const f32x4 qa = phi_feat(Pj, xq, 0), qb = phi_feat(Pj, xq, 1);
-        const f32x4 ka = phi_feat(Pj, xk, 0), kb = phi_feat(Pj, xk, 1);
-        bf16x8 qt[2];  // split phi(q) of the step's tokens, four per lane
-#pragma unroll
-        for (int j = 0; j < 2; ++j) qt[j] = hilo(phi_tok(Pj, xq, j, g));
         // double-buffered tiles and partials: the previous step's readers use the other
         // buffers, and a buffer is written again only after every wave has passed the next
         // step's barriers
         const int sb = step & 1;
         uint16_t *VT = VT2[sb], *VR = VR2[sb], *GRh = GRh2[sb], *GRl = GRl2[sb], *GTh = GTh2[sb], *GTl = GTl2[sb];
         float* P = P2[sb];
-        stage_v(ax.v, n, VR, VT, tid);
-        stage_g(ax.gp, n, GRh, GRl, GTh, GTl, tid);
+        stage_v(in.v, n, VR, VT, tid);
+        stage_g(in.gp, n, GRh, GRl, GTh, GTl, tid);
+        prefetch();
+        const f32x4 qa = phi_feat(Pj, xq, 0), qb = phi_feat(Pj, xq, 1);
+        const f32x4 ka = phi_feat(Pj, xk, 0), kb = phi_feat(Pj, xk, 1);
+        bf16x8 qt[2];  // split phi(q) of the step's tokens, four per lane
+#pragma unroll
+        for (int j = 0; j < 2; ++j) qt[j] = hilo(phi_tok(Pj, xq, j, g));
         __syncthreads();
         // this wave's part of A[i][j] over its features, masked i >= j (lane: i = 4g + r, j = c)
         f32x4 aw = mfma_bf16(pk_pair(qa, qb), pk_pair(ka, kb), kZero4);
