@@ -784,9 +784,9 @@ struct VjpK {
   static constexpr int NW = NF / 2, NT = NW * 64;
   static constexpr int RT = 32, NRB = RT / 16;  // rows per tile
   static constexpr int LX = D + 8, LR = D + 4;
-  // x tile, per-wave partials, 1/|x| per row (negative where |x| is clamped), and each
-  // thread's own dphi pieces ([piece][thread], 8 bytes each)
-  static constexpr int oX = 0, oR = RT * LX * 2, oI = oR + NW * RT * LR * 4, oD = oI + RT * 4;
+  // x tiles and 1/|x| per row (negative where |x| is clamped), both double-buffered by tile
+  // parity; per-wave partials; each thread's own dphi pieces ([piece][thread], 8 bytes each)
+  static constexpr int oX = 0, oR = 2 * RT * LX * 2, oI = oR + NW * RT * LR * 4, oD = oI + 2 * RT * 4;
   static constexpr int kLds = oD + NRB * 2 * NT * 8;
   static_assert(NT >= RT * 8 && NT == RT * 16, "one x piece per thread (some idle), one output piece per thread");
 };
@@ -844,9 +844,7 @@ __device__ __forceinline__ void vjp_load(const uint16_t* __restrict__ x, const u
 template <class K>
 __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   extern __shared__ __align__(16) char lds_raw[];
-  uint16_t* sX = reinterpret_cast<uint16_t*>(lds_raw + K::oX);
   float* sR = reinterpret_cast<float*>(lds_raw + K::oR);
-  float* sI = reinterpret_cast<float*>(lds_raw + K::oI);
   uint2* sD = reinterpret_cast<uint2*>(lds_raw + K::oD);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -872,7 +870,13 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   auto load_tile = [&](int64_t t, VjpPref<K>& dst) {
     vjp_load<K>(x, dphi, p.n_rows, t * K::RT, tid, wave, g, c16, dst);
   };
-  auto tile_body = [&](int64_t tile, VjpPref<K>& pf) {
+  auto tile_body = [&](int64_t tile, VjpPref<K>& pf, int buf) {
+    // sX and sI of this tile's parity: their last readers (the tile before the previous one)
+    // are done once every thread has passed the previous tile's staging barrier, which it
+    // reaches after its own reads of them; sR is written only after this tile's staging
+    // barrier, and sD is read back only by the thread that wrote it
+    uint16_t* sX = reinterpret_cast<uint16_t*>(lds_raw + K::oX) + buf * K::RT * K::LX;
+    float* sI = reinterpret_cast<float*>(lds_raw + K::oI) + buf * K::RT;
     const int64_t r0 = tile * K::RT;
     const int tset = (int)((r0 / p.rows_per_head) % p.n_draw_sets);  // a tile never spans two draw sets
     if (tset != set && r0 < p.n_rows) {  // this wave's rows of P, as both operands
@@ -905,7 +909,6 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       }
       wait_vmem();  // here, where the reload is rare, rather than at the first use
     }
-    __syncthreads();  // the previous tile's readers of sX, sR and sD are done
 #pragma unroll
     for (int rb = 0; rb < K::NRB; ++rb)
 #pragma unroll
@@ -990,8 +993,8 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   load_tile(blockIdx.x, pf0);
   load_tile(blockIdx.x + gs, pf1);
   for (int64_t tile = blockIdx.x; tile < n_tiles; tile += 2 * gs) {
-    tile_body(tile, pf0);
-    tile_body(tile + gs, pf1);  // past the last tile: zeros in, nothing out
+    tile_body(tile, pf0, 0);
+    tile_body(tile + gs, pf1, 1);  // past the last tile: zeros in, nothing out
   }
 }
 
