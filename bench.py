@@ -130,7 +130,7 @@ TRAFFIC_UNITS = {
     # description); the counters of each unit come from runs of that part alone
     "fused_fwd_h16_l16k_bf16": ("fwd", (("pass1s", 1), ("scan4_kernel", 1), ("pass2s", 1)),
                                 "one causal forward, B1 H16 L16384 bf16 (segment states + scan + main pass)"),
-    "fused_fwd_b4h8_l2k_bf16": ("small", (("pass1_kernel", 1), ("scan4_kernel", 1), ("pass2s", 1)),
+    "fused_fwd_b4h8_l2k_bf16": ("small", (("pass1s", 1), ("scan4_kernel", 1), ("pass2s", 1)),
                                 "one causal forward, B4 H8 L2048 F = 96 bf16 (segment states + scan + main pass)"),
     "featmap_h16_l16k_bf16": ("featmap", (("featmap_kernel<unsigned short, unsigned short", 1),),
                               "one feature-map launch over 262144 bf16 rows, F = 256"),
@@ -211,7 +211,7 @@ COUNTER_UNITS = {
     # bench --only part: (summary name, kernel-name fragments, description)
     "fwd": ("fused_fwd_h16_l16k_bf16", ("pass1s", "scan4_kernel", "pass2s"),
             "causal forward, B1 H16 L16384 d=dv=64 F=256 bf16"),
-    "small": ("fused_fwd_b4h8_l2k_bf16", ("pass1_kernel", "scan4_kernel", "pass2s"),
+    "small": ("fused_fwd_b4h8_l2k_bf16", ("pass1s", "scan4_kernel", "pass2s"),
               "causal forward, B4 H8 L2048 d=dv=64 F=96 bf16"),
     "featmap": ("featmap_h16_l16k_bf16", ("featmap_kernel",), "feature map of 262144 bf16 rows, F = 256"),
     "backward": ("backward_h16_l16k_bf16", ("pb_state", "scan4_kernel", "pb_g", "pb_dq", "pb_dk", "vjp"),
