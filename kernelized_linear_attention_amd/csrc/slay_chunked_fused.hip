@@ -1242,6 +1242,15 @@ __global__ __launch_bounds__(K::NT, 2) void ncout_kernel(Params p) {
   }
 }
 
+// The non-causal output pass reads phi(q) and the bf16 S'^T copy only as
+// 16-byte MFMA operands (16 rows per access), which run without bank
+// conflicts at a row stride of 32 (mod 64) bytes: F + 16 elements.  The
+// causal passes keep F + 8, with which their mix of accesses measured faster.
+template <class K>
+struct NcCfg : K {
+  static constexpr int LDF = K::F + 16;
+};
+
 template <class K>
 constexpr int ncout_lds() {
   return 2 * K::C * K::LDX * 2 + 4 * K::C * 4 + 2 * K::C * K::LDF * 2 + K::VROWS * K::LDF * 2;
@@ -1457,11 +1466,12 @@ hipError_t launch_nc_t(const ChunkedArgs& a, hipStream_t s) {
   if (a.Lq == 0) return hipSuccess;
   p.n_qseg = segments_of<K>(a.n_heads, a.Lq);
   p.qseg_len = seg_len_for<K>(a.n_heads, a.Lq);
-  constexpr int lds = ncout_lds<K>();
+  using KN = NcCfg<K>;
+  constexpr int lds = ncout_lds<KN>();
   static_assert(lds <= 160 * 1024, "LDS budget");
-  e = set_max_lds(reinterpret_cast<const void*>(&ncout_kernel<K>), lds);
+  e = set_max_lds(reinterpret_cast<const void*>(&ncout_kernel<KN>), lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ncout_kernel<K>, dim3((unsigned)(a.n_heads * p.n_qseg)), dim3(K::NT), lds, s, p);
+  hipLaunchKernelGGL(ncout_kernel<KN>, dim3((unsigned)(a.n_heads * p.n_qseg)), dim3(KN::NT), lds, s, p);
   return hipGetLastError();
 }
 
