@@ -1004,7 +1004,7 @@ using V256 = VjpK<16>;
 // Segments of the precise kernels: about PB_WG workgroups over all heads, whole
 // 16-token steps, at least 64 tokens each.
 #ifndef PB_WG
-#define PB_WG 512
+#define PB_WG 256
 #endif
 int64_t pb_seg_len(int64_t n_heads, int64_t L) {
   const int64_t want = (L * n_heads + PB_WG - 1) / PB_WG;

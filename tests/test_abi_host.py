@@ -240,11 +240,11 @@ def test_backward_validation_and_workspace(lib):
         assert _bwd(lib, p, **{name: None}) == E_INV, name
         assert _bwd(lib, p, **{name: FAKE + 4}) == E_INV, name
     assert _bwd(lib, p) == E_INV and b"workspace too small" in lib.slay_last_error()
-    # MFMA path: one fp32 state per (head, 512-token segment: about 512 segments in all), an fp32
+    # MFMA path: one fp32 state per (head, 1024-token segment: about 256 segments in all), an fp32
     # 80-column g' per token and bf16 dphi(q), dphi(k) (phi itself is recomputed on chip)
     n = lib.slay_attn_chunked_bwd_workspace_size(ctypes.byref(p), 1, 16, 16384, 64, 64, _lib.SLAY_BF16)
     rows = 16 * 16384
-    assert n == 4 * 16 * 32 * 256 * 80 + 4 * rows * 80 + 2 * 2 * rows * 256
+    assert n == 4 * 16 * 16 * 256 * 80 + 4 * rows * 80 + 2 * 2 * rows * 256
     # general path (fp32): fp32 phi(q), phi(k), dphi(q), dphi(k), g' and one state per chunk
     p32 = _params(R=2, m=16, dt=_lib.SLAY_F32)
     n32 = lib.slay_attn_chunked_bwd_workspace_size(ctypes.byref(p32), 1, 2, 100, 64, 32, _lib.SLAY_F32)
