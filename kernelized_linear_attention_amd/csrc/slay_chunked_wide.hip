@@ -491,9 +491,10 @@ __global__ __launch_bounds__(K::NT) void wout_kernel(WParams p) {
   }
 }
 
-// Segments: about two workgroups per CU over the whole batch, whole chunks each.
+// Segments: about one workgroup per CU over the whole batch (the output and
+// state passes hold one workgroup per CU), whole chunks each.
 int64_t w_seg_len(int64_t n_heads, int64_t L) {
-  constexpr int64_t kTargetGroups = 512;
+  constexpr int64_t kTargetGroups = 256;
   int64_t s = (n_heads * L + kTargetGroups - 1) / kTargetGroups;
   s = (s + 31) / 32 * 32;
   return s < 32 ? 32 : s;

@@ -117,13 +117,13 @@ def test_workspace_sizes(lib):
 def test_wide_path_workspace(lib):
     """bf16 shapes the fused kernels do not cover take the wide path: phi(q) and
     phi(k) in bf16 (256-byte aligned each) plus one fp32 state of F x (dv+16)
-    per (head, segment), segments of whole 32-token chunks, about 512 of them
+    per (head, segment), segments of whole 32-token chunks, about 256 of them
     over the batch."""
     r256 = lambda x: (x + 255) // 256 * 256
     p = _params(d=128, R=4, m=128)
-    # B1 H8 L131072 d=dv=128 F=512, chunk 128: segments of 2048 tokens, 64 per head
+    # B1 H8 L131072 d=dv=128 F=512, chunk 128: segments of 4096 tokens, 32 per head
     n = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p), 1, 8, 131072, 128, 128, _lib.SLAY_BF16)
-    assert n == 2 * r256(8 * 131072 * 512 * 2) + 4 * 8 * 64 * 512 * 144
+    assert n == 2 * r256(8 * 131072 * 512 * 2) + 4 * 8 * 32 * 512 * 144
     # a short ragged sequence: segments of one chunk (32 tokens), ceil(1000 / 32) = 32 of them
     n = lib.slay_attn_chunked_fwd_workspace_size(ctypes.byref(p), 1, 2, 1000, 128, 32, _lib.SLAY_BF16)
     assert n == 2 * r256(2 * 1000 * 512 * 2) + 4 * 2 * 32 * 512 * 144
