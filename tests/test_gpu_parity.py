@@ -61,6 +61,7 @@ def test_featmap_parity(lib, orc, name, out):
 
 @pytest.mark.parametrize("base,d,R,m,out", [
     ("h16_l16k_bf16", 64, 4, 64, "bf16"),        # bf16 -> bf16, d = 64 (the forward's and backward's map)
+    ("h16_l16k_bf16", 64, 5, 32, "bf16"),        # F = 160: the second 128-feature slice is partial
     ("h16_l16k_bf16", 32, 4, 64, "bf16"),        # d = 32, four feature blocks per wave
     ("h8_l128k_d128_bf16", 128, 4, 128, "bf16"),  # d = 128, F = 512
     ("h16_l16k_bf16", 64, 4, 64, "f32"),         # bf16 -> fp32
