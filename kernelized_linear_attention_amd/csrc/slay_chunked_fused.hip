@@ -1072,7 +1072,7 @@ __global__ __launch_bounds__(K::NTW) void pass2s_kernel(Params p) {
       phase_k<K, true, true>(sK(bn), sInv(bn, 2), sInv(bn, 3), sPk(bn), fb0, lane, pa, pg, c1, c0, kf, sV(c % 3), vo,
                              kf, st);
       phase_q<K>(sQ(bn), sInv(bn, 0), sInv(bn, 1), sPq(bn), wave, lane, pa, pg, c1, c0);
-      mfma_valu_interleave<K::NTB * K::FBW * K::NKS * 4 + K::NTS * K::NE * K::FBW, 4>();
+      mfma_valu_interleave<K::NTB * K::FBW * K::NKS * 4 + K::NTS * K::NE * K::FBW, 3>();
       interval_b(c);
     }
     {  // [A] of the last chunk: its state update only
