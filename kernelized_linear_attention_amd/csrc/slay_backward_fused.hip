@@ -51,6 +51,7 @@
 //      summed through LDS), then U += phi(Q)^T G';
 //   6. vjp_kernel maps dphi back to dq and dk.
 #include <algorithm>
+#include <type_traits>
 
 #include "slay_device.hpp"
 #include "slay_internal.hpp"
@@ -96,11 +97,6 @@ __device__ __forceinline__ bf16x8 hilo(const f32x4& x) {
   split4(x, h, l);
   return cat(h, l);
 }
-// the hi parts of a split operand alone (k-slots 4-7 zero)
-__device__ __forceinline__ bf16x8 hi_only(const bf16x8& x) {
-  const uint4 u = __builtin_bit_cast(uint4, x);
-  return __builtin_bit_cast(bf16x8, make_uint4(u.x, u.y, 0u, 0u));
-}
 
 // ---------------------------------------------------------------------------
 // Precise segment kernels.
@@ -111,7 +107,10 @@ constexpr int kNE = kE / 16;
 constexpr int kDV = 64;
 constexpr int kW = 8, kNT = kW * 64;  // waves; wave w owns feature blocks 2w, 2w + 1
 // LDS row strides in elements (odd multiples of 16 bytes)
-constexpr int kLT = kT + 4;        // [e][t] tiles: 40-byte rows keep the staging stores and 8-byte column reads apart in banks
+// [e][t] tiles hold each group of four tokens twice (v', g' hi) or once and then four zeros (g' lo), so that
+// one 16-byte read gives a lane its whole operand: four tokens against the split other side's hi and lo parts
+// (or, with the zeros, against its hi parts alone).  96-byte rows keep the 16-byte reads apart in banks.
+constexpr int kLD = 48;
 constexpr int kLR = kE + 8;        // [t][e] tiles
 constexpr int kLP = kE + 8;        // fp32 partials [w][t][e] (row stride 32 mod 64 bytes: 16-byte accesses in one pass)
 constexpr int kLPV = kDV + 8;
@@ -180,37 +179,51 @@ struct XRows {
 struct StepIn {
   uint4 qa, qb, ka, kb;  // rows t0 + c of q and k: columns 8g .. and 32 + 8g ..
   uint4 v;               // threads < 128: v row t0 + tid/8, columns 8 (tid % 8) ..
-  f32x4 gp;              // staging thread u = (tid + 256) % 512 < 320: g' row t0 + u/20, columns 4 (u % 20) ..
+  f32x4 gp;              // staging thread u = (tid + 256) % 512 < 320: the g' piece of g_piece(u)
 };
+
+// g' pieces: staging thread u < 320 holds row t = 2 (u / 40) + u % 2, columns 4 ((u % 40) / 2) ..,
+// so that lanes u and u^1 hold the same columns of a token pair
+__device__ __forceinline__ void g_piece(int u, int& t, int& e0) {
+  t = 2 * (u / (kE / 2)) + (u & 1);
+  e0 = 4 * ((u % (kE / 2)) >> 1);
+}
+
+// Global accesses of a step: a wave-uniform row base (scalar registers) plus a 32-bit lane offset in
+// elements, so no lane holds a 64-bit address.
+template <class T, class E>
+__device__ __forceinline__ T& at_row(E* base, int64_t row0, int row_elems, uint32_t off) {
+  using B = typename std::conditional<std::is_const<E>::value, const char, char>::type;
+  B* b = reinterpret_cast<B*>(base + row0 * row_elems);
+  return *reinterpret_cast<T*>(b + off * (uint32_t)sizeof(E));
+}
 
 template <bool Q, bool K, bool V, bool G>
 __device__ __forceinline__ void load_step(StepIn& s, const PbParams& p, int64_t row0, int n, int g, int c, int tid) {
-  const int64_t rx = row0 + min(c, n - 1);
+  const uint32_t rx = (uint32_t)min(c, n - 1) * kDV;
   if (Q) {
-    s.qa = *reinterpret_cast<const uint4*>(p.q + rx * kDV + 8 * g);
-    s.qb = *reinterpret_cast<const uint4*>(p.q + rx * kDV + 32 + 8 * g);
+    s.qa = at_row<const uint4>(p.q, row0, kDV, rx + 8 * g);
+    s.qb = at_row<const uint4>(p.q, row0, kDV, rx + 32 + 8 * g);
   }
   if (K) {
-    s.ka = *reinterpret_cast<const uint4*>(p.k + rx * kDV + 8 * g);
-    s.kb = *reinterpret_cast<const uint4*>(p.k + rx * kDV + 32 + 8 * g);
+    s.ka = at_row<const uint4>(p.k, row0, kDV, rx + 8 * g);
+    s.kb = at_row<const uint4>(p.k, row0, kDV, rx + 32 + 8 * g);
   }
-  if (V && tid < kT * 8) {
-    const int64_t rv = row0 + min(tid >> 3, n - 1);
-    s.v = *reinterpret_cast<const uint4*>(p.v + rv * kDV + 8 * (tid & 7));
-  }
+  if (V && tid < kT * 8)
+    s.v = at_row<const uint4>(p.v, row0, kDV, (uint32_t)min(tid >> 3, n - 1) * kDV + 8 * (tid & 7));
   if (G) {
     const int u = (tid + 256) & (kNT - 1);
     if (u < kT * (kE / 4)) {
-      const int64_t rg = row0 + min(u / (kE / 4), n - 1);
-      s.gp = *reinterpret_cast<const f32x4*>(p.g + rg * kE + 4 * (u % (kE / 4)));
+      int t, e0;
+      g_piece(u, t, e0);
+      s.gp = at_row<const f32x4>(p.g, row0, kE, (uint32_t)min(t, n - 1) * kE + e0);
     }
   }
 }
 
 // every thread: dout row t0 + tid/32, columns 2(tid%32), 2(tid%32) + 1
 __device__ __forceinline__ uint32_t load_dout(const PbParams& p, int64_t row0, int n, int tid) {
-  const int64_t rd = row0 + min(tid >> 5, n - 1);
-  return *reinterpret_cast<const uint32_t*>(p.dout + rd * kDV + 2 * (tid & 31));
+  return at_row<const uint32_t>(p.dout, row0, kDV, (uint32_t)min(tid >> 5, n - 1) * kDV + 2 * (tid & 31));
 }
 
 __device__ __forceinline__ XRows finish_x(uint4 a, uint4 b, bool valid) {
@@ -227,7 +240,7 @@ __device__ __forceinline__ XRows finish_x(uint4 a, uint4 b, bool valid) {
   }
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
-  X.inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+  X.inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));  // 1 / max(|x|, 1e-12), within 1 ulp
   X.lg = 2.0f * __builtin_amdgcn_logf(X.inv);  // log2(inv^2)
   return X;
 }
@@ -260,15 +273,26 @@ __device__ __forceinline__ f32x4 phi_tok(const Proj& P, const XRows& X, int j, i
   return o;
 }
 
-// V' = [v | 1 | 0] of the step's tokens (zero rows past n) as [t][e] rows and [e][t] columns.
+// position of token t in a row of an [e][t] tile (the first of its two places)
+__device__ __forceinline__ int tok_at(int t) { return 8 * (t >> 2) + (t & 3); }
+
+// Zero n bytes of LDS (a multiple of 16), every thread taking part: the [e][t] tiles' parts
+// that never change (the zero columns of V', the zero halves of the g' lo tiles) are set once.
+__device__ __forceinline__ void zero_lds(void* p, int n, int tid) {
+  for (int i = tid; i < n / 16; i += kNT) static_cast<uint4*>(p)[i] = make_uint4(0, 0, 0, 0);
+}
+
+// V' = [v | 1 | 0] of the step's tokens (zero rows past n) as [t][e] rows and [e][t] columns
+// (either may be null; the zero columns of the latter are set once, before the walk).
 // The columns are written as token pairs: lanes t and t^1 (lane ^ 8) trade their
 // eight values, and the even token's lane writes four columns, the odd one's the
-// other four, one 4-byte store each.
+// other four, 4-byte stores into both places of the pair.
 __device__ __forceinline__ void stage_v(uint4 x, int n, uint16_t* VR, uint16_t* VT, int tid) {
   if (tid < kT * 8) {
     const int t = tid >> 3, e0 = 8 * (tid & 7);
     if (t >= n) x = make_uint4(0, 0, 0, 0);
     if (VR) *reinterpret_cast<uint4*>(VR + t * kLR + e0) = x;
+    if (!VT) return;
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};  // columns (e0 + 2i, e0 + 2i + 1) of token t
     uint32_t o[4];                                // the same of token t ^ 1
 #pragma unroll
@@ -280,9 +304,11 @@ __device__ __forceinline__ void stage_v(uint4 x, int n, uint16_t* VR, uint16_t* 
       const int sh = 16 * (r & 1);
       const uint32_t mine = (w[i] >> sh) & 0xFFFFu, other = (o[i] >> sh) & 0xFFFFu;
       const uint32_t pair = odd ? (other | (mine << 16)) : (mine | (other << 16));  // even token in the low half
-      *reinterpret_cast<uint32_t*>(VT + (e0 + 4 * (odd ? 1 : 0) + r) * kLT + (t & ~1)) = pair;
+      uint32_t* d = reinterpret_cast<uint32_t*>(VT + (e0 + 4 * (odd ? 1 : 0) + r) * kLD + tok_at(t & ~1));
+      d[0] = pair;
+      d[2] = pair;
     }
-  } else if (tid < kT * 8 + kT / 2) {  // the ones column and the zero columns, a token pair per thread
+  } else if (tid < kT * 8 + kT / 2) {  // the ones column, a token pair per thread
     const int t = 2 * (tid - kT * 8);
     const uint32_t one = (t < n ? 0x3F80u : 0u) | (t + 1 < n ? 0x3F800000u : 0u);
     if (VR) {
@@ -292,37 +318,53 @@ __device__ __forceinline__ void stage_v(uint4 x, int n, uint16_t* VR, uint16_t* 
         *reinterpret_cast<uint4*>(VR + (t + u) * kLR + kDV + 8) = make_uint4(0, 0, 0, 0);
       }
     }
-    *reinterpret_cast<uint32_t*>(VT + kDV * kLT + t) = one;
-#pragma unroll
-    for (int e = kDV + 1; e < kE; ++e) *reinterpret_cast<uint32_t*>(VT + e * kLT + t) = 0u;
+    if (VT) {
+      uint32_t* d = reinterpret_cast<uint32_t*>(VT + kDV * kLD + tok_at(t));
+      d[0] = one;
+      d[2] = one;
+    }
   }
 }
 
-// g' of the step's tokens split into hi and lo bf16, as [t][e] rows and [e][t] columns
+// g' of the step's tokens split into hi and lo bf16, as [t][e] rows and [e][t] columns (the
+// zero halves of the lo columns are set once, before the walk).  Like V', the columns are
+// written as token pairs: lanes u and u^1 hold tokens t and t^1 of the same four columns,
+// trade them, and the even token's lane writes two columns, the odd one's the other two.
 __device__ __forceinline__ void stage_g(f32x4 x, int n, uint16_t* GRh, uint16_t* GRl, uint16_t* GTh, uint16_t* GTl,
                                         int tid) {
   const int u = (tid + 256) & (kNT - 1);
   if (u < kT * (kE / 4)) {
-    const int t = u / (kE / 4), e0 = 4 * (u % (kE / 4));
+    int t, e0;
+    g_piece(u, t, e0);
     if (t >= n) x = kZero4;
     uint2 h, l;
     split4(x, h, l);
     *reinterpret_cast<uint2*>(GRh + t * kLR + e0) = h;
     *reinterpret_cast<uint2*>(GRl + t * kLR + e0) = l;
-    const uint32_t hw[2] = {h.x, h.y}, lw[2] = {l.x, l.y};
+    if (!GTh) return;
+    const bool odd = t & 1;
+    const uint32_t mh = odd ? h.y : h.x, ml = odd ? l.y : l.x;  // columns e0 + 2 odd, e0 + 2 odd + 1 of token t
+    const uint32_t oh = (uint32_t)__shfl_xor((int)(odd ? h.x : h.y), 1, 64);  // the same columns of token t ^ 1
+    const uint32_t ol = (uint32_t)__shfl_xor((int)(odd ? l.x : l.y), 1, 64);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      GTh[(e0 + 2 * i) * kLT + t] = (uint16_t)(hw[i] & 0xFFFFu);
-      GTh[(e0 + 2 * i + 1) * kLT + t] = (uint16_t)(hw[i] >> 16);
-      GTl[(e0 + 2 * i) * kLT + t] = (uint16_t)(lw[i] & 0xFFFFu);
-      GTl[(e0 + 2 * i + 1) * kLT + t] = (uint16_t)(lw[i] >> 16);
+    for (int k = 0; k < 2; ++k) {
+      const int sh = 16 * k;
+      const uint32_t ah = (mh >> sh) & 0xFFFFu, bh = (oh >> sh) & 0xFFFFu;
+      const uint32_t al = (ml >> sh) & 0xFFFFu, bl = (ol >> sh) & 0xFFFFu;
+      const uint32_t ph = odd ? (bh | (ah << 16)) : (ah | (bh << 16));  // even token in the low half
+      const uint32_t pl = odd ? (bl | (al << 16)) : (al | (bl << 16));
+      const int at = (e0 + 2 * (odd ? 1 : 0) + k) * kLD + tok_at(t & ~1);
+      uint32_t* dh = reinterpret_cast<uint32_t*>(GTh + at);
+      dh[0] = ph;
+      dh[2] = ph;
+      *reinterpret_cast<uint32_t*>(GTl + at) = pl;
     }
   }
 }
 
-// four consecutive tokens of column e of an [e][t] tile: the lane's k-slots 4g .. 4g+3
-__device__ __forceinline__ uint2 col4(const uint16_t* T, int e, int g) {
-  return *reinterpret_cast<const uint2*>(T + e * kLT + 4 * g);
+// the lane's operand from row e of an [e][t] tile: tokens 4g .. 4g+3, then the same again (or zeros)
+__device__ __forceinline__ bf16x8 col8(const uint16_t* T, int e, int g) {
+  return ld8(T + e * kLD + 8 * g);
 }
 // columns 16 e0 + 4g .. +3 and 16 e1 + 4g .. +3 of row r of a [t][e] tile (e1 < 0: zeros)
 __device__ __forceinline__ bf16x8 row4x2(const uint16_t* R, int r, int e0, int e1, int g) {
@@ -385,9 +427,11 @@ __device__ __forceinline__ void walk_steps(int64_t t_begin, int64_t t_end, LOAD 
 
 // (1) sum over each segment's keys (all segments but the last) of phi(k) v'^T, in the item order
 __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
-  __shared__ __align__(16) uint16_t VT2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t VT2[2][kE * kLD];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  zero_lds(VT2, sizeof(VT2), tid);
+  __syncthreads();
   const int n_items = p.n_seg - 1;
   const int64_t h = blockIdx.x / n_items;
   const int seg = (int)(blockIdx.x - h * n_items);
@@ -418,10 +462,7 @@ __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
         for (int j = 0; j < 2; ++j) {
           const bf16x8 a = hilo(kt[j]);
 #pragma unroll
-          for (int eb = 0; eb < kNE; ++eb) {
-            const uint2 v4 = col4(VT, 16 * eb + c, g);
-            S[j][eb] = mfma_bf16(a, cat(v4, v4), S[j][eb]);
-          }
+          for (int eb = 0; eb < kNE; ++eb) S[j][eb] = mfma_bf16(a, col8(VT, 16 * eb + c, g), S[j][eb]);
         }
       });
   float* item = item_ptr(p, h, seg);
@@ -434,10 +475,12 @@ __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
 // (2) numerators, denominators and g' of every token, with S' (the item: the state before the segment) in
 // accumulators
 __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
-  __shared__ __align__(16) uint16_t VT2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t VT2[2][kE * kLD];
   __shared__ __align__(16) float P2[2][kW * kT * kLP];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  zero_lds(VT2, sizeof(VT2), tid);
+  __syncthreads();
   const int64_t h = blockIdx.x / p.n_seg;
   const int seg = (int)(blockIdx.x - h * p.n_seg);
   const int64_t t_begin = seg * p.seg_len;
@@ -485,8 +528,7 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
         // num'^T[e][i] partial = V'^T A^T (this wave's A part) + S'^T phi(Q)^T over this wave's features
 #pragma unroll
         for (int eb = 0; eb < kNE; ++eb) {
-          const uint2 v4 = col4(VT, 16 * eb + c, g);
-          f32x4 acc = mfma_bf16(cat(v4, v4), atb, kZero4);
+          f32x4 acc = mfma_bf16(col8(VT, 16 * eb + c, g), atb, kZero4);
           uint2 s0h, s0l, s1h, s1l;
           split4(S[0][eb], s0h, s0l);
           split4(S[1][eb], s1h, s1l);
@@ -501,10 +543,7 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
         for (int j = 0; j < 2; ++j) {
           const bf16x8 a = hilo(kt[j]);
 #pragma unroll
-          for (int eb = 0; eb < kNE; ++eb) {
-            const uint2 v4 = col4(VT, 16 * eb + c, g);
-            S[j][eb] = mfma_bf16(a, cat(v4, v4), S[j][eb]);
-          }
+          for (int eb = 0; eb < kNE; ++eb) S[j][eb] = mfma_bf16(a, col8(VT, 16 * eb + c, g), S[j][eb]);
         }
         __syncthreads();
         // g' = [dout / den | -(dout . num) / den^2 | 0]: 32 threads per token (every wave), two columns each
@@ -526,7 +565,7 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
           dot += __shfl_xor(dot, 16, 64);  // the token's other 16 lanes
           if (i < n) {
             const float inv = __builtin_amdgcn_rcpf(den);  // v_rcp_f32, within 1 ulp
-            float* gr = p.g + (row0 + i) * kE;
+            float* gr = &at_row<float>(p.g, row0, kE, (uint32_t)i * kE);
             *reinterpret_cast<float2*>(gr + e0) = make_float2(d0 * inv, d1 * inv);
             const int q = tid & 31;
             if (q < (kE - kDV) / 4) {  // h and the zero columns, 16 bytes per thread
@@ -542,14 +581,17 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
 // (3) dphi(Q) = D phi(K) + G' S'^T for this wave's features, and the segment's sum phi(Q)^T G' (written over
 // the item once the walk is done)
 __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
-  __shared__ __align__(16) uint16_t VT2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t VT2[2][kE * kLD];
   __shared__ __align__(16) uint16_t VR2[2][kT * kLR];
   __shared__ __align__(16) uint16_t GRh2[2][kT * kLR];
   __shared__ __align__(16) uint16_t GRl2[2][kT * kLR];
-  __shared__ __align__(16) uint16_t GTh2[2][kE * kLT];
-  __shared__ __align__(16) uint16_t GTl2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t GTh2[2][kE * kLD];
+  __shared__ __align__(16) uint16_t GTl2[2][kE * kLD];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  zero_lds(VT2, sizeof(VT2), tid);
+  zero_lds(GTl2, sizeof(GTl2), tid);
+  __syncthreads();
   const int64_t h = blockIdx.x / p.n_seg;
   const int seg = (int)(blockIdx.x - h * p.n_seg);
   const int64_t t_begin = seg * p.seg_len;
@@ -607,7 +649,7 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
         for (int j = 0; j < 2; ++j) {
           const int fb = 2 * w + j;
           f32x4 acc = mfma_bf16(kt[j], cat(d4, d4), kZero4);
-          acc = mfma_bf16(hi_only(kt[j]), cat(d4l, kZero2), acc);
+          acc = mfma_bf16(kt[j], cat(d4l, kZero2), acc);  // lo parts against zeros
 #pragma unroll
           for (int e0 = 0; e0 < kNE; e0 += 2) {
             const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
@@ -620,18 +662,16 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
             acc = mfma_bf16(sl, gh, acc);
             acc = mfma_bf16(sh, gl, acc);
           }
-          if (c < n) *reinterpret_cast<uint2*>(p.dphiq + (row0 + c) * kF + 16 * fb + 4 * g) = pk4(acc);
+          if (c < n) at_row<uint2>(p.dphiq, row0, kF, (uint32_t)c * kF + 16 * fb + 4 * g) = pk4(acc);
         }
         // U += phi(Q)^T G' and S' += V'^T phi(K) for this wave's features
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
           for (int eb = 0; eb < kNE; ++eb) {
-            const uint2 gh = col4(GTh, 16 * eb + c, g), gl = col4(GTl, 16 * eb + c, g);
-            U[j][eb] = mfma_bf16(qt[j], cat(gh, gh), U[j][eb]);
-            U[j][eb] = mfma_bf16(hi_only(qt[j]), cat(gl, kZero2), U[j][eb]);
-            const uint2 v4 = col4(VT, 16 * eb + c, g);
-            S[eb][j] = mfma_bf16(cat(v4, v4), kt[j], S[eb][j]);
+            U[j][eb] = mfma_bf16(qt[j], col8(GTh, 16 * eb + c, g), U[j][eb]);
+            U[j][eb] = mfma_bf16(qt[j], col8(GTl, 16 * eb + c, g), U[j][eb]);  // g' lo against phi hi (lo: zeros)
+            S[eb][j] = mfma_bf16(col8(VT, 16 * eb + c, g), kt[j], S[eb][j]);
           }
         }
       });
@@ -646,14 +686,15 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
 // summed through LDS), walking the segment backward with U (the item: U after the segment) in accumulators
 __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
   __shared__ __align__(16) uint16_t VR2[2][kT * kLR];
-  __shared__ __align__(16) uint16_t VT2[2][kE * kLT];
   __shared__ __align__(16) uint16_t GRh2[2][kT * kLR];
   __shared__ __align__(16) uint16_t GRl2[2][kT * kLR];
-  __shared__ __align__(16) uint16_t GTh2[2][kE * kLT];
-  __shared__ __align__(16) uint16_t GTl2[2][kE * kLT];
+  __shared__ __align__(16) uint16_t GTh2[2][kE * kLD];
+  __shared__ __align__(16) uint16_t GTl2[2][kE * kLD];
   __shared__ __align__(16) float P2[2][kW * kT * kLPV];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  zero_lds(GTl2, sizeof(GTl2), tid);
+  __syncthreads();
   const int64_t h = blockIdx.x / p.n_seg;
   const int seg = (int)(blockIdx.x - h * p.n_seg);
   const int64_t t_begin = seg * p.seg_len;
@@ -679,9 +720,9 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
         // buffers, and a buffer is written again only after every wave has passed the next
         // step's barriers
         const int sb = step & 1;
-        uint16_t *VT = VT2[sb], *VR = VR2[sb], *GRh = GRh2[sb], *GRl = GRl2[sb], *GTh = GTh2[sb], *GTl = GTl2[sb];
+        uint16_t *VR = VR2[sb], *GRh = GRh2[sb], *GRl = GRl2[sb], *GTh = GTh2[sb], *GTl = GTl2[sb];
         float* P = P2[sb];
-        stage_v(in.v, n, VR, VT, tid);
+        stage_v(in.v, n, VR, nullptr, tid);
         stage_g(in.gp, n, GRh, GRl, GTh, GTl, tid);
         prefetch();
         const f32x4 qa = phi_feat(Pj, xq, 0), qb = phi_feat(Pj, xq, 1);
@@ -717,7 +758,7 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
         for (int j = 0; j < 2; ++j) {
           const int fb = 2 * w + j;
           f32x4 acc = mfma_bf16(qt[j], cat(d4, d4), kZero4);
-          acc = mfma_bf16(hi_only(qt[j]), cat(d4l, kZero2), acc);
+          acc = mfma_bf16(qt[j], cat(d4l, kZero2), acc);  // lo parts against zeros
 #pragma unroll
           for (int e0 = 0; e0 < kNE; e0 += 2) {
             const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
@@ -728,26 +769,25 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
             acc = mfma_bf16(cat(a0h, a1h), vr, acc);
             acc = mfma_bf16(cat(a0l, a1l), vr, acc);
           }
-          if (c < n) *reinterpret_cast<uint2*>(p.dphik + (row0 + c) * kF + 16 * fb + 4 * g) = pk4(acc);
+          if (c < n) at_row<uint2>(p.dphik, row0, kF, (uint32_t)c * kF + 16 * fb + 4 * g) = pk4(acc);
         }
         // dV^T[e][j] partial (e < dv): G^T A over this wave's A part, and U^T phi(K)^T over its features
 #pragma unroll
         for (int eb = 0; eb < kDV / 16; ++eb) {
-          f32x4 acc = mfma_bf16(cat(col4(GTh, 16 * eb + c, g), kZero2), awb, kZero4);
+          f32x4 acc = mfma_bf16(col8(GTh, 16 * eb + c, g), awb, kZero4);  // second copy against zeros
           acc = mfma_bf16(pk_pair(UA[0][eb], UA[1][eb]), pk_pair(ka, kb), acc);
           *reinterpret_cast<f32x4*>(P + (w * kT + c) * kLPV + 16 * eb + 4 * g) = acc;  // lane: e = 16 eb + 4g + r, j = c
         }
         // U += phi(Q)^T G' (both orders) for the earlier chunks
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const bf16x8 aqh = hi_only(qt[j]);
 #pragma unroll
           for (int eb = 0; eb < kNE; ++eb) {
-            const uint2 gh = col4(GTh, 16 * eb + c, g), gl = col4(GTl, 16 * eb + c, g);
-            UA[j][eb] = mfma_bf16(qt[j], cat(gh, gh), UA[j][eb]);
-            UA[j][eb] = mfma_bf16(aqh, cat(gl, kZero2), UA[j][eb]);
-            UB[eb][j] = mfma_bf16(cat(gh, gh), qt[j], UB[eb][j]);
-            UB[eb][j] = mfma_bf16(cat(gl, kZero2), aqh, UB[eb][j]);
+            const bf16x8 gh = col8(GTh, 16 * eb + c, g), gl = col8(GTl, 16 * eb + c, g);
+            UA[j][eb] = mfma_bf16(qt[j], gh, UA[j][eb]);
+            UA[j][eb] = mfma_bf16(qt[j], gl, UA[j][eb]);  // g' lo against phi hi (lo: zeros)
+            UB[eb][j] = mfma_bf16(gh, qt[j], UB[eb][j]);
+            UB[eb][j] = mfma_bf16(gl, qt[j], UB[eb][j]);
           }
         }
         __syncthreads();
@@ -762,7 +802,7 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
           }
           if (jj < n) {
             const uint2 lo = pk4(a0), hi = pk4(a1);
-            *reinterpret_cast<uint4*>(p.dv + (row0 + jj) * kDV + e0) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            at_row<uint4>(p.dv, row0, kDV, (uint32_t)jj * kDV + e0) = make_uint4(lo.x, lo.y, hi.x, hi.y);
           }
         }
       });
@@ -878,7 +918,8 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
     uint16_t* sX = reinterpret_cast<uint16_t*>(lds_raw + K::oX) + buf * K::RT * K::LX;
     float* sI = reinterpret_cast<float*>(lds_raw + K::oI) + buf * K::RT;
     const int64_t r0 = tile * K::RT;
-    const int tset = (int)((r0 / p.rows_per_head) % p.n_draw_sets);  // a tile never spans two draw sets
+    // a tile never spans two draw sets; one set skips the 64-bit division on the scalar unit
+    const int tset = p.n_draw_sets == 1 ? 0 : (int)((r0 / p.rows_per_head) % p.n_draw_sets);
     if (tset != set && r0 < p.n_rows) {  // this wave's rows of P, as both operands
       set = tset;
       const uint16_t* A = p.anchors + set * p.draw_set_stride;
