@@ -109,8 +109,10 @@ constexpr int kW = 8, kNT = kW * 64;  // waves; wave w owns feature blocks 2w, 2
 // LDS row strides in elements (odd multiples of 16 bytes)
 // [e][t] tiles hold each group of four tokens twice (v', g' hi) or once and then four zeros (g' lo), so that
 // one 16-byte read gives a lane its whole operand: four tokens against the split other side's hi and lo parts
-// (or, with the zeros, against its hi parts alone).  96-byte rows keep the 16-byte reads apart in banks.
-constexpr int kLD = 48;
+// (or, with the zeros, against its hi parts alone).  80-byte rows: at 96 bytes (which keeps the 16-byte
+// reads apart in banks) the staging stores, whose rows lie 8 apart, collide, and the backward measured
+// 843 against 831 us; 64-byte rows 888 us, 112- and 144-byte rows no better than 80.
+constexpr int kLD = 40;
 constexpr int kLR = kE + 8;        // [t][e] tiles
 constexpr int kLP = kE + 8;        // fp32 partials [w][t][e] (row stride 32 mod 64 bytes: 16-byte accesses in one pass)
 constexpr int kLPV = kDV + 8;
