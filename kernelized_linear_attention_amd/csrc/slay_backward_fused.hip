@@ -704,12 +704,15 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
   const float* item = item_ptr(p, h, seg);
   Proj Pj;
   load_proj(Pj, p, h, w, g, c);
-  f32x4 UA[2][kNE], UB[kNE][2];  // U as C[f][e] (contraction over f: dV) and as C[e][f] (over e: dphi(K))
+  // U as C[e][f] (contraction over e: dphi(K)) and, for its dv columns, as C[f][e] (over f: dV).  dV
+  // rounds its copy to single bf16, so that copy takes g' hi alone.
+  constexpr int kNEA = kDV / 16;
+  f32x4 UA[2][kNEA], UB[kNE][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int eb = 0; eb < kNE; ++eb) {
-      UA[j][eb] = load_fe(item, 2 * w + j, eb, lane);
+      if (eb < kNEA) UA[j][eb] = load_fe(item, 2 * w + j, eb, lane);
       UB[eb][j] = load_ef(item, 2 * w + j, eb, g, c);
     }
   walk_steps<true>(
@@ -786,8 +789,7 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
 #pragma unroll
           for (int eb = 0; eb < kNE; ++eb) {
             const bf16x8 gh = col8(GTh, 16 * eb + c, g), gl = col8(GTl, 16 * eb + c, g);
-            UA[j][eb] = mfma_bf16(qt[j], gh, UA[j][eb]);
-            UA[j][eb] = mfma_bf16(qt[j], gl, UA[j][eb]);  // g' lo against phi hi (lo: zeros)
+            if (eb < kNEA) UA[j][eb] = mfma_bf16(qt[j], gh, UA[j][eb]);
             UB[eb][j] = mfma_bf16(gh, qt[j], UB[eb][j]);
             UB[eb][j] = mfma_bf16(gl, qt[j], UB[eb][j]);
           }
@@ -883,6 +885,11 @@ __device__ __forceinline__ void vjp_load(const uint16_t* __restrict__ x, const u
                                                       0, 0));
 }
 
+// 2x of a bf16 value, exactly (through fp32)
+__device__ __forceinline__ uint16_t twice_bf16(uint16_t b) {
+  return (uint16_t)(__float_as_uint(2.0f * __uint_as_float((uint32_t)b << 16)) >> 16);
+}
+
 template <class K>
 __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   extern __shared__ __align__(16) char lds_raw[];
@@ -939,7 +946,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
           uint16_t e[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            e[i] = A[(fb * 16 + 4 * g + i) * K::D + cb * 16 + c16];
+            e[i] = twice_bf16(A[(fb * 16 + 4 * g + i) * K::D + cb * 16 + c16]);  // the anchor weight's factor 2
             e[4 + i] = G[(fb * 16 + 4 * g + i) * K::D + cb * 16 + c16];
           }
           pt[j][cb] = __builtin_bit_cast(bf16x8, make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
@@ -988,7 +995,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
         const uint2 dr = sD[(rb * 2 + j) * K::NT + tid];  // this thread's own piece
         const float dp[4] = {__uint_as_float(dr.x << 16), __uint_as_float(dr.x & 0xFFFF0000u),
                              __uint_as_float(dr.y << 16), __uint_as_float(dr.y & 0xFFFF0000u)};
-        // u = dphi * a * e: w_a = 2u, w_g = u a sqrt(beta)
+        // u = dphi * a * e: w_a = 2u (the 2 is in the transposed anchor rows), w_g = u a sqrt(beta)
         const float s1 = inv * c1[j];
         f32x4 wa, wg;
 #pragma unroll
@@ -996,7 +1003,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
           const float a = ya[r] * inv;
           const float e = fast_exp2(fmaf(yg[r], s1, c0[j]));
           const float u = dp[r] * (a * e);
-          wa[r] = u + u;
+          wa[r] = u;
           wg[r] = (u * a) * sb[j];
         }
         const bf16x8 w = pk_pair(wa, wg);
