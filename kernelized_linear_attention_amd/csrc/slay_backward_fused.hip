@@ -113,7 +113,11 @@ constexpr int kW = 8, kNT = kW * 64;  // waves; wave w owns feature blocks 2w, 2
 // reads apart in banks) the staging stores, whose rows lie 8 apart, collide, and the backward measured
 // 843 against 831 us; 64-byte rows 888 us, 112- and 144-byte rows no better than 80.
 constexpr int kLD = 40;
-constexpr int kLR = kE + 8;        // [t][e] tiles
+// [t][e] tiles ("row tiles") keep each token's 80 columns as 16-byte chunks that pair the two 16-column
+// blocks one 16x16x32 step contracts together: chunk 4p + g holds columns 32p + 4g .. +3 and
+// 32p + 16 + 4g .. +3 (p = 0, 1), chunk 8 + g columns 64 + 4g .. +3 and four zeros, so a lane's operand
+// is one 16-byte read.  224-byte rows keep those reads apart in banks.
+constexpr int kLR = 112;
 constexpr int kLP = kE + 8;        // fp32 partials [w][t][e] (row stride 32 mod 64 bytes: 16-byte accesses in one pass)
 constexpr int kLPV = kDV + 8;
 
@@ -275,6 +279,12 @@ __device__ __forceinline__ f32x4 phi_tok(const Proj& P, const XRows& X, int j, i
   return o;
 }
 
+// position of column e (a multiple of 4: four columns together) in a row of a row tile
+__device__ __forceinline__ int rcol(int e) {
+  const int b = e >> 4, g = (e >> 2) & 3;
+  return b < 4 ? 8 * (4 * (b >> 1) + g) + 4 * (b & 1) : 8 * (8 + g);
+}
+
 // position of token t in a row of an [e][t] tile (the first of its two places)
 __device__ __forceinline__ int tok_at(int t) { return 8 * (t >> 2) + (t & 3); }
 
@@ -293,7 +303,10 @@ __device__ __forceinline__ void stage_v(uint4 x, int n, uint16_t* VR, uint16_t* 
   if (tid < kT * 8) {
     const int t = tid >> 3, e0 = 8 * (tid & 7);
     if (t >= n) x = make_uint4(0, 0, 0, 0);
-    if (VR) *reinterpret_cast<uint4*>(VR + t * kLR + e0) = x;
+    if (VR) {
+      *reinterpret_cast<uint2*>(VR + t * kLR + rcol(e0)) = make_uint2(x.x, x.y);
+      *reinterpret_cast<uint2*>(VR + t * kLR + rcol(e0 + 4)) = make_uint2(x.z, x.w);
+    }
     if (!VT) return;
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};  // columns (e0 + 2i, e0 + 2i + 1) of token t
     uint32_t o[4];                                // the same of token t ^ 1
@@ -316,8 +329,11 @@ __device__ __forceinline__ void stage_v(uint4 x, int n, uint16_t* VR, uint16_t* 
     if (VR) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        // chunks 8 .. 11: column 64 (ones) and zeros
+        static_assert(8 * 8 == kDV, "the last block's chunks follow the first 64 columns");
         *reinterpret_cast<uint4*>(VR + (t + u) * kLR + kDV) = make_uint4((one >> (16 * u)) & 0xFFFFu, 0, 0, 0);
-        *reinterpret_cast<uint4*>(VR + (t + u) * kLR + kDV + 8) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int q = 1; q < 4; ++q) *reinterpret_cast<uint4*>(VR + (t + u) * kLR + kDV + 8 * q) = make_uint4(0, 0, 0, 0);
       }
     }
     if (VT) {
@@ -341,8 +357,8 @@ __device__ __forceinline__ void stage_g(f32x4 x, int n, uint16_t* GRh, uint16_t*
     if (t >= n) x = kZero4;
     uint2 h, l;
     split4(x, h, l);
-    *reinterpret_cast<uint2*>(GRh + t * kLR + e0) = h;
-    *reinterpret_cast<uint2*>(GRl + t * kLR + e0) = l;
+    *reinterpret_cast<uint2*>(GRh + t * kLR + rcol(e0)) = h;  // the last block's zero halves are set once
+    *reinterpret_cast<uint2*>(GRl + t * kLR + rcol(e0)) = l;
     if (!GTh) return;
     const bool odd = t & 1;
     const uint32_t mh = odd ? h.y : h.x, ml = odd ? l.y : l.x;  // columns e0 + 2 odd, e0 + 2 odd + 1 of token t
@@ -368,12 +384,9 @@ __device__ __forceinline__ void stage_g(f32x4 x, int n, uint16_t* GRh, uint16_t*
 __device__ __forceinline__ bf16x8 col8(const uint16_t* T, int e, int g) {
   return ld8(T + e * kLD + 8 * g);
 }
-// columns 16 e0 + 4g .. +3 and 16 e1 + 4g .. +3 of row r of a [t][e] tile (e1 < 0: zeros)
-__device__ __forceinline__ bf16x8 row4x2(const uint16_t* R, int r, int e0, int e1, int g) {
-  const uint2 a = *reinterpret_cast<const uint2*>(R + r * kLR + 16 * e0 + 4 * g);
-  const uint2 b = e1 >= 0 ? *reinterpret_cast<const uint2*>(R + r * kLR + 16 * e1 + 4 * g) : kZero2;
-  return cat(a, b);
-}
+// chunk q of row r of a row tile: for q = 2 e0 + g, columns 16 e0 + 4g .. +3 and 16 (e0 + 1) + 4g .. +3
+// (e0 even; for the last block, zeros in place of the second four)
+__device__ __forceinline__ bf16x8 rchunk(const uint16_t* R, int r, int q) { return ld8(R + r * kLR + 8 * q); }
 
 // state item of (head, seg) and its accumulator tiles: element (f = 16 fb + 4g + r, e = 16 eb + c) of the
 // tile (fb, eb) in lane 16 g + c, slot r ("C[f][e]" order: one 16-byte access per lane)
@@ -593,6 +606,8 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   zero_lds(VT2, sizeof(VT2), tid);
   zero_lds(GTl2, sizeof(GTl2), tid);
+  zero_lds(GRh2, sizeof(GRh2), tid);
+  zero_lds(GRl2, sizeof(GRl2), tid);
   __syncthreads();
   const int64_t h = blockIdx.x / p.n_seg;
   const int seg = (int)(blockIdx.x - h * p.n_seg);
@@ -632,40 +647,41 @@ __global__ __launch_bounds__(kNT) void pb_dq_kernel(PbParams p) {
         // D^T[j][i] = v'_j . g'_i (split g'), masked j <= i < n; every wave forms it (lane: j = 4g + r, i = c)
         f32x4 dt = kZero4;
 #pragma unroll
-        for (int kk = 0; kk < 64; kk += 32) {
-          const bf16x8 vr = ld8(VR + c * kLR + kk + 8 * g);
-          dt = mfma_bf16(vr, ld8(GRh + c * kLR + kk + 8 * g), dt);
-          dt = mfma_bf16(vr, ld8(GRl + c * kLR + kk + 8 * g), dt);
-        }
-        {
-          const bf16x8 vr = row4x2(VR, c, 4, -1, g);
-          dt = mfma_bf16(vr, row4x2(GRh, c, 4, -1, g), dt);
-          dt = mfma_bf16(vr, row4x2(GRl, c, 4, -1, g), dt);
+        for (int e0 = 0; e0 < kNE; e0 += 2) {
+          const bf16x8 vr = rchunk(VR, c, 2 * e0 + g);
+          dt = mfma_bf16(vr, rchunk(GRh, c, 2 * e0 + g), dt);
+          dt = mfma_bf16(vr, rchunk(GRl, c, 2 * e0 + g), dt);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) dt[r] = (4 * g + r <= c && c < n) ? dt[r] : 0.f;
         uint2 d4, d4l;
         split4(dt, d4, d4l);
-        // dphi(Q)^T[f][i] for this wave's features
+        // dphi(Q)^T[f][i] for this wave's features (both blocks per chunk of g', so each chunk is read once
+        // and its registers are free before the next)
+        f32x4 acc[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int fb = 2 * w + j;
-          f32x4 acc = mfma_bf16(kt[j], cat(d4, d4), kZero4);
-          acc = mfma_bf16(kt[j], cat(d4l, kZero2), acc);  // lo parts against zeros
+          acc[j] = mfma_bf16(kt[j], cat(d4, d4), kZero4);
+          acc[j] = mfma_bf16(kt[j], cat(d4l, kZero2), acc[j]);  // lo parts against zeros
+        }
 #pragma unroll
-          for (int e0 = 0; e0 < kNE; e0 += 2) {
-            const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
+        for (int e0 = 0; e0 < kNE; e0 += 2) {
+          const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
+          const bf16x8 gh = rchunk(GRh, c, 2 * e0 + g), gl = rchunk(GRl, c, 2 * e0 + g);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
             uint2 a0h, a0l, a1h = kZero2, a1l = kZero2;
             split4(S[e0][j], a0h, a0l);
             if (e1 >= 0) split4(S[e1][j], a1h, a1l);
             const bf16x8 sh = cat(a0h, a1h), sl = cat(a0l, a1l);
-            const bf16x8 gh = row4x2(GRh, c, e0, e1, g), gl = row4x2(GRl, c, e0, e1, g);
-            acc = mfma_bf16(sh, gh, acc);
-            acc = mfma_bf16(sl, gh, acc);
-            acc = mfma_bf16(sh, gl, acc);
+            acc[j] = mfma_bf16(sh, gh, acc[j]);
+            acc[j] = mfma_bf16(sl, gh, acc[j]);
+            acc[j] = mfma_bf16(sh, gl, acc[j]);
           }
-          if (c < n) at_row<uint2>(p.dphiq, row0, kF, (uint32_t)c * kF + 16 * fb + 4 * g) = pk4(acc);
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (c < n) at_row<uint2>(p.dphiq, row0, kF, (uint32_t)c * kF + 16 * (2 * w + j) + 4 * g) = pk4(acc[j]);
         // U += phi(Q)^T G' and S' += V'^T phi(K) for this wave's features
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -696,6 +712,8 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   zero_lds(GTl2, sizeof(GTl2), tid);
+  zero_lds(GRh2, sizeof(GRh2), tid);
+  zero_lds(GRl2, sizeof(GRl2), tid);
   __syncthreads();
   const int64_t h = blockIdx.x / p.n_seg;
   const int seg = (int)(blockIdx.x - h * p.n_seg);
@@ -744,38 +762,38 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
         // D[i][j] = g'_i . v'_j (split g'), masked i >= j (lane: i = 4g + r, j = c)
         f32x4 dm = kZero4;
 #pragma unroll
-        for (int kk = 0; kk < 64; kk += 32) {
-          const bf16x8 vr = ld8(VR + c * kLR + kk + 8 * g);
-          dm = mfma_bf16(ld8(GRh + c * kLR + kk + 8 * g), vr, dm);
-          dm = mfma_bf16(ld8(GRl + c * kLR + kk + 8 * g), vr, dm);
-        }
-        {
-          const bf16x8 vr = row4x2(VR, c, 4, -1, g);
-          dm = mfma_bf16(row4x2(GRh, c, 4, -1, g), vr, dm);
-          dm = mfma_bf16(row4x2(GRl, c, 4, -1, g), vr, dm);
+        for (int e0 = 0; e0 < kNE; e0 += 2) {
+          const bf16x8 vr = rchunk(VR, c, 2 * e0 + g);
+          dm = mfma_bf16(rchunk(GRh, c, 2 * e0 + g), vr, dm);
+          dm = mfma_bf16(rchunk(GRl, c, 2 * e0 + g), vr, dm);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) dm[r] = (4 * g + r >= c && 4 * g + r < n) ? dm[r] : 0.f;
         uint2 d4, d4l;
         split4(dm, d4, d4l);
-        // dphi(K)^T[f][j] for this wave's features
+        // dphi(K)^T[f][j] for this wave's features (both blocks per chunk of v', as for dphi(Q))
+        f32x4 acc[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int fb = 2 * w + j;
-          f32x4 acc = mfma_bf16(qt[j], cat(d4, d4), kZero4);
-          acc = mfma_bf16(qt[j], cat(d4l, kZero2), acc);  // lo parts against zeros
+          acc[j] = mfma_bf16(qt[j], cat(d4, d4), kZero4);
+          acc[j] = mfma_bf16(qt[j], cat(d4l, kZero2), acc[j]);  // lo parts against zeros
+        }
 #pragma unroll
-          for (int e0 = 0; e0 < kNE; e0 += 2) {
-            const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
+        for (int e0 = 0; e0 < kNE; e0 += 2) {
+          const int e1 = e0 + 1 < kNE ? e0 + 1 : -1;
+          const bf16x8 vr = rchunk(VR, c, 2 * e0 + g);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
             uint2 a0h, a0l, a1h = kZero2, a1l = kZero2;
             split4(UB[e0][j], a0h, a0l);
             if (e1 >= 0) split4(UB[e1][j], a1h, a1l);
-            const bf16x8 vr = row4x2(VR, c, e0, e1, g);
-            acc = mfma_bf16(cat(a0h, a1h), vr, acc);
-            acc = mfma_bf16(cat(a0l, a1l), vr, acc);
+            acc[j] = mfma_bf16(cat(a0h, a1h), vr, acc[j]);
+            acc[j] = mfma_bf16(cat(a0l, a1l), vr, acc[j]);
           }
-          if (c < n) at_row<uint2>(p.dphik, row0, kF, (uint32_t)c * kF + 16 * fb + 4 * g) = pk4(acc);
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (c < n) at_row<uint2>(p.dphik, row0, kF, (uint32_t)c * kF + 16 * (2 * w + j) + 4 * g) = pk4(acc[j]);
         // dV^T[e][j] partial (e < dv): G^T A over this wave's A part, and U^T phi(K)^T over its features
 #pragma unroll
         for (int eb = 0; eb < kDV / 16; ++eb) {
