@@ -839,7 +839,7 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
 // features' y, the weights w and its partial dxh over those features into its
 // own fp32 LDS tile; then, summing the waves' partials, the projection
 // dx = (dxh - xh (xh . dxh)) / |x|, 16 lanes per row.  x and dphi of the
-// next two tiles are in flight while the current one is computed.
+// next tiles are in flight while the current one is computed.
 template <int NF_>
 struct VjpK {
   static constexpr int NF = NF_, F = NF * 16, D = 64;
@@ -847,9 +847,9 @@ struct VjpK {
   static constexpr int RT = 32, NRB = RT / 16;  // rows per tile
   static constexpr int LX = D + 8, LR = D + 4;
   // x tiles and 1/|x| per row (negative where |x| is clamped), both double-buffered by tile
-  // parity; per-wave partials; each thread's own dphi pieces ([piece][thread], 8 bytes each)
-  static constexpr int oX = 0, oR = 2 * RT * LX * 2, oI = oR + NW * RT * LR * 4, oD = oI + 2 * RT * 4;
-  static constexpr int kLds = oD + NRB * 2 * NT * 8;
+  // parity; per-wave partials
+  static constexpr int oX = 0, oR = 2 * RT * LX * 2, oI = oR + NW * RT * LR * 4;
+  static constexpr int kLds = oI + 2 * RT * 4;
   static_assert(NT >= RT * 8 && NT == RT * 16, "one x piece per thread (some idle), one output piece per thread");
 };
 
@@ -912,7 +912,6 @@ template <class K>
 __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   extern __shared__ __align__(16) char lds_raw[];
   float* sR = reinterpret_cast<float*>(lds_raw + K::oR);
-  uint2* sD = reinterpret_cast<uint2*>(lds_raw + K::oD);
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int side = blockIdx.y;
@@ -924,10 +923,12 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
   bf16x8 pa[2][2], pg[2][2], pt[2][K::D / 16];
   float c1[2], c0[2], sb[2];
   int set = -1;
-  // The two tiles after the one being computed are in flight, in two
-  // register sets that alternate (the loop body is taken twice per
-  // iteration, once per set); a tile's inputs move to LDS before its set is
-  // reloaded, so no loaded value is copied between registers.  Vector loads
+  // Tiles are loaded two ahead, into two register sets that alternate (the
+  // loop body is taken twice per iteration, once per set).  A tile's x rows
+  // move to LDS at its start; its dphi pieces are read from the registers by
+  // the thread that loaded them, and the set is reloaded (for the tile two
+  // ahead) once they have been used, so no loaded value is copied between
+  // registers and dphi needs no trip through LDS.  Vector loads
   // and stores retire in issue order and share one counter; every load and
   // store here is a bounded buffer access issued by every thread for every
   // tile (a tile past the last one reads zeros and writes nothing), so the
@@ -941,7 +942,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
     // sX and sI of this tile's parity: their last readers (the tile before the previous one)
     // are done once every thread has passed the previous tile's staging barrier, which it
     // reaches after its own reads of them; sR is written only after this tile's staging
-    // barrier, and sD is read back only by the thread that wrote it
+    // barrier
     uint16_t* sX = reinterpret_cast<uint16_t*>(lds_raw + K::oX) + buf * K::RT * K::LX;
     float* sI = reinterpret_cast<float*>(lds_raw + K::oI) + buf * K::RT;
     const int64_t r0 = tile * K::RT;
@@ -977,10 +978,6 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       }
       wait_vmem();  // here, where the reload is rare, rather than at the first use
     }
-#pragma unroll
-    for (int rb = 0; rb < K::NRB; ++rb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) sD[(rb * 2 + j) * K::NT + tid] = pf.dp[rb][j];
     if (tid < K::RT * 8) {  // x rows, and 1/|x| once per row (eight threads per row)
       *reinterpret_cast<uint4*>(sX + (tid >> 3) * K::LX + 8 * (tid & 7)) = pf.x;
       const uint32_t wds[4] = {pf.x.x, pf.x.y, pf.x.z, pf.x.w};
@@ -993,7 +990,6 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       ss = sum_lanes8(ss);
       if ((tid & 7) == 0) sI[tid >> 3] = ss < 1e-24f ? -1e12f : __builtin_amdgcn_rsqf(ss);
     }
-    load_tile(tile + 2 * gs, pf);
     __syncthreads();
 #pragma unroll
     for (int rb = 0; rb < K::NRB; ++rb) {
@@ -1010,7 +1006,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
         ya = mfma_bf16(pa[j][1], xb1, ya);
         f32x4 yg = mfma_bf16(pg[j][0], xb0, kZero4);
         yg = mfma_bf16(pg[j][1], xb1, yg);
-        const uint2 dr = sD[(rb * 2 + j) * K::NT + tid];  // this thread's own piece
+        const uint2 dr = pf.dp[rb][j];
         const float dp[4] = {__uint_as_float(dr.x << 16), __uint_as_float(dr.x & 0xFFFF0000u),
                              __uint_as_float(dr.y << 16), __uint_as_float(dr.y & 0xFFFF0000u)};
         // u = dphi * a * e: w_a = 2u (the 2 is in the transposed anchor rows), w_g = u a sqrt(beta)
@@ -1033,6 +1029,7 @@ __global__ __launch_bounds__(K::NT) void vjp_kernel(VjpParams p) {
       for (int cb = 0; cb < K::D / 16; ++cb)
         *reinterpret_cast<f32x4*>(sR + (wave * K::RT + rb * 16 + c16) * K::LR + cb * 16 + 4 * g) = dX[cb];
     }
+    load_tile(tile + 2 * gs, pf);
     __syncthreads();
     const __amdgpu_buffer_rsrc_t ro = tile_rsrc(dx, r0, p.n_rows, K::RT, K::D * 2);
     {  // 16 lanes per row, four columns each
