@@ -294,6 +294,20 @@ __device__ __forceinline__ void zero_lds(void* p, int n, int tid) {
   for (int i = tid; i < n / 16; i += kNT) static_cast<uint4*>(p)[i] = make_uint4(0, 0, 0, 0);
 }
 
+// A 16 x 16 fp32 tile in the MFMA result order (lane (g, c): rows 4g .. 4g+3 of column c) moved to
+// the transposed order through the wave's own LDS tile: tr_put stores it, tr_get returns rows
+// 4g .. 4g+3 of column c of the transpose.  phi of one operand order becomes the other's this way
+// rather than by a second projection and epilogue.  The wave's LDS accesses run in order, so no
+// barrier separates the two.
+constexpr int kLTR = 24;  // 96-byte rows: the 16-byte reads stay apart in banks
+__device__ __forceinline__ void tr_put(float* T, const f32x4& v, int g, int c) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) T[(4 * g + r) * kLTR + c] = v[r];
+}
+__device__ __forceinline__ f32x4 tr_get(const float* T, int g, int c) {
+  return *reinterpret_cast<const f32x4*>(T + c * kLTR + 4 * g);
+}
+
 // V' = [v | 1 | 0] of the step's tokens (zero rows past n) as [t][e] rows and [e][t] columns
 // (either may be null; the zero columns of the latter are set once, before the walk).
 // The columns are written as token pairs: lanes t and t^1 (lane ^ 8) trade their
@@ -492,6 +506,7 @@ __global__ __launch_bounds__(kNT) void pb_state_kernel(PbParams p) {
 __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
   __shared__ __align__(16) uint16_t VT2[2][kE * kLD];
   __shared__ __align__(16) float P2[2][kW * kT * kLP];
+  __shared__ __align__(16) float TR[kW][2][kT * kLTR];  // each wave's phi(k) transposes
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   zero_lds(VT2, sizeof(VT2), tid);
@@ -523,9 +538,8 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
         prefetch();
         const f32x4 qa = phi_feat(Pj, xq, 0), qb = phi_feat(Pj, xq, 1);
         const f32x4 ka = phi_feat(Pj, xk, 0), kb = phi_feat(Pj, xk, 1);
-        f32x4 kt[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) kt[j] = phi_tok(Pj, xk, j, g);
+        tr_put(TR[w][0], ka, g, c);  // phi(k) with tokens in k-slots, for the state update
+        tr_put(TR[w][1], kb, g, c);
         __syncthreads();
         // this wave's part of A^T[j][i] = sum_f phi(K_j)_f phi(Q_i)_f over its features (split phi), masked j <= i
         uint2 qh0, ql0, qh1, ql1, kh0, kl0, kh1, kl1;
@@ -556,7 +570,7 @@ __global__ __launch_bounds__(kNT) void pb_g_kernel(PbParams p) {
         // S' += phi(K)^T V' for this wave's features (after its use: S' is the state before the chunk)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const bf16x8 a = hilo(kt[j]);
+          const bf16x8 a = hilo(tr_get(TR[w][j], g, c));
 #pragma unroll
           for (int eb = 0; eb < kNE; ++eb) S[j][eb] = mfma_bf16(a, col8(VT, 16 * eb + c, g), S[j][eb]);
         }
@@ -709,6 +723,7 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
   __shared__ __align__(16) uint16_t GTh2[2][kE * kLD];
   __shared__ __align__(16) uint16_t GTl2[2][kE * kLD];
   __shared__ __align__(16) float P2[2][kW * kT * kLPV];
+  __shared__ __align__(16) float TR[kW][2][kT * kLTR];  // each wave's phi(q) transposes
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   zero_lds(GTl2, sizeof(GTl2), tid);
@@ -750,10 +765,12 @@ __global__ __launch_bounds__(kNT) void pb_dk_kernel(PbParams p) {
         prefetch();
         const f32x4 qa = phi_feat(Pj, xq, 0), qb = phi_feat(Pj, xq, 1);
         const f32x4 ka = phi_feat(Pj, xk, 0), kb = phi_feat(Pj, xk, 1);
+        tr_put(TR[w][0], qa, g, c);  // phi(q) with tokens in k-slots, for dphi(K) and U
+        tr_put(TR[w][1], qb, g, c);
+        __syncthreads();
         bf16x8 qt[2];  // split phi(q) of the step's tokens, four per lane
 #pragma unroll
-        for (int j = 0; j < 2; ++j) qt[j] = hilo(phi_tok(Pj, xq, j, g));
-        __syncthreads();
+        for (int j = 0; j < 2; ++j) qt[j] = hilo(tr_get(TR[w][j], g, c));
         // this wave's part of A[i][j] over its features, masked i >= j (lane: i = 4g + r, j = c)
         f32x4 aw = mfma_bf16(pk_pair(qa, qb), pk_pair(ka, kb), kZero4);
 #pragma unroll
